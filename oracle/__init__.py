@@ -1,0 +1,21 @@
+"""CPU oracle for the W8A8_DYNAMIC path. TEST INFRASTRUCTURE ONLY.
+
+This package is a plain, slow, obviously correct NumPy restatement of what the
+W8A8_DYNAMIC linear and MoE paths compute. Only ``tests/``,
+``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of ``bench.py`` may import
+or call it. The HIP library never uses it, and it shares no code, constants or
+helpers with the HIP library.
+
+Sources (web pages, cited by title and section):
+  * "DeepSeek-V4 W8A8 执行链从量化权重到 Ascend INT8 算子": §一 (the per-token /
+    per-channel symmetric INT8 recipe), §二 (dense path: dynamic quant, INT8
+    matmul, BF16 output), §三 (MoE path: group_list, W13 -> SwiGLU -> requant ->
+    W2).
+  * "Qwen3.8-FP8 on Ascend 950: Why Weights Become MXFP8 at Load Time": Deep Dive
+    1-5 (block-FP8 resolve, MX re-quantization, runtime MX matmul).
+
+Parity status per function is listed in ``oracle/w8a8_ref.py``'s header.
+"""
+
+from .w8a8_ref import *  # noqa: F401,F403
+from .w8a8_ref import __all__  # noqa: F401
