@@ -1,0 +1,439 @@
+#!/usr/bin/env python3
+"""Benchmark of the W8A8_DYNAMIC hot path on one MI355X.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode|prefill|moe|tiny]
+
+Prints ONE JSON line. A step is one pass of the workload's whole hot path over
+resident, seeded synthetic inputs:
+  decode   (default) per-token quant + INT8 linear for M = 1, 4, 16 and 64 rows,
+           K = 7168, N = 4096, no bias. Sixteen copies of the packed weight
+           (16 x 29.4 MB) are used round-robin so that no weight read is served
+           by the 256 MB MALL: every step reads its weights from HBM.
+           value = algorithmic HBM bytes of the step / step time (GB/s).
+  prefill  quant + INT8 linear, M = 8192, K = 7168, N = 4096, bias.
+           value = 2*M*N*K / step time (TOPS).
+  moe      quant -> W13 grouped GEMM -> SwiGLU + requant -> W2 grouped GEMM for
+           T = 2048 tokens routed top-8 over 256 experts, H = 4096, I = 2048.
+           value = tokens / step time (tokens/s).
+  tiny     quant + INT8 linear, 16 x 256 x 128 with bias (latency case).
+
+Every step is captured once as a HIP graph (the C ABI calls only enqueue
+kernels) and replayed, so host-side Python does not pace the GPU. The average
+duration of the dominant kernel comes from HIP events recorded around its
+launches on the same stream inside the captured steps.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, GB/s
+PEAK_INT8_TOPS = 5000.0        # MI355X dense INT8 MFMA, TOP/s
+BYTES_INT8 = 1
+
+
+def _args():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="decode", choices=["decode", "prefill", "moe", "tiny"])
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="approximate budget of the oracle timing on the host")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+# ---------------------------------------------------------------------------
+# workloads
+# ---------------------------------------------------------------------------
+
+class Workload:
+    """A list of phase graphs (step i replays phase i % len), each bracketing its
+    dominant-kernel launches with event pairs."""
+    name = ""
+    metric = "W8A8 linear TOPS and HBM GB/s (% of peak); MoE grouped-GEMM tokens/s"
+    unit = ""
+    bound = "hbm"
+
+    def __init__(self, w, torch):
+        self.w = w
+        self.torch = torch
+        self.phases = []          # list of (graph, [(ev_start, ev_end, key)])
+
+    def capture(self, fns):
+        """fns: list of callables, each enqueuing one step and returning a list of
+        (start_event, end_event, key) it recorded."""
+        torch = self.torch
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            for fn in fns:      # eager warm-up of every phase outside capture
+                fn(record=False)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        for fn in fns:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                evs = fn(record=True)
+            self.phases.append((g, evs))
+
+    def step(self, i):
+        self.phases[i % len(self.phases)][0].replay()
+
+
+def _ev(torch):
+    return torch.cuda.Event(enable_timing=True)
+
+
+class DenseWorkload(Workload):
+    def __init__(self, w, torch, name, Ms, K, N, bias, outlier, copies):
+        super().__init__(w, torch)
+        import numpy as np
+
+        import synth
+        self.name, self.Ms, self.K, self.N = name, list(Ms), K, N
+        self.has_bias = bias
+        self.copies = copies
+        Mmax = max(self.Ms)
+        if name == "decode":
+            d = synth.decode(seed=0, M=Mmax)
+        elif name == "prefill":
+            d = synth.prefill(seed=0)
+        elif name == "tiny":
+            d = synth.tiny(seed=0)
+        else:
+            d = synth.dense(Mmax, K, N, outlier_frac=outlier, bias=bias, seed=0, name=name)
+        self.d = d
+        dev = "cuda"
+        self.x = torch.from_numpy(d.x.view(np.int16)).to(dev).view(torch.bfloat16)
+        self.w_scale = torch.from_numpy(d.w_scale).to(dev)
+        self.bias = (torch.from_numpy(d.bias.view(np.int16)).to(dev).view(torch.bfloat16)
+                     if d.bias is not None else None)
+        packed = w.prepack_weight(torch.from_numpy(d.w).to(dev))
+        nb = packed.numel()
+        self.wp = torch.empty((copies, nb), dtype=torch.uint8, device=dev)
+        for c in range(copies):
+            self.wp[c].copy_(packed)
+        del packed
+        self.q = {M: torch.empty((M, K), dtype=torch.int8, device=dev) for M in self.Ms}
+        self.s = {M: torch.empty((M,), dtype=torch.float32, device=dev) for M in self.Ms}
+        self.y = {M: torch.empty((M, N), dtype=torch.bfloat16, device=dev) for M in self.Ms}
+        self.ws = {M: torch.empty((max(1, w.linear_workspace_bytes(M, N, K)),), dtype=torch.uint8,
+                                  device=dev) for M in self.Ms}
+        # round-robin over weight copies: phase p uses copies p*len(Ms) + j
+        per = len(self.Ms)
+        nphase = max(1, copies // per)
+        fns = []
+        for p in range(nphase):
+            fns.append(self._make_step([(p * per + j) % copies for j in range(per)]))
+        self.capture(fns)
+        self.unit = "GB/s" if name != "prefill" else "TOPS"
+        self.bound = "hbm" if name != "prefill" else "mfma"
+
+    def _make_step(self, copy_ids):
+        w, torch = self.w, self.torch
+
+        def fn(record):
+            evs = []
+            for M, c in zip(self.Ms, copy_ids):
+                xm = self.x[:M]
+                w.dynamic_quant(xm, self.q[M], self.s[M])
+                if record:
+                    a, b = _ev(torch), _ev(torch)
+                    a.record()
+                w.linear(self.q[M], self.s[M], self.wp[c], self.w_scale, self.N, bias=self.bias,
+                         y=self.y[M], workspace=self.ws[M])
+                if record:
+                    b.record()
+                    evs.append((a, b, M))
+            return evs
+        return fn
+
+    # algorithmic bytes / ops
+    def gemm_bytes(self, M):
+        b = self.N * self.K * BYTES_INT8 + 4 * self.N + M * self.K + 4 * M + 2 * M * self.N
+        if self.has_bias:
+            b += 2 * self.N
+        return b
+
+    def step_bytes(self):
+        # quant (BF16 in, INT8 + scale out) + GEMM (W, scales, q, bias, BF16 out)
+        return sum(2 * M * self.K + M * self.K + 4 * M + self.gemm_bytes(M) for M in self.Ms)
+
+    def step_ops(self):
+        return sum(2 * M * self.N * self.K for M in self.Ms)
+
+    def value(self, sec_per_step):
+        if self.unit == "TOPS":
+            return self.step_ops() / sec_per_step / 1e12
+        return self.step_bytes() / sec_per_step / 1e9
+
+    def dominant(self, per_key_ms):
+        """Roofline of the linear kernel(s): per launch algorithmic bytes / ops."""
+        tot_ms = sum(per_key_ms[M] for M in self.Ms)
+        if self.bound == "mfma":
+            ops = sum(2 * M * self.N * self.K for M in self.Ms)
+            ach = ops / (tot_ms * 1e-3) / 1e12
+            return dict(bound="mfma", achieved=ach, peak=PEAK_INT8_TOPS, unit="TOP/s",
+                        frac=ach / PEAK_INT8_TOPS)
+        byts = sum(self.gemm_bytes(M) for M in self.Ms)
+        ach = byts / (tot_ms * 1e-3) / 1e9
+        return dict(bound="hbm", achieved=ach, peak=PEAK_HBM_GBS, unit="GB/s",
+                    frac=ach / PEAK_HBM_GBS)
+
+    def config(self):
+        c = {"workload": self.name, "M": self.Ms if len(self.Ms) > 1 else self.Ms[0], "K": self.K,
+             "N": self.N, "bias": self.has_bias, "weight_copies": self.copies,
+             "x": "N(0,1) with outliers x20", "w": "int8 uniform [-127,127]"}
+        return c
+
+    def cpu_baseline(self, budget_s):
+        import oracle as O
+        d = self.d
+        if self.name == "prefill":
+            rows = 128
+            xs = d.x[:rows]
+            t0 = time.perf_counter()
+            n = 0
+            while True:
+                q, s = O.dynamic_quant(xs)
+                O.linear(q, s, d.w, d.w_scale, d.bias)
+                n += 1
+                if time.perf_counter() - t0 > budget_s:
+                    break
+            dt = (time.perf_counter() - t0) / n
+            ops = 2 * rows * self.N * self.K
+            return dict(value=ops / dt / 1e12, unit="TOPS",
+                        sample=f"oracle quant + linear on the first {rows} of 8192 rows "
+                               f"({n} repetitions), full N and K")
+        t0 = time.perf_counter()
+        n = 0
+        while True:
+            for M in self.Ms:
+                q, s = O.dynamic_quant(d.x[:M])
+                O.linear(q, s, d.w, d.w_scale, d.bias)
+            n += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
+        dt = (time.perf_counter() - t0) / n
+        return dict(value=self.step_bytes() / dt / 1e9, unit="GB/s",
+                    sample=f"oracle quant + linear for every M of the step, {n} full steps")
+
+
+class MoeWorkload(Workload):
+    def __init__(self, w, torch):
+        super().__init__(w, torch)
+        import numpy as np
+
+        import synth
+        self.name = "moe"
+        m = synth.moe(seed=0)
+        self.m = m
+        E, H, I = m.E, m.H, m.I
+        dev = "cuda"
+        per13 = w.packed_weight_bytes(1, 2 * I, H)
+        per2 = w.packed_weight_bytes(1, H, I)
+        self.w13p = torch.empty((E * per13,), dtype=torch.uint8, device=dev)
+        self.w2p = torch.empty((E * per2,), dtype=torch.uint8, device=dev)
+        for e in range(E):
+            w.prepack_weight(torch.from_numpy(m.w13(e)).to(dev), out=self.w13p[e * per13:(e + 1) * per13])
+            w.prepack_weight(torch.from_numpy(m.w2(e)).to(dev), out=self.w2p[e * per2:(e + 1) * per2])
+            m.drop_cache()
+        self.w13s = torch.from_numpy(m.w13_scale).to(dev)
+        self.w2s = torch.from_numpy(m.w2_scale).to(dev)
+        self.gl = torch.from_numpy(m.group_list).to(dev)
+        self.x = torch.from_numpy(m.x_rows().view(np.int16)).to(dev).view(torch.bfloat16)
+        R = m.R
+        self.y = torch.empty((R, H), dtype=torch.bfloat16, device=dev)
+        self.ws = torch.empty((w.moe_workspace_bytes(R, E, H, I),), dtype=torch.uint8, device=dev)
+        # sub-stage buffers for the per-kernel timing phase
+        self.q1 = torch.empty((R, H), dtype=torch.int8, device=dev)
+        self.s1 = torch.empty((R,), dtype=torch.float32, device=dev)
+        self.h = torch.empty((R, 2 * I), dtype=torch.bfloat16, device=dev)
+        self.q2 = torch.empty((R, I), dtype=torch.int8, device=dev)
+        self.s2 = torch.empty((R,), dtype=torch.float32, device=dev)
+        self.unit = "tokens/s"
+        self.bound = "hbm"
+        self.capture([self._step])
+
+    def _step(self, record):
+        """Same kernels as moe_grouped, through the sub-stage entry points so the
+        two grouped GEMM launches can be bracketed by events."""
+        w, torch, m = self.w, self.torch, self.m
+        evs = []
+        w.dynamic_quant(self.x, self.q1, self.s1)
+        a, b = (_ev(torch), _ev(torch)) if record else (None, None)
+        if record:
+            a.record()
+        w.grouped_gemm(self.q1, self.s1, self.gl, self.w13p, self.w13s, 2 * m.I, y=self.h)
+        if record:
+            b.record()
+            evs.append((a, b, "w13"))
+        w.swiglu_quant(self.h, self.q2, self.s2)
+        a, b = (_ev(torch), _ev(torch)) if record else (None, None)
+        if record:
+            a.record()
+        w.grouped_gemm(self.q2, self.s2, self.gl, self.w2p, self.w2s, m.H, y=self.y)
+        if record:
+            b.record()
+            evs.append((a, b, "w2"))
+        return evs
+
+    def nonempty(self):
+        return int((self.m.group_list > 0).sum())
+
+    def gemm_bytes(self, which):
+        m = self.m
+        ne = self.nonempty()
+        R, H, I = m.R, m.H, m.I
+        if which == "w13":
+            return ne * (2 * I * H + 4 * 2 * I) + R * H + 4 * R + 2 * R * 2 * I + 8 * m.E
+        return ne * (H * I + 4 * H) + R * I + 4 * R + 2 * R * H + 8 * m.E
+
+    def value(self, sec_per_step):
+        return self.m.T / sec_per_step
+
+    def dominant(self, per_key_ms):
+        byts = self.gemm_bytes("w13") + self.gemm_bytes("w2")
+        tot = per_key_ms["w13"] + per_key_ms["w2"]
+        ach = byts / (tot * 1e-3) / 1e9
+        return dict(bound="hbm", achieved=ach, peak=PEAK_HBM_GBS, unit="GB/s",
+                    frac=ach / PEAK_HBM_GBS)
+
+    def config(self):
+        m = self.m
+        g = m.group_list
+        return {"workload": "moe", "T": m.T, "top_k": m.top_k, "E": m.E, "H": m.H, "I": m.I,
+                "R": m.R, "nonempty_experts": self.nonempty(), "max_rows_per_expert": int(g.max()),
+                "experts_le4_rows": int(((g > 0) & (g <= 4)).sum()),
+                "routing": "logits N(0,1) + expert bias N(0,1.5), top-8"}
+
+    def cpu_baseline(self, budget_s):
+        import numpy as np
+
+        import oracle as O
+        m = self.m
+        off = O.group_offsets(m.group_list)
+        xr = m.x_rows()
+        t0 = time.perf_counter()
+        rows = 0
+        e = 0
+        while time.perf_counter() - t0 < budget_s and e < m.E:
+            a, b = int(off[e]), int(off[e + 1])
+            if b > a:
+                g1 = np.array([b - a], np.int64)
+                O.moe_grouped(g1, m.w13(e)[None], m.w13_scale[e][None], m.w2(e)[None],
+                              m.w2_scale[e][None], x_bits=xr[a:b])
+                m.drop_cache()
+                rows += b - a
+            e += 1
+        dt = time.perf_counter() - t0
+        return dict(value=rows / m.top_k / dt, unit="tokens/s",
+                    sample=f"oracle MoE chain over experts 0..{e - 1} ({rows} of {m.R} rows, "
+                           f"weights drawn per expert inside the timing), tokens = rows / top_k")
+
+
+# ---------------------------------------------------------------------------
+
+def _blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        n = [i.get("num_threads", 0) for i in threadpool_info() if i.get("user_api") == "blas"]
+        return max(n) if n else 1
+    except Exception:
+        return os.cpu_count() or 1
+
+
+def main():
+    args = _args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU only; --gpus must be 1 "
+                                   "(the multi-GPU sharding is described, not built)"}))
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(3)
+    torch.cuda.set_device(0)
+    import moe_token_amax_amd as w
+
+    if args.workload == "decode":
+        wl = DenseWorkload(w, torch, "decode", [1, 4, 16, 64], 7168, 4096, False, 0.005, 16)
+    elif args.workload == "prefill":
+        wl = DenseWorkload(w, torch, "prefill", [8192], 7168, 4096, True, 0.005, 2)
+    elif args.workload == "tiny":
+        wl = DenseWorkload(w, torch, "tiny", [16], 256, 128, True, 0.01, 1)
+    else:
+        wl = MoeWorkload(w, torch)
+
+    for i in range(args.warmup):
+        wl.step(i)
+    torch.cuda.synchronize()
+    # Timed region. Before phase p is replayed again, the events of its previous
+    # replay (several steps back) are read; waiting on them leaves the newer
+    # replays queued, so the GPU never idles on the host.
+    nph = len(wl.phases)
+    pending = [False] * nph
+    per_key, counts = {}, {}
+
+    def collect(p):
+        for a, b, k in wl.phases[p][1]:
+            b.synchronize()
+            per_key[k] = per_key.get(k, 0.0) + a.elapsed_time(b)
+            counts[k] = counts.get(k, 0) + 1
+
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        p = (args.warmup + i) % nph
+        if pending[p]:
+            collect(p)
+        wl.phases[p][0].replay()
+        pending[p] = True
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    for p in range(nph):
+        if pending[p]:
+            collect(p)
+    sec = elapsed / args.steps
+    avg_ms = {k: per_key[k] / counts[k] for k in per_key}
+
+    roof = wl.dominant(avg_ms)
+    roof["traffic"] = None
+    roof["kernel_avg_us"] = {str(k): round(v * 1e3, 3) for k, v in avg_ms.items()}
+
+    out = {
+        "metric": wl.metric,
+        "value": round(wl.value(sec), 3),
+        "unit": wl.unit,
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(sec * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic (seeded numpy; see synth/)",
+        "config": wl.config(),
+        "roofline": {k: (round(v, 4) if isinstance(v, float) else v) for k, v in roof.items()},
+    }
+    if not args.no_cpu_baseline:
+        cb = wl.cpu_baseline(args.cpu_seconds)
+        cb.update(cores=_blas_threads(), kind="oracle", host=platform.processor() or platform.machine())
+        cb["value"] = round(cb["value"], 4)
+        out["cpu_baseline"] = cb
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,174 @@
+/*
+ * w8a8.h — C ABI of the MI355X (gfx950) W8A8_DYNAMIC hot path.
+ *
+ * W8A8_DYNAMIC linear: per-token symmetric INT8 activation quantization, an
+ * INT8 x INT8 -> INT32 matmul against offline per-channel INT8 weights, and a
+ * dequant epilogue (acc * x_scale[m] * w_scale[n] + bias[n] -> BF16). The MoE
+ * form runs the same matmul as a grouped GEMM driven by per-expert row counts:
+ * W13 -> SwiGLU -> per-token requant -> W2.
+ *
+ * Page tags used in the comments:
+ *   [DSV4]  "DeepSeek-V4 W8A8 执行链从量化权重到 Ascend INT8 算子"
+ *
+ * Conventions for every entry point:
+ *   - Pointers named as device buffers are HIP device pointers on the current
+ *     device. BF16 values travel as their uint16_t bit patterns.
+ *   - `stream` is a hipStream_t (NULL = the legacy default stream). Every call
+ *     only enqueues work on it and returns without synchronizing.
+ *   - The caller owns every buffer. The library never allocates or frees device
+ *     memory and keeps no pointer after a call returns.
+ *   - Arguments are checked on the host before anything is launched. A failed
+ *     check launches nothing and returns a non-zero w8a8_status;
+ *     w8a8_last_error() then returns a message for the calling thread.
+ *   - Device-side problems (e.g. a group_list whose counts do not sum to R)
+ *     are not detected; results are then undefined.
+ *   - Sizes are int64_t element counts. M == 0 or R == 0 is a valid no-op.
+ */
+#ifndef W8A8_H
+#define W8A8_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  W8A8_OK = 0,
+  W8A8_ERR_NULL = 1,        /* a required pointer is NULL */
+  W8A8_ERR_SHAPE = 2,       /* a size is negative, zero where not allowed, or too large */
+  W8A8_ERR_ALIGN = 3,       /* a buffer is not aligned as documented */
+  W8A8_ERR_UNSUPPORTED = 4, /* a valid request this library does not implement */
+  W8A8_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required */
+  W8A8_ERR_LAUNCH = 6       /* a HIP launch failed (message from hipGetLastError) */
+} w8a8_status;
+
+typedef enum {
+  W8A8_OUT_BF16 = 0,  /* epilogue output: BF16 bits, uint16_t */
+  W8A8_OUT_I32 = 1    /* raw INT32 accumulator (no epilogue), int32_t */
+} w8a8_out;
+
+/* Largest K (reduction length) accepted: K * 127 * 127 stays below 2^31. */
+#define W8A8_MAX_K 133144
+
+const char* w8a8_status_str(int status);
+/* Message of the last failed call on this thread ("" if none). */
+const char* w8a8_last_error(void);
+/* ABI version, bumped on any signature change. */
+int w8a8_abi_version(void);
+
+/*
+ * Per-token symmetric INT8 quantization.  [DSV4 §一 recipe "act: per_token,
+ * int8, symmetric"; §二 npu_dynamic_quant]
+ *   x       device, BF16 [M, K] row-major (row stride K)
+ *   q       device, int8 [M, K] row-major (row stride K), written
+ *   x_scale device, float [M], written
+ * For each row: amax = max_k |x[m,k]|; x_scale[m] = amax / 127 (one IEEE fp32
+ * division); q[m,k] = round-half-even(x[m,k] / x_scale[m]) (one IEEE fp32
+ * division) clamped to [-127, 127]. A row with amax == 0 gets scale 0 and
+ * all-zero codes. K >= 1.
+ */
+int w8a8_dynamic_quant(const uint16_t* x, int64_t M, int64_t K, int8_t* q,
+                       float* x_scale, void* stream);
+
+/*
+ * Load-time weight prepack.  [DSV4 §二: the INT8 [N, K] weight is transposed
+ * and format-cast once at load and reused by every forward]
+ * Packed layout ("P16x64"): K is zero-padded to Kp = ceil(K/64)*64 and N to
+ * Np = ceil(N/16)*16. The packed buffer is a sequence of 1024-byte blocks
+ * ordered [e][n/16][k/64]; inside a block byte (l*16 + j), l in [0,64),
+ * j in [0,16), holds w[e][16*(n/16) + l%16][64*(k/64) + 16*(l/16) + j] — the
+ * operand order of one 16x16x64 INT8 MFMA.
+ *   w        device, int8 [E, N, K] row-major
+ *   w_packed device, w8a8_packed_weight_bytes(E, N, K) bytes, 16-byte aligned
+ * The packed buffer can be rewritten in place by a later call (stable address).
+ */
+int64_t w8a8_packed_weight_bytes(int64_t E, int64_t N, int64_t K);
+int w8a8_prepack_weight(const int8_t* w, int64_t E, int64_t N, int64_t K,
+                        void* w_packed, void* stream);
+
+/*
+ * Dense W8A8 quant matmul with the fused dequant epilogue.  [DSV4 §二:
+ * npu_quant_matmul(q, weight, weight_scale, pertoken_scale, bias,
+ * output_dtype=BF16)]
+ *   q        device, int8 [M, K] row-major (from w8a8_dynamic_quant)
+ *   x_scale  device, float [M]
+ *   w_packed device, packed weight of one [N, K] matrix (E = 1)
+ *   w_scale  device, float [N]
+ *   bias     device, BF16 [N] or NULL
+ *   y        device, [M, N] row-major; BF16 bits when out == W8A8_OUT_BF16,
+ *            int32 raw accumulators when out == W8A8_OUT_I32
+ *   workspace/ws_bytes: device scratch of at least
+ *            w8a8_linear_workspace_bytes(M, N, K) bytes (may be 0 → NULL ok)
+ * y[m,n] = BF16(((float(acc[m,n]) * x_scale[m]) * w_scale[n]) + bias[n]),
+ * each step one fp32 rounding (round to nearest even), acc exact in INT32.
+ * 1 <= K <= W8A8_MAX_K.
+ */
+int64_t w8a8_linear_workspace_bytes(int64_t M, int64_t N, int64_t K);
+int w8a8_linear(const int8_t* q, const float* x_scale, int64_t M, int64_t K,
+                const void* w_packed, const float* w_scale, int64_t N,
+                const uint16_t* bias, void* y, int out, void* workspace,
+                int64_t ws_bytes, void* stream);
+
+/*
+ * Grouped INT8 matmul over experts.  [DSV4 §三: npu_grouped_matmul(x, weight,
+ * scale, per_token_scale, group_list=expert_tokens); group_list gives the
+ * number of rows of every expert]
+ *   a          device, int8 [R, K] row-major; rows grouped by expert in
+ *              expert order (expert e owns rows [off_e, off_e + n_e) where
+ *              off_e = n_0 + ... + n_{e-1})
+ *   a_scale    device, float [R]
+ *   group_list device, int64 [E] row counts n_e >= 0 with sum R (read on the
+ *              device only; never copied to the host)
+ *   w_packed   device, packed [E, N, K] weight
+ *   w_scale    device, float [E, N]
+ *   y          device, [R, N]; BF16 bits or int32 as for w8a8_linear
+ * Experts with n_e == 0 cost no work. No bias.
+ */
+int64_t w8a8_grouped_workspace_bytes(int64_t R, int64_t E, int64_t N, int64_t K);
+int w8a8_grouped_gemm(const int8_t* a, const float* a_scale,
+                      const int64_t* group_list, int64_t R, int64_t E,
+                      int64_t N, int64_t K, const void* w_packed,
+                      const float* w_scale, void* y, int out, void* workspace,
+                      int64_t ws_bytes, void* stream);
+
+/*
+ * Fused SwiGLU + per-token requant.  [DSV4 §三 and §五: "SwiGLU + Requant"
+ * produces a new INT8 payload and a new per-token scale between W13 and W2;
+ * §一: W13 is gate_proj + up_proj]
+ *   h     device, BF16 [R, 2I]; columns [0, I) gate, [I, 2I) up
+ *   q     device, int8 [R, I], written
+ *   scale device, float [R], written
+ * a[r,j] = silu(gate) * up evaluated in fp32 (exp by a fixed Cody-Waite +
+ * degree-7 Taylor sequence, each step one fp32 rounding); then the
+ * w8a8_dynamic_quant rule on a (no BF16 rounding of a). I >= 1.
+ */
+int w8a8_swiglu_quant(const uint16_t* h, int64_t R, int64_t I, int8_t* q,
+                      float* scale, void* stream);
+
+/*
+ * MoE expert chain.  [DSV4 §三: routed hidden -> W13 grouped matmul -> SwiGLU
+ * -> requant -> W2 grouped matmul -> BF16; the hidden states are quantized
+ * only when they arrive without a per-token scale]
+ *   x_rows     device; if x_scale == NULL: BF16 [R, H], quantized inside;
+ *              else int8 [R, H] with its per-token scale x_scale [R]
+ *   group_list device, int64 [E], as for w8a8_grouped_gemm
+ *   w13_packed packed [E, 2I, H]; w13_scale float [E, 2I]
+ *   w2_packed  packed [E, H, I];  w2_scale  float [E, H]
+ *   y          device, BF16 [R, H] (rows in the same expert-grouped order,
+ *              not combined across top-k)
+ *   workspace  at least w8a8_moe_workspace_bytes(R, E, H, I) bytes
+ */
+int64_t w8a8_moe_workspace_bytes(int64_t R, int64_t E, int64_t H, int64_t I);
+int w8a8_moe_grouped(const void* x_rows, const float* x_scale,
+                     const int64_t* group_list, int64_t R, int64_t E, int64_t H,
+                     int64_t I, const void* w13_packed, const float* w13_scale,
+                     const void* w2_packed, const float* w2_scale, uint16_t* y,
+                     void* workspace, int64_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W8A8_H */

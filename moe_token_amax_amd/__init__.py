@@ -1,0 +1,271 @@
+"""Python binding of libw8a8.so, the gfx950 W8A8_DYNAMIC library.
+
+Argument marshalling only: every function checks dtype, device and layout of the
+torch tensors it is given, passes their device pointers and the current HIP
+stream to the C ABI (include/w8a8.h), and raises ``RuntimeError`` with the
+library's message on a non-zero status. Every step of the path runs in the HIP
+kernels; there is no CPU or PyTorch fallback. Importing this package fails when
+the built library is missing.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "LIB_PATH",
+    "lib",
+    "W8A8Error",
+    "OUT_BF16",
+    "OUT_I32",
+    "dynamic_quant",
+    "packed_weight_bytes",
+    "prepack_weight",
+    "linear_workspace_bytes",
+    "linear",
+    "grouped_gemm",
+    "swiglu_quant",
+    "moe_workspace_bytes",
+    "moe_grouped",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libw8a8.so")
+
+OUT_BF16 = 0
+OUT_I32 = 1
+
+_c_i64 = ctypes.c_int64
+_c_p = ctypes.c_void_p
+
+
+class W8A8Error(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"w8a8 status {status}: {msg}")
+        self.status = status
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is not built; run `python -c 'import __graft_entry__ as g; g.build()'` "
+            "or `python moe_token_amax_amd/_build.py` first")
+    L = ctypes.CDLL(LIB_PATH)
+    sig = {
+        "w8a8_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+        "w8a8_last_error": (ctypes.c_char_p, []),
+        "w8a8_abi_version": (ctypes.c_int, []),
+        "w8a8_dynamic_quant": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p]),
+        "w8a8_packed_weight_bytes": (_c_i64, [_c_i64, _c_i64, _c_i64]),
+        "w8a8_prepack_weight": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p]),
+        "w8a8_linear_workspace_bytes": (_c_i64, [_c_i64, _c_i64, _c_i64]),
+        "w8a8_linear": (ctypes.c_int, [_c_p, _c_p, _c_i64, _c_i64, _c_p, _c_p, _c_i64, _c_p, _c_p,
+                                       ctypes.c_int, _c_p, _c_i64, _c_p]),
+        "w8a8_grouped_workspace_bytes": (_c_i64, [_c_i64, _c_i64, _c_i64, _c_i64]),
+        "w8a8_grouped_gemm": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i64,
+                                             _c_p, _c_p, _c_p, ctypes.c_int, _c_p, _c_i64, _c_p]),
+        "w8a8_swiglu_quant": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p]),
+        "w8a8_moe_workspace_bytes": (_c_i64, [_c_i64, _c_i64, _c_i64, _c_i64]),
+        "w8a8_moe_grouped": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i64,
+                                            _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_p]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(L, name)
+        f.restype = res
+        f.argtypes = args
+    return L
+
+
+lib = _load()
+
+
+def _check(status: int):
+    if status != 0:
+        raise W8A8Error(status, lib.w8a8_last_error().decode())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t: torch.Tensor, dtype, name: str, ndim: int | None = None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a GPU device")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {t.dim()}")
+
+
+def dynamic_quant(x: torch.Tensor, q: torch.Tensor | None = None,
+                  scale: torch.Tensor | None = None):
+    """BF16 [M, K] -> (int8 [M, K], float32 [M])."""
+    _need(x, torch.bfloat16, "x", 2)
+    M, K = x.shape
+    if q is None:
+        q = torch.empty((M, K), dtype=torch.int8, device=x.device)
+    if scale is None:
+        scale = torch.empty((M,), dtype=torch.float32, device=x.device)
+    _need(q, torch.int8, "q", 2)
+    _need(scale, torch.float32, "scale", 1)
+    if tuple(q.shape) != (M, K) or scale.shape[0] != M:
+        raise ValueError("q / scale shape mismatch")
+    _check(lib.w8a8_dynamic_quant(_ptr(x), M, K, _ptr(q), _ptr(scale), _stream()))
+    return q, scale
+
+
+def packed_weight_bytes(E: int, N: int, K: int) -> int:
+    return int(lib.w8a8_packed_weight_bytes(E, N, K))
+
+
+def prepack_weight(w: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """int8 [N, K] or [E, N, K] -> packed uint8 buffer (stable, caller-owned)."""
+    _need(w, torch.int8, "w")
+    if w.dim() == 2:
+        E, (N, K) = 1, w.shape
+    elif w.dim() == 3:
+        E, N, K = w.shape
+    else:
+        raise ValueError("w must be [N, K] or [E, N, K]")
+    nbytes = packed_weight_bytes(E, N, K)
+    if out is None:
+        out = torch.empty((nbytes,), dtype=torch.uint8, device=w.device)
+    _need(out, torch.uint8, "out", 1)
+    if out.numel() < nbytes:
+        raise ValueError(f"out needs {nbytes} bytes")
+    _check(lib.w8a8_prepack_weight(_ptr(w), E, N, K, _ptr(out), _stream()))
+    return out
+
+
+def linear_workspace_bytes(M: int, N: int, K: int) -> int:
+    return int(lib.w8a8_linear_workspace_bytes(M, N, K))
+
+
+def _workspace(nbytes: int, device, ws: torch.Tensor | None):
+    if nbytes <= 0:
+        return ws, 0
+    if ws is None:
+        ws = torch.empty((nbytes,), dtype=torch.uint8, device=device)
+    _need(ws, torch.uint8, "workspace", 1)
+    return ws, ws.numel()
+
+
+def linear(q: torch.Tensor, x_scale: torch.Tensor, w_packed: torch.Tensor, w_scale: torch.Tensor,
+           N: int, bias: torch.Tensor | None = None, out: int = OUT_BF16,
+           y: torch.Tensor | None = None, workspace: torch.Tensor | None = None):
+    """INT8 [M, K] x packed W [N, K] -> BF16 [M, N] (or int32 with out=OUT_I32)."""
+    _need(q, torch.int8, "q", 2)
+    _need(x_scale, torch.float32, "x_scale", 1)
+    _need(w_packed, torch.uint8, "w_packed", 1)
+    _need(w_scale, torch.float32, "w_scale", 1)
+    M, K = q.shape
+    if x_scale.shape[0] != M or w_scale.shape[0] != N:
+        raise ValueError("scale shape mismatch")
+    if w_packed.numel() < packed_weight_bytes(1, N, K):
+        raise ValueError("w_packed too small for [N, K]")
+    if bias is not None:
+        _need(bias, torch.bfloat16, "bias", 1)
+        if bias.shape[0] != N:
+            raise ValueError("bias shape mismatch")
+    ydt = torch.bfloat16 if out == OUT_BF16 else torch.int32
+    if y is None:
+        y = torch.empty((M, N), dtype=ydt, device=q.device)
+    _need(y, ydt, "y", 2)
+    ws, ws_n = _workspace(linear_workspace_bytes(M, N, K), q.device, workspace)
+    _check(lib.w8a8_linear(_ptr(q), _ptr(x_scale), M, K, _ptr(w_packed), _ptr(w_scale), N,
+                           _ptr(bias), _ptr(y), out, _ptr(ws), ws_n, _stream()))
+    return y
+
+
+def grouped_gemm(a: torch.Tensor, a_scale: torch.Tensor, group_list: torch.Tensor,
+                 w_packed: torch.Tensor, w_scale: torch.Tensor, N: int, out: int = OUT_BF16,
+                 y: torch.Tensor | None = None, workspace: torch.Tensor | None = None):
+    """INT8 rows [R, K] grouped by expert x packed W [E, N, K] -> [R, N]."""
+    _need(a, torch.int8, "a", 2)
+    _need(a_scale, torch.float32, "a_scale", 1)
+    _need(group_list, torch.int64, "group_list", 1)
+    _need(w_packed, torch.uint8, "w_packed", 1)
+    _need(w_scale, torch.float32, "w_scale", 2)
+    R, K = a.shape
+    E = group_list.shape[0]
+    if tuple(w_scale.shape) != (E, N) or a_scale.shape[0] != R:
+        raise ValueError("scale shape mismatch")
+    if w_packed.numel() < packed_weight_bytes(E, N, K):
+        raise ValueError("w_packed too small for [E, N, K]")
+    ydt = torch.bfloat16 if out == OUT_BF16 else torch.int32
+    if y is None:
+        y = torch.empty((R, N), dtype=ydt, device=a.device)
+    _need(y, ydt, "y", 2)
+    ws, ws_n = _workspace(int(lib.w8a8_grouped_workspace_bytes(R, E, N, K)), a.device, workspace)
+    _check(lib.w8a8_grouped_gemm(_ptr(a), _ptr(a_scale), _ptr(group_list), R, E, N, K,
+                                 _ptr(w_packed), _ptr(w_scale), _ptr(y), out, _ptr(ws), ws_n,
+                                 _stream()))
+    return y
+
+
+def swiglu_quant(h: torch.Tensor, q: torch.Tensor | None = None,
+                 scale: torch.Tensor | None = None):
+    """BF16 h [R, 2I] (gate | up) -> (int8 [R, I], float32 [R])."""
+    _need(h, torch.bfloat16, "h", 2)
+    R, I2 = h.shape
+    if I2 % 2:
+        raise ValueError("h must have an even number of columns (gate | up)")
+    I = I2 // 2
+    if q is None:
+        q = torch.empty((R, I), dtype=torch.int8, device=h.device)
+    if scale is None:
+        scale = torch.empty((R,), dtype=torch.float32, device=h.device)
+    _need(q, torch.int8, "q", 2)
+    _need(scale, torch.float32, "scale", 1)
+    _check(lib.w8a8_swiglu_quant(_ptr(h), R, I, _ptr(q), _ptr(scale), _stream()))
+    return q, scale
+
+
+def moe_workspace_bytes(R: int, E: int, H: int, I: int) -> int:
+    return int(lib.w8a8_moe_workspace_bytes(R, E, H, I))
+
+
+def moe_grouped(x_rows: torch.Tensor, group_list: torch.Tensor, w13_packed: torch.Tensor,
+                w13_scale: torch.Tensor, w2_packed: torch.Tensor, w2_scale: torch.Tensor,
+                x_scale: torch.Tensor | None = None, y: torch.Tensor | None = None,
+                workspace: torch.Tensor | None = None):
+    """MoE expert chain on expert-grouped rows -> BF16 [R, H].
+
+    ``x_rows`` is BF16 [R, H] (quantized inside) or int8 [R, H] with ``x_scale``.
+    """
+    if x_scale is None:
+        _need(x_rows, torch.bfloat16, "x_rows", 2)
+    else:
+        _need(x_rows, torch.int8, "x_rows", 2)
+        _need(x_scale, torch.float32, "x_scale", 1)
+    _need(group_list, torch.int64, "group_list", 1)
+    _need(w13_scale, torch.float32, "w13_scale", 2)
+    _need(w2_scale, torch.float32, "w2_scale", 2)
+    _need(w13_packed, torch.uint8, "w13_packed", 1)
+    _need(w2_packed, torch.uint8, "w2_packed", 1)
+    R, H = x_rows.shape
+    E = group_list.shape[0]
+    I = w13_scale.shape[1] // 2
+    if tuple(w13_scale.shape) != (E, 2 * I) or tuple(w2_scale.shape) != (E, H):
+        raise ValueError("scale shape mismatch")
+    if w13_packed.numel() < packed_weight_bytes(E, 2 * I, H) or \
+            w2_packed.numel() < packed_weight_bytes(E, H, I):
+        raise ValueError("packed weights too small")
+    if y is None:
+        y = torch.empty((R, H), dtype=torch.bfloat16, device=x_rows.device)
+    _need(y, torch.bfloat16, "y", 2)
+    ws, ws_n = _workspace(moe_workspace_bytes(R, E, H, I), x_rows.device, workspace)
+    _check(lib.w8a8_moe_grouped(_ptr(x_rows), _ptr(x_scale), _ptr(group_list), R, E, H, I,
+                                _ptr(w13_packed), _ptr(w13_scale), _ptr(w2_packed),
+                                _ptr(w2_scale), _ptr(y), _ptr(ws), ws_n, _stream()))
+    return y

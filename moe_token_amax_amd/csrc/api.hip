@@ -1,0 +1,228 @@
+// C ABI of the W8A8_DYNAMIC library: argument checks, workspace sizing and the
+// MoE chain. Declarations and contracts are in include/w8a8.h.
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/w8a8.h"
+#include "launch.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+int ok() {
+  g_last_error.clear();
+  return W8A8_OK;
+}
+
+int launched(hipError_t err, const char* what) {
+  if (err != hipSuccess) return fail(W8A8_ERR_LAUNCH, "%s: %s", what, hipGetErrorString(err));
+  return ok();
+}
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+constexpr int64_t kMaxDim = (int64_t)1 << 31;  // rows / columns limit of the grids
+constexpr int64_t kMaxExperts = 1024;           // LDS tile table of the grouped kernel
+
+int64_t align256(int64_t b) { return (b + 255) & ~(int64_t)255; }
+
+struct MoeWs {
+  int64_t q1, s1, h, q2, s2, inner, total;
+};
+
+MoeWs moe_layout(int64_t R, int64_t E, int64_t H, int64_t I) {
+  MoeWs w{};
+  int64_t o = 0;
+  w.q1 = o; o += align256(R * H);                // int8 [R, H] (BF16 input only)
+  w.s1 = o; o += align256(R * 4);                // f32 [R]
+  w.h = o;  o += align256(R * 2 * I * 2);        // BF16 [R, 2I]
+  w.q2 = o; o += align256(R * I);                // int8 [R, I]
+  w.s2 = o; o += align256(R * 4);                // f32 [R]
+  w.inner = o;
+  o += align256(std::max(w8a8::grouped_ws_bytes(R, E, 2 * I, H), w8a8::grouped_ws_bytes(R, E, H, I)));
+  w.total = o;
+  return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* w8a8_status_str(int s) {
+  switch (s) {
+    case W8A8_OK: return "ok";
+    case W8A8_ERR_NULL: return "null pointer";
+    case W8A8_ERR_SHAPE: return "invalid shape";
+    case W8A8_ERR_ALIGN: return "misaligned buffer";
+    case W8A8_ERR_UNSUPPORTED: return "unsupported";
+    case W8A8_ERR_WORKSPACE: return "workspace too small";
+    case W8A8_ERR_LAUNCH: return "launch failed";
+    default: return "unknown status";
+  }
+}
+
+const char* w8a8_last_error(void) { return g_last_error.c_str(); }
+
+int w8a8_abi_version(void) { return 1; }
+
+int w8a8_dynamic_quant(const uint16_t* x, int64_t M, int64_t K, int8_t* q, float* x_scale,
+                       void* stream) {
+  if (M < 0 || K < 1 || M >= kMaxDim * 4 || K > W8A8_MAX_K)
+    return fail(W8A8_ERR_SHAPE, "dynamic_quant: need M >= 0 and 1 <= K <= %d (M=%lld K=%lld)",
+                W8A8_MAX_K, (long long)M, (long long)K);
+  if (M == 0) return ok();
+  if (!x || !q || !x_scale) return fail(W8A8_ERR_NULL, "dynamic_quant: null pointer");
+  if (!aligned(x, 2) || !aligned(x_scale, 4))
+    return fail(W8A8_ERR_ALIGN, "dynamic_quant: x must be 2-byte and x_scale 4-byte aligned");
+  return launched(w8a8::launch_dynamic_quant(x, M, K, q, x_scale, (hipStream_t)stream),
+                  "dynamic_quant");
+}
+
+int64_t w8a8_packed_weight_bytes(int64_t E, int64_t N, int64_t K) {
+  if (E < 0 || N < 0 || K < 0) return -1;
+  return E * w8a8::round_up(N, 16) * w8a8::round_up(K, 64);
+}
+
+int w8a8_prepack_weight(const int8_t* w, int64_t E, int64_t N, int64_t K, void* w_packed,
+                        void* stream) {
+  if (E < 1 || N < 1 || K < 1 || N >= kMaxDim || K > W8A8_MAX_K)
+    return fail(W8A8_ERR_SHAPE, "prepack_weight: need E, N >= 1 and 1 <= K <= %d", W8A8_MAX_K);
+  if (!w || !w_packed) return fail(W8A8_ERR_NULL, "prepack_weight: null pointer");
+  if (!aligned(w_packed, 16)) return fail(W8A8_ERR_ALIGN, "prepack_weight: w_packed not 16-byte aligned");
+  return launched(w8a8::launch_prepack(w, E, N, K, w_packed, (hipStream_t)stream), "prepack_weight");
+}
+
+int64_t w8a8_linear_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  if (M <= 0 || N <= 0 || K <= 0) return 0;
+  return w8a8::plan_dense(M, N, K).ws_bytes;
+}
+
+int w8a8_linear(const int8_t* q, const float* x_scale, int64_t M, int64_t K, const void* w_packed,
+                const float* w_scale, int64_t N, const uint16_t* bias, void* y, int out,
+                void* workspace, int64_t ws_bytes, void* stream) {
+  if (M < 0 || K < 1 || N < 1 || M >= kMaxDim || N >= kMaxDim || K > W8A8_MAX_K)
+    return fail(W8A8_ERR_SHAPE, "linear: need M >= 0, N >= 1, 1 <= K <= %d", W8A8_MAX_K);
+  if (out != W8A8_OUT_BF16 && out != W8A8_OUT_I32)
+    return fail(W8A8_ERR_UNSUPPORTED, "linear: unknown output kind %d", out);
+  if (M == 0) return ok();
+  if (!q || !x_scale || !w_packed || !w_scale || !y) return fail(W8A8_ERR_NULL, "linear: null pointer");
+  if (!aligned(w_packed, 16) || !aligned(x_scale, 4) || !aligned(w_scale, 4) || !aligned(y, 4) ||
+      (bias && !aligned(bias, 2)))
+    return fail(W8A8_ERR_ALIGN, "linear: w_packed needs 16-byte, scales and y 4-byte alignment");
+  const w8a8::DensePlan plan = w8a8::plan_dense(M, N, K);
+  if (plan.ws_bytes > 0 && (!workspace || ws_bytes < plan.ws_bytes || !aligned(workspace, 16)))
+    return fail(W8A8_ERR_WORKSPACE, "linear: needs %lld workspace bytes (16-byte aligned), got %lld",
+                (long long)plan.ws_bytes, (long long)ws_bytes);
+  return launched(w8a8::launch_dense_gemm(plan, q, x_scale, M, K, w_packed, w_scale, N, bias, y, out,
+                                          workspace, (hipStream_t)stream),
+                  "linear");
+}
+
+int64_t w8a8_grouped_workspace_bytes(int64_t R, int64_t E, int64_t N, int64_t K) {
+  return w8a8::grouped_ws_bytes(R, E, N, K);
+}
+
+static int check_grouped(const char* who, int64_t R, int64_t E, int64_t N, int64_t K) {
+  if (R < 0 || E < 1 || N < 1 || K < 1 || R >= kMaxDim || N >= kMaxDim || K > W8A8_MAX_K)
+    return fail(W8A8_ERR_SHAPE, "%s: need R >= 0, E >= 1, N >= 1, 1 <= K <= %d", who, W8A8_MAX_K);
+  if (E > kMaxExperts)
+    return fail(W8A8_ERR_UNSUPPORTED, "%s: at most %lld experts", who, (long long)kMaxExperts);
+  return W8A8_OK;
+}
+
+int w8a8_grouped_gemm(const int8_t* a, const float* a_scale, const int64_t* group_list, int64_t R,
+                      int64_t E, int64_t N, int64_t K, const void* w_packed, const float* w_scale,
+                      void* y, int out, void* workspace, int64_t ws_bytes, void* stream) {
+  int st = check_grouped("grouped_gemm", R, E, N, K);
+  if (st) return st;
+  if (out != W8A8_OUT_BF16 && out != W8A8_OUT_I32)
+    return fail(W8A8_ERR_UNSUPPORTED, "grouped_gemm: unknown output kind %d", out);
+  if (R == 0) return ok();
+  if (!a || !a_scale || !group_list || !w_packed || !w_scale || !y)
+    return fail(W8A8_ERR_NULL, "grouped_gemm: null pointer");
+  if (!aligned(w_packed, 16) || !aligned(a_scale, 4) || !aligned(w_scale, 4) || !aligned(y, 4) ||
+      !aligned(group_list, 8))
+    return fail(W8A8_ERR_ALIGN, "grouped_gemm: misaligned buffer");
+  const int64_t need = w8a8::grouped_ws_bytes(R, E, N, K);
+  if (need > 0 && (!workspace || ws_bytes < need))
+    return fail(W8A8_ERR_WORKSPACE, "grouped_gemm: needs %lld workspace bytes", (long long)need);
+  return launched(w8a8::launch_grouped_gemm(a, a_scale, group_list, R, E, N, K, w_packed, w_scale, y,
+                                            out, workspace, (hipStream_t)stream),
+                  "grouped_gemm");
+}
+
+int w8a8_swiglu_quant(const uint16_t* h, int64_t R, int64_t I, int8_t* q, float* scale,
+                      void* stream) {
+  if (R < 0 || I < 1 || R >= kMaxDim * 4 || I > W8A8_MAX_K)
+    return fail(W8A8_ERR_SHAPE, "swiglu_quant: need R >= 0 and 1 <= I <= %d", W8A8_MAX_K);
+  if (R == 0) return ok();
+  if (!h || !q || !scale) return fail(W8A8_ERR_NULL, "swiglu_quant: null pointer");
+  if (!aligned(h, 2) || !aligned(scale, 4)) return fail(W8A8_ERR_ALIGN, "swiglu_quant: misaligned buffer");
+  return launched(w8a8::launch_swiglu_quant(h, R, I, q, scale, (hipStream_t)stream), "swiglu_quant");
+}
+
+int64_t w8a8_moe_workspace_bytes(int64_t R, int64_t E, int64_t H, int64_t I) {
+  if (R <= 0 || E <= 0 || H <= 0 || I <= 0) return 0;
+  return moe_layout(R, E, H, I).total;
+}
+
+int w8a8_moe_grouped(const void* x_rows, const float* x_scale, const int64_t* group_list, int64_t R,
+                     int64_t E, int64_t H, int64_t I, const void* w13_packed,
+                     const float* w13_scale, const void* w2_packed, const float* w2_scale,
+                     uint16_t* y, void* workspace, int64_t ws_bytes, void* stream) {
+  int st = check_grouped("moe_grouped", R, E, 2 * I, H);
+  if (st) return st;
+  st = check_grouped("moe_grouped", R, E, H, I);
+  if (st) return st;
+  if (R == 0) return ok();
+  if (!x_rows || !group_list || !w13_packed || !w13_scale || !w2_packed || !w2_scale || !y)
+    return fail(W8A8_ERR_NULL, "moe_grouped: null pointer");
+  if (!aligned(w13_packed, 16) || !aligned(w2_packed, 16) || !aligned(group_list, 8) ||
+      !aligned(w13_scale, 4) || !aligned(w2_scale, 4) || !aligned(y, 4) ||
+      (x_scale && !aligned(x_scale, 4)) || !aligned(x_rows, 2))
+    return fail(W8A8_ERR_ALIGN, "moe_grouped: misaligned buffer");
+  const MoeWs L = moe_layout(R, E, H, I);
+  if (!workspace || ws_bytes < L.total || !aligned(workspace, 256))
+    return fail(W8A8_ERR_WORKSPACE, "moe_grouped: needs %lld workspace bytes (256-byte aligned), got %lld",
+                (long long)L.total, (long long)ws_bytes);
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = reinterpret_cast<char*>(workspace);
+  const int8_t* q1 = reinterpret_cast<const int8_t*>(x_rows);
+  const float* s1 = x_scale;
+  hipError_t err;
+  if (!x_scale) {
+    // rows arrived as BF16 without a per-token scale: quantize them first
+    err = w8a8::launch_dynamic_quant(reinterpret_cast<const uint16_t*>(x_rows), R, H,
+                                     reinterpret_cast<int8_t*>(ws + L.q1),
+                                     reinterpret_cast<float*>(ws + L.s1), s);
+    if (err != hipSuccess) return launched(err, "moe_grouped: dynamic_quant");
+    q1 = reinterpret_cast<const int8_t*>(ws + L.q1);
+    s1 = reinterpret_cast<const float*>(ws + L.s1);
+  }
+  uint16_t* h = reinterpret_cast<uint16_t*>(ws + L.h);
+  int8_t* q2 = reinterpret_cast<int8_t*>(ws + L.q2);
+  float* s2 = reinterpret_cast<float*>(ws + L.s2);
+  err = w8a8::launch_grouped_gemm(q1, s1, group_list, R, E, 2 * I, H, w13_packed, w13_scale, h,
+                                  w8a8::kOutBf16, ws + L.inner, s);
+  if (err != hipSuccess) return launched(err, "moe_grouped: W13");
+  err = w8a8::launch_swiglu_quant(h, R, I, q2, s2, s);
+  if (err != hipSuccess) return launched(err, "moe_grouped: swiglu_quant");
+  err = w8a8::launch_grouped_gemm(q2, s2, group_list, R, E, H, I, w2_packed, w2_scale, y,
+                                  w8a8::kOutBf16, ws + L.inner, s);
+  return launched(err, "moe_grouped: W2");
+}
+
+}  // extern "C"

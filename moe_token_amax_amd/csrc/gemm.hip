@@ -1,0 +1,451 @@
+// INT8 x INT8 -> INT32 GEMM kernels for gfx950 with the fused dequant epilogue.
+//
+// ("DeepSeek-V4 W8A8 执行链从量化权重到 Ascend INT8 算子": §二 npu_quant_matmul
+// with a per-token and a per-channel scale, optional bias, BF16 output;
+// §三 npu_grouped_matmul driven by group_list; §四 the kernel variant depends
+// on M, so prefill-sized and decode-sized calls take different tilings.)
+//
+// Data path of one workgroup tile (BM x BN, K in stages of BKB*64):
+//   * A (activations, int8 row-major) and B (weights prepacked in 1 KB blocks
+//     of 16 columns x 64 k, already in MFMA operand order) are copied
+//     global -> VGPR -> LDS by whole 1 KB blocks: one wavefront instruction
+//     moves one block, lane l carrying bytes [16l, 16l+16). For A the lane
+//     reads row l%16, k-chunk l/16 of the block, so LDS receives A in the same
+//     MFMA operand order as B and every LDS write and read is a linear 16 B per
+//     lane (no bank conflicts).
+//   * Two LDS stages: the global loads of stage s+1 are in flight while the
+//     MFMAs of stage s run.
+//   * Each wavefront owns a (BM/WM) x (BN/WN) sub-tile of 16x16 INT32
+//     accumulators and issues v_mfma_i32_16x16x64_i8.
+//   * Epilogue in registers: y = BF16(((float(acc) * xs[m]) * ws[n]) + b[n]),
+//     or raw INT32, or (split-K) INT32 partial sums that a fixup kernel adds
+//     exactly and then runs through the same epilogue.
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace w8a8 {
+
+constexpr int kBlockBytes = 1024;  // 16 rows/cols x 64 k of int8
+
+struct GemmArgs {
+  const int8_t* a;          // [rows, K] row-major
+  const float* a_scale;     // [rows]
+  int64_t M;                // rows (dense) / R (grouped)
+  int64_t K;
+  int KB;                   // packed k-blocks: ceil(K / 64)
+  const uint8_t* w;         // packed weight
+  int NB;                   // packed n-blocks per expert: ceil(N / 16)
+  const float* w_scale;     // [E, N]
+  int64_t N;
+  const uint16_t* bias;     // [N] or null
+  void* y;                  // [rows, N]
+  int out;                  // OutKind
+  int32_t* partial;         // split-K partial sums [split, M, N] (dense only)
+  int split;                // number of K slices
+  int kb_per_split;         // k-blocks per slice
+  bool a_vec;               // K % 16 == 0 and a 16-byte aligned
+  const int64_t* group_list;  // grouped only
+  int E;
+};
+
+// 16 bytes of A: row `row`, columns [kcol, kcol + 16). Rows outside
+// [.., row_end) and columns at or past K read as zero.
+__device__ __forceinline__ i32x4 load_a16(const GemmArgs& p, int64_t row, int64_t row_end,
+                                          int64_t kcol) {
+  i32x4 v = {0, 0, 0, 0};
+  if (row >= row_end || kcol >= p.K) return v;
+  const int8_t* src = p.a + row * p.K + kcol;
+  if (p.a_vec) return *reinterpret_cast<const i32x4*>(src);
+  uint32_t w[4] = {0, 0, 0, 0};
+  const int64_t n = min((int64_t)16, p.K - kcol);
+  for (int j = 0; j < n; ++j) w[j >> 2] |= (uint32_t)(uint8_t)src[j] << (8 * (j & 3));
+  v[0] = (int)w[0];
+  v[1] = (int)w[1];
+  v[2] = (int)w[2];
+  v[3] = (int)w[3];
+  return v;
+}
+
+template <int BM, int BN, int WM, int WN, int BKB>
+struct Tile {
+  static constexpr int kThreads = WM * WN * kWave;
+  static constexpr int kWaves = WM * WN;
+  static constexpr int TM = BM / WM / 16;
+  static constexpr int TN = BN / WN / 16;
+  static constexpr int kABlocks = (BM / 16) * BKB;
+  static constexpr int kBBlocks = (BN / 16) * BKB;
+  static constexpr int kBlocks = kABlocks + kBBlocks;
+  static constexpr int kPerWave = (kBlocks + kWaves - 1) / kWaves;
+  static constexpr int kStageBytes = kBlocks * kBlockBytes;
+  static_assert(BM % (16 * WM) == 0 && BN % (16 * WN) == 0, "tile shape");
+  static_assert(kBlocks % kWaves == 0, "blocks must split evenly over waves");
+
+  // Copies the blocks of one K stage owned by this wave into registers.
+  __device__ __forceinline__ static void load_stage(const GemmArgs& p, i32x4 (&r)[kPerWave],
+                                                    int wave, int lane, int64_t row0,
+                                                    int64_t row_end, int64_t wblk0, int nb0,
+                                                    int kb_stage, int kb_end) {
+#pragma unroll
+    for (int i = 0; i < kPerWave; ++i) {
+      const int bi = wave + i * kWaves;
+      i32x4 v = {0, 0, 0, 0};
+      if (bi < kABlocks) {
+        const int mb = bi / BKB, kbl = bi % BKB;
+        const int kb = kb_stage + kbl;
+        if (kb < kb_end)
+          v = load_a16(p, row0 + mb * 16 + (lane & 15), row_end,
+                       (int64_t)kb * 64 + (lane >> 4) * 16);
+      } else {
+        const int bj = bi - kABlocks;
+        const int nb = bj / BKB, kbl = bj % BKB;
+        const int kb = kb_stage + kbl;
+        if (kb < kb_end && nb0 + nb < p.NB)
+          v = *reinterpret_cast<const i32x4*>(p.w + (wblk0 + (int64_t)(nb0 + nb) * p.KB + kb) *
+                                                        kBlockBytes + lane * 16);
+      }
+      r[i] = v;
+    }
+  }
+
+  __device__ __forceinline__ static void store_stage(uint8_t* stage, const i32x4 (&r)[kPerWave],
+                                                     int wave, int lane) {
+#pragma unroll
+    for (int i = 0; i < kPerWave; ++i) {
+      const int bi = wave + i * kWaves;
+      *reinterpret_cast<i32x4*>(stage + bi * kBlockBytes + lane * 16) = r[i];
+    }
+  }
+
+  __device__ __forceinline__ static void compute_stage(const uint8_t* stage,
+                                                       i32x4 (&acc)[TM][TN], int wm, int wn,
+                                                       int lane) {
+#pragma unroll
+    for (int kbl = 0; kbl < BKB; ++kbl) {
+      i32x4 af[TM], bf[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+        af[i] = *reinterpret_cast<const i32x4*>(stage + ((wm * TM + i) * BKB + kbl) * kBlockBytes +
+                                                lane * 16);
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        bf[j] = *reinterpret_cast<const i32x4*>(
+            stage + (kABlocks + (wn * TN + j) * BKB + kbl) * kBlockBytes + lane * 16);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = mfma16x16x64(af[i], bf[j], acc[i][j]);
+    }
+  }
+
+  // Full K loop of one tile: rows [row0, row_end) of A (row0 is the tile's
+  // first row), weight blocks of expert `e` starting at n-block nb0,
+  // k-blocks [kb_begin, kb_end).
+  __device__ __forceinline__ static void mainloop(const GemmArgs& p, uint8_t* smem,
+                                                  i32x4 (&acc)[TM][TN], int64_t row0,
+                                                  int64_t row_end, int e, int nb0, int kb_begin,
+                                                  int kb_end) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int wm = wave / WN, wn = wave % WN;
+    const int64_t wblk0 = (int64_t)e * p.NB * p.KB;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) acc[i][j] = i32x4{0, 0, 0, 0};
+    const int nst = (kb_end - kb_begin + BKB - 1) / BKB;
+    if (nst <= 0) return;
+    i32x4 r[kPerWave];
+    load_stage(p, r, wave, lane, row0, row_end, wblk0, nb0, kb_begin, kb_end);
+    store_stage(smem, r, wave, lane);
+    __syncthreads();
+    for (int s = 0; s < nst; ++s) {
+      uint8_t* cur = smem + (s & 1) * kStageBytes;
+      uint8_t* nxt = smem + ((s + 1) & 1) * kStageBytes;
+      const bool more = s + 1 < nst;
+      if (more)
+        load_stage(p, r, wave, lane, row0, row_end, wblk0, nb0, kb_begin + (s + 1) * BKB, kb_end);
+      compute_stage(cur, acc, wm, wn, lane);
+      if (more) store_stage(nxt, r, wave, lane);
+      __syncthreads();
+    }
+  }
+
+  // Writes the tile. Local row i of the tile is global row row0 + i; rows at or
+  // past row_end and columns at or past N are skipped. `e` selects the w_scale
+  // row. With a split slice z > 0 or split > 1 the raw sums go to `partial`.
+  __device__ __forceinline__ static void epilogue(const GemmArgs& p, const i32x4 (&acc)[TM][TN],
+                                                  int64_t row0, int64_t row_end, int e, int64_t n0,
+                                                  int z) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int wm = wave / WN, wn = wave % WN;
+    const float* wsc = p.w_scale + (int64_t)e * p.N;
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int64_t n = n0 + (wn * TN + j) * 16 + (lane & 15);
+      if (n >= p.N) continue;
+      const float ws = wsc[n];
+      const float b = p.bias ? bf16_to_f32(p.bias[n]) : 0.0f;
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int64_t m = row0 + (wm * TM + i) * 16 + (lane >> 4) * 4 + t;
+          if (m >= row_end) continue;
+          const int32_t v = acc[i][j][t];
+          if (p.split > 1) {
+            p.partial[((int64_t)z * p.M + m) * p.N + n] = v;
+          } else if (p.out == kOutI32) {
+            reinterpret_cast<int32_t*>(p.y)[m * p.N + n] = v;
+          } else {
+            float f = (float)v;
+            f = f * p.a_scale[m];
+            f = f * ws;
+            if (p.bias) f = f + b;
+            reinterpret_cast<uint16_t*>(p.y)[m * p.N + n] = (uint16_t)f32_to_bf16(f);
+          }
+        }
+      }
+    }
+  }
+};
+
+// ---------------------------------------------------------------------------
+// dense kernel: grid.x = tiles (n fastest), grid.y = split slice
+// ---------------------------------------------------------------------------
+template <int BM, int BN, int WM, int WN, int BKB>
+__global__ __launch_bounds__(WM* WN* kWave) void dense_gemm_kernel(GemmArgs p) {
+  using T = Tile<BM, BN, WM, WN, BKB>;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * T::kStageBytes];
+  const int64_t nt = (p.N + BN - 1) / BN;
+  const int64_t tm = blockIdx.x / nt, tn = blockIdx.x % nt;
+  const int z = blockIdx.y;
+  const int64_t row0 = tm * BM;
+  const int kb_begin = z * p.kb_per_split;
+  const int kb_end = min(p.KB, kb_begin + p.kb_per_split);
+  i32x4 acc[T::TM][T::TN];
+  T::mainloop(p, smem, acc, row0, p.M, 0, (int)(tn * BN / 16), kb_begin, kb_end);
+  T::epilogue(p, acc, row0, p.M, 0, tn * BN, z);
+}
+
+// Sums the split-K partials exactly (INT32) and applies the epilogue.
+__global__ __launch_bounds__(256) void splitk_fixup_kernel(GemmArgs p) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= p.M * p.N) return;
+  const int64_t m = idx / p.N, n = idx % p.N;
+  int32_t s = 0;
+  for (int z = 0; z < p.split; ++z) s += p.partial[(int64_t)z * p.M * p.N + idx];
+  if (p.out == kOutI32) {
+    reinterpret_cast<int32_t*>(p.y)[idx] = s;
+    return;
+  }
+  float f = (float)s;
+  f = f * p.a_scale[m];
+  f = f * p.w_scale[n];
+  if (p.bias) f = f + bf16_to_f32(p.bias[n]);
+  reinterpret_cast<uint16_t*>(p.y)[idx] = (uint16_t)f32_to_bf16(f);
+}
+
+// ---------------------------------------------------------------------------
+// grouped kernel: persistent walk over the (expert, m-tile, n-tile) list.
+// Every workgroup derives the list itself from group_list (prefix sums of the
+// per-expert row counts and m-tile counts, in LDS), so there is no host sync
+// and no extra launch. Experts with 0 rows own no tiles.
+// ---------------------------------------------------------------------------
+constexpr int kMaxExperts = 1024;
+
+// Exclusive prefix sums of the per-expert row counts and m-tile counts, for
+// E <= 1024 experts, by a 256-thread workgroup: each thread owns 4 consecutive
+// experts, a wavefront scans with shfl_up, and the 4 wave totals are combined
+// through LDS. row_off[E] / tile_off[E] receive the totals.
+template <int BM>
+__device__ void build_schedule(const int64_t* __restrict__ gl, int E, int64_t* row_off,
+                               int* tile_off) {
+  __shared__ int64_t wave_rows[4];
+  __shared__ int wave_tiles[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int64_t n[4];
+  int64_t rs = 0;
+  int ts = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = 4 * tid + j;
+    n[j] = e < E ? max(gl[e], (int64_t)0) : 0;  // a negative count owns no rows
+    rs += n[j];
+    ts += (int)((n[j] + BM - 1) / BM);
+  }
+  int64_t ri = rs;
+  int ti = ts;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int64_t ro = __shfl_up(ri, d, 64);
+    const int to = __shfl_up(ti, d, 64);
+    if (lane >= d) {
+      ri += ro;
+      ti += to;
+    }
+  }
+  if (lane == 63) {
+    wave_rows[wave] = ri;
+    wave_tiles[wave] = ti;
+  }
+  __syncthreads();
+  int64_t r = ri - rs;
+  int t = ti - ts;
+  for (int w = 0; w < wave; ++w) {
+    r += wave_rows[w];
+    t += wave_tiles[w];
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = 4 * tid + j;
+    if (e < E) {
+      row_off[e] = r;
+      tile_off[e] = t;
+    }
+    r += n[j];
+    t += (int)((n[j] + BM - 1) / BM);
+  }
+  if (tid == 255) {
+    row_off[E] = r;
+    tile_off[E] = t;
+  }
+  __syncthreads();
+}
+
+template <int BM, int BN, int WM, int WN, int BKB>
+__global__ __launch_bounds__(WM* WN* kWave) void grouped_gemm_kernel(GemmArgs p) {
+  static_assert(WM * WN * kWave == 256, "schedule scan assumes 256 threads");
+  using T = Tile<BM, BN, WM, WN, BKB>;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * T::kStageBytes];
+  __shared__ int64_t row_off[kMaxExperts + 1];   // first row of each expert
+  __shared__ int tile_off[kMaxExperts + 1];      // first m-tile of each expert
+  const int E = p.E;
+  build_schedule<BM>(p.group_list, E, row_off, tile_off);
+  const int64_t nt = (p.N + BN - 1) / BN;
+  const int64_t total = (int64_t)tile_off[E] * nt;
+  for (int64_t t = blockIdx.x; t < total; t += gridDim.x) {
+    const int mt = (int)(t / nt);
+    const int64_t tn = t % nt;
+    // expert owning m-tile mt: last e with tile_off[e] <= mt (binary search)
+    int lo = 0, hi = E - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (tile_off[mid] <= mt) lo = mid; else hi = mid - 1;
+    }
+    const int e = lo;
+    const int64_t row0 = row_off[e] + (int64_t)(mt - tile_off[e]) * BM;
+    // counts that sum past R are a caller error; rows at or past R are skipped
+    // so that such a list cannot make the kernel touch memory outside [0, R)
+    const int64_t row_end = min(row_off[e + 1], p.M);
+    if (row0 >= row_end) continue;
+    i32x4 acc[T::TM][T::TN];
+    T::mainloop(p, smem, acc, row0, row_end, e, (int)(tn * BN / 16), 0, p.KB);
+    T::epilogue(p, acc, row0, row_end, e, tn * BN, 0);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// host side: variants and plans
+// ---------------------------------------------------------------------------
+namespace {
+
+struct DenseVariant {
+  int BM, BN;
+  void (*fn)(GemmArgs);
+  int threads;
+};
+
+// 0: prefill-sized M (128x128 tiles, 4 waves of 64x64, two k-blocks per stage)
+// 1: decode M <= 16 (16x64 tiles, 4 waves of 16x16, four k-blocks per stage)
+// 2: decode 16 < M <= 64 (64x64 tiles, 4 waves of 32x32)
+const DenseVariant kDense[] = {
+    {128, 128, dense_gemm_kernel<128, 128, 2, 2, 2>, 256},
+    {16, 64, dense_gemm_kernel<16, 64, 1, 4, 4>, 256},
+    {64, 64, dense_gemm_kernel<64, 64, 2, 2, 2>, 256},
+};
+
+int pick_split(int64_t tiles, int KB, int64_t M, int64_t N) {
+  // Enough workgroups to cover the 256 CUs twice, at least 4 k-blocks per slice,
+  // partial traffic bounded by the weight traffic.
+  int s = 1;
+  while (tiles * s < 512 && KB / (s * 2) >= 4) s *= 2;
+  (void)M;
+  (void)N;
+  return s;
+}
+
+}  // namespace
+
+DensePlan plan_dense(int64_t M, int64_t N, int64_t K) {
+  DensePlan pl{};
+  const int KB = (int)ceil_div(K, 64);
+  pl.variant = M <= 16 ? 1 : (M <= 64 ? 2 : 0);
+  const DenseVariant& v = kDense[pl.variant];
+  const int64_t tiles = ceil_div(M, v.BM) * ceil_div(N, v.BN);
+  pl.split = pl.variant == 0 ? 1 : pick_split(tiles, KB, M, N);
+  pl.ws_bytes = pl.split > 1 ? (int64_t)pl.split * M * N * 4 : 0;
+  return pl;
+}
+
+static GemmArgs make_args(const int8_t* a, const float* a_scale, int64_t M, int64_t K,
+                          const void* w_packed, const float* w_scale, int64_t N,
+                          const uint16_t* bias, void* y, int out) {
+  GemmArgs p{};
+  p.a = a;
+  p.a_scale = a_scale;
+  p.M = M;
+  p.K = K;
+  p.KB = (int)ceil_div(K, 64);
+  p.w = reinterpret_cast<const uint8_t*>(w_packed);
+  p.NB = (int)ceil_div(N, 16);
+  p.w_scale = w_scale;
+  p.N = N;
+  p.bias = bias;
+  p.y = y;
+  p.out = out;
+  p.split = 1;
+  p.kb_per_split = p.KB;
+  p.a_vec = (K % 16 == 0) && (((uintptr_t)a & 15) == 0);
+  return p;
+}
+
+hipError_t launch_dense_gemm(const DensePlan& plan, const int8_t* q, const float* x_scale, int64_t M,
+                             int64_t K, const void* w_packed, const float* w_scale, int64_t N,
+                             const uint16_t* bias, void* y, int out, void* ws, hipStream_t stream) {
+  if (M == 0 || N == 0) return hipSuccess;
+  GemmArgs p = make_args(q, x_scale, M, K, w_packed, w_scale, N, bias, y, out);
+  const DenseVariant& v = kDense[plan.variant];
+  p.split = plan.split;
+  p.kb_per_split = (int)ceil_div(p.KB, plan.split);
+  p.partial = reinterpret_cast<int32_t*>(ws);
+  const int64_t tiles = ceil_div(M, v.BM) * ceil_div(N, v.BN);
+  hipLaunchKernelGGL(v.fn, dim3((unsigned)tiles, (unsigned)plan.split), dim3(v.threads), 0, stream,
+                     p);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || plan.split == 1) return err;
+  hipLaunchKernelGGL(splitk_fixup_kernel, dim3((unsigned)ceil_div(M * N, 256)), dim3(256), 0,
+                     stream, p);
+  return hipGetLastError();
+}
+
+int64_t grouped_ws_bytes(int64_t, int64_t, int64_t, int64_t) { return 0; }
+
+hipError_t launch_grouped_gemm(const int8_t* a, const float* a_scale, const int64_t* group_list,
+                               int64_t R, int64_t E, int64_t N, int64_t K, const void* w_packed,
+                               const float* w_scale, void* y, int out, void*,
+                               hipStream_t stream) {
+  if (R == 0 || N == 0) return hipSuccess;
+  GemmArgs p = make_args(a, a_scale, R, K, w_packed, w_scale, N, nullptr, y, out);
+  p.group_list = group_list;
+  p.E = (int)E;
+  constexpr int BM = 128, BN = 128;
+  // upper bound on tiles: sum_e ceil(n_e / BM) <= R / BM + E
+  const int64_t max_tiles = (ceil_div(R, BM) + E) * ceil_div(N, BN);
+  const int64_t grid = std::min<int64_t>(max_tiles, 256 * 4);
+  hipLaunchKernelGGL((grouped_gemm_kernel<BM, BN, 2, 2, 2>), dim3((unsigned)grid), dim3(256), 0,
+                     stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace w8a8

@@ -1,0 +1,40 @@
+// Internal launchers of the gfx950 kernels (host side). Arguments are checked
+// by the C ABI layer before these are called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace w8a8 {
+
+hipError_t launch_dynamic_quant(const uint16_t* x, int64_t M, int64_t K, int8_t* q, float* scale,
+                                hipStream_t stream);
+hipError_t launch_swiglu_quant(const uint16_t* h, int64_t R, int64_t I, int8_t* q, float* scale,
+                               hipStream_t stream);
+hipError_t launch_prepack(const int8_t* w, int64_t E, int64_t N, int64_t K, void* packed,
+                          hipStream_t stream);
+
+// Output kinds of the GEMM kernels.
+enum OutKind { kOutBf16 = 0, kOutI32 = 1 };
+
+// Dense GEMM plan: kernel variant and split-K factor chosen from the shape.
+struct DensePlan {
+  int variant;   // index into the dense kernel table
+  int split;     // number of K slices (1 = fused epilogue, no workspace)
+  int64_t ws_bytes;
+};
+DensePlan plan_dense(int64_t M, int64_t N, int64_t K);
+hipError_t launch_dense_gemm(const DensePlan& plan, const int8_t* q, const float* x_scale, int64_t M,
+                             int64_t K, const void* w_packed, const float* w_scale, int64_t N,
+                             const uint16_t* bias, void* y, int out, void* ws, hipStream_t stream);
+
+int64_t grouped_ws_bytes(int64_t R, int64_t E, int64_t N, int64_t K);
+hipError_t launch_grouped_gemm(const int8_t* a, const float* a_scale, const int64_t* group_list,
+                               int64_t R, int64_t E, int64_t N, int64_t K, const void* w_packed,
+                               const float* w_scale, void* y, int out, void* ws,
+                               hipStream_t stream);
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
+
+}  // namespace w8a8

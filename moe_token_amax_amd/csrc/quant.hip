@@ -1,0 +1,209 @@
+// Per-token INT8 quantization kernels for gfx950.
+//
+//  * dynamic quant: BF16 [M, K] -> INT8 [M, K] + fp32 scale [M]
+//    ("DeepSeek-V4 W8A8 执行链从量化权重到 Ascend INT8 算子", §一 recipe
+//    per_token / int8 / symmetric, §二 npu_dynamic_quant).
+//  * SwiGLU + requant: BF16 h [R, 2I] -> INT8 [R, I] + fp32 scale [R]
+//    (same page, §三 and §五: the fused "SwiGLU + Requant" step between the W13
+//    and W2 grouped matmuls; §一: W13 = gate_proj + up_proj).
+//
+// One wavefront owns one row. The fast kernels keep the whole row in registers
+// (CPL chunks of 8 elements per lane, 16-byte loads), reduce the row amax with
+// DPP row reductions plus four readlanes, then divide every element by the
+// scale and store 8 codes per chunk. Rows are independent, so four rows share a
+// 256-thread workgroup and the grid is ceil(M / 4) workgroups. HBM traffic is
+// one read of the input and one write of the codes.
+//
+// Shapes outside the fast kernels' limits (K not a multiple of 8, K > 8192,
+// unaligned pointers) take a two-pass kernel with one element per lane per step.
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace w8a8 {
+
+constexpr int kRowsPerBlock = 4;
+
+// |BF16| bit patterns of the two halves of a 32-bit word, max-reduced.
+__device__ __forceinline__ uint32_t abs_bf16_pair_max(uint32_t w) {
+  return max(w & 0x7FFFu, (w >> 16) & 0x7FFFu);
+}
+
+template <int CPL>
+__global__ __launch_bounds__(256) void quant_rows_vec(const uint16_t* __restrict__ x, int64_t M,
+                                                      int64_t K, int8_t* __restrict__ q,
+                                                      float* __restrict__ scale) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+  if (row >= M) return;  // whole wave leaves together
+  const int nchunk = (int)(K >> 3);
+  const uint4* xr = reinterpret_cast<const uint4*>(x + row * K);
+  uint4 v[CPL];
+  uint32_t amax = 0;
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) {
+    const int c = lane + i * kWave;
+    if (c < nchunk) {
+      v[i] = xr[c];
+      amax = max(amax, max(max(abs_bf16_pair_max(v[i].x), abs_bf16_pair_max(v[i].y)),
+                           max(abs_bf16_pair_max(v[i].z), abs_bf16_pair_max(v[i].w))));
+    }
+  }
+  amax = wave_max_u32(amax);
+  const float s = bf16_to_f32(amax) / 127.0f;
+  if (lane == 0) scale[row] = s;
+  uint2* qr = reinterpret_cast<uint2*>(q + row * K);
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) {
+    const int c = lane + i * kWave;
+    if (c < nchunk) {
+      const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+      int code[8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        code[2 * j] = quant_code(bf16_to_f32(w[j] & 0xFFFFu), s);
+        code[2 * j + 1] = quant_code(bf16_to_f32(w[j] >> 16), s);
+      }
+      uint2 o;
+      o.x = pack4(code[0], code[1], code[2], code[3]);
+      o.y = pack4(code[4], code[5], code[6], code[7]);
+      qr[c] = o;
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void quant_rows_generic(const uint16_t* __restrict__ x, int64_t M,
+                                                          int64_t K, int8_t* __restrict__ q,
+                                                          float* __restrict__ scale) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+  if (row >= M) return;
+  const uint16_t* xr = x + row * K;
+  uint32_t amax = 0;
+  for (int64_t k = lane; k < K; k += kWave) amax = max(amax, (uint32_t)xr[k] & 0x7FFFu);
+  amax = wave_max_u32(amax);
+  const float s = bf16_to_f32(amax) / 127.0f;
+  if (lane == 0) scale[row] = s;
+  int8_t* qr = q + row * K;
+  for (int64_t k = lane; k < K; k += kWave) qr[k] = (int8_t)quant_code(bf16_to_f32(xr[k]), s);
+}
+
+// ---------------------------------------------------------------------------
+// SwiGLU + requant
+// ---------------------------------------------------------------------------
+template <int CPL>
+__global__ __launch_bounds__(256) void swiglu_quant_vec(const uint16_t* __restrict__ h, int64_t R,
+                                                        int64_t I, int8_t* __restrict__ q,
+                                                        float* __restrict__ scale) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+  if (row >= R) return;
+  const int nchunk = (int)(I >> 3);
+  const uint4* gr = reinterpret_cast<const uint4*>(h + row * 2 * I);
+  const uint4* ur = reinterpret_cast<const uint4*>(h + row * 2 * I + I);
+  float a[CPL][8];
+  uint32_t amax = 0;
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) {
+    const int c = lane + i * kWave;
+    if (c < nchunk) {
+      const uint4 g4 = gr[c];
+      const uint4 u4 = ur[c];
+      const uint32_t gw[4] = {g4.x, g4.y, g4.z, g4.w};
+      const uint32_t uw[4] = {u4.x, u4.y, u4.z, u4.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        a[i][2 * j] = swiglu_fixed(bf16_to_f32(gw[j] & 0xFFFFu), bf16_to_f32(uw[j] & 0xFFFFu));
+        a[i][2 * j + 1] = swiglu_fixed(bf16_to_f32(gw[j] >> 16), bf16_to_f32(uw[j] >> 16));
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) amax = max(amax, __float_as_uint(a[i][j]) & 0x7FFFFFFFu);
+    }
+  }
+  amax = wave_max_u32(amax);
+  const float s = __uint_as_float(amax) / 127.0f;
+  if (lane == 0) scale[row] = s;
+  uint2* qr = reinterpret_cast<uint2*>(q + row * I);
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) {
+    const int c = lane + i * kWave;
+    if (c < nchunk) {
+      uint2 o;
+      o.x = pack4(quant_code(a[i][0], s), quant_code(a[i][1], s), quant_code(a[i][2], s),
+                  quant_code(a[i][3], s));
+      o.y = pack4(quant_code(a[i][4], s), quant_code(a[i][5], s), quant_code(a[i][6], s),
+                  quant_code(a[i][7], s));
+      qr[c] = o;
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void swiglu_quant_generic(const uint16_t* __restrict__ h, int64_t R,
+                                                            int64_t I, int8_t* __restrict__ q,
+                                                            float* __restrict__ scale) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+  if (row >= R) return;
+  const uint16_t* gr = h + row * 2 * I;
+  const uint16_t* ur = gr + I;
+  uint32_t amax = 0;
+  for (int64_t j = lane; j < I; j += kWave) {
+    const float a = swiglu_fixed(bf16_to_f32(gr[j]), bf16_to_f32(ur[j]));
+    amax = max(amax, __float_as_uint(a) & 0x7FFFFFFFu);
+  }
+  amax = wave_max_u32(amax);
+  const float s = __uint_as_float(amax) / 127.0f;
+  if (lane == 0) scale[row] = s;
+  int8_t* qr = q + row * I;
+  for (int64_t j = lane; j < I; j += kWave) {
+    // recomputed: the same fp32 steps give the same bits as in the amax pass
+    const float a = swiglu_fixed(bf16_to_f32(gr[j]), bf16_to_f32(ur[j]));
+    qr[j] = (int8_t)quant_code(a, s);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+static inline bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+hipError_t launch_dynamic_quant(const uint16_t* x, int64_t M, int64_t K, int8_t* q, float* scale,
+                                hipStream_t stream) {
+  if (M == 0) return hipSuccess;
+  const dim3 grid((unsigned)((M + kRowsPerBlock - 1) / kRowsPerBlock)), block(256);
+  const bool vec = (K % 8 == 0) && aligned(x, 16) && aligned(q, 8);
+  const int64_t chunks = K / 8;
+  if (vec && chunks <= 64 * 1)
+    hipLaunchKernelGGL(quant_rows_vec<1>, grid, block, 0, stream, x, M, K, q, scale);
+  else if (vec && chunks <= 64 * 2)
+    hipLaunchKernelGGL(quant_rows_vec<2>, grid, block, 0, stream, x, M, K, q, scale);
+  else if (vec && chunks <= 64 * 4)
+    hipLaunchKernelGGL(quant_rows_vec<4>, grid, block, 0, stream, x, M, K, q, scale);
+  else if (vec && chunks <= 64 * 8)
+    hipLaunchKernelGGL(quant_rows_vec<8>, grid, block, 0, stream, x, M, K, q, scale);
+  else if (vec && chunks <= 64 * 16)
+    hipLaunchKernelGGL(quant_rows_vec<16>, grid, block, 0, stream, x, M, K, q, scale);
+  else
+    hipLaunchKernelGGL(quant_rows_generic, grid, block, 0, stream, x, M, K, q, scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_swiglu_quant(const uint16_t* h, int64_t R, int64_t I, int8_t* q, float* scale,
+                               hipStream_t stream) {
+  if (R == 0) return hipSuccess;
+  const dim3 grid((unsigned)((R + kRowsPerBlock - 1) / kRowsPerBlock)), block(256);
+  const bool vec = (I % 8 == 0) && aligned(h, 16) && aligned(q, 8);
+  const int64_t chunks = I / 8;
+  if (vec && chunks <= 64 * 1)
+    hipLaunchKernelGGL(swiglu_quant_vec<1>, grid, block, 0, stream, h, R, I, q, scale);
+  else if (vec && chunks <= 64 * 2)
+    hipLaunchKernelGGL(swiglu_quant_vec<2>, grid, block, 0, stream, h, R, I, q, scale);
+  else if (vec && chunks <= 64 * 4)
+    hipLaunchKernelGGL(swiglu_quant_vec<4>, grid, block, 0, stream, h, R, I, q, scale);
+  else if (vec && chunks <= 64 * 8)
+    hipLaunchKernelGGL(swiglu_quant_vec<8>, grid, block, 0, stream, h, R, I, q, scale);
+  else
+    hipLaunchKernelGGL(swiglu_quant_generic, grid, block, 0, stream, h, R, I, q, scale);
+  return hipGetLastError();
+}
+
+}  // namespace w8a8

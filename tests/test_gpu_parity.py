@@ -1,0 +1,282 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+INT8 codes, scales, INT32 accumulators and the BF16 outputs of the canonical
+epilogue are compared bit for bit; BF16 outputs are also checked against the
+unrounded float64 value with max(2**-8 * |ref|, 1e-5). Inputs come from the
+seeded generators in ``synth``; expected values only from ``oracle``.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synth
+from tests.conftest import gpu_available
+from tests.gpu_util import bf16_dev, bf16_host, dev, host, show, sync
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
+
+
+@pytest.fixture(scope="module")
+def w():
+    import moe_token_amax_amd as w
+    return w
+
+
+def _assert_eq(got, want, what):
+    got = np.asarray(got)
+    want = np.asarray(want)
+    assert got.shape == want.shape, (what, got.shape, want.shape)
+    bad = np.argwhere(got != want)
+    assert bad.size == 0, f"{what}: {len(bad)} mismatches, first at {bad[:5].tolist()}: " \
+                          f"got {got[tuple(bad[0])]} want {want[tuple(bad[0])]}"
+
+
+# ---------------------------------------------------------------------------
+# dynamic quant
+# ---------------------------------------------------------------------------
+
+QUANT_SHAPES = [(16, 256), (1, 7168), (64, 7168), (5, 8), (3, 37), (7, 100), (4, 8200),
+                (9, 16384), (130, 4096), (2, 1)]
+
+
+@pytest.mark.parametrize("M,K", QUANT_SHAPES)
+def test_dynamic_quant_bit_exact(w, M, K):
+    show(f"dynamic_quant M={M} K={K}")
+    xb = synth.activations(M, K, 0.01, seed=M * 1000 + K)
+    if M > 2:
+        xb[1] = 0  # all-zero row
+    q, s = w.dynamic_quant(bf16_dev(xb))
+    sync()
+    qo, so = O.dynamic_quant(xb)
+    _assert_eq(host(s).view(np.uint32), so.view(np.uint32), "scale")
+    _assert_eq(host(q), qo, "q")
+
+
+def test_dynamic_quant_ties(w):
+    # rows whose elements sit exactly on .5 after division
+    rows = np.array([[127, 2.5, -0.5, 1.5, -3.5, 0, 0, 0],
+                     [254, 5, 7, -1, 0, 0, 0, 0],
+                     [22, -11, 0, 0, 0, 0, 0, 0],
+                     [15.25, 7.625, 0, 0, 0, 0, 0, 0]], np.float32)
+    xb = O.f32_to_bf16(rows)
+    q, s = w.dynamic_quant(bf16_dev(xb))
+    sync()
+    qo, so = O.dynamic_quant(xb)
+    _assert_eq(host(q), qo, "q")
+    _assert_eq(host(s), so, "scale")
+
+
+def test_dynamic_quant_empty(w):
+    x = torch.empty((0, 64), dtype=torch.bfloat16, device="cuda")
+    q, s = w.dynamic_quant(x)
+    assert q.shape == (0, 64) and s.shape == (0,)
+
+
+# ---------------------------------------------------------------------------
+# prepack + dense linear
+# ---------------------------------------------------------------------------
+
+def _run_linear(w, d: synth.Dense, out):
+    xb = bf16_dev(d.x)
+    q, s = w.dynamic_quant(xb)
+    wp = w.prepack_weight(dev(d.w))
+    y = w.linear(q, s, wp, dev(d.w_scale), d.N,
+                 bias=None if d.bias is None else bf16_dev(d.bias), out=out)
+    sync()
+    return q, s, y
+
+
+LINEAR_SHAPES = [  # M, K, N, bias
+    (16, 256, 128, True), (1, 64, 16, False), (17, 100, 50, True), (3, 37, 5, False),
+    (33, 448, 96, True), (64, 1024, 192, False), (129, 320, 144, True), (300, 512, 260, False),
+    (4, 7168, 512, False), (16, 7168, 256, True),
+]
+
+
+@pytest.mark.parametrize("M,K,N,bias", LINEAR_SHAPES)
+def test_linear_acc_and_bf16_bit_exact(w, M, K, N, bias):
+    show(f"linear M={M} K={K} N={N} bias={bias}")
+    d = synth.dense(M, K, N, outlier_frac=0.01, bias=bias, seed=M + K + N)
+    q, s, acc = _run_linear(w, d, w.OUT_I32)
+    qo, so = O.dynamic_quant(d.x)
+    _assert_eq(host(q), qo, "q")
+    acc_o = O.int8_matmul_acc(qo, d.w)
+    _assert_eq(host(acc), acc_o.astype(np.int32), "acc")
+    _, _, y = _run_linear(w, d, w.OUT_BF16)
+    yo, _ = O.linear(qo, so, d.w, d.w_scale, d.bias)
+    yh = bf16_host(y)
+    _assert_eq(yh, yo, "y")
+    assert O.bf16_within_tolerance(yh, O.linear_ref64(acc_o, so, d.w_scale, d.bias)).all()
+
+
+def test_tiny_config(w):
+    d = synth.tiny(seed=0)
+    _, _, y = _run_linear(w, d, w.OUT_BF16)
+    qo, so = O.dynamic_quant(d.x)
+    yo, _ = O.linear(qo, so, d.w, d.w_scale, d.bias)
+    _assert_eq(bf16_host(y), yo, "tiny y")
+
+
+@pytest.mark.parametrize("M", [1, 4, 16, 64])
+def test_decode_config_full(w, M):
+    show(f"decode M={M}")
+    d = synth.decode(seed=0, M=M)
+    q, s, y = _run_linear(w, d, w.OUT_BF16)
+    qo, so = O.dynamic_quant(d.x)
+    _assert_eq(host(q), qo, "q")
+    yo, acc = O.linear(qo, so, d.w, d.w_scale, None)
+    yh = bf16_host(y)
+    _assert_eq(yh, yo, "y")
+    assert O.bf16_within_tolerance(yh, O.linear_ref64(acc, so, d.w_scale, None)).all()
+
+
+@pytest.mark.timeout(300)
+def test_prefill_config_sampled_rows(w):
+    show("prefill full size, sampled rows")
+    d = synth.prefill(seed=0)
+    q, s, y = _run_linear(w, d, w.OUT_BF16)
+    qo, so = O.dynamic_quant(d.x)
+    _assert_eq(host(q), qo, "q")
+    _assert_eq(host(s), so, "scale")
+    rng = np.random.default_rng(0)
+    rows = np.unique(np.concatenate([[0, 8191], rng.integers(0, 8192, 30)]))
+    yo, acc = O.linear(qo[rows], so[rows], d.w, d.w_scale, d.bias)
+    yh = bf16_host(y)[rows]
+    _assert_eq(yh, yo, "y rows")
+
+
+# ---------------------------------------------------------------------------
+# grouped GEMM
+# ---------------------------------------------------------------------------
+
+def _grouped_case(counts, N, K, seed):
+    g = np.asarray(counts, np.int64)
+    R, E = int(g.sum()), len(g)
+    a = synth.int8_weight((R, K), seed, 11)
+    xs = synth.scales(R, seed, 12)
+    wt = synth.int8_weight((E, N, K), seed, 13)
+    ws = synth.scales((E, N), seed, 14)
+    return g, a, xs, wt, ws
+
+
+GROUPED_CASES = [
+    ([12, 7, 0, 19], 48, 64),
+    ([12, 7, 0, 19], 20, 100),
+    ([0, 0, 9, 0, 0], 130, 256),
+    ([0, 300, 1, 0, 129, 2, 0], 256, 320),
+    ([5] * 33, 64, 128),
+    ([0, 0, 0], 16, 64),
+]
+
+
+@pytest.mark.parametrize("counts,N,K", GROUPED_CASES)
+def test_grouped_gemm_bit_exact(w, counts, N, K):
+    show(f"grouped counts={counts} N={N} K={K}")
+    g, a, xs, wt, ws = _grouped_case(counts, N, K, seed=len(counts) + N)
+    R, E = int(g.sum()), len(g)
+    wp = w.prepack_weight(dev(wt))
+    if R == 0:
+        a_d = torch.empty((0, K), dtype=torch.int8, device="cuda")
+        y = w.grouped_gemm(a_d, torch.empty(0, device="cuda"), dev(g), wp, dev(ws), N)
+        assert y.shape == (0, N)
+        return
+    acc = w.grouped_gemm(dev(a), dev(xs), dev(g), wp, dev(ws), N, out=w.OUT_I32)
+    y = w.grouped_gemm(dev(a), dev(xs), dev(g), wp, dev(ws), N, out=w.OUT_BF16)
+    sync()
+    yo, acc_o = O.grouped_gemm_bf16(a, xs, g, wt, ws)
+    _assert_eq(host(acc), acc_o.astype(np.int32), "acc")
+    _assert_eq(bf16_host(y), yo, "y")
+
+
+# ---------------------------------------------------------------------------
+# SwiGLU + requant
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("R,I", [(16, 2048), (5, 24), (3, 37), (9, 4096), (2, 8200), (64, 512)])
+def test_swiglu_quant_bit_exact(w, R, I):
+    show(f"swiglu_quant R={R} I={I}")
+    rng = np.random.default_rng(R * 7 + I)
+    h = (rng.standard_normal((R, 2 * I)) * 4).astype(np.float32)
+    h[0, :4] = [100.0, -100.0, 0.0, -90.0]       # saturating exp on both sides
+    if R > 2:
+        h[2] = 0.0                               # all-zero row
+    hb = O.f32_to_bf16(h)
+    q, s = w.swiglu_quant(bf16_dev(hb))
+    sync()
+    qo, so = O.swiglu_quant(hb, I)
+    _assert_eq(host(s).view(np.uint32), so.view(np.uint32), "scale")
+    _assert_eq(host(q), qo, "q")
+
+
+# ---------------------------------------------------------------------------
+# MoE chain
+# ---------------------------------------------------------------------------
+
+def _moe_small(counts, H, I, seed):
+    g = np.asarray(counts, np.int64)
+    E, R = len(g), int(g.sum())
+    x = synth.activations(R, H, 0.01, seed)
+    w13 = synth.int8_weight((E, 2 * I, H), seed, 6)
+    w2 = synth.int8_weight((E, H, I), seed, 7)
+    w13s = synth.scales((E, 2 * I), seed, 8)
+    w2s = synth.scales((E, H), seed, 9)
+    return g, x, w13, w13s, w2, w2s
+
+
+@pytest.mark.parametrize("counts,H,I", [([12, 7, 0, 19], 64, 32), ([0, 200, 3, 0, 70], 256, 128)])
+def test_moe_chain_bit_exact(w, counts, H, I):
+    show(f"moe chain counts={counts} H={H} I={I}")
+    g, x, w13, w13s, w2, w2s = _moe_small(counts, H, I, seed=H)
+    st = O.moe_grouped(g, w13, w13s, w2, w2s, x_bits=x, keep=True)
+    w13p, w2p = w.prepack_weight(dev(w13)), w.prepack_weight(dev(w2))
+    y = w.moe_grouped(bf16_dev(x), dev(g), w13p, dev(w13s), w2p, dev(w2s))
+    # stage by stage through the sub-stage entry points
+    q, s = w.dynamic_quant(bf16_dev(x))
+    h = w.grouped_gemm(q, s, dev(g), w13p, dev(w13s), 2 * I)
+    q2, s2 = w.swiglu_quant(h)
+    # the pre-quantized entry: INT8 rows + scale skip the first quant
+    y2 = w.moe_grouped(q, dev(g), w13p, dev(w13s), w2p, dev(w2s), x_scale=s)
+    sync()
+    _assert_eq(bf16_host(h), st["h"], "h")
+    _assert_eq(host(q2), st["q2"], "q2")
+    _assert_eq(host(s2), st["s2"], "s2")
+    _assert_eq(bf16_host(y), st["y"], "y")
+    _assert_eq(bf16_host(y2), st["y"], "y (int8 input)")
+
+
+@pytest.mark.timeout(600)
+def test_moe_config_sampled_rows(w):
+    """Full MoE workload; the oracle recomputes a sample of rows one by one."""
+    show("moe full size, sampled rows")
+    m = synth.moe(seed=0)
+    E, H, I = m.E, m.H, m.I
+    w13p = torch.empty(w.packed_weight_bytes(E, 2 * I, H), dtype=torch.uint8, device="cuda")
+    w2p = torch.empty(w.packed_weight_bytes(E, H, I), dtype=torch.uint8, device="cuda")
+    per13 = w.packed_weight_bytes(1, 2 * I, H)
+    per2 = w.packed_weight_bytes(1, H, I)
+    for e in range(E):  # prepack expert by expert (bounded staging memory)
+        w.prepack_weight(dev(m.w13(e)), out=w13p[e * per13:(e + 1) * per13])
+        w.prepack_weight(dev(m.w2(e)), out=w2p[e * per2:(e + 1) * per2])
+        m.drop_cache()
+    xr = m.x_rows()
+    y = w.moe_grouped(bf16_dev(xr), dev(m.group_list), w13p, dev(m.w13_scale), w2p,
+                      dev(m.w2_scale))
+    yh = bf16_host(y)
+    ex = O.expert_of_rows(m.group_list)
+    rng = np.random.default_rng(1)
+    off = O.group_offsets(m.group_list)
+    rows = set(rng.integers(0, m.R, 24).tolist())
+    big = int(np.argmax(m.group_list))
+    rows |= {int(off[big]), int(off[big + 1]) - 1, 0, m.R - 1}
+    for r in sorted(rows):
+        e = int(ex[r])
+        one = np.array([1], np.int64)
+        st = O.moe_grouped(one, m.w13(e)[None], m.w13_scale[e][None], m.w2(e)[None],
+                           m.w2_scale[e][None], x_bits=xr[r:r + 1])
+        _assert_eq(yh[r:r + 1], st, f"row {r} (expert {e})")
+        m.drop_cache()

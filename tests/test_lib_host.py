@@ -1,0 +1,66 @@
+"""The C-ABI library loads and validates on the host (CPU only, no GPU calls).
+
+Every call here fails argument validation before anything is launched, or is a
+pure size query, so nothing touches a device.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "w8a8.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(w8a8_\w+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def w():
+    import moe_token_amax_amd as w
+    return w
+
+
+def test_exports_every_declared_symbol(w):
+    names = _declared()
+    assert len(names) >= 13
+    raw = ctypes.CDLL(w.LIB_PATH)
+    missing = [n for n in names if not hasattr(raw, n)]
+    assert not missing, missing
+
+
+def test_abi_and_status_strings(w):
+    assert w.lib.w8a8_abi_version() == 1
+    assert w.lib.w8a8_status_str(0) == b"ok"
+    assert w.lib.w8a8_status_str(5) == b"workspace too small"
+
+
+def test_packed_bytes_formula(w):
+    # K padded to 64, N padded to 16
+    assert w.packed_weight_bytes(1, 128, 256) == 128 * 256
+    assert w.packed_weight_bytes(2, 17, 65) == 2 * 32 * 128
+    assert w.packed_weight_bytes(256, 4096, 4096) == 256 * 4096 * 4096
+
+
+def test_validation_before_launch(w):
+    L = w.lib
+    p = ctypes.c_void_p(16)  # never dereferenced: validation fails first
+    assert L.w8a8_dynamic_quant(p, 4, 0, p, p, None) == 2
+    assert L.w8a8_dynamic_quant(None, 4, 8, None, None, None) == 1
+    assert b"null" in L.w8a8_last_error()
+    assert L.w8a8_dynamic_quant(None, 0, 8, None, None, None) == 0  # M == 0 is a no-op
+    assert L.w8a8_linear(p, p, 4, 200000, p, p, 8, None, p, 0, None, 0, None) == 2
+    assert L.w8a8_linear(p, p, 4, 64, p, p, 8, None, p, 7, None, 0, None) == 4
+    assert L.w8a8_linear(p, p, 4, 64, ctypes.c_void_p(24), p, 8, None, p, 0, None, 0, None) == 3
+    # decode-sized M needs a split-K workspace
+    need = L.w8a8_linear_workspace_bytes(4, 4096, 7168)
+    assert need > 0
+    assert L.w8a8_linear(p, p, 4, 7168, p, p, 4096, None, p, 0, None, 0, None) == 5
+    assert L.w8a8_grouped_gemm(p, p, p, 8, 2000, 16, 16, p, p, p, 0, None, 0, None) == 4
+    assert L.w8a8_swiglu_quant(p, 4, 0, p, p, None) == 2
+    assert L.w8a8_moe_grouped(p, None, p, 16, 4, 64, 32, p, p, p, p, p, None, 0, None) == 5
