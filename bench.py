@@ -58,8 +58,8 @@ def _args():
 # ---------------------------------------------------------------------------
 
 class Workload:
-    """A list of phase graphs (step i replays phase i % len), each bracketing its
-    dominant-kernel launches with event pairs."""
+    """Step graphs (step i replays phase i % len(phases)) and, separately, graphs
+    holding only launches of the dominant kernel, for its event timing."""
     name = ""
     metric = "W8A8 linear TOPS and HBM GB/s (% of peak); MoE grouped-GEMM tokens/s"
     unit = ""
@@ -68,27 +68,30 @@ class Workload:
     def __init__(self, w, torch):
         self.w = w
         self.torch = torch
-        self.phases = []          # list of (graph, [(ev_start, ev_end, key)])
+        self.phases = []          # step graphs
+        self.dominant_graphs = []  # (graph, launches per replay, key)
 
-    def capture(self, fns):
-        """fns: list of callables, each enqueuing one step and returning a list of
-        (start_event, end_event, key) it recorded."""
+    def _graph(self, fn):
         torch = self.torch
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(s):
-            for fn in fns:      # eager warm-up of every phase outside capture
-                fn(record=False)
+            fn()                  # eager run outside capture
         torch.cuda.current_stream().wait_stream(s)
         torch.cuda.synchronize()
-        for fn in fns:
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                evs = fn(record=True)
-            self.phases.append((g, evs))
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        return g
+
+    def capture(self, step_fns, dominant):
+        """step_fns: callables enqueuing one step each; dominant: (callable,
+        launches, key) triples enqueuing only dominant-kernel launches."""
+        self.phases = [self._graph(fn) for fn in step_fns]
+        self.dominant_graphs = [(self._graph(fn), n, key) for fn, n, key in dominant]
 
     def step(self, i):
-        self.phases[i % len(self.phases)][0].replay()
+        self.phases[i % len(self.phases)].replay()
 
 
 def _ev(torch):
@@ -133,30 +136,28 @@ class DenseWorkload(Workload):
         # round-robin over weight copies: phase p uses copies p*len(Ms) + j
         per = len(self.Ms)
         nphase = max(1, copies // per)
-        fns = []
-        for p in range(nphase):
-            fns.append(self._make_step([(p * per + j) % copies for j in range(per)]))
-        self.capture(fns)
+        steps = [self._make_step([(p * per + j) % copies for j in range(per)])
+                 for p in range(nphase)]
+        dom = [(self._make_linears(M), copies, M) for M in self.Ms]
+        self.capture(steps, dom)
         self.unit = "GB/s" if name != "prefill" else "TOPS"
         self.bound = "hbm" if name != "prefill" else "mfma"
 
-    def _make_step(self, copy_ids):
-        w, torch = self.w, self.torch
+    def _linear(self, M, c):
+        self.w.linear(self.q[M], self.s[M], self.wp[c], self.w_scale, self.N, bias=self.bias,
+                      y=self.y[M], workspace=self.ws[M])
 
-        def fn(record):
-            evs = []
+    def _make_step(self, copy_ids):
+        def fn():
             for M, c in zip(self.Ms, copy_ids):
-                xm = self.x[:M]
-                w.dynamic_quant(xm, self.q[M], self.s[M])
-                if record:
-                    a, b = _ev(torch), _ev(torch)
-                    a.record()
-                w.linear(self.q[M], self.s[M], self.wp[c], self.w_scale, self.N, bias=self.bias,
-                         y=self.y[M], workspace=self.ws[M])
-                if record:
-                    b.record()
-                    evs.append((a, b, M))
-            return evs
+                self.w.dynamic_quant(self.x[:M], self.q[M], self.s[M])
+                self._linear(M, c)
+        return fn
+
+    def _make_linears(self, M):
+        def fn():
+            for c in range(self.copies):
+                self._linear(M, c)
         return fn
 
     # algorithmic bytes / ops
@@ -264,30 +265,21 @@ class MoeWorkload(Workload):
         self.s2 = torch.empty((R,), dtype=torch.float32, device=dev)
         self.unit = "tokens/s"
         self.bound = "hbm"
-        self.capture([self._step])
+        self.capture([self._step], [(self._w13, 1, "w13"), (self._w2, 1, "w2")])
 
-    def _step(self, record):
-        """Same kernels as moe_grouped, through the sub-stage entry points so the
-        two grouped GEMM launches can be bracketed by events."""
-        w, torch, m = self.w, self.torch, self.m
-        evs = []
+    def _step(self):
+        """Same kernels as moe_grouped, through the sub-stage entry points."""
+        w = self.w
         w.dynamic_quant(self.x, self.q1, self.s1)
-        a, b = (_ev(torch), _ev(torch)) if record else (None, None)
-        if record:
-            a.record()
-        w.grouped_gemm(self.q1, self.s1, self.gl, self.w13p, self.w13s, 2 * m.I, y=self.h)
-        if record:
-            b.record()
-            evs.append((a, b, "w13"))
+        self._w13()
         w.swiglu_quant(self.h, self.q2, self.s2)
-        a, b = (_ev(torch), _ev(torch)) if record else (None, None)
-        if record:
-            a.record()
-        w.grouped_gemm(self.q2, self.s2, self.gl, self.w2p, self.w2s, m.H, y=self.y)
-        if record:
-            b.record()
-            evs.append((a, b, "w2"))
-        return evs
+        self._w2()
+
+    def _w13(self):
+        self.w.grouped_gemm(self.q1, self.s1, self.gl, self.w13p, self.w13s, 2 * self.m.I, y=self.h)
+
+    def _w2(self):
+        self.w.grouped_gemm(self.q2, self.s2, self.gl, self.w2p, self.w2s, self.m.H, y=self.y)
 
     def nonempty(self):
         return int((self.m.group_list > 0).sum())
@@ -379,32 +371,31 @@ def main():
     for i in range(args.warmup):
         wl.step(i)
     torch.cuda.synchronize()
-    # Timed region. Before phase p is replayed again, the events of its previous
-    # replay (several steps back) are read; waiting on them leaves the newer
-    # replays queued, so the GPU never idles on the host.
-    nph = len(wl.phases)
-    pending = [False] * nph
-    per_key, counts = {}, {}
-
-    def collect(p):
-        for a, b, k in wl.phases[p][1]:
-            b.synchronize()
-            per_key[k] = per_key.get(k, 0.0) + a.elapsed_time(b)
-            counts[k] = counts.get(k, 0) + 1
-
+    # timed region: K steps, each a replay of the step's graph
     t0 = time.perf_counter()
     for i in range(args.steps):
-        p = (args.warmup + i) % nph
-        if pending[p]:
-            collect(p)
-        wl.phases[p][0].replay()
-        pending[p] = True
+        wl.step(args.warmup + i)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    for p in range(nph):
-        if pending[p]:
-            collect(p)
     sec = elapsed / args.steps
+
+    # dominant kernel: HIP events on the launch stream around replays of graphs
+    # that hold only its launches (same buffers and weight rotation as the step)
+    stream = torch.cuda.current_stream()
+    per_key, counts = {}, {}
+    reps = max(3, min(args.steps, 50))
+    for g, n, key in wl.dominant_graphs:
+        g.replay()                                   # warm
+        evs = []
+        for _ in range(reps):
+            a, b = _ev(torch), _ev(torch)
+            a.record(stream)
+            g.replay()
+            b.record(stream)
+            evs.append((a, b))
+        torch.cuda.synchronize()
+        per_key[key] = sum(a.elapsed_time(b) for a, b in evs)
+        counts[key] = reps * n
     avg_ms = {k: per_key[k] / counts[k] for k in per_key}
 
     roof = wl.dominant(avg_ms)

@@ -18,8 +18,7 @@
 //   * Each wavefront owns a (BM/WM) x (BN/WN) sub-tile of 16x16 INT32
 //     accumulators and issues v_mfma_i32_16x16x64_i8.
 //   * Epilogue in registers: y = BF16(((float(acc) * xs[m]) * ws[n]) + b[n]),
-//     or raw INT32, or (split-K) INT32 partial sums that a fixup kernel adds
-//     exactly and then runs through the same epilogue.
+//     or the raw INT32 sums.
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -40,9 +39,6 @@ struct GemmArgs {
   const uint16_t* bias;     // [N] or null
   void* y;                  // [rows, N]
   int out;                  // OutKind
-  int32_t* partial;         // split-K partial sums [split, M, N] (dense only)
-  int split;                // number of K slices
-  int kb_per_split;         // k-blocks per slice
   bool a_vec;               // K % 16 == 0 and a 16-byte aligned
   const int64_t* group_list;  // grouped only
   int E;
@@ -164,6 +160,7 @@ struct Tile {
       const bool more = s + 1 < nst;
       if (more)
         load_stage(p, r, wave, lane, row0, row_end, wblk0, nb0, kb_begin + (s + 1) * BKB, kb_end);
+      __builtin_amdgcn_sched_barrier(0);  // next stage's loads issue before this stage's MFMAs
       compute_stage(cur, acc, wm, wn, lane);
       if (more) store_stage(nxt, r, wave, lane);
       __syncthreads();
@@ -172,10 +169,9 @@ struct Tile {
 
   // Writes the tile. Local row i of the tile is global row row0 + i; rows at or
   // past row_end and columns at or past N are skipped. `e` selects the w_scale
-  // row. With a split slice z > 0 or split > 1 the raw sums go to `partial`.
+  // row.
   __device__ __forceinline__ static void epilogue(const GemmArgs& p, const i32x4 (&acc)[TM][TN],
-                                                  int64_t row0, int64_t row_end, int e, int64_t n0,
-                                                  int z) {
+                                                  int64_t row0, int64_t row_end, int e, int64_t n0) {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int wm = wave / WN, wn = wave % WN;
@@ -193,9 +189,7 @@ struct Tile {
           const int64_t m = row0 + (wm * TM + i) * 16 + (lane >> 4) * 4 + t;
           if (m >= row_end) continue;
           const int32_t v = acc[i][j][t];
-          if (p.split > 1) {
-            p.partial[((int64_t)z * p.M + m) * p.N + n] = v;
-          } else if (p.out == kOutI32) {
+          if (p.out == kOutI32) {
             reinterpret_cast<int32_t*>(p.y)[m * p.N + n] = v;
           } else {
             float f = (float)v;
@@ -211,7 +205,7 @@ struct Tile {
 };
 
 // ---------------------------------------------------------------------------
-// dense kernel: grid.x = tiles (n fastest), grid.y = split slice
+// dense kernel (M > 64): grid.x = tiles, n fastest
 // ---------------------------------------------------------------------------
 template <int BM, int BN, int WM, int WN, int BKB>
 __global__ __launch_bounds__(WM* WN* kWave) void dense_gemm_kernel(GemmArgs p) {
@@ -219,31 +213,10 @@ __global__ __launch_bounds__(WM* WN* kWave) void dense_gemm_kernel(GemmArgs p) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * T::kStageBytes];
   const int64_t nt = (p.N + BN - 1) / BN;
   const int64_t tm = blockIdx.x / nt, tn = blockIdx.x % nt;
-  const int z = blockIdx.y;
   const int64_t row0 = tm * BM;
-  const int kb_begin = z * p.kb_per_split;
-  const int kb_end = min(p.KB, kb_begin + p.kb_per_split);
   i32x4 acc[T::TM][T::TN];
-  T::mainloop(p, smem, acc, row0, p.M, 0, (int)(tn * BN / 16), kb_begin, kb_end);
-  T::epilogue(p, acc, row0, p.M, 0, tn * BN, z);
-}
-
-// Sums the split-K partials exactly (INT32) and applies the epilogue.
-__global__ __launch_bounds__(256) void splitk_fixup_kernel(GemmArgs p) {
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= p.M * p.N) return;
-  const int64_t m = idx / p.N, n = idx % p.N;
-  int32_t s = 0;
-  for (int z = 0; z < p.split; ++z) s += p.partial[(int64_t)z * p.M * p.N + idx];
-  if (p.out == kOutI32) {
-    reinterpret_cast<int32_t*>(p.y)[idx] = s;
-    return;
-  }
-  float f = (float)s;
-  f = f * p.a_scale[m];
-  f = f * p.w_scale[n];
-  if (p.bias) f = f + bf16_to_f32(p.bias[n]);
-  reinterpret_cast<uint16_t*>(p.y)[idx] = (uint16_t)f32_to_bf16(f);
+  T::mainloop(p, smem, acc, row0, p.M, 0, (int)(tn * BN / 16), 0, p.KB);
+  T::epilogue(p, acc, row0, p.M, 0, tn * BN);
 }
 
 // ---------------------------------------------------------------------------
@@ -341,7 +314,86 @@ __global__ __launch_bounds__(WM* WN* kWave) void grouped_gemm_kernel(GemmArgs p)
     if (row0 >= row_end) continue;
     i32x4 acc[T::TM][T::TN];
     T::mainloop(p, smem, acc, row0, row_end, e, (int)(tn * BN / 16), 0, p.KB);
-    T::epilogue(p, acc, row0, row_end, e, tn * BN, 0);
+    T::epilogue(p, acc, row0, row_end, e, tn * BN);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// decode kernel (M <= 64): weight-streaming GEMV-like path.
+// One workgroup owns one 16-column n-block over the full K; its WAVES
+// wavefronts take interleaved k-blocks (wave w: w, w + WAVES, ...) so that the
+// workgroup streams contiguous 1 KB weight blocks. Weights go straight from
+// HBM into MFMA operand registers (the packed layout is the operand layout),
+// UNR blocks per wave in flight at once; the MB m-blocks of A (<= 64 rows,
+// shared by all workgroups and served from L2) are loaded the same way. The
+// per-wave INT32 partial sums are added in LDS and the epilogue runs on the
+// full sums: one kernel, no workspace, no second pass. Grid = ceil(N / 16).
+// ---------------------------------------------------------------------------
+template <int MB, int WAVES, int UNR, bool AVEC>
+__global__ __launch_bounds__(WAVES* kWave) void decode_gemm_kernel(GemmArgs p) {
+  __shared__ i32x4 red[WAVES][MB][kWave];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nb = blockIdx.x;
+  const uint8_t* wcol = p.w + (int64_t)nb * p.KB * kBlockBytes + lane * 16;
+  const int64_t mlast = p.M - 1;
+  i32x4 acc[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) acc[mb] = i32x4{0, 0, 0, 0};
+  for (int kb0 = wave; kb0 < p.KB; kb0 += WAVES * UNR) {
+    i32x4 b[UNR];
+    i32x4 a[UNR][MB];
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const int kb = kb0 + u * WAVES;
+      const int kbc = kb < p.KB ? kb : p.KB - 1;    // clamped: loads stay in bounds
+      b[u] = *reinterpret_cast<const i32x4*>(wcol + (int64_t)kbc * kBlockBytes);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        // A rows past M are read clamped to row M-1: they only feed output
+        // rows >= M, which are never stored
+        const int64_t row = mb * 16 + (lane & 15);
+        const int64_t kcol = (int64_t)kbc * 64 + (lane >> 4) * 16;
+        if (AVEC)
+          a[u][mb] = *reinterpret_cast<const i32x4*>(p.a + (row < p.M ? row : mlast) * p.K + kcol);
+        else
+          a[u][mb] = load_a16(p, row, p.M, kcol);
+      }
+    }
+    // keep every load of this round ahead of the first MFMA: without the
+    // barrier the scheduler interleaves load / wait / MFMA and only a couple of
+    // blocks are in flight per wavefront
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      if (kb0 + u * WAVES >= p.KB) break;  // wave-uniform: clamped duplicate blocks add nothing
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) acc[mb] = mfma16x16x64(a[u][mb], b[u], acc[mb]);
+    }
+  }
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) red[wave][mb][lane] = acc[mb];
+  __syncthreads();
+  if (wave >= MB) return;
+  i32x4 sum = red[0][wave][lane];
+#pragma unroll
+  for (int w = 1; w < WAVES; ++w) sum += red[w][wave][lane];
+  const int64_t n = (int64_t)nb * 16 + (lane & 15);
+  if (n >= p.N) return;
+  const float ws = p.w_scale[n];
+  const float bsv = p.bias ? bf16_to_f32(p.bias[n]) : 0.0f;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int64_t m = wave * 16 + (lane >> 4) * 4 + t;
+    if (m >= p.M) continue;
+    if (p.out == kOutI32) {
+      reinterpret_cast<int32_t*>(p.y)[m * p.N + n] = sum[t];
+    } else {
+      float f = (float)sum[t];
+      f = f * p.a_scale[m];
+      f = f * ws;
+      if (p.bias) f = f + bsv;
+      reinterpret_cast<uint16_t*>(p.y)[m * p.N + n] = (uint16_t)f32_to_bf16(f);
+    }
   }
 }
 
@@ -354,37 +406,36 @@ struct DenseVariant {
   int BM, BN;
   void (*fn)(GemmArgs);
   int threads;
+  bool decode;   // grid = n-blocks, one workgroup per 16 columns
 };
 
-// 0: prefill-sized M (128x128 tiles, 4 waves of 64x64, two k-blocks per stage)
-// 1: decode M <= 16 (16x64 tiles, 4 waves of 16x16, four k-blocks per stage)
-// 2: decode 16 < M <= 64 (64x64 tiles, 4 waves of 32x32)
+constexpr int kDecodeWaves = 8;
+
+// 0: M > 64: 128x128 tiles, 4 waves of 64x64, two k-blocks per LDS stage
+// 1..3: M <= 16 / 32 / 64: decode kernel with 1 / 2 / 4 m-blocks
+// 4..6: the same for K % 16 != 0 or an unaligned activation pointer
 const DenseVariant kDense[] = {
-    {128, 128, dense_gemm_kernel<128, 128, 2, 2, 2>, 256},
-    {16, 64, dense_gemm_kernel<16, 64, 1, 4, 4>, 256},
-    {64, 64, dense_gemm_kernel<64, 64, 2, 2, 2>, 256},
+    {128, 128, dense_gemm_kernel<128, 128, 2, 2, 2>, 256, false},
+    {16, 16, decode_gemm_kernel<1, kDecodeWaves, 14, true>, kDecodeWaves * 64, true},
+    {32, 16, decode_gemm_kernel<2, kDecodeWaves, 14, true>, kDecodeWaves * 64, true},
+    {64, 16, decode_gemm_kernel<4, kDecodeWaves, 7, true>, kDecodeWaves * 64, true},
+    {16, 16, decode_gemm_kernel<1, kDecodeWaves, 14, false>, kDecodeWaves * 64, true},
+    {32, 16, decode_gemm_kernel<2, kDecodeWaves, 14, false>, kDecodeWaves * 64, true},
+    {64, 16, decode_gemm_kernel<4, kDecodeWaves, 7, false>, kDecodeWaves * 64, true},
 };
-
-int pick_split(int64_t tiles, int KB, int64_t M, int64_t N) {
-  // Enough workgroups to cover the 256 CUs twice, at least 4 k-blocks per slice,
-  // partial traffic bounded by the weight traffic.
-  int s = 1;
-  while (tiles * s < 512 && KB / (s * 2) >= 4) s *= 2;
-  (void)M;
-  (void)N;
-  return s;
-}
 
 }  // namespace
 
 DensePlan plan_dense(int64_t M, int64_t N, int64_t K) {
+  (void)N;
   DensePlan pl{};
-  const int KB = (int)ceil_div(K, 64);
-  pl.variant = M <= 16 ? 1 : (M <= 64 ? 2 : 0);
-  const DenseVariant& v = kDense[pl.variant];
-  const int64_t tiles = ceil_div(M, v.BM) * ceil_div(N, v.BN);
-  pl.split = pl.variant == 0 ? 1 : pick_split(tiles, KB, M, N);
-  pl.ws_bytes = pl.split > 1 ? (int64_t)pl.split * M * N * 4 : 0;
+  if (M > 64) {
+    pl.variant = 0;
+  } else {
+    pl.variant = M <= 16 ? 1 : (M <= 32 ? 2 : 3);
+    if (K % 16 != 0) pl.variant += 3;
+  }
+  pl.ws_bytes = 0;
   return pl;
 }
 
@@ -404,8 +455,6 @@ static GemmArgs make_args(const int8_t* a, const float* a_scale, int64_t M, int6
   p.bias = bias;
   p.y = y;
   p.out = out;
-  p.split = 1;
-  p.kb_per_split = p.KB;
   p.a_vec = (K % 16 == 0) && (((uintptr_t)a & 15) == 0);
   return p;
 }
@@ -413,19 +462,15 @@ static GemmArgs make_args(const int8_t* a, const float* a_scale, int64_t M, int6
 hipError_t launch_dense_gemm(const DensePlan& plan, const int8_t* q, const float* x_scale, int64_t M,
                              int64_t K, const void* w_packed, const float* w_scale, int64_t N,
                              const uint16_t* bias, void* y, int out, void* ws, hipStream_t stream) {
+  (void)ws;
   if (M == 0 || N == 0) return hipSuccess;
   GemmArgs p = make_args(q, x_scale, M, K, w_packed, w_scale, N, bias, y, out);
-  const DenseVariant& v = kDense[plan.variant];
-  p.split = plan.split;
-  p.kb_per_split = (int)ceil_div(p.KB, plan.split);
-  p.partial = reinterpret_cast<int32_t*>(ws);
-  const int64_t tiles = ceil_div(M, v.BM) * ceil_div(N, v.BN);
-  hipLaunchKernelGGL(v.fn, dim3((unsigned)tiles, (unsigned)plan.split), dim3(v.threads), 0, stream,
-                     p);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess || plan.split == 1) return err;
-  hipLaunchKernelGGL(splitk_fixup_kernel, dim3((unsigned)ceil_div(M * N, 256)), dim3(256), 0,
-                     stream, p);
+  int variant = plan.variant;
+  // the decode kernels load A rows with 16-byte loads when the pointer allows it
+  if (kDense[variant].decode && variant <= 3 && !p.a_vec) variant += 3;
+  const DenseVariant& v = kDense[variant];
+  const int64_t tiles = v.decode ? ceil_div(N, 16) : ceil_div(M, v.BM) * ceil_div(N, v.BN);
+  hipLaunchKernelGGL(v.fn, dim3((unsigned)tiles), dim3(v.threads), 0, stream, p);
   return hipGetLastError();
 }
 

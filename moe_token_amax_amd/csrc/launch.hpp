@@ -17,11 +17,10 @@ hipError_t launch_prepack(const int8_t* w, int64_t E, int64_t N, int64_t K, void
 // Output kinds of the GEMM kernels.
 enum OutKind { kOutBf16 = 0, kOutI32 = 1 };
 
-// Dense GEMM plan: kernel variant and split-K factor chosen from the shape.
+// Dense GEMM plan: kernel variant chosen from the shape.
 struct DensePlan {
-  int variant;   // index into the dense kernel table
-  int split;     // number of K slices (1 = fused epilogue, no workspace)
-  int64_t ws_bytes;
+  int variant;       // index into the dense kernel table
+  int64_t ws_bytes;  // device workspace the variant needs (0 for every variant today)
 };
 DensePlan plan_dense(int64_t M, int64_t N, int64_t K);
 hipError_t launch_dense_gemm(const DensePlan& plan, const int8_t* q, const float* x_scale, int64_t M,

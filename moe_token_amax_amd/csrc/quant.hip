@@ -71,6 +71,60 @@ __global__ __launch_bounds__(256) void quant_rows_vec(const uint16_t* __restrict
   }
 }
 
+// Few rows (decode-sized M): one 1024-thread workgroup per row, so the row's
+// divisions spread over 16 wavefronts instead of one. The amax is reduced per
+// wavefront with DPP, then across the 16 wavefronts through LDS.
+constexpr int kRowBlock = 1024;
+
+template <int CPL>
+__global__ __launch_bounds__(kRowBlock) void quant_rows_block(const uint16_t* __restrict__ x,
+                                                              int64_t M, int64_t K,
+                                                              int8_t* __restrict__ q,
+                                                              float* __restrict__ scale) {
+  __shared__ uint32_t wave_max[kRowBlock / kWave];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t row = blockIdx.x;
+  const int nchunk = (int)(K >> 3);
+  const uint4* xr = reinterpret_cast<const uint4*>(x + row * K);
+  uint4 v[CPL];
+  uint32_t amax = 0;
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) {
+    const int c = tid + i * kRowBlock;
+    if (c < nchunk) {
+      v[i] = xr[c];
+      amax = max(amax, max(max(abs_bf16_pair_max(v[i].x), abs_bf16_pair_max(v[i].y)),
+                           max(abs_bf16_pair_max(v[i].z), abs_bf16_pair_max(v[i].w))));
+    }
+  }
+  amax = wave_max_u32(amax);
+  if (lane == 0) wave_max[wave] = amax;
+  __syncthreads();
+  amax = wave_max[0];
+#pragma unroll
+  for (int w = 1; w < kRowBlock / kWave; ++w) amax = max(amax, wave_max[w]);
+  const float s = bf16_to_f32(amax) / 127.0f;
+  if (tid == 0) scale[row] = s;
+  uint2* qr = reinterpret_cast<uint2*>(q + row * K);
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) {
+    const int c = tid + i * kRowBlock;
+    if (c < nchunk) {
+      const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+      int code[8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        code[2 * j] = quant_code(bf16_to_f32(w[j] & 0xFFFFu), s);
+        code[2 * j + 1] = quant_code(bf16_to_f32(w[j] >> 16), s);
+      }
+      uint2 o;
+      o.x = pack4(code[0], code[1], code[2], code[3]);
+      o.y = pack4(code[4], code[5], code[6], code[7]);
+      qr[c] = o;
+    }
+  }
+}
+
 __global__ __launch_bounds__(256) void quant_rows_generic(const uint16_t* __restrict__ x, int64_t M,
                                                           int64_t K, int8_t* __restrict__ q,
                                                           float* __restrict__ scale) {
@@ -172,7 +226,15 @@ hipError_t launch_dynamic_quant(const uint16_t* x, int64_t M, int64_t K, int8_t*
   const dim3 grid((unsigned)((M + kRowsPerBlock - 1) / kRowsPerBlock)), block(256);
   const bool vec = (K % 8 == 0) && aligned(x, 16) && aligned(q, 8);
   const int64_t chunks = K / 8;
-  if (vec && chunks <= 64 * 1)
+  if (vec && M <= 512 && chunks <= 2 * kRowBlock) {
+    // few rows: a whole workgroup per row
+    if (chunks <= kRowBlock)
+      hipLaunchKernelGGL(quant_rows_block<1>, dim3((unsigned)M), dim3(kRowBlock), 0, stream, x, M,
+                         K, q, scale);
+    else
+      hipLaunchKernelGGL(quant_rows_block<2>, dim3((unsigned)M), dim3(kRowBlock), 0, stream, x, M,
+                         K, q, scale);
+  } else if (vec && chunks <= 64 * 1)
     hipLaunchKernelGGL(quant_rows_vec<1>, grid, block, 0, stream, x, M, K, q, scale);
   else if (vec && chunks <= 64 * 2)
     hipLaunchKernelGGL(quant_rows_vec<2>, grid, block, 0, stream, x, M, K, q, scale);
