@@ -205,6 +205,200 @@ struct Tile {
 };
 
 // ---------------------------------------------------------------------------
+// LDS-DMA pipelined tile (K % 16 == 0 and 16-byte aligned activations).
+//
+// Four wavefronts (2 x 2), each owning a (BM/2) x (BN/2) block of 16x16 INT32
+// accumulators. K advances one 64-deep k-block per stage through a ring of
+// STAGES LDS buffers filled by global_load_lds_dwordx4: the data goes from
+// L2 straight into LDS with no VGPR staging, and lane l of the instruction
+// lands at byte 16*l of a 1 KB block, i.e. already in MFMA operand order (A:
+// row l%16, k-chunk l/16; B: the prepacked block). STAGES-1 k-blocks are in
+// flight while one is consumed. Every stage ends with
+// "s_waitcnt vmcnt(<loads of later stages>) lgkmcnt(0); s_barrier": the
+// wavefront's own loads of the stage it is about to read have landed, its
+// LDS reads of the previous stage are done, and every other wavefront got
+// that far too, so the buffer refilled next is free.
+//
+// Reads that would leave the operands are clamped to valid addresses instead
+// of being masked: an A row past the tile's last row reads that last row (it
+// only feeds output rows that are never stored), an A column past K reads the
+// last 16 bytes of the row (multiplied by the zero padding of the weight), and
+// an n-block past the weight's last one reads the last block (it only feeds
+// columns >= N, never stored).
+// ---------------------------------------------------------------------------
+#define W8A8_LDS __attribute__((address_space(3)))
+
+template <int VM>
+__device__ __forceinline__ void wait_vm_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(VM) : "memory");
+}
+
+template <int BM, int BN, int STAGES>
+struct DmaTile {
+  static constexpr int kWaves = 4, WM = 2, WN = 2;
+  static constexpr int TM = BM / WM / 16;
+  static constexpr int TN = BN / WN / 16;
+  static constexpr int kABlocks = BM / 16;
+  static constexpr int kBBlocks = BN / 16;
+  static constexpr int kBlocks = kABlocks + kBBlocks;
+  static constexpr int kPerWave = kBlocks / kWaves;
+  static constexpr int kStageBytes = kBlocks * kBlockBytes;
+  static constexpr int kLdsBytes = STAGES * kStageBytes;
+  static_assert(kBlocks % kWaves == 0 && TM >= 1 && TN >= 1, "tile shape");
+  static_assert(STAGES >= 2 && STAGES <= 4, "stages");
+  static_assert((STAGES - 2) * kPerWave <= 63, "vmcnt range");
+
+  // Issues the DMA loads of k-block kb into ring buffer `buf`.
+  __device__ __forceinline__ static void issue(const GemmArgs& p, uint8_t* smem, int buf, int kb,
+                                               int wave, int lane, int64_t row0, int64_t row_last,
+                                               int64_t wblk0, int nb0) {
+#pragma unroll
+    for (int i = 0; i < kPerWave; ++i) {
+      const int bi = wave * kPerWave + i;  // wave-uniform
+      const void* src;
+      if (bi < kABlocks) {
+        int64_t row = row0 + bi * 16 + (lane & 15);
+        row = row < row_last ? row : row_last;
+        int64_t col = (int64_t)kb * 64 + (lane >> 4) * 16;
+        col = col < p.K - 16 ? col : p.K - 16;
+        src = p.a + row * p.K + col;
+      } else {
+        int nb = nb0 + (bi - kABlocks);
+        nb = nb < p.NB ? nb : p.NB - 1;
+        src = p.w + (wblk0 + (int64_t)nb * p.KB + kb) * kBlockBytes + lane * 16;
+      }
+      W8A8_LDS void* dst = (W8A8_LDS void*)((W8A8_LDS uint8_t*)smem + buf * kStageBytes +
+                                            bi * kBlockBytes);
+      __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+    }
+  }
+
+  __device__ __forceinline__ static void compute(const uint8_t* st, i32x4 (&acc)[TM][TN], int wm,
+                                                 int wn, int lane) {
+    i32x4 bf[TN];
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+      bf[j] = *reinterpret_cast<const i32x4*>(st + (kABlocks + wn * TN + j) * kBlockBytes + lane * 16);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const i32x4 af =
+          *reinterpret_cast<const i32x4*>(st + (wm * TM + i) * kBlockBytes + lane * 16);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) acc[i][j] = mfma16x16x64(af, bf[j], acc[i][j]);
+    }
+  }
+
+  __device__ __forceinline__ static void wait_stage(int later) {
+    // later = number of k-blocks issued after the one about to be consumed
+    if (STAGES >= 4 && later >= 2) wait_vm_barrier<(STAGES >= 4 ? 2 : 0) * kPerWave>();
+    else if (STAGES >= 3 && later >= 1) wait_vm_barrier<(STAGES >= 3 ? 1 : 0) * kPerWave>();
+    else wait_vm_barrier<0>();
+  }
+
+  // Full K loop: rows [row0, row_end) (row_end > row0), weights of expert e from
+  // n-block nb0. The caller's previous use of smem must be finished (the loop
+  // ends with every wavefront past its last LDS read, see mainloop's tail).
+  __device__ __forceinline__ static void mainloop(const GemmArgs& p, uint8_t* smem,
+                                                  i32x4 (&acc)[TM][TN], int64_t row0,
+                                                  int64_t row_end, int e, int nb0) {
+    const int lane = threadIdx.x & 63;
+    // wave index as a scalar: the per-wave choice between A and B blocks in
+    // issue() becomes a uniform branch and the LDS destination an SGPR (M0)
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave / WN, wn = wave % WN;
+    const int64_t wblk0 = (int64_t)e * p.NB * p.KB;
+    const int64_t row_last = row_end - 1;
+    const int KB = p.KB;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) acc[i][j] = i32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int s = 0; s < STAGES - 1; ++s)
+      if (s < KB) issue(p, smem, s, s, wave, lane, row0, row_last, wblk0, nb0);
+    for (int kb = 0; kb < KB; ++kb) {
+      const int ahead = KB - 1 - kb;
+      wait_stage(ahead < STAGES - 2 ? ahead : STAGES - 2);
+      const int nk = kb + STAGES - 1;
+      if (nk < KB) issue(p, smem, nk % STAGES, nk, wave, lane, row0, row_last, wblk0, nb0);
+      compute(smem + (kb % STAGES) * kStageBytes, acc, wm, wn, lane);
+    }
+    // all LDS reads of this tile done in every wavefront before smem is reused
+    wait_vm_barrier<0>();
+  }
+
+  __device__ __forceinline__ static void epilogue(const GemmArgs& p, const i32x4 (&acc)[TM][TN],
+                                                  int64_t row0, int64_t row_end, int e,
+                                                  int64_t n0) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int wm = wave / WN, wn = wave % WN;
+    const float* wsc = p.w_scale + (int64_t)e * p.N;
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int64_t n = n0 + (wn * TN + j) * 16 + (lane & 15);
+      if (n >= p.N) continue;
+      const float ws = wsc[n];
+      const float b = p.bias ? bf16_to_f32(p.bias[n]) : 0.0f;
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int64_t m = row0 + (wm * TM + i) * 16 + (lane >> 4) * 4 + t;
+          if (m >= row_end) continue;
+          const int32_t v = acc[i][j][t];
+          if (p.out == kOutI32) {
+            reinterpret_cast<int32_t*>(p.y)[m * p.N + n] = v;
+          } else {
+            float f = (float)v;
+            f = f * p.a_scale[m];
+            f = f * ws;
+            if (p.bias) f = f + b;
+            reinterpret_cast<uint16_t*>(p.y)[m * p.N + n] = (uint16_t)f32_to_bf16(f);
+          }
+        }
+      }
+    }
+  }
+};
+
+// Tile index -> (tm, tn). Workgroup w runs on XCD w % 8 (round-robin
+// dispatch), so each XCD is given a contiguous range of tile indices, and
+// inside a range tiles go GROUP_M m-rows at a time: the tiles an XCD runs
+// together share A rows and weight columns in that XCD's L2.
+template <int GROUP_M>
+__device__ __forceinline__ bool xcd_tile(int64_t w, int64_t MT, int64_t NT, int64_t& tm,
+                                         int64_t& tn) {
+  const int64_t T = MT * NT;
+  const int64_t per = (T + 7) / 8;
+  const int64_t t = (w % 8) * per + w / 8;
+  if (t >= T) return false;
+  const int64_t in_group = (int64_t)GROUP_M * NT;
+  const int64_t g = t / in_group;
+  const int64_t first_m = g * GROUP_M;
+  const int64_t gm = MT - first_m < GROUP_M ? MT - first_m : GROUP_M;
+  const int64_t r = t % in_group;
+  tm = first_m + r % gm;
+  tn = r / gm;
+  return true;
+}
+
+template <int BM, int BN, int STAGES, int GROUP_M>
+__global__ __launch_bounds__(256) void dense_dma_kernel(GemmArgs p) {
+  using T = DmaTile<BM, BN, STAGES>;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[T::kLdsBytes];
+  const int64_t MT = (p.M + BM - 1) / BM, NT = (p.N + BN - 1) / BN;
+  // grid = 8 * ceil(MT*NT / 8): a few workgroups of the last XCD range may be idle
+  int64_t tm, tn;
+  if (!xcd_tile<GROUP_M>(blockIdx.x, MT, NT, tm, tn)) return;
+  const int64_t row0 = tm * BM;
+  const int64_t row_end = min(row0 + BM, p.M);
+  i32x4 acc[T::TM][T::TN];
+  T::mainloop(p, smem, acc, row0, row_end, 0, (int)(tn * BN / 16));
+  T::epilogue(p, acc, row0, row_end, 0, tn * BN);
+}
+
+// ---------------------------------------------------------------------------
 // dense kernel (M > 64): grid.x = tiles, n fastest
 // ---------------------------------------------------------------------------
 template <int BM, int BN, int WM, int WN, int BKB>
@@ -411,7 +605,7 @@ struct DenseVariant {
 
 constexpr int kDecodeWaves = 8;
 
-// 0: M > 64: 128x128 tiles, 4 waves of 64x64, two k-blocks per LDS stage
+// 0: M > 64 fallback (K % 16 != 0 or unaligned A): 128x128 tiles, VGPR-staged
 // 1..3: M <= 16 / 32 / 64: decode kernel with 1 / 2 / 4 m-blocks
 // 4..6: the same for K % 16 != 0 or an unaligned activation pointer
 const DenseVariant kDense[] = {
@@ -468,6 +662,15 @@ hipError_t launch_dense_gemm(const DensePlan& plan, const int8_t* q, const float
   int variant = plan.variant;
   // the decode kernels load A rows with 16-byte loads when the pointer allows it
   if (kDense[variant].decode && variant <= 3 && !p.a_vec) variant += 3;
+  if (variant == 0 && p.a_vec) {
+    // prefill-sized M: 256x256 tiles through the LDS-DMA ring
+    constexpr int BM = 256, BN = 256;
+    const int64_t tiles = ceil_div(M, BM) * ceil_div(N, BN);
+    const int64_t grid = round_up(tiles, 8);
+    hipLaunchKernelGGL((dense_dma_kernel<BM, BN, 4, 8>), dim3((unsigned)grid), dim3(256), 0, stream,
+                       p);
+    return hipGetLastError();
+  }
   const DenseVariant& v = kDense[variant];
   const int64_t tiles = v.decode ? ceil_div(N, 16) : ceil_div(M, v.BM) * ceil_div(N, v.BN);
   hipLaunchKernelGGL(v.fn, dim3((unsigned)tiles), dim3(v.threads), 0, stream, p);

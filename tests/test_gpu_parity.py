@@ -95,6 +95,12 @@ LINEAR_SHAPES = [  # M, K, N, bias
     (16, 256, 128, True), (1, 64, 16, False), (17, 100, 50, True), (3, 37, 5, False),
     (33, 448, 96, True), (64, 1024, 192, False), (129, 320, 144, True), (300, 512, 260, False),
     (4, 7168, 512, False), (16, 7168, 256, True),
+    # prefill-sized M (LDS-DMA tiles): ragged K (K % 64 != 0), tiny K, N tails,
+    # a single partial 256-row tile, several tiles in both directions
+    (100, 80, 300, True), (65, 16, 40, False), (257, 4096, 512, True), (520, 1088, 600, False),
+    (96, 48, 16, True),
+    # prefill-sized M with K % 16 != 0 (VGPR-staged fallback)
+    (65, 100, 50, True), (200, 37, 33, False),
 ]
 
 
