@@ -16,6 +16,9 @@ resident, seeded synthetic inputs:
            T = 2048 tokens routed top-8 over 256 experts, H = 4096, I = 2048.
            value = tokens / step time (tokens/s).
   tiny     quant + INT8 linear, 16 x 256 x 128 with bias (latency case).
+  copy     a plain 512 MiB device-to-device copy (torch's copy kernel): the
+           measured HBM ceiling, and the reference dispatch that scales the
+           FETCH_SIZE / WRITE_SIZE counters (it moves exactly 2 x 512 MiB).
 
 Every step is captured once as a HIP graph (the C ABI calls only enqueue
 kernels) and replayed, so host-side Python does not pace the GPU. The average
@@ -46,7 +49,8 @@ def _args():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="decode", choices=["decode", "prefill", "moe", "tiny"])
+    ap.add_argument("--workload", default="decode",
+                    choices=["decode", "prefill", "moe", "tiny", "copy"])
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="approximate budget of the oracle timing on the host")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -335,6 +339,46 @@ class MoeWorkload(Workload):
                            f"weights drawn per expert inside the timing), tokens = rows / top_k")
 
 
+class CopyWorkload(Workload):
+    """512 MiB device copy: HBM reference, not part of the W8A8 path."""
+    NBYTES = 512 << 20
+
+    def __init__(self, w, torch):
+        super().__init__(w, torch)
+        self.name = "copy"
+        self.src = torch.empty((self.NBYTES,), dtype=torch.uint8, device="cuda").fill_(1)
+        self.dst = torch.empty_like(self.src)
+        self.unit = "GB/s"
+        self.bound = "hbm"
+        self.capture([self._copy], [(self._copy, 1, "copy")])
+
+    def _copy(self):
+        self.dst.copy_(self.src)
+
+    def value(self, sec_per_step):
+        return 2 * self.NBYTES / sec_per_step / 1e9
+
+    def dominant(self, per_key_ms):
+        ach = 2 * self.NBYTES / (per_key_ms["copy"] * 1e-3) / 1e9
+        return dict(bound="hbm", achieved=ach, peak=PEAK_HBM_GBS, unit="GB/s",
+                    frac=ach / PEAK_HBM_GBS)
+
+    def config(self):
+        return {"workload": "copy", "bytes": self.NBYTES, "kernel": "torch device copy"}
+
+    def cpu_baseline(self, budget_s):
+        import numpy as np
+        a = np.ones(self.NBYTES, np.uint8)
+        b = np.empty_like(a)
+        t0 = time.perf_counter()
+        n = 0
+        while time.perf_counter() - t0 < min(budget_s, 3.0):
+            np.copyto(b, a)
+            n += 1
+        dt = (time.perf_counter() - t0) / n
+        return dict(value=2 * self.NBYTES / dt / 1e9, unit="GB/s", sample="numpy copy of 512 MiB")
+
+
 # ---------------------------------------------------------------------------
 
 def _blas_threads():
@@ -365,6 +409,8 @@ def main():
         wl = DenseWorkload(w, torch, "prefill", [8192], 7168, 4096, True, 0.005, 2)
     elif args.workload == "tiny":
         wl = DenseWorkload(w, torch, "tiny", [16], 256, 128, True, 0.01, 1)
+    elif args.workload == "copy":
+        wl = CopyWorkload(w, torch)
     else:
         wl = MoeWorkload(w, torch)
 

@@ -233,10 +233,24 @@ __device__ __forceinline__ void wait_vm_barrier() {
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(VM) : "memory");
 }
 
-template <int BM, int BN, int STAGES>
+#ifndef W8A8_DMA_STAGES
+#define W8A8_DMA_STAGES 4
+#endif
+#ifndef W8A8_DMA_GROUP_M
+#define W8A8_DMA_GROUP_M 8
+#endif
+#ifndef W8A8_DMA_WM
+#define W8A8_DMA_WM 2
+#endif
+#ifndef W8A8_DMA_WN
+#define W8A8_DMA_WN 4
+#endif
+
+template <int BM, int BN, int STAGES, int WM, int WN>
 struct DmaTile {
-  static constexpr int kWaves = 4, WM = 2, WN = 2;
-  static constexpr int TM = BM / WM / 16;
+  static constexpr int kWaves = WM * WN;
+  static constexpr int kThreads = kWaves * kWave;
+  static constexpr int TM = BM / WM / 16;  // 16x16 accumulator blocks per wavefront
   static constexpr int TN = BN / WN / 16;
   static constexpr int kABlocks = BM / 16;
   static constexpr int kBBlocks = BN / 16;
@@ -244,89 +258,154 @@ struct DmaTile {
   static constexpr int kPerWave = kBlocks / kWaves;
   static constexpr int kStageBytes = kBlocks * kBlockBytes;
   static constexpr int kLdsBytes = STAGES * kStageBytes;
-  static_assert(kBlocks % kWaves == 0 && TM >= 1 && TN >= 1, "tile shape");
-  static_assert(STAGES >= 2 && STAGES <= 4, "stages");
+  static_assert(kBlocks % kWaves == 0 && TM >= 2 && TM % 2 == 0 && TN >= 1, "tile shape");
+  static_assert(STAGES >= 3 && STAGES <= 5, "stages");
   static_assert((STAGES - 2) * kPerWave <= 63, "vmcnt range");
 
-  // Issues the DMA loads of k-block kb into ring buffer `buf`.
-  __device__ __forceinline__ static void issue(const GemmArgs& p, uint8_t* smem, int buf, int kb,
-                                               int wave, int lane, int64_t row0, int64_t row_last,
-                                               int64_t wblk0, int nb0) {
+  // Per-tile DMA sources of this wavefront's kPerWave blocks: the address of
+  // k-block 0 and the step per k-block (64 bytes along an A row, 1 KB through
+  // the packed weight). Block bi < kABlocks is A rows [16*bi, 16*bi + 16).
+  struct Src {
+    const uint8_t* base[kPerWave];
+    int64_t step[kPerWave];
+  };
+
+  // The LDS fragments one wavefront reads from a stage: TN B blocks, TM A blocks.
+  struct Frags {
+    i32x4 b[TN];
+    i32x4 a[TM];
+  };
+
+  __device__ __forceinline__ static void sources(const GemmArgs& p, Src& s, int wave, int lane,
+                                                 int64_t row0, int64_t row_last, int64_t wblk0,
+                                                 int nb0) {
 #pragma unroll
     for (int i = 0; i < kPerWave; ++i) {
       const int bi = wave * kPerWave + i;  // wave-uniform
-      const void* src;
       if (bi < kABlocks) {
         int64_t row = row0 + bi * 16 + (lane & 15);
         row = row < row_last ? row : row_last;
-        int64_t col = (int64_t)kb * 64 + (lane >> 4) * 16;
-        col = col < p.K - 16 ? col : p.K - 16;
-        src = p.a + row * p.K + col;
+        s.base[i] = reinterpret_cast<const uint8_t*>(p.a) + row * p.K + (lane >> 4) * 16;
+        s.step[i] = 64;
       } else {
         int nb = nb0 + (bi - kABlocks);
         nb = nb < p.NB ? nb : p.NB - 1;
-        src = p.w + (wblk0 + (int64_t)nb * p.KB + kb) * kBlockBytes + lane * 16;
+        s.base[i] = p.w + (wblk0 + (int64_t)nb * p.KB) * kBlockBytes + lane * 16;
+        s.step[i] = kBlockBytes;
       }
-      W8A8_LDS void* dst = (W8A8_LDS void*)((W8A8_LDS uint8_t*)smem + buf * kStageBytes +
-                                            bi * kBlockBytes);
-      __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
     }
   }
 
-  __device__ __forceinline__ static void compute(const uint8_t* st, i32x4 (&acc)[TM][TN], int wm,
-                                                 int wn, int lane) {
-    i32x4 bf[TN];
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-      bf[j] = *reinterpret_cast<const i32x4*>(st + (kABlocks + wn * TN + j) * kBlockBytes + lane * 16);
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      const i32x4 af =
-          *reinterpret_cast<const i32x4*>(st + (wm * TM + i) * kBlockBytes + lane * 16);
-#pragma unroll
-      for (int j = 0; j < TN; ++j) acc[i][j] = mfma16x16x64(af, bf[j], acc[i][j]);
+  // DMA of block i (of this wavefront) of k-block kb into ring buffer buf.
+  __device__ __forceinline__ static void issue_one(const GemmArgs& p, const Src& s, uint8_t* smem,
+                                                   int buf, int kb, int wave, int lane, int i) {
+    const int bi = wave * kPerWave + i;
+    const uint8_t* src = s.base[i] + kb * s.step[i];
+    if (bi < kABlocks && (p.K & 63) && kb == p.KB - 1) {
+      // last k-block of a ragged K: keep the 16 bytes inside the row
+      const int64_t col = (int64_t)kb * 64 + (lane >> 4) * 16;
+      if (col > p.K - 16) src -= col - (p.K - 16);
     }
+    W8A8_LDS void* dst =
+        (W8A8_LDS void*)((W8A8_LDS uint8_t*)smem + buf * kStageBytes + bi * kBlockBytes);
+    __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
   }
 
+  // later = k-blocks issued after the one about to be read (<= STAGES - 2):
+  // their loads may stay in flight
   __device__ __forceinline__ static void wait_stage(int later) {
-    // later = number of k-blocks issued after the one about to be consumed
-    if (STAGES >= 4 && later >= 2) wait_vm_barrier<(STAGES >= 4 ? 2 : 0) * kPerWave>();
-    else if (STAGES >= 3 && later >= 1) wait_vm_barrier<(STAGES >= 3 ? 1 : 0) * kPerWave>();
+    if (STAGES >= 5 && later >= 3) wait_vm_barrier<(STAGES >= 5 ? 3 : 0) * kPerWave>();
+    else if (STAGES >= 4 && later >= 2) wait_vm_barrier<(STAGES >= 4 ? 2 : 0) * kPerWave>();
+    else if (later >= 1) wait_vm_barrier<kPerWave>();
     else wait_vm_barrier<0>();
   }
 
+  __device__ __forceinline__ static void read_frags(const uint8_t* st, Frags& f, int wm, int wn,
+                                                    int lane) {
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+      f.b[j] = *reinterpret_cast<const i32x4*>(st + (kABlocks + wn * TN + j) * kBlockBytes +
+                                               lane * 16);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+      f.a[i] = *reinterpret_cast<const i32x4*>(st + (wm * TM + i) * kBlockBytes + lane * 16);
+  }
+
+  __device__ __forceinline__ static void mfma_row(const Frags& f, i32x4 (&acc)[TM][TN], int i) {
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = mfma16x16x64(f.a[i], f.b[j], acc[i][j]);
+  }
+
   // Full K loop: rows [row0, row_end) (row_end > row0), weights of expert e from
-  // n-block nb0. The caller's previous use of smem must be finished (the loop
-  // ends with every wavefront past its last LDS read, see mainloop's tail).
+  // n-block nb0. Ends with every wavefront past its last LDS read of smem.
+  //
+  // Software pipeline of one k-block (stage) kb, with its fragments already in
+  // registers (F):
+  //   1. first half of the MFMA rows of F, with the DMA loads of k-block
+  //      kb + STAGES - 1 issued between the rows;
+  //   2. wait for this wavefront's loads of k-block kb + 1, s_barrier (so every
+  //      wavefront's loads of it landed and every read of the buffer about to
+  //      be refilled is done), then LDS reads of its fragments (G);
+  //   3. second half of the MFMA rows of F while those reads are in flight.
+  // With one wavefront per SIMD the LDS latency, the barrier and the DMA issue
+  // thus overlap the MFMAs instead of stalling them.
   __device__ __forceinline__ static void mainloop(const GemmArgs& p, uint8_t* smem,
                                                   i32x4 (&acc)[TM][TN], int64_t row0,
                                                   int64_t row_end, int e, int nb0) {
     const int lane = threadIdx.x & 63;
-    // wave index as a scalar: the per-wave choice between A and B blocks in
-    // issue() becomes a uniform branch and the LDS destination an SGPR (M0)
+    // wave index as a scalar: per-wave choices are uniform branches and the
+    // LDS destination of every DMA is an SGPR (M0)
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = wave / WN, wn = wave % WN;
     const int64_t wblk0 = (int64_t)e * p.NB * p.KB;
-    const int64_t row_last = row_end - 1;
     const int KB = p.KB;
+    Src src;
+    sources(p, src, wave, lane, row0, row_end - 1, wblk0, nb0);
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int j = 0; j < TN; ++j) acc[i][j] = i32x4{0, 0, 0, 0};
 #pragma unroll
     for (int s = 0; s < STAGES - 1; ++s)
-      if (s < KB) issue(p, smem, s, s, wave, lane, row0, row_last, wblk0, nb0);
+      if (s < KB) {
+#pragma unroll
+        for (int i = 0; i < kPerWave; ++i) issue_one(p, src, smem, s, s, wave, lane, i);
+      }
+    wait_stage(KB - 1 < STAGES - 2 ? KB - 1 : STAGES - 2);
+    Frags F;
+    read_frags(smem, F, wm, wn, lane);
     for (int kb = 0; kb < KB; ++kb) {
-      const int ahead = KB - 1 - kb;
-      wait_stage(ahead < STAGES - 2 ? ahead : STAGES - 2);
       const int nk = kb + STAGES - 1;
-      if (nk < KB) issue(p, smem, nk % STAGES, nk, wave, lane, row0, row_last, wblk0, nb0);
-      compute(smem + (kb % STAGES) * kStageBytes, acc, wm, wn, lane);
+      const bool more = nk < KB;
+      const int nbuf = nk % STAGES;
+      constexpr int H = TM / 2;
+#pragma unroll
+      for (int i = 0; i < H; ++i) {
+#pragma unroll
+        for (int d = (i * kPerWave) / H; d < ((i + 1) * kPerWave) / H; ++d)
+          if (more) issue_one(p, src, smem, nbuf, nk, wave, lane, d);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_row(F, acc, i);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      Frags G = F;
+      if (kb + 1 < KB) {
+        const int later = KB - 2 - kb;
+        wait_stage(later < STAGES - 2 ? later : STAGES - 2);
+        read_frags(smem + ((kb + 1) % STAGES) * kStageBytes, G, wm, wn, lane);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = H; i < TM; ++i) mfma_row(F, acc, i);
+      __builtin_amdgcn_sched_barrier(0);
+      F = G;
     }
     // all LDS reads of this tile done in every wavefront before smem is reused
     wait_vm_barrier<0>();
   }
 
+  // Output element of accumulator register v of block (i, j) for this lane:
+  // row 4*(l/16) + v, column l%16 of the 16x16 block.
   __device__ __forceinline__ static void epilogue(const GemmArgs& p, const i32x4 (&acc)[TM][TN],
                                                   int64_t row0, int64_t row_end, int e,
                                                   int64_t n0) {
@@ -343,14 +422,14 @@ struct DmaTile {
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const int64_t m = row0 + (wm * TM + i) * 16 + (lane >> 4) * 4 + t;
+        for (int v = 0; v < 4; ++v) {
+          const int64_t m = row0 + (wm * TM + i) * 16 + (lane >> 4) * 4 + v;
           if (m >= row_end) continue;
-          const int32_t v = acc[i][j][t];
+          const int32_t val = acc[i][j][v];
           if (p.out == kOutI32) {
-            reinterpret_cast<int32_t*>(p.y)[m * p.N + n] = v;
+            reinterpret_cast<int32_t*>(p.y)[m * p.N + n] = val;
           } else {
-            float f = (float)v;
+            float f = (float)val;
             f = f * p.a_scale[m];
             f = f * ws;
             if (p.bias) f = f + b;
@@ -383,9 +462,9 @@ __device__ __forceinline__ bool xcd_tile(int64_t w, int64_t MT, int64_t NT, int6
   return true;
 }
 
-template <int BM, int BN, int STAGES, int GROUP_M>
-__global__ __launch_bounds__(256) void dense_dma_kernel(GemmArgs p) {
-  using T = DmaTile<BM, BN, STAGES>;
+template <int BM, int BN, int STAGES, int GROUP_M, int WM, int WN>
+__global__ __launch_bounds__(WM* WN* kWave) void dense_dma_kernel(GemmArgs p) {
+  using T = DmaTile<BM, BN, STAGES, WM, WN>;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[T::kLdsBytes];
   const int64_t MT = (p.M + BM - 1) / BM, NT = (p.N + BN - 1) / BN;
   // grid = 8 * ceil(MT*NT / 8): a few workgroups of the last XCD range may be idle
@@ -667,8 +746,9 @@ hipError_t launch_dense_gemm(const DensePlan& plan, const int8_t* q, const float
     constexpr int BM = 256, BN = 256;
     const int64_t tiles = ceil_div(M, BM) * ceil_div(N, BN);
     const int64_t grid = round_up(tiles, 8);
-    hipLaunchKernelGGL((dense_dma_kernel<BM, BN, 4, 8>), dim3((unsigned)grid), dim3(256), 0, stream,
-                       p);
+    hipLaunchKernelGGL(
+        (dense_dma_kernel<BM, BN, W8A8_DMA_STAGES, W8A8_DMA_GROUP_M, W8A8_DMA_WM, W8A8_DMA_WN>),
+        dim3((unsigned)grid), dim3(64 * W8A8_DMA_WM * W8A8_DMA_WN), 0, stream, p);
     return hipGetLastError();
   }
   const DenseVariant& v = kDense[variant];
