@@ -124,7 +124,9 @@ int w8a8_linear(const int8_t* q, const float* x_scale, int64_t M, int64_t K,
  *   w_packed   device, packed [E, N, K] weight
  *   w_scale    device, float [E, N]
  *   y          device, [R, N]; BF16 bits or int32 as for w8a8_linear
- * Experts with n_e == 0 cost no work. No bias.
+ *   workspace  device scratch of w8a8_grouped_workspace_bytes(R, E, N, K)
+ *              bytes, 256-byte aligned (per-expert row and tile offsets)
+ * Experts with n_e == 0 cost no work. No bias. E <= 1024.
  */
 int64_t w8a8_grouped_workspace_bytes(int64_t R, int64_t E, int64_t N, int64_t K);
 int w8a8_grouped_gemm(const int8_t* a, const float* a_scale,

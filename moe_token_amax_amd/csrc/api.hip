@@ -157,8 +157,9 @@ int w8a8_grouped_gemm(const int8_t* a, const float* a_scale, const int64_t* grou
       !aligned(group_list, 8))
     return fail(W8A8_ERR_ALIGN, "grouped_gemm: misaligned buffer");
   const int64_t need = w8a8::grouped_ws_bytes(R, E, N, K);
-  if (need > 0 && (!workspace || ws_bytes < need))
-    return fail(W8A8_ERR_WORKSPACE, "grouped_gemm: needs %lld workspace bytes", (long long)need);
+  if (need > 0 && (!workspace || ws_bytes < need || !aligned(workspace, 256)))
+    return fail(W8A8_ERR_WORKSPACE, "grouped_gemm: needs %lld workspace bytes (256-byte aligned), got %lld",
+                (long long)need, (long long)ws_bytes);
   return launched(w8a8::launch_grouped_gemm(a, a_scale, group_list, R, E, N, K, w_packed, w_scale, y,
                                             out, workspace, (hipStream_t)stream),
                   "grouped_gemm");

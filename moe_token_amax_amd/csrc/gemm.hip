@@ -331,7 +331,12 @@ struct DmaTile {
       f.a[i] = *reinterpret_cast<const i32x4*>(st + (wm * TM + i) * kBlockBytes + lane * 16);
   }
 
-  __device__ __forceinline__ static void mfma_row(const Frags& f, i32x4 (&acc)[TM][TN], int i) {
+  // Row i of this wavefront's blocks; skipped (wave-uniform) when the 16-row
+  // block lies past the tile's last valid row, so a short tile (the last
+  // m-tile of an expert) costs MFMA time for its valid 16-row blocks only.
+  __device__ __forceinline__ static void mfma_row(const Frags& f, i32x4 (&acc)[TM][TN], int i,
+                                                  int row_blocks) {
+    if (i >= row_blocks) return;
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = mfma16x16x64(f.a[i], f.b[j], acc[i][j]);
   }
@@ -359,6 +364,9 @@ struct DmaTile {
     const int wm = wave / WN, wn = wave % WN;
     const int64_t wblk0 = (int64_t)e * p.NB * p.KB;
     const int KB = p.KB;
+    // 16-row blocks of this wavefront that hold valid rows (wave-uniform)
+    const int64_t valid = row_end - row0 - (int64_t)wm * TM * 16;
+    const int row_blocks = valid <= 0 ? 0 : (valid >= TM * 16 ? TM : (int)((valid + 15) / 16));
     Src src;
     sources(p, src, wave, lane, row0, row_end - 1, wblk0, nb0);
 #pragma unroll
@@ -385,7 +393,7 @@ struct DmaTile {
         for (int d = (i * kPerWave) / H; d < ((i + 1) * kPerWave) / H; ++d)
           if (more) issue_one(p, src, smem, nbuf, nk, wave, lane, d);
         __builtin_amdgcn_sched_barrier(0);
-        mfma_row(F, acc, i);
+        mfma_row(F, acc, i, row_blocks);
         __builtin_amdgcn_sched_barrier(0);
       }
       Frags G = F;
@@ -396,7 +404,7 @@ struct DmaTile {
       }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int i = H; i < TM; ++i) mfma_row(F, acc, i);
+      for (int i = H; i < TM; ++i) mfma_row(F, acc, i, row_blocks);
       __builtin_amdgcn_sched_barrier(0);
       F = G;
     }
@@ -592,6 +600,200 @@ __global__ __launch_bounds__(WM* WN* kWave) void grouped_gemm_kernel(GemmArgs p)
 }
 
 // ---------------------------------------------------------------------------
+// Grouped GEMM, fast path (K % 16 == 0, 16-byte aligned rows).
+//
+// The row counts are skewed: with top-8 routing over 256 experts most
+// non-empty experts own a handful of rows while a few own thousands. The two
+// kinds are served by two kernels that read one schedule:
+//   * experts with at most kSmallRows rows: weight streaming, like the decode
+//     kernel; every wavefront owns one 16-column block of one expert over the
+//     full K, so each weight byte is read once and no MFMA tile is padded to
+//     256 rows;
+//   * larger experts: 256 x 256 LDS-DMA tiles, walked persistently.
+// ---------------------------------------------------------------------------
+constexpr int kSmallRows = 64;
+constexpr int kGroupBM = 256, kGroupBN = 256;
+
+// Schedule in the workspace: row_off[E + 1] (first row of each expert) and
+// tile_off[E + 1] (first m-tile of each large expert; small and empty experts
+// own none).
+struct GroupSched {
+  int64_t* row_off;
+  int* tile_off;
+};
+
+__host__ __device__ inline int64_t group_sched_bytes(int64_t E) {
+  return ((E + 1) * 8 + 255) / 256 * 256 + ((E + 1) * 4 + 255) / 256 * 256;
+}
+
+__host__ __device__ inline GroupSched group_sched(void* ws, int64_t E) {
+  GroupSched g;
+  g.row_off = reinterpret_cast<int64_t*>(ws);
+  g.tile_off = reinterpret_cast<int*>(reinterpret_cast<char*>(ws) + ((E + 1) * 8 + 255) / 256 * 256);
+  return g;
+}
+
+// One 1024-thread workgroup: each thread owns one expert (E <= 1024); the
+// exclusive scans of the row counts and of the large experts' m-tile counts
+// run as wavefront shfl_up scans combined through LDS.
+__global__ __launch_bounds__(1024) void group_schedule_kernel(const int64_t* __restrict__ gl, int E,
+                                                              GroupSched out) {
+  __shared__ int64_t wrows[16];
+  __shared__ int wtiles[16];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t n = tid < E ? max(gl[tid], (int64_t)0) : 0;  // a negative count owns no rows
+  const int t = n > kSmallRows ? (int)((n + kGroupBM - 1) / kGroupBM) : 0;
+  int64_t ri = n;
+  int ti = t;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int64_t ro = __shfl_up(ri, d, 64);
+    const int to = __shfl_up(ti, d, 64);
+    if (lane >= d) {
+      ri += ro;
+      ti += to;
+    }
+  }
+  if (lane == 63) {
+    wrows[wave] = ri;
+    wtiles[wave] = ti;
+  }
+  __syncthreads();
+  for (int w = 0; w < wave; ++w) {
+    ri += wrows[w];
+    ti += wtiles[w];
+  }
+  if (tid < E) {
+    out.row_off[tid] = ri - n;
+    out.tile_off[tid] = ti - t;
+  }
+  if (tid == E - 1) {
+    out.row_off[E] = ri;
+    out.tile_off[E] = ti;
+  }
+}
+
+// Rows [row0, row0 + rows) (rows <= 16 * MB) of expert e against n-block nb,
+// full K, one wavefront. UNR weight blocks (and their A fragments, read through
+// L1: the wavefronts of a workgroup share them) are in flight at once.
+template <int MB, int UNR>
+__device__ __forceinline__ void small_expert_block(const GemmArgs& p, int e, int64_t row0,
+                                                   int64_t rows, int nb, int lane) {
+  const uint8_t* wcol = p.w + ((int64_t)e * p.NB + nb) * p.KB * kBlockBytes + lane * 16;
+  const int KB = p.KB;
+  i32x4 acc[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) acc[mb] = i32x4{0, 0, 0, 0};
+  const int8_t* arow[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    // rows past the expert's last read that last row: they only feed output
+    // rows that are never stored
+    int64_t r = mb * 16 + (lane & 15);
+    r = r < rows ? r : rows - 1;
+    arow[mb] = p.a + (row0 + r) * p.K + (lane >> 4) * 16;
+  }
+  for (int kb0 = 0; kb0 < KB; kb0 += UNR) {
+    i32x4 b[UNR];
+    i32x4 a[UNR][MB];
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const int kb = kb0 + u < KB ? kb0 + u : KB - 1;  // clamped: loads stay in bounds
+      b[u] = *reinterpret_cast<const i32x4*>(wcol + (int64_t)kb * kBlockBytes);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+        a[u][mb] = *reinterpret_cast<const i32x4*>(arow[mb] + (int64_t)kb * 64);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // all loads of the round before the first MFMA
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      if (kb0 + u < KB) {  // wave-uniform: clamped duplicate blocks add nothing
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) acc[mb] = mfma16x16x64(a[u][mb], b[u], acc[mb]);
+      }
+    }
+  }
+  const int64_t n = (int64_t)nb * 16 + (lane & 15);
+  if (n >= p.N) return;
+  const float ws = p.w_scale[(int64_t)e * p.N + n];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int64_t m = mb * 16 + (lane >> 4) * 4 + t;
+      if (m >= rows) continue;
+      const int64_t row = row0 + m;
+      if (p.out == kOutI32) {
+        reinterpret_cast<int32_t*>(p.y)[row * p.N + n] = acc[mb][t];
+      } else {
+        float f = (float)acc[mb][t];
+        f = f * p.a_scale[row];
+        f = f * ws;
+        reinterpret_cast<uint16_t*>(p.y)[row * p.N + n] = (uint16_t)f32_to_bf16(f);
+      }
+    }
+  }
+}
+
+constexpr int kSmallWaves = 8;
+
+// grid = E * ceil(NB / 8): workgroup (e, g) covers n-blocks [8g, 8g + 8) of
+// expert e when e is small and non-empty, else returns at once.
+__global__ __launch_bounds__(kSmallWaves* kWave) void grouped_small_kernel(GemmArgs p,
+                                                                           GroupSched sc) {
+  const int groups = (p.NB + kSmallWaves - 1) / kSmallWaves;
+  const int e = blockIdx.x / groups;
+  const int g = blockIdx.x % groups;
+  const int64_t row0 = sc.row_off[e];
+  // counts that sum past R are a caller error: rows at or past R are never
+  // touched
+  const int64_t row_end = min(sc.row_off[e + 1], p.M);
+  const int64_t rows = row_end - row0;
+  if (rows <= 0 || sc.row_off[e + 1] - row0 > kSmallRows) return;
+  const int lane = threadIdx.x & 63;
+  const int nb = g * kSmallWaves + (threadIdx.x >> 6);
+  if (nb >= p.NB) return;
+  // (UNR x MB operand registers stay under the budget of 2 wavefronts per
+  // SIMD; larger unrolls get demoted to scratch memory)
+  if (rows <= 16) small_expert_block<1, 16>(p, e, row0, rows, nb, lane);
+  else if (rows <= 32) small_expert_block<2, 8>(p, e, row0, rows, nb, lane);
+  else small_expert_block<4, 4>(p, e, row0, rows, nb, lane);
+}
+
+// Persistent walk over the large experts' tiles, ordered (expert, n-tile,
+// m-tile) so that tiles running together share weight columns; each XCD
+// (workgroup b runs on XCD b % 8) takes one contiguous eighth of the list.
+template <int STAGES, int WM, int WN>
+__global__ __launch_bounds__(WM* WN* kWave) void grouped_tile_kernel(GemmArgs p, GroupSched sc) {
+  using T = DmaTile<kGroupBM, kGroupBN, STAGES, WM, WN>;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[T::kLdsBytes];
+  const int E = p.E;
+  const int64_t NT = (p.N + kGroupBN - 1) / kGroupBN;
+  const int64_t total = (int64_t)sc.tile_off[E] * NT;
+  const int64_t per = (total + 7) / 8;
+  const int64_t xcd = blockIdx.x % 8, wg_per_xcd = gridDim.x / 8;
+  const int64_t t_end = min((xcd + 1) * per, total);
+  for (int64_t t = xcd * per + blockIdx.x / 8; t < t_end; t += wg_per_xcd) {
+    // expert owning tile t: last e with tile_off[e] * NT <= t
+    int lo = 0, hi = E - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if ((int64_t)sc.tile_off[mid] * NT <= t) lo = mid; else hi = mid - 1;
+    }
+    const int e = lo;
+    const int64_t mtiles = sc.tile_off[e + 1] - sc.tile_off[e];
+    const int64_t local = t - (int64_t)sc.tile_off[e] * NT;
+    const int64_t tn = local / mtiles, mt = local % mtiles;
+    const int64_t row0 = sc.row_off[e] + mt * kGroupBM;
+    const int64_t row_end = min(sc.row_off[e + 1], p.M);
+    if (row0 >= row_end) continue;
+    i32x4 acc[T::TM][T::TN];
+    T::mainloop(p, smem, acc, row0, row_end, e, (int)(tn * kGroupBN / 16));
+    T::epilogue(p, acc, row0, row_end, e, tn * kGroupBN);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // decode kernel (M <= 64): weight-streaming GEMV-like path.
 // One workgroup owns one 16-column n-block over the full K; its WAVES
 // wavefronts take interleaved k-blocks (wave w: w, w + WAVES, ...) so that the
@@ -757,22 +959,37 @@ hipError_t launch_dense_gemm(const DensePlan& plan, const int8_t* q, const float
   return hipGetLastError();
 }
 
-int64_t grouped_ws_bytes(int64_t, int64_t, int64_t, int64_t) { return 0; }
+int64_t grouped_ws_bytes(int64_t, int64_t E, int64_t, int64_t) { return group_sched_bytes(E); }
 
 hipError_t launch_grouped_gemm(const int8_t* a, const float* a_scale, const int64_t* group_list,
                                int64_t R, int64_t E, int64_t N, int64_t K, const void* w_packed,
-                               const float* w_scale, void* y, int out, void*,
+                               const float* w_scale, void* y, int out, void* ws,
                                hipStream_t stream) {
   if (R == 0 || N == 0) return hipSuccess;
   GemmArgs p = make_args(a, a_scale, R, K, w_packed, w_scale, N, nullptr, y, out);
   p.group_list = group_list;
   p.E = (int)E;
-  constexpr int BM = 128, BN = 128;
-  // upper bound on tiles: sum_e ceil(n_e / BM) <= R / BM + E
-  const int64_t max_tiles = (ceil_div(R, BM) + E) * ceil_div(N, BN);
-  const int64_t grid = std::min<int64_t>(max_tiles, 256 * 4);
-  hipLaunchKernelGGL((grouped_gemm_kernel<BM, BN, 2, 2, 2>), dim3((unsigned)grid), dim3(256), 0,
-                     stream, p);
+  if (!p.a_vec) {
+    // K % 16 != 0 or unaligned rows: VGPR-staged tiles, schedule built in LDS
+    constexpr int BM = 128, BN = 128;
+    // upper bound on tiles: sum_e ceil(n_e / BM) <= R / BM + E
+    const int64_t max_tiles = (ceil_div(R, BM) + E) * ceil_div(N, BN);
+    const int64_t grid = std::min<int64_t>(max_tiles, 256 * 4);
+    hipLaunchKernelGGL((grouped_gemm_kernel<BM, BN, 2, 2, 2>), dim3((unsigned)grid), dim3(256), 0,
+                       stream, p);
+    return hipGetLastError();
+  }
+  const GroupSched sc = group_sched(ws, E);
+  hipLaunchKernelGGL(group_schedule_kernel, dim3(1), dim3(1024), 0, stream, group_list, (int)E, sc);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const int groups = (int)ceil_div(p.NB, kSmallWaves);
+  hipLaunchKernelGGL(grouped_small_kernel, dim3((unsigned)(E * groups)), dim3(kSmallWaves * 64), 0,
+                     stream, p, sc);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL((grouped_tile_kernel<W8A8_DMA_STAGES, W8A8_DMA_WM, W8A8_DMA_WN>), dim3(256),
+                     dim3(64 * W8A8_DMA_WM * W8A8_DMA_WN), 0, stream, p, sc);
   return hipGetLastError();
 }
 

@@ -177,6 +177,10 @@ GROUPED_CASES = [
     ([0, 300, 1, 0, 129, 2, 0], 256, 320),
     ([5] * 33, 64, 128),
     ([0, 0, 0], 16, 64),
+    # small/large boundary (64 rows streamed, 65 rows tiled), a multi-tile
+    # expert, ragged K (K % 64 != 0) and an N tail on the tiled path
+    ([64, 65, 0, 600], 200, 208),
+    ([1, 700, 2, 64, 0, 257], 272, 1024),
 ]
 
 
