@@ -17,5 +17,6 @@ Sources (web pages, cited by title and section):
 Parity status per function is listed in ``oracle/w8a8_ref.py``'s header.
 """
 
+from . import mx_ref as mx  # noqa: F401
 from .w8a8_ref import *  # noqa: F401,F403
 from .w8a8_ref import __all__  # noqa: F401
