@@ -16,6 +16,11 @@ resident, seeded synthetic inputs:
            T = 2048 tokens routed top-8 over 256 experts, H = 4096, I = 2048.
            value = tokens / step time (tokens/s).
   tiny     quant + INT8 linear, 16 x 256 x 128 with bias (latency case).
+  mx       MXFP8 linear: dynamic MX quant of BF16 activations [2048, 17408] +
+           block-scaled E4M3 GEMM against a weight [5120, 17408] that was
+           resolved from 128 x 128-tile block FP8 and MX-requantized at load
+           time (load-time prep timed once and reported in config).
+           value = 2*M*N*K / step time (TFLOPS).
   copy     a plain 512 MiB device-to-device copy (torch's copy kernel): the
            measured HBM ceiling, and the reference dispatch that scales the
            FETCH_SIZE / WRITE_SIZE counters (it moves exactly 2 x 512 MiB).
@@ -41,6 +46,7 @@ if ROOT not in sys.path:
 
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, GB/s
 PEAK_INT8_TOPS = 5000.0        # MI355X dense INT8 MFMA, TOP/s
+PEAK_FP8_TFLOPS = 5000.0       # MI355X dense FP8 MFMA, TFLOP/s
 BYTES_INT8 = 1
 
 
@@ -50,7 +56,7 @@ def _args():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode",
-                    choices=["decode", "prefill", "moe", "tiny", "copy"])
+                    choices=["decode", "prefill", "moe", "tiny", "copy", "mx"])
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="approximate budget of the oracle timing on the host")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -339,6 +345,89 @@ class MoeWorkload(Workload):
                            f"weights drawn per expert inside the timing), tokens = rows / top_k")
 
 
+class MxWorkload(Workload):
+    def __init__(self, w, torch):
+        super().__init__(w, torch)
+        import numpy as np
+
+        import synth
+        self.name = "mx"
+        d = synth.mx_block_fp8(seed=0)
+        self.d = d
+        N, K = d.w_e4m3.shape
+        M = d.x.shape[0]
+        self.M, self.N, self.K = M, N, K
+        dev = "cuda"
+        w8 = torch.from_numpy(d.w_e4m3).to(dev)
+        sinv = torch.from_numpy(d.scale_inv).to(dev)
+        torch.cuda.synchronize()
+        # load-time prep: resolve -> BF16 -> MX quant -> prepack (timed once)
+        a, b = _ev(torch), _ev(torch)
+        a.record()
+        wb = w.mx_resolve_block_fp8(w8, sinv, d.bn, d.bk)
+        wp, ws = w.mx_quant(wb)
+        self.packed = w.mx_prepack_weight(wp, ws)
+        b.record()
+        torch.cuda.synchronize()
+        self.prep_ms = a.elapsed_time(b)
+        del wb, wp, ws, w8
+        self.x = torch.from_numpy(d.x.view(np.int16)).to(dev).view(torch.bfloat16)
+        self.y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        self.ws = torch.empty((w.mx_linear_workspace_bytes(M, K),), dtype=torch.uint8, device=dev)
+        self.y2 = torch.empty_like(self.y)
+        self.unit = "TFLOPS"
+        self.bound = "mfma"
+        self._linear()
+        torch.cuda.synchronize()
+        self.a_e4m3, self.a_skb = w.mx_workspace_operands(self.ws, M, K)
+        self.capture([self._linear], [(self._gemm, 1, "mx_gemm")])
+
+    def _linear(self):
+        self.w.mx_linear(self.x, self.packed, self.N, y=self.y, workspace=self.ws)
+
+    def _gemm(self):
+        self.w.mx_gemm(self.a_e4m3, self.a_skb, self.packed, self.N, y=self.y2)
+
+    def flops(self):
+        return 2.0 * self.M * self.N * self.K
+
+    def value(self, sec_per_step):
+        return self.flops() / sec_per_step / 1e12
+
+    def dominant(self, per_key_ms):
+        ach = self.flops() / (per_key_ms["mx_gemm"] * 1e-3) / 1e12
+        return dict(bound="mfma", achieved=ach, peak=PEAK_FP8_TFLOPS, unit="TFLOP/s",
+                    frac=ach / PEAK_FP8_TFLOPS)
+
+    def config(self):
+        return {"workload": "mx", "M": self.M, "N": self.N, "K": self.K, "group": 32,
+                "source_block": [self.d.bn, self.d.bk], "scale_alg": 0,
+                "load_prep_ms": round(self.prep_ms, 3),
+                "load_prep": "resolve + MX quant + prepack of the weight, once"}
+
+    def cpu_baseline(self, budget_s):
+        import oracle as O
+        d = self.d
+        ns = 256                                   # weight rows in the sample
+        wb = O.mx.mx_resolve(d.w_e4m3[:ns], d.scale_inv[: -(-ns // d.bn)], d.bn, d.bk)
+        wp, ws = O.mx.mx_quant(O.bf16_to_f32(wb))
+        rows = 16
+        t0 = time.perf_counter()
+        n = 0
+        while True:
+            r0 = (n * rows) % self.M
+            ap, as_ = O.mx.mx_quant(O.bf16_to_f32(d.x[r0:r0 + rows]))
+            O.mx.mx_gemm_ref64(ap, as_, wp, ws)
+            n += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
+        dt = time.perf_counter() - t0
+        return dict(value=n * 2.0 * rows * ns * self.K / dt / 1e12, unit="TFLOPS",
+                    sample=f"oracle MX quant of {rows} activation rows + float64 GEMM against "
+                           f"{ns} of the {self.N} weight rows (weight prep outside the timing), "
+                           f"{n} repetitions")
+
+
 class CopyWorkload(Workload):
     """512 MiB device copy: HBM reference, not part of the W8A8 path."""
     NBYTES = 512 << 20
@@ -411,6 +500,8 @@ def main():
         wl = DenseWorkload(w, torch, "tiny", [16], 256, 128, True, 0.01, 1)
     elif args.workload == "copy":
         wl = CopyWorkload(w, torch)
+    elif args.workload == "mx":
+        wl = MxWorkload(w, torch)
     else:
         wl = MoeWorkload(w, torch)
 
@@ -459,7 +550,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int8",
+        "dtype": "fp8-e4m3 (MX)" if wl.name == "mx" else "int8",
         "data": "synthetic (seeded numpy; see synth/)",
         "config": wl.config(),
         "roofline": {k: (round(v, 4) if isinstance(v, float) else v) for k, v in roof.items()},

@@ -169,6 +169,71 @@ int w8a8_moe_grouped(const void* x_rows, const float* x_scale,
                      const void* w2_packed, const float* w2_scale, uint16_t* y,
                      void* workspace, int64_t ws_bytes, void* stream);
 
+/*
+ * MXFP8 variant.  [MXFP8] = "Qwen3.8-FP8 on Ascend 950: Why Weights Become
+ * MXFP8 at Load Time". E4M3 = OCP E4M3FN (largest finite 448); E8M0 byte b
+ * stands for 2^(b - 127). Scales are row-major [rows, K/32] at this boundary.
+ * K must be a multiple of 32 (else W8A8_ERR_UNSUPPORTED; [MXFP8] "Where It
+ * Breaks or Falls Back": such layers do not take the MX path).
+ *
+ * w8a8_mx_quant  [MXFP8 Deep Dive 3 and 5]: BF16 x [M, K] -> E4M3 payload
+ *   e4m3 [M, K] + e8m0 [M, K/32], one shared exponent per 32 values along K:
+ *   scale_alg 0: E = floor(log2(amax)) - 8; scale_alg 1: the smallest E with
+ *   amax / 2^E <= 448; E clamped to [-127, 127], amax == 0 -> byte 0. Payload =
+ *   E4M3(x / 2^E), round to nearest even, subnormals kept, saturating at 448,
+ *   sign of zero kept. x 16-byte aligned, e4m3 8-byte aligned.
+ */
+int w8a8_mx_quant(const uint16_t* x, int64_t M, int64_t K, uint8_t* e4m3, uint8_t* e8m0,
+                  int scale_alg, void* stream);
+
+/*
+ * w8a8_mx_resolve_block_fp8  [MXFP8 Deep Dive 1 and 2, resolve equation]:
+ *   w_bf16[i, j] = BF16(fp32(w_e4m3[i, j]) * scale_inv[i / BN, j / BK]), the
+ *   product one fp32 rounding, BF16 round to nearest even; scale_inv is fp32
+ *   [ceil(N/BN), ceil(K/BK)] (edge tiles cropped). All device pointers.
+ */
+int w8a8_mx_resolve_block_fp8(const uint8_t* w_e4m3, const float* scale_inv, int64_t N,
+                              int64_t K, int64_t BN, int64_t BK, uint16_t* w_bf16, void* stream);
+
+/*
+ * w8a8_mx_prepack_weight  [MXFP8 Deep Dive 4: the MX weight and its scales
+ *   are re-laid out once for the kernel, into stable buffers]: E4M3 [N, K] +
+ *   E8M0 [N, K/32] -> one packed buffer of w8a8_mx_packed_bytes(N, K) bytes,
+ *   256-byte aligned (payload in the P16x64 block layout of
+ *   w8a8_prepack_weight, then the scales k-block major).
+ */
+int64_t w8a8_mx_packed_bytes(int64_t N, int64_t K);
+int w8a8_mx_prepack_weight(const uint8_t* w_e4m3, const uint8_t* w_e8m0, int64_t N, int64_t K,
+                           void* packed, void* stream);
+
+/*
+ * w8a8_mx_linear  [MXFP8 Deep Dive 5]: y [M, N] BF16 = block-scaled product of
+ *   the MX activation and the packed MX weight, fp32 accumulation
+ *   (v_mfma_scale_f32_32x32x64_f8f6f4), BF16 round to nearest even.
+ *   x: BF16 [M, K] (MX-quantized inside with scale_alg) when x_e8m0 == NULL,
+ *   else an E4M3 payload [M, K] with its E8M0 scales x_e8m0 [M, K/32].
+ *   workspace: w8a8_mx_linear_workspace_bytes(M, K) bytes, 256-byte aligned.
+ */
+int64_t w8a8_mx_linear_workspace_bytes(int64_t M, int64_t K);
+int w8a8_mx_linear(const void* x, const uint8_t* x_e8m0, int64_t M, int64_t K,
+                   const void* w_packed, int64_t N, uint16_t* y, int scale_alg, void* workspace,
+                   int64_t ws_bytes, void* stream);
+
+/*
+ * w8a8_mx_gemm  [MXFP8 Deep Dive 5, the block-scaled matmul alone]: the GEMM
+ *   stage of w8a8_mx_linear, for stage-wise tests and timing. a_e4m3: E4M3
+ *   [M, K] row-major, 16-byte aligned; a_scale_kb: E8M0 bytes "k-block major",
+ *   [ceil(K/64)][Mp][2] with Mp = M rounded up to even, 4-byte aligned (the
+ *   two 32-groups of one 64-deep k-block of a row adjacent; when K/32 is odd
+ *   the last k-block's second byte of every row must be 0; the pad row, if
+ *   any, is never used).
+ *   After a BF16 call of w8a8_mx_linear its workspace holds exactly these two
+ *   operands: the payload at offset 0, the scales at offset M*K rounded up to
+ *   256. w_packed as for w8a8_mx_linear; y BF16 [M, N].
+ */
+int w8a8_mx_gemm(const uint8_t* a_e4m3, const uint8_t* a_scale_kb, int64_t M, int64_t K,
+                 const void* w_packed, int64_t N, uint16_t* y, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

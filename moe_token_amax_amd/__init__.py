@@ -30,6 +30,14 @@ __all__ = [
     "swiglu_quant",
     "moe_workspace_bytes",
     "moe_grouped",
+    "mx_quant",
+    "mx_resolve_block_fp8",
+    "mx_packed_bytes",
+    "mx_prepack_weight",
+    "mx_linear_workspace_bytes",
+    "mx_linear",
+    "mx_gemm",
+    "mx_workspace_operands",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libw8a8.so")
@@ -70,6 +78,15 @@ def _load():
         "w8a8_moe_workspace_bytes": (_c_i64, [_c_i64, _c_i64, _c_i64, _c_i64]),
         "w8a8_moe_grouped": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i64,
                                             _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_p]),
+        "w8a8_mx_quant": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_p, ctypes.c_int, _c_p]),
+        "w8a8_mx_resolve_block_fp8": (ctypes.c_int, [_c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i64,
+                                                     _c_p, _c_p]),
+        "w8a8_mx_packed_bytes": (_c_i64, [_c_i64, _c_i64]),
+        "w8a8_mx_prepack_weight": (ctypes.c_int, [_c_p, _c_p, _c_i64, _c_i64, _c_p, _c_p]),
+        "w8a8_mx_linear_workspace_bytes": (_c_i64, [_c_i64, _c_i64]),
+        "w8a8_mx_linear": (ctypes.c_int, [_c_p, _c_p, _c_i64, _c_i64, _c_p, _c_i64, _c_p,
+                                          ctypes.c_int, _c_p, _c_i64, _c_p]),
+        "w8a8_mx_gemm": (ctypes.c_int, [_c_p, _c_p, _c_i64, _c_i64, _c_p, _c_i64, _c_p, _c_p]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -268,4 +285,114 @@ def moe_grouped(x_rows: torch.Tensor, group_list: torch.Tensor, w13_packed: torc
     _check(lib.w8a8_moe_grouped(_ptr(x_rows), _ptr(x_scale), _ptr(group_list), R, E, H, I,
                                 _ptr(w13_packed), _ptr(w13_scale), _ptr(w2_packed),
                                 _ptr(w2_scale), _ptr(y), _ptr(ws), ws_n, _stream()))
+    return y
+
+
+# ---------------------------------------------------------------------------
+# MXFP8 variant
+# ---------------------------------------------------------------------------
+
+def mx_quant(x: torch.Tensor, scale_alg: int = 0, payload: torch.Tensor | None = None,
+             scales: torch.Tensor | None = None):
+    """BF16 [M, K] -> (E4M3 payload uint8 [M, K], E8M0 scales uint8 [M, K/32])."""
+    _need(x, torch.bfloat16, "x", 2)
+    M, K = x.shape
+    if payload is None:
+        payload = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((M, max(K // 32, 0)), dtype=torch.uint8, device=x.device)
+    _need(payload, torch.uint8, "payload", 2)
+    _need(scales, torch.uint8, "scales", 2)
+    _check(lib.w8a8_mx_quant(_ptr(x), M, K, _ptr(payload), _ptr(scales), scale_alg, _stream()))
+    return payload, scales
+
+
+def mx_resolve_block_fp8(w_e4m3: torch.Tensor, scale_inv: torch.Tensor, bn: int, bk: int,
+                         out: torch.Tensor | None = None) -> torch.Tensor:
+    """E4M3 [N, K] with fp32 tile scales [ceil(N/bn), ceil(K/bk)] -> BF16 [N, K]."""
+    _need(w_e4m3, torch.uint8, "w_e4m3", 2)
+    _need(scale_inv, torch.float32, "scale_inv", 2)
+    N, K = w_e4m3.shape
+    if tuple(scale_inv.shape) != (-(-N // bn), -(-K // bk)):
+        raise ValueError("scale_inv shape does not match the tile grid")
+    if out is None:
+        out = torch.empty((N, K), dtype=torch.bfloat16, device=w_e4m3.device)
+    _need(out, torch.bfloat16, "out", 2)
+    _check(lib.w8a8_mx_resolve_block_fp8(_ptr(w_e4m3), _ptr(scale_inv), N, K, bn, bk, _ptr(out),
+                                         _stream()))
+    return out
+
+
+def mx_packed_bytes(N: int, K: int) -> int:
+    return int(lib.w8a8_mx_packed_bytes(N, K))
+
+
+def mx_prepack_weight(w_e4m3: torch.Tensor, w_e8m0: torch.Tensor,
+                      out: torch.Tensor | None = None) -> torch.Tensor:
+    """E4M3 [N, K] + E8M0 [N, K/32] -> packed MX weight (uint8, stable buffer)."""
+    _need(w_e4m3, torch.uint8, "w_e4m3", 2)
+    _need(w_e8m0, torch.uint8, "w_e8m0", 2)
+    N, K = w_e4m3.shape
+    if tuple(w_e8m0.shape) != (N, K // 32):
+        raise ValueError("w_e8m0 must be [N, K/32]")
+    nbytes = mx_packed_bytes(N, K)
+    if out is None:
+        out = torch.empty((nbytes,), dtype=torch.uint8, device=w_e4m3.device)
+    _need(out, torch.uint8, "out", 1)
+    _check(lib.w8a8_mx_prepack_weight(_ptr(w_e4m3), _ptr(w_e8m0), N, K, _ptr(out), _stream()))
+    return out
+
+
+def mx_linear_workspace_bytes(M: int, K: int) -> int:
+    return int(lib.w8a8_mx_linear_workspace_bytes(M, K))
+
+
+def mx_linear(x: torch.Tensor, w_packed: torch.Tensor, N: int, x_e8m0: torch.Tensor | None = None,
+              scale_alg: int = 0, y: torch.Tensor | None = None,
+              workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """MX block-scaled linear: BF16 x (or E4M3 x with x_e8m0) times packed MX W -> BF16 [M, N]."""
+    if x_e8m0 is None:
+        _need(x, torch.bfloat16, "x", 2)
+    else:
+        _need(x, torch.uint8, "x", 2)
+        _need(x_e8m0, torch.uint8, "x_e8m0", 2)
+    _need(w_packed, torch.uint8, "w_packed", 1)
+    M, K = x.shape
+    if w_packed.numel() < mx_packed_bytes(N, K):
+        raise ValueError("w_packed too small for [N, K]")
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    _need(y, torch.bfloat16, "y", 2)
+    ws, ws_n = _workspace(mx_linear_workspace_bytes(M, K), x.device, workspace)
+    _check(lib.w8a8_mx_linear(_ptr(x), _ptr(x_e8m0), M, K, _ptr(w_packed), N, _ptr(y), scale_alg,
+                              _ptr(ws), ws_n, _stream()))
+    return y
+
+
+def mx_workspace_operands(workspace: torch.Tensor, M: int, K: int):
+    """(E4M3 payload [M, K], k-block-major E8M0 bytes) views of an mx_linear workspace."""
+    _need(workspace, torch.uint8, "workspace", 1)
+    off = -(-M * K // 256) * 256
+    nsc = -(-K // 64) * (M + (M & 1)) * 2
+    if workspace.numel() < off + nsc:
+        raise ValueError("workspace too small")
+    return workspace[:M * K].view(M, K), workspace[off:off + nsc]
+
+
+def mx_gemm(a_e4m3: torch.Tensor, a_scale_kb: torch.Tensor, w_packed: torch.Tensor, N: int,
+            y: torch.Tensor | None = None) -> torch.Tensor:
+    """GEMM stage of mx_linear: E4M3 [M, K] + k-block-major E8M0 -> BF16 [M, N]."""
+    _need(a_e4m3, torch.uint8, "a_e4m3", 2)
+    _need(a_scale_kb, torch.uint8, "a_scale_kb", 1)
+    _need(w_packed, torch.uint8, "w_packed", 1)
+    M, K = a_e4m3.shape
+    if a_scale_kb.numel() < -(-K // 64) * (M + (M & 1)) * 2:
+        raise ValueError("a_scale_kb must hold ceil(K/64) * (M rounded up to even) * 2 bytes")
+    if w_packed.numel() < mx_packed_bytes(N, K):
+        raise ValueError("w_packed too small for [N, K]")
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=a_e4m3.device)
+    _need(y, torch.bfloat16, "y", 2)
+    _check(lib.w8a8_mx_gemm(_ptr(a_e4m3), _ptr(a_scale_kb), M, K, _ptr(w_packed), N, _ptr(y),
+                            _stream()))
     return y

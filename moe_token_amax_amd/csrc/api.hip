@@ -7,6 +7,7 @@
 
 #include "../../include/w8a8.h"
 #include "launch.hpp"
+#include "mx.hpp"
 
 namespace {
 
@@ -224,6 +225,123 @@ int w8a8_moe_grouped(const void* x_rows, const float* x_scale, const int64_t* gr
   err = w8a8::launch_grouped_gemm(q2, s2, group_list, R, E, H, I, w2_packed, w2_scale, y,
                                   w8a8::kOutBf16, ws + L.inner, s);
   return launched(err, "moe_grouped: W2");
+}
+
+// ---------------------------------------------------------------------------
+// MXFP8 variant
+// ---------------------------------------------------------------------------
+static int64_t mx_payload_bytes(int64_t N, int64_t K) {
+  return align256(w8a8::round_up(N, 16) * w8a8::round_up(K, 64));
+}
+
+static int check_mx_k(const char* who, int64_t K) {
+  if (K < 32 || K > W8A8_MAX_K) return fail(W8A8_ERR_SHAPE, "%s: need 32 <= K <= %d", who, W8A8_MAX_K);
+  if (K % 32)
+    return fail(W8A8_ERR_UNSUPPORTED, "%s: K = %lld is not a multiple of the MX group size 32", who,
+                (long long)K);
+  return W8A8_OK;
+}
+
+int w8a8_mx_quant(const uint16_t* x, int64_t M, int64_t K, uint8_t* e4m3, uint8_t* e8m0,
+                  int scale_alg, void* stream) {
+  int st = check_mx_k("mx_quant", K);
+  if (st) return st;
+  if (M < 0 || M >= kMaxDim) return fail(W8A8_ERR_SHAPE, "mx_quant: bad M");
+  if (scale_alg != 0 && scale_alg != 1) return fail(W8A8_ERR_UNSUPPORTED, "mx_quant: scale_alg must be 0 or 1");
+  if (M == 0) return ok();
+  if (!x || !e4m3 || !e8m0) return fail(W8A8_ERR_NULL, "mx_quant: null pointer");
+  if (!aligned(x, 16) || !aligned(e4m3, 8)) return fail(W8A8_ERR_ALIGN, "mx_quant: x needs 16-byte, e4m3 8-byte alignment");
+  return launched(w8a8::launch_mx_quant(x, M, K, scale_alg, e4m3, e8m0, nullptr, 0, (hipStream_t)stream),
+                  "mx_quant");
+}
+
+int w8a8_mx_resolve_block_fp8(const uint8_t* w_e4m3, const float* scale_inv, int64_t N, int64_t K,
+                              int64_t BN, int64_t BK, uint16_t* w_bf16, void* stream) {
+  if (N < 1 || K < 1 || BN < 1 || BK < 1 || N >= kMaxDim || K >= kMaxDim)
+    return fail(W8A8_ERR_SHAPE, "mx_resolve: need N, K, BN, BK >= 1");
+  if (!w_e4m3 || !scale_inv || !w_bf16) return fail(W8A8_ERR_NULL, "mx_resolve: null pointer");
+  if (!aligned(scale_inv, 4) || !aligned(w_bf16, 2)) return fail(W8A8_ERR_ALIGN, "mx_resolve: misaligned buffer");
+  return launched(w8a8::launch_mx_resolve(w_e4m3, scale_inv, N, K, BN, BK, w_bf16, (hipStream_t)stream),
+                  "mx_resolve");
+}
+
+int64_t w8a8_mx_packed_bytes(int64_t N, int64_t K) {
+  if (N < 1 || K < 1) return 0;
+  return mx_payload_bytes(N, K) + align256(w8a8::mx_scale_kb_bytes(w8a8::round_up(N, 16), K));
+}
+
+int w8a8_mx_prepack_weight(const uint8_t* w_e4m3, const uint8_t* w_e8m0, int64_t N, int64_t K,
+                           void* packed, void* stream) {
+  int st = check_mx_k("mx_prepack_weight", K);
+  if (st) return st;
+  if (N < 1 || N >= kMaxDim) return fail(W8A8_ERR_SHAPE, "mx_prepack_weight: bad N");
+  if (!w_e4m3 || !w_e8m0 || !packed) return fail(W8A8_ERR_NULL, "mx_prepack_weight: null pointer");
+  if (!aligned(packed, 256)) return fail(W8A8_ERR_ALIGN, "mx_prepack_weight: packed needs 256-byte alignment");
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = w8a8::launch_prepack(reinterpret_cast<const int8_t*>(w_e4m3), 1, N, K, packed, s);
+  if (e != hipSuccess) return launched(e, "mx_prepack_weight: payload");
+  e = w8a8::launch_mx_scale_relayout(w_e8m0, N, K, w8a8::round_up(N, 16),
+                                     reinterpret_cast<uint8_t*>(packed) + mx_payload_bytes(N, K), s);
+  return launched(e, "mx_prepack_weight: scales");
+}
+
+int64_t w8a8_mx_linear_workspace_bytes(int64_t M, int64_t K) {
+  if (M < 1 || K < 1) return 0;
+  return align256(M * K) + align256(w8a8::mx_scale_kb_bytes(w8a8::round_up(M, 2), K));
+}
+
+int w8a8_mx_linear(const void* x, const uint8_t* x_e8m0, int64_t M, int64_t K, const void* w_packed,
+                   int64_t N, uint16_t* y, int scale_alg, void* workspace, int64_t ws_bytes,
+                   void* stream) {
+  int st = check_mx_k("mx_linear", K);
+  if (st) return st;
+  if (M < 0 || N < 1 || M >= kMaxDim || N >= kMaxDim) return fail(W8A8_ERR_SHAPE, "mx_linear: bad M or N");
+  if (scale_alg != 0 && scale_alg != 1) return fail(W8A8_ERR_UNSUPPORTED, "mx_linear: scale_alg must be 0 or 1");
+  if (M == 0) return ok();
+  if (!x || !w_packed || !y) return fail(W8A8_ERR_NULL, "mx_linear: null pointer");
+  if (!aligned(w_packed, 256) || !aligned(y, 4) || !aligned(x, 16))
+    return fail(W8A8_ERR_ALIGN, "mx_linear: x needs 16-byte, w_packed 256-byte, y 4-byte alignment");
+  const int64_t need = w8a8_mx_linear_workspace_bytes(M, K);
+  if (!workspace || ws_bytes < need || !aligned(workspace, 256))
+    return fail(W8A8_ERR_WORKSPACE, "mx_linear: needs %lld workspace bytes (256-byte aligned), got %lld",
+                (long long)need, (long long)ws_bytes);
+  hipStream_t s = (hipStream_t)stream;
+  uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
+  uint8_t* a_payload = ws;
+  uint8_t* a_scale_kb = ws + align256(M * K);
+  const int64_t Mp = w8a8::round_up(M, 2);  // even row count: dword-aligned scale pairs
+  hipError_t e;
+  const uint8_t* a;
+  if (!x_e8m0) {
+    // BF16 activation: dynamic MX quantization first
+    e = w8a8::launch_mx_quant(reinterpret_cast<const uint16_t*>(x), M, K, scale_alg, a_payload,
+                              nullptr, a_scale_kb, Mp, s);
+    if (e != hipSuccess) return launched(e, "mx_linear: quant");
+    a = a_payload;
+  } else {
+    // pre-quantized activation: E4M3 [M, K] with its row-major E8M0 [M, K/32]
+    e = w8a8::launch_mx_scale_relayout(x_e8m0, M, K, Mp, a_scale_kb, s);
+    if (e != hipSuccess) return launched(e, "mx_linear: scales");
+    a = reinterpret_cast<const uint8_t*>(x);
+  }
+  const uint8_t* wp = reinterpret_cast<const uint8_t*>(w_packed);
+  e = w8a8::launch_mx_gemm(a, a_scale_kb, Mp, M, K, wp, wp + mx_payload_bytes(N, K), N, y, s);
+  return launched(e, "mx_linear: gemm");
+}
+
+int w8a8_mx_gemm(const uint8_t* a_e4m3, const uint8_t* a_scale_kb, int64_t M, int64_t K,
+                 const void* w_packed, int64_t N, uint16_t* y, void* stream) {
+  int st = check_mx_k("mx_gemm", K);
+  if (st) return st;
+  if (M < 0 || N < 1 || M >= kMaxDim || N >= kMaxDim) return fail(W8A8_ERR_SHAPE, "mx_gemm: bad M or N");
+  if (M == 0) return ok();
+  if (!a_e4m3 || !a_scale_kb || !w_packed || !y) return fail(W8A8_ERR_NULL, "mx_gemm: null pointer");
+  if (!aligned(a_e4m3, 16) || !aligned(a_scale_kb, 4) || !aligned(w_packed, 256) || !aligned(y, 2))
+    return fail(W8A8_ERR_ALIGN, "mx_gemm: a needs 16-byte, scales 4-byte, w_packed 256-byte alignment");
+  const uint8_t* wp = reinterpret_cast<const uint8_t*>(w_packed);
+  return launched(w8a8::launch_mx_gemm(a_e4m3, a_scale_kb, w8a8::round_up(M, 2), M, K, wp,
+                                       wp + mx_payload_bytes(N, K), N, y, (hipStream_t)stream),
+                  "mx_gemm");
 }
 
 }  // extern "C"

@@ -1,0 +1,414 @@
+// MXFP8 variant for gfx950: block-FP8 resolve, MX quantization and the
+// block-scaled GEMM on v_mfma_scale_f32_32x32x64_f8f6f4.
+//
+// ("Qwen3.8-FP8 on Ascend 950: Why Weights Become MXFP8 at Load Time":
+// Deep Dive 2 resolve equation, Deep Dive 3 E4M3 payload + E8M0 scale per 32
+// values along K, Deep Dive 5 runtime activation MX quant + block-scaled
+// matmul to the model dtype.)
+//
+// Formats: E4M3 = OCP E4M3FN (bias 7, largest finite 448, no infinities);
+// E8M0 byte b = 2^(b - 127). Encoding rounds to nearest, ties to the even
+// code, keeps subnormals, saturates to 448 and keeps the sign of zero. The
+// shared exponent of a group of 32 is floor(log2(amax)) - 8 (scale rule 0) or
+// the smallest E with amax / 2^E <= 448 (scale rule 1), clamped to
+// [-127, 127]; amax == 0 gives byte 0.
+//
+// Layouts: payloads are row-major [rows, K] (activations) or prepacked into
+// the P16x64 blocks of the INT8 path (weights). Scales at the C ABI are
+// row-major [rows, K/32]; the GEMM reads them "k-block major",
+// [K/64][rows_p][2] (the two 32-groups of one 64-deep k-block of a row are
+// adjacent; rows_p = rows rounded up to even for activations, to 16 for
+// weights), so the scales of one stage are a contiguous, dword-aligned run
+// per operand.
+#include "device_common.hpp"
+#include "launch.hpp"
+#include "mx.hpp"
+
+namespace w8a8 {
+
+#define W8A8_LDS_MX __attribute__((address_space(3)))
+
+// ---------------------------------------------------------------------------
+// E4M3 / E8M0 helpers
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
+  const uint32_t e = (b >> 3) & 15u, m = b & 7u;
+  float v = e ? __builtin_ldexpf((float)(8u + m), (int)e - 10) : __builtin_ldexpf((float)m, -9);
+  return (b & 0x80u) ? -v : v;
+}
+
+// |v| < 2^9 expected (the group scaling guarantees it); larger saturates.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float v) {
+  const uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
+  const float a = fabsf(v);
+  uint32_t code;
+  if (a >= 448.0f) {
+    code = 0x7Eu;
+  } else if (a < 0.015625f) {                 // below 2^-6: subnormal grid of 2^-9
+    code = (uint32_t)__builtin_rintf(a * 512.0f);  // 0..8 (8 = smallest normal)
+  } else {
+    const int e = __builtin_amdgcn_frexp_expf(a) - 1;                // floor(log2 a), -6..8
+    const uint32_t m = (uint32_t)__builtin_rintf(__builtin_ldexpf(a, 3 - e));  // 8..16
+    code = (uint32_t)(e + 7) * 8u + (m - 8u);  // m == 16 carries into the exponent
+  }
+  return code | sign;
+}
+
+// shared exponent of a group (without the +127 bias)
+__device__ __forceinline__ int mx_exponent(float amax, int scale_alg) {
+  if (!(amax > 0.0f)) return -127;
+  int e = __builtin_amdgcn_frexp_expf(amax) - 1 - 8;
+  if (scale_alg == 1 && __builtin_ldexpf(amax, -e) > 448.0f) e += 1;
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
+// ---------------------------------------------------------------------------
+// resolve: BF16(fl32(fp32(e4m3) * S[i / BN, j / BK]))
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void mx_resolve_kernel(const uint8_t* __restrict__ w,
+                                                         const float* __restrict__ s, int64_t N,
+                                                         int64_t K, int64_t BN, int64_t BK,
+                                                         uint16_t* __restrict__ out, int vec) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;  // one thread, 8 elements
+  const int64_t per_row = (K + 7) / 8;
+  if (idx >= N * per_row) return;
+  const int64_t i = idx / per_row, j0 = (idx % per_row) * 8;
+  const int64_t scols = (K + BK - 1) / BK;
+  const float* srow = s + (i / BN) * scols;
+  if (vec) {  // K % 8 == 0, w 8-byte and out 16-byte aligned: one load, one store
+    const uint2 v = *reinterpret_cast<const uint2*>(w + i * K + j0);
+    const uint32_t b[2] = {v.x, v.y};
+    uint32_t o[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t j = j0 + 2 * u;
+      const float f0 = e4m3_to_f32((b[u / 2] >> (16 * (u & 1))) & 0xFFu) * srow[j / BK];
+      const float f1 = e4m3_to_f32((b[u / 2] >> (16 * (u & 1) + 8)) & 0xFFu) * srow[(j + 1) / BK];
+      o[u] = f32_to_bf16(f0) | (f32_to_bf16(f1) << 16);
+    }
+    *reinterpret_cast<uint4*>(out + i * K + j0) = uint4{o[0], o[1], o[2], o[3]};
+    return;
+  }
+  for (int u = 0; u < 8; ++u) {
+    const int64_t j = j0 + u;
+    if (j >= K) break;
+    const float f = e4m3_to_f32(w[i * K + j]) * srow[j / BK];
+    out[i * K + j] = (uint16_t)f32_to_bf16(f);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// MX quant: BF16 [M, K] -> E4M3 [M, K] + E8M0. Four consecutive lanes own one
+// 32-group (8 values each); the group amax is two DPP steps inside the quad.
+// Scales go to `scale_rm` ([M, K/32], may be null) and/or `scale_kb`
+// ([ceil(K/64)][Mp][2], may be null; Mp = rows of that layout).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void mx_quant_kernel(const uint16_t* __restrict__ x, int64_t M,
+                                                       int64_t K, int scale_alg,
+                                                       uint8_t* __restrict__ payload,
+                                                       uint8_t* __restrict__ scale_rm,
+                                                       uint8_t* __restrict__ scale_kb,
+                                                       int64_t Mp) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t chunks = K / 8;             // K % 32 == 0, so quads never straddle rows
+  const bool live = t < M * chunks;
+  const int64_t tc = live ? t : 0;
+  const int64_t row = tc / chunks, c = tc % chunks;
+  uint4 v = live ? *reinterpret_cast<const uint4*>(x + row * K + c * 8) : uint4{0u, 0u, 0u, 0u};
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  uint32_t amax = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) amax = max(amax, max(w[j] & 0x7FFFu, (w[j] >> 16) & 0x7FFFu));
+  amax = max(amax, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)amax, 0xB1, 0xF, 0xF, false));
+  amax = max(amax, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)amax, 0x4E, 0xF, 0xF, false));
+  if (!live) return;
+  const int e = mx_exponent(bf16_to_f32(amax), scale_alg);
+  uint32_t b[8];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    b[2 * j] = f32_to_e4m3(__builtin_ldexpf(bf16_to_f32(w[j] & 0xFFFFu), -e));
+    b[2 * j + 1] = f32_to_e4m3(__builtin_ldexpf(bf16_to_f32(w[j] >> 16), -e));
+  }
+  uint2 o;
+  o.x = b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24);
+  o.y = b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24);
+  *reinterpret_cast<uint2*>(payload + row * K + c * 8) = o;
+  if ((c & 3) == 0) {
+    const int64_t g = c / 4;                 // 32-group index along K
+    const uint8_t sb = (uint8_t)(e + 127);
+    if (scale_rm) scale_rm[row * (K / 32) + g] = sb;
+    if (scale_kb) {
+      scale_kb[((g / 2) * Mp + row) * 2 + (g & 1)] = sb;
+      // odd group count: the last k-block's second slot covers no data; give it
+      // byte 0 so that the padded half of that k-block multiplies out to zero
+      if (g == K / 32 - 1 && (g & 1) == 0) scale_kb[((g / 2) * Mp + row) * 2 + 1] = 0;
+    }
+  }
+}
+
+// row-major [R, K/32] scales -> k-block-major [ceil(K/64)][Rp][2]; pads with 0
+__global__ __launch_bounds__(256) void mx_scale_relayout_kernel(const uint8_t* __restrict__ src,
+                                                                int64_t R, int64_t G, int64_t Rp,
+                                                                uint8_t* __restrict__ dst) {
+  const int64_t KB = (G + 1) / 2;
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= KB * Rp * 2) return;
+  const int64_t g2 = t & 1, r = (t >> 1) % Rp, kb = (t >> 1) / Rp;
+  const int64_t g = kb * 2 + g2;
+  dst[t] = (r < R && g < G) ? src[r * G + g] : (uint8_t)0;
+}
+
+// ---------------------------------------------------------------------------
+// Block-scaled GEMM tile: 256 x 256, 8 wavefronts (2 x 4) of 128 x 64, each a
+// 4 x 2 grid of 32 x 32 fp32 accumulator blocks. One 64-deep k-block per
+// stage; a stage holds 16 A blocks + 16 B blocks (1 KB each, MFMA operand
+// order) + 1 KB of scales (256 A rows x 2, then 256 B columns x 2), filled by
+// LDS-DMA: every wavefront issues 4 payload blocks (16 bytes per lane) and one
+// 128-byte scale slice (4 bytes per lane on lanes 0..31) per stage, so every
+// wavefront has the same number of loads in flight per stage. The rest of the pipeline is the INT8 tile's: a ring of
+// STAGES buffers, "s_waitcnt vmcnt(...) lgkmcnt(0); s_barrier" per stage.
+// ---------------------------------------------------------------------------
+struct MxArgs {
+  const uint8_t* a;        // E4M3 [M, K] row-major
+  const uint8_t* a_scale;  // k-block-major [KB][Mp][2], Mp even
+  int64_t Mp;
+  const uint8_t* w;        // packed E4M3 (P16x64), NB x KB blocks
+  const uint8_t* w_scale;  // k-block-major [KB][Np][2], Np = NB * 16
+  int64_t M, N, K;
+  int KB, NB;
+  uint16_t* y;             // BF16 [M, N]
+};
+
+template <int VM>
+__device__ __forceinline__ void mx_wait_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(VM) : "memory");
+}
+
+typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+struct MxTile {
+  static constexpr int BM = 256, BN = 256, STAGES = 4, WM = 2, WN = 4, kWaves = 8;
+  static constexpr int TM = BM / WM / 32;  // 4
+  static constexpr int TN = BN / WN / 32;  // 2
+  static constexpr int kABlocks = BM / 16, kBBlocks = BN / 16;
+  static constexpr int kPerWave = (kABlocks + kBBlocks) / kWaves;  // 4 payload blocks
+  static constexpr int kVmPerStage = kPerWave + 1;                 // + one scale slice
+  static constexpr int kScaleBytes = 1024;
+  static constexpr int kStageBytes = (kABlocks + kBBlocks) * 1024 + kScaleBytes;
+  static constexpr int kLdsBytes = STAGES * kStageBytes;
+
+  struct Src {
+    const uint8_t* base[kPerWave];
+    int64_t step[kPerWave];
+    const uint8_t* sbase;   // scale slice of k-block 0
+    int64_t sstep;
+  };
+
+  __device__ __forceinline__ static void sources(const MxArgs& p, Src& s, int wave, int lane,
+                                                 int64_t row0, int64_t row_last, int nb0) {
+#pragma unroll
+    for (int i = 0; i < kPerWave; ++i) {
+      const int bi = wave * kPerWave + i;
+      if (bi < kABlocks) {
+        int64_t row = row0 + bi * 16 + (lane & 15);
+        row = row < row_last ? row : row_last;
+        s.base[i] = p.a + row * p.K + (lane >> 4) * 16;
+        s.step[i] = 64;
+      } else {
+        int nb = nb0 + (bi - kABlocks);
+        nb = nb < p.NB ? nb : p.NB - 1;
+        s.base[i] = p.w + (int64_t)nb * p.KB * 1024 + lane * 16;
+        s.step[i] = 1024;
+      }
+    }
+    // scale slice: wavefronts 0..3 -> A rows [64w, 64w + 64), 4..7 -> B columns;
+    // lanes 0..31 each bring one dword = the scale pairs of two rows (columns).
+    // Rows past the padded count are clamped; their outputs are discarded.
+    if (wave < 4) {
+      int64_t r = row0 + wave * 64 + 2 * (lane & 31);
+      r = r < p.Mp - 2 ? r : p.Mp - 2;
+      s.sbase = p.a_scale + r * 2;
+      s.sstep = p.Mp * 2;
+    } else {
+      const int64_t np = (int64_t)p.NB * 16;
+      int64_t c = (int64_t)nb0 * 16 + (wave - 4) * 64 + 2 * (lane & 31);
+      c = c < np - 2 ? c : np - 2;
+      s.sbase = p.w_scale + c * 2;
+      s.sstep = np * 2;
+    }
+  }
+
+  __device__ __forceinline__ static void issue(const MxArgs& p, const Src& s, uint8_t* smem,
+                                               int buf, int kb, int wave, int lane) {
+    uint8_t* st = smem + buf * kStageBytes;
+#pragma unroll
+    for (int i = 0; i < kPerWave; ++i) {
+      const int bi = wave * kPerWave + i;
+      const uint8_t* src = s.base[i] + kb * s.step[i];
+      if (bi < kABlocks && (p.K & 63) && kb == p.KB - 1) {
+        const int64_t col = (int64_t)kb * 64 + (lane >> 4) * 16;
+        if (col > p.K - 16) src -= col - (p.K - 16);  // stay inside the row
+      }
+      __builtin_amdgcn_global_load_lds(src, (W8A8_LDS_MX void*)((W8A8_LDS_MX uint8_t*)st + bi * 1024),
+                                       16, 0, 0);
+    }
+    if (lane < 32)  // 32 lanes x 4 bytes: lane l lands at slice + 4 l
+      __builtin_amdgcn_global_load_lds(
+          s.sbase + kb * s.sstep,
+          (W8A8_LDS_MX void*)((W8A8_LDS_MX uint8_t*)st + (kABlocks + kBBlocks) * 1024 + wave * 128),
+          4, 0, 0);
+  }
+
+  __device__ __forceinline__ static void wait_stage(int later) {
+    if (later >= 2) mx_wait_barrier<2 * kVmPerStage>();
+    else if (later == 1) mx_wait_barrier<kVmPerStage>();
+    else mx_wait_barrier<0>();
+  }
+
+  __device__ static void mainloop(const MxArgs& p, uint8_t* smem, f32x16 (&acc)[TM][TN],
+                                  int64_t row0, int64_t row_end, int nb0) {
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave / WN, wn = wave % WN;
+    const int KB = p.KB;
+    Src src;
+    sources(p, src, wave, lane, row0, row_end - 1, nb0);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) acc[i][j] = f32x16{};
+#pragma unroll
+    for (int s = 0; s < STAGES - 1; ++s)
+      if (s < KB) issue(p, src, smem, s, s, wave, lane);
+    // operand of 32 rows (columns) starting at block 2i: lane l reads block
+    // 2i + (l>>4 & 1), rows l & 15, k-chunks 2g and 2g + 1 with g = l >> 5
+    const int lblk = (lane >> 4) & 1;
+    const int lofs = ((2 * (lane >> 5)) * 16 + (lane & 15)) * 16;
+    const int g = lane >> 5;
+    for (int kb = 0; kb < KB; ++kb) {
+      const int ahead = KB - 1 - kb;
+      wait_stage(ahead < STAGES - 2 ? ahead : STAGES - 2);
+      const int nk = kb + STAGES - 1;
+      if (nk < KB) issue(p, src, smem, nk % STAGES, nk, wave, lane);
+      const uint8_t* st = smem + (kb % STAGES) * kStageBytes;
+      const uint8_t* sc = st + (kABlocks + kBBlocks) * 1024;
+      i32x8 bf[TN];
+      int sb[TN];
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const uint8_t* bp = st + (kABlocks + (wn * TN + j) * 2 + lblk) * 1024 + lofs;
+        const i32x4 lo = *reinterpret_cast<const i32x4*>(bp);
+        const i32x4 hi = *reinterpret_cast<const i32x4*>(bp + 256);
+        bf[j] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        sb[j] = sc[512 + ((wn * TN + j) * 32 + (lane & 31)) * 2 + g];
+      }
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const uint8_t* ap = st + ((wm * TM + i) * 2 + lblk) * 1024 + lofs;
+        const i32x4 lo = *reinterpret_cast<const i32x4*>(ap);
+        const i32x4 hi = *reinterpret_cast<const i32x4*>(ap + 256);
+        const i32x8 af = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        const int sa = sc[((wm * TM + i) * 32 + (lane & 31)) * 2 + g];
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, bf[j], acc[i][j], 0, 0, 0,
+                                                                      sa, 0, sb[j]);
+      }
+    }
+    mx_wait_barrier<0>();
+  }
+
+  // register v of block (i, j): row 8*(v/4) + 4*(l/32) + v%4, column l%32
+  __device__ static void epilogue(const MxArgs& p, const f32x16 (&acc)[TM][TN], int64_t row0,
+                                  int64_t row_end, int64_t n0) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int wm = wave / WN, wn = wave % WN;
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int64_t n = n0 + (wn * TN + j) * 32 + (lane & 31);
+      if (n >= p.N) continue;
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int64_t m = row0 + (wm * TM + i) * 32 + 8 * (v / 4) + 4 * (lane >> 5) + (v & 3);
+          if (m < row_end) p.y[m * p.N + n] = (uint16_t)f32_to_bf16(acc[i][j][v]);
+        }
+      }
+    }
+  }
+};
+
+__global__ __launch_bounds__(512) void mx_gemm_kernel(MxArgs p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[MxTile::kLdsBytes];
+  const int64_t MT = (p.M + MxTile::BM - 1) / MxTile::BM, NT = (p.N + MxTile::BN - 1) / MxTile::BN;
+  const int64_t T = MT * NT;
+  // XCD-chunked tile order, m fastest inside an XCD's range
+  const int64_t per = (T + 7) / 8;
+  const int64_t t = (blockIdx.x % 8) * per + blockIdx.x / 8;
+  if (t >= T) return;
+  const int64_t tm = t % MT, tn = t / MT;
+  const int64_t row0 = tm * MxTile::BM;
+  const int64_t row_end = min(row0 + MxTile::BM, p.M);
+  f32x16 acc[MxTile::TM][MxTile::TN];
+  MxTile::mainloop(p, smem, acc, row0, row_end, (int)(tn * MxTile::BN / 16));
+  MxTile::epilogue(p, acc, row0, row_end, tn * MxTile::BN);
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+int64_t mx_scale_kb_bytes(int64_t rows_padded, int64_t K) { return ceil_div(K, 64) * rows_padded * 2; }
+
+hipError_t launch_mx_resolve(const uint8_t* w, const float* s, int64_t N, int64_t K, int64_t BN,
+                             int64_t BK, uint16_t* out, hipStream_t stream) {
+  const int64_t n = N * ceil_div(K, 8);
+  if (n == 0) return hipSuccess;
+  const int vec = (K % 8 == 0) && ((uintptr_t)w % 8 == 0) && ((uintptr_t)out % 16 == 0);
+  hipLaunchKernelGGL(mx_resolve_kernel, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, stream, w, s,
+                     N, K, BN, BK, out, vec);
+  return hipGetLastError();
+}
+
+hipError_t launch_mx_quant(const uint16_t* x, int64_t M, int64_t K, int scale_alg, uint8_t* payload,
+                           uint8_t* scale_rm, uint8_t* scale_kb, int64_t Mp, hipStream_t stream) {
+  const int64_t n = M * (K / 8);
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(mx_quant_kernel, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, stream, x, M, K,
+                     scale_alg, payload, scale_rm, scale_kb, Mp);
+  return hipGetLastError();
+}
+
+hipError_t launch_mx_scale_relayout(const uint8_t* src, int64_t R, int64_t K, int64_t Rp,
+                                    uint8_t* dst, hipStream_t stream) {
+  const int64_t n = ceil_div(K, 64) * Rp * 2;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(mx_scale_relayout_kernel, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, stream,
+                     src, R, K / 32, Rp, dst);
+  return hipGetLastError();
+}
+
+hipError_t launch_mx_gemm(const uint8_t* a, const uint8_t* a_scale_kb, int64_t Mp, int64_t M,
+                          int64_t K, const uint8_t* w_packed, const uint8_t* w_scale_kb, int64_t N,
+                          uint16_t* y, hipStream_t stream) {
+  if (M == 0) return hipSuccess;
+  MxArgs p{};
+  p.a = a;
+  p.a_scale = a_scale_kb;
+  p.Mp = Mp;
+  p.w = w_packed;
+  p.w_scale = w_scale_kb;
+  p.M = M;
+  p.N = N;
+  p.K = K;
+  p.KB = (int)ceil_div(K, 64);
+  p.NB = (int)ceil_div(N, 16);
+  p.y = y;
+  const int64_t T = ceil_div(M, MxTile::BM) * ceil_div(N, MxTile::BN);
+  hipLaunchKernelGGL(mx_gemm_kernel, dim3((unsigned)round_up(T, 8)), dim3(512), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace w8a8

@@ -1,0 +1,22 @@
+// Internal launchers of the MXFP8 kernels (host side).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace w8a8 {
+
+// bytes of k-block-major scales [ceil(K/64)][rows_padded][2]
+int64_t mx_scale_kb_bytes(int64_t rows_padded, int64_t K);
+hipError_t launch_mx_resolve(const uint8_t* w, const float* s, int64_t N, int64_t K, int64_t BN,
+                             int64_t BK, uint16_t* out, hipStream_t stream);
+// scale_rm: [M, K/32] (or null); scale_kb: [ceil(K/64)][Mp][2] (or null)
+hipError_t launch_mx_quant(const uint16_t* x, int64_t M, int64_t K, int scale_alg, uint8_t* payload,
+                           uint8_t* scale_rm, uint8_t* scale_kb, int64_t Mp, hipStream_t stream);
+hipError_t launch_mx_scale_relayout(const uint8_t* src, int64_t R, int64_t K, int64_t Rp,
+                                    uint8_t* dst, hipStream_t stream);
+hipError_t launch_mx_gemm(const uint8_t* a, const uint8_t* a_scale_kb, int64_t Mp, int64_t M,
+                          int64_t K, const uint8_t* w_packed, const uint8_t* w_scale_kb, int64_t N,
+                          uint16_t* y, hipStream_t stream);
+
+}  // namespace w8a8

@@ -28,7 +28,8 @@ import numpy as np
 import torch
 
 # stream tags
-_T_X, _T_W, _T_WS, _T_B, _T_LOGITS, _T_EBIAS, _T_W13, _T_W2, _T_W13S, _T_W2S = range(10)
+(_T_X, _T_W, _T_WS, _T_B, _T_LOGITS, _T_EBIAS, _T_W13, _T_W2, _T_W13S, _T_W2S, _T_MXW,
+ _T_MXS) = range(12)
 
 
 def rng_for(seed: int, tag: int, index: int = 0) -> np.random.Generator:
@@ -185,3 +186,31 @@ def moe(T: int = 2048, H: int = 4096, I: int = 2048, E: int = 256, top_k: int = 
     w13s = np.stack([scales(2 * I, seed, _T_W13S, e) for e in range(E)])
     w2s = np.stack([scales(H, seed, _T_W2S, e) for e in range(E)])
     return MoE(T, H, I, E, top_k, seed, x, row_token, group_list, w13s, w2s)
+
+
+# ---------------------------------------------------------------------------
+# MXFP8 variant inputs
+# ---------------------------------------------------------------------------
+
+def e4m3_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> E4M3FN codes with torch's CPU conversion (values must be in range)."""
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy().copy()
+
+
+@dataclass
+class MX:
+    x: np.ndarray            # BF16 bits [M, K]
+    w_e4m3: np.ndarray       # uint8 codes [N, K] (block-FP8 checkpoint payload)
+    scale_inv: np.ndarray    # f32 [ceil(N/bn), ceil(K/bk)]
+    bn: int
+    bk: int
+
+
+def mx_block_fp8(M: int = 2048, N: int = 5120, K: int = 17408, bn: int = 128, bk: int = 128,
+                 seed: int = 0) -> MX:
+    """MXFP8 workload: E4M3 weight [N, K] = RNE(N(0,1)) with fp32 weight_scale_inv per
+    bn x bk tile U[1e-3, 1e-2]; activations BF16 [M, K] N(0,1)."""
+    w = e4m3_bits(rng_for(seed, _T_MXW).standard_normal((N, K), dtype=np.float32))
+    s = rng_for(seed, _T_MXS).uniform(1e-3, 1e-2, size=(-(-N // bn), -(-K // bk))).astype(np.float32)
+    return MX(activations(M, K, 0.0, seed, index=5), w, s, bn, bk)

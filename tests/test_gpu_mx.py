@@ -1,0 +1,242 @@
+"""Parity of the MXFP8 variant (through the C ABI) with the CPU oracle.
+
+Resolve, MX quantization (payload and E8M0 bytes) are compared bit for bit;
+the block-scaled GEMM's BF16 output is checked against the unrounded float64
+product of the dequantized operands with max(2**-8 * |ref|, 1e-5). Inputs come
+from ``synth``; expected values only from ``oracle.mx``.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synth
+from tests.conftest import gpu_available
+from tests.gpu_util import DEV, bf16_dev, bf16_host, dev, host, show, sync
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
+
+MX = O.mx
+
+
+@pytest.fixture(scope="module")
+def w():
+    import moe_token_amax_amd as w
+    return w
+
+
+def _assert_eq(got, want, what):
+    got = np.asarray(got)
+    want = np.asarray(want)
+    assert got.shape == want.shape, (what, got.shape, want.shape)
+    bad = np.argwhere(got != want)
+    assert bad.size == 0, f"{what}: {len(bad)} mismatches, first at {bad[:5].tolist()}: " \
+                          f"got {got[tuple(bad[0])]} want {want[tuple(bad[0])]}"
+
+
+def _assert_tol(y_bits, ref64, what):
+    ok = O.bf16_within_tolerance(y_bits, ref64)
+    if not ok.all():
+        bad = np.argwhere(~ok)
+        i = tuple(bad[0])
+        got = O.bf16_to_f32(y_bits)[i]
+        raise AssertionError(f"{what}: {len(bad)} of {ok.size} outside tolerance, first {i}: "
+                             f"got {got} want {ref64[i]}")
+
+
+def _resolve_inputs(N, K, bn, bk, seed):
+    r = np.random.default_rng([seed, 77])
+    w8 = synth.e4m3_bits(r.standard_normal((N, K), dtype=np.float32))
+    s = r.uniform(1e-3, 1e-2, size=(-(-N // bn), -(-K // bk))).astype(np.float32)
+    return w8, s
+
+
+# ---------------------------------------------------------------------------
+# resolve (block-FP8 -> BF16)
+# ---------------------------------------------------------------------------
+
+RESOLVE_CASES = [(256, 512, 128, 128), (130, 300, 128, 128), (40, 96, 16, 32), (4, 8, 2, 4),
+                 (33, 17, 8, 8)]
+
+
+@pytest.mark.parametrize("N,K,bn,bk", RESOLVE_CASES)
+def test_mx_resolve_bit_exact(w, N, K, bn, bk):
+    show(f"mx_resolve N={N} K={K} bn={bn} bk={bk}")
+    w8, s = _resolve_inputs(N, K, bn, bk, seed=N + K)
+    w8[0, : min(K, 4)] = [0x00, 0x80, 0x01, 0x7E][: min(K, 4)]  # +0, -0, min subnormal, 448
+    got = w.mx_resolve_block_fp8(dev(w8), dev(s), bn, bk)
+    sync()
+    _assert_eq(bf16_host(got), MX.mx_resolve(w8, s, bn, bk), "resolve")
+
+
+# ---------------------------------------------------------------------------
+# MX quantization
+# ---------------------------------------------------------------------------
+
+MXQ_SHAPES = [(16, 256), (3, 32), (5, 96), (64, 2048), (2, 7168), (130, 544)]
+
+
+def _special_rows(xb):
+    """Rows that hit saturation, subnormal codes, ties, signed zeros, tiny groups."""
+    K = xb.shape[1]
+    f = np.zeros((6, K), np.float32)
+    f[0, :32] = np.linspace(-1.0, 1.875, 32)          # amax 1.875: saturates under rule 0
+    f[1, :32] = 2.0 ** -17                             # 2^-17 / 2^-8 = 2^-9: smallest subnormal
+    f[1, 0] = 1.0
+    f[1, 1:4] = [2.0 ** -18, 1.5 * 2.0 ** -18, -(2.0 ** -18)]   # tie to 0, round up, -0
+    f[2, :32] = np.arange(32, dtype=np.float32) / 16.0 + 1.0     # many exact ties
+    f[3, :32] = -0.0
+    f[4, :32] = 1e-39                                   # BF16/fp32 subnormals: clamp at -127
+    f[4, 1] = -3e-39
+    f[5, :32] = 3.0e38
+    f[5, 3] = -1.0
+    rows = synth.to_bf16_bits(f)
+    n = min(len(rows), xb.shape[0])
+    xb[:n] = rows[:n]
+    return xb
+
+
+@pytest.mark.parametrize("alg", [0, 1])
+@pytest.mark.parametrize("M,K", MXQ_SHAPES)
+def test_mx_quant_bit_exact(w, M, K, alg):
+    show(f"mx_quant M={M} K={K} alg={alg}")
+    xb = synth.activations(M, K, 0.01, seed=M * 7 + K)
+    xb = _special_rows(xb)
+    p, s = w.mx_quant(bf16_dev(xb), scale_alg=alg)
+    sync()
+    po, so = MX.mx_quant(O.bf16_to_f32(xb), alg)
+    _assert_eq(host(s), so, "e8m0")
+    _assert_eq(host(p), po, "e4m3")
+
+
+def test_mx_quant_empty(w):
+    p, s = w.mx_quant(torch.empty((0, 64), dtype=torch.bfloat16, device=DEV))
+    sync()
+    assert p.shape == (0, 64) and s.shape == (0, 2)
+
+
+def test_mx_k_not_multiple_of_32_is_unsupported(w):
+    x = torch.zeros((4, 48), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(w.W8A8Error) as e:
+        w.mx_quant(x, payload=torch.empty((4, 48), dtype=torch.uint8, device=DEV),
+                   scales=torch.empty((4, 1), dtype=torch.uint8, device=DEV))
+    assert e.value.status == 4
+
+
+# ---------------------------------------------------------------------------
+# block-scaled GEMM
+# ---------------------------------------------------------------------------
+
+def _mx_weight(w, N, K, seed):
+    """Resolve -> MX quant -> prepack on the GPU; oracle payload/scales alongside."""
+    w8, s = _resolve_inputs(N, K, 128, 128, seed)
+    wb = MX.mx_resolve(w8, s, 128, 128)
+    wp_o, ws_o = MX.mx_quant(O.bf16_to_f32(wb))
+    wp, ws = w.mx_quant(bf16_dev(wb))
+    packed = w.mx_prepack_weight(wp, ws)
+    sync()
+    _assert_eq(host(ws), ws_o, "weight e8m0")
+    _assert_eq(host(wp), wp_o, "weight e4m3")
+    return packed, wp_o, ws_o
+
+
+LINEAR_CASES = [(16, 128, 256), (100, 80, 288), (3, 16, 32), (257, 300, 512), (520, 520, 1056),
+                (1, 256, 4096), (300, 17, 96)]
+
+
+@pytest.mark.parametrize("M,N,K", LINEAR_CASES)
+def test_mx_linear_within_tolerance(w, M, N, K):
+    show(f"mx_linear M={M} N={N} K={K}")
+    packed, wp_o, ws_o = _mx_weight(w, N, K, seed=M + N + K)
+    xb = synth.activations(M, K, 0.005, seed=M * 3 + K)
+    y = w.mx_linear(bf16_dev(xb), packed, N)
+    sync()
+    ap_o, as_o = MX.mx_quant(O.bf16_to_f32(xb))
+    ref = MX.mx_gemm_ref64(ap_o, as_o, wp_o, ws_o)
+    _assert_tol(bf16_host(y), ref, "mx_linear")
+    # the pre-quantized branch (E4M3 + E8M0 handed in) gives the same bits
+    y2 = w.mx_linear(dev(ap_o), packed, N, x_e8m0=dev(as_o))
+    sync()
+    _assert_eq(bf16_host(y2), bf16_host(y), "pre-quantized branch")
+
+
+def test_mx_linear_scale_alg_1(w):
+    M, N, K = 64, 64, 256
+    show("mx_linear scale_alg=1")
+    packed, wp_o, ws_o = _mx_weight(w, N, K, seed=5)
+    xb = synth.activations(M, K, 0.01, seed=6)
+    y = w.mx_linear(bf16_dev(xb), packed, N, scale_alg=1)
+    sync()
+    ap_o, as_o = MX.mx_quant(O.bf16_to_f32(xb), 1)
+    _assert_tol(bf16_host(y), MX.mx_gemm_ref64(ap_o, as_o, wp_o, ws_o), "mx_linear alg 1")
+
+
+def test_mx_linear_zero_rows(w):
+    packed, _, _ = _mx_weight(w, 32, 64, seed=1)
+    y = w.mx_linear(torch.empty((0, 64), dtype=torch.bfloat16, device=DEV), packed, 32)
+    sync()
+    assert y.shape == (0, 32)
+    # an all-zero activation row gives exact zeros
+    y = w.mx_linear(torch.zeros((5, 64), dtype=torch.bfloat16, device=DEV), packed, 32)
+    sync()
+    assert not bf16_host(y).any() or np.all(O.bf16_to_f32(bf16_host(y)) == 0)
+
+
+@pytest.mark.timeout(900)
+def test_mx_block_fp8_full_size(w):
+    """Weight [5120, 17408] from 128x128-tile block FP8, activations [2048, 17408]:
+    full resolve and both MX quantizations bit-exact, GEMM rows sampled."""
+    show("mx full size: generate")
+    d = synth.mx_block_fp8()
+    N, K = d.w_e4m3.shape
+    M = d.x.shape[0]
+    wb = w.mx_resolve_block_fp8(dev(d.w_e4m3), dev(d.scale_inv), d.bn, d.bk)
+    wp, ws = w.mx_quant(wb)
+    packed = w.mx_prepack_weight(wp, ws)
+    x = bf16_dev(d.x)
+    y = w.mx_linear(x, packed, N)
+    ap, as_ = w.mx_quant(x)
+    sync()
+    show("mx full size: resolve")
+    wb_o = MX.mx_resolve(d.w_e4m3, d.scale_inv, d.bn, d.bk)
+    _assert_eq(bf16_host(wb), wb_o, "resolve")
+    show("mx full size: weight quant")
+    wp_o, ws_o = MX.mx_quant(O.bf16_to_f32(wb_o))
+    del wb_o
+    _assert_eq(host(ws), ws_o, "weight e8m0")
+    _assert_eq(host(wp), wp_o, "weight e4m3")
+    show("mx full size: activation quant")
+    ap_o, as_o = MX.mx_quant(O.bf16_to_f32(d.x))
+    _assert_eq(host(as_), as_o, "activation e8m0")
+    _assert_eq(host(ap), ap_o, "activation e4m3")
+    show("mx full size: sampled rows")
+    rows = np.unique(np.concatenate([[0, 255, 256, M - 1],
+                                     np.random.default_rng(3).choice(M, 12, replace=False)]))
+    ref = MX.mx_gemm_ref64(ap_o[rows], as_o[rows], wp_o, ws_o)
+    _assert_tol(bf16_host(y)[rows], ref, "mx_linear sampled rows")
+
+
+@pytest.mark.parametrize("M", [200, 201])
+def test_mx_gemm_stage_matches_linear(w, M):
+    N, K = 96, 352                  # K / 32 = 11: odd group count, ragged k-block
+    show("mx_gemm stage")
+    packed, _, _ = _mx_weight(w, N, K, seed=9)
+    xb = synth.activations(M, K, 0.01, seed=10)
+    ws = torch.empty((w.mx_linear_workspace_bytes(M, K),), dtype=torch.uint8, device=DEV)
+    y = w.mx_linear(bf16_dev(xb), packed, N, workspace=ws)
+    a, skb = w.mx_workspace_operands(ws, M, K)
+    y2 = w.mx_gemm(a, skb, packed, N)
+    sync()
+    _assert_eq(bf16_host(y2), bf16_host(y), "mx_gemm vs mx_linear")
+    ap_o, as_o = MX.mx_quant(O.bf16_to_f32(xb))
+    _assert_eq(host(a), ap_o, "workspace payload")
+    Mp = M + (M & 1)
+    kb = host(skb).reshape(-(-K // 64), Mp, 2)[:, :M]
+    want = np.zeros((-(-K // 64), M, 2), np.uint8)
+    for g in range(K // 32):
+        want[g // 2, :, g % 2] = as_o[:, g]
+    _assert_eq(kb, want, "workspace k-block-major scales")

@@ -24,7 +24,7 @@ def _hipcc():
 
 
 @pytest.mark.skipif(_hipcc() is None, reason="hipcc not available")
-@pytest.mark.parametrize("src", ["quant.hip", "prepack.hip", "gemm.hip"])
+@pytest.mark.parametrize("src", ["quant.hip", "prepack.hip", "gemm.hip", "mx.hip"])
 def test_kernels_use_no_array_scratch(src, tmp_path):
     from moe_token_amax_amd._build import FLAGS
     cmd = [_hipcc(), *FLAGS, "--cuda-device-only", "-c", os.path.join(CSRC, src), "-o",

@@ -63,3 +63,29 @@ def test_validation_before_launch(w):
     assert L.w8a8_grouped_gemm(p, p, p, 8, 2000, 16, 16, p, p, p, 0, None, 0, None) == 4
     assert L.w8a8_swiglu_quant(p, 4, 0, p, p, None) == 2
     assert L.w8a8_moe_grouped(p, None, p, 16, 4, 64, 32, p, p, p, p, p, None, 0, None) == 5
+
+
+def test_mx_validation_before_launch(w):
+    L = w.lib
+    p = ctypes.c_void_p(256)  # never dereferenced: validation fails first
+    # K must be a multiple of the MX group size 32: UNSUPPORTED, nothing launched
+    assert L.w8a8_mx_quant(p, 4, 48, p, p, 0, None) == 4
+    assert L.w8a8_mx_quant(p, 4, 48, p, p, 0, None) == 4 and b"32" in L.w8a8_last_error()
+    assert L.w8a8_mx_prepack_weight(p, p, 16, 100, p, None) == 4
+    assert L.w8a8_mx_linear(p, None, 4, 100, p, 16, p, 0, p, 1 << 20, None) == 4
+    assert L.w8a8_mx_quant(p, 4, 16, p, p, 0, None) == 2          # K < 32
+    assert L.w8a8_mx_quant(p, 4, 64, p, p, 2, None) == 4          # unknown scale rule
+    assert L.w8a8_mx_quant(None, 0, 64, None, None, 0, None) == 0  # M == 0 is a no-op
+    assert L.w8a8_mx_quant(None, 4, 64, None, None, 0, None) == 1
+    assert L.w8a8_mx_linear(p, None, 4, 64, p, 16, p, 0, None, 0, None) == 5
+    assert L.w8a8_mx_linear(p, None, 4, 64, ctypes.c_void_p(272), 16, p, 0, p, 1 << 20, None) == 3
+    assert L.w8a8_mx_resolve_block_fp8(p, p, 0, 64, 128, 128, p, None) == 2
+
+
+def test_mx_sizes(w):
+    # payload: N padded to 16, K to 64; scales: ceil(K/64) k-blocks x padded N x 2
+    assert w.mx_packed_bytes(5120, 17408) == 5120 * 17408 + 272 * 5120 * 2
+    assert w.mx_packed_bytes(17, 96) == 32 * 128 + 256
+    assert w.mx_linear_workspace_bytes(2048, 17408) == 2048 * 17408 + 272 * 2048 * 2
+    assert w.mx_linear_workspace_bytes(3, 32) == 256 + 256
+    assert w.mx_linear_workspace_bytes(257, 4096) == 257 * 4096 + 64 * 258 * 2
