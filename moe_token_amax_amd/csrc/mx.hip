@@ -281,11 +281,15 @@ struct MxTile {
 #pragma unroll
     for (int s = 0; s < STAGES - 1; ++s)
       if (s < KB) issue(p, src, smem, s, s, wave, lane);
-    // operand of 32 rows (columns) starting at block 2i: lane l reads block
-    // 2i + (l>>4 & 1), rows l & 15, k-chunks 2g and 2g + 1 with g = l >> 5
+    // Operand of 32 rows (columns) starting at 16-row block 2i. The scaled
+    // 32x32x64 MFMA takes, in lane l (row l & 31, h = l >> 5), bytes 0..15 =
+    // k [16h, 16h + 16) of the first 32-group and bytes 16..31 = k [32 + 16h,
+    // 48 + 16h) of the second, and lane l's scale byte belongs to group h. So
+    // lane l reads block 2i + (l>>4 & 1), row l & 15, 16-byte k-chunks h and
+    // h + 2, and the scale of (row, group h).
     const int lblk = (lane >> 4) & 1;
-    const int lofs = ((2 * (lane >> 5)) * 16 + (lane & 15)) * 16;
     const int g = lane >> 5;
+    const int lofs = (g * 16 + (lane & 15)) * 16;
     for (int kb = 0; kb < KB; ++kb) {
       const int ahead = KB - 1 - kb;
       wait_stage(ahead < STAGES - 2 ? ahead : STAGES - 2);
@@ -299,7 +303,7 @@ struct MxTile {
       for (int j = 0; j < TN; ++j) {
         const uint8_t* bp = st + (kABlocks + (wn * TN + j) * 2 + lblk) * 1024 + lofs;
         const i32x4 lo = *reinterpret_cast<const i32x4*>(bp);
-        const i32x4 hi = *reinterpret_cast<const i32x4*>(bp + 256);
+        const i32x4 hi = *reinterpret_cast<const i32x4*>(bp + 512);
         bf[j] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         sb[j] = sc[512 + ((wn * TN + j) * 32 + (lane & 31)) * 2 + g];
       }
@@ -307,7 +311,7 @@ struct MxTile {
       for (int i = 0; i < TM; ++i) {
         const uint8_t* ap = st + ((wm * TM + i) * 2 + lblk) * 1024 + lofs;
         const i32x4 lo = *reinterpret_cast<const i32x4*>(ap);
-        const i32x4 hi = *reinterpret_cast<const i32x4*>(ap + 256);
+        const i32x4 hi = *reinterpret_cast<const i32x4*>(ap + 512);
         const i32x8 af = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         const int sa = sc[((wm * TM + i) * 32 + (lane & 31)) * 2 + g];
 #pragma unroll
