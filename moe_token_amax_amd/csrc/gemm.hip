@@ -234,7 +234,7 @@ __device__ __forceinline__ void wait_vm_barrier() {
 }
 
 #ifndef W8A8_DMA_STAGES
-#define W8A8_DMA_STAGES 4
+#define W8A8_DMA_STAGES 5
 #endif
 #ifndef W8A8_DMA_GROUP_M
 #define W8A8_DMA_GROUP_M 8
@@ -259,8 +259,8 @@ struct DmaTile {
   static constexpr int kStageBytes = kBlocks * kBlockBytes;
   static constexpr int kLdsBytes = STAGES * kStageBytes;
   static_assert(kBlocks % kWaves == 0 && TM >= 2 && TM % 2 == 0 && TN >= 1, "tile shape");
-  static_assert(STAGES >= 3 && STAGES <= 5, "stages");
-  static_assert((STAGES - 2) * kPerWave <= 63, "vmcnt range");
+  static_assert(STAGES == 5, "stages");
+  static_assert(3 * kPerWave <= 63, "vmcnt range");
 
   // Per-tile DMA sources of this wavefront's kPerWave blocks: the address of
   // k-block 0 and the step per k-block (64 bytes along an A row, 1 KB through
@@ -311,15 +311,6 @@ struct DmaTile {
     __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
   }
 
-  // later = k-blocks issued after the one about to be read (<= STAGES - 2):
-  // their loads may stay in flight
-  __device__ __forceinline__ static void wait_stage(int later) {
-    if (STAGES >= 5 && later >= 3) wait_vm_barrier<(STAGES >= 5 ? 3 : 0) * kPerWave>();
-    else if (STAGES >= 4 && later >= 2) wait_vm_barrier<(STAGES >= 4 ? 2 : 0) * kPerWave>();
-    else if (later >= 1) wait_vm_barrier<kPerWave>();
-    else wait_vm_barrier<0>();
-  }
-
   __device__ __forceinline__ static void read_frags(const uint8_t* st, Frags& f, int wm, int wn,
                                                     int lane) {
 #pragma unroll
@@ -331,32 +322,38 @@ struct DmaTile {
       f.a[i] = *reinterpret_cast<const i32x4*>(st + (wm * TM + i) * kBlockBytes + lane * 16);
   }
 
-  // Row i of this wavefront's blocks; skipped (wave-uniform) when the 16-row
-  // block lies past the tile's last valid row, so a short tile (the last
-  // m-tile of an expert) costs MFMA time for its valid 16-row blocks only.
-  __device__ __forceinline__ static void mfma_row(const Frags& f, i32x4 (&acc)[TM][TN], int i,
-                                                  int row_blocks) {
-    if (i >= row_blocks) return;
+  __device__ __forceinline__ static void mfma_row(const Frags& f, i32x4 (&acc)[TM][TN], int i) {
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = mfma16x16x64(f.a[i], f.b[j], acc[i][j]);
   }
 
-  // Full K loop: rows [row0, row_end) (row_end > row0), weights of expert e from
-  // n-block nb0. Ends with every wavefront past its last LDS read of smem.
+  __device__ __forceinline__ static void mfma_rows(const Frags& f, i32x4 (&acc)[TM][TN], int lo,
+                                                   int hi) {
+#pragma unroll
+    for (int i = lo; i < hi; ++i) mfma_row(f, acc, i);
+  }
+
+  // Full K loop over rows [row0, row_end) (row_end > row0), weights of expert
+  // e from n-block nb0. Rows past row_end are read clamped and computed; only
+  // the epilogue drops them. Ends with every wavefront past its last LDS read.
   //
-  // Software pipeline of one k-block (stage) kb, with its fragments already in
-  // registers (F):
-  //   1. first half of the MFMA rows of F, with the DMA loads of k-block
-  //      kb + STAGES - 1 issued between the rows;
-  //   2. wait for this wavefront's loads of k-block kb + 1, s_barrier (so every
-  //      wavefront's loads of it landed and every read of the buffer about to
-  //      be refilled is done), then LDS reads of its fragments (G);
-  //   3. second half of the MFMA rows of F while those reads are in flight.
-  // With one wavefront per SIMD the LDS latency, the barrier and the DMA issue
-  // thus overlap the MFMAs instead of stalling them.
+  // The ring holds five k-blocks (the whole 160 KB of LDS) and advances two at
+  // a time, with one wait + barrier per pair of k-blocks (kb, kb + 1) whose
+  // fragments are F and G:
+  //   F rows 0..H-1 | LDS reads of G | F rows H..TM-1 | G rows 0..H-1 |
+  //   wait for the DMA of kb + 2, kb + 3 (kb + 4 stays in flight), s_barrier |
+  //   DMA of kb + 5, kb + 6 into the buffers of kb, kb + 1 | LDS reads of the
+  //   next F (kb + 2) | G rows H..TM-1.
+  // So two to three k-blocks of DMA are always in flight (a wait for every
+  // load at each barrier would drain the DMA queue and expose its latency once
+  // per pair), one barrier per two k-blocks keeps the two wavefronts of a SIMD
+  // out of lockstep (a barrier per k-block cost about a fifth of the loop),
+  // the LDS reads run under MFMAs, and F / G are distinct register sets, so no
+  // fragment or accumulator is copied.
   __device__ __forceinline__ static void mainloop(const GemmArgs& p, uint8_t* smem,
                                                   i32x4 (&acc)[TM][TN], int64_t row0,
                                                   int64_t row_end, int e, int nb0) {
+    static_assert(STAGES == 5, "the pairwise ring needs five k-block buffers");
     const int lane = threadIdx.x & 63;
     // wave index as a scalar: per-wave choices are uniform branches and the
     // LDS destination of every DMA is an SGPR (M0)
@@ -364,9 +361,7 @@ struct DmaTile {
     const int wm = wave / WN, wn = wave % WN;
     const int64_t wblk0 = (int64_t)e * p.NB * p.KB;
     const int KB = p.KB;
-    // 16-row blocks of this wavefront that hold valid rows (wave-uniform)
-    const int64_t valid = row_end - row0 - (int64_t)wm * TM * 16;
-    const int row_blocks = valid <= 0 ? 0 : (valid >= TM * 16 ? TM : (int)((valid + 15) / 16));
+    constexpr int H = TM / 2;
     Src src;
     sources(p, src, wave, lane, row0, row_end - 1, wblk0, nb0);
 #pragma unroll
@@ -374,39 +369,52 @@ struct DmaTile {
 #pragma unroll
       for (int j = 0; j < TN; ++j) acc[i][j] = i32x4{0, 0, 0, 0};
 #pragma unroll
-    for (int s = 0; s < STAGES - 1; ++s)
+    for (int s = 0; s < 5; ++s)
       if (s < KB) {
 #pragma unroll
         for (int i = 0; i < kPerWave; ++i) issue_one(p, src, smem, s, s, wave, lane, i);
       }
-    wait_stage(KB - 1 < STAGES - 2 ? KB - 1 : STAGES - 2);
-    Frags F;
+    // k-blocks 0 and 1 landed; 2, 3 and 4 may still be in flight
+    if (KB >= 5) wait_vm_barrier<3 * kPerWave>();
+    else if (KB == 4) wait_vm_barrier<2 * kPerWave>();
+    else if (KB == 3) wait_vm_barrier<kPerWave>();
+    else wait_vm_barrier<0>();
+    Frags F, G;
     read_frags(smem, F, wm, wn, lane);
-    for (int kb = 0; kb < KB; ++kb) {
-      const int nk = kb + STAGES - 1;
-      const bool more = nk < KB;
-      const int nbuf = nk % STAGES;
-      constexpr int H = TM / 2;
+    int buf = 0;  // ring buffer of k-block kb (kb % 5)
+    for (int kb = 0; kb < KB; kb += 2) {
+      const int buf1 = buf == 4 ? 0 : buf + 1;
+      const int buf2 = buf1 == 4 ? 0 : buf1 + 1;
+      const bool has1 = kb + 1 < KB;
+      const bool more = kb + 2 < KB;
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_rows(F, acc, 0, H);
+      __builtin_amdgcn_sched_barrier(0);
+      if (has1) read_frags(smem + buf1 * kStageBytes, G, wm, wn, lane);
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_rows(F, acc, H, TM);
+      __builtin_amdgcn_sched_barrier(0);
+      if (has1) mfma_rows(G, acc, 0, H);
+      __builtin_amdgcn_sched_barrier(0);
+      if (more) {
+        // every wavefront's DMA of kb + 2 and kb + 3 landed (kb + 4 may still
+        // be in flight), every read of the buffers of kb and kb + 1 done;
+        // refill those with kb + 5 and kb + 6
+        if (kb + 4 < KB) wait_vm_barrier<kPerWave>();
+        else wait_vm_barrier<0>();
+        if (kb + 5 < KB) {
 #pragma unroll
-      for (int i = 0; i < H; ++i) {
+          for (int i = 0; i < kPerWave; ++i) issue_one(p, src, smem, buf, kb + 5, wave, lane, i);
+        }
+        if (kb + 6 < KB) {
 #pragma unroll
-        for (int d = (i * kPerWave) / H; d < ((i + 1) * kPerWave) / H; ++d)
-          if (more) issue_one(p, src, smem, nbuf, nk, wave, lane, d);
-        __builtin_amdgcn_sched_barrier(0);
-        mfma_row(F, acc, i, row_blocks);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      Frags G = F;
-      if (kb + 1 < KB) {
-        const int later = KB - 2 - kb;
-        wait_stage(later < STAGES - 2 ? later : STAGES - 2);
-        read_frags(smem + ((kb + 1) % STAGES) * kStageBytes, G, wm, wn, lane);
+          for (int i = 0; i < kPerWave; ++i) issue_one(p, src, smem, buf1, kb + 6, wave, lane, i);
+        }
+        read_frags(smem + buf2 * kStageBytes, F, wm, wn, lane);
       }
       __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int i = H; i < TM; ++i) mfma_row(F, acc, i, row_blocks);
-      __builtin_amdgcn_sched_barrier(0);
-      F = G;
+      if (has1) mfma_rows(G, acc, H, TM);
+      buf = buf2;
     }
     // all LDS reads of this tile done in every wavefront before smem is reused
     wait_vm_barrier<0>();
