@@ -386,7 +386,7 @@ class MxWorkload(Workload):
         self.w.mx_linear(self.x, self.packed, self.N, y=self.y, workspace=self.ws)
 
     def _gemm(self):
-        self.w.mx_gemm(self.a_e4m3, self.a_skb, self.packed, self.N, y=self.y2)
+        self.w.mx_gemm(self.a_e4m3, self.a_skb, self.M, self.K, self.packed, self.N, y=self.y2)
 
     def flops(self):
         return 2.0 * self.M * self.N * self.K

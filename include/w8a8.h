@@ -221,15 +221,17 @@ int w8a8_mx_linear(const void* x, const uint8_t* x_e8m0, int64_t M, int64_t K,
 
 /*
  * w8a8_mx_gemm  [MXFP8 Deep Dive 5, the block-scaled matmul alone]: the GEMM
- *   stage of w8a8_mx_linear, for stage-wise tests and timing. a_e4m3: E4M3
- *   [M, K] row-major, 16-byte aligned; a_scale_kb: E8M0 bytes "k-block major",
- *   [ceil(K/64)][Mp][2] with Mp = M rounded up to even, 4-byte aligned (the
- *   two 32-groups of one 64-deep k-block of a row adjacent; when K/32 is odd
- *   the last k-block's second byte of every row must be 0; the pad row, if
- *   any, is never used).
- *   After a BF16 call of w8a8_mx_linear its workspace holds exactly these two
- *   operands: the payload at offset 0, the scales at offset M*K rounded up to
- *   256. w_packed as for w8a8_mx_linear; y BF16 [M, N].
+ *   stage of w8a8_mx_linear, for stage-wise tests and timing. a_e4m3: the
+ *   E4M3 activation in the packed block layout of w8a8_prepack_weight (1 KB
+ *   blocks [ceil(M/16)][ceil(K/64)], K zero-padded to 64), 256-byte aligned;
+ *   a_scale_kb: E8M0 bytes "k-block major", [ceil(K/64)][Mp][2] with Mp = M
+ *   rounded up to even, 4-byte aligned (the two 32-groups of one 64-deep
+ *   k-block of a row adjacent; when K/32 is odd the last k-block's second
+ *   byte of every row must be 0; the pad row, if any, is never used).
+ *   After a call of w8a8_mx_linear its workspace holds exactly these two
+ *   operands: the blocks at offset 0, the scales at offset
+ *   ceil(M/16) * 16 * ceil(K/64) * 64 rounded up to 256. w_packed as for
+ *   w8a8_mx_linear; y BF16 [M, N].
  */
 int w8a8_mx_gemm(const uint8_t* a_e4m3, const uint8_t* a_scale_kb, int64_t M, int64_t K,
                  const void* w_packed, int64_t N, uint16_t* y, void* stream);

@@ -370,22 +370,26 @@ def mx_linear(x: torch.Tensor, w_packed: torch.Tensor, N: int, x_e8m0: torch.Ten
 
 
 def mx_workspace_operands(workspace: torch.Tensor, M: int, K: int):
-    """(E4M3 payload [M, K], k-block-major E8M0 bytes) views of an mx_linear workspace."""
+    """(E4M3 payload in 1 KB P16x64 blocks, k-block-major E8M0 bytes) views of an
+    mx_linear workspace."""
     _need(workspace, torch.uint8, "workspace", 1)
-    off = -(-M * K // 256) * 256
+    nblk = -(-M // 16) * 16 * (-(-K // 64)) * 64
+    off = -(-nblk // 256) * 256
     nsc = -(-K // 64) * (M + (M & 1)) * 2
     if workspace.numel() < off + nsc:
         raise ValueError("workspace too small")
-    return workspace[:M * K].view(M, K), workspace[off:off + nsc]
+    return workspace[:nblk], workspace[off:off + nsc]
 
 
-def mx_gemm(a_e4m3: torch.Tensor, a_scale_kb: torch.Tensor, w_packed: torch.Tensor, N: int,
-            y: torch.Tensor | None = None) -> torch.Tensor:
-    """GEMM stage of mx_linear: E4M3 [M, K] + k-block-major E8M0 -> BF16 [M, N]."""
-    _need(a_e4m3, torch.uint8, "a_e4m3", 2)
+def mx_gemm(a_e4m3: torch.Tensor, a_scale_kb: torch.Tensor, M: int, K: int,
+            w_packed: torch.Tensor, N: int, y: torch.Tensor | None = None) -> torch.Tensor:
+    """GEMM stage of mx_linear: E4M3 activation blocks (as mx_workspace_operands
+    gives them) + k-block-major E8M0 -> BF16 [M, N]."""
+    _need(a_e4m3, torch.uint8, "a_e4m3", 1)
     _need(a_scale_kb, torch.uint8, "a_scale_kb", 1)
     _need(w_packed, torch.uint8, "w_packed", 1)
-    M, K = a_e4m3.shape
+    if a_e4m3.numel() < -(-M // 16) * 16 * (-(-K // 64)) * 64:
+        raise ValueError("a_e4m3 too small for [M, K] in blocks")
     if a_scale_kb.numel() < -(-K // 64) * (M + (M & 1)) * 2:
         raise ValueError("a_scale_kb must hold ceil(K/64) * (M rounded up to even) * 2 bytes")
     if w_packed.numel() < mx_packed_bytes(N, K):

@@ -251,7 +251,8 @@ int w8a8_mx_quant(const uint16_t* x, int64_t M, int64_t K, uint8_t* e4m3, uint8_
   if (M == 0) return ok();
   if (!x || !e4m3 || !e8m0) return fail(W8A8_ERR_NULL, "mx_quant: null pointer");
   if (!aligned(x, 16) || !aligned(e4m3, 8)) return fail(W8A8_ERR_ALIGN, "mx_quant: x needs 16-byte, e4m3 8-byte alignment");
-  return launched(w8a8::launch_mx_quant(x, M, K, scale_alg, e4m3, e8m0, nullptr, 0, (hipStream_t)stream),
+  return launched(w8a8::launch_mx_quant(x, M, K, scale_alg, e4m3, false, e8m0, nullptr, 0,
+                                        (hipStream_t)stream),
                   "mx_quant");
 }
 
@@ -287,7 +288,7 @@ int w8a8_mx_prepack_weight(const uint8_t* w_e4m3, const uint8_t* w_e8m0, int64_t
 
 int64_t w8a8_mx_linear_workspace_bytes(int64_t M, int64_t K) {
   if (M < 1 || K < 1) return 0;
-  return align256(M * K) + align256(w8a8::mx_scale_kb_bytes(w8a8::round_up(M, 2), K));
+  return mx_payload_bytes(M, K) + align256(w8a8::mx_scale_kb_bytes(w8a8::round_up(M, 2), K));
 }
 
 int w8a8_mx_linear(const void* x, const uint8_t* x_e8m0, int64_t M, int64_t K, const void* w_packed,
@@ -307,25 +308,25 @@ int w8a8_mx_linear(const void* x, const uint8_t* x_e8m0, int64_t M, int64_t K, c
                 (long long)need, (long long)ws_bytes);
   hipStream_t s = (hipStream_t)stream;
   uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
+  // workspace: the activation payload in P16x64 blocks, then its k-block-major scales
   uint8_t* a_payload = ws;
-  uint8_t* a_scale_kb = ws + align256(M * K);
+  uint8_t* a_scale_kb = ws + mx_payload_bytes(M, K);
   const int64_t Mp = w8a8::round_up(M, 2);  // even row count: dword-aligned scale pairs
   hipError_t e;
-  const uint8_t* a;
   if (!x_e8m0) {
-    // BF16 activation: dynamic MX quantization first
-    e = w8a8::launch_mx_quant(reinterpret_cast<const uint16_t*>(x), M, K, scale_alg, a_payload,
+    // BF16 activation: dynamic MX quantization, written straight into blocks
+    e = w8a8::launch_mx_quant(reinterpret_cast<const uint16_t*>(x), M, K, scale_alg, a_payload, true,
                               nullptr, a_scale_kb, Mp, s);
     if (e != hipSuccess) return launched(e, "mx_linear: quant");
-    a = a_payload;
   } else {
     // pre-quantized activation: E4M3 [M, K] with its row-major E8M0 [M, K/32]
+    e = w8a8::launch_prepack(reinterpret_cast<const int8_t*>(x), 1, M, K, a_payload, s);
+    if (e != hipSuccess) return launched(e, "mx_linear: payload");
     e = w8a8::launch_mx_scale_relayout(x_e8m0, M, K, Mp, a_scale_kb, s);
     if (e != hipSuccess) return launched(e, "mx_linear: scales");
-    a = reinterpret_cast<const uint8_t*>(x);
   }
   const uint8_t* wp = reinterpret_cast<const uint8_t*>(w_packed);
-  e = w8a8::launch_mx_gemm(a, a_scale_kb, Mp, M, K, wp, wp + mx_payload_bytes(N, K), N, y, s);
+  e = w8a8::launch_mx_gemm(a_payload, a_scale_kb, Mp, M, K, wp, wp + mx_payload_bytes(N, K), N, y, s);
   return launched(e, "mx_linear: gemm");
 }
 
@@ -336,8 +337,8 @@ int w8a8_mx_gemm(const uint8_t* a_e4m3, const uint8_t* a_scale_kb, int64_t M, in
   if (M < 0 || N < 1 || M >= kMaxDim || N >= kMaxDim) return fail(W8A8_ERR_SHAPE, "mx_gemm: bad M or N");
   if (M == 0) return ok();
   if (!a_e4m3 || !a_scale_kb || !w_packed || !y) return fail(W8A8_ERR_NULL, "mx_gemm: null pointer");
-  if (!aligned(a_e4m3, 16) || !aligned(a_scale_kb, 4) || !aligned(w_packed, 256) || !aligned(y, 2))
-    return fail(W8A8_ERR_ALIGN, "mx_gemm: a needs 16-byte, scales 4-byte, w_packed 256-byte alignment");
+  if (!aligned(a_e4m3, 256) || !aligned(a_scale_kb, 4) || !aligned(w_packed, 256) || !aligned(y, 2))
+    return fail(W8A8_ERR_ALIGN, "mx_gemm: a needs 256-byte, scales 4-byte, w_packed 256-byte alignment");
   const uint8_t* wp = reinterpret_cast<const uint8_t*>(w_packed);
   return launched(w8a8::launch_mx_gemm(a_e4m3, a_scale_kb, w8a8::round_up(M, 2), M, K, wp,
                                        wp + mx_payload_bytes(N, K), N, y, (hipStream_t)stream),

@@ -13,8 +13,9 @@
 // the smallest E with amax / 2^E <= 448 (scale rule 1), clamped to
 // [-127, 127]; amax == 0 gives byte 0.
 //
-// Layouts: payloads are row-major [rows, K] (activations) or prepacked into
-// the P16x64 blocks of the INT8 path (weights). Scales at the C ABI are
+// Layouts: payloads are row-major [rows, K] at the C ABI; the GEMM reads both
+// operands in the P16x64 blocks of the INT8 path (the weight prepacked at
+// load time, the activation written that way by the MX quant of the linear). Scales at the C ABI are
 // row-major [rows, K/32]; the GEMM reads them "k-block major",
 // [K/64][rows_p][2] (the two 32-groups of one 64-deep k-block of a row are
 // adjacent; rows_p = rows rounded up to even for activations, to 16 for
@@ -105,7 +106,7 @@ __global__ __launch_bounds__(256) void mx_resolve_kernel(const uint8_t* __restri
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void mx_quant_kernel(const uint16_t* __restrict__ x, int64_t M,
                                                        int64_t K, int scale_alg,
-                                                       uint8_t* __restrict__ payload,
+                                                       uint8_t* __restrict__ payload, int blocked,
                                                        uint8_t* __restrict__ scale_rm,
                                                        uint8_t* __restrict__ scale_kb,
                                                        int64_t Mp) {
@@ -132,7 +133,19 @@ __global__ __launch_bounds__(256) void mx_quant_kernel(const uint16_t* __restric
   uint2 o;
   o.x = b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24);
   o.y = b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24);
-  *reinterpret_cast<uint2*>(payload + row * K + c * 8) = o;
+  if (!blocked) {
+    *reinterpret_cast<uint2*>(payload + row * K + c * 8) = o;
+  } else {
+    // P16x64 blocks [row / 16][k / 64], byte (row % 16 + 16 * (k % 64 / 16)) * 16 + k % 16
+    const int64_t KB = (K + 63) / 64;
+    const int64_t k = c * 8;
+    const int64_t blk = (row / 16) * KB + k / 64;
+    const int64_t at = blk * 1024 + ((row & 15) + 16 * ((k & 63) >> 4)) * 16 + (k & 15);
+    *reinterpret_cast<uint2*>(payload + at) = o;
+    // a ragged last k-block (K % 64 == 32): its upper 32 bytes per row are
+    // zero, the partners of the weight's zero padding
+    if ((K & 63) && k >= K - 32) *reinterpret_cast<uint2*>(payload + at + 32 * 16) = uint2{0u, 0u};
+  }
   if ((c & 3) == 0) {
     const int64_t g = c / 4;                 // 32-group index along K
     const uint8_t sb = (uint8_t)(e + 127);
@@ -159,17 +172,19 @@ __global__ __launch_bounds__(256) void mx_scale_relayout_kernel(const uint8_t* _
 }
 
 // ---------------------------------------------------------------------------
-// Block-scaled GEMM tile: 256 x 256, 8 wavefronts (2 x 4) of 128 x 64, each a
-// 4 x 2 grid of 32 x 32 fp32 accumulator blocks. One 64-deep k-block per
-// stage; a stage holds 16 A blocks + 16 B blocks (1 KB each, MFMA operand
-// order) + 1 KB of scales (256 A rows x 2, then 256 B columns x 2), filled by
-// LDS-DMA: every wavefront issues 4 payload blocks (16 bytes per lane) and one
-// 128-byte scale slice (4 bytes per lane on lanes 0..31) per stage, so every
-// wavefront has the same number of loads in flight per stage. The rest of the pipeline is the INT8 tile's: a ring of
-// STAGES buffers, "s_waitcnt vmcnt(...) lgkmcnt(0); s_barrier" per stage.
+// Block-scaled GEMM tile: 192 x 256 (M x N), 8 wavefronts (2 x 4) of 96 x 64,
+// each a 3 x 2 grid of 32 x 32 fp32 accumulator blocks, one 64-deep k-block
+// per stage. A stage holds 12 A blocks + 16 B blocks (1 KB each, MFMA operand
+// order) + 1 KB of scales (192 A rows x 2 at byte 0, 256 B columns x 2 at
+// byte 512). 192-row tiles give 220 tiles for a 2048 x 5120 output, one round
+// on 256 CUs (256-row tiles would give 160). Every wavefront issues 5 LDS-DMA
+// loads per stage: wavefronts 0..3 four payload blocks and one scale slice,
+// 4..7 three payload blocks and two scale slices (the seven 128-byte slices
+// of a stage, the spare ones repeating the last slice: identical bytes to the
+// same place), so the per-wavefront vmcnt bookkeeping is uniform.
 // ---------------------------------------------------------------------------
 struct MxArgs {
-  const uint8_t* a;        // E4M3 [M, K] row-major
+  const uint8_t* a;        // E4M3, P16x64 blocks [ceil(M/16)][KB] (K zero-padded to 64)
   const uint8_t* a_scale;  // k-block-major [KB][Mp][2], Mp even
   int64_t Mp;
   const uint8_t* w;        // packed E4M3 (P16x64), NB x KB blocks
@@ -188,84 +203,164 @@ typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 struct MxTile {
-  static constexpr int BM = 256, BN = 256, STAGES = 4, WM = 2, WN = 4, kWaves = 8;
-  static constexpr int TM = BM / WM / 32;  // 4
+  static constexpr int BM = 192, BN = 256, WM = 2, WN = 4, kWaves = 8, RING = 5;
+  static constexpr int TM = BM / WM / 32;  // 3
   static constexpr int TN = BN / WN / 32;  // 2
-  static constexpr int kABlocks = BM / 16, kBBlocks = BN / 16;
-  static constexpr int kPerWave = (kABlocks + kBBlocks) / kWaves;  // 4 payload blocks
-  static constexpr int kVmPerStage = kPerWave + 1;                 // + one scale slice
-  static constexpr int kScaleBytes = 1024;
-  static constexpr int kStageBytes = (kABlocks + kBBlocks) * 1024 + kScaleBytes;
-  static constexpr int kLdsBytes = STAGES * kStageBytes;
+  static constexpr int kABlocks = BM / 16, kBBlocks = BN / 16;  // 12, 16
+  static constexpr int kLoads = 5;                              // DMA per wavefront per stage
+  static constexpr int kScaleOfs = (kABlocks + kBBlocks) * 1024;
+  static constexpr int kStageBytes = kScaleOfs + 1024;
+  static constexpr int kLdsBytes = RING * kStageBytes;
+  static_assert(kABlocks + kBBlocks == 4 * 4 + 4 * 3, "payload split over the wavefronts");
+  static_assert(kLdsBytes <= 163840, "LDS");
 
+  // DMA sources of one wavefront: payload blocks (16 bytes per lane) and scale
+  // slices (4 bytes per lane on lanes 0..31), k-block 0 address + step.
   struct Src {
-    const uint8_t* base[kPerWave];
-    int64_t step[kPerWave];
-    const uint8_t* sbase;   // scale slice of k-block 0
-    int64_t sstep;
+    const uint8_t* pbase[4];
+    int64_t pstep[4];
+    int pdst[4];            // LDS offset inside a stage
+    const uint8_t* sbase[2];
+    int64_t sstep[2];
+    int sdst[2];
   };
+
+  __device__ __forceinline__ static void payload_src(const MxArgs& p, int bi, int lane, int64_t row0,
+                                                     int64_t row_last, int nb0, const uint8_t*& base,
+                                                     int64_t& step) {
+    if (bi < kABlocks) {
+      // A in the P16x64 block layout: 16-row block mb, k-block kb at
+      // (mb * KB + kb) KB; blocks past the last one are read clamped
+      int64_t mb = row0 / 16 + bi;
+      mb = mb < row_last / 16 ? mb : row_last / 16;
+      base = p.a + mb * p.KB * 1024 + lane * 16;
+      step = 1024;
+    } else {
+      int nb = nb0 + (bi - kABlocks);
+      nb = nb < p.NB ? nb : p.NB - 1;
+      base = p.w + (int64_t)nb * p.KB * 1024 + lane * 16;
+      step = 1024;
+    }
+  }
+
+  // scale slice q (0..6): A rows [64q, 64q + 64) for q < 3, else B columns
+  // [64(q-3), 64(q-3) + 64); lanes 0..31 bring two rows (columns) each
+  __device__ __forceinline__ static void scale_src(const MxArgs& p, int q, int lane, int64_t row0,
+                                                   int nb0, const uint8_t*& base, int64_t& step,
+                                                   int& dst) {
+    if (q < 3) {
+      int64_t r = row0 + q * 64 + 2 * (lane & 31);
+      r = r < p.Mp - 2 ? r : p.Mp - 2;
+      base = p.a_scale + r * 2;
+      step = p.Mp * 2;
+      dst = kScaleOfs + q * 128;
+    } else {
+      const int64_t np = (int64_t)p.NB * 16;
+      int64_t c = (int64_t)nb0 * 16 + (q - 3) * 64 + 2 * (lane & 31);
+      c = c < np - 2 ? c : np - 2;
+      base = p.w_scale + c * 2;
+      step = np * 2;
+      dst = kScaleOfs + 512 + (q - 3) * 128;
+    }
+  }
 
   __device__ __forceinline__ static void sources(const MxArgs& p, Src& s, int wave, int lane,
                                                  int64_t row0, int64_t row_last, int nb0) {
+    // payload: wavefronts 0..3 blocks 4w..4w+3, 4..7 blocks 16+3(w-4)..+2
+    const int first = wave < 4 ? 4 * wave : 16 + 3 * (wave - 4);
+    const int count = wave < 4 ? 4 : 3;
 #pragma unroll
-    for (int i = 0; i < kPerWave; ++i) {
-      const int bi = wave * kPerWave + i;
-      if (bi < kABlocks) {
-        int64_t row = row0 + bi * 16 + (lane & 15);
-        row = row < row_last ? row : row_last;
-        s.base[i] = p.a + row * p.K + (lane >> 4) * 16;
-        s.step[i] = 64;
-      } else {
-        int nb = nb0 + (bi - kABlocks);
-        nb = nb < p.NB ? nb : p.NB - 1;
-        s.base[i] = p.w + (int64_t)nb * p.KB * 1024 + lane * 16;
-        s.step[i] = 1024;
-      }
+    for (int i = 0; i < 4; ++i) {
+      const int bi = first + (i < count ? i : count - 1);
+      payload_src(p, bi, lane, row0, row_last, nb0, s.pbase[i], s.pstep[i]);
+      s.pdst[i] = bi * 1024;
     }
-    // scale slice: wavefronts 0..3 -> A rows [64w, 64w + 64), 4..7 -> B columns;
-    // lanes 0..31 each bring one dword = the scale pairs of two rows (columns).
-    // Rows past the padded count are clamped; their outputs are discarded.
-    if (wave < 4) {
-      int64_t r = row0 + wave * 64 + 2 * (lane & 31);
-      r = r < p.Mp - 2 ? r : p.Mp - 2;
-      s.sbase = p.a_scale + r * 2;
-      s.sstep = p.Mp * 2;
-    } else {
-      const int64_t np = (int64_t)p.NB * 16;
-      int64_t c = (int64_t)nb0 * 16 + (wave - 4) * 64 + 2 * (lane & 31);
-      c = c < np - 2 ? c : np - 2;
-      s.sbase = p.w_scale + c * 2;
-      s.sstep = np * 2;
-    }
+    // scale slices: wavefronts 0..3 slice w; 4: 4, 5; 5: 6, 6; 6, 7: 6, 6
+    const int q0 = wave < 4 ? wave : (wave == 4 ? 4 : 6);
+    const int q1 = wave == 4 ? 5 : 6;
+    scale_src(p, q0, lane, row0, nb0, s.sbase[0], s.sstep[0], s.sdst[0]);
+    scale_src(p, q1, lane, row0, nb0, s.sbase[1], s.sstep[1], s.sdst[1]);
   }
 
-  __device__ __forceinline__ static void issue(const MxArgs& p, const Src& s, uint8_t* smem,
-                                               int buf, int kb, int wave, int lane) {
+  // the 5 loads of k-block kb into ring buffer buf
+  __device__ __forceinline__ static void issue(const MxArgs& p, const Src& s, uint8_t* smem, int buf,
+                                               int kb, int wave, int lane) {
     uint8_t* st = smem + buf * kStageBytes;
+    const bool four = wave < 4;
 #pragma unroll
-    for (int i = 0; i < kPerWave; ++i) {
-      const int bi = wave * kPerWave + i;
-      const uint8_t* src = s.base[i] + kb * s.step[i];
-      if (bi < kABlocks && (p.K & 63) && kb == p.KB - 1) {
-        const int64_t col = (int64_t)kb * 64 + (lane >> 4) * 16;
-        if (col > p.K - 16) src -= col - (p.K - 16);  // stay inside the row
-      }
-      __builtin_amdgcn_global_load_lds(src, (W8A8_LDS_MX void*)((W8A8_LDS_MX uint8_t*)st + bi * 1024),
+    for (int i = 0; i < 4; ++i) {
+      if (i == 3 && !four) break;
+      const uint8_t* src = s.pbase[i] + kb * s.pstep[i];
+      __builtin_amdgcn_global_load_lds(src, (W8A8_LDS_MX void*)((W8A8_LDS_MX uint8_t*)st + s.pdst[i]),
                                        16, 0, 0);
     }
-    if (lane < 32)  // 32 lanes x 4 bytes: lane l lands at slice + 4 l
-      __builtin_amdgcn_global_load_lds(
-          s.sbase + kb * s.sstep,
-          (W8A8_LDS_MX void*)((W8A8_LDS_MX uint8_t*)st + (kABlocks + kBBlocks) * 1024 + wave * 128),
-          4, 0, 0);
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      if (q == 1 && four) break;
+      if (lane < 32)  // 32 lanes x 4 bytes: lane l lands at slice + 4 l
+        __builtin_amdgcn_global_load_lds(s.sbase[q] + kb * s.sstep[q],
+                                         (W8A8_LDS_MX void*)((W8A8_LDS_MX uint8_t*)st + s.sdst[q]), 4,
+                                         0, 0);
+    }
   }
 
-  __device__ __forceinline__ static void wait_stage(int later) {
-    if (later >= 2) mx_wait_barrier<2 * kVmPerStage>();
-    else if (later == 1) mx_wait_barrier<kVmPerStage>();
-    else mx_wait_barrier<0>();
+  struct Frags {
+    i32x8 a[TM];
+    i32x8 b[TN];
+    int sa[TM];
+    int sb[TN];
+  };
+
+  // Operand of 32 rows (columns) starting at 16-row block 2i. The scaled
+  // 32x32x64 MFMA takes, in lane l (row l & 31, h = l >> 5), bytes 0..15 =
+  // k [16h, 16h + 16) of the first 32-group and bytes 16..31 = k [32 + 16h,
+  // 48 + 16h) of the second, and lane l's scale byte belongs to group h. So
+  // lane l reads block 2i + (l>>4 & 1), row l & 15, 16-byte k-chunks h and
+  // h + 2, and the scale of (row, group h).
+  __device__ __forceinline__ static i32x8 read_operand(const uint8_t* blk, int lane) {
+    const uint8_t* q = blk + (((lane >> 4) & 1) * 1024) + ((lane >> 5) * 16 + (lane & 15)) * 16;
+    const i32x4 lo = *reinterpret_cast<const i32x4*>(q);
+    const i32x4 hi = *reinterpret_cast<const i32x4*>(q + 512);
+    return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   }
 
+  __device__ __forceinline__ static void read_frags(const uint8_t* st, Frags& f, int wm, int wn,
+                                                    int lane) {
+    const int r = lane & 31, g = lane >> 5;
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int c32 = wn * TN + j;
+      f.b[j] = read_operand(st + (kABlocks + c32 * 2) * 1024, lane);
+      f.sb[j] = st[kScaleOfs + 512 + (c32 * 32 + r) * 2 + g];
+    }
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int r32 = wm * TM + i;
+      f.a[i] = read_operand(st + r32 * 2 * 1024, lane);
+      f.sa[i] = st[kScaleOfs + (r32 * 32 + r) * 2 + g];
+    }
+  }
+
+  __device__ __forceinline__ static void mfma_row(const Frags& f, f32x16 (&acc)[TM][TN], int i) {
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[i], f.b[j], acc[i][j], 0, 0, 0,
+                                                                  f.sa[i], 0, f.sb[j]);
+  }
+
+  __device__ __forceinline__ static void mfma_rows(const Frags& f, f32x16 (&acc)[TM][TN], int lo,
+                                                   int hi) {
+#pragma unroll
+    for (int i = lo; i < hi; ++i) mfma_row(f, acc, i);
+  }
+
+  // K loop in pairs of k-blocks over a five-buffer ring: one wait + barrier
+  // per pair, two to three k-blocks of DMA always in flight (the same ring as
+  // the INT8 tile). One fragment set F: the MFMAs of a k-block are issued,
+  // then F is refilled for the next one; with one barrier per pair the two
+  // wavefronts of a SIMD drift apart, so one's LDS reads run under the other's
+  // MFMAs (two sets of the 8-register MFMA operands do not fit next to the
+  // accumulators).
   __device__ static void mainloop(const MxArgs& p, uint8_t* smem, f32x16 (&acc)[TM][TN],
                                   int64_t row0, int64_t row_end, int nb0) {
     const int lane = threadIdx.x & 63;
@@ -279,46 +374,35 @@ struct MxTile {
 #pragma unroll
       for (int j = 0; j < TN; ++j) acc[i][j] = f32x16{};
 #pragma unroll
-    for (int s = 0; s < STAGES - 1; ++s)
+    for (int s = 0; s < RING; ++s)
       if (s < KB) issue(p, src, smem, s, s, wave, lane);
-    // Operand of 32 rows (columns) starting at 16-row block 2i. The scaled
-    // 32x32x64 MFMA takes, in lane l (row l & 31, h = l >> 5), bytes 0..15 =
-    // k [16h, 16h + 16) of the first 32-group and bytes 16..31 = k [32 + 16h,
-    // 48 + 16h) of the second, and lane l's scale byte belongs to group h. So
-    // lane l reads block 2i + (l>>4 & 1), row l & 15, 16-byte k-chunks h and
-    // h + 2, and the scale of (row, group h).
-    const int lblk = (lane >> 4) & 1;
-    const int g = lane >> 5;
-    const int lofs = (g * 16 + (lane & 15)) * 16;
-    for (int kb = 0; kb < KB; ++kb) {
-      const int ahead = KB - 1 - kb;
-      wait_stage(ahead < STAGES - 2 ? ahead : STAGES - 2);
-      const int nk = kb + STAGES - 1;
-      if (nk < KB) issue(p, src, smem, nk % STAGES, nk, wave, lane);
-      const uint8_t* st = smem + (kb % STAGES) * kStageBytes;
-      const uint8_t* sc = st + (kABlocks + kBBlocks) * 1024;
-      i32x8 bf[TN];
-      int sb[TN];
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const uint8_t* bp = st + (kABlocks + (wn * TN + j) * 2 + lblk) * 1024 + lofs;
-        const i32x4 lo = *reinterpret_cast<const i32x4*>(bp);
-        const i32x4 hi = *reinterpret_cast<const i32x4*>(bp + 512);
-        bf[j] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        sb[j] = sc[512 + ((wn * TN + j) * 32 + (lane & 31)) * 2 + g];
+    if (KB >= 5) mx_wait_barrier<3 * kLoads>();
+    else if (KB == 4) mx_wait_barrier<2 * kLoads>();
+    else if (KB == 3) mx_wait_barrier<kLoads>();
+    else mx_wait_barrier<0>();
+    Frags F;
+    read_frags(smem, F, wm, wn, lane);
+    int buf = 0;
+    for (int kb = 0; kb < KB; kb += 2) {
+      const int buf1 = buf == RING - 1 ? 0 : buf + 1;
+      const int buf2 = buf1 == RING - 1 ? 0 : buf1 + 1;
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_rows(F, acc, 0, TM);
+      __builtin_amdgcn_sched_barrier(0);
+      if (kb + 1 < KB) {
+        read_frags(smem + buf1 * kStageBytes, F, wm, wn, lane);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_rows(F, acc, 0, TM);
+        __builtin_amdgcn_sched_barrier(0);
       }
-#pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        const uint8_t* ap = st + ((wm * TM + i) * 2 + lblk) * 1024 + lofs;
-        const i32x4 lo = *reinterpret_cast<const i32x4*>(ap);
-        const i32x4 hi = *reinterpret_cast<const i32x4*>(ap + 512);
-        const i32x8 af = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        const int sa = sc[((wm * TM + i) * 32 + (lane & 31)) * 2 + g];
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, bf[j], acc[i][j], 0, 0, 0,
-                                                                      sa, 0, sb[j]);
+      if (kb + 2 < KB) {
+        if (kb + 4 < KB) mx_wait_barrier<kLoads>();
+        else mx_wait_barrier<0>();
+        if (kb + 5 < KB) issue(p, src, smem, buf, kb + 5, wave, lane);
+        if (kb + 6 < KB) issue(p, src, smem, buf1, kb + 6, wave, lane);
+        read_frags(smem + buf2 * kStageBytes, F, wm, wn, lane);
       }
+      buf = buf2;
     }
     mx_wait_barrier<0>();
   }
@@ -377,11 +461,12 @@ hipError_t launch_mx_resolve(const uint8_t* w, const float* s, int64_t N, int64_
 }
 
 hipError_t launch_mx_quant(const uint16_t* x, int64_t M, int64_t K, int scale_alg, uint8_t* payload,
-                           uint8_t* scale_rm, uint8_t* scale_kb, int64_t Mp, hipStream_t stream) {
+                           bool blocked, uint8_t* scale_rm, uint8_t* scale_kb, int64_t Mp,
+                           hipStream_t stream) {
   const int64_t n = M * (K / 8);
   if (n == 0) return hipSuccess;
   hipLaunchKernelGGL(mx_quant_kernel, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, stream, x, M, K,
-                     scale_alg, payload, scale_rm, scale_kb, Mp);
+                     scale_alg, payload, blocked ? 1 : 0, scale_rm, scale_kb, Mp);
   return hipGetLastError();
 }
 

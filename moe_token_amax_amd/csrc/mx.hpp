@@ -10,11 +10,15 @@ namespace w8a8 {
 int64_t mx_scale_kb_bytes(int64_t rows_padded, int64_t K);
 hipError_t launch_mx_resolve(const uint8_t* w, const float* s, int64_t N, int64_t K, int64_t BN,
                              int64_t BK, uint16_t* out, hipStream_t stream);
-// scale_rm: [M, K/32] (or null); scale_kb: [ceil(K/64)][Mp][2] (or null)
+// payload: row-major [M, K], or (blocked) the P16x64 blocks [ceil(M/16)][ceil(K/64)]
+// with a zeroed ragged K tail; scale_rm: [M, K/32] (or null);
+// scale_kb: [ceil(K/64)][Mp][2] (or null)
 hipError_t launch_mx_quant(const uint16_t* x, int64_t M, int64_t K, int scale_alg, uint8_t* payload,
-                           uint8_t* scale_rm, uint8_t* scale_kb, int64_t Mp, hipStream_t stream);
+                           bool blocked, uint8_t* scale_rm, uint8_t* scale_kb, int64_t Mp,
+                           hipStream_t stream);
 hipError_t launch_mx_scale_relayout(const uint8_t* src, int64_t R, int64_t K, int64_t Rp,
                                     uint8_t* dst, hipStream_t stream);
+// a: E4M3 activations in P16x64 blocks (as launch_mx_quant with blocked = true)
 hipError_t launch_mx_gemm(const uint8_t* a, const uint8_t* a_scale_kb, int64_t Mp, int64_t M,
                           int64_t K, const uint8_t* w_packed, const uint8_t* w_scale_kb, int64_t N,
                           uint16_t* y, hipStream_t stream);

@@ -263,6 +263,14 @@ def test_mx_block_fp8_full_size(w):
                "mx_linear sampled rows")
 
 
+def _unblock(buf, M, K):
+    """P16x64 blocks [ceil(M/16)][ceil(K/64)] -> row-major [16 ceil(M/16), 64 ceil(K/64)]:
+    byte (r + 16 c) * 16 + j of block (mb, kb) is element (16 mb + r, 64 kb + 16 c + j)."""
+    MB, KB = -(-M // 16), -(-K // 64)
+    b = np.asarray(buf)[:MB * KB * 1024].reshape(MB, KB, 4, 16, 16)
+    return b.transpose(0, 3, 1, 2, 4).reshape(MB * 16, KB * 64)
+
+
 @pytest.mark.parametrize("M", [200, 201])
 def test_mx_gemm_stage_matches_linear(w, M):
     N, K = 96, 352                  # K / 32 = 11: odd group count, ragged k-block
@@ -272,11 +280,13 @@ def test_mx_gemm_stage_matches_linear(w, M):
     ws = torch.empty((w.mx_linear_workspace_bytes(M, K),), dtype=torch.uint8, device=DEV)
     y = w.mx_linear(bf16_dev(xb), packed, N, workspace=ws)
     a, skb = w.mx_workspace_operands(ws, M, K)
-    y2 = w.mx_gemm(a, skb, packed, N)
+    y2 = w.mx_gemm(a, skb, M, K, packed, N)
     sync()
     _assert_eq(bf16_host(y2), bf16_host(y), "mx_gemm vs mx_linear")
     ap_o, as_o = MX.mx_quant(O.bf16_to_f32(xb))
-    _assert_eq(host(a), ap_o, "workspace payload")
+    full = _unblock(host(a), M, K)
+    _assert_eq(full[:M, :K], ap_o, "workspace payload (blocks)")
+    assert not full[:M, K:].any(), "ragged K tail of the activation blocks must be zero"
     Mp = M + (M & 1)
     kb = host(skb).reshape(-(-K // 64), Mp, 2)[:, :M]
     want = np.zeros((-(-K // 64), M, 2), np.uint8)

@@ -86,6 +86,7 @@ def test_mx_sizes(w):
     # payload: N padded to 16, K to 64; scales: ceil(K/64) k-blocks x padded N x 2
     assert w.mx_packed_bytes(5120, 17408) == 5120 * 17408 + 272 * 5120 * 2
     assert w.mx_packed_bytes(17, 96) == 32 * 128 + 256
+    # activation blocks: M padded to 16, K to 64; scales: k-blocks x M padded to even x 2
     assert w.mx_linear_workspace_bytes(2048, 17408) == 2048 * 17408 + 272 * 2048 * 2
-    assert w.mx_linear_workspace_bytes(3, 32) == 256 + 256
-    assert w.mx_linear_workspace_bytes(257, 4096) == 257 * 4096 + 64 * 258 * 2
+    assert w.mx_linear_workspace_bytes(3, 32) == 16 * 64 + 256
+    assert w.mx_linear_workspace_bytes(257, 4096) == 272 * 4096 + 64 * 258 * 2
