@@ -812,24 +812,35 @@ __global__ __launch_bounds__(WM* WN* kWave) void grouped_tile_kernel(GemmArgs p,
 // per-wave INT32 partial sums are added in LDS and the epilogue runs on the
 // full sums: one kernel, no workspace, no second pass. Grid = ceil(N / 16).
 // ---------------------------------------------------------------------------
-template <int MB, int WAVES, int UNR, bool AVEC>
+template <int MB, int NBW, int WAVES, int UNR, bool AVEC>
 __global__ __launch_bounds__(WAVES* kWave) void decode_gemm_kernel(GemmArgs p) {
-  __shared__ i32x4 red[WAVES][MB][kWave];
+  static_assert(MB * NBW <= WAVES, "one wavefront per output block in the epilogue");
+  __shared__ i32x4 red[WAVES][MB * NBW][kWave];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int nb = blockIdx.x;
-  const uint8_t* wcol = p.w + (int64_t)nb * p.KB * kBlockBytes + lane * 16;
-  const int64_t mlast = p.M - 1;
-  i32x4 acc[MB];
+  const int nb0 = blockIdx.x * NBW;
+  const uint8_t* wcol[NBW];
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb) acc[mb] = i32x4{0, 0, 0, 0};
+  for (int j = 0; j < NBW; ++j) {
+    // n-blocks past the last one read the last (their outputs are not stored)
+    const int nb = nb0 + j < p.NB ? nb0 + j : p.NB - 1;
+    wcol[j] = p.w + (int64_t)nb * p.KB * kBlockBytes + lane * 16;
+  }
+  const int64_t mlast = p.M - 1;
+  i32x4 acc[MB][NBW];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int j = 0; j < NBW; ++j) acc[mb][j] = i32x4{0, 0, 0, 0};
   for (int kb0 = wave; kb0 < p.KB; kb0 += WAVES * UNR) {
-    i32x4 b[UNR];
+    i32x4 b[UNR][NBW];
     i32x4 a[UNR][MB];
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
       const int kb = kb0 + u * WAVES;
       const int kbc = kb < p.KB ? kb : p.KB - 1;    // clamped: loads stay in bounds
-      b[u] = *reinterpret_cast<const i32x4*>(wcol + (int64_t)kbc * kBlockBytes);
+#pragma unroll
+      for (int j = 0; j < NBW; ++j)
+        b[u][j] = *reinterpret_cast<const i32x4*>(wcol[j] + (int64_t)kbc * kBlockBytes);
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
         // A rows past M are read clamped to row M-1: they only feed output
@@ -850,23 +861,29 @@ __global__ __launch_bounds__(WAVES* kWave) void decode_gemm_kernel(GemmArgs p) {
     for (int u = 0; u < UNR; ++u) {
       if (kb0 + u * WAVES >= p.KB) break;  // wave-uniform: clamped duplicate blocks add nothing
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) acc[mb] = mfma16x16x64(a[u][mb], b[u], acc[mb]);
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int j = 0; j < NBW; ++j) acc[mb][j] = mfma16x16x64(a[u][mb], b[u][j], acc[mb][j]);
     }
   }
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb) red[wave][mb][lane] = acc[mb];
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int j = 0; j < NBW; ++j) red[wave][mb * NBW + j][lane] = acc[mb][j];
   __syncthreads();
-  if (wave >= MB) return;
+  if (wave >= MB * NBW) return;
+  // wavefront w finishes output block (m-block w / NBW, n-block w % NBW)
   i32x4 sum = red[0][wave][lane];
 #pragma unroll
   for (int w = 1; w < WAVES; ++w) sum += red[w][wave][lane];
-  const int64_t n = (int64_t)nb * 16 + (lane & 15);
+  const int mbk = wave / NBW, jn = wave % NBW;
+  const int64_t n = (int64_t)(nb0 + jn) * 16 + (lane & 15);
   if (n >= p.N) return;
   const float ws = p.w_scale[n];
   const float bsv = p.bias ? bf16_to_f32(p.bias[n]) : 0.0f;
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
-    const int64_t m = wave * 16 + (lane >> 4) * 4 + t;
+    const int64_t m = mbk * 16 + (lane >> 4) * 4 + t;
     if (m >= p.M) continue;
     if (p.out == kOutI32) {
       reinterpret_cast<int32_t*>(p.y)[m * p.N + n] = sum[t];
@@ -889,7 +906,8 @@ struct DenseVariant {
   int BM, BN;
   void (*fn)(GemmArgs);
   int threads;
-  bool decode;   // grid = n-blocks, one workgroup per 16 columns
+  bool decode;   // grid = n-blocks / nbw, one workgroup per nbw 16-column blocks
+  int nbw;
 };
 
 constexpr int kDecodeWaves = 8;
@@ -897,14 +915,22 @@ constexpr int kDecodeWaves = 8;
 // 0: M > 64 fallback (K % 16 != 0 or unaligned A): 128x128 tiles, VGPR-staged
 // 1..3: M <= 16 / 32 / 64: decode kernel with 1 / 2 / 4 m-blocks
 // 4..6: the same for K % 16 != 0 or an unaligned activation pointer
+#ifndef W8A8_DECODE64_NBW
+#define W8A8_DECODE64_NBW 1
+#endif
+#ifndef W8A8_DECODE64_UNR
+#define W8A8_DECODE64_UNR 7
+#endif
+constexpr int kNbw64 = W8A8_DECODE64_NBW;
+constexpr int kUnr64 = W8A8_DECODE64_UNR;
 const DenseVariant kDense[] = {
-    {128, 128, dense_gemm_kernel<128, 128, 2, 2, 2>, 256, false},
-    {16, 16, decode_gemm_kernel<1, kDecodeWaves, 14, true>, kDecodeWaves * 64, true},
-    {32, 16, decode_gemm_kernel<2, kDecodeWaves, 14, true>, kDecodeWaves * 64, true},
-    {64, 16, decode_gemm_kernel<4, kDecodeWaves, 7, true>, kDecodeWaves * 64, true},
-    {16, 16, decode_gemm_kernel<1, kDecodeWaves, 14, false>, kDecodeWaves * 64, true},
-    {32, 16, decode_gemm_kernel<2, kDecodeWaves, 14, false>, kDecodeWaves * 64, true},
-    {64, 16, decode_gemm_kernel<4, kDecodeWaves, 7, false>, kDecodeWaves * 64, true},
+    {128, 128, dense_gemm_kernel<128, 128, 2, 2, 2>, 256, false, 1},
+    {16, 16, decode_gemm_kernel<1, 1, kDecodeWaves, 14, true>, kDecodeWaves * 64, true, 1},
+    {32, 16, decode_gemm_kernel<2, 1, kDecodeWaves, 14, true>, kDecodeWaves * 64, true, 1},
+    {64, 16, decode_gemm_kernel<4, kNbw64, kDecodeWaves, kUnr64, true>, kDecodeWaves * 64, true, kNbw64},
+    {16, 16, decode_gemm_kernel<1, 1, kDecodeWaves, 14, false>, kDecodeWaves * 64, true, 1},
+    {32, 16, decode_gemm_kernel<2, 1, kDecodeWaves, 14, false>, kDecodeWaves * 64, true, 1},
+    {64, 16, decode_gemm_kernel<4, kNbw64, kDecodeWaves, kUnr64, false>, kDecodeWaves * 64, true, kNbw64},
 };
 
 }  // namespace
@@ -962,7 +988,7 @@ hipError_t launch_dense_gemm(const DensePlan& plan, const int8_t* q, const float
     return hipGetLastError();
   }
   const DenseVariant& v = kDense[variant];
-  const int64_t tiles = v.decode ? ceil_div(N, 16) : ceil_div(M, v.BM) * ceil_div(N, v.BN);
+  const int64_t tiles = v.decode ? ceil_div(ceil_div(N, 16), v.nbw) : ceil_div(M, v.BM) * ceil_div(N, v.BN);
   hipLaunchKernelGGL(v.fn, dim3((unsigned)tiles), dim3(v.threads), 0, stream, p);
   return hipGetLastError();
 }
