@@ -177,6 +177,10 @@ class DenseWorkload(Workload):
             b += 2 * self.N
         return b
 
+    def alg_bytes(self):
+        """Algorithmic bytes of the dominant unit (the GEMM launches of one step)."""
+        return sum(self.gemm_bytes(M) for M in self.Ms)
+
     def step_bytes(self):
         # quant (BF16 in, INT8 + scale out) + GEMM (W, scales, q, bias, BF16 out)
         return sum(2 * M * self.K + M * self.K + 4 * M + self.gemm_bytes(M) for M in self.Ms)
@@ -302,6 +306,9 @@ class MoeWorkload(Workload):
             return ne * (2 * I * H + 4 * 2 * I) + R * H + 4 * R + 2 * R * 2 * I + 8 * m.E
         return ne * (H * I + 4 * H) + R * I + 4 * R + 2 * R * H + 8 * m.E
 
+    def alg_bytes(self):
+        return self.gemm_bytes("w13") + self.gemm_bytes("w2")
+
     def value(self, sec_per_step):
         return self.m.T / sec_per_step
 
@@ -391,6 +398,11 @@ class MxWorkload(Workload):
     def flops(self):
         return 2.0 * self.M * self.N * self.K
 
+    def alg_bytes(self):
+        """E4M3 activation + its E8M0 scales, packed weight + scales, BF16 output."""
+        M, N, K = self.M, self.N, self.K
+        return M * K + M * K // 32 + N * K + N * K // 32 + 2 * M * N
+
     def value(self, sec_per_step):
         return self.flops() / sec_per_step / 1e12
 
@@ -444,6 +456,9 @@ class CopyWorkload(Workload):
     def _copy(self):
         self.dst.copy_(self.src)
 
+    def alg_bytes(self):
+        return 2 * self.NBYTES
+
     def value(self, sec_per_step):
         return 2 * self.NBYTES / sec_per_step / 1e9
 
@@ -469,6 +484,26 @@ class CopyWorkload(Workload):
 
 
 # ---------------------------------------------------------------------------
+
+def _traffic(name):
+    """HBM bytes of the dominant unit measured by rocprofv3 (profiles/pmc_traffic.md),
+    or None when no figure exists or a listed kernel source changed since."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "pmc_traffic.md")
+    try:
+        text = open(path).read()
+        blob = text[text.index("```json") + 7:]
+        data = json.loads(blob[:blob.index("```")])
+        rec = data[name]
+        h = hashlib.sha256()
+        for f in rec["sources"]:
+            h.update(open(os.path.join(ROOT, f), "rb").read())
+        if h.hexdigest() != rec["sha256"]:
+            return None
+        return float(rec["traffic_bytes"])
+    except (OSError, ValueError, KeyError):
+        return None
+
 
 def _blas_threads():
     try:
@@ -536,7 +571,8 @@ def main():
     avg_ms = {k: per_key[k] / counts[k] for k in per_key}
 
     roof = wl.dominant(avg_ms)
-    roof["traffic"] = None
+    roof["traffic"] = _traffic(wl.name)
+    roof["algorithmic_bytes"] = wl.alg_bytes()
     roof["kernel_avg_us"] = {str(k): round(v * 1e3, 3) for k, v in avg_ms.items()}
 
     out = {

@@ -455,6 +455,66 @@ struct DmaTile {
       }
     }
   }
+
+  // BF16 epilogue through LDS (the ring is idle after the K loop): every
+  // wavefront writes its BF16 results into a row-major BM x BN tile (row pitch
+  // BN * 2 + 16 bytes, so the four row groups of a 16x16 block land in
+  // different banks), then the workgroup writes whole rows with 16-byte
+  // stores. The values are the direct epilogue's, bit for bit; only the store
+  // pattern changes (each 128-byte line of y is written by one instruction
+  // instead of four 32-byte pieces spread over the epilogue).
+  static constexpr int kPitch = BN * 2 + 16;
+  static_assert(BM * kPitch <= kLdsBytes, "staged tile fits the LDS ring");
+
+  __device__ __forceinline__ static void epilogue_staged(const GemmArgs& p, const i32x4 (&acc)[TM][TN],
+                                                         uint8_t* smem, int64_t row0, int64_t row_end,
+                                                         int e, int64_t n0) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int wm = wave / WN, wn = wave % WN;
+    const float* wsc = p.w_scale + (int64_t)e * p.N;
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int col = (wn * TN + j) * 16 + (lane & 15);
+      const int64_t n = n0 + col;
+      const int64_t nc = n < p.N ? n : p.N - 1;  // columns past N: computed, never stored
+      const float ws = wsc[nc];
+      const float b = p.bias ? bf16_to_f32(p.bias[nc]) : 0.0f;
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int r = (wm * TM + i) * 16 + (lane >> 4) * 4 + v;
+          const int64_t m = row0 + r;
+          const float xs = p.a_scale[m < row_end ? m : row_end - 1];
+          float f = (float)acc[i][j][v];
+          f = f * xs;
+          f = f * ws;
+          if (p.bias) f = f + b;
+          *reinterpret_cast<uint16_t*>(smem + r * kPitch + col * 2) = (uint16_t)f32_to_bf16(f);
+        }
+      }
+    }
+    __syncthreads();
+    constexpr int kChunks = BN * 2 / 16;  // 16-byte pieces per staged row
+    const bool vec = (p.N % 8 == 0) && (((uintptr_t)p.y & 15) == 0);
+    for (int c = threadIdx.x; c < BM * kChunks; c += kThreads) {
+      const int r = c / kChunks, cc = c % kChunks;
+      const int64_t m = row0 + r;
+      if (m >= row_end) continue;
+      const int64_t n = n0 + cc * 8;
+      if (n >= p.N) continue;
+      const uint8_t* src = smem + r * kPitch + cc * 16;
+      uint16_t* dst = reinterpret_cast<uint16_t*>(p.y) + m * p.N + n;
+      if (vec && n + 8 <= p.N) {
+        *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
+      } else {
+        for (int t = 0; t < 8 && n + t < p.N; ++t) dst[t] = reinterpret_cast<const uint16_t*>(src)[t];
+      }
+    }
+    // the LDS is the next tile's ring: every read of the staged tile done first
+    __syncthreads();
+  }
 };
 
 // Tile index -> (tm, tn). Workgroup w runs on XCD w % 8 (round-robin
@@ -490,7 +550,8 @@ __global__ __launch_bounds__(WM* WN* kWave) void dense_dma_kernel(GemmArgs p) {
   const int64_t row_end = min(row0 + BM, p.M);
   i32x4 acc[T::TM][T::TN];
   T::mainloop(p, smem, acc, row0, row_end, 0, (int)(tn * BN / 16));
-  T::epilogue(p, acc, row0, row_end, 0, tn * BN);
+  if (p.out == kOutI32) T::epilogue(p, acc, row0, row_end, 0, tn * BN);
+  else T::epilogue_staged(p, acc, smem, row0, row_end, 0, tn * BN);
 }
 
 // ---------------------------------------------------------------------------
