@@ -262,12 +262,16 @@ struct DmaTile {
   static_assert(STAGES == 5, "stages");
   static_assert(3 * kPerWave <= 63, "vmcnt range");
 
-  // Per-tile DMA sources of this wavefront's kPerWave blocks: the address of
-  // k-block 0 and the step per k-block (64 bytes along an A row, 1 KB through
-  // the packed weight). Block bi < kABlocks is A rows [16*bi, 16*bi + 16).
+  // Per-tile DMA sources of this wavefront's kPerWave blocks: a wave-uniform
+  // base (the activation, or this expert's packed weight), a per-lane 32-bit
+  // byte offset of k-block 0 and the step per k-block (64 bytes along an A
+  // row, 1 KB through the packed weight). Block bi < kABlocks is A rows
+  // [16*bi, 16*bi + 16). The host keeps M * K and N * K below 2^32 here.
   struct Src {
     const uint8_t* base[kPerWave];
-    int64_t step[kPerWave];
+    uint32_t off[kPerWave];
+    int step[kPerWave];
+    uint32_t adj;  // pull-back of this lane's A chunk in the last k-block of a ragged K
   };
 
   // The LDS fragments one wavefront reads from a stage: TN B blocks, TM A blocks.
@@ -285,30 +289,32 @@ struct DmaTile {
       if (bi < kABlocks) {
         int64_t row = row0 + bi * 16 + (lane & 15);
         row = row < row_last ? row : row_last;
-        s.base[i] = reinterpret_cast<const uint8_t*>(p.a) + row * p.K + (lane >> 4) * 16;
+        s.base[i] = reinterpret_cast<const uint8_t*>(p.a);
+        s.off[i] = (uint32_t)(row * p.K + (lane >> 4) * 16);
         s.step[i] = 64;
       } else {
         int nb = nb0 + (bi - kABlocks);
         nb = nb < p.NB ? nb : p.NB - 1;
-        s.base[i] = p.w + (wblk0 + (int64_t)nb * p.KB) * kBlockBytes + lane * 16;
+        s.base[i] = p.w + wblk0 * kBlockBytes;
+        s.off[i] = (uint32_t)((int64_t)nb * p.KB * kBlockBytes + lane * 16);
         s.step[i] = kBlockBytes;
       }
     }
+    // last k-block of a ragged K: a 16-byte A chunk that would run past the
+    // row end is read from K - 16 instead (its values meet zero weights)
+    const int64_t col = (int64_t)(p.KB - 1) * 64 + (lane >> 4) * 16;
+    s.adj = col > p.K - 16 ? (uint32_t)(col - (p.K - 16)) : 0u;
   }
 
   // DMA of block i (of this wavefront) of k-block kb into ring buffer buf.
   __device__ __forceinline__ static void issue_one(const GemmArgs& p, const Src& s, uint8_t* smem,
                                                    int buf, int kb, int wave, int lane, int i) {
     const int bi = wave * kPerWave + i;
-    const uint8_t* src = s.base[i] + kb * s.step[i];
-    if (bi < kABlocks && (p.K & 63) && kb == p.KB - 1) {
-      // last k-block of a ragged K: keep the 16 bytes inside the row
-      const int64_t col = (int64_t)kb * 64 + (lane >> 4) * 16;
-      if (col > p.K - 16) src -= col - (p.K - 16);
-    }
+    uint32_t off = s.off[i] + (uint32_t)(kb * s.step[i]);
+    if (bi < kABlocks && kb == p.KB - 1) off -= s.adj;  // wave-uniform condition
     W8A8_LDS void* dst =
         (W8A8_LDS void*)((W8A8_LDS uint8_t*)smem + buf * kStageBytes + bi * kBlockBytes);
-    __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(s.base[i] + off, dst, 16, 0, 0);
   }
 
   __device__ __forceinline__ static void read_frags(const uint8_t* st, Frags& f, int wm, int wn,
@@ -473,10 +479,21 @@ struct DmaTile {
     const int wave = threadIdx.x >> 6;
     const int wm = wave / WN, wn = wave % WN;
     const float* wsc = p.w_scale + (int64_t)e * p.N;
+    // this lane's element (i, j, v) sits at lbase + i * 16 * kPitch + v * kPitch + j * 32
+    const int r0 = wm * TM * 16 + (lane >> 4) * 4;
+    const int c0 = wn * TN * 16 + (lane & 15);
+    uint8_t* lbase = smem + r0 * kPitch + c0 * 2;
+    float xs[TM][4];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int64_t m = row0 + r0 + i * 16 + v;
+        xs[i][v] = p.a_scale[m < row_end ? m : row_end - 1];
+      }
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
-      const int col = (wn * TN + j) * 16 + (lane & 15);
-      const int64_t n = n0 + col;
+      const int64_t n = n0 + c0 + j * 16;
       const int64_t nc = n < p.N ? n : p.N - 1;  // columns past N: computed, never stored
       const float ws = wsc[nc];
       const float b = p.bias ? bf16_to_f32(p.bias[nc]) : 0.0f;
@@ -484,14 +501,12 @@ struct DmaTile {
       for (int i = 0; i < TM; ++i) {
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const int r = (wm * TM + i) * 16 + (lane >> 4) * 4 + v;
-          const int64_t m = row0 + r;
-          const float xs = p.a_scale[m < row_end ? m : row_end - 1];
           float f = (float)acc[i][j][v];
-          f = f * xs;
+          f = f * xs[i][v];
           f = f * ws;
           if (p.bias) f = f + b;
-          *reinterpret_cast<uint16_t*>(smem + r * kPitch + col * 2) = (uint16_t)f32_to_bf16(f);
+          *reinterpret_cast<uint16_t*>(lbase + (i * 16 + v) * kPitch + j * 32) =
+              (uint16_t)f32_to_bf16(f);
         }
       }
     }
@@ -858,7 +873,8 @@ __global__ __launch_bounds__(WM* WN* kWave) void grouped_tile_kernel(GemmArgs p,
     if (row0 >= row_end) continue;
     i32x4 acc[T::TM][T::TN];
     T::mainloop(p, smem, acc, row0, row_end, e, (int)(tn * kGroupBN / 16));
-    T::epilogue(p, acc, row0, row_end, e, tn * kGroupBN);
+    if (p.out == kOutI32) T::epilogue(p, acc, row0, row_end, e, tn * kGroupBN);
+    else T::epilogue_staged(p, acc, smem, row0, row_end, e, tn * kGroupBN);
   }
 }
 
