@@ -1045,6 +1045,13 @@ static GemmArgs make_args(const int8_t* a, const float* a_scale, int64_t M, int6
   return p;
 }
 
+// The LDS-DMA tile kernels address A and one expert's packed weight with
+// 32-bit per-lane byte offsets.
+static bool offsets32_ok(const GemmArgs& p) {
+  const int64_t lim = (int64_t)1 << 32;
+  return p.M * p.K + 64 < lim && (int64_t)p.NB * p.KB * kBlockBytes < lim;
+}
+
 hipError_t launch_dense_gemm(const DensePlan& plan, const int8_t* q, const float* x_scale, int64_t M,
                              int64_t K, const void* w_packed, const float* w_scale, int64_t N,
                              const uint16_t* bias, void* y, int out, void* ws, hipStream_t stream) {
@@ -1054,7 +1061,7 @@ hipError_t launch_dense_gemm(const DensePlan& plan, const int8_t* q, const float
   int variant = plan.variant;
   // the decode kernels load A rows with 16-byte loads when the pointer allows it
   if (kDense[variant].decode && variant <= 3 && !p.a_vec) variant += 3;
-  if (variant == 0 && p.a_vec) {
+  if (variant == 0 && p.a_vec && offsets32_ok(p)) {
     // prefill-sized M: 256x256 tiles through the LDS-DMA ring
     constexpr int BM = 256, BN = 256;
     const int64_t tiles = ceil_div(M, BM) * ceil_div(N, BN);
@@ -1080,8 +1087,9 @@ hipError_t launch_grouped_gemm(const int8_t* a, const float* a_scale, const int6
   GemmArgs p = make_args(a, a_scale, R, K, w_packed, w_scale, N, nullptr, y, out);
   p.group_list = group_list;
   p.E = (int)E;
-  if (!p.a_vec) {
-    // K % 16 != 0 or unaligned rows: VGPR-staged tiles, schedule built in LDS
+  if (!p.a_vec || !offsets32_ok(p)) {
+    // K % 16 != 0, unaligned rows or operands past 4 GB: VGPR-staged tiles,
+    // schedule built in LDS
     constexpr int BM = 128, BN = 128;
     // upper bound on tiles: sum_e ceil(n_e / BM) <= R / BM + E
     const int64_t max_tiles = (ceil_div(R, BM) + E) * ceil_div(N, BN);
