@@ -148,7 +148,10 @@ class DenseWorkload(Workload):
         nphase = max(1, copies // per)
         steps = [self._make_step([(p * per + j) % copies for j in range(per)])
                  for p in range(nphase)]
-        dom = [(self._make_linears(M), copies, M) for M in self.Ms]
+        # at least 16 launches per timing graph, so that the graph launch itself
+        # does not enter the per-kernel time
+        nl = max(copies, 16)
+        dom = [(self._make_linears(M, nl), nl, M) for M in self.Ms]
         self.capture(steps, dom)
         self.unit = "GB/s" if name != "prefill" else "TOPS"
         self.bound = "hbm" if name != "prefill" else "mfma"
@@ -164,10 +167,10 @@ class DenseWorkload(Workload):
                 self._linear(M, c)
         return fn
 
-    def _make_linears(self, M):
+    def _make_linears(self, M, n):
         def fn():
-            for c in range(self.copies):
-                self._linear(M, c)
+            for i in range(n):
+                self._linear(M, i % self.copies)
         return fn
 
     # algorithmic bytes / ops
