@@ -138,7 +138,12 @@ class DenseWorkload(Workload):
         for c in range(copies):
             self.wp[c].copy_(packed)
         del packed
-        self.q = {M: torch.empty((M, K), dtype=torch.int8, device=dev) for M in self.Ms}
+        # codes in the packed block layout from 16 rows up (whole 1 KB blocks per
+        # 16 rows); below that the row-major codes read fewer bytes
+        self.packed = {M: M >= 16 and K % 8 == 0 for M in self.Ms}
+        self.q = {M: (torch.empty((w.packed_weight_bytes(1, M, K),), dtype=torch.uint8, device=dev)
+                      if self.packed[M] else torch.empty((M, K), dtype=torch.int8, device=dev))
+                  for M in self.Ms}
         self.s = {M: torch.empty((M,), dtype=torch.float32, device=dev) for M in self.Ms}
         self.y = {M: torch.empty((M, N), dtype=torch.bfloat16, device=dev) for M in self.Ms}
         self.ws = {M: torch.empty((max(1, w.linear_workspace_bytes(M, N, K)),), dtype=torch.uint8,
@@ -157,13 +162,23 @@ class DenseWorkload(Workload):
         self.bound = "hbm" if name != "prefill" else "mfma"
 
     def _linear(self, M, c):
-        self.w.linear(self.q[M], self.s[M], self.wp[c], self.w_scale, self.N, bias=self.bias,
-                      y=self.y[M], workspace=self.ws[M])
+        if self.packed[M]:
+            self.w.linear_packed(self.q[M], self.s[M], self.K, self.wp[c], self.w_scale, self.N,
+                                 bias=self.bias, y=self.y[M], workspace=self.ws[M])
+        else:
+            self.w.linear(self.q[M], self.s[M], self.wp[c], self.w_scale, self.N, bias=self.bias,
+                          y=self.y[M], workspace=self.ws[M])
+
+    def _quant(self, M):
+        if self.packed[M]:
+            self.w.dynamic_quant_packed(self.x[:M], self.q[M], self.s[M])
+        else:
+            self.w.dynamic_quant(self.x[:M], self.q[M], self.s[M])
 
     def _make_step(self, copy_ids):
         def fn():
             for M, c in zip(self.Ms, copy_ids):
-                self.w.dynamic_quant(self.x[:M], self.q[M], self.s[M])
+                self._quant(M)
                 self._linear(M, c)
         return fn
 
@@ -212,6 +227,7 @@ class DenseWorkload(Workload):
     def config(self):
         c = {"workload": self.name, "M": self.Ms if len(self.Ms) > 1 else self.Ms[0], "K": self.K,
              "N": self.N, "bias": self.has_bias, "weight_copies": self.copies,
+             "packed_codes_for_M": [M for M in self.Ms if self.packed[M]],
              "x": "N(0,1) with outliers x20", "w": "int8 uniform [-127,127]"}
         return c
 

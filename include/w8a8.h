@@ -49,6 +49,10 @@ typedef enum {
   W8A8_OUT_I32 = 1    /* raw INT32 accumulator (no epilogue), int32_t */
 } w8a8_out;
 
+/* Flag OR-ed into the `out` argument of w8a8_linear: q is in the packed block
+ * layout written by w8a8_dynamic_quant_packed instead of row-major. */
+#define W8A8_A_PACKED 4
+
 /* Largest K (reduction length) accepted: K * 127 * 127 stays below 2^31. */
 #define W8A8_MAX_K 133144
 
@@ -73,6 +77,20 @@ int w8a8_dynamic_quant(const uint16_t* x, int64_t M, int64_t K, int8_t* q,
                        float* x_scale, void* stream);
 
 /*
+ * The same quantization with the codes written in the packed block layout of
+ * the weights (w8a8_prepack_weight with E = 1, the activation rows in the
+ * place of the weight rows): 1 KB blocks [ceil(M/16)][ceil(K/64)], byte
+ * (l*16 + j) of block (b, c) holding q[16 b + l%16][64 c + 16 (l/16) + j].
+ * Codes of rows >= M and columns >= K inside the last blocks are left as
+ * they are (they only ever meet zero weight padding or unstored outputs).
+ * The tiled and decode GEMMs read such blocks as whole 1 KB pieces.
+ *   q_packed device, w8a8_packed_weight_bytes(1, M, K) bytes, 16-byte aligned
+ *   x        16-byte aligned; K % 8 == 0 (else W8A8_ERR_UNSUPPORTED)
+ */
+int w8a8_dynamic_quant_packed(const uint16_t* x, int64_t M, int64_t K, void* q_packed,
+                              float* x_scale, void* stream);
+
+/*
  * Load-time weight prepack.  [DSV4 §二: the INT8 [N, K] weight is transposed
  * and format-cast once at load and reused by every forward]
  * Packed layout ("P16x64"): K is zero-padded to Kp = ceil(K/64)*64 and N to
@@ -92,7 +110,9 @@ int w8a8_prepack_weight(const int8_t* w, int64_t E, int64_t N, int64_t K,
  * Dense W8A8 quant matmul with the fused dequant epilogue.  [DSV4 §二:
  * npu_quant_matmul(q, weight, weight_scale, pertoken_scale, bias,
  * output_dtype=BF16)]
- *   q        device, int8 [M, K] row-major (from w8a8_dynamic_quant)
+ *   q        device, int8 [M, K] row-major (from w8a8_dynamic_quant), or,
+ *            with W8A8_A_PACKED in `out`, the packed blocks of
+ *            w8a8_dynamic_quant_packed
  *   x_scale  device, float [M]
  *   w_packed device, packed weight of one [N, K] matrix (E = 1)
  *   w_scale  device, float [N]

@@ -21,11 +21,14 @@ __all__ = [
     "W8A8Error",
     "OUT_BF16",
     "OUT_I32",
+    "A_PACKED",
     "dynamic_quant",
+    "dynamic_quant_packed",
     "packed_weight_bytes",
     "prepack_weight",
     "linear_workspace_bytes",
     "linear",
+    "linear_packed",
     "grouped_gemm",
     "swiglu_quant",
     "moe_workspace_bytes",
@@ -44,6 +47,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libw8a8.so"
 
 OUT_BF16 = 0
 OUT_I32 = 1
+A_PACKED = 4   # flag for linear's `out`: q in the packed block layout
 
 _c_i64 = ctypes.c_int64
 _c_p = ctypes.c_void_p
@@ -66,6 +70,7 @@ def _load():
         "w8a8_last_error": (ctypes.c_char_p, []),
         "w8a8_abi_version": (ctypes.c_int, []),
         "w8a8_dynamic_quant": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p]),
+        "w8a8_dynamic_quant_packed": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p]),
         "w8a8_packed_weight_bytes": (_c_i64, [_c_i64, _c_i64, _c_i64]),
         "w8a8_prepack_weight": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p]),
         "w8a8_linear_workspace_bytes": (_c_i64, [_c_i64, _c_i64, _c_i64]),
@@ -141,6 +146,25 @@ def dynamic_quant(x: torch.Tensor, q: torch.Tensor | None = None,
     return q, scale
 
 
+def dynamic_quant_packed(x: torch.Tensor, q: torch.Tensor | None = None,
+                         scale: torch.Tensor | None = None):
+    """BF16 [M, K] -> (int8 codes in 1 KB blocks [ceil(M/16)][ceil(K/64)] as a uint8
+    buffer, float32 [M])."""
+    _need(x, torch.bfloat16, "x", 2)
+    M, K = x.shape
+    nbytes = packed_weight_bytes(1, M, K)
+    if q is None:
+        q = torch.empty((max(nbytes, 1),), dtype=torch.uint8, device=x.device)
+    if scale is None:
+        scale = torch.empty((M,), dtype=torch.float32, device=x.device)
+    _need(q, torch.uint8, "q", 1)
+    _need(scale, torch.float32, "scale", 1)
+    if q.numel() < nbytes or scale.shape[0] != M:
+        raise ValueError("q / scale too small")
+    _check(lib.w8a8_dynamic_quant_packed(_ptr(x), M, K, _ptr(q), _ptr(scale), _stream()))
+    return q, scale
+
+
 def packed_weight_bytes(E: int, N: int, K: int) -> int:
     return int(lib.w8a8_packed_weight_bytes(E, N, K))
 
@@ -201,6 +225,36 @@ def linear(q: torch.Tensor, x_scale: torch.Tensor, w_packed: torch.Tensor, w_sca
     ws, ws_n = _workspace(linear_workspace_bytes(M, N, K), q.device, workspace)
     _check(lib.w8a8_linear(_ptr(q), _ptr(x_scale), M, K, _ptr(w_packed), _ptr(w_scale), N,
                            _ptr(bias), _ptr(y), out, _ptr(ws), ws_n, _stream()))
+    return y
+
+
+def linear_packed(q: torch.Tensor, x_scale: torch.Tensor, K: int, w_packed: torch.Tensor,
+                  w_scale: torch.Tensor, N: int, bias: torch.Tensor | None = None,
+                  out: int = OUT_BF16, y: torch.Tensor | None = None,
+                  workspace: torch.Tensor | None = None):
+    """linear() on codes in the packed block layout of dynamic_quant_packed."""
+    _need(q, torch.uint8, "q", 1)
+    _need(x_scale, torch.float32, "x_scale", 1)
+    _need(w_packed, torch.uint8, "w_packed", 1)
+    _need(w_scale, torch.float32, "w_scale", 1)
+    M = x_scale.shape[0]
+    if q.numel() < packed_weight_bytes(1, M, K):
+        raise ValueError("q too small for [M, K] in blocks")
+    if w_scale.shape[0] != N:
+        raise ValueError("scale shape mismatch")
+    if w_packed.numel() < packed_weight_bytes(1, N, K):
+        raise ValueError("w_packed too small for [N, K]")
+    if bias is not None:
+        _need(bias, torch.bfloat16, "bias", 1)
+        if bias.shape[0] != N:
+            raise ValueError("bias shape mismatch")
+    ydt = torch.bfloat16 if out == OUT_BF16 else torch.int32
+    if y is None:
+        y = torch.empty((M, N), dtype=ydt, device=q.device)
+    _need(y, ydt, "y", 2)
+    ws, ws_n = _workspace(linear_workspace_bytes(M, N, K), q.device, workspace)
+    _check(lib.w8a8_linear(_ptr(q), _ptr(x_scale), M, K, _ptr(w_packed), _ptr(w_scale), N,
+                           _ptr(bias), _ptr(y), out | A_PACKED, _ptr(ws), ws_n, _stream()))
     return y
 
 

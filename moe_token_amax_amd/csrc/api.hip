@@ -88,8 +88,23 @@ int w8a8_dynamic_quant(const uint16_t* x, int64_t M, int64_t K, int8_t* q, float
   if (!x || !q || !x_scale) return fail(W8A8_ERR_NULL, "dynamic_quant: null pointer");
   if (!aligned(x, 2) || !aligned(x_scale, 4))
     return fail(W8A8_ERR_ALIGN, "dynamic_quant: x must be 2-byte and x_scale 4-byte aligned");
-  return launched(w8a8::launch_dynamic_quant(x, M, K, q, x_scale, (hipStream_t)stream),
+  return launched(w8a8::launch_dynamic_quant(x, M, K, q, x_scale, false, (hipStream_t)stream),
                   "dynamic_quant");
+}
+
+int w8a8_dynamic_quant_packed(const uint16_t* x, int64_t M, int64_t K, void* q_packed,
+                              float* x_scale, void* stream) {
+  if (M < 0 || K < 1 || M >= kMaxDim * 4 || K > W8A8_MAX_K)
+    return fail(W8A8_ERR_SHAPE, "dynamic_quant_packed: need M >= 0 and 1 <= K <= %d", W8A8_MAX_K);
+  if (K % 8)
+    return fail(W8A8_ERR_UNSUPPORTED, "dynamic_quant_packed: needs K %% 8 == 0 (K=%lld)", (long long)K);
+  if (M == 0) return ok();
+  if (!x || !q_packed || !x_scale) return fail(W8A8_ERR_NULL, "dynamic_quant_packed: null pointer");
+  if (!aligned(x, 16) || !aligned(q_packed, 16) || !aligned(x_scale, 4))
+    return fail(W8A8_ERR_ALIGN, "dynamic_quant_packed: x and q_packed need 16-byte alignment");
+  return launched(w8a8::launch_dynamic_quant(x, M, K, reinterpret_cast<int8_t*>(q_packed), x_scale,
+                                             true, (hipStream_t)stream),
+                  "dynamic_quant_packed");
 }
 
 int64_t w8a8_packed_weight_bytes(int64_t E, int64_t N, int64_t K) {
@@ -116,19 +131,24 @@ int w8a8_linear(const int8_t* q, const float* x_scale, int64_t M, int64_t K, con
                 void* workspace, int64_t ws_bytes, void* stream) {
   if (M < 0 || K < 1 || N < 1 || M >= kMaxDim || N >= kMaxDim || K > W8A8_MAX_K)
     return fail(W8A8_ERR_SHAPE, "linear: need M >= 0, N >= 1, 1 <= K <= %d", W8A8_MAX_K);
+  const bool packed = (out & W8A8_A_PACKED) != 0;
+  out &= ~W8A8_A_PACKED;
   if (out != W8A8_OUT_BF16 && out != W8A8_OUT_I32)
     return fail(W8A8_ERR_UNSUPPORTED, "linear: unknown output kind %d", out);
+  if (packed && w8a8::round_up(M, 16) * w8a8::round_up(K, 64) >= ((int64_t)1 << 32))
+    return fail(W8A8_ERR_UNSUPPORTED, "linear: packed activations past 4 GB");
   if (M == 0) return ok();
   if (!q || !x_scale || !w_packed || !w_scale || !y) return fail(W8A8_ERR_NULL, "linear: null pointer");
   if (!aligned(w_packed, 16) || !aligned(x_scale, 4) || !aligned(w_scale, 4) || !aligned(y, 4) ||
-      (bias && !aligned(bias, 2)))
-    return fail(W8A8_ERR_ALIGN, "linear: w_packed needs 16-byte, scales and y 4-byte alignment");
+      (bias && !aligned(bias, 2)) || (packed && !aligned(q, 16)))
+    return fail(W8A8_ERR_ALIGN,
+                "linear: w_packed (and packed q) need 16-byte, scales and y 4-byte alignment");
   const w8a8::DensePlan plan = w8a8::plan_dense(M, N, K);
   if (plan.ws_bytes > 0 && (!workspace || ws_bytes < plan.ws_bytes || !aligned(workspace, 16)))
     return fail(W8A8_ERR_WORKSPACE, "linear: needs %lld workspace bytes (16-byte aligned), got %lld",
                 (long long)plan.ws_bytes, (long long)ws_bytes);
   return launched(w8a8::launch_dense_gemm(plan, q, x_scale, M, K, w_packed, w_scale, N, bias, y, out,
-                                          workspace, (hipStream_t)stream),
+                                          packed, workspace, (hipStream_t)stream),
                   "linear");
 }
 
@@ -209,7 +229,7 @@ int w8a8_moe_grouped(const void* x_rows, const float* x_scale, const int64_t* gr
     // rows arrived as BF16 without a per-token scale: quantize them first
     err = w8a8::launch_dynamic_quant(reinterpret_cast<const uint16_t*>(x_rows), R, H,
                                      reinterpret_cast<int8_t*>(ws + L.q1),
-                                     reinterpret_cast<float*>(ws + L.s1), s);
+                                     reinterpret_cast<float*>(ws + L.s1), false, s);
     if (err != hipSuccess) return launched(err, "moe_grouped: dynamic_quant");
     q1 = reinterpret_cast<const int8_t*>(ws + L.q1);
     s1 = reinterpret_cast<const float*>(ws + L.s1);

@@ -39,6 +39,7 @@ struct GemmArgs {
   const uint16_t* bias;     // [N] or null
   void* y;                  // [rows, N]
   int out;                  // OutKind
+  int a_blk;                // A in 1 KB blocks [ceil(M/16)][KB] (dense kernels only)
   bool a_vec;               // K % 16 == 0 and a 16-byte aligned
   const int64_t* group_list;  // grouped only
   int E;
@@ -286,7 +287,15 @@ struct DmaTile {
 #pragma unroll
     for (int i = 0; i < kPerWave; ++i) {
       const int bi = wave * kPerWave + i;  // wave-uniform
-      if (bi < kABlocks) {
+      if (bi < kABlocks && p.a_blk) {
+        // packed A: 16-row block mb, k-block kb at (mb * KB + kb) KB; blocks
+        // past the last one are read clamped
+        int64_t mb = row0 / 16 + bi;
+        mb = mb < row_last / 16 ? mb : row_last / 16;
+        s.base[i] = reinterpret_cast<const uint8_t*>(p.a);
+        s.off[i] = (uint32_t)(mb * p.KB * kBlockBytes + lane * 16);
+        s.step[i] = kBlockBytes;
+      } else if (bi < kABlocks) {
         int64_t row = row0 + bi * 16 + (lane & 15);
         row = row < row_last ? row : row_last;
         s.base[i] = reinterpret_cast<const uint8_t*>(p.a);
@@ -303,7 +312,7 @@ struct DmaTile {
     // last k-block of a ragged K: a 16-byte A chunk that would run past the
     // row end is read from K - 16 instead (its values meet zero weights)
     const int64_t col = (int64_t)(p.KB - 1) * 64 + (lane >> 4) * 16;
-    s.adj = col > p.K - 16 ? (uint32_t)(col - (p.K - 16)) : 0u;
+    s.adj = (!p.a_blk && col > p.K - 16) ? (uint32_t)(col - (p.K - 16)) : 0u;
   }
 
   // DMA of block i (of this wavefront) of k-block kb into ring buffer buf.
@@ -889,7 +898,7 @@ __global__ __launch_bounds__(WM* WN* kWave) void grouped_tile_kernel(GemmArgs p,
 // per-wave INT32 partial sums are added in LDS and the epilogue runs on the
 // full sums: one kernel, no workspace, no second pass. Grid = ceil(N / 16).
 // ---------------------------------------------------------------------------
-template <int MB, int NBW, int WAVES, int UNR, bool AVEC>
+template <int MB, int NBW, int WAVES, int UNR, bool AVEC, bool ABLK = false>
 __global__ __launch_bounds__(WAVES* kWave) void decode_gemm_kernel(GemmArgs p) {
   static_assert(MB * NBW <= WAVES, "one wavefront per output block in the epilogue");
   __shared__ i32x4 red[WAVES][MB * NBW][kWave];
@@ -924,10 +933,17 @@ __global__ __launch_bounds__(WAVES* kWave) void decode_gemm_kernel(GemmArgs p) {
         // rows >= M, which are never stored
         const int64_t row = mb * 16 + (lane & 15);
         const int64_t kcol = (int64_t)kbc * 64 + (lane >> 4) * 16;
-        if (AVEC)
+        if (ABLK) {
+          // packed A: one contiguous 1 KB block per (m-block, k-block); m-blocks
+          // past the last one are read clamped (their rows are never stored)
+          const int64_t mbc = mb <= mlast / 16 ? mb : mlast / 16;
+          a[u][mb] = *reinterpret_cast<const i32x4*>(p.a + (mbc * p.KB + kbc) * kBlockBytes +
+                                                     lane * 16);
+        } else if (AVEC) {
           a[u][mb] = *reinterpret_cast<const i32x4*>(p.a + (row < p.M ? row : mlast) * p.K + kcol);
-        else
+        } else {
           a[u][mb] = load_a16(p, row, p.M, kcol);
+        }
       }
     }
     // keep every load of this round ahead of the first MFMA: without the
@@ -1008,6 +1024,10 @@ const DenseVariant kDense[] = {
     {16, 16, decode_gemm_kernel<1, 1, kDecodeWaves, 14, false>, kDecodeWaves * 64, true, 1},
     {32, 16, decode_gemm_kernel<2, 1, kDecodeWaves, 14, false>, kDecodeWaves * 64, true, 1},
     {64, 16, decode_gemm_kernel<4, kNbw64, kDecodeWaves, kUnr64, false>, kDecodeWaves * 64, true, kNbw64},
+    // 7..9: M <= 16 / 32 / 64 with packed A (1 KB blocks)
+    {16, 16, decode_gemm_kernel<1, 1, kDecodeWaves, 14, true, true>, kDecodeWaves * 64, true, 1},
+    {32, 16, decode_gemm_kernel<2, 1, kDecodeWaves, 14, true, true>, kDecodeWaves * 64, true, 1},
+    {64, 16, decode_gemm_kernel<4, kNbw64, kDecodeWaves, kUnr64, true, true>, kDecodeWaves * 64, true, kNbw64},
 };
 
 }  // namespace
@@ -1054,11 +1074,30 @@ static bool offsets32_ok(const GemmArgs& p) {
 
 hipError_t launch_dense_gemm(const DensePlan& plan, const int8_t* q, const float* x_scale, int64_t M,
                              int64_t K, const void* w_packed, const float* w_scale, int64_t N,
-                             const uint16_t* bias, void* y, int out, void* ws, hipStream_t stream) {
+                             const uint16_t* bias, void* y, int out, bool a_packed, void* ws,
+                             hipStream_t stream) {
   (void)ws;
   if (M == 0 || N == 0) return hipSuccess;
   GemmArgs p = make_args(q, x_scale, M, K, w_packed, w_scale, N, bias, y, out);
   int variant = plan.variant;
+  if (a_packed) {
+    // packed A (1 KB blocks): the decode kernels' block variants, or the tiles
+    p.a_blk = 1;
+    p.a_vec = true;
+    if (variant != 0) {
+      const DenseVariant& v = kDense[6 + (M <= 16 ? 1 : (M <= 32 ? 2 : 3))];
+      hipLaunchKernelGGL(v.fn, dim3((unsigned)ceil_div(ceil_div(N, 16), v.nbw)), dim3(v.threads), 0,
+                         stream, p);
+      return hipGetLastError();
+    }
+    if (!offsets32_ok(p)) return hipErrorInvalidValue;
+    constexpr int BM = 256, BN = 256;
+    const int64_t grid = round_up(ceil_div(M, BM) * ceil_div(N, BN), 8);
+    hipLaunchKernelGGL(
+        (dense_dma_kernel<BM, BN, W8A8_DMA_STAGES, W8A8_DMA_GROUP_M, W8A8_DMA_WM, W8A8_DMA_WN>),
+        dim3((unsigned)grid), dim3(64 * W8A8_DMA_WM * W8A8_DMA_WN), 0, stream, p);
+    return hipGetLastError();
+  }
   // the decode kernels load A rows with 16-byte loads when the pointer allows it
   if (kDense[variant].decode && variant <= 3 && !p.a_vec) variant += 3;
   if (variant == 0 && p.a_vec && offsets32_ok(p)) {

@@ -7,8 +7,10 @@
 
 namespace w8a8 {
 
+// codes row-major [M, K], or (packed) in the weight's 1 KB block layout
+// [ceil(M/16)][ceil(K/64)]; packed needs K % 8 == 0 and 16-byte aligned rows
 hipError_t launch_dynamic_quant(const uint16_t* x, int64_t M, int64_t K, int8_t* q, float* scale,
-                                hipStream_t stream);
+                                bool packed, hipStream_t stream);
 hipError_t launch_swiglu_quant(const uint16_t* h, int64_t R, int64_t I, int8_t* q, float* scale,
                                hipStream_t stream);
 hipError_t launch_prepack(const int8_t* w, int64_t E, int64_t N, int64_t K, void* packed,
@@ -25,7 +27,8 @@ struct DensePlan {
 DensePlan plan_dense(int64_t M, int64_t N, int64_t K);
 hipError_t launch_dense_gemm(const DensePlan& plan, const int8_t* q, const float* x_scale, int64_t M,
                              int64_t K, const void* w_packed, const float* w_scale, int64_t N,
-                             const uint16_t* bias, void* y, int out, void* ws, hipStream_t stream);
+                             const uint16_t* bias, void* y, int out, bool a_packed, void* ws,
+                             hipStream_t stream);
 
 int64_t grouped_ws_bytes(int64_t R, int64_t E, int64_t N, int64_t K);
 hipError_t launch_grouped_gemm(const int8_t* a, const float* a_scale, const int64_t* group_list,

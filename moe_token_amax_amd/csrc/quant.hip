@@ -28,10 +28,25 @@ __device__ __forceinline__ uint32_t abs_bf16_pair_max(uint32_t w) {
   return max(w & 0x7FFFu, (w >> 16) & 0x7FFFu);
 }
 
+// Store of 8 codes (row, k = 8 c .. 8 c + 7): row-major q [M, K] when kb == 0,
+// else the packed block layout of the weights with kb k-blocks per 16 rows:
+// block (row / 16, k / 64), byte (row % 16 + 16 (k % 64 / 16)) * 16 + k % 16.
+__device__ __forceinline__ void store_codes8(int8_t* q, int64_t row, int c, int64_t K, int64_t kb,
+                                             uint2 o) {
+  if (kb == 0) {
+    reinterpret_cast<uint2*>(q + row * K)[c] = o;
+  } else {
+    const int64_t k = (int64_t)c * 8;
+    const int64_t at = ((row >> 4) * kb + (k >> 6)) * 1024 + ((row & 15) + 16 * ((k & 63) >> 4)) * 16 +
+                       (k & 15);
+    *reinterpret_cast<uint2*>(q + at) = o;
+  }
+}
+
 template <int CPL>
 __global__ __launch_bounds__(256) void quant_rows_vec(const uint16_t* __restrict__ x, int64_t M,
                                                       int64_t K, int8_t* __restrict__ q,
-                                                      float* __restrict__ scale) {
+                                                      float* __restrict__ scale, int64_t kb) {
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
   if (row >= M) return;  // whole wave leaves together
@@ -51,7 +66,6 @@ __global__ __launch_bounds__(256) void quant_rows_vec(const uint16_t* __restrict
   amax = wave_max_u32(amax);
   const float s = bf16_to_f32(amax) / 127.0f;
   if (lane == 0) scale[row] = s;
-  uint2* qr = reinterpret_cast<uint2*>(q + row * K);
 #pragma unroll
   for (int i = 0; i < CPL; ++i) {
     const int c = lane + i * kWave;
@@ -66,7 +80,7 @@ __global__ __launch_bounds__(256) void quant_rows_vec(const uint16_t* __restrict
       uint2 o;
       o.x = pack4(code[0], code[1], code[2], code[3]);
       o.y = pack4(code[4], code[5], code[6], code[7]);
-      qr[c] = o;
+      store_codes8(q, row, c, K, kb, o);
     }
   }
 }
@@ -80,7 +94,7 @@ template <int CPL>
 __global__ __launch_bounds__(kRowBlock) void quant_rows_block(const uint16_t* __restrict__ x,
                                                               int64_t M, int64_t K,
                                                               int8_t* __restrict__ q,
-                                                              float* __restrict__ scale) {
+                                                              float* __restrict__ scale, int64_t kb) {
   __shared__ uint32_t wave_max[kRowBlock / kWave];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t row = blockIdx.x;
@@ -105,7 +119,6 @@ __global__ __launch_bounds__(kRowBlock) void quant_rows_block(const uint16_t* __
   for (int w = 1; w < kRowBlock / kWave; ++w) amax = max(amax, wave_max[w]);
   const float s = bf16_to_f32(amax) / 127.0f;
   if (tid == 0) scale[row] = s;
-  uint2* qr = reinterpret_cast<uint2*>(q + row * K);
 #pragma unroll
   for (int i = 0; i < CPL; ++i) {
     const int c = tid + i * kRowBlock;
@@ -120,8 +133,69 @@ __global__ __launch_bounds__(kRowBlock) void quant_rows_block(const uint16_t* __
       uint2 o;
       o.x = pack4(code[0], code[1], code[2], code[3]);
       o.y = pack4(code[4], code[5], code[6], code[7]);
-      qr[c] = o;
+      store_codes8(q, row, c, K, kb, o);
     }
+  }
+}
+
+// Packed codes for many rows: one 1024-thread workgroup per 16-row block.
+// Phase 1: wavefront w takes the amax (and scale) of row 16 b + w. Phase 2:
+// the workgroup walks the block's 1 KB pieces in order, thread t writing the
+// 16 codes of byte range [16 t, 16 t + 16) of the row-block's blocks — a
+// whole 1 KB block per wavefront store — from 16 BF16 values it re-reads (L2
+// hot after phase 1). Rows past M get zero codes. K % 8 == 0.
+__global__ __launch_bounds__(kRowBlock) void quant_rows16_packed(const uint16_t* __restrict__ x,
+                                                                 int64_t M, int64_t K,
+                                                                 int8_t* __restrict__ q,
+                                                                 float* __restrict__ scale) {
+  __shared__ float row_scale[16];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t b = blockIdx.x;
+  const int64_t kb = (K + 63) / 64;
+  {
+    const int64_t row = b * 16 + wave;
+    uint32_t amax = 0;
+    if (row < M) {
+      const uint4* xr = reinterpret_cast<const uint4*>(x + row * K);
+      for (int64_t c = lane; c < K / 8; c += kWave) {
+        const uint4 v = xr[c];
+        amax = max(amax, max(max(abs_bf16_pair_max(v.x), abs_bf16_pair_max(v.y)),
+                             max(abs_bf16_pair_max(v.z), abs_bf16_pair_max(v.w))));
+      }
+    }
+    amax = wave_max_u32(amax);
+    const float s = bf16_to_f32(amax) / 127.0f;
+    if (lane == 0) {
+      row_scale[wave] = s;
+      if (row < M) scale[row] = s;
+    }
+  }
+  __syncthreads();
+  int8_t* qb = q + b * kb * 1024;
+  for (int64_t t = tid; t < kb * 64; t += kRowBlock) {
+    const int l = (int)(t & 63);
+    const int r = l & 15;
+    const int64_t row = b * 16 + r;
+    const int64_t k0 = (t >> 6) * 64 + (l >> 4) * 16;
+    uint4 o = uint4{0u, 0u, 0u, 0u};
+    if (row < M && k0 < K) {
+      const uint16_t* xr = x + row * K + k0;
+      const uint4 v0 = *reinterpret_cast<const uint4*>(xr);
+      const uint4 v1 = k0 + 16 <= K ? *reinterpret_cast<const uint4*>(xr + 8) : uint4{0u, 0u, 0u, 0u};
+      const float s = row_scale[r];
+      const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+      int code[16];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        code[2 * j] = quant_code(bf16_to_f32(w[j] & 0xFFFFu), s);
+        code[2 * j + 1] = quant_code(bf16_to_f32(w[j] >> 16), s);
+      }
+      o.x = pack4(code[0], code[1], code[2], code[3]);
+      o.y = pack4(code[4], code[5], code[6], code[7]);
+      o.z = pack4(code[8], code[9], code[10], code[11]);
+      o.w = pack4(code[12], code[13], code[14], code[15]);
+    }
+    *reinterpret_cast<uint4*>(qb + t * 16) = o;
   }
 }
 
@@ -221,29 +295,38 @@ __global__ __launch_bounds__(256) void swiglu_quant_generic(const uint16_t* __re
 static inline bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
 hipError_t launch_dynamic_quant(const uint16_t* x, int64_t M, int64_t K, int8_t* q, float* scale,
-                                hipStream_t stream) {
+                                bool packed, hipStream_t stream) {
   if (M == 0) return hipSuccess;
   const dim3 grid((unsigned)((M + kRowsPerBlock - 1) / kRowsPerBlock)), block(256);
   const bool vec = (K % 8 == 0) && aligned(x, 16) && aligned(q, 8);
+  // packed codes need the vector kernels (the caller checks K % 16 == 0 and alignment)
+  if (packed && !vec) return hipErrorInvalidValue;
+  const int64_t kb = packed ? (K + 63) / 64 : 0;
+  if (packed && M > 512) {
+    // many rows: whole 1 KB blocks per store
+    hipLaunchKernelGGL(quant_rows16_packed, dim3((unsigned)((M + 15) / 16)), dim3(kRowBlock), 0,
+                       stream, x, M, K, q, scale);
+    return hipGetLastError();
+  }
   const int64_t chunks = K / 8;
   if (vec && M <= 512 && chunks <= 2 * kRowBlock) {
     // few rows: a whole workgroup per row
     if (chunks <= kRowBlock)
       hipLaunchKernelGGL(quant_rows_block<1>, dim3((unsigned)M), dim3(kRowBlock), 0, stream, x, M,
-                         K, q, scale);
+                         K, q, scale, kb);
     else
       hipLaunchKernelGGL(quant_rows_block<2>, dim3((unsigned)M), dim3(kRowBlock), 0, stream, x, M,
-                         K, q, scale);
+                         K, q, scale, kb);
   } else if (vec && chunks <= 64 * 1)
-    hipLaunchKernelGGL(quant_rows_vec<1>, grid, block, 0, stream, x, M, K, q, scale);
+    hipLaunchKernelGGL(quant_rows_vec<1>, grid, block, 0, stream, x, M, K, q, scale, kb);
   else if (vec && chunks <= 64 * 2)
-    hipLaunchKernelGGL(quant_rows_vec<2>, grid, block, 0, stream, x, M, K, q, scale);
+    hipLaunchKernelGGL(quant_rows_vec<2>, grid, block, 0, stream, x, M, K, q, scale, kb);
   else if (vec && chunks <= 64 * 4)
-    hipLaunchKernelGGL(quant_rows_vec<4>, grid, block, 0, stream, x, M, K, q, scale);
+    hipLaunchKernelGGL(quant_rows_vec<4>, grid, block, 0, stream, x, M, K, q, scale, kb);
   else if (vec && chunks <= 64 * 8)
-    hipLaunchKernelGGL(quant_rows_vec<8>, grid, block, 0, stream, x, M, K, q, scale);
+    hipLaunchKernelGGL(quant_rows_vec<8>, grid, block, 0, stream, x, M, K, q, scale, kb);
   else if (vec && chunks <= 64 * 16)
-    hipLaunchKernelGGL(quant_rows_vec<16>, grid, block, 0, stream, x, M, K, q, scale);
+    hipLaunchKernelGGL(quant_rows_vec<16>, grid, block, 0, stream, x, M, K, q, scale, kb);
   else
     hipLaunchKernelGGL(quant_rows_generic, grid, block, 0, stream, x, M, K, q, scale);
   return hipGetLastError();

@@ -290,3 +290,53 @@ def test_moe_config_sampled_rows(w):
                            m.w2_scale[e][None], x_bits=xr[r:r + 1])
         _assert_eq(yh[r:r + 1], st, f"row {r} (expert {e})")
         m.drop_cache()
+
+
+# ---------------------------------------------------------------------------
+# packed activation codes (dynamic_quant_packed + linear on blocks)
+# ---------------------------------------------------------------------------
+
+def _unpack_codes(buf, M, K):
+    """1 KB blocks [ceil(M/16)][ceil(K/64)] -> int8 [M, K]: byte (r + 16 c) * 16 + j of
+    block (b, kb) is element (16 b + r, 64 kb + 16 c + j)."""
+    MB, KB = -(-M // 16), -(-K // 64)
+    b = np.asarray(buf)[:MB * KB * 1024].reshape(MB, KB, 4, 16, 16)
+    return b.transpose(0, 3, 1, 2, 4).reshape(MB * 16, KB * 64)[:M, :K].view(np.int8)
+
+
+PACKED_QUANT_SHAPES = [(1, 7168), (16, 256), (17, 7168), (64, 7168), (300, 1024), (5, 96), (33, 520),
+                       (600, 520), (1030, 7168), (513, 64)]
+
+
+@pytest.mark.parametrize("M,K", PACKED_QUANT_SHAPES)
+def test_dynamic_quant_packed_bit_exact(w, M, K):
+    show(f"dynamic_quant_packed M={M} K={K}")
+    xb = synth.activations(M, K, 0.01, seed=M * 31 + K)
+    q, s = w.dynamic_quant_packed(bf16_dev(xb))
+    sync()
+    qo, so = O.dynamic_quant(xb)
+    _assert_eq(host(s).view(np.uint32), so.view(np.uint32), "scale")
+    _assert_eq(_unpack_codes(host(q), M, K), qo, "q (blocks)")
+
+
+PACKED_LINEAR_SHAPES = [(1, 4096, 7168), (4, 256, 512), (16, 4096, 7168), (33, 300, 1024),
+                        (64, 512, 7168), (65, 300, 520), (300, 1088, 600), (520, 512, 1024)]
+
+
+@pytest.mark.parametrize("M,N,K", PACKED_LINEAR_SHAPES)
+def test_linear_packed_matches_row_major(w, M, N, K):
+    show(f"linear packed M={M} N={N} K={K}")
+    d = synth.dense(M, K, N, outlier_frac=0.005, bias=True, seed=M + N + K)
+    wp = w.prepack_weight(dev(d.w))
+    ws_ = dev(d.w_scale)
+    bias = bf16_dev(d.bias)
+    x = bf16_dev(d.x)
+    q, s = w.dynamic_quant(x)
+    qp, sp = w.dynamic_quant_packed(x)
+    y_rm = w.linear(q, s, wp, ws_, N, bias=bias)
+    y_pk = w.linear_packed(qp, sp, K, wp, ws_, N, bias=bias)
+    acc_pk = w.linear_packed(qp, sp, K, wp, ws_, N, out=w.OUT_I32)
+    sync()
+    _assert_eq(bf16_host(y_pk), bf16_host(y_rm), "packed vs row-major BF16")
+    qo, so = O.dynamic_quant(d.x)
+    _assert_eq(host(acc_pk), O.int8_matmul_acc(qo, d.w), "packed INT32")

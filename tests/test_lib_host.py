@@ -63,6 +63,11 @@ def test_validation_before_launch(w):
     assert L.w8a8_grouped_gemm(p, p, p, 8, 2000, 16, 16, p, p, p, 0, None, 0, None) == 4
     assert L.w8a8_swiglu_quant(p, 4, 0, p, p, None) == 2
     assert L.w8a8_moe_grouped(p, None, p, 16, 4, 64, 32, p, p, p, p, p, None, 0, None) == 5
+    # packed activation codes: K % 8 != 0 is unsupported, unknown flag bits too
+    assert L.w8a8_dynamic_quant_packed(p, 4, 100, p, p, None) == 4
+    assert L.w8a8_dynamic_quant_packed(ctypes.c_void_p(24), 4, 64, p, p, None) == 3
+    assert L.w8a8_linear(p, p, 4, 64, p, p, 8, None, p, 8, None, 0, None) == 4
+    assert L.w8a8_linear(ctypes.c_void_p(8), p, 4, 64, p, p, 8, None, p, 4, None, 0, None) == 3
 
 
 def test_mx_validation_before_launch(w):
