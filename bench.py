@@ -141,6 +141,8 @@ class DenseWorkload(Workload):
         # codes in the packed block layout from 16 rows up (whole 1 KB blocks per
         # 16 rows); below that the row-major codes read fewer bytes
         self.packed = {M: M >= 16 and K % 8 == 0 for M in self.Ms}
+        # up to 2 rows: BF16 straight into linear, which fuses the quant into the GEMM
+        self.fused = {M: M <= 2 and K % 8 == 0 for M in self.Ms}
         self.q = {M: (torch.empty((w.packed_weight_bytes(1, M, K),), dtype=torch.uint8, device=dev)
                       if self.packed[M] else torch.empty((M, K), dtype=torch.int8, device=dev))
                   for M in self.Ms}
@@ -162,7 +164,10 @@ class DenseWorkload(Workload):
         self.bound = "hbm" if name != "prefill" else "mfma"
 
     def _linear(self, M, c):
-        if self.packed[M]:
+        if self.fused[M]:
+            self.w.linear_bf16(self.x[:M], self.wp[c], self.w_scale, self.N, bias=self.bias,
+                               y=self.y[M], workspace=self.ws[M])
+        elif self.packed[M]:
             self.w.linear_packed(self.q[M], self.s[M], self.K, self.wp[c], self.w_scale, self.N,
                                  bias=self.bias, y=self.y[M], workspace=self.ws[M])
         else:
@@ -170,6 +175,8 @@ class DenseWorkload(Workload):
                           y=self.y[M], workspace=self.ws[M])
 
     def _quant(self, M):
+        if self.fused[M]:
+            return  # inside the linear
         if self.packed[M]:
             self.w.dynamic_quant_packed(self.x[:M], self.q[M], self.s[M])
         else:
@@ -190,7 +197,10 @@ class DenseWorkload(Workload):
 
     # algorithmic bytes / ops
     def gemm_bytes(self, M):
-        b = self.N * self.K * BYTES_INT8 + 4 * self.N + M * self.K + 4 * M + 2 * M * self.N
+        """One dominant launch: weight + scales, activation in (BF16 for the fused
+        quant, else INT8 codes + scales), BF16 out (+ bias)."""
+        a_in = 2 * M * self.K if self.fused[M] else M * self.K + 4 * M
+        b = self.N * self.K * BYTES_INT8 + 4 * self.N + a_in + 2 * M * self.N
         if self.has_bias:
             b += 2 * self.N
         return b
@@ -200,8 +210,14 @@ class DenseWorkload(Workload):
         return sum(self.gemm_bytes(M) for M in self.Ms)
 
     def step_bytes(self):
-        # quant (BF16 in, INT8 + scale out) + GEMM (W, scales, q, bias, BF16 out)
-        return sum(2 * M * self.K + M * self.K + 4 * M + self.gemm_bytes(M) for M in self.Ms)
+        """External operands of the step: BF16 activations in, weight + scales
+        (+ bias), BF16 out, per M (the INT8 codes are an internal intermediate)."""
+        b = 0
+        for M in self.Ms:
+            b += 2 * M * self.K + self.N * self.K * BYTES_INT8 + 4 * self.N + 2 * M * self.N
+            if self.has_bias:
+                b += 2 * self.N
+        return b
 
     def step_ops(self):
         return sum(2 * M * self.N * self.K for M in self.Ms)
@@ -228,6 +244,7 @@ class DenseWorkload(Workload):
         c = {"workload": self.name, "M": self.Ms if len(self.Ms) > 1 else self.Ms[0], "K": self.K,
              "N": self.N, "bias": self.has_bias, "weight_copies": self.copies,
              "packed_codes_for_M": [M for M in self.Ms if self.packed[M]],
+             "fused_quant_for_M": [M for M in self.Ms if self.fused[M]],
              "x": "N(0,1) with outliers x20", "w": "int8 uniform [-127,127]"}
         return c
 

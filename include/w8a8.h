@@ -112,15 +112,21 @@ int w8a8_prepack_weight(const int8_t* w, int64_t E, int64_t N, int64_t K,
  * output_dtype=BF16)]
  *   q        device, int8 [M, K] row-major (from w8a8_dynamic_quant), or,
  *            with W8A8_A_PACKED in `out`, the packed blocks of
- *            w8a8_dynamic_quant_packed
- *   x_scale  device, float [M]
+ *            w8a8_dynamic_quant_packed; or, when x_scale == NULL, the BF16
+ *            activation x [M, K] row-major, quantized inside exactly as
+ *            w8a8_dynamic_quant does ([DSV4 §三]: quantize only when the
+ *            per-token scale is missing) — for M <= 2 (K % 8 == 0, x 16-byte
+ *            aligned) in the same kernel as the product, else through the
+ *            workspace; the result equals quant + linear bit for bit
+ *   x_scale  device, float [M], or NULL for BF16 input
  *   w_packed device, packed weight of one [N, K] matrix (E = 1)
  *   w_scale  device, float [N]
  *   bias     device, BF16 [N] or NULL
  *   y        device, [M, N] row-major; BF16 bits when out == W8A8_OUT_BF16,
  *            int32 raw accumulators when out == W8A8_OUT_I32
- *   workspace/ws_bytes: device scratch of at least
- *            w8a8_linear_workspace_bytes(M, N, K) bytes (may be 0 → NULL ok)
+ *   workspace/ws_bytes: device scratch of w8a8_linear_workspace_bytes(M, N,
+ *            K) bytes, 256-byte aligned; needed only by the BF16-input branch
+ *            beyond the fused case (INT8 input: NULL / 0 is fine)
  * y[m,n] = BF16(((float(acc[m,n]) * x_scale[m]) * w_scale[n]) + bias[n]),
  * each step one fp32 rounding (round to nearest even), acc exact in INT32.
  * 1 <= K <= W8A8_MAX_K.

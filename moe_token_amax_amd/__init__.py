@@ -29,6 +29,7 @@ __all__ = [
     "linear_workspace_bytes",
     "linear",
     "linear_packed",
+    "linear_bf16",
     "grouped_gemm",
     "swiglu_quant",
     "moe_workspace_bytes",
@@ -255,6 +256,32 @@ def linear_packed(q: torch.Tensor, x_scale: torch.Tensor, K: int, w_packed: torc
     ws, ws_n = _workspace(linear_workspace_bytes(M, N, K), q.device, workspace)
     _check(lib.w8a8_linear(_ptr(q), _ptr(x_scale), M, K, _ptr(w_packed), _ptr(w_scale), N,
                            _ptr(bias), _ptr(y), out | A_PACKED, _ptr(ws), ws_n, _stream()))
+    return y
+
+
+def linear_bf16(x: torch.Tensor, w_packed: torch.Tensor, w_scale: torch.Tensor, N: int,
+                bias: torch.Tensor | None = None, out: int = OUT_BF16,
+                y: torch.Tensor | None = None, workspace: torch.Tensor | None = None):
+    """BF16 [M, K] -> quant (inside) -> linear; bit-identical to dynamic_quant + linear."""
+    _need(x, torch.bfloat16, "x", 2)
+    _need(w_packed, torch.uint8, "w_packed", 1)
+    _need(w_scale, torch.float32, "w_scale", 1)
+    M, K = x.shape
+    if w_scale.shape[0] != N:
+        raise ValueError("scale shape mismatch")
+    if w_packed.numel() < packed_weight_bytes(1, N, K):
+        raise ValueError("w_packed too small for [N, K]")
+    if bias is not None:
+        _need(bias, torch.bfloat16, "bias", 1)
+        if bias.shape[0] != N:
+            raise ValueError("bias shape mismatch")
+    ydt = torch.bfloat16 if out == OUT_BF16 else torch.int32
+    if y is None:
+        y = torch.empty((M, N), dtype=ydt, device=x.device)
+    _need(y, ydt, "y", 2)
+    ws, ws_n = _workspace(linear_workspace_bytes(M, N, K), x.device, workspace)
+    _check(lib.w8a8_linear(_ptr(x), None, M, K, _ptr(w_packed), _ptr(w_scale), N, _ptr(bias),
+                           _ptr(y), out, _ptr(ws), ws_n, _stream()))
     return y
 
 

@@ -121,9 +121,14 @@ int w8a8_prepack_weight(const int8_t* w, int64_t E, int64_t N, int64_t K, void* 
   return launched(w8a8::launch_prepack(w, E, N, K, w_packed, (hipStream_t)stream), "prepack_weight");
 }
 
+// BF16-input branch of w8a8_linear: codes (packed-size bound) + scales
+static int64_t bf16_codes_bytes(int64_t M, int64_t K) {
+  return align256(w8a8::round_up(M, 16) * w8a8::round_up(K, 64));
+}
+
 int64_t w8a8_linear_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   if (M <= 0 || N <= 0 || K <= 0) return 0;
-  return w8a8::plan_dense(M, N, K).ws_bytes;
+  return w8a8::plan_dense(M, N, K).ws_bytes + bf16_codes_bytes(M, K) + align256(4 * M);
 }
 
 int w8a8_linear(const int8_t* q, const float* x_scale, int64_t M, int64_t K, const void* w_packed,
@@ -138,7 +143,34 @@ int w8a8_linear(const int8_t* q, const float* x_scale, int64_t M, int64_t K, con
   if (packed && w8a8::round_up(M, 16) * w8a8::round_up(K, 64) >= ((int64_t)1 << 32))
     return fail(W8A8_ERR_UNSUPPORTED, "linear: packed activations past 4 GB");
   if (M == 0) return ok();
-  if (!q || !x_scale || !w_packed || !w_scale || !y) return fail(W8A8_ERR_NULL, "linear: null pointer");
+  if (!x_scale) {
+    // BF16 activation: quantize inside (w8a8_dynamic_quant's numerics), then multiply
+    if (packed) return fail(W8A8_ERR_UNSUPPORTED, "linear: W8A8_A_PACKED needs INT8 codes and x_scale");
+    if (!q || !w_packed || !w_scale || !y) return fail(W8A8_ERR_NULL, "linear: null pointer");
+    if (!aligned(q, 2) || !aligned(w_packed, 16) || !aligned(w_scale, 4) || !aligned(y, 4) ||
+        (bias && !aligned(bias, 2)))
+      return fail(W8A8_ERR_ALIGN, "linear: x 2-byte, w_packed 16-byte, w_scale and y 4-byte alignment");
+    const uint16_t* x = reinterpret_cast<const uint16_t*>(q);
+    hipStream_t s = (hipStream_t)stream;
+    if (w8a8::decode_fused_ok(M, K, x))
+      return launched(w8a8::launch_decode_fused(x, M, K, w_packed, w_scale, N, bias, y, out, s),
+                      "linear (fused quant)");
+    const int64_t need = w8a8_linear_workspace_bytes(M, N, K);
+    if (!workspace || ws_bytes < need || !aligned(workspace, 256))
+      return fail(W8A8_ERR_WORKSPACE, "linear: BF16 input needs %lld workspace bytes (256-byte aligned), got %lld",
+                  (long long)need, (long long)ws_bytes);
+    int8_t* codes = reinterpret_cast<int8_t*>(workspace);
+    float* scales = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(workspace) + bf16_codes_bytes(M, K));
+    // packed codes from 16 rows up (whole 1 KB blocks per 16 rows), row-major below
+    const bool pk = M >= 16 && K % 8 == 0 && aligned(x, 16);
+    hipError_t e = w8a8::launch_dynamic_quant(x, M, K, codes, scales, pk, s);
+    if (e != hipSuccess) return launched(e, "linear: quant");
+    const w8a8::DensePlan plan = w8a8::plan_dense(M, N, K);
+    return launched(w8a8::launch_dense_gemm(plan, codes, scales, M, K, w_packed, w_scale, N, bias, y, out,
+                                            pk, nullptr, s),
+                    "linear");
+  }
+  if (!q || !w_packed || !w_scale || !y) return fail(W8A8_ERR_NULL, "linear: null pointer");
   if (!aligned(w_packed, 16) || !aligned(x_scale, 4) || !aligned(w_scale, 4) || !aligned(y, 4) ||
       (bias && !aligned(bias, 2)) || (packed && !aligned(q, 16)))
     return fail(W8A8_ERR_ALIGN,

@@ -51,10 +51,22 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 
 // ---------------------------------------------------------------------------
 // Symmetric INT8 code of one value: round-half-even(x / s) clamped to
-// [-127, 127]; s == 0 (all-zero row) gives 0. x / s is one IEEE division.
+// [-127, 127], x / s one IEEE division; s == 0 (all-zero row) gives 0.
+//
+// Fast path with the same result: t = x * rcp(s) (v_rcp_f32, within 1 ulp,
+// for a normal s) is within |q| * 2^-22 <= 2^-15 of q = x / s; fl32(q) moves
+// q by at most 2^-17 for |q| < 256. So when t lies at least 2^-12 away from
+// every half-integer, fl32(q) lies on the same side of it and rint(fl32(q)) =
+// rint(t). Otherwise (near a tie, or s outside [2^-120, 2^120]) the IEEE
+// division decides. |t - rint(t)| is exact (Sterbenz).
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int quant_code(float x, float s) {
   if (!(s > 0.0f)) return 0;
+  if (s >= 0x1p-120f && s <= 0x1p+120f) {
+    const float t = x * __builtin_amdgcn_rcpf(s);
+    const float n = __builtin_rintf(t);
+    if (fabsf(t - n) <= 0.5f - 0x1p-12f) return (int)fminf(fmaxf(n, -127.0f), 127.0f);
+  }
   float v = __builtin_rintf(x / s);
   v = fminf(fmaxf(v, -127.0f), 127.0f);
   return (int)v;

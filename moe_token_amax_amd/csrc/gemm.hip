@@ -991,6 +991,143 @@ __global__ __launch_bounds__(WAVES* kWave) void decode_gemm_kernel(GemmArgs p) {
 }
 
 // ---------------------------------------------------------------------------
+// Dynamic quant fused into the decode GEMM, for a few rows (M <= 2): every
+// workgroup quantizes the M BF16 rows itself (they are L2-resident after the
+// first reads) into LDS — row amax over the workgroup, one IEEE division for
+// the scale and one per element, exactly as the standalone quant — and then
+// runs the decode K loop with the A fragments from LDS (rows >= M read as
+// zero). Saves the quant launch; the results are bit-identical to
+// quant + linear. Dynamic LDS: M * ceil(K/64) * 64 code bytes.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t bf16_pair_absmax(uint32_t w) {
+  return max(w & 0x7FFFu, (w >> 16) & 0x7FFFu);
+}
+
+template <int UNR>
+__global__ __launch_bounds__(8 * kWave) void decode_fused_kernel(GemmArgs p) {
+  constexpr int WAVES = 8, kThreadsF = WAVES * kWave;
+  constexpr int kRows = 4, kCpt = 4;  // rows, 8-value chunks per thread and row (K <= 16384)
+  __shared__ i32x4 red[WAVES][kWave];
+  __shared__ uint32_t wmax[WAVES][kRows];
+  __shared__ float srow[kRows];
+  extern __shared__ __attribute__((aligned(16))) int8_t qlds[];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint16_t* x = reinterpret_cast<const uint16_t*>(p.a);
+  const int64_t K = p.K, Kp = (int64_t)p.KB * 64;
+  const int M = (int)p.M;
+  const int nchunk = (int)(K / 8), nchunk_p = (int)(Kp / 8);
+  // The activation rows are loaded first and the first round of weights right
+  // after: the wait for the activations (loads retire in issue order) then
+  // leaves every weight load in flight while the rows are quantized.
+  uint4 v[kRows][kCpt];
+#pragma unroll
+  for (int r = 0; r < kRows; ++r)
+#pragma unroll
+    for (int i = 0; i < kCpt; ++i) {
+      const int c = tid + i * kThreadsF;
+      v[r][i] = (r < M && c < nchunk) ? reinterpret_cast<const uint4*>(x + (int64_t)r * K)[c]
+                                      : uint4{0u, 0u, 0u, 0u};
+    }
+  __builtin_amdgcn_sched_barrier(0);
+  const int nb = blockIdx.x;
+  const uint8_t* wcol = p.w + (int64_t)nb * p.KB * kBlockBytes + lane * 16;
+  i32x4 b[UNR];
+#pragma unroll
+  for (int u = 0; u < UNR; ++u) {
+    const int kb = wave + u * WAVES;
+    const int kbc = kb < p.KB ? kb : p.KB - 1;    // clamped: loads stay in bounds
+    b[u] = *reinterpret_cast<const i32x4*>(wcol + (int64_t)kbc * kBlockBytes);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  // quant of the M rows: one barrier for the amax, one for the codes
+#pragma unroll
+  for (int r = 0; r < kRows; ++r) {
+    uint32_t am = 0;
+#pragma unroll
+    for (int i = 0; i < kCpt; ++i)
+      am = max(am, max(max(bf16_pair_absmax(v[r][i].x), bf16_pair_absmax(v[r][i].y)),
+                       max(bf16_pair_absmax(v[r][i].z), bf16_pair_absmax(v[r][i].w))));
+    am = wave_max_u32(am);
+    if (lane == 0) wmax[wave][r] = am;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < kRows; ++r) {
+    if (r >= M) break;
+    uint32_t amax = wmax[0][r];
+#pragma unroll
+    for (int w = 1; w < WAVES; ++w) amax = max(amax, wmax[w][r]);
+    const float sc = bf16_to_f32(amax) / 127.0f;
+    if (tid == 0) srow[r] = sc;
+#pragma unroll
+    for (int i = 0; i < kCpt; ++i) {
+      const int c = tid + i * kThreadsF;
+      if (c >= nchunk_p) break;
+      uint2 o = uint2{0u, 0u};
+      if (c < nchunk) {
+        const uint32_t w4[4] = {v[r][i].x, v[r][i].y, v[r][i].z, v[r][i].w};
+        int code[8];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          code[2 * j] = quant_code(bf16_to_f32(w4[j] & 0xFFFFu), sc);
+          code[2 * j + 1] = quant_code(bf16_to_f32(w4[j] >> 16), sc);
+        }
+        o.x = pack4(code[0], code[1], code[2], code[3]);
+        o.y = pack4(code[4], code[5], code[6], code[7]);
+      }
+      *reinterpret_cast<uint2*>(qlds + r * Kp + (int64_t)c * 8) = o;
+    }
+  }
+  __syncthreads();
+  const int arow = lane & 15;
+  i32x4 acc = i32x4{0, 0, 0, 0};
+  for (int kb0 = wave; kb0 < p.KB; kb0 += WAVES * UNR) {
+    if (kb0 != wave) {
+#pragma unroll
+      for (int u = 0; u < UNR; ++u) {
+        const int kb = kb0 + u * WAVES;
+        const int kbc = kb < p.KB ? kb : p.KB - 1;
+        b[u] = *reinterpret_cast<const i32x4*>(wcol + (int64_t)kbc * kBlockBytes);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const int kb = kb0 + u * WAVES;
+      if (kb >= p.KB) break;  // wave-uniform
+      const i32x4 a = arow < M ? *reinterpret_cast<const i32x4*>(qlds + arow * Kp + kb * 64 +
+                                                                  (lane >> 4) * 16)
+                               : i32x4{0, 0, 0, 0};
+      acc = mfma16x16x64(a, b[u], acc);
+    }
+  }
+  red[wave][lane] = acc;
+  __syncthreads();
+  if (wave != 0) return;
+  i32x4 sum = red[0][lane];
+#pragma unroll
+  for (int w = 1; w < WAVES; ++w) sum += red[w][lane];
+  const int64_t n = (int64_t)nb * 16 + (lane & 15);
+  if (n >= p.N) return;
+  const float ws = p.w_scale[n];
+  const float bsv = p.bias ? bf16_to_f32(p.bias[n]) : 0.0f;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int m = (lane >> 4) * 4 + t;
+    if (m >= M) continue;
+    if (p.out == kOutI32) {
+      reinterpret_cast<int32_t*>(p.y)[m * p.N + n] = sum[t];
+    } else {
+      float f = (float)sum[t];
+      f = f * srow[m];
+      f = f * ws;
+      if (p.bias) f = f + bsv;
+      reinterpret_cast<uint16_t*>(p.y)[m * p.N + n] = (uint16_t)f32_to_bf16(f);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // host side: variants and plans
 // ---------------------------------------------------------------------------
 namespace {
@@ -1113,6 +1250,27 @@ hipError_t launch_dense_gemm(const DensePlan& plan, const int8_t* q, const float
   const DenseVariant& v = kDense[variant];
   const int64_t tiles = v.decode ? ceil_div(ceil_div(N, 16), v.nbw) : ceil_div(M, v.BM) * ceil_div(N, v.BN);
   hipLaunchKernelGGL(v.fn, dim3((unsigned)tiles), dim3(v.threads), 0, stream, p);
+  return hipGetLastError();
+}
+
+bool decode_fused_ok(int64_t M, int64_t K, const void* x) {
+  // K <= 16384: four 8-value chunks per thread and row
+  // (M <= 2: every workgroup quantizes the rows again, which outgrows the
+  // saved launch at four rows)
+  return M >= 1 && M <= 2 && K % 8 == 0 && K <= 16384 && ((uintptr_t)x & 15) == 0 &&
+         M * round_up(K, 64) <= kFusedLdsBytes;
+}
+
+hipError_t launch_decode_fused(const uint16_t* x, int64_t M, int64_t K, const void* w_packed,
+                               const float* w_scale, int64_t N, const uint16_t* bias, void* y, int out,
+                               hipStream_t stream) {
+  if (M == 0 || N == 0) return hipSuccess;
+  if (!decode_fused_ok(M, K, x)) return hipErrorInvalidValue;
+  GemmArgs p = make_args(reinterpret_cast<const int8_t*>(x), nullptr, M, K, w_packed, w_scale, N, bias,
+                         y, out);
+  const size_t lds = (size_t)(M * round_up(K, 64));
+  hipLaunchKernelGGL(decode_fused_kernel<14>, dim3((unsigned)ceil_div(N, 16)), dim3(8 * 64), lds, stream,
+                     p);
   return hipGetLastError();
 }
 

@@ -25,6 +25,13 @@ struct DensePlan {
   int64_t ws_bytes;  // device workspace the variant needs (0 for every variant today)
 };
 DensePlan plan_dense(int64_t M, int64_t N, int64_t K);
+// quant fused into the decode GEMM (BF16 input, M <= 2, K % 8 == 0, 16-byte
+// aligned x, the codes of all rows within kFusedLdsBytes of LDS)
+constexpr int64_t kFusedLdsBytes = 65536;
+bool decode_fused_ok(int64_t M, int64_t K, const void* x);
+hipError_t launch_decode_fused(const uint16_t* x, int64_t M, int64_t K, const void* w_packed,
+                               const float* w_scale, int64_t N, const uint16_t* bias, void* y, int out,
+                               hipStream_t stream);
 hipError_t launch_dense_gemm(const DensePlan& plan, const int8_t* q, const float* x_scale, int64_t M,
                              int64_t K, const void* w_packed, const float* w_scale, int64_t N,
                              const uint16_t* bias, void* y, int out, bool a_packed, void* ws,

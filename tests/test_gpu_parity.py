@@ -340,3 +340,32 @@ def test_linear_packed_matches_row_major(w, M, N, K):
     _assert_eq(bf16_host(y_pk), bf16_host(y_rm), "packed vs row-major BF16")
     qo, so = O.dynamic_quant(d.x)
     _assert_eq(host(acc_pk), O.int8_matmul_acc(qo, d.w), "packed INT32")
+
+
+# ---------------------------------------------------------------------------
+# BF16-input linear (quant inside; fused with the product for M <= 4)
+# ---------------------------------------------------------------------------
+
+BF16_LINEAR_SHAPES = [(1, 4096, 7168), (2, 256, 512), (3, 100, 256), (4, 4096, 7168), (5, 300, 520),
+                      (16, 4096, 7168), (64, 512, 7168), (65, 300, 520), (3, 64, 100), (300, 1088, 600),
+                      (4, 64, 16392)]
+
+
+@pytest.mark.parametrize("M,N,K", BF16_LINEAR_SHAPES)
+def test_linear_bf16_input_matches_quant_then_linear(w, M, N, K):
+    show(f"linear bf16 M={M} N={N} K={K}")
+    d = synth.dense(M, K, N, outlier_frac=0.01, bias=True, seed=M * 7 + N + K)
+    if M > 2:
+        d.x[1] = 0  # all-zero row
+    wp = w.prepack_weight(dev(d.w))
+    ws_ = dev(d.w_scale)
+    bias = bf16_dev(d.bias)
+    x = bf16_dev(d.x)
+    q, s = w.dynamic_quant(x)
+    y_ref = w.linear(q, s, wp, ws_, N, bias=bias)
+    y = w.linear_bf16(x, wp, ws_, N, bias=bias)
+    acc = w.linear_bf16(x, wp, ws_, N, out=w.OUT_I32)
+    sync()
+    _assert_eq(bf16_host(y), bf16_host(y_ref), "BF16 input vs quant + linear")
+    qo, so = O.dynamic_quant(d.x)
+    _assert_eq(host(acc), O.int8_matmul_acc(qo, d.w), "BF16 input INT32")

@@ -57,9 +57,11 @@ def test_validation_before_launch(w):
     assert L.w8a8_linear(p, p, 4, 200000, p, p, 8, None, p, 0, None, 0, None) == 2
     assert L.w8a8_linear(p, p, 4, 64, p, p, 8, None, p, 7, None, 0, None) == 4
     assert L.w8a8_linear(p, p, 4, 64, ctypes.c_void_p(24), p, 8, None, p, 0, None, 0, None) == 3
-    # no dense shape needs a workspace
-    assert L.w8a8_linear_workspace_bytes(4, 4096, 7168) == 0
-    assert L.w8a8_linear_workspace_bytes(8192, 4096, 7168) == 0
+    # the workspace serves the BF16-input branch: codes (M to 16, K to 64) + scales
+    assert L.w8a8_linear_workspace_bytes(4, 4096, 7168) == 16 * 7168 + 256
+    assert L.w8a8_linear_workspace_bytes(8192, 4096, 7168) == 8192 * 7168 + 32768
+    # BF16 input with the packed flag is not a thing
+    assert L.w8a8_linear(p, None, 4, 64, p, p, 8, None, p, 4, None, 0, None) == 4
     assert L.w8a8_grouped_gemm(p, p, p, 8, 2000, 16, 16, p, p, p, 0, None, 0, None) == 4
     assert L.w8a8_swiglu_quant(p, 4, 0, p, p, None) == 2
     assert L.w8a8_moe_grouped(p, None, p, 16, 4, 64, 32, p, p, p, p, p, None, 0, None) == 5
