@@ -71,6 +71,25 @@ def test_dynamic_quant_ties(w):
     _assert_eq(host(s), so, "scale")
 
 
+def test_dynamic_quant_near_ties(w):
+    """The kernels take the code from x * rcp(s) unless that lands within 2^-12 of
+    a half-integer, where the IEEE division decides: 2M random values put
+    hundreds of elements in that band; every code must match the oracle's."""
+    xb = synth.activations(256, 8192, 0.01, seed=99)
+    x = O.bf16_to_f32(xb).astype(np.float64)
+    s = O.dynamic_quant_f32(O.bf16_to_f32(xb))[1].astype(np.float64)
+    t = np.abs(x / np.where(s > 0, s, 1.0)[:, None])
+    band = int((np.abs(t - np.floor(t) - 0.5) < 2.0 ** -12).sum())
+    assert band >= 50, band
+    show(f"near-tie elements: {band}")
+    q, sc = w.dynamic_quant(bf16_dev(xb))
+    qp, scp = w.dynamic_quant_packed(bf16_dev(xb))
+    sync()
+    qo, so = O.dynamic_quant(xb)
+    _assert_eq(host(q), qo, "q")
+    _assert_eq(_unpack_codes(host(qp), 256, 8192), qo, "q (blocks)")
+
+
 def test_dynamic_quant_empty(w):
     x = torch.empty((0, 64), dtype=torch.bfloat16, device="cuda")
     q, s = w.dynamic_quant(x)
