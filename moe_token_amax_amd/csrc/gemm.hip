@@ -45,6 +45,16 @@ struct GemmArgs {
   int E;
 };
 
+// threadIdx.x through an empty asm statement: values derived from it are
+// computed where they are used instead of being hoisted out of a persistent
+// loop and kept live across all of its work items (which ran the grouped
+// kernel out of registers).
+__device__ __forceinline__ int opaque_tid() {
+  int t = (int)threadIdx.x;
+  asm volatile("" : "+v"(t));
+  return t;
+}
+
 // 16 bytes of A: row `row`, columns [kcol, kcol + 16). Rows outside
 // [.., row_end) and columns at or past K read as zero.
 __device__ __forceinline__ i32x4 load_a16(const GemmArgs& p, int64_t row, int64_t row_end,
@@ -369,10 +379,10 @@ struct DmaTile {
                                                   i32x4 (&acc)[TM][TN], int64_t row0,
                                                   int64_t row_end, int e, int nb0) {
     static_assert(STAGES == 5, "the pairwise ring needs five k-block buffers");
-    const int lane = threadIdx.x & 63;
+    const int lane = opaque_tid() & 63;
     // wave index as a scalar: per-wave choices are uniform branches and the
     // LDS destination of every DMA is an SGPR (M0)
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wave = __builtin_amdgcn_readfirstlane(opaque_tid() >> 6);
     const int wm = wave / WN, wn = wave % WN;
     const int64_t wblk0 = (int64_t)e * p.NB * p.KB;
     const int KB = p.KB;
@@ -440,8 +450,8 @@ struct DmaTile {
   __device__ __forceinline__ static void epilogue(const GemmArgs& p, const i32x4 (&acc)[TM][TN],
                                                   int64_t row0, int64_t row_end, int e,
                                                   int64_t n0) {
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int lane = opaque_tid() & 63;
+    const int wave = opaque_tid() >> 6;
     const int wm = wave / WN, wn = wave % WN;
     const float* wsc = p.w_scale + (int64_t)e * p.N;
 #pragma unroll
@@ -484,8 +494,8 @@ struct DmaTile {
   __device__ __forceinline__ static void epilogue_staged(const GemmArgs& p, const i32x4 (&acc)[TM][TN],
                                                          uint8_t* smem, int64_t row0, int64_t row_end,
                                                          int e, int64_t n0) {
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int lane = opaque_tid() & 63;
+    const int wave = opaque_tid() >> 6;
     const int wm = wave / WN, wn = wave % WN;
     const float* wsc = p.w_scale + (int64_t)e * p.N;
     // this lane's element (i, j, v) sits at lbase + i * 16 * kPitch + v * kPitch + j * 32
@@ -522,7 +532,7 @@ struct DmaTile {
     __syncthreads();
     constexpr int kChunks = BN * 2 / 16;  // 16-byte pieces per staged row
     const bool vec = (p.N % 8 == 0) && (((uintptr_t)p.y & 15) == 0);
-    for (int c = threadIdx.x; c < BM * kChunks; c += kThreads) {
+    for (int c = opaque_tid(); c < BM * kChunks; c += kThreads) {
       const int r = c / kChunks, cc = c % kChunks;
       const int64_t m = row0 + r;
       if (m >= row_end) continue;
@@ -697,32 +707,44 @@ __global__ __launch_bounds__(WM* WN* kWave) void grouped_gemm_kernel(GemmArgs p)
 //
 // The row counts are skewed: with top-8 routing over 256 experts most
 // non-empty experts own a handful of rows while a few own thousands. The two
-// kinds are served by two kernels that read one schedule:
-//   * experts with at most kSmallRows rows: weight streaming, like the decode
-//     kernel; every wavefront owns one 16-column block of one expert over the
-//     full K, so each weight byte is read once and no MFMA tile is padded to
-//     256 rows;
-//   * larger experts: 256 x 256 LDS-DMA tiles, walked persistently.
+// kinds are served by one persistent kernel that reads a schedule:
+//   * experts with at most kSmallRows rows: weight streaming; each weight
+//     byte is read once and no MFMA tile is padded to 256 rows;
+//   * larger experts: 256 x 256 LDS-DMA tiles.
 // ---------------------------------------------------------------------------
 constexpr int kSmallRows = 64;
 constexpr int kGroupBM = 256, kGroupBN = 256;
 
-// Schedule in the workspace: row_off[E + 1] (first row of each expert) and
+// Schedule in the workspace: row_off[E + 1] (first row of each expert),
 // tile_off[E + 1] (first m-tile of each large expert; small and empty experts
-// own none).
+// own none), small[E + 1] (the ids of the non-empty small experts, their
+// count in small[E]) and the work-queue counters of the mixed kernel (one per
+// XCD).
+constexpr int kQueues = 8;
+
 struct GroupSched {
   int64_t* row_off;
   int* tile_off;
+  int* small;
+  unsigned* queue;
 };
 
+__host__ __device__ inline int64_t sched_align(int64_t b) { return (b + 255) / 256 * 256; }
+
 __host__ __device__ inline int64_t group_sched_bytes(int64_t E) {
-  return ((E + 1) * 8 + 255) / 256 * 256 + ((E + 1) * 4 + 255) / 256 * 256;
+  return sched_align((E + 1) * 8) + 2 * sched_align((E + 1) * 4) + sched_align(kQueues * 4);
 }
 
 __host__ __device__ inline GroupSched group_sched(void* ws, int64_t E) {
   GroupSched g;
-  g.row_off = reinterpret_cast<int64_t*>(ws);
-  g.tile_off = reinterpret_cast<int*>(reinterpret_cast<char*>(ws) + ((E + 1) * 8 + 255) / 256 * 256);
+  char* b = reinterpret_cast<char*>(ws);
+  g.row_off = reinterpret_cast<int64_t*>(b);
+  b += sched_align((E + 1) * 8);
+  g.tile_off = reinterpret_cast<int*>(b);
+  b += sched_align((E + 1) * 4);
+  g.small = reinterpret_cast<int*>(b);
+  b += sched_align((E + 1) * 4);
+  g.queue = reinterpret_cast<unsigned*>(b);
   return g;
 }
 
@@ -733,157 +755,300 @@ __global__ __launch_bounds__(1024) void group_schedule_kernel(const int64_t* __r
                                                               GroupSched out) {
   __shared__ int64_t wrows[16];
   __shared__ int wtiles[16];
+  __shared__ int wsmall[16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t n = tid < E ? max(gl[tid], (int64_t)0) : 0;  // a negative count owns no rows
   const int t = n > kSmallRows ? (int)((n + kGroupBM - 1) / kGroupBM) : 0;
+  const int sm = (n > 0 && n <= kSmallRows) ? 1 : 0;
   int64_t ri = n;
-  int ti = t;
+  int ti = t, si = sm;
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) {
     const int64_t ro = __shfl_up(ri, d, 64);
     const int to = __shfl_up(ti, d, 64);
+    const int so = __shfl_up(si, d, 64);
     if (lane >= d) {
       ri += ro;
       ti += to;
+      si += so;
     }
   }
   if (lane == 63) {
     wrows[wave] = ri;
     wtiles[wave] = ti;
+    wsmall[wave] = si;
   }
   __syncthreads();
   for (int w = 0; w < wave; ++w) {
     ri += wrows[w];
     ti += wtiles[w];
+    si += wsmall[w];
   }
   if (tid < E) {
     out.row_off[tid] = ri - n;
     out.tile_off[tid] = ti - t;
+    if (sm) out.small[si - 1] = tid;
   }
   if (tid == E - 1) {
     out.row_off[E] = ri;
     out.tile_off[E] = ti;
+    out.small[E] = si;
   }
+  if (tid < kQueues) out.queue[tid] = 0u;
 }
 
-// Rows [row0, row0 + rows) (rows <= 16 * MB) of expert e against n-block nb,
-// full K, one wavefront. UNR weight blocks (and their A fragments, read through
-// L1: the wavefronts of a workgroup share them) are in flight at once.
-template <int MB, int UNR>
-__device__ __forceinline__ void small_expert_block(const GemmArgs& p, int e, int64_t row0,
-                                                   int64_t rows, int nb, int lane) {
-  const uint8_t* wcol = p.w + ((int64_t)e * p.NB + nb) * p.KB * kBlockBytes + lane * 16;
-  const int KB = p.KB;
-  i32x4 acc[MB];
+// Small-expert items. An item is the rows of one expert (at most 16 * MB)
+// against kSmallNB consecutive n-blocks over the full K; wavefront w owns
+// n-blocks nb0 + kSmallNBW * w + j. The expert's A rows go through LDS once
+// per workgroup, in chunks of kSmallCK k-blocks stored in MFMA operand order
+// (wavefront w stages k-block w of each chunk, all m-blocks) into two
+// buffers; the weight blocks go straight from HBM into registers, one chunk
+// ahead of the MFMAs, in two register sets used for alternate chunks (no
+// operand is ever copied). Registers thus hold weights in flight rather than
+// A fragments re-read by every wavefront, which keeps enough weight bytes in
+// flight per CU to stream at HBM rate. Step c: load chunk c + 1 (A pieces
+// and weights), run the MFMAs of chunk c from buffer c % 2, store the A
+// pieces of chunk c + 1 into buffer (c + 1) % 2 (last read by chunk c - 1,
+// whose readers all passed the barrier of step c - 1), barrier on LDS. A is
+// staged through VGPRs rather than by LDS DMA: the compiler then tracks the
+// LDS contents and keeps the next chunk's weight loads in flight across the
+// MFMAs instead of draining them.
+constexpr int kSmallCK = 8, kSmallNBW = 2;
+constexpr int kSmallNB = 8 * kSmallNBW;
+
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+template <int MB>
+struct SmallItem {
+  static constexpr int CK = kSmallCK, NBW = kSmallNBW;
+  static constexpr int kChunkBytes = MB * CK * kBlockBytes;
+  using Regs = i32x4[CK][NBW];
+
+  struct Src {
+    const uint8_t* a;     // activation base (wave-uniform)
+    const uint8_t* w;     // this expert's packed weight (wave-uniform)
+    uint32_t aoff[MB];    // lane's A chunk of k-block 0, per m-block
+    uint32_t woff[NBW];   // lane's 16 bytes of k-block 0, per owned n-block
+    uint32_t adj;         // pull-back of the lane's A chunk in a ragged last k-block
+  };
+
+  // Loads of chunk c: the A pieces of k-block c * CK + wave (clamped to the
+  // last one; the MFMAs skip k-blocks past it) and the chunk's weight blocks
+  // (clamped the same way). A first: the store of the pieces then waits for
+  // them only, not for the weights behind them.
+  __device__ __forceinline__ static void load(const GemmArgs& p, const Src& s, i32x4 (&ar)[MB],
+                                              Regs& wr, int c, int wave) {
+    const int KB = p.KB;
+    int kb = c * CK + wave;
+    kb = kb < KB ? kb : KB - 1;  // wave-uniform
+    const uint32_t pull = kb == KB - 1 ? s.adj : 0u;
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb) acc[mb] = i32x4{0, 0, 0, 0};
-  const int8_t* arow[MB];
+    for (int mb = 0; mb < MB; ++mb)
+      ar[mb] = *reinterpret_cast<const i32x4*>(s.a + (s.aoff[mb] + (uint32_t)kb * 64u - pull));
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
-    // rows past the expert's last read that last row: they only feed output
-    // rows that are never stored
-    int64_t r = mb * 16 + (lane & 15);
-    r = r < rows ? r : rows - 1;
-    arow[mb] = p.a + (row0 + r) * p.K + (lane >> 4) * 16;
-  }
-  for (int kb0 = 0; kb0 < KB; kb0 += UNR) {
-    i32x4 b[UNR];
-    i32x4 a[UNR][MB];
+    for (int u = 0; u < CK; ++u) {
+      int k = c * CK + u;
+      k = k < KB ? k : KB - 1;
 #pragma unroll
-    for (int u = 0; u < UNR; ++u) {
-      const int kb = kb0 + u < KB ? kb0 + u : KB - 1;  // clamped: loads stay in bounds
-      b[u] = *reinterpret_cast<const i32x4*>(wcol + (int64_t)kb * kBlockBytes);
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-        a[u][mb] = *reinterpret_cast<const i32x4*>(arow[mb] + (int64_t)kb * 64);
+      for (int j = 0; j < NBW; ++j)
+        wr[u][j] = *reinterpret_cast<const i32x4*>(s.w + (s.woff[j] + (uint32_t)k * kBlockBytes));
     }
-    __builtin_amdgcn_sched_barrier(0);  // all loads of the round before the first MFMA
+  }
+
+  template <int BUF>
+  __device__ __forceinline__ static void stage(uint8_t* smem, const i32x4 (&ar)[MB], int wave,
+                                               int lane) {
+    uint8_t* dst = smem + BUF * kChunkBytes + wave * kBlockBytes + lane * 16;
 #pragma unroll
-    for (int u = 0; u < UNR; ++u) {
-      if (kb0 + u < KB) {  // wave-uniform: clamped duplicate blocks add nothing
+    for (int mb = 0; mb < MB; ++mb)
+      *reinterpret_cast<i32x4*>(dst + mb * CK * kBlockBytes) = ar[mb];
+  }
+
+  // FULL: every k-block of chunk c lies below KB (all chunks but the last)
+  template <bool FULL, int BUF>
+  __device__ __forceinline__ static void compute(const GemmArgs& p, const uint8_t* smem,
+                                                 const Regs& wr, i32x4 (&acc)[MB][NBW], int c,
+                                                 int lane) {
+    const uint8_t* buf = smem + BUF * kChunkBytes + lane * 16;
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) acc[mb] = mfma16x16x64(a[u][mb], b[u], acc[mb]);
+    for (int u = 0; u < CK; ++u) {
+      if (FULL || c * CK + u < p.KB) {  // wave-uniform: clamped duplicate k-blocks add nothing
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          const i32x4 a = *reinterpret_cast<const i32x4*>(buf + (mb * CK + u) * kBlockBytes);
+#pragma unroll
+          for (int j = 0; j < NBW; ++j) acc[mb][j] = mfma16x16x64(a, wr[u][j], acc[mb][j]);
+        }
       }
     }
   }
-  const int64_t n = (int64_t)nb * 16 + (lane & 15);
-  if (n >= p.N) return;
-  const float ws = p.w_scale[(int64_t)e * p.N + n];
+
+  __device__ __forceinline__ static void run(const GemmArgs& p, uint8_t* smem, int e, int64_t row0,
+                                             int64_t rows, int nb0) {
+    const int tid = opaque_tid();
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int KB = p.KB;
+    Src s;
+    s.a = reinterpret_cast<const uint8_t*>(p.a);
+    s.w = p.w + (int64_t)e * p.NB * KB * kBlockBytes;
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
+    for (int mb = 0; mb < MB; ++mb) {
+      // rows past the expert's last read that last row: they only feed
+      // output rows that are never stored
+      int64_t r = mb * 16 + (lane & 15);
+      r = r < rows ? r : rows - 1;
+      s.aoff[mb] = (uint32_t)((row0 + r) * p.K + (lane >> 4) * 16);
+    }
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int64_t m = mb * 16 + (lane >> 4) * 4 + t;
-      if (m >= rows) continue;
-      const int64_t row = row0 + m;
-      if (p.out == kOutI32) {
-        reinterpret_cast<int32_t*>(p.y)[row * p.N + n] = acc[mb][t];
-      } else {
-        float f = (float)acc[mb][t];
-        f = f * p.a_scale[row];
-        f = f * ws;
-        reinterpret_cast<uint16_t*>(p.y)[row * p.N + n] = (uint16_t)f32_to_bf16(f);
+    for (int j = 0; j < NBW; ++j) {
+      int nb = nb0 + wave * NBW + j;
+      nb = nb < p.NB ? nb : p.NB - 1;  // past the last n-block: never stored
+      s.woff[j] = (uint32_t)((int64_t)nb * KB * kBlockBytes + lane * 16);
+    }
+    // last k-block of a ragged K: a 16-byte A chunk that would run past the
+    // row end is read from K - 16 instead (its values meet zero weights)
+    const int64_t col = (int64_t)(KB - 1) * 64 + (lane >> 4) * 16;
+    s.adj = col > p.K - 16 ? (uint32_t)(col - (p.K - 16)) : 0u;
+
+    i32x4 acc[MB][NBW];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int j = 0; j < NBW; ++j) acc[mb][j] = i32x4{0, 0, 0, 0};
+    // chunk c lives in buffer c % 2 and register set c % 2 (c starts even)
+    const int nchunk = (KB + CK - 1) / CK;
+    i32x4 ar[MB];
+    Regs wa, wb;
+    load(p, s, ar, wa, 0, wave);
+    stage<0>(smem, ar, wave, lane);
+    lds_barrier();
+    int c = 0;
+    for (; c + 2 < nchunk; c += 2) {
+      load(p, s, ar, wb, c + 1, wave);
+      compute<true, 0>(p, smem, wa, acc, c, lane);
+      stage<1>(smem, ar, wave, lane);
+      lds_barrier();
+      load(p, s, ar, wa, c + 2, wave);
+      compute<true, 1>(p, smem, wb, acc, c + 1, lane);
+      stage<0>(smem, ar, wave, lane);
+      lds_barrier();
+    }
+    if (c + 1 < nchunk) {
+      load(p, s, ar, wb, c + 1, wave);
+      compute<true, 0>(p, smem, wa, acc, c, lane);
+      stage<1>(smem, ar, wave, lane);
+      lds_barrier();
+      compute<false, 1>(p, smem, wb, acc, c + 1, lane);
+    } else {
+      compute<false, 0>(p, smem, wa, acc, c, lane);
+    }
+
+#pragma unroll
+    for (int j = 0; j < NBW; ++j) {
+      const int64_t n = (int64_t)(nb0 + wave * NBW + j) * 16 + (lane & 15);
+      if (n >= p.N) continue;
+      const float ws = p.w_scale[(int64_t)e * p.N + n];
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int64_t m = mb * 16 + (lane >> 4) * 4 + t;
+          if (m >= rows) continue;
+          const int64_t row = row0 + m;
+          if (p.out == kOutI32) {
+            reinterpret_cast<int32_t*>(p.y)[row * p.N + n] = acc[mb][j][t];
+          } else {
+            float f = (float)acc[mb][j][t];
+            f = f * p.a_scale[row];
+            f = f * ws;
+            reinterpret_cast<uint16_t*>(p.y)[row * p.N + n] = (uint16_t)f32_to_bf16(f);
+          }
+        }
       }
     }
   }
-}
+};
 
-constexpr int kSmallWaves = 8;
-
-// grid = E * ceil(NB / 8): workgroup (e, g) covers n-blocks [8g, 8g + 8) of
-// expert e when e is small and non-empty, else returns at once.
-__global__ __launch_bounds__(kSmallWaves* kWave) void grouped_small_kernel(GemmArgs p,
-                                                                           GroupSched sc) {
-  const int groups = (p.NB + kSmallWaves - 1) / kSmallWaves;
-  const int e = blockIdx.x / groups;
-  const int g = blockIdx.x % groups;
+// Small-expert item g of expert e: n-blocks [g * kSmallNB, (g + 1) * kSmallNB).
+// Every wavefront of the workgroup takes part (the A DMA and the barriers are
+// shared), also one whose n-blocks lie past the last.
+__device__ __forceinline__ void small_item(const GemmArgs& p, const GroupSched& sc, uint8_t* smem,
+                                           int e, int g) {
   const int64_t row0 = sc.row_off[e];
   // counts that sum past R are a caller error: rows at or past R are never
   // touched
-  const int64_t row_end = min(sc.row_off[e + 1], p.M);
-  const int64_t rows = row_end - row0;
-  if (rows <= 0 || sc.row_off[e + 1] - row0 > kSmallRows) return;
-  const int lane = threadIdx.x & 63;
-  const int nb = g * kSmallWaves + (threadIdx.x >> 6);
-  if (nb >= p.NB) return;
-  // (UNR x MB operand registers stay under the budget of 2 wavefronts per
-  // SIMD; larger unrolls get demoted to scratch memory)
-  if (rows <= 16) small_expert_block<1, 16>(p, e, row0, rows, nb, lane);
-  else if (rows <= 32) small_expert_block<2, 8>(p, e, row0, rows, nb, lane);
-  else small_expert_block<4, 4>(p, e, row0, rows, nb, lane);
+  const int64_t rows = min(sc.row_off[e + 1], p.M) - row0;
+  if (rows <= 0) return;  // uniform
+  const int nb0 = g * kSmallNB;
+  if (rows <= 16) SmallItem<1>::run(p, smem, e, row0, rows, nb0);
+  else if (rows <= 32) SmallItem<2>::run(p, smem, e, row0, rows, nb0);
+  else SmallItem<4>::run(p, smem, e, row0, rows, nb0);
 }
 
-// Persistent walk over the large experts' tiles, ordered (expert, n-tile,
-// m-tile) so that tiles running together share weight columns; each XCD
-// (workgroup b runs on XCD b % 8) takes one contiguous eighth of the list.
+// Grouped GEMM over both kinds of expert in one persistent launch (one
+// workgroup per CU). Work items: the 256x256 tiles of the large experts
+// (MFMA-bound, ordered expert, n-tile, m-tile) and the kSmallNB-n-block
+// groups of the small experts (weight streaming, HBM-bound), merged in proportion
+// (item i is a tile when floor((i + 1) T / I) > floor(i T / I)) so that at
+// any time some CUs compute while others stream. XCD x (workgroups b with
+// b % 8 == x) works through its own contiguous eighth of the item list,
+// taking items from its queue counter (zeroed by the schedule kernel); every
+// workgroup leaves when its XCD's range is exhausted.
 template <int STAGES, int WM, int WN>
-__global__ __launch_bounds__(WM* WN* kWave) void grouped_tile_kernel(GemmArgs p, GroupSched sc) {
+__global__ __launch_bounds__(WM* WN* kWave) void grouped_mixed_kernel(GemmArgs p, GroupSched sc) {
   using T = DmaTile<kGroupBM, kGroupBN, STAGES, WM, WN>;
+  static_assert(WM * WN == kSmallCK, "one wavefront per k-block of a small-item chunk");
+  static_assert(2 * SmallItem<4>::kChunkBytes <= T::kLdsBytes, "small items fit the ring");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[T::kLdsBytes];
+  // the item index is passed through the first bytes of the ring, which is
+  // idle between items (a second barrier keeps the next DMA off it until
+  // every wavefront has read it)
+  int64_t* item_slot = reinterpret_cast<int64_t*>(smem);
   const int E = p.E;
   const int64_t NT = (p.N + kGroupBN - 1) / kGroupBN;
-  const int64_t total = (int64_t)sc.tile_off[E] * NT;
-  const int64_t per = (total + 7) / 8;
-  const int64_t xcd = blockIdx.x % 8, wg_per_xcd = gridDim.x / 8;
-  const int64_t t_end = min((xcd + 1) * per, total);
-  for (int64_t t = xcd * per + blockIdx.x / 8; t < t_end; t += wg_per_xcd) {
-    // expert owning tile t: last e with tile_off[e] * NT <= t
-    int lo = 0, hi = E - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if ((int64_t)sc.tile_off[mid] * NT <= t) lo = mid; else hi = mid - 1;
+  const int64_t groups = (p.NB + kSmallNB - 1) / kSmallNB;
+  const int64_t n_tile = (int64_t)sc.tile_off[E] * NT;
+  const int64_t n_small = (int64_t)sc.small[E] * groups;
+  const int64_t total = n_tile + n_small;
+  const int64_t per = (total + kQueues - 1) / kQueues;
+  const int xcd = blockIdx.x % kQueues;
+  const int64_t first = xcd * per, end = min(first + per, total);
+  for (;;) {
+    if (threadIdx.x == 0) *item_slot = first + (int64_t)atomicAdd(&sc.queue[xcd], 1u);
+    __syncthreads();
+    const int64_t i = *item_slot;
+    __syncthreads();
+    if (i >= end) break;  // uniform: every wavefront leaves together
+    const int64_t tiles_before = total ? i * n_tile / total : 0;
+    const bool is_tile = (i + 1) * n_tile / total > tiles_before;
+    if (is_tile) {
+      const int64_t t = tiles_before;
+      // expert owning tile t: last e with tile_off[e] * NT <= t
+      int lo = 0, hi = E - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if ((int64_t)sc.tile_off[mid] * NT <= t) lo = mid; else hi = mid - 1;
+      }
+      const int e = lo;
+      const int64_t mtiles = sc.tile_off[e + 1] - sc.tile_off[e];
+      const int64_t local = t - (int64_t)sc.tile_off[e] * NT;
+      const int64_t tn = local / mtiles, mt = local % mtiles;
+      const int64_t row0 = sc.row_off[e] + mt * kGroupBM;
+      const int64_t row_end = min(sc.row_off[e + 1], p.M);
+      if (row0 < row_end) {
+        i32x4 acc[T::TM][T::TN];
+        T::mainloop(p, smem, acc, row0, row_end, e, (int)(tn * kGroupBN / 16));
+        if (p.out == kOutI32) T::epilogue(p, acc, row0, row_end, e, tn * kGroupBN);
+        else T::epilogue_staged(p, acc, smem, row0, row_end, e, tn * kGroupBN);
+      }
+    } else {
+      const int64_t si = i - tiles_before;
+      small_item(p, sc, smem, sc.small[si / groups], (int)(si % groups));
     }
-    const int e = lo;
-    const int64_t mtiles = sc.tile_off[e + 1] - sc.tile_off[e];
-    const int64_t local = t - (int64_t)sc.tile_off[e] * NT;
-    const int64_t tn = local / mtiles, mt = local % mtiles;
-    const int64_t row0 = sc.row_off[e] + mt * kGroupBM;
-    const int64_t row_end = min(sc.row_off[e + 1], p.M);
-    if (row0 >= row_end) continue;
-    i32x4 acc[T::TM][T::TN];
-    T::mainloop(p, smem, acc, row0, row_end, e, (int)(tn * kGroupBN / 16));
-    if (p.out == kOutI32) T::epilogue(p, acc, row0, row_end, e, tn * kGroupBN);
-    else T::epilogue_staged(p, acc, smem, row0, row_end, e, tn * kGroupBN);
+    __syncthreads();  // the item's last LDS use done before the slot is rewritten
   }
 }
 
@@ -1299,12 +1464,7 @@ hipError_t launch_grouped_gemm(const int8_t* a, const float* a_scale, const int6
   hipLaunchKernelGGL(group_schedule_kernel, dim3(1), dim3(1024), 0, stream, group_list, (int)E, sc);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  const int groups = (int)ceil_div(p.NB, kSmallWaves);
-  hipLaunchKernelGGL(grouped_small_kernel, dim3((unsigned)(E * groups)), dim3(kSmallWaves * 64), 0,
-                     stream, p, sc);
-  err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  hipLaunchKernelGGL((grouped_tile_kernel<W8A8_DMA_STAGES, W8A8_DMA_WM, W8A8_DMA_WN>), dim3(256),
+  hipLaunchKernelGGL((grouped_mixed_kernel<W8A8_DMA_STAGES, W8A8_DMA_WM, W8A8_DMA_WN>), dim3(256),
                      dim3(64 * W8A8_DMA_WM * W8A8_DMA_WN), 0, stream, p, sc);
   return hipGetLastError();
 }
