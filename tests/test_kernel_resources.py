@@ -73,7 +73,10 @@ def test_mfma_loops_do_not_touch_scratch(src, tmp_path):
     asm = out.read_text()
     bad = []
     checked = 0
+    functions = set(re.findall(r"^\s*\.type\s+(\S+),@function", asm, re.M))
     for m in re.finditer(r"^(_Z\S+):\s*(?:;.*)?$", asm, re.M):
+        if m.group(1) not in functions:
+            continue  # a data symbol (device array)
         body = asm[m.end():]
         body = body[:body.index(".Lfunc_end")]
         lines = body.split("\n")
