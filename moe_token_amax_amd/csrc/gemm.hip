@@ -1077,6 +1077,17 @@ __global__ __launch_bounds__(WAVES* kWave) void decode_gemm_kernel(GemmArgs p) {
     wcol[j] = p.w + (int64_t)nb * p.KB * kBlockBytes + lane * 16;
   }
   const int64_t mlast = p.M - 1;
+  // 16-byte A rows (AVEC): this lane's chunk of k-block 0 per m-block, and
+  // its pull-back in a ragged last k-block (a chunk that would run past the
+  // row end is read from K - 16; its values meet zero weights)
+  const int8_t* arow[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    const int64_t row = mb * 16 + (lane & 15);
+    arow[mb] = p.a + (row < p.M ? row : mlast) * p.K + (lane >> 4) * 16;
+  }
+  const int64_t col_last = (int64_t)(p.KB - 1) * 64 + (lane >> 4) * 16;
+  const int64_t pull = col_last > p.K - 16 ? col_last - (p.K - 16) : 0;
   i32x4 acc[MB][NBW];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
@@ -1094,8 +1105,6 @@ __global__ __launch_bounds__(WAVES* kWave) void decode_gemm_kernel(GemmArgs p) {
         b[u][j] = *reinterpret_cast<const i32x4*>(wcol[j] + (int64_t)kbc * kBlockBytes);
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
-        // A rows past M are read clamped to row M-1: they only feed output
-        // rows >= M, which are never stored
         const int64_t row = mb * 16 + (lane & 15);
         const int64_t kcol = (int64_t)kbc * 64 + (lane >> 4) * 16;
         if (ABLK) {
@@ -1105,7 +1114,10 @@ __global__ __launch_bounds__(WAVES* kWave) void decode_gemm_kernel(GemmArgs p) {
           a[u][mb] = *reinterpret_cast<const i32x4*>(p.a + (mbc * p.KB + kbc) * kBlockBytes +
                                                      lane * 16);
         } else if (AVEC) {
-          a[u][mb] = *reinterpret_cast<const i32x4*>(p.a + (row < p.M ? row : mlast) * p.K + kcol);
+          // lanes of rows past M load nothing: their products only feed
+          // output rows >= M, which are never stored
+          const int8_t* src = arow[mb] + (int64_t)kbc * 64 - (kbc == p.KB - 1 ? pull : 0);
+          a[u][mb] = row < p.M ? *reinterpret_cast<const i32x4*>(src) : i32x4{0, 0, 0, 0};
         } else {
           a[u][mb] = load_a16(p, row, p.M, kcol);
         }

@@ -114,6 +114,8 @@ LINEAR_SHAPES = [  # M, K, N, bias
     (16, 256, 128, True), (1, 64, 16, False), (17, 100, 50, True), (3, 37, 5, False),
     (33, 448, 96, True), (64, 1024, 192, False), (129, 320, 144, True), (300, 512, 260, False),
     (4, 7168, 512, False), (16, 7168, 256, True),
+    # decode kernel, 16-byte rows with a ragged last k-block (K % 64 == 16)
+    (4, 2064, 160, True), (40, 1040, 96, False),
     # prefill-sized M (LDS-DMA tiles): ragged K (K % 64 != 0), tiny K, N tails,
     # a single partial 256-row tile, several tiles in both directions
     (100, 80, 300, True), (65, 16, 40, False), (257, 4096, 512, True), (520, 1088, 600, False),
