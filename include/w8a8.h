@@ -151,7 +151,10 @@ int w8a8_linear(const int8_t* q, const float* x_scale, int64_t M, int64_t K,
  *   w_scale    device, float [E, N]
  *   y          device, [R, N]; BF16 bits or int32 as for w8a8_linear
  *   workspace  device scratch of w8a8_grouped_workspace_bytes(R, E, N, K)
- *              bytes, 256-byte aligned (per-expert row and tile offsets)
+ *              bytes, 256-byte aligned: the schedule the call builds first
+ *              (per-expert row and tile offsets, the list of experts with at
+ *              most 64 rows, the work-queue counters). Every call rewrites it,
+ *              so two calls that share a workspace must not run concurrently.
  * Experts with n_e == 0 cost no work. No bias. E <= 1024.
  */
 int64_t w8a8_grouped_workspace_bytes(int64_t R, int64_t E, int64_t N, int64_t K);
