@@ -54,18 +54,21 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 // [-127, 127], x / s one IEEE division; s == 0 (all-zero row) gives 0.
 //
 // Fast path with the same result: t = x * rcp(s) (v_rcp_f32, within 1 ulp,
-// for a normal s) is within |q| * 2^-22 <= 2^-15 of q = x / s; fl32(q) moves
-// q by at most 2^-17 for |q| < 256. So when t lies at least 2^-12 away from
-// every half-integer, fl32(q) lies on the same side of it and rint(fl32(q)) =
-// rint(t). Otherwise (near a tie, or s outside [2^-120, 2^120]) the IEEE
-// division decides. |t - rint(t)| is exact (Sterbenz).
+// for a normal s) is within |q| * 2^-22 of q = x / s, i.e. within 2^-15 where
+// it matters (|q| <= 128: beyond, both roundings clamp to 127); fl32(q) moves
+// q by at most 2^-18 there. So |t - fl32(q)| < 2^-14, and when t lies at least
+// 2^-14 away from every half-integer, fl32(q) lies on the same side of it and
+// rint(fl32(q)) = rint(t). Otherwise (near a tie, or s outside [2^-120,
+// 2^120]) the IEEE division decides. |t - rint(t)| is exact (Sterbenz).
 // ---------------------------------------------------------------------------
+constexpr float kQuantMargin = 0.5f - 0x1p-14f;
+
 __device__ __forceinline__ int quant_code(float x, float s) {
   if (!(s > 0.0f)) return 0;
   if (s >= 0x1p-120f && s <= 0x1p+120f) {
     const float t = x * __builtin_amdgcn_rcpf(s);
     const float n = __builtin_rintf(t);
-    if (fabsf(t - n) <= 0.5f - 0x1p-12f) return (int)fminf(fmaxf(n, -127.0f), 127.0f);
+    if (fabsf(t - n) <= kQuantMargin) return (int)fminf(fmaxf(n, -127.0f), 127.0f);
   }
   float v = __builtin_rintf(x / s);
   v = fminf(fmaxf(v, -127.0f), 127.0f);
@@ -76,6 +79,50 @@ __device__ __forceinline__ int quant_code(float x, float s) {
 __device__ __forceinline__ uint32_t pack4(int a, int b, int c, int d) {
   return (uint32_t)(a & 0xFF) | ((uint32_t)(b & 0xFF) << 8) |
          ((uint32_t)(c & 0xFF) << 16) | ((uint32_t)(d & 0xFF) << 24);
+}
+
+// quant_code of 8 values with one scale per lane, packed (value 0 in the low
+// byte of .x). The fast path of all 8 runs without branches; one wavefront
+// vote follows (about 6% of votes over 8 x 64 values find a value within
+// 2^-14 of a tie), and only then are the flagged values of the flagged lanes
+// done by the division. quant_code one value at a time costs about twice the
+// instructions (a branch per value).
+__device__ __forceinline__ uint2 quant8(const float (&x)[8], float s) {
+  const bool fast = s >= 0x1p-120f && s <= 0x1p+120f;  // false for 0, NaN, extreme scales
+  const float r = __builtin_amdgcn_rcpf(s);
+  int code[8];
+  bool near = !fast;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float t = x[j] * r;
+    const float n = __builtin_rintf(t);
+    near = near || !(fabsf(t - n) <= kQuantMargin);
+    code[j] = (int)fminf(fmaxf(n, -127.0f), 127.0f);
+  }
+  if (__builtin_amdgcn_ballot_w64(near) != 0) {
+    if (near) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float t = x[j] * r;
+        if (!fast || !(fabsf(t - __builtin_rintf(t)) <= kQuantMargin)) {
+          float v = s > 0.0f ? __builtin_rintf(x[j] / s) : 0.0f;
+          code[j] = (int)fminf(fmaxf(v, -127.0f), 127.0f);
+        }
+      }
+    }
+  }
+  return uint2{pack4(code[0], code[1], code[2], code[3]), pack4(code[4], code[5], code[6], code[7])};
+}
+
+// quant8 of 8 BF16 values held as 4 pairs (low half first)
+__device__ __forceinline__ uint2 quant8_bf16(const uint32_t (&w)[4], float s) {
+  float x[8];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    x[2 * j] = __uint_as_float(w[j] << 16);
+    x[2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
+  }
+  return quant8(x, s);
 }
 
 // ---------------------------------------------------------------------------

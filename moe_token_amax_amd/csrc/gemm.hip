@@ -1243,14 +1243,7 @@ __global__ __launch_bounds__(8 * kWave) void decode_fused_kernel(GemmArgs p) {
       uint2 o = uint2{0u, 0u};
       if (c < nchunk) {
         const uint32_t w4[4] = {v[r][i].x, v[r][i].y, v[r][i].z, v[r][i].w};
-        int code[8];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          code[2 * j] = quant_code(bf16_to_f32(w4[j] & 0xFFFFu), sc);
-          code[2 * j + 1] = quant_code(bf16_to_f32(w4[j] >> 16), sc);
-        }
-        o.x = pack4(code[0], code[1], code[2], code[3]);
-        o.y = pack4(code[4], code[5], code[6], code[7]);
+        o = quant8_bf16(w4, sc);
       }
       *reinterpret_cast<uint2*>(qlds + r * Kp + (int64_t)c * 8) = o;
     }

@@ -71,16 +71,7 @@ __global__ __launch_bounds__(256) void quant_rows_vec(const uint16_t* __restrict
     const int c = lane + i * kWave;
     if (c < nchunk) {
       const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
-      int code[8];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        code[2 * j] = quant_code(bf16_to_f32(w[j] & 0xFFFFu), s);
-        code[2 * j + 1] = quant_code(bf16_to_f32(w[j] >> 16), s);
-      }
-      uint2 o;
-      o.x = pack4(code[0], code[1], code[2], code[3]);
-      o.y = pack4(code[4], code[5], code[6], code[7]);
-      store_codes8(q, row, c, K, kb, o);
+      store_codes8(q, row, c, K, kb, quant8_bf16(w, s));
     }
   }
 }
@@ -124,16 +115,7 @@ __global__ __launch_bounds__(kRowBlock) void quant_rows_block(const uint16_t* __
     const int c = tid + i * kRowBlock;
     if (c < nchunk) {
       const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
-      int code[8];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        code[2 * j] = quant_code(bf16_to_f32(w[j] & 0xFFFFu), s);
-        code[2 * j + 1] = quant_code(bf16_to_f32(w[j] >> 16), s);
-      }
-      uint2 o;
-      o.x = pack4(code[0], code[1], code[2], code[3]);
-      o.y = pack4(code[4], code[5], code[6], code[7]);
-      store_codes8(q, row, c, K, kb, o);
+      store_codes8(q, row, c, K, kb, quant8_bf16(w, s));
     }
   }
 }
@@ -183,17 +165,10 @@ __global__ __launch_bounds__(kRowBlock) void quant_rows16_packed(const uint16_t*
       const uint4 v0 = *reinterpret_cast<const uint4*>(xr);
       const uint4 v1 = k0 + 16 <= K ? *reinterpret_cast<const uint4*>(xr + 8) : uint4{0u, 0u, 0u, 0u};
       const float s = row_scale[r];
-      const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-      int code[16];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        code[2 * j] = quant_code(bf16_to_f32(w[j] & 0xFFFFu), s);
-        code[2 * j + 1] = quant_code(bf16_to_f32(w[j] >> 16), s);
-      }
-      o.x = pack4(code[0], code[1], code[2], code[3]);
-      o.y = pack4(code[4], code[5], code[6], code[7]);
-      o.z = pack4(code[8], code[9], code[10], code[11]);
-      o.w = pack4(code[12], code[13], code[14], code[15]);
+      const uint32_t w0[4] = {v0.x, v0.y, v0.z, v0.w};
+      const uint32_t w1[4] = {v1.x, v1.y, v1.z, v1.w};
+      const uint2 lo = quant8_bf16(w0, s), hi = quant8_bf16(w1, s);
+      o = uint4{lo.x, lo.y, hi.x, hi.y};
     }
     *reinterpret_cast<uint4*>(qb + t * 16) = o;
   }
@@ -255,12 +230,7 @@ __global__ __launch_bounds__(256) void swiglu_quant_vec(const uint16_t* __restri
   for (int i = 0; i < CPL; ++i) {
     const int c = lane + i * kWave;
     if (c < nchunk) {
-      uint2 o;
-      o.x = pack4(quant_code(a[i][0], s), quant_code(a[i][1], s), quant_code(a[i][2], s),
-                  quant_code(a[i][3], s));
-      o.y = pack4(quant_code(a[i][4], s), quant_code(a[i][5], s), quant_code(a[i][6], s),
-                  quant_code(a[i][7], s));
-      qr[c] = o;
+      qr[c] = quant8(a[i], s);
     }
   }
 }

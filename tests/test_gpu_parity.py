@@ -71,23 +71,28 @@ def test_dynamic_quant_ties(w):
     _assert_eq(host(s), so, "scale")
 
 
-def test_dynamic_quant_near_ties(w):
-    """The kernels take the code from x * rcp(s) unless that lands within 2^-12 of
-    a half-integer, where the IEEE division decides: 2M random values put
-    hundreds of elements in that band; every code must match the oracle's."""
-    xb = synth.activations(256, 8192, 0.01, seed=99)
+@pytest.mark.parametrize("M,K", [(256, 8192), (1024, 4096)])
+def test_dynamic_quant_near_ties(w, M, K):
+    """The kernels take the code from x * rcp(s) unless that lands within 2^-14 of
+    a half-integer, where the IEEE division decides. Random values put hundreds
+    of elements in that band and in the band from 2^-14 to 2^-12 next to it
+    (decided by the reciprocal alone); every code must match the oracle's.
+    M <= 512 and M > 512 take different kernels."""
+    xb = synth.activations(M, K, 0.01, seed=99 + M)
     x = O.bf16_to_f32(xb).astype(np.float64)
     s = O.dynamic_quant_f32(O.bf16_to_f32(xb))[1].astype(np.float64)
     t = np.abs(x / np.where(s > 0, s, 1.0)[:, None])
-    band = int((np.abs(t - np.floor(t) - 0.5) < 2.0 ** -12).sum())
-    assert band >= 50, band
-    show(f"near-tie elements: {band}")
+    d = np.abs(t - np.floor(t) - 0.5)
+    inner = int((d < 2.0 ** -14).sum())
+    outer = int(((d >= 2.0 ** -14) & (d < 2.0 ** -12)).sum())
+    assert inner >= 20 and outer >= 50, (inner, outer)
+    show(f"near-tie elements: {inner} within 2^-14, {outer} from 2^-14 to 2^-12")
     q, sc = w.dynamic_quant(bf16_dev(xb))
     qp, scp = w.dynamic_quant_packed(bf16_dev(xb))
     sync()
     qo, so = O.dynamic_quant(xb)
     _assert_eq(host(q), qo, "q")
-    _assert_eq(_unpack_codes(host(qp), 256, 8192), qo, "q (blocks)")
+    _assert_eq(_unpack_codes(host(qp), M, K), qo, "q (blocks)")
 
 
 def test_dynamic_quant_empty(w):
@@ -326,7 +331,9 @@ def _unpack_codes(buf, M, K):
 
 
 PACKED_QUANT_SHAPES = [(1, 7168), (16, 256), (17, 7168), (64, 7168), (300, 1024), (5, 96), (33, 520),
-                       (600, 520), (1030, 7168), (513, 64)]
+                       (600, 520), (1030, 7168), (513, 64),
+                       # many-row kernels: K % 16 == 8 (one pass), K > 8192 (two passes)
+                       (520, 1032), (530, 8200)]
 
 
 @pytest.mark.parametrize("M,K", PACKED_QUANT_SHAPES)
