@@ -56,7 +56,7 @@ def _args():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode",
-                    choices=["decode", "prefill", "moe", "tiny", "copy", "mx"])
+                    choices=["decode", "prefill", "moe", "tiny", "copy", "mx", "static"])
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="approximate budget of the oracle timing on the host")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -476,6 +476,107 @@ class MxWorkload(Workload):
                            f"{n} repetitions")
 
 
+class StaticWorkload(Workload):
+    """Static W8A8 on the prefill shape (M = 8192, K = 7168, N = 4096, bias): a step is
+    the fixed-scale activation quant + the static linear. The dequant scale, the
+    integer bias and the packed weight are prepared once at setup (timed apart as
+    config.load_prep_ms)."""
+    SCALE, OFFSET = 6.0 / 127.0, 3.0   # fixed calibration of N(0, 1) activations
+
+    def __init__(self, w, torch):
+        super().__init__(w, torch)
+        import numpy as np
+
+        import synth
+        self.name = "static"
+        d = synth.prefill(seed=0)
+        self.d = d
+        self.M, self.K = d.x.shape
+        self.N = d.w.shape[0]
+        dev = "cuda"
+        self.x = torch.from_numpy(d.x.view(np.int16)).to(dev).view(torch.bfloat16)
+        wdev = torch.from_numpy(d.w).to(dev)
+        wsc = torch.from_numpy(d.w_scale).to(dev)
+        bias = torch.from_numpy(d.bias.view(np.int16)).to(dev).view(torch.bfloat16)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        self.deq, self.qb = w.static_prepare(wdev, wsc, bias, self.SCALE, self.OFFSET)
+        packed = w.prepack_weight(wdev)
+        torch.cuda.synchronize()
+        self.load_prep_ms = (time.perf_counter() - t0) * 1e3
+        self.copies = 2
+        self.wp = torch.empty((self.copies, packed.numel()), dtype=torch.uint8, device=dev)
+        for c in range(self.copies):
+            self.wp[c].copy_(packed)
+        del packed, wdev
+        # codes in the weight's block layout (whole 1 KB blocks for the tiles)
+        self.q = torch.empty((w.packed_weight_bytes(1, self.M, self.K),), dtype=torch.uint8,
+                             device=dev)
+        self.y = torch.empty((self.M, self.N), dtype=torch.bfloat16, device=dev)
+        steps = [self._make_step(c) for c in range(self.copies)]
+        self.capture(steps, [(self._make_linears(16), 16, "static_linear")])
+        self.unit = "TOPS"
+        self.bound = "mfma"
+
+    def _linear(self, c):
+        self.w.static_linear(self.q, self.wp[c], self.deq, self.qb, self.N, y=self.y, M=self.M,
+                             K=self.K)
+
+    def _make_step(self, c):
+        def fn():
+            self.w.static_quant_packed(self.x, self.SCALE, self.OFFSET, q=self.q)
+            self._linear(c)
+        return fn
+
+    def _make_linears(self, n):
+        def fn():
+            for i in range(n):
+                self._linear(i % self.copies)
+        return fn
+
+    def ops(self):
+        return 2 * self.M * self.N * self.K
+
+    def alg_bytes(self):
+        """One static linear launch: weight, dequant scale and integer bias, INT8
+        codes in, BF16 out."""
+        return self.N * self.K * BYTES_INT8 + 8 * self.N + self.M * self.K + 2 * self.M * self.N
+
+    def value(self, sec_per_step):
+        return self.ops() / sec_per_step / 1e12
+
+    def dominant(self, per_key_ms):
+        ach = self.ops() / (per_key_ms["static_linear"] * 1e-3) / 1e12
+        return dict(bound="mfma", achieved=ach, peak=PEAK_INT8_TOPS, unit="TOP/s",
+                    frac=ach / PEAK_INT8_TOPS)
+
+    def config(self):
+        return {"workload": "static", "M": self.M, "K": self.K, "N": self.N, "bias": True,
+                "scheme": "static W8A8 (per-tensor input_scale / input_offset, integer bias)",
+                "input_scale": round(self.SCALE, 8), "input_offset": self.OFFSET,
+                "weight_copies": self.copies, "packed_codes": True,
+                "load_prep_ms": round(self.load_prep_ms, 3),
+                "x": "N(0,1) with outliers x20", "w": "int8 uniform [-127,127]"}
+
+    def cpu_baseline(self, budget_s):
+        import oracle as O
+        d = self.d
+        deq, qb = O.static.static_prepare(d.w, d.w_scale, d.bias, self.SCALE, self.OFFSET)
+        rows = 128
+        t0 = time.perf_counter()
+        n = 0
+        while True:
+            q = O.static.static_quant(d.x[:rows], self.SCALE, self.OFFSET)
+            O.static.static_linear(q, d.w, deq, qb)
+            n += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
+        dt = (time.perf_counter() - t0) / n
+        return dict(value=2 * rows * self.N * self.K / dt / 1e12, unit="TOPS",
+                    sample=f"oracle static quant + static linear on the first {rows} of "
+                           f"{self.M} rows ({n} repetitions), full N and K; prepare outside")
+
+
 class CopyWorkload(Workload):
     """512 MiB device copy: HBM reference, not part of the W8A8 path."""
     NBYTES = 512 << 20
@@ -573,6 +674,8 @@ def main():
         wl = CopyWorkload(w, torch)
     elif args.workload == "mx":
         wl = MxWorkload(w, torch)
+    elif args.workload == "static":
+        wl = StaticWorkload(w, torch)
     else:
         wl = MoeWorkload(w, torch)
 

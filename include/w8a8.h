@@ -265,6 +265,47 @@ int w8a8_mx_linear(const void* x, const uint8_t* x_e8m0, int64_t M, int64_t K,
 int w8a8_mx_gemm(const uint8_t* a_e4m3, const uint8_t* a_scale_kb, int64_t M, int64_t K,
                  const void* w_packed, int64_t N, uint16_t* y, void* stream);
 
+/*
+ * Static W8A8  [DSV4, the static W8A8 comparison at the end of the page:
+ * deq_scale = input_scale * weight_scale; quant_bias = round(fp_bias /
+ * deq_scale - sum_k(Qw) * input_offset) as int32; BF16 X -> npu_quantize with
+ * a fixed input_scale / input_offset -> INT8 X -> npu_quant_matmul(x, W,
+ * deq_scale, bias=quant_bias) -> BF16 Y]. Per-tensor input_scale > 0 and
+ * input_offset, both finite, passed by value.
+ *
+ * w8a8_static_quant: q[i] = clamp(rint(fl32(fl32(x[i] / input_scale) +
+ *   input_offset)), -128, 127) elementwise (IEEE fp32 division and add, round
+ *   half to even). x device BF16 [M, K] row-major, q device int8 [M, K].
+ *   Non-finite x give unspecified codes.
+ * w8a8_static_quant_packed: the same codes written in the packed block layout
+ *   of w8a8_dynamic_quant_packed (1 KB blocks [ceil(M/16)][ceil(K/64)]; codes
+ *   of rows past M and of columns past K are 0), w8a8_packed_weight_bytes(1,
+ *   M, K) bytes, 16-byte aligned; for w8a8_static_linear with W8A8_A_PACKED.
+ * w8a8_static_prepare (load time): from the INT8 weight w [N, K] row-major
+ *   (the one given to w8a8_prepack_weight, E = 1), w_scale float [N] (every
+ *   entry > 0, finite) and an optional BF16 bias [N] (NULL: fp_bias = 0),
+ *   writes deq_scale[n] = fl32(input_scale * w_scale[n]) and quant_bias[n] =
+ *   saturate_int32(rint(fl32(fl32(fp_bias[n] / deq_scale[n]) -
+ *   fl32(fp32(S_n) * input_offset)))), S_n the exact sum of row n (float
+ *   [N] and int32 [N], caller-owned, 4-byte aligned).
+ * w8a8_static_linear: y[m, n] = BF16(fl32(fp32(acc[m, n] + quant_bias[n]) *
+ *   deq_scale[n])) for out == W8A8_OUT_BF16, or the raw INT32 acc for
+ *   W8A8_OUT_I32; q int8 [M, K] row-major (from w8a8_static_quant), or with
+ *   W8A8_A_PACKED in `out` the blocks of w8a8_static_quant_packed; w_packed
+ *   from w8a8_prepack_weight (E = 1). acc + quant_bias must fit in int32.
+ *   Same kernels and plans as w8a8_linear.
+ */
+int w8a8_static_quant(const uint16_t* x, int64_t M, int64_t K, float input_scale,
+                      float input_offset, int8_t* q, void* stream);
+int w8a8_static_quant_packed(const uint16_t* x, int64_t M, int64_t K, float input_scale,
+                             float input_offset, void* q_packed, void* stream);
+int w8a8_static_prepare(const int8_t* w, int64_t N, int64_t K, const float* w_scale,
+                        const uint16_t* bias, float input_scale, float input_offset,
+                        float* deq_scale, int32_t* quant_bias, void* stream);
+int w8a8_static_linear(const int8_t* q, int64_t M, int64_t K, const void* w_packed,
+                       const float* deq_scale, const int32_t* quant_bias, int64_t N, void* y,
+                       int out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -42,6 +42,10 @@ __all__ = [
     "mx_linear",
     "mx_gemm",
     "mx_workspace_operands",
+    "static_quant",
+    "static_quant_packed",
+    "static_prepare",
+    "static_linear",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libw8a8.so")
@@ -93,6 +97,14 @@ def _load():
         "w8a8_mx_linear": (ctypes.c_int, [_c_p, _c_p, _c_i64, _c_i64, _c_p, _c_i64, _c_p,
                                           ctypes.c_int, _c_p, _c_i64, _c_p]),
         "w8a8_mx_gemm": (ctypes.c_int, [_c_p, _c_p, _c_i64, _c_i64, _c_p, _c_i64, _c_p, _c_p]),
+        "w8a8_static_quant": (ctypes.c_int, [_c_p, _c_i64, _c_i64, ctypes.c_float, ctypes.c_float,
+                                             _c_p, _c_p]),
+        "w8a8_static_quant_packed": (ctypes.c_int, [_c_p, _c_i64, _c_i64, ctypes.c_float,
+                                                    ctypes.c_float, _c_p, _c_p]),
+        "w8a8_static_prepare": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_p, ctypes.c_float,
+                                               ctypes.c_float, _c_p, _c_p, _c_p]),
+        "w8a8_static_linear": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_i64, _c_p,
+                                              ctypes.c_int, _c_p]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -480,4 +492,83 @@ def mx_gemm(a_e4m3: torch.Tensor, a_scale_kb: torch.Tensor, M: int, K: int,
     _need(y, torch.bfloat16, "y", 2)
     _check(lib.w8a8_mx_gemm(_ptr(a_e4m3), _ptr(a_scale_kb), M, K, _ptr(w_packed), N, _ptr(y),
                             _stream()))
+    return y
+
+
+# ---------------------------------------------------------------------------
+# static W8A8
+# ---------------------------------------------------------------------------
+
+def static_quant(x: torch.Tensor, input_scale: float, input_offset: float,
+                 q: torch.Tensor | None = None) -> torch.Tensor:
+    """BF16 [M, K] -> int8 [M, K] with a fixed per-tensor scale and offset."""
+    _need(x, torch.bfloat16, "x", 2)
+    M, K = x.shape
+    if q is None:
+        q = torch.empty((M, K), dtype=torch.int8, device=x.device)
+    _need(q, torch.int8, "q", 2)
+    if tuple(q.shape) != (M, K):
+        raise ValueError("q must be [M, K]")
+    _check(lib.w8a8_static_quant(_ptr(x), M, K, float(input_scale), float(input_offset), _ptr(q),
+                                 _stream()))
+    return q
+
+
+def static_quant_packed(x: torch.Tensor, input_scale: float, input_offset: float,
+                        q: torch.Tensor | None = None) -> torch.Tensor:
+    """BF16 [M, K] -> int8 codes in the weight's 1 KB block layout (uint8 buffer)."""
+    _need(x, torch.bfloat16, "x", 2)
+    M, K = x.shape
+    nbytes = packed_weight_bytes(1, M, K)
+    if q is None:
+        q = torch.empty((nbytes,), dtype=torch.uint8, device=x.device)
+    _need(q, torch.uint8, "q", 1)
+    if q.numel() < nbytes:
+        raise ValueError("q too small for the packed layout")
+    _check(lib.w8a8_static_quant_packed(_ptr(x), M, K, float(input_scale), float(input_offset), _ptr(q),
+                                        _stream()))
+    return q
+
+
+def static_prepare(w: torch.Tensor, w_scale: torch.Tensor, bias: torch.Tensor | None,
+                   input_scale: float, input_offset: float):
+    """int8 [N, K], float [N], BF16 [N] or None -> (deq_scale float [N], quant_bias int32 [N])."""
+    _need(w, torch.int8, "w", 2)
+    _need(w_scale, torch.float32, "w_scale", 1)
+    N, K = w.shape
+    if bias is not None:
+        _need(bias, torch.bfloat16, "bias", 1)
+    deq = torch.empty((N,), dtype=torch.float32, device=w.device)
+    qb = torch.empty((N,), dtype=torch.int32, device=w.device)
+    _check(lib.w8a8_static_prepare(_ptr(w), N, K, _ptr(w_scale), _ptr(bias), float(input_scale),
+                                   float(input_offset), _ptr(deq), _ptr(qb), _stream()))
+    return deq, qb
+
+
+def static_linear(q: torch.Tensor, w_packed: torch.Tensor, deq_scale: torch.Tensor,
+                  quant_bias: torch.Tensor, N: int, out: int = OUT_BF16,
+                  y: torch.Tensor | None = None, M: int | None = None,
+                  K: int | None = None) -> torch.Tensor:
+    """Static W8A8 matmul: int8 [M, K] codes (or, with M and K given, the uint8
+    packed blocks of static_quant_packed) -> BF16 (or raw INT32) [M, N]."""
+    packed = q.dtype == torch.uint8
+    if packed:
+        _need(q, torch.uint8, "q", 1)
+        if M is None or K is None:
+            raise ValueError("packed codes need M and K")
+        if q.numel() < packed_weight_bytes(1, M, K):
+            raise ValueError("q too small for the packed layout")
+    else:
+        _need(q, torch.int8, "q", 2)
+        M, K = q.shape
+    _need(w_packed, torch.uint8, "w_packed", 1)
+    _need(deq_scale, torch.float32, "deq_scale", 1)
+    _need(quant_bias, torch.int32, "quant_bias", 1)
+    dt = torch.bfloat16 if out == OUT_BF16 else torch.int32
+    if y is None:
+        y = torch.empty((M, N), dtype=dt, device=q.device)
+    _need(y, dt, "y", 2)
+    flag = A_PACKED if packed else 0
+    _check(lib.w8a8_static_linear(_ptr(q), M, K, _ptr(w_packed), _ptr(deq_scale), _ptr(quant_bias), N,
+                                  _ptr(y), out | flag, _stream()))
     return y

@@ -398,3 +398,77 @@ int w8a8_mx_gemm(const uint8_t* a_e4m3, const uint8_t* a_scale_kb, int64_t M, in
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// static W8A8
+// ---------------------------------------------------------------------------
+
+static bool finite_f(float v) { return v == v && v - v == 0.0f; }
+
+int w8a8_static_quant(const uint16_t* x, int64_t M, int64_t K, float input_scale,
+                      float input_offset, int8_t* q, void* stream) {
+  if (M < 0 || K < 1 || M >= kMaxDim || K > W8A8_MAX_K)
+    return fail(W8A8_ERR_SHAPE, "static_quant: need M >= 0, 1 <= K <= %d", W8A8_MAX_K);
+  if (!(input_scale > 0.0f) || !finite_f(input_scale) || !finite_f(input_offset))
+    return fail(W8A8_ERR_SHAPE, "static_quant: input_scale must be > 0 and finite, input_offset finite");
+  if (M == 0) return ok();
+  if (!x || !q) return fail(W8A8_ERR_NULL, "static_quant: null pointer");
+  if (!aligned(x, 2)) return fail(W8A8_ERR_ALIGN, "static_quant: x not 2-byte aligned");
+  return launched(w8a8::launch_static_quant(x, M * K, input_scale, input_offset, q, (hipStream_t)stream),
+                  "static_quant");
+}
+
+int w8a8_static_quant_packed(const uint16_t* x, int64_t M, int64_t K, float input_scale,
+                             float input_offset, void* q_packed, void* stream) {
+  if (M < 0 || K < 1 || M >= kMaxDim || K > W8A8_MAX_K)
+    return fail(W8A8_ERR_SHAPE, "static_quant_packed: need M >= 0, 1 <= K <= %d", W8A8_MAX_K);
+  if (!(input_scale > 0.0f) || !finite_f(input_scale) || !finite_f(input_offset))
+    return fail(W8A8_ERR_SHAPE, "static_quant_packed: input_scale must be > 0 and finite, input_offset finite");
+  if (w8a8::round_up(M, 16) * w8a8::round_up(K, 64) >= ((int64_t)1 << 32))
+    return fail(W8A8_ERR_UNSUPPORTED, "static_quant_packed: packed activations past 4 GB");
+  if (M == 0) return ok();
+  if (!x || !q_packed) return fail(W8A8_ERR_NULL, "static_quant_packed: null pointer");
+  if (!aligned(x, 2) || !aligned(q_packed, 16))
+    return fail(W8A8_ERR_ALIGN, "static_quant_packed: x 2-byte, q_packed 16-byte alignment");
+  return launched(w8a8::launch_static_quant_packed(x, M, K, input_scale, input_offset, q_packed,
+                                                   (hipStream_t)stream),
+                  "static_quant_packed");
+}
+
+int w8a8_static_prepare(const int8_t* w, int64_t N, int64_t K, const float* w_scale,
+                        const uint16_t* bias, float input_scale, float input_offset,
+                        float* deq_scale, int32_t* quant_bias, void* stream) {
+  if (N < 1 || K < 1 || N >= kMaxDim || K > W8A8_MAX_K)
+    return fail(W8A8_ERR_SHAPE, "static_prepare: need N >= 1, 1 <= K <= %d", W8A8_MAX_K);
+  if (!(input_scale > 0.0f) || !finite_f(input_scale) || !finite_f(input_offset))
+    return fail(W8A8_ERR_SHAPE, "static_prepare: input_scale must be > 0 and finite, input_offset finite");
+  if (!w || !w_scale || !deq_scale || !quant_bias) return fail(W8A8_ERR_NULL, "static_prepare: null pointer");
+  if (!aligned(w_scale, 4) || !aligned(deq_scale, 4) || !aligned(quant_bias, 4) || (bias && !aligned(bias, 2)))
+    return fail(W8A8_ERR_ALIGN, "static_prepare: scales and quant_bias 4-byte, bias 2-byte alignment");
+  return launched(w8a8::launch_static_prepare(w, N, K, w_scale, bias, input_scale, input_offset, deq_scale,
+                                              quant_bias, (hipStream_t)stream),
+                  "static_prepare");
+}
+
+int w8a8_static_linear(const int8_t* q, int64_t M, int64_t K, const void* w_packed,
+                       const float* deq_scale, const int32_t* quant_bias, int64_t N, void* y,
+                       int out, void* stream) {
+  if (M < 0 || K < 1 || N < 1 || M >= kMaxDim || N >= kMaxDim || K > W8A8_MAX_K)
+    return fail(W8A8_ERR_SHAPE, "static_linear: need M >= 0, N >= 1, 1 <= K <= %d", W8A8_MAX_K);
+  const bool packed = (out & W8A8_A_PACKED) != 0;
+  out &= ~W8A8_A_PACKED;
+  if (out != W8A8_OUT_BF16 && out != W8A8_OUT_I32)
+    return fail(W8A8_ERR_UNSUPPORTED, "static_linear: unknown output kind %d", out);
+  if (packed && w8a8::round_up(M, 16) * w8a8::round_up(K, 64) >= ((int64_t)1 << 32))
+    return fail(W8A8_ERR_UNSUPPORTED, "static_linear: packed activations past 4 GB");
+  if (M == 0) return ok();
+  if (!q || !w_packed || !deq_scale || !quant_bias || !y) return fail(W8A8_ERR_NULL, "static_linear: null pointer");
+  if (!aligned(w_packed, 16) || !aligned(deq_scale, 4) || !aligned(quant_bias, 4) || !aligned(y, 4) ||
+      (packed && !aligned(q, 16)))
+    return fail(W8A8_ERR_ALIGN,
+                "static_linear: w_packed (and packed q) 16-byte, deq_scale, quant_bias and y 4-byte alignment");
+  const w8a8::DensePlan plan = w8a8::plan_dense(M, N, K);
+  return launched(w8a8::launch_dense_gemm(plan, q, nullptr, M, K, w_packed, deq_scale, N, nullptr, y, out,
+                                          packed, nullptr, (hipStream_t)stream, quant_bias),
+                  "static_linear");
+}

@@ -43,7 +43,24 @@ struct GemmArgs {
   bool a_vec;               // K % 16 == 0 and a 16-byte aligned
   const int64_t* group_list;  // grouped only
   int E;
+  // static W8A8 (dense kernels): the integer bias added to the accumulator,
+  // with w_scale holding the dequant scale and a_scale / bias unused; null
+  // for the dynamic scheme
+  const int32_t* qbias;
 };
+
+// fp32 value of one output before the BF16 rounding. Dynamic scheme:
+// ((fp32(acc) * xs) * ws) + bias. Static scheme: fp32(acc + qb) * ws, ws the
+// dequant scale. One IEEE rounding per operation, no fused multiply-add.
+__device__ __forceinline__ float out_value(const GemmArgs& p, int32_t acc, float xs, float ws,
+                                           float b, int32_t qb) {
+  if (p.qbias) return (float)(acc + qb) * ws;
+  float f = (float)acc;
+  f = f * xs;
+  f = f * ws;
+  if (p.bias) f = f + b;
+  return f;
+}
 
 // threadIdx.x through an empty asm statement: values derived from it are
 // computed where they are used instead of being hoisted out of a persistent
@@ -193,6 +210,7 @@ struct Tile {
       if (n >= p.N) continue;
       const float ws = wsc[n];
       const float b = p.bias ? bf16_to_f32(p.bias[n]) : 0.0f;
+      const int32_t qb = p.qbias ? p.qbias[n] : 0;
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
 #pragma unroll
@@ -203,10 +221,7 @@ struct Tile {
           if (p.out == kOutI32) {
             reinterpret_cast<int32_t*>(p.y)[m * p.N + n] = v;
           } else {
-            float f = (float)v;
-            f = f * p.a_scale[m];
-            f = f * ws;
-            if (p.bias) f = f + b;
+            const float f = out_value(p, v, p.a_scale ? p.a_scale[m] : 0.0f, ws, b, qb);
             reinterpret_cast<uint16_t*>(p.y)[m * p.N + n] = (uint16_t)f32_to_bf16(f);
           }
         }
@@ -460,6 +475,7 @@ struct DmaTile {
       if (n >= p.N) continue;
       const float ws = wsc[n];
       const float b = p.bias ? bf16_to_f32(p.bias[n]) : 0.0f;
+      const int32_t qb = p.qbias ? p.qbias[n] : 0;
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
 #pragma unroll
@@ -470,10 +486,7 @@ struct DmaTile {
           if (p.out == kOutI32) {
             reinterpret_cast<int32_t*>(p.y)[m * p.N + n] = val;
           } else {
-            float f = (float)val;
-            f = f * p.a_scale[m];
-            f = f * ws;
-            if (p.bias) f = f + b;
+            const float f = out_value(p, val, p.a_scale ? p.a_scale[m] : 0.0f, ws, b, qb);
             reinterpret_cast<uint16_t*>(p.y)[m * p.N + n] = (uint16_t)f32_to_bf16(f);
           }
         }
@@ -508,7 +521,7 @@ struct DmaTile {
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int64_t m = row0 + r0 + i * 16 + v;
-        xs[i][v] = p.a_scale[m < row_end ? m : row_end - 1];
+        xs[i][v] = p.a_scale ? p.a_scale[m < row_end ? m : row_end - 1] : 0.0f;
       }
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
@@ -516,14 +529,12 @@ struct DmaTile {
       const int64_t nc = n < p.N ? n : p.N - 1;  // columns past N: computed, never stored
       const float ws = wsc[nc];
       const float b = p.bias ? bf16_to_f32(p.bias[nc]) : 0.0f;
+      const int32_t qb = p.qbias ? p.qbias[nc] : 0;
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          float f = (float)acc[i][j][v];
-          f = f * xs[i][v];
-          f = f * ws;
-          if (p.bias) f = f + b;
+          const float f = out_value(p, acc[i][j][v], xs[i][v], ws, b, qb);
           *reinterpret_cast<uint16_t*>(lbase + (i * 16 + v) * kPitch + j * 32) =
               (uint16_t)f32_to_bf16(f);
         }
@@ -1151,6 +1162,7 @@ __global__ __launch_bounds__(WAVES* kWave) void decode_gemm_kernel(GemmArgs p) {
   if (n >= p.N) return;
   const float ws = p.w_scale[n];
   const float bsv = p.bias ? bf16_to_f32(p.bias[n]) : 0.0f;
+  const int32_t qb = p.qbias ? p.qbias[n] : 0;
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     const int64_t m = mbk * 16 + (lane >> 4) * 4 + t;
@@ -1158,10 +1170,7 @@ __global__ __launch_bounds__(WAVES* kWave) void decode_gemm_kernel(GemmArgs p) {
     if (p.out == kOutI32) {
       reinterpret_cast<int32_t*>(p.y)[m * p.N + n] = sum[t];
     } else {
-      float f = (float)sum[t];
-      f = f * p.a_scale[m];
-      f = f * ws;
-      if (p.bias) f = f + bsv;
+      const float f = out_value(p, sum[t], p.a_scale ? p.a_scale[m] : 0.0f, ws, bsv, qb);
       reinterpret_cast<uint16_t*>(p.y)[m * p.N + n] = (uint16_t)f32_to_bf16(f);
     }
   }
@@ -1382,10 +1391,11 @@ static bool offsets32_ok(const GemmArgs& p) {
 hipError_t launch_dense_gemm(const DensePlan& plan, const int8_t* q, const float* x_scale, int64_t M,
                              int64_t K, const void* w_packed, const float* w_scale, int64_t N,
                              const uint16_t* bias, void* y, int out, bool a_packed, void* ws,
-                             hipStream_t stream) {
+                             hipStream_t stream, const int32_t* qbias) {
   (void)ws;
   if (M == 0 || N == 0) return hipSuccess;
   GemmArgs p = make_args(q, x_scale, M, K, w_packed, w_scale, N, bias, y, out);
+  p.qbias = qbias;
   int variant = plan.variant;
   if (a_packed) {
     // packed A (1 KB blocks): the decode kernels' block variants, or the tiles

@@ -35,7 +35,17 @@ hipError_t launch_decode_fused(const uint16_t* x, int64_t M, int64_t K, const vo
 hipError_t launch_dense_gemm(const DensePlan& plan, const int8_t* q, const float* x_scale, int64_t M,
                              int64_t K, const void* w_packed, const float* w_scale, int64_t N,
                              const uint16_t* bias, void* y, int out, bool a_packed, void* ws,
-                             hipStream_t stream);
+                             hipStream_t stream, const int32_t* qbias = nullptr);
+// static W8A8: the GEMM above with qbias set (w_scale = the dequant scale,
+// x_scale = bias = null); the static activation quant and the load-time
+// dequant scale / integer bias
+hipError_t launch_static_quant(const uint16_t* x, int64_t n, float input_scale, float input_offset,
+                               int8_t* q, hipStream_t stream);
+hipError_t launch_static_quant_packed(const uint16_t* x, int64_t M, int64_t K, float input_scale,
+                                      float input_offset, void* q, hipStream_t stream);
+hipError_t launch_static_prepare(const int8_t* w, int64_t N, int64_t K, const float* w_scale,
+                                 const uint16_t* bias, float input_scale, float input_offset,
+                                 float* deq_scale, int32_t* quant_bias, hipStream_t stream);
 
 int64_t grouped_ws_bytes(int64_t R, int64_t E, int64_t N, int64_t K);
 hipError_t launch_grouped_gemm(const int8_t* a, const float* a_scale, const int64_t* group_list,

@@ -97,3 +97,31 @@ def test_mx_sizes(w):
     assert w.mx_linear_workspace_bytes(2048, 17408) == 2048 * 17408 + 272 * 2048 * 2
     assert w.mx_linear_workspace_bytes(3, 32) == 16 * 64 + 256
     assert w.mx_linear_workspace_bytes(257, 4096) == 272 * 4096 + 64 * 258 * 2
+
+
+def test_static_validation_before_launch(w):
+    L = w.lib
+    p = ctypes.c_void_p(256)  # never dereferenced: validation fails first
+    nan, inf = float("nan"), float("inf")
+    # input_scale must be > 0 and finite, the offset finite
+    assert L.w8a8_static_quant(p, 4, 64, 0.0, 0.0, p, None) == 2
+    assert L.w8a8_static_quant(p, 4, 64, -1.0, 0.0, p, None) == 2
+    assert L.w8a8_static_quant(p, 4, 64, inf, 0.0, p, None) == 2
+    assert L.w8a8_static_quant(p, 4, 64, 0.5, nan, p, None) == 2
+    assert L.w8a8_static_quant(p, 4, 0, 0.5, 0.0, p, None) == 2           # K < 1
+    assert L.w8a8_static_quant(None, 0, 64, 0.5, 0.0, None, None) == 0     # M == 0 is a no-op
+    assert L.w8a8_static_quant(None, 4, 64, 0.5, 0.0, None, None) == 1
+    assert L.w8a8_static_quant(ctypes.c_void_p(257), 4, 64, 0.5, 0.0, p, None) == 3
+    assert L.w8a8_static_prepare(p, 16, 200000, p, None, 0.5, 1.0, p, p, None) == 2
+    assert L.w8a8_static_prepare(p, 16, 64, p, None, 0.0, 1.0, p, p, None) == 2
+    assert L.w8a8_static_prepare(p, 16, 64, None, None, 0.5, 1.0, p, p, None) == 1
+    assert L.w8a8_static_prepare(p, 16, 64, p, ctypes.c_void_p(257), 0.5, 1.0, p, p, None) == 3
+    assert L.w8a8_static_linear(p, 4, 64, p, p, p, 16, p, 7, None) == 4     # unknown output kind
+    assert L.w8a8_static_linear(p, 4, 64, p, p, None, 16, p, 0, None) == 1
+    assert L.w8a8_static_linear(p, 4, 64, ctypes.c_void_p(264), p, p, 16, p, 0, None) == 3
+    assert L.w8a8_static_linear(None, 0, 64, None, None, None, 16, None, 0, None) == 0
+    assert L.w8a8_static_quant_packed(p, 4, 64, 0.5, 0.0, ctypes.c_void_p(264), None) == 3
+    assert L.w8a8_static_quant_packed(None, 4, 64, 0.5, 0.0, None, None) == 1
+    assert L.w8a8_static_quant_packed(p, 4, 64, 0.0, 0.0, p, None) == 2
+    assert L.w8a8_static_linear(ctypes.c_void_p(8), 4, 64, p, p, p, 16, p, 4, None) == 3  # packed q
+    assert L.w8a8_static_linear(p, 4, 64, p, p, p, 16, p, 8, None) == 4   # unknown flag bit
