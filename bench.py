@@ -56,7 +56,8 @@ def _args():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode",
-                    choices=["decode", "prefill", "moe", "tiny", "copy", "mx", "static"])
+                    choices=["decode", "prefill", "moe", "moe_layer", "tiny", "copy", "mx",
+                             "static"])
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="approximate budget of the oracle timing on the host")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -388,6 +389,85 @@ class MoeWorkload(Workload):
                            f"weights drawn per expert inside the timing), tokens = rows / top_k")
 
 
+class MoeLayerWorkload(MoeWorkload):
+    """The MoE workload as a whole layer: BF16 tokens in, BF16 tokens out
+    (quantize once, route, gather, W13 -> SwiGLU + requant -> W2, combine)."""
+
+    def __init__(self, w, torch):
+        super().__init__(w, torch)
+        m = self.m
+        self.name = "moe_layer"
+        E, H, I, T, k = m.E, m.H, m.I, m.T, m.top_k
+        dev = "cuda"
+        self.xt = torch.from_numpy(m.x_tokens.view("int16")).to(dev).view(torch.bfloat16)
+        self.ids = torch.from_numpy(m.topk_ids).to(dev)
+        self.wts = torch.from_numpy(m.topk_weights).to(dev)
+        self.out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+        self.lws = torch.empty((w.moe_layer_workspace_bytes(T, k, E, H, I),), dtype=torch.uint8,
+                               device=dev)
+        # sub-stage buffers for the per-kernel timing of the steps around the chain
+        self.gl2 = torch.empty((E,), dtype=torch.int64, device=dev)
+        self.rt = torch.empty((T * k,), dtype=torch.int32, device=dev)
+        self.pr = torch.empty((T, k), dtype=torch.int32, device=dev)
+        self.qt = torch.empty((T, H), dtype=torch.int8, device=dev)
+        self.st = torch.empty((T,), dtype=torch.float32, device=dev)
+        self.phases, self.dominant_graphs = [], []
+        self.capture([self._layer], [(self._w13, 1, "w13"), (self._w2, 1, "w2"),
+                                     (self._route, 1, "route"), (self._gather, 1, "gather"),
+                                     (self._combine, 1, "combine")])
+
+    def _layer(self):
+        self.w.moe_layer(self.xt, self.ids, self.wts, self.w13p, self.w13s, self.w2p, self.w2s,
+                         out=self.out, workspace=self.lws)
+
+    def _route(self):
+        self.w.moe_route(self.ids, self.m.E, self.gl2, self.rt, self.pr)
+
+    def _gather(self):
+        self.w.moe_gather(self.qt, self.st, self.rt, self.q1, self.s1)
+
+    def _combine(self):
+        self.w.moe_combine(self.y, self.pr, self.wts, out=self.out)
+
+    def alg_bytes(self):
+        """Whole layer: the two grouped GEMMs plus token quant (BF16 in, INT8 +
+        scale out), route (ids in; counts, rows and pair rows out), gather (INT8
+        rows and scales in and out) and combine (BF16 rows and weights in, BF16
+        tokens out)."""
+        m = self.m
+        T, k, H, R = m.T, m.top_k, m.H, m.R
+        quant = T * H * 2 + T * H + 4 * T
+        route = 4 * T * k + 8 * m.E + 4 * R + 4 * T * k
+        gather = 4 * R + (R * H + 4 * R) * 2
+        combine = 4 * T * k * 2 + 2 * R * H + 2 * T * H
+        return super().alg_bytes() + quant + route + gather + combine
+
+    def config(self):
+        c = super().config()
+        c["workload"] = "moe_layer"
+        c["combine"] = "topk_weights = softmax of the chosen routing scores"
+        return c
+
+    def cpu_baseline(self, budget_s):
+        import numpy as np
+
+        import oracle as O
+        m = self.m
+        IO = O.moe_io
+        t0 = time.perf_counter()
+        gl, rt, pr = IO.route(m.topk_ids, m.E)
+        IO.dispatch_int8(m.x_tokens, rt)
+        y = np.zeros((m.R, m.H), np.uint16)
+        IO.combine(y, pr, m.topk_weights)
+        t_io = time.perf_counter() - t0
+        chain = MoeWorkload.cpu_baseline(self, max(1.0, budget_s - t_io))
+        t_chain = m.top_k / chain["value"] * m.T          # oracle chain time for all R rows
+        return dict(value=m.T / (t_io + t_chain), unit="tokens/s",
+                    sample=f"oracle route + INT8 dispatch + combine over all {m.T} tokens "
+                           f"({t_io:.2f} s), plus the " + chain["sample"] +
+                           ", scaled to all rows")
+
+
 class MxWorkload(Workload):
     def __init__(self, w, torch):
         super().__init__(w, torch)
@@ -676,6 +756,8 @@ def main():
         wl = MxWorkload(w, torch)
     elif args.workload == "static":
         wl = StaticWorkload(w, torch)
+    elif args.workload == "moe_layer":
+        wl = MoeLayerWorkload(w, torch)
     else:
         wl = MoeWorkload(w, torch)
 

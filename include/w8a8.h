@@ -199,6 +199,54 @@ int w8a8_moe_grouped(const void* x_rows, const float* x_scale,
                      void* workspace, int64_t ws_bytes, void* stream);
 
 /*
+ * Around the MoE chain on one GPU.  [DSV4 §三: the INT8 dispatch quantizes the
+ * local BF16 hidden states once, to INT8 with one scale per token, and hands
+ * the runner those rows together with topk_ids, topk_weights and the number
+ * of rows of every expert; the runner feeds them to W13 without quantizing
+ * again. The order of the rows and the combine arithmetic are not on the
+ * page; the readings below are this library's.]
+ *
+ * w8a8_moe_route: topk_ids device int32 [T, top_k] -> group_list int64 [E]
+ *   (rows per expert), row_token int32 [T * top_k] (the token of every
+ *   expert-major row; entries past sum(group_list) are 0) and pair_row int32
+ *   [T, top_k] (the row of pair (t, j), -1 for an id outside [0, E), which is
+ *   dropped). Rows of one expert keep the order of the pair index
+ *   t * top_k + j. 1 <= E <= 1024, T * top_k < 2^31. One workgroup does it.
+ * w8a8_moe_gather: q int8 [T, H] and scale float [T] of the tokens (from
+ *   w8a8_dynamic_quant) -> q_rows int8 [R, H], s_rows float [R] with row p =
+ *   token row_token[p]; a token outside [0, T) gives a zero row, scale 0.
+ * w8a8_moe_combine: y_rows BF16 [R, H] (from w8a8_moe_grouped), pair_row int32
+ *   [T, top_k], topk_weights float [T, top_k] -> out BF16 [T, H] with
+ *   out[t] = BF16(sum over j = 0 .. top_k - 1 in that order of
+ *   fl32(w[t, j] * y_rows[pair_row[t, j]])), every product and every partial
+ *   sum one fp32 rounding (no fused multiply-add) from +0.0; pair rows outside
+ *   [0, R) contribute nothing.
+ * w8a8_moe_layer: the whole layer, x BF16 [T, H] -> out BF16 [T, H]:
+ *   w8a8_dynamic_quant of the T tokens, route, gather, the w8a8_moe_grouped
+ *   chain on the INT8 rows (R = T * top_k; rows past sum(group_list) are not
+ *   computed), combine. w13/w2 as for w8a8_moe_grouped; workspace of
+ *   w8a8_moe_layer_workspace_bytes(T, top_k, E, H, I) bytes, 256-byte aligned,
+ *   rewritten by every call.
+ * All buffers are device memory owned by the caller; int32 / float arrays
+ * 4-byte aligned, group_list 8-byte aligned.
+ */
+int w8a8_moe_route(const int32_t* topk_ids, int64_t T, int64_t top_k, int64_t E,
+                   int64_t* group_list, int32_t* row_token, int32_t* pair_row, void* stream);
+int w8a8_moe_gather(const int8_t* q, const float* scale, int64_t T, int64_t H,
+                    const int32_t* row_token, int64_t R, int8_t* q_rows, float* s_rows,
+                    void* stream);
+int w8a8_moe_combine(const uint16_t* y_rows, int64_t R, int64_t H, const int32_t* pair_row,
+                     const float* topk_weights, int64_t T, int64_t top_k, uint16_t* out,
+                     void* stream);
+int64_t w8a8_moe_layer_workspace_bytes(int64_t T, int64_t top_k, int64_t E, int64_t H,
+                                       int64_t I);
+int w8a8_moe_layer(const uint16_t* x, int64_t T, int64_t H, const int32_t* topk_ids,
+                   const float* topk_weights, int64_t top_k, int64_t E, int64_t I,
+                   const void* w13_packed, const float* w13_scale, const void* w2_packed,
+                   const float* w2_scale, uint16_t* out, void* workspace, int64_t ws_bytes,
+                   void* stream);
+
+/*
  * MXFP8 variant.  [MXFP8] = "Qwen3.8-FP8 on Ascend 950: Why Weights Become
  * MXFP8 at Load Time". E4M3 = OCP E4M3FN (largest finite 448); E8M0 byte b
  * stands for 2^(b - 127). Scales are row-major [rows, K/32] at this boundary.

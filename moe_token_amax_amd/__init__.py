@@ -34,6 +34,11 @@ __all__ = [
     "swiglu_quant",
     "moe_workspace_bytes",
     "moe_grouped",
+    "moe_route",
+    "moe_gather",
+    "moe_combine",
+    "moe_layer_workspace_bytes",
+    "moe_layer",
     "mx_quant",
     "mx_resolve_block_fp8",
     "mx_packed_bytes",
@@ -88,6 +93,14 @@ def _load():
         "w8a8_moe_workspace_bytes": (_c_i64, [_c_i64, _c_i64, _c_i64, _c_i64]),
         "w8a8_moe_grouped": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i64,
                                             _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_p]),
+        "w8a8_moe_route": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p]),
+        "w8a8_moe_gather": (ctypes.c_int, [_c_p, _c_p, _c_i64, _c_i64, _c_p, _c_i64, _c_p, _c_p,
+                                           _c_p]),
+        "w8a8_moe_combine": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_i64, _c_i64, _c_p,
+                                            _c_p]),
+        "w8a8_moe_layer_workspace_bytes": (_c_i64, [_c_i64, _c_i64, _c_i64, _c_i64, _c_i64]),
+        "w8a8_moe_layer": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_i64, _c_i64, _c_i64,
+                                          _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_p]),
         "w8a8_mx_quant": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_p, ctypes.c_int, _c_p]),
         "w8a8_mx_resolve_block_fp8": (ctypes.c_int, [_c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i64,
                                                      _c_p, _c_p]),
@@ -379,6 +392,112 @@ def moe_grouped(x_rows: torch.Tensor, group_list: torch.Tensor, w13_packed: torc
                                 _ptr(w13_packed), _ptr(w13_scale), _ptr(w2_packed),
                                 _ptr(w2_scale), _ptr(y), _ptr(ws), ws_n, _stream()))
     return y
+
+
+def moe_route(topk_ids: torch.Tensor, E: int, group_list: torch.Tensor | None = None,
+              row_token: torch.Tensor | None = None, pair_row: torch.Tensor | None = None):
+    """int32 expert ids [T, top_k] -> (group_list int64 [E], row_token int32 [T * top_k],
+    pair_row int32 [T, top_k]); rows expert-major, pair order inside an expert."""
+    _need(topk_ids, torch.int32, "topk_ids", 2)
+    T, k = topk_ids.shape
+    dev = topk_ids.device
+    if group_list is None:
+        group_list = torch.empty((E,), dtype=torch.int64, device=dev)
+    if row_token is None:
+        row_token = torch.empty((T * k,), dtype=torch.int32, device=dev)
+    if pair_row is None:
+        pair_row = torch.empty((T, k), dtype=torch.int32, device=dev)
+    _need(group_list, torch.int64, "group_list", 1)
+    _need(row_token, torch.int32, "row_token", 1)
+    _need(pair_row, torch.int32, "pair_row", 2)
+    if group_list.shape[0] != E or row_token.shape[0] != T * k or tuple(pair_row.shape) != (T, k):
+        raise ValueError("route output shape mismatch")
+    _check(lib.w8a8_moe_route(_ptr(topk_ids), T, k, E, _ptr(group_list), _ptr(row_token),
+                              _ptr(pair_row), _stream()))
+    return group_list, row_token, pair_row
+
+
+def moe_gather(q: torch.Tensor, scale: torch.Tensor, row_token: torch.Tensor,
+               q_rows: torch.Tensor | None = None, s_rows: torch.Tensor | None = None):
+    """INT8 tokens [T, H] + scales [T] -> rows [R, H] + scales [R], row p = token row_token[p]."""
+    _need(q, torch.int8, "q", 2)
+    _need(scale, torch.float32, "scale", 1)
+    _need(row_token, torch.int32, "row_token", 1)
+    T, H = q.shape
+    R = row_token.shape[0]
+    if scale.shape[0] != T:
+        raise ValueError("scale must have T entries")
+    if q_rows is None:
+        q_rows = torch.empty((R, H), dtype=torch.int8, device=q.device)
+    if s_rows is None:
+        s_rows = torch.empty((R,), dtype=torch.float32, device=q.device)
+    _need(q_rows, torch.int8, "q_rows", 2)
+    _need(s_rows, torch.float32, "s_rows", 1)
+    if tuple(q_rows.shape) != (R, H) or s_rows.shape[0] != R:
+        raise ValueError("gather output shape mismatch")
+    _check(lib.w8a8_moe_gather(_ptr(q), _ptr(scale), T, H, _ptr(row_token), R, _ptr(q_rows),
+                               _ptr(s_rows), _stream()))
+    return q_rows, s_rows
+
+
+def moe_combine(y_rows: torch.Tensor, pair_row: torch.Tensor, topk_weights: torch.Tensor,
+                out: torch.Tensor | None = None):
+    """BF16 rows [R, H] -> BF16 tokens [T, H]: weighted sum of every token's top_k rows."""
+    _need(y_rows, torch.bfloat16, "y_rows", 2)
+    _need(pair_row, torch.int32, "pair_row", 2)
+    _need(topk_weights, torch.float32, "topk_weights", 2)
+    R, H = y_rows.shape
+    T, k = pair_row.shape
+    if tuple(topk_weights.shape) != (T, k):
+        raise ValueError("topk_weights must match pair_row")
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=y_rows.device)
+    _need(out, torch.bfloat16, "out", 2)
+    if tuple(out.shape) != (T, H):
+        raise ValueError("out shape mismatch")
+    _check(lib.w8a8_moe_combine(_ptr(y_rows), R, H, _ptr(pair_row), _ptr(topk_weights), T, k,
+                                _ptr(out), _stream()))
+    return out
+
+
+def moe_layer_workspace_bytes(T: int, top_k: int, E: int, H: int, I: int) -> int:
+    return int(lib.w8a8_moe_layer_workspace_bytes(T, top_k, E, H, I))
+
+
+def moe_layer(x: torch.Tensor, topk_ids: torch.Tensor, topk_weights: torch.Tensor,
+              w13_packed: torch.Tensor, w13_scale: torch.Tensor, w2_packed: torch.Tensor,
+              w2_scale: torch.Tensor, out: torch.Tensor | None = None,
+              workspace: torch.Tensor | None = None):
+    """Whole MoE layer: BF16 tokens [T, H] -> quantize once, route, gather, W13 ->
+    SwiGLU + requant -> W2, weighted combine -> BF16 [T, H]."""
+    _need(x, torch.bfloat16, "x", 2)
+    _need(topk_ids, torch.int32, "topk_ids", 2)
+    _need(topk_weights, torch.float32, "topk_weights", 2)
+    _need(w13_scale, torch.float32, "w13_scale", 2)
+    _need(w2_scale, torch.float32, "w2_scale", 2)
+    _need(w13_packed, torch.uint8, "w13_packed", 1)
+    _need(w2_packed, torch.uint8, "w2_packed", 1)
+    T, H = x.shape
+    k = topk_ids.shape[1]
+    E = w13_scale.shape[0]
+    I = w13_scale.shape[1] // 2
+    if topk_ids.shape[0] != T or tuple(topk_weights.shape) != tuple(topk_ids.shape):
+        raise ValueError("topk_ids / topk_weights must be [T, top_k]")
+    if tuple(w13_scale.shape) != (E, 2 * I) or tuple(w2_scale.shape) != (E, H):
+        raise ValueError("scale shape mismatch")
+    if w13_packed.numel() < packed_weight_bytes(E, 2 * I, H) or \
+            w2_packed.numel() < packed_weight_bytes(E, H, I):
+        raise ValueError("packed weights too small")
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
+    _need(out, torch.bfloat16, "out", 2)
+    if tuple(out.shape) != (T, H):
+        raise ValueError("out shape mismatch")
+    ws, ws_n = _workspace(moe_layer_workspace_bytes(T, k, E, H, I), x.device, workspace)
+    _check(lib.w8a8_moe_layer(_ptr(x), T, H, _ptr(topk_ids), _ptr(topk_weights), k, E, I,
+                              _ptr(w13_packed), _ptr(w13_scale), _ptr(w2_packed), _ptr(w2_scale),
+                              _ptr(out), _ptr(ws), ws_n, _stream()))
+    return out
 
 
 # ---------------------------------------------------------------------------

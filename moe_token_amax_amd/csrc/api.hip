@@ -280,6 +280,141 @@ int w8a8_moe_grouped(const void* x_rows, const float* x_scale, const int64_t* gr
 }
 
 // ---------------------------------------------------------------------------
+// Around the MoE chain: route, INT8 gather, weighted combine, whole layer
+// ---------------------------------------------------------------------------
+static int check_route(const char* who, int64_t T, int64_t top_k, int64_t E) {
+  if (T < 0 || top_k < 1 || E < 1 || T * top_k >= kMaxDim)
+    return fail(W8A8_ERR_SHAPE, "%s: need T >= 0, top_k >= 1, E >= 1 and T * top_k < 2^31", who);
+  if (E > kMaxExperts)
+    return fail(W8A8_ERR_UNSUPPORTED, "%s: at most %lld experts", who, (long long)kMaxExperts);
+  return W8A8_OK;
+}
+
+int w8a8_moe_route(const int32_t* topk_ids, int64_t T, int64_t top_k, int64_t E,
+                   int64_t* group_list, int32_t* row_token, int32_t* pair_row, void* stream) {
+  int st = check_route("moe_route", T, top_k, E);
+  if (st) return st;
+  if (!group_list || (T > 0 && (!topk_ids || !row_token || !pair_row)))
+    return fail(W8A8_ERR_NULL, "moe_route: null pointer");
+  if (!aligned(group_list, 8) || !aligned(topk_ids, 4) || !aligned(row_token, 4) ||
+      !aligned(pair_row, 4))
+    return fail(W8A8_ERR_ALIGN, "moe_route: misaligned buffer");
+  return launched(w8a8::launch_route(topk_ids, T, top_k, E, group_list, row_token, pair_row,
+                                     (hipStream_t)stream),
+                  "moe_route");
+}
+
+int w8a8_moe_gather(const int8_t* q, const float* scale, int64_t T, int64_t H,
+                    const int32_t* row_token, int64_t R, int8_t* q_rows, float* s_rows,
+                    void* stream) {
+  if (T < 0 || R < 0 || H < 1 || T >= kMaxDim || R >= kMaxDim || H > W8A8_MAX_K)
+    return fail(W8A8_ERR_SHAPE, "moe_gather: need T >= 0, R >= 0 and 1 <= H <= %d", W8A8_MAX_K);
+  if (R == 0) return ok();
+  if (!q || !scale || !row_token || !q_rows || !s_rows)
+    return fail(W8A8_ERR_NULL, "moe_gather: null pointer");
+  if (!aligned(scale, 4) || !aligned(row_token, 4) || !aligned(s_rows, 4))
+    return fail(W8A8_ERR_ALIGN, "moe_gather: misaligned buffer");
+  return launched(w8a8::launch_gather_rows(q, scale, row_token, T, R, H, q_rows, s_rows,
+                                           (hipStream_t)stream),
+                  "moe_gather");
+}
+
+int w8a8_moe_combine(const uint16_t* y_rows, int64_t R, int64_t H, const int32_t* pair_row,
+                     const float* topk_weights, int64_t T, int64_t top_k, uint16_t* out,
+                     void* stream) {
+  if (T < 0 || R < 0 || H < 1 || top_k < 1 || T * top_k >= kMaxDim || R >= kMaxDim ||
+      H >= kMaxDim)
+    return fail(W8A8_ERR_SHAPE, "moe_combine: need T >= 0, R >= 0, H >= 1, top_k >= 1");
+  if (T == 0) return ok();
+  if (!pair_row || !topk_weights || !out || (R > 0 && !y_rows))
+    return fail(W8A8_ERR_NULL, "moe_combine: null pointer");
+  if (!aligned(y_rows, 2) || !aligned(pair_row, 4) || !aligned(topk_weights, 4) ||
+      !aligned(out, 2))
+    return fail(W8A8_ERR_ALIGN, "moe_combine: misaligned buffer");
+  return launched(w8a8::launch_combine(y_rows, pair_row, topk_weights, T, top_k, R, H, out,
+                                       (hipStream_t)stream),
+                  "moe_combine");
+}
+
+namespace {
+
+struct LayerWs {
+  int64_t q, s, gl, rt, pr, qr, sr, y, chain, total;
+};
+
+LayerWs layer_layout(int64_t T, int64_t k, int64_t E, int64_t H, int64_t I) {
+  const int64_t P = T * k;
+  LayerWs w{};
+  int64_t o = 0;
+  w.q = o;  o += align256(T * H);          // int8 [T, H]: the tokens, quantized once
+  w.s = o;  o += align256(T * 4);          // f32 [T]
+  w.gl = o; o += align256(E * 8);          // int64 [E]
+  w.rt = o; o += align256(P * 4);          // int32 [P]
+  w.pr = o; o += align256(P * 4);          // int32 [T, k]
+  w.qr = o; o += align256(P * H);          // int8 [P, H]
+  w.sr = o; o += align256(P * 4);          // f32 [P]
+  w.y = o;  o += align256(P * H * 2);      // BF16 [P, H]
+  w.chain = o;
+  o += moe_layout(P, E, H, I).total;
+  w.total = o;
+  return w;
+}
+
+}  // namespace
+
+int64_t w8a8_moe_layer_workspace_bytes(int64_t T, int64_t top_k, int64_t E, int64_t H, int64_t I) {
+  if (T <= 0 || top_k <= 0 || E <= 0 || H <= 0 || I <= 0) return 0;
+  return layer_layout(T, top_k, E, H, I).total;
+}
+
+int w8a8_moe_layer(const uint16_t* x, int64_t T, int64_t H, const int32_t* topk_ids,
+                   const float* topk_weights, int64_t top_k, int64_t E, int64_t I,
+                   const void* w13_packed, const float* w13_scale, const void* w2_packed,
+                   const float* w2_scale, uint16_t* out, void* workspace, int64_t ws_bytes,
+                   void* stream) {
+  int st = check_route("moe_layer", T, top_k, E);
+  if (st) return st;
+  const int64_t P = T * top_k;
+  st = check_grouped("moe_layer", P, E, 2 * I, H);
+  if (st) return st;
+  st = check_grouped("moe_layer", P, E, H, I);
+  if (st) return st;
+  if (T == 0) return ok();
+  if (!x || !topk_ids || !topk_weights || !w13_packed || !w13_scale || !w2_packed || !w2_scale ||
+      !out)
+    return fail(W8A8_ERR_NULL, "moe_layer: null pointer");
+  if (!aligned(x, 2) || !aligned(topk_ids, 4) || !aligned(topk_weights, 4) ||
+      !aligned(w13_packed, 16) || !aligned(w2_packed, 16) || !aligned(w13_scale, 4) ||
+      !aligned(w2_scale, 4) || !aligned(out, 2))
+    return fail(W8A8_ERR_ALIGN, "moe_layer: misaligned buffer");
+  const LayerWs L = layer_layout(T, top_k, E, H, I);
+  if (!workspace || ws_bytes < L.total || !aligned(workspace, 256))
+    return fail(W8A8_ERR_WORKSPACE, "moe_layer: needs %lld workspace bytes (256-byte aligned), got %lld",
+                (long long)L.total, (long long)ws_bytes);
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = reinterpret_cast<char*>(workspace);
+  int8_t* q = reinterpret_cast<int8_t*>(ws + L.q);
+  float* sc = reinterpret_cast<float*>(ws + L.s);
+  int64_t* gl = reinterpret_cast<int64_t*>(ws + L.gl);
+  int32_t* rt = reinterpret_cast<int32_t*>(ws + L.rt);
+  int32_t* pr = reinterpret_cast<int32_t*>(ws + L.pr);
+  int8_t* qr = reinterpret_cast<int8_t*>(ws + L.qr);
+  float* sr = reinterpret_cast<float*>(ws + L.sr);
+  uint16_t* y = reinterpret_cast<uint16_t*>(ws + L.y);
+  hipError_t err = w8a8::launch_dynamic_quant(x, T, H, q, sc, false, s);
+  if (err != hipSuccess) return launched(err, "moe_layer: dynamic_quant");
+  err = w8a8::launch_route(topk_ids, T, top_k, E, gl, rt, pr, s);
+  if (err != hipSuccess) return launched(err, "moe_layer: route");
+  err = w8a8::launch_gather_rows(q, sc, rt, T, P, H, qr, sr, s);
+  if (err != hipSuccess) return launched(err, "moe_layer: gather");
+  st = w8a8_moe_grouped(qr, sr, gl, P, E, H, I, w13_packed, w13_scale, w2_packed, w2_scale, y,
+                        ws + L.chain, L.total - L.chain, stream);
+  if (st) return st;
+  return launched(w8a8::launch_combine(y, pr, topk_weights, T, top_k, P, H, out, s),
+                  "moe_layer: combine");
+}
+
+// ---------------------------------------------------------------------------
 // MXFP8 variant
 // ---------------------------------------------------------------------------
 static int64_t mx_payload_bytes(int64_t N, int64_t K) {

@@ -48,6 +48,16 @@ hipError_t launch_static_prepare(const int8_t* w, int64_t N, int64_t K, const fl
                                  float* deq_scale, int32_t* quant_bias, hipStream_t stream);
 
 int64_t grouped_ws_bytes(int64_t R, int64_t E, int64_t N, int64_t K);
+
+// around the MoE chain: routing of (token, slot) expert ids, gather of the INT8
+// rows, and the weighted combine (moe_io.hip)
+hipError_t launch_route(const int32_t* ids, int64_t T, int64_t k, int64_t E, int64_t* group_list,
+                        int32_t* row_token, int32_t* pair_row, hipStream_t stream);
+hipError_t launch_gather_rows(const int8_t* q, const float* scale, const int32_t* row_token,
+                              int64_t T, int64_t R, int64_t H, int8_t* q_rows, float* s_rows,
+                              hipStream_t stream);
+hipError_t launch_combine(const uint16_t* y, const int32_t* pair_row, const float* wts, int64_t T,
+                          int64_t k, int64_t R, int64_t H, uint16_t* out, hipStream_t stream);
 hipError_t launch_grouped_gemm(const int8_t* a, const float* a_scale, const int64_t* group_list,
                                int64_t R, int64_t E, int64_t N, int64_t K, const void* w_packed,
                                const float* w_scale, void* y, int out, void* ws,

@@ -112,19 +112,31 @@ def prefill(seed: int = 0, M: int = 8192) -> Dense:
 # MoE routing inputs
 # ---------------------------------------------------------------------------
 
-def route_topk(T: int, E: int, top_k: int, seed: int, ebias_sigma: float = 1.5):
-    """Top-k routing from logits N(0,1) + per-expert bias N(0, sigma).
+def topk_routing(T: int, E: int, top_k: int, seed: int, ebias_sigma: float = 1.5):
+    """Top-k routing inputs from logits N(0,1) + per-expert bias N(0, sigma).
 
-    Ties in score go to the lower expert id. The (token, expert) pairs are then
-    grouped by expert, tokens ascending inside each expert.
-    Returns (row_token [T*k], row_expert [T*k], group_list [E] int64).
+    Returns (topk_ids int32 [T, top_k], topk_weights float32 [T, top_k]): the
+    experts of every token by descending score (ties to the lower id) and
+    weights that are the softmax of the chosen scores (an input recipe only).
     """
     logits = rng_for(seed, _T_LOGITS).standard_normal((T, E), dtype=np.float32)
     ebias = rng_for(seed, _T_EBIAS).normal(0.0, ebias_sigma, size=E).astype(np.float32)
     score = logits + ebias[None, :]
-    order = np.argsort(-score, axis=1, kind="stable")[:, :top_k]
+    ids = np.argsort(-score, axis=1, kind="stable")[:, :top_k]
+    chosen = np.take_along_axis(score, ids, axis=1).astype(np.float64)
+    wts = np.exp(chosen - chosen.max(axis=1, keepdims=True))
+    wts = (wts / wts.sum(axis=1, keepdims=True)).astype(np.float32)
+    return ids.astype(np.int32), wts
+
+
+def route_topk(T: int, E: int, top_k: int, seed: int, ebias_sigma: float = 1.5):
+    """The (token, expert) pairs of ``topk_routing`` grouped by expert, tokens
+    ascending inside each expert.
+    Returns (row_token [T*k], row_expert [T*k], group_list [E] int64).
+    """
+    ids, _ = topk_routing(T, E, top_k, seed, ebias_sigma)
     tok = np.repeat(np.arange(T, dtype=np.int64), top_k)
-    exp_ = order.reshape(-1).astype(np.int64)
+    exp_ = ids.reshape(-1).astype(np.int64)
     perm = np.lexsort((tok, exp_))
     row_token, row_expert = tok[perm], exp_[perm]
     group_list = np.bincount(row_expert, minlength=E).astype(np.int64)
@@ -144,6 +156,8 @@ class MoE:
     group_list: np.ndarray    # int64 [E]
     w13_scale: np.ndarray     # f32 [E, 2I]
     w2_scale: np.ndarray      # f32 [E, H]
+    topk_ids: np.ndarray = None       # int32 [T, top_k]
+    topk_weights: np.ndarray = None   # f32 [T, top_k]
     _w13: dict = field(default_factory=dict, repr=False)
     _w2: dict = field(default_factory=dict, repr=False)
 
@@ -183,9 +197,10 @@ def moe(T: int = 2048, H: int = 4096, I: int = 2048, E: int = 256, top_k: int = 
         seed: int = 0, ebias_sigma: float = 1.5) -> MoE:
     x = activations(T, H, 0.0, seed)
     row_token, _, group_list = route_topk(T, E, top_k, seed, ebias_sigma)
+    ids, wts = topk_routing(T, E, top_k, seed, ebias_sigma)
     w13s = np.stack([scales(2 * I, seed, _T_W13S, e) for e in range(E)])
     w2s = np.stack([scales(H, seed, _T_W2S, e) for e in range(E)])
-    return MoE(T, H, I, E, top_k, seed, x, row_token, group_list, w13s, w2s)
+    return MoE(T, H, I, E, top_k, seed, x, row_token, group_list, w13s, w2s, ids, wts)
 
 
 # ---------------------------------------------------------------------------

@@ -125,3 +125,41 @@ def test_static_validation_before_launch(w):
     assert L.w8a8_static_quant_packed(p, 4, 64, 0.0, 0.0, p, None) == 2
     assert L.w8a8_static_linear(ctypes.c_void_p(8), 4, 64, p, p, p, 16, p, 4, None) == 3  # packed q
     assert L.w8a8_static_linear(p, 4, 64, p, p, p, 16, p, 8, None) == 4   # unknown flag bit
+
+
+def test_moe_io_validation_before_launch(w):
+    L = w.lib
+    p = ctypes.c_void_p(256)  # never dereferenced: validation fails first
+    # route: E in [1, 1024], top_k >= 1, T * top_k < 2^31
+    assert L.w8a8_moe_route(p, 4, 2, 0, p, p, p, None) == 2
+    assert L.w8a8_moe_route(p, 4, 0, 8, p, p, p, None) == 2
+    assert L.w8a8_moe_route(p, 1 << 28, 8, 8, p, p, p, None) == 2
+    assert L.w8a8_moe_route(p, 4, 2, 1025, p, p, p, None) == 4
+    assert L.w8a8_moe_route(p, 4, 2, 8, None, p, p, None) == 1
+    assert L.w8a8_moe_route(p, 4, 2, 8, p, None, p, None) == 1
+    assert L.w8a8_moe_route(p, 4, 2, 8, ctypes.c_void_p(260), p, p, None) == 3  # group_list 8-byte
+    assert L.w8a8_moe_route(p, 4, 2, 8, p, p, ctypes.c_void_p(258), None) == 3
+    # gather
+    assert L.w8a8_moe_gather(p, p, 4, 0, p, 8, p, p, None) == 2
+    assert L.w8a8_moe_gather(p, p, 4, 64, p, -1, p, p, None) == 2
+    assert L.w8a8_moe_gather(None, None, 4, 64, None, 0, None, None, None) == 0   # R == 0
+    assert L.w8a8_moe_gather(p, p, 4, 64, p, 8, None, p, None) == 1
+    assert L.w8a8_moe_gather(p, ctypes.c_void_p(258), 4, 64, p, 8, p, p, None) == 3
+    # combine
+    assert L.w8a8_moe_combine(p, 8, 0, p, p, 4, 2, p, None) == 2
+    assert L.w8a8_moe_combine(p, 8, 64, p, p, 4, 0, p, None) == 2
+    assert L.w8a8_moe_combine(None, 8, 64, None, None, 0, 2, None, None) == 0     # T == 0
+    assert L.w8a8_moe_combine(p, 8, 64, p, None, 4, 2, p, None) == 1
+    assert L.w8a8_moe_combine(ctypes.c_void_p(257), 8, 64, p, p, 4, 2, p, None) == 3
+    # whole layer
+    assert L.w8a8_moe_layer_workspace_bytes(0, 8, 256, 4096, 2048) == 0
+    need = L.w8a8_moe_layer_workspace_bytes(64, 8, 16, 256, 128)
+    assert need >= 64 * 256 + 64 * 8 * (256 + 2 * 256)
+    assert L.w8a8_moe_layer(p, 64, 256, p, p, 8, 16, 128, p, p, p, p, p, p, need - 1, None) == 5
+    assert L.w8a8_moe_layer(p, 64, 256, p, p, 8, 16, 128, p, p, p, p, p, None, need, None) == 5
+    assert L.w8a8_moe_layer(p, 64, 256, p, p, 8, 2000, 128, p, p, p, p, p, p, need, None) == 4
+    assert L.w8a8_moe_layer(p, 64, 256, p, None, 8, 16, 128, p, p, p, p, p, p, need, None) == 1
+    assert L.w8a8_moe_layer(p, 64, 256, p, p, 8, 16, 128, ctypes.c_void_p(264), p, p, p, p, p,
+                            need, None) == 3
+    assert L.w8a8_moe_layer(None, 0, 256, None, None, 8, 16, 128, None, None, None, None, None,
+                            None, 0, None) == 0
