@@ -18,38 +18,79 @@
 namespace w8a8 {
 
 constexpr int kRouteThreads = 1024, kRouteWaves = kRouteThreads / kWave;
-constexpr int kMaxExpertsDev = 1024;  // one scan value per thread
+constexpr int kMaxExpertsDev = 1024;  // one scan value per thread; ids need 10 bits
 
-// One 1024-thread workgroup (E <= 1024). Counts with LDS atomics, exclusive
-// scan, then the pairs in chunks of 1024: a pair's place within its expert is
-// the expert's count from earlier chunks, plus those of earlier wavefronts in
-// the chunk, plus those of earlier lanes in its wavefront (shuffles), so the
-// order is the pair order. Row slots past the number of routed pairs get
-// token 0 (a valid index for a gather over all T * top_k rows).
+// Lanes of the wavefront whose key (0 .. 2^11 - 1) equals this lane's: one
+// ballot per bit. Every lane of the wavefront must take part.
+__device__ __forceinline__ uint64_t match_lanes(int key) {
+  uint64_t same = ~0ull;
+#pragma unroll
+  for (int bit = 0; bit < 11; ++bit) {
+    const int mine = (key >> bit) & 1;
+    const uint64_t b = __ballot(mine);
+    same &= mine ? b : ~b;
+  }
+  return same;
+}
+
+// One workgroup per chunk of 1024 pairs (E <= 1024), one launch. Every
+// workgroup counts all pairs itself in LDS (per-expert totals, and the counts
+// of the pairs before its chunk), scans the totals into expert offsets, and
+// places the pairs of its chunk: a pair's row is its expert's offset, plus
+// that expert's pairs in earlier chunks, in earlier wavefronts of this chunk
+// and in earlier lanes of its wavefront. Lanes with the same expert are found
+// with one ballot per bit of the id, so the order is the pair order. Row
+// slots past the number of routed pairs get token 0 (a valid index for a
+// gather over all T * top_k rows).
 __global__ __launch_bounds__(kRouteThreads) void route_kernel(const int32_t* __restrict__ ids,
                                                               int64_t P, int k, int E,
                                                               int64_t* __restrict__ group_list,
                                                               int32_t* __restrict__ row_token,
                                                               int32_t* __restrict__ pair_row) {
-  __shared__ int cnt[kMaxExpertsDev];
+  __shared__ int tot[kMaxExpertsDev];
+  __shared__ int pre[kMaxExpertsDev];
   __shared__ int off[kMaxExpertsDev];
-  __shared__ int base[kMaxExpertsDev];
-  __shared__ unsigned char wcnt[kRouteWaves][kMaxExpertsDev];
+  __shared__ __align__(16) unsigned char wcnt[kRouteWaves][kMaxExpertsDev];
   __shared__ int wsum[kRouteWaves];
+  static_assert(kRouteWaves * kMaxExpertsDev == 16 * kRouteThreads, "one 16-byte clear per thread");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t c0 = (int64_t)blockIdx.x * kRouteThreads;
   for (int e = tid; e < E; e += kRouteThreads) {
-    cnt[e] = 0;
-    base[e] = 0;
+    tot[e] = 0;
+    pre[e] = 0;
   }
-  for (int i = tid; i < kRouteWaves * kMaxExpertsDev; i += kRouteThreads) (&wcnt[0][0])[i] = 0;
+  reinterpret_cast<uint4*>(&wcnt[0][0])[tid] = uint4{0u, 0u, 0u, 0u};
   __syncthreads();
-  for (int64_t i = tid; i < P; i += kRouteThreads) {
-    const int e = ids[i];
-    if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+  auto count = [&](int e, int64_t i) {
+    if (e >= 0 && e < E) {
+      atomicAdd(&tot[e], 1);
+      if (i < c0) atomicAdd(&pre[e], 1);
+    }
+  };
+  // four ids per 16-byte load when the array allows it (a thread's loads of one
+  // step issued before its atomics), the rest one by one
+  const int64_t P4 = (reinterpret_cast<uintptr_t>(ids) & 15) == 0 ? P / 4 : 0;
+  constexpr int kBatch = 4;
+  for (int64_t v0 = tid; v0 < P4; v0 += kBatch * kRouteThreads) {
+    int4 q[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int64_t v = v0 + (int64_t)u * kRouteThreads;
+      q[u] = v < P4 ? reinterpret_cast<const int4*>(ids)[v] : int4{-1, -1, -1, -1};
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int64_t v = v0 + (int64_t)u * kRouteThreads;
+      count(q[u].x, 4 * v);
+      count(q[u].y, 4 * v + 1);
+      count(q[u].z, 4 * v + 2);
+      count(q[u].w, 4 * v + 3);
+    }
   }
+  for (int64_t i = 4 * P4 + tid; i < P; i += kRouteThreads) count(ids[i], i);
   __syncthreads();
-  // exclusive scan of cnt[0 .. E) (one value per thread)
-  const int c = tid < E ? cnt[tid] : 0;
+  // exclusive scan of tot[0 .. E) (one value per thread)
+  const int c = tid < E ? tot[tid] : 0;
   int incl = c;
 #pragma unroll
   for (int d = 1; d < kWave; d <<= 1) {
@@ -61,77 +102,87 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(const int32_t* __r
   for (int w = 0; w < wave; ++w) incl += wsum[w];
   if (tid < E) {
     off[tid] = incl - c;
-    group_list[tid] = c;
+    if (blockIdx.x == 0) group_list[tid] = c;
   }
+  // this workgroup's chunk
+  const int64_t i = c0 + tid;
+  int e = i < P ? ids[i] : -1;
+  const bool valid = e >= 0 && e < E;
+  const uint64_t same = match_lanes(valid ? e : kMaxExpertsDev);
+  const int before = __popcll(same & ((1ull << lane) - 1ull));
+  if (valid && before == 0) wcnt[wave][e] = (unsigned char)__popcll(same);
   __syncthreads();
-  const int routed = off[E - 1] + cnt[E - 1];
-  for (int64_t c0 = 0; c0 < P; c0 += kRouteThreads) {
-    const int64_t i = c0 + tid;
-    int e = -1;
-    if (i < P) {
-      e = ids[i];
-      if (e < 0 || e >= E) e = -1;
-    }
-    int before = 0, total = 0;
-    for (int d = 0; d < kWave; ++d) {
-      const int ed = __shfl(e, d, kWave);
-      const int same = (ed == e) ? 1 : 0;
-      before += (d < lane) ? same : 0;
-      total += same;
-    }
-    if (e >= 0 && before == 0) wcnt[wave][e] = (unsigned char)total;
-    __syncthreads();
-    if (e >= 0) {
-      int pos = off[e] + base[e] + before;
-      for (int w = 0; w < wave; ++w) pos += wcnt[w][e];
-      row_token[pos] = (int32_t)(i / k);
-      pair_row[i] = pos;
-    } else if (i < P) {
-      pair_row[i] = -1;
-    }
-    __syncthreads();
-    for (int ee = tid; ee < E; ee += kRouteThreads) {
-      int s = 0;
-#pragma unroll
-      for (int w = 0; w < kRouteWaves; ++w) {
-        s += wcnt[w][ee];
-        wcnt[w][ee] = 0;
-      }
-      base[ee] += s;
-    }
-    __syncthreads();
+  if (valid) {
+    int pos = off[e] + pre[e] + before;
+    for (int w = 0; w < wave; ++w) pos += wcnt[w][e];
+    row_token[pos] = (int32_t)(i / k);
+    pair_row[i] = pos;
+  } else if (i < P) {
+    pair_row[i] = -1;
   }
-  for (int64_t p = routed + tid; p < P; p += kRouteThreads) row_token[p] = 0;
+  const int routed = off[E - 1] + tot[E - 1];
+  for (int64_t p = routed + c0 + tid; p < P; p += (int64_t)gridDim.x * kRouteThreads)
+    row_token[p] = 0;
 }
 
-// rows[p] = src[row_token[p]] (H bytes per row) and their scales; 16-byte
-// pieces when H % 16 == 0 and the buffers allow it. A token outside [0, T)
-// gives a zero row with scale 0.
+// rows[p] = src[row_token[p]] (H bytes per row) and their scales; a token
+// outside [0, T) gives a zero row with scale 0. kGatherRows rows per
+// workgroup, every thread loading its piece of each row before storing any,
+// 16-byte pieces when H % 16 == 0 and the buffers allow it.
+constexpr int kGatherRows = 4;
+
 __global__ __launch_bounds__(256) void gather_rows_kernel(const int8_t* __restrict__ q,
                                                           const float* __restrict__ scale,
                                                           const int32_t* __restrict__ row_token,
                                                           int64_t T, int64_t R, int64_t H, bool vec,
                                                           int8_t* __restrict__ q_rows,
                                                           float* __restrict__ s_rows) {
-  const int64_t per = vec ? H / 16 : H;
-  const int64_t total = R * per;
-  const int64_t stride = (int64_t)gridDim.x * 256;
-  for (int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x; g < total; g += stride) {
-    const int64_t p = g / per, c = g % per;
-    const int64_t t = row_token[p];
-    const bool in = t >= 0 && t < T;
-    if (vec) {
-      reinterpret_cast<uint4*>(q_rows + p * H)[c] =
-          in ? reinterpret_cast<const uint4*>(q + t * H)[c] : uint4{0u, 0u, 0u, 0u};
-    } else {
-      q_rows[p * H + c] = in ? q[t * H + c] : (int8_t)0;
+  const int64_t p0 = (int64_t)blockIdx.x * kGatherRows;
+  int64_t t[kGatherRows];
+  bool in[kGatherRows];
+#pragma unroll
+  for (int r = 0; r < kGatherRows; ++r) {
+    const bool live = p0 + r < R;
+    t[r] = live ? row_token[p0 + r] : 0;
+    in[r] = live && t[r] >= 0 && t[r] < T;
+    if (live && threadIdx.x == 0) s_rows[p0 + r] = in[r] ? scale[t[r]] : 0.f;
+  }
+  if (vec) {
+    const int64_t per = H / 16;
+    for (int64_t c = threadIdx.x; c < per; c += 256) {
+      uint4 v[kGatherRows];
+#pragma unroll
+      for (int r = 0; r < kGatherRows; ++r)
+        v[r] = in[r] ? reinterpret_cast<const uint4*>(q + t[r] * H)[c] : uint4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int r = 0; r < kGatherRows; ++r)
+        if (p0 + r < R) reinterpret_cast<uint4*>(q_rows + (p0 + r) * H)[c] = v[r];
     }
-    if (c == 0) s_rows[p] = in ? scale[t] : 0.f;
+  } else {
+    for (int64_t c = threadIdx.x; c < H; c += 256) {
+#pragma unroll
+      for (int r = 0; r < kGatherRows; ++r)
+        if (p0 + r < R) q_rows[(p0 + r) * H + c] = in[r] ? q[t[r] * H + c] : (int8_t)0;
+    }
   }
 }
 
-// One 256-thread workgroup per token, 8 BF16 values per thread and step. Pair
-// rows outside [0, R) contribute nothing.
+// One 256-thread workgroup per token, 8 BF16 values per thread and step. The
+// rows of up to kCombineSlots slots are loaded before the sum, which then
+// runs in slot order; pair rows outside [0, R) contribute nothing.
+constexpr int kCombineSlots = 8;
+
+__device__ __forceinline__ void combine_add(float (&acc)[8], float w, const uint4& v) {
+  const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    const float a = w * bf16_to_f32(u[h] & 0xFFFFu);
+    const float b = w * bf16_to_f32(u[h] >> 16);
+    acc[2 * h] = acc[2 * h] + a;
+    acc[2 * h + 1] = acc[2 * h + 1] + b;
+  }
+}
+
 __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ y,
                                                       const int32_t* __restrict__ pair_row,
                                                       const float* __restrict__ wts, int64_t T,
@@ -142,19 +193,21 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
   if (vec) {
     for (int64_t c = threadIdx.x; c < H / 8; c += 256) {
       float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-      for (int j = 0; j < k; ++j) {
-        const int32_t p = pair_row[t * k + j];
-        if (p < 0 || p >= R) continue;
-        const float w = wts[t * k + j];
-        const uint4 v = reinterpret_cast<const uint4*>(y + (int64_t)p * H)[c];
-        const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+      for (int j0 = 0; j0 < k; j0 += kCombineSlots) {
+        uint4 v[kCombineSlots];
+        float w[kCombineSlots];
+        bool use[kCombineSlots];
 #pragma unroll
-        for (int h = 0; h < 4; ++h) {
-          const float a = w * bf16_to_f32(u[h] & 0xFFFFu);
-          const float b = w * bf16_to_f32(u[h] >> 16);
-          acc[2 * h] = acc[2 * h] + a;
-          acc[2 * h + 1] = acc[2 * h + 1] + b;
+        for (int j = 0; j < kCombineSlots; ++j) {
+          const int32_t p = j0 + j < k ? pair_row[t * k + j0 + j] : -1;
+          use[j] = p >= 0 && p < R;
+          w[j] = use[j] ? wts[t * k + j0 + j] : 0.f;
+          v[j] = use[j] ? reinterpret_cast<const uint4*>(y + (int64_t)p * H)[c]
+                        : uint4{0u, 0u, 0u, 0u};
         }
+#pragma unroll
+        for (int j = 0; j < kCombineSlots; ++j)
+          if (use[j]) combine_add(acc, w[j], v[j]);
       }
       uint4 o;
       o.x = f32_to_bf16(acc[0]) | (f32_to_bf16(acc[1]) << 16);
@@ -181,9 +234,11 @@ static inline bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & 
 
 hipError_t launch_route(const int32_t* ids, int64_t T, int64_t k, int64_t E, int64_t* group_list,
                         int32_t* row_token, int32_t* pair_row, hipStream_t stream) {
-  // T == 0 still runs: it writes the zero counts
-  hipLaunchKernelGGL(route_kernel, dim3(1), dim3(kRouteThreads), 0, stream, ids, T * k, (int)k,
-                     (int)E, group_list, row_token, pair_row);
+  // T == 0 still runs one workgroup: it writes the zero counts
+  const int64_t P = T * k;
+  const int64_t grid = std::max<int64_t>(1, (P + kRouteThreads - 1) / kRouteThreads);
+  hipLaunchKernelGGL(route_kernel, dim3((unsigned)grid), dim3(kRouteThreads), 0, stream, ids, P,
+                     (int)k, (int)E, group_list, row_token, pair_row);
   return hipGetLastError();
 }
 
@@ -192,8 +247,7 @@ hipError_t launch_gather_rows(const int8_t* q, const float* scale, const int32_t
                               hipStream_t stream) {
   if (R == 0) return hipSuccess;
   const bool vec = H % 16 == 0 && aligned(q, 16) && aligned(q_rows, 16);
-  const int64_t total = R * (vec ? H / 16 : H);
-  const int64_t grid = std::min<int64_t>((total + 255) / 256, 256 * 32);
+  const int64_t grid = (R + kGatherRows - 1) / kGatherRows;
   hipLaunchKernelGGL(gather_rows_kernel, dim3((unsigned)grid), dim3(256), 0, stream, q, scale,
                      row_token, T, R, H, vec, q_rows, s_rows);
   return hipGetLastError();
