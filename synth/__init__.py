@@ -29,7 +29,7 @@ import torch
 
 # stream tags
 (_T_X, _T_W, _T_WS, _T_B, _T_LOGITS, _T_EBIAS, _T_W13, _T_W2, _T_W13S, _T_W2S, _T_MXW,
- _T_MXS) = range(12)
+ _T_MXS, _T_MXW13, _T_MXS13, _T_MXW2, _T_MXS2) = range(16)
 
 
 def rng_for(seed: int, tag: int, index: int = 0) -> np.random.Generator:
@@ -229,3 +229,52 @@ def mx_block_fp8(M: int = 2048, N: int = 5120, K: int = 17408, bn: int = 128, bk
     w = e4m3_bits(rng_for(seed, _T_MXW).standard_normal((N, K), dtype=np.float32))
     s = rng_for(seed, _T_MXS).uniform(1e-3, 1e-2, size=(-(-N // bn), -(-K // bk))).astype(np.float32)
     return MX(activations(M, K, 0.0, seed, index=5), w, s, bn, bk)
+
+
+# ---------------------------------------------------------------------------
+# MXFP8 MoE inputs: block-FP8 expert stacks (E4M3 = RNE(N(0,1)), fp32
+# weight_scale_inv per bn x bk tile U[1e-3, 1e-2]) on the MoE workload's shapes
+# and routing
+# ---------------------------------------------------------------------------
+
+@dataclass
+class MxMoE:
+    T: int
+    H: int
+    I: int
+    E: int
+    top_k: int
+    seed: int
+    bn: int
+    bk: int
+    x_tokens: np.ndarray      # BF16 bits [T, H]
+    row_token: np.ndarray     # [R]
+    group_list: np.ndarray    # int64 [E]
+
+    @property
+    def R(self):
+        return int(self.row_token.shape[0])
+
+    def x_rows(self) -> np.ndarray:
+        return self.x_tokens[self.row_token]
+
+    def _block_fp8(self, N, K, tw, ts, e):
+        w = e4m3_bits(rng_for(self.seed, tw, e).standard_normal((N, K), dtype=np.float32))
+        s = rng_for(self.seed, ts, e).uniform(
+            1e-3, 1e-2, size=(-(-N // self.bn), -(-K // self.bk))).astype(np.float32)
+        return w, s
+
+    def w13(self, e: int):
+        """(E4M3 codes [2I, H], weight_scale_inv) of expert e."""
+        return self._block_fp8(2 * self.I, self.H, _T_MXW13, _T_MXS13, e)
+
+    def w2(self, e: int):
+        """(E4M3 codes [H, I], weight_scale_inv) of expert e."""
+        return self._block_fp8(self.H, self.I, _T_MXW2, _T_MXS2, e)
+
+
+def mx_moe(T: int = 2048, H: int = 4096, I: int = 2048, E: int = 256, top_k: int = 8,
+           seed: int = 0, bn: int = 128, bk: int = 128, ebias_sigma: float = 1.5) -> MxMoE:
+    x = activations(T, H, 0.0, seed)
+    row_token, _, group_list = route_topk(T, E, top_k, seed, ebias_sigma)
+    return MxMoE(T, H, I, E, top_k, seed, bn, bk, x, row_token, group_list)
