@@ -57,7 +57,7 @@ def _args():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode",
                     choices=["decode", "prefill", "moe", "moe_layer", "tiny", "copy", "mx",
-                             "static"])
+                             "mx_moe", "static"])
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="approximate budget of the oracle timing on the host")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -476,6 +476,134 @@ class MoeLayerWorkload(MoeWorkload):
                            ", scaled to all rows")
 
 
+class MxMoeWorkload(Workload):
+    """The MoE workload with MXFP8 experts: block-FP8 source weights prepared
+    one expert at a time (resolve -> MX requant over the source bytes ->
+    kernel layout), then the MX chain on the expert-grouped rows."""
+
+    def __init__(self, w, torch):
+        super().__init__(w, torch)
+        import numpy as np
+
+        import synth
+        self.name = "mx_moe"
+        m = synth.mx_moe(seed=0)
+        self.m = m
+        E, H, I = m.E, m.H, m.I
+        dev = "cuda"
+        s13 = w.mx_moe_packed_bytes(1, 2 * I, H)
+        s2 = w.mx_moe_packed_bytes(1, H, I)
+        self.w13p = torch.empty((E * s13,), dtype=torch.uint8, device=dev)
+        self.w2p = torch.empty((E * s2,), dtype=torch.uint8, device=dev)
+        st = torch.empty((w.mx_moe_staging_bytes(2 * I, H),), dtype=torch.uint8, device=dev)
+        prep_ms = 0.0
+        for e in range(E):
+            (wa, sa), (wb, sb) = m.w13(e), m.w2(e)
+            a_d, sa_d = torch.from_numpy(wa[None]).to(dev), torch.from_numpy(sa[None]).to(dev)
+            b_d, sb_d = torch.from_numpy(wb[None]).to(dev), torch.from_numpy(sb[None]).to(dev)
+            torch.cuda.synchronize()
+            a, b = _ev(torch), _ev(torch)
+            a.record()
+            w.mx_moe_prepare(a_d, sa_d, m.bn, m.bk, packed=self.w13p[e * s13:(e + 1) * s13], staging=st)
+            w.mx_moe_prepare(b_d, sb_d, m.bn, m.bk, packed=self.w2p[e * s2:(e + 1) * s2], staging=st)
+            b.record()
+            torch.cuda.synchronize()
+            prep_ms += a.elapsed_time(b)
+            if (e + 1) % 32 == 0:
+                print(f"mx_moe: {e + 1} of {E} experts prepared", file=sys.stderr, flush=True)
+        self.prep_ms = prep_ms
+        del st
+        self.gl = torch.from_numpy(m.group_list).to(dev)
+        self.x = torch.from_numpy(m.x_rows().view(np.int16)).to(dev).view(torch.bfloat16)
+        R = m.R
+        self.y = torch.empty((R, H), dtype=torch.bfloat16, device=dev)
+        self.h = torch.empty((R, 2 * I), dtype=torch.bfloat16, device=dev)
+        self.ws = torch.empty((w.mx_moe_workspace_bytes(R, E, H, I),), dtype=torch.uint8, device=dev)
+        self.ws13 = torch.empty((w.mx_grouped_workspace_bytes(R, E, H),), dtype=torch.uint8, device=dev)
+        self.ws2 = torch.empty((w.mx_grouped_workspace_bytes(R, E, I),), dtype=torch.uint8, device=dev)
+        self.unit = "tokens/s"
+        self.bound = "hbm"
+        self.capture([self._step], [(self._w13, 1, "w13"), (self._w2, 1, "w2")])
+
+    def _step(self):
+        self.w.mx_moe_grouped(self.x, self.gl, self.w13p, self.w2p, self.m.I, y=self.y,
+                              workspace=self.ws)
+
+    def _w13(self):
+        self.w.mx_grouped_gemm(self.x, self.gl, self.w13p, 2 * self.m.I, y=self.h,
+                               workspace=self.ws13)
+
+    def _w2(self):
+        self.w.mx_grouped_gemm(self.h, self.gl, self.w2p, self.m.H, act=self.w.ACT_SWIGLU,
+                               y=self.y, workspace=self.ws2)
+
+    def nonempty(self):
+        return int((self.m.group_list > 0).sum())
+
+    def stage_bytes(self, which):
+        """One grouped call: the non-empty experts' MX weights (1 byte per value +
+        1 scale byte per 32), the BF16 input rows (h: gate and up), the MX
+        activation written and read back, the BF16 output."""
+        m = self.m
+        ne = self.nonempty()
+        R, H, I = m.R, m.H, m.I
+        if which == "w13":
+            N, K, kin = 2 * I, H, H
+        else:
+            N, K, kin = H, I, 2 * I
+        wbytes = ne * N * (K + K // 32)
+        act = R * (K + K // 32)
+        return wbytes + 2 * R * kin + 2 * act + 2 * R * N
+
+    def alg_bytes(self):
+        return self.stage_bytes("w13") + self.stage_bytes("w2")
+
+    def value(self, sec_per_step):
+        return self.m.T / sec_per_step
+
+    def dominant(self, per_key_ms):
+        byts = self.alg_bytes()
+        tot = per_key_ms["w13"] + per_key_ms["w2"]
+        ach = byts / (tot * 1e-3) / 1e9
+        return dict(bound="hbm", achieved=ach, peak=PEAK_HBM_GBS, unit="GB/s",
+                    frac=ach / PEAK_HBM_GBS)
+
+    def config(self):
+        m = self.m
+        g = m.group_list
+        return {"workload": "mx_moe", "T": m.T, "top_k": m.top_k, "E": m.E, "H": m.H, "I": m.I,
+                "R": m.R, "nonempty_experts": self.nonempty(), "max_rows_per_expert": int(g.max()),
+                "weights": "block-FP8 E4M3 RNE(N(0,1)), weight_scale_inv per 128x128 U[1e-3,1e-2], "
+                           "prepared one expert at a time",
+                "weight_prep_ms": round(self.prep_ms, 2),
+                "routing": "logits N(0,1) + expert bias N(0,1.5), top-8"}
+
+    def cpu_baseline(self, budget_s):
+        import numpy as np
+
+        import oracle as O
+        m = self.m
+        off = O.group_offsets(m.group_list)
+        xr = m.x_rows()
+        t0 = time.perf_counter()
+        rows = 0
+        e = 0
+        while time.perf_counter() - t0 < budget_s and e < m.E:
+            a, b = int(off[e]), int(off[e + 1])
+            if b > a:
+                (wa, sa), (wb, sb) = m.w13(e), m.w2(e)
+                o13 = O.mx_moe.mx_moe_prepare(wa[None], sa[None], m.bn, m.bk)
+                o2 = O.mx_moe.mx_moe_prepare(wb[None], sb[None], m.bn, m.bk)
+                O.mx_moe.mx_moe_grouped(np.array([b - a], np.int64), xr[a:b], *o13, *o2)
+                rows += b - a
+            e += 1
+        dt = time.perf_counter() - t0
+        return dict(value=rows / m.top_k / dt, unit="tokens/s",
+                    sample=f"oracle MX chain over experts 0..{e - 1} ({rows} of {m.R} rows, "
+                           f"weights drawn and prepared per expert inside the timing), "
+                           f"tokens = rows / top_k")
+
+
 class MxWorkload(Workload):
     def __init__(self, w, torch):
         super().__init__(w, torch)
@@ -766,6 +894,8 @@ def main():
         wl = StaticWorkload(w, torch)
     elif args.workload == "moe_layer":
         wl = MoeLayerWorkload(w, torch)
+    elif args.workload == "mx_moe":
+        wl = MxMoeWorkload(w, torch)
     else:
         wl = MoeWorkload(w, torch)
 
@@ -815,7 +945,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8-e4m3 (MX)" if wl.name == "mx" else "int8",
+        "dtype": "fp8-e4m3 (MX)" if wl.name in ("mx", "mx_moe") else "int8",
         "data": "synthetic (seeded numpy; see synth/)",
         "config": wl.config(),
         "roofline": {k: (round(v, 4) if isinstance(v, float) else v) for k, v in roof.items()},

@@ -53,6 +53,13 @@ typedef enum {
  * layout written by w8a8_dynamic_quant_packed instead of row-major. */
 #define W8A8_A_PACKED 4
 
+/* Input of w8a8_mx_grouped_gemm: the rows themselves, or the SwiGLU of
+ * [gate | up] rows rounded to BF16. */
+typedef enum {
+  W8A8_ACT_NONE = 0,
+  W8A8_ACT_SWIGLU = 1
+} w8a8_act;
+
 /* Largest K (reduction length) accepted: K * 127 * 127 stays below 2^31. */
 #define W8A8_MAX_K 133144
 
@@ -312,6 +319,62 @@ int w8a8_mx_linear(const void* x, const uint8_t* x_e8m0, int64_t M, int64_t K,
  */
 int w8a8_mx_gemm(const uint8_t* a_e4m3, const uint8_t* a_scale_kb, int64_t M, int64_t K,
                  const void* w_packed, int64_t N, uint16_t* y, void* stream);
+
+/*
+ * MXFP8 MoE path.  [MXFP8] Deep Dive 6: the fused-MoE weights take the dense
+ * contract (resolve -> MX re-quantization -> kernel layout) one expert at a
+ * time, the expert's MXFP8 bytes written back over its FP8 source bytes and
+ * its E8M0 scales into a separate buffer, so that the staging memory is one
+ * dense expert; at run time the expert chain gets MX-quantized activations
+ * (Deep Dive 5) and the routing metadata (group_list). The chain itself is
+ * the INT8 path's ([DSV4] §三): W13 -> SwiGLU -> W2, with the SwiGLU output
+ * rounded to BF16 and MX-quantized like any activation (a reading).
+ *
+ * w8a8_mx_moe_prepare (load time): w_e4m3 device uint8 [E, N, K], block-FP8
+ *   E4M3 codes on entry, overwritten expert by expert with the MX payload
+ *   (8-byte aligned, N * K % 8 == 0); scale_inv float [E, ceil(N/BN),
+ *   ceil(K/BK)]; w_e8m0 uint8 [E, N, K/32] written; packed (optional, may be
+ *   NULL) receives every expert's kernel layout at e * w8a8_mx_packed_bytes(N,
+ *   K) (w8a8_mx_moe_packed_bytes(E, N, K) bytes, 256-byte aligned); staging
+ *   at least w8a8_mx_moe_staging_bytes(N, K) bytes (one BF16 expert, 16-byte
+ *   aligned). Per expert: w8a8_mx_resolve_block_fp8, w8a8_mx_quant (scale_alg),
+ *   w8a8_mx_prepack_weight.
+ * w8a8_mx_swiglu_quant: h BF16 [R, 2I] (gate | up, 16-byte aligned) -> e4m3
+ *   [R, I] and e8m0 [R, I/32]: a = BF16(silu(gate) * up) by the fixed fp32
+ *   sequence of w8a8_swiglu_quant, rounded once to BF16, then the MX quant of a.
+ * w8a8_mx_grouped_gemm: rows grouped by expert as for w8a8_grouped_gemm
+ *   (group_list int64 [E], counts cut to R rows in total); x BF16 [R, K]
+ *   (act W8A8_ACT_NONE) or [R, 2K] = [gate | up] (act W8A8_ACT_SWIGLU, the
+ *   input is then the BF16 SwiGLU above), 16-byte aligned; each row is
+ *   MX-quantized at run time (scale_alg), multiplied with its expert's
+ *   prepared weight (w_packed: E x w8a8_mx_packed_bytes(N, K), from
+ *   w8a8_mx_moe_prepare) by the block-scaled MFMA with fp32 accumulation ->
+ *   y BF16 [R, N]. workspace: w8a8_mx_grouped_workspace_bytes(R, E, K), 256-byte
+ *   aligned (tile schedule and the MX activation, every expert padded to 16
+ *   rows). K % 32 == 0, E <= 1024.
+ * w8a8_mx_moe_grouped: the chain on expert-grouped BF16 rows x [R, H] ->
+ *   y BF16 [R, H]: w8a8_mx_grouped_gemm with w13 (N = 2I, K = H), then with
+ *   w2 (N = H, K = I) on the SwiGLU of its output. workspace:
+ *   w8a8_mx_moe_workspace_bytes(R, E, H, I). H % 32 == 0 and I % 32 == 0.
+ * Results of the matmuls are the fp32 sums of exactly dequantized products,
+ * rounded to BF16 (not bit-exact against a float64 sum; see w8a8_mx_linear).
+ */
+int64_t w8a8_mx_moe_staging_bytes(int64_t N, int64_t K);
+int64_t w8a8_mx_moe_packed_bytes(int64_t E, int64_t N, int64_t K);
+int w8a8_mx_moe_prepare(uint8_t* w_e4m3, const float* scale_inv, int64_t E, int64_t N, int64_t K,
+                        int64_t BN, int64_t BK, int scale_alg, uint8_t* w_e8m0, void* packed,
+                        void* staging, int64_t staging_bytes, void* stream);
+int w8a8_mx_swiglu_quant(const uint16_t* h, int64_t R, int64_t I, int scale_alg, uint8_t* e4m3,
+                         uint8_t* e8m0, void* stream);
+int64_t w8a8_mx_grouped_workspace_bytes(int64_t R, int64_t E, int64_t K);
+int w8a8_mx_grouped_gemm(const uint16_t* x, const int64_t* group_list, int64_t R, int64_t E,
+                         int64_t N, int64_t K, int act, const void* w_packed, int scale_alg,
+                         uint16_t* y, void* workspace, int64_t ws_bytes, void* stream);
+int64_t w8a8_mx_moe_workspace_bytes(int64_t R, int64_t E, int64_t H, int64_t I);
+int w8a8_mx_moe_grouped(const uint16_t* x_rows, const int64_t* group_list, int64_t R, int64_t E,
+                        int64_t H, int64_t I, const void* w13_packed, const void* w2_packed,
+                        int scale_alg, uint16_t* y, void* workspace, int64_t ws_bytes,
+                        void* stream);
 
 /*
  * Static W8A8  [DSV4, the static W8A8 comparison at the end of the page:

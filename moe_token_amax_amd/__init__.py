@@ -46,6 +46,16 @@ __all__ = [
     "mx_linear_workspace_bytes",
     "mx_linear",
     "mx_gemm",
+    "ACT_NONE",
+    "ACT_SWIGLU",
+    "mx_moe_staging_bytes",
+    "mx_moe_packed_bytes",
+    "mx_moe_prepare",
+    "mx_swiglu_quant",
+    "mx_grouped_workspace_bytes",
+    "mx_grouped_gemm",
+    "mx_moe_workspace_bytes",
+    "mx_moe_grouped",
     "mx_workspace_operands",
     "static_quant",
     "static_quant_packed",
@@ -110,6 +120,19 @@ def _load():
         "w8a8_mx_linear": (ctypes.c_int, [_c_p, _c_p, _c_i64, _c_i64, _c_p, _c_i64, _c_p,
                                           ctypes.c_int, _c_p, _c_i64, _c_p]),
         "w8a8_mx_gemm": (ctypes.c_int, [_c_p, _c_p, _c_i64, _c_i64, _c_p, _c_i64, _c_p, _c_p]),
+        "w8a8_mx_moe_staging_bytes": (_c_i64, [_c_i64, _c_i64]),
+        "w8a8_mx_moe_packed_bytes": (_c_i64, [_c_i64, _c_i64, _c_i64]),
+        "w8a8_mx_moe_prepare": (ctypes.c_int, [_c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64,
+                                               ctypes.c_int, _c_p, _c_p, _c_p, _c_i64, _c_p]),
+        "w8a8_mx_swiglu_quant": (ctypes.c_int, [_c_p, _c_i64, _c_i64, ctypes.c_int, _c_p, _c_p,
+                                                _c_p]),
+        "w8a8_mx_grouped_workspace_bytes": (_c_i64, [_c_i64, _c_i64, _c_i64]),
+        "w8a8_mx_grouped_gemm": (ctypes.c_int, [_c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i64,
+                                                ctypes.c_int, _c_p, ctypes.c_int, _c_p, _c_p,
+                                                _c_i64, _c_p]),
+        "w8a8_mx_moe_workspace_bytes": (_c_i64, [_c_i64, _c_i64, _c_i64, _c_i64]),
+        "w8a8_mx_moe_grouped": (ctypes.c_int, [_c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i64, _c_p,
+                                               _c_p, ctypes.c_int, _c_p, _c_p, _c_i64, _c_p]),
         "w8a8_static_quant": (ctypes.c_int, [_c_p, _c_i64, _c_i64, ctypes.c_float, ctypes.c_float,
                                              _c_p, _c_p]),
         "w8a8_static_quant_packed": (ctypes.c_int, [_c_p, _c_i64, _c_i64, ctypes.c_float,
@@ -578,6 +601,108 @@ def mx_linear(x: torch.Tensor, w_packed: torch.Tensor, N: int, x_e8m0: torch.Ten
     ws, ws_n = _workspace(mx_linear_workspace_bytes(M, K), x.device, workspace)
     _check(lib.w8a8_mx_linear(_ptr(x), _ptr(x_e8m0), M, K, _ptr(w_packed), N, _ptr(y), scale_alg,
                               _ptr(ws), ws_n, _stream()))
+    return y
+
+
+# ---------------------------------------------------------------------------
+# MXFP8 MoE path
+# ---------------------------------------------------------------------------
+ACT_NONE, ACT_SWIGLU = 0, 1
+
+
+def mx_moe_staging_bytes(N: int, K: int) -> int:
+    return int(lib.w8a8_mx_moe_staging_bytes(N, K))
+
+
+def mx_moe_packed_bytes(E: int, N: int, K: int) -> int:
+    return int(lib.w8a8_mx_moe_packed_bytes(E, N, K))
+
+
+def mx_moe_prepare(w_e4m3: torch.Tensor, scale_inv: torch.Tensor, bn: int, bk: int,
+                   scale_alg: int = 0, pack: bool = True, w_e8m0: torch.Tensor | None = None,
+                   packed: torch.Tensor | None = None, staging: torch.Tensor | None = None):
+    """Block-FP8 expert stack -> MXFP8, one expert at a time. ``w_e4m3`` (uint8
+    [E, N, K]) is overwritten with the MX payload. Returns (w_e8m0 [E, N, K/32],
+    packed stack or None)."""
+    _need(w_e4m3, torch.uint8, "w_e4m3", 3)
+    _need(scale_inv, torch.float32, "scale_inv", 3)
+    E, N, K = w_e4m3.shape
+    dev = w_e4m3.device
+    if tuple(scale_inv.shape) != (E, -(-N // bn), -(-K // bk)):
+        raise ValueError("scale_inv must be [E, ceil(N/bn), ceil(K/bk)]")
+    if w_e8m0 is None:
+        w_e8m0 = torch.empty((E, N, K // 32), dtype=torch.uint8, device=dev)
+    _need(w_e8m0, torch.uint8, "w_e8m0", 3)
+    if pack and packed is None:
+        packed = torch.empty((mx_moe_packed_bytes(E, N, K),), dtype=torch.uint8, device=dev)
+    if packed is not None:
+        _need(packed, torch.uint8, "packed", 1)
+    st, st_n = _workspace(mx_moe_staging_bytes(N, K), dev, staging)
+    _check(lib.w8a8_mx_moe_prepare(_ptr(w_e4m3), _ptr(scale_inv), E, N, K, bn, bk, scale_alg,
+                                   _ptr(w_e8m0), _ptr(packed), _ptr(st), st_n, _stream()))
+    return w_e8m0, packed
+
+
+def mx_swiglu_quant(h: torch.Tensor, scale_alg: int = 0):
+    """BF16 h [R, 2I] (gate | up) -> (E4M3 [R, I], E8M0 [R, I/32]) of BF16(SwiGLU)."""
+    _need(h, torch.bfloat16, "h", 2)
+    R, I2 = h.shape
+    I = I2 // 2
+    p = torch.empty((R, I), dtype=torch.uint8, device=h.device)
+    sc = torch.empty((R, max(I // 32, 1)), dtype=torch.uint8, device=h.device)
+    _check(lib.w8a8_mx_swiglu_quant(_ptr(h), R, I, scale_alg, _ptr(p), _ptr(sc), _stream()))
+    return p, sc
+
+
+def mx_grouped_workspace_bytes(R: int, E: int, K: int) -> int:
+    return int(lib.w8a8_mx_grouped_workspace_bytes(R, E, K))
+
+
+def mx_grouped_gemm(x: torch.Tensor, group_list: torch.Tensor, w_packed: torch.Tensor, N: int,
+                    act: int = ACT_NONE, scale_alg: int = 0, y: torch.Tensor | None = None,
+                    workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """Expert-grouped BF16 rows (or [gate | up] rows with act=ACT_SWIGLU) times each
+    expert's prepared MX weight -> BF16 [R, N]."""
+    _need(x, torch.bfloat16, "x", 2)
+    _need(group_list, torch.int64, "group_list", 1)
+    _need(w_packed, torch.uint8, "w_packed", 1)
+    R, Kx = x.shape
+    K = Kx // 2 if act == ACT_SWIGLU else Kx
+    E = group_list.shape[0]
+    if w_packed.numel() < mx_moe_packed_bytes(E, N, K):
+        raise ValueError("w_packed too small for [E, N, K]")
+    if y is None:
+        y = torch.empty((R, N), dtype=torch.bfloat16, device=x.device)
+    _need(y, torch.bfloat16, "y", 2)
+    ws, ws_n = _workspace(mx_grouped_workspace_bytes(R, E, K), x.device, workspace)
+    _check(lib.w8a8_mx_grouped_gemm(_ptr(x), _ptr(group_list), R, E, N, K, act, _ptr(w_packed),
+                                    scale_alg, _ptr(y), _ptr(ws), ws_n, _stream()))
+    return y
+
+
+def mx_moe_workspace_bytes(R: int, E: int, H: int, I: int) -> int:
+    return int(lib.w8a8_mx_moe_workspace_bytes(R, E, H, I))
+
+
+def mx_moe_grouped(x_rows: torch.Tensor, group_list: torch.Tensor, w13_packed: torch.Tensor,
+                   w2_packed: torch.Tensor, I: int, scale_alg: int = 0,
+                   y: torch.Tensor | None = None, workspace: torch.Tensor | None = None):
+    """MXFP8 expert chain on expert-grouped BF16 rows [R, H] -> BF16 [R, H]."""
+    _need(x_rows, torch.bfloat16, "x_rows", 2)
+    _need(group_list, torch.int64, "group_list", 1)
+    _need(w13_packed, torch.uint8, "w13_packed", 1)
+    _need(w2_packed, torch.uint8, "w2_packed", 1)
+    R, H = x_rows.shape
+    E = group_list.shape[0]
+    if w13_packed.numel() < mx_moe_packed_bytes(E, 2 * I, H) or \
+            w2_packed.numel() < mx_moe_packed_bytes(E, H, I):
+        raise ValueError("packed expert weights too small")
+    if y is None:
+        y = torch.empty((R, H), dtype=torch.bfloat16, device=x_rows.device)
+    _need(y, torch.bfloat16, "y", 2)
+    ws, ws_n = _workspace(mx_moe_workspace_bytes(R, E, H, I), x_rows.device, workspace)
+    _check(lib.w8a8_mx_moe_grouped(_ptr(x_rows), _ptr(group_list), R, E, H, I, _ptr(w13_packed),
+                                   _ptr(w2_packed), scale_alg, _ptr(y), _ptr(ws), ws_n, _stream()))
     return y
 
 

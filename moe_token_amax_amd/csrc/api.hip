@@ -532,6 +532,196 @@ int w8a8_mx_gemm(const uint8_t* a_e4m3, const uint8_t* a_scale_kb, int64_t M, in
                   "mx_gemm");
 }
 
+// ---------------------------------------------------------------------------
+// MXFP8 MoE: one-expert-at-a-time weight preparation and the grouped chain
+// ---------------------------------------------------------------------------
+int64_t w8a8_mx_moe_staging_bytes(int64_t N, int64_t K) {
+  if (N < 1 || K < 1) return 0;
+  return N * K * 2;
+}
+
+int w8a8_mx_moe_prepare(uint8_t* w_e4m3, const float* scale_inv, int64_t E, int64_t N, int64_t K,
+                        int64_t BN, int64_t BK, int scale_alg, uint8_t* w_e8m0, void* packed,
+                        void* staging, int64_t staging_bytes, void* stream) {
+  int st = check_mx_k("mx_moe_prepare", K);
+  if (st) return st;
+  if (E < 1 || N < 1 || BN < 1 || BK < 1 || N >= kMaxDim || E >= kMaxDim)
+    return fail(W8A8_ERR_SHAPE, "mx_moe_prepare: need E, N, BN, BK >= 1");
+  if (scale_alg != 0 && scale_alg != 1)
+    return fail(W8A8_ERR_UNSUPPORTED, "mx_moe_prepare: scale_alg must be 0 or 1");
+  if (!w_e4m3 || !scale_inv || !w_e8m0 || !staging)
+    return fail(W8A8_ERR_NULL, "mx_moe_prepare: null pointer");
+  if (!aligned(w_e4m3, 8) || (N * K) % 8 || !aligned(scale_inv, 4) || !aligned(staging, 16) ||
+      (packed && !aligned(packed, 256)))
+    return fail(W8A8_ERR_ALIGN, "mx_moe_prepare: misaligned buffer");
+  if (staging_bytes < w8a8_mx_moe_staging_bytes(N, K))
+    return fail(W8A8_ERR_WORKSPACE, "mx_moe_prepare: needs %lld staging bytes, got %lld",
+                (long long)w8a8_mx_moe_staging_bytes(N, K), (long long)staging_bytes);
+  hipStream_t s = (hipStream_t)stream;
+  uint16_t* bf16 = reinterpret_cast<uint16_t*>(staging);
+  const int64_t sn = (N + BN - 1) / BN, sk = (K + BK - 1) / BK;
+  const int64_t stride = w8a8_mx_packed_bytes(N, K);
+  for (int64_t e = 0; e < E; ++e) {
+    // resolve one expert into the staging buffer, then write its MX payload
+    // over its own FP8 source bytes and its scales into the scale buffer
+    uint8_t* we = w_e4m3 + e * N * K;
+    uint8_t* se = w_e8m0 + e * N * (K / 32);
+    hipError_t err = w8a8::launch_mx_resolve(we, scale_inv + e * sn * sk, N, K, BN, BK, bf16, s);
+    if (err != hipSuccess) return launched(err, "mx_moe_prepare: resolve");
+    err = w8a8::launch_mx_quant(bf16, N, K, scale_alg, we, false, se, nullptr, 0, s);
+    if (err != hipSuccess) return launched(err, "mx_moe_prepare: quant");
+    if (packed) {
+      uint8_t* pe = reinterpret_cast<uint8_t*>(packed) + e * stride;
+      err = w8a8::launch_prepack(reinterpret_cast<const int8_t*>(we), 1, N, K, pe, s);
+      if (err != hipSuccess) return launched(err, "mx_moe_prepare: prepack");
+      err = w8a8::launch_mx_scale_relayout(se, N, K, w8a8::round_up(N, 16), pe + mx_payload_bytes(N, K), s);
+      if (err != hipSuccess) return launched(err, "mx_moe_prepare: scales");
+    }
+  }
+  return ok();
+}
+
+int w8a8_mx_swiglu_quant(const uint16_t* h, int64_t R, int64_t I, int scale_alg, uint8_t* e4m3,
+                         uint8_t* e8m0, void* stream) {
+  int st = check_mx_k("mx_swiglu_quant", I);
+  if (st) return st;
+  if (R < 0 || R >= kMaxDim) return fail(W8A8_ERR_SHAPE, "mx_swiglu_quant: bad R");
+  if (scale_alg != 0 && scale_alg != 1)
+    return fail(W8A8_ERR_UNSUPPORTED, "mx_swiglu_quant: scale_alg must be 0 or 1");
+  if (R == 0) return ok();
+  if (!h || !e4m3 || !e8m0) return fail(W8A8_ERR_NULL, "mx_swiglu_quant: null pointer");
+  if (!aligned(h, 16) || !aligned(e4m3, 8))
+    return fail(W8A8_ERR_ALIGN, "mx_swiglu_quant: h needs 16-byte, e4m3 8-byte alignment");
+  return launched(w8a8::launch_mx_swiglu_quant(h, R, I, scale_alg, e4m3, e8m0, (hipStream_t)stream),
+                  "mx_swiglu_quant");
+}
+
+namespace {
+
+struct MxGroupWs {
+  int64_t tiles, count, payload, scales, total;
+};
+
+MxGroupWs mx_group_layout(int64_t R, int64_t E, int64_t K) {
+  const int64_t Rs = w8a8::mx_padded_rows(R, E);
+  MxGroupWs w{};
+  int64_t o = 0;
+  w.tiles = o;   o += align256(w8a8::mx_max_tiles(R, E) * 16);   // int4 tile records
+  w.count = o;   o += 256;                                        // int: records written
+  w.payload = o; o += align256(Rs * w8a8::round_up(K, 64));       // P16x64 blocks, padded rows
+  w.scales = o;  o += align256(w8a8::mx_scale_kb_bytes(Rs, K));   // [KB][Rs][2]
+  w.total = o;
+  return w;
+}
+
+int check_mx_grouped(const char* who, int64_t R, int64_t E, int64_t N, int64_t K, int scale_alg) {
+  int st = check_mx_k(who, K);
+  if (st) return st;
+  if (R < 0 || E < 1 || N < 1 || R >= kMaxDim / 2 || N >= kMaxDim)
+    return fail(W8A8_ERR_SHAPE, "%s: need R >= 0, E >= 1, N >= 1", who);
+  if (E > kMaxExperts) return fail(W8A8_ERR_UNSUPPORTED, "%s: at most %lld experts", who, (long long)kMaxExperts);
+  if (scale_alg != 0 && scale_alg != 1) return fail(W8A8_ERR_UNSUPPORTED, "%s: scale_alg must be 0 or 1", who);
+  return W8A8_OK;
+}
+
+}  // namespace
+
+int64_t w8a8_mx_moe_packed_bytes(int64_t E, int64_t N, int64_t K) {
+  if (E < 1) return 0;
+  return E * w8a8_mx_packed_bytes(N, K);
+}
+
+int64_t w8a8_mx_grouped_workspace_bytes(int64_t R, int64_t E, int64_t K) {
+  if (R < 1 || E < 1 || K < 1) return 0;
+  return mx_group_layout(R, E, K).total;
+}
+
+int w8a8_mx_grouped_gemm(const uint16_t* x, const int64_t* group_list, int64_t R, int64_t E, int64_t N,
+                         int64_t K, int act, const void* w_packed, int scale_alg, uint16_t* y,
+                         void* workspace, int64_t ws_bytes, void* stream) {
+  int st = check_mx_grouped("mx_grouped_gemm", R, E, N, K, scale_alg);
+  if (st) return st;
+  if (act != W8A8_ACT_NONE && act != W8A8_ACT_SWIGLU)
+    return fail(W8A8_ERR_UNSUPPORTED, "mx_grouped_gemm: unknown act %d", act);
+  if (R == 0) return ok();
+  if (!x || !group_list || !w_packed || !y) return fail(W8A8_ERR_NULL, "mx_grouped_gemm: null pointer");
+  if (!aligned(x, 16) || !aligned(group_list, 8) || !aligned(w_packed, 256) || !aligned(y, 2))
+    return fail(W8A8_ERR_ALIGN, "mx_grouped_gemm: misaligned buffer");
+  const MxGroupWs L = mx_group_layout(R, E, K);
+  if (!workspace || ws_bytes < L.total || !aligned(workspace, 256))
+    return fail(W8A8_ERR_WORKSPACE, "mx_grouped_gemm: needs %lld workspace bytes (256-byte aligned), got %lld",
+                (long long)L.total, (long long)ws_bytes);
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = reinterpret_cast<char*>(workspace);
+  int4* tiles = reinterpret_cast<int4*>(ws + L.tiles);
+  int* count = reinterpret_cast<int*>(ws + L.count);
+  uint8_t* pay = reinterpret_cast<uint8_t*>(ws + L.payload);
+  uint8_t* sc = reinterpret_cast<uint8_t*>(ws + L.scales);
+  hipError_t err = w8a8::launch_mx_group_schedule(group_list, E, R, tiles, count, s);
+  if (err != hipSuccess) return launched(err, "mx_grouped_gemm: schedule");
+  const int64_t ldx = act == W8A8_ACT_SWIGLU ? 2 * K : K;
+  err = w8a8::launch_mx_quant_tiles(x, ldx, K, act, tiles, count, R, E, scale_alg, pay, sc, s);
+  if (err != hipSuccess) return launched(err, "mx_grouped_gemm: quant");
+  const uint8_t* wp = reinterpret_cast<const uint8_t*>(w_packed);
+  return launched(w8a8::launch_mx_grouped_gemm(pay, sc, R, E, K, tiles, count, wp,
+                                               w8a8_mx_packed_bytes(N, K), mx_payload_bytes(N, K), N,
+                                               y, s),
+                  "mx_grouped_gemm: gemm");
+}
+
+int64_t w8a8_mx_moe_workspace_bytes(int64_t R, int64_t E, int64_t H, int64_t I) {
+  if (R < 1 || E < 1 || H < 1 || I < 1) return 0;
+  const MxGroupWs a = mx_group_layout(R, E, H), b = mx_group_layout(R, E, I);
+  return std::max(a.total, b.total) + align256(R * 2 * I * 2);
+}
+
+int w8a8_mx_moe_grouped(const uint16_t* x_rows, const int64_t* group_list, int64_t R, int64_t E,
+                        int64_t H, int64_t I, const void* w13_packed, const void* w2_packed,
+                        int scale_alg, uint16_t* y, void* workspace, int64_t ws_bytes, void* stream) {
+  int st = check_mx_grouped("mx_moe_grouped", R, E, 2 * I, H, scale_alg);
+  if (st) return st;
+  st = check_mx_grouped("mx_moe_grouped", R, E, H, I, scale_alg);
+  if (st) return st;
+  if (R == 0) return ok();
+  if (!x_rows || !group_list || !w13_packed || !w2_packed || !y)
+    return fail(W8A8_ERR_NULL, "mx_moe_grouped: null pointer");
+  if (!aligned(x_rows, 16) || !aligned(group_list, 8) || !aligned(w13_packed, 256) ||
+      !aligned(w2_packed, 256) || !aligned(y, 2))
+    return fail(W8A8_ERR_ALIGN, "mx_moe_grouped: misaligned buffer");
+  const int64_t need = w8a8_mx_moe_workspace_bytes(R, E, H, I);
+  if (!workspace || ws_bytes < need || !aligned(workspace, 256))
+    return fail(W8A8_ERR_WORKSPACE, "mx_moe_grouped: needs %lld workspace bytes (256-byte aligned), got %lld",
+                (long long)need, (long long)ws_bytes);
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = reinterpret_cast<char*>(workspace);
+  // the two stages share the schedule and the activation region (W13's MX
+  // input is dead once W13 has run); h [R, 2I] BF16 sits after it
+  const MxGroupWs L = mx_group_layout(R, E, std::max(H, I));
+  int4* tiles = reinterpret_cast<int4*>(ws + L.tiles);
+  int* count = reinterpret_cast<int*>(ws + L.count);
+  uint8_t* pay = reinterpret_cast<uint8_t*>(ws + L.payload);
+  const int64_t Rs = w8a8::mx_padded_rows(R, E);
+  uint16_t* h = reinterpret_cast<uint16_t*>(ws + need - align256(R * 2 * I * 2));
+  const uint8_t* w13 = reinterpret_cast<const uint8_t*>(w13_packed);
+  const uint8_t* w2 = reinterpret_cast<const uint8_t*>(w2_packed);
+  hipError_t err = w8a8::launch_mx_group_schedule(group_list, E, R, tiles, count, s);
+  if (err != hipSuccess) return launched(err, "mx_moe_grouped: schedule");
+  // W13: MX quant of the rows, grouped block-scaled matmul -> h
+  uint8_t* sc1 = pay + align256(Rs * w8a8::round_up(H, 64));
+  err = w8a8::launch_mx_quant_tiles(x_rows, H, H, 0, tiles, count, R, E, scale_alg, pay, sc1, s);
+  if (err != hipSuccess) return launched(err, "mx_moe_grouped: quant");
+  err = w8a8::launch_mx_grouped_gemm(pay, sc1, R, E, H, tiles, count, w13, w8a8_mx_packed_bytes(2 * I, H),
+                                     mx_payload_bytes(2 * I, H), 2 * I, h, s);
+  if (err != hipSuccess) return launched(err, "mx_moe_grouped: W13");
+  // SwiGLU -> BF16 -> MX quant, grouped block-scaled matmul -> y
+  uint8_t* sc2 = pay + align256(Rs * w8a8::round_up(I, 64));
+  err = w8a8::launch_mx_quant_tiles(h, 2 * I, I, 1, tiles, count, R, E, scale_alg, pay, sc2, s);
+  if (err != hipSuccess) return launched(err, "mx_moe_grouped: swiglu quant");
+  return launched(w8a8::launch_mx_grouped_gemm(pay, sc2, R, E, I, tiles, count, w2,
+                                               w8a8_mx_packed_bytes(H, I), mx_payload_bytes(H, I), H, y, s),
+                  "mx_moe_grouped: W2");
+}
+
 }  // extern "C"
 
 // ---------------------------------------------------------------------------

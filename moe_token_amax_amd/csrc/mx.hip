@@ -101,38 +101,61 @@ __global__ __launch_bounds__(256) void mx_resolve_kernel(const uint8_t* __restri
 // ---------------------------------------------------------------------------
 // MX quant: BF16 [M, K] -> E4M3 [M, K] + E8M0. Four consecutive lanes own one
 // 32-group (8 values each); the group amax is two DPP steps inside the quad.
-// Scales go to `scale_rm` ([M, K/32], may be null) and/or `scale_kb`
-// ([ceil(K/64)][Mp][2], may be null; Mp = rows of that layout).
+// ACT 0 quantizes the rows of x (row stride ldx); ACT 1 quantizes the SwiGLU
+// of h = [gate | up] (row stride ldx = 2K): a = BF16(silu(gate) * up), the
+// fixed fp32 sequence, rounded once to BF16 before the MX quant.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void mx_quant_kernel(const uint16_t* __restrict__ x, int64_t M,
-                                                       int64_t K, int scale_alg,
-                                                       uint8_t* __restrict__ payload, int blocked,
-                                                       uint8_t* __restrict__ scale_rm,
-                                                       uint8_t* __restrict__ scale_kb,
-                                                       int64_t Mp) {
-  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t chunks = K / 8;             // K % 32 == 0, so quads never straddle rows
-  const bool live = t < M * chunks;
-  const int64_t tc = live ? t : 0;
-  const int64_t row = tc / chunks, c = tc % chunks;
-  uint4 v = live ? *reinterpret_cast<const uint4*>(x + row * K + c * 8) : uint4{0u, 0u, 0u, 0u};
-  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+
+// 8 BF16 values (as 4 packed pairs) of chunk c of row `row`
+template <int ACT>
+__device__ __forceinline__ void mx_load8(const uint16_t* __restrict__ x, int64_t ldx, int64_t K,
+                                         int64_t row, int64_t c, uint32_t (&w)[4]) {
+  const uint4 v = *reinterpret_cast<const uint4*>(x + row * ldx + c * 8);
+  if (ACT == 0) {
+    w[0] = v.x;
+    w[1] = v.y;
+    w[2] = v.z;
+    w[3] = v.w;
+  } else {
+    const uint4 u = *reinterpret_cast<const uint4*>(x + row * ldx + K + c * 8);
+    const uint32_t g[4] = {v.x, v.y, v.z, v.w}, up[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float a0 = swiglu_fixed(bf16_to_f32(g[j] & 0xFFFFu), bf16_to_f32(up[j] & 0xFFFFu));
+      const float a1 = swiglu_fixed(bf16_to_f32(g[j] >> 16), bf16_to_f32(up[j] >> 16));
+      w[j] = f32_to_bf16(a0) | (f32_to_bf16(a1) << 16);
+    }
+  }
+}
+
+// group amax of 4 lanes (every lane of the quad must take part)
+__device__ __forceinline__ uint32_t mx_quad_amax(const uint32_t (&w)[4]) {
   uint32_t amax = 0;
 #pragma unroll
   for (int j = 0; j < 4; ++j) amax = max(amax, max(w[j] & 0x7FFFu, (w[j] >> 16) & 0x7FFFu));
   amax = max(amax, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)amax, 0xB1, 0xF, 0xF, false));
   amax = max(amax, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)amax, 0x4E, 0xF, 0xF, false));
-  if (!live) return;
-  const int e = mx_exponent(bf16_to_f32(amax), scale_alg);
+  return amax;
+}
+
+__device__ __forceinline__ uint2 mx_codes8(const uint32_t (&w)[4], int e) {
   uint32_t b[8];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     b[2 * j] = f32_to_e4m3(__builtin_ldexpf(bf16_to_f32(w[j] & 0xFFFFu), -e));
     b[2 * j + 1] = f32_to_e4m3(__builtin_ldexpf(bf16_to_f32(w[j] >> 16), -e));
   }
-  uint2 o;
-  o.x = b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24);
-  o.y = b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24);
+  return uint2{b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24),
+               b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24)};
+}
+
+// stores of chunk c (8 codes) of row `row` and, on the first lane of the
+// quad, the group's scale byte: payload row-major [.., K] or P16x64 blocks,
+// scales row-major [.., K/32] and/or k-block-major [KB][Mp][2]
+__device__ __forceinline__ void mx_store8(uint2 o, uint8_t sb, int64_t row, int64_t c, int64_t K,
+                                          uint8_t* __restrict__ payload, int blocked,
+                                          uint8_t* __restrict__ scale_rm,
+                                          uint8_t* __restrict__ scale_kb, int64_t Mp) {
   if (!blocked) {
     *reinterpret_cast<uint2*>(payload + row * K + c * 8) = o;
   } else {
@@ -148,7 +171,6 @@ __global__ __launch_bounds__(256) void mx_quant_kernel(const uint16_t* __restric
   }
   if ((c & 3) == 0) {
     const int64_t g = c / 4;                 // 32-group index along K
-    const uint8_t sb = (uint8_t)(e + 127);
     if (scale_rm) scale_rm[row * (K / 32) + g] = sb;
     if (scale_kb) {
       scale_kb[((g / 2) * Mp + row) * 2 + (g & 1)] = sb;
@@ -157,6 +179,27 @@ __global__ __launch_bounds__(256) void mx_quant_kernel(const uint16_t* __restric
       if (g == K / 32 - 1 && (g & 1) == 0) scale_kb[((g / 2) * Mp + row) * 2 + 1] = 0;
     }
   }
+}
+
+template <int ACT>
+__global__ __launch_bounds__(256) void mx_quant_kernel(const uint16_t* __restrict__ x, int64_t ldx,
+                                                       int64_t M, int64_t K, int scale_alg,
+                                                       uint8_t* __restrict__ payload, int blocked,
+                                                       uint8_t* __restrict__ scale_rm,
+                                                       uint8_t* __restrict__ scale_kb,
+                                                       int64_t Mp) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t chunks = K / 8;             // K % 32 == 0, so quads never straddle rows
+  const bool live = t < M * chunks;
+  const int64_t tc = live ? t : 0;
+  const int64_t row = tc / chunks, c = tc % chunks;
+  uint32_t w[4] = {0u, 0u, 0u, 0u};
+  if (live) mx_load8<ACT>(x, ldx, K, row, c, w);
+  const uint32_t amax = mx_quad_amax(w);
+  if (!live) return;
+  const int e = mx_exponent(bf16_to_f32(amax), scale_alg);
+  mx_store8(mx_codes8(w, e), (uint8_t)(e + 127), row, c, K, payload, blocked, scale_rm, scale_kb,
+            Mp);
 }
 
 // row-major [R, K/32] scales -> k-block-major [ceil(K/64)][Rp][2]; pads with 0
@@ -186,7 +229,8 @@ __global__ __launch_bounds__(256) void mx_scale_relayout_kernel(const uint8_t* _
 struct MxArgs {
   const uint8_t* a;        // E4M3, P16x64 blocks [ceil(M/16)][KB] (K zero-padded to 64)
   const uint8_t* a_scale;  // k-block-major [KB][Mp][2], Mp even
-  int64_t Mp;
+  int64_t Mp;              // row stride of a_scale
+  int64_t Mclamp;          // a_scale rows readable from a_scale (even)
   const uint8_t* w;        // packed E4M3 (P16x64), NB x KB blocks
   const uint8_t* w_scale;  // k-block-major [KB][Np][2], Np = NB * 16
   int64_t M, N, K;
@@ -250,7 +294,7 @@ struct MxTile {
                                                    int& dst) {
     if (q < 3) {
       int64_t r = row0 + q * 64 + 2 * (lane & 31);
-      r = r < p.Mp - 2 ? r : p.Mp - 2;
+      r = r < p.Mclamp - 2 ? r : p.Mclamp - 2;
       base = p.a_scale + r * 2;
       step = p.Mp * 2;
       dst = kScaleOfs + q * 128;
@@ -446,6 +490,124 @@ __global__ __launch_bounds__(512) void mx_gemm_kernel(MxArgs p) {
 }
 
 // ---------------------------------------------------------------------------
+// Grouped (MoE) form. The routed rows of expert e are R rows grouped by expert
+// (group_list, as the INT8 grouped path); the MX activation of a grouped
+// matmul is written in the P16x64 block layout with every expert starting on
+// a 16-row boundary ("padded rows"), so that a 192-row tile of one expert is
+// a run of whole blocks. A schedule of tile records {expert, first source row,
+// first padded row, rows} drives both the quant and the matmul.
+// ---------------------------------------------------------------------------
+constexpr int kMxSub = MxTile::BM / 16;  // 16-row groups per tile
+
+// exclusive scan over the 1024 threads of the block (one value each)
+__device__ __forceinline__ int block_scan_1024(int v, int* wsum, int& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int o = __shfl_up(incl, d, kWave);
+    if (lane >= d) incl += o;
+  }
+  __syncthreads();  // wsum free from an earlier scan
+  if (lane == kWave - 1) wsum[wave] = incl;
+  __syncthreads();
+  int before = 0;
+  total = 0;
+  for (int w = 0; w < 16; ++w) {
+    before += w < wave ? wsum[w] : 0;
+    total += wsum[w];
+  }
+  return before + incl - v;
+}
+
+// One 1024-thread workgroup, thread e = expert e (E <= 1024). Counts are cut
+// to what fits in R rows (a group_list summing past R writes nothing out of
+// bounds), so sum(padded rows) <= R + 15 E and records <= ceil(R/192) + E.
+__global__ __launch_bounds__(1024) void mx_group_schedule_kernel(const int64_t* __restrict__ group_list,
+                                                                 int E, int64_t R, int64_t max_tiles,
+                                                                 int4* __restrict__ tiles,
+                                                                 int* __restrict__ n_tiles) {
+  __shared__ int wsum[16];
+  const int e = threadIdx.x;
+  int64_t n = e < E ? group_list[e] : 0;
+  n = n < 0 ? 0 : (n > R ? R : n);
+  int total;
+  const int roff = block_scan_1024((int)n, wsum, total);
+  const int64_t left = R - roff;
+  const int rows = (int)(left <= 0 ? 0 : (n < left ? n : left));
+  const int poff = block_scan_1024((rows + 15) & ~15, wsum, total);
+  const int nt = (rows + MxTile::BM - 1) / MxTile::BM;
+  int nt_total;
+  const int toff = block_scan_1024(nt, wsum, nt_total);
+  for (int j = 0; j < nt; ++j) {
+    if (toff + j >= max_tiles) break;
+    const int r = j * MxTile::BM;
+    tiles[toff + j] = int4{e, roff + r, poff + r, min(MxTile::BM, rows - r)};
+  }
+  if (threadIdx.x == 0) *n_tiles = (int)(nt_total < max_tiles ? nt_total : max_tiles);
+}
+
+// MX quant of the rows of the tile records: block (tile, 16-row group); rows
+// of the group past the tile's rows get zero codes and scale byte 0.
+template <int ACT>
+__global__ __launch_bounds__(256) void mx_quant_tiles_kernel(const uint16_t* __restrict__ x,
+                                                             int64_t ldx, int64_t K,
+                                                             const int4* __restrict__ tiles,
+                                                             const int* __restrict__ n_tiles,
+                                                             int scale_alg,
+                                                             uint8_t* __restrict__ payload,
+                                                             uint8_t* __restrict__ scale_kb,
+                                                             int64_t Rs) {
+  const int tm = blockIdx.x / kMxSub, sub = blockIdx.x % kMxSub;
+  if (tm >= *n_tiles) return;
+  const int4 rec = tiles[tm];
+  if (16 * sub >= rec.w) return;
+  const int64_t chunks = K / 8;
+  const int64_t total = 16 * chunks;
+  for (int64_t base = 0; base < total; base += 256) {
+    const int64_t idx = base + threadIdx.x;
+    const bool live = idx < total;
+    const int64_t lr = 16 * sub + (live ? idx / chunks : 0), c = live ? idx % chunks : 0;
+    const bool real = live && lr < rec.w;
+    uint32_t w[4] = {0u, 0u, 0u, 0u};
+    if (real) mx_load8<ACT>(x, ldx, K, rec.y + lr, c, w);
+    const uint32_t amax = mx_quad_amax(w);
+    if (live) {
+      const int e = mx_exponent(bf16_to_f32(amax), scale_alg);
+      mx_store8(mx_codes8(w, e), (uint8_t)(e + 127), rec.z + lr, c, K, payload, 1, nullptr,
+                scale_kb, Rs);
+    }
+  }
+}
+
+// Grouped block-scaled matmul: one 192 x 256 tile per workgroup, tiles of all
+// experts (records) x n-tiles, XCD-chunked with m fastest; workgroups past the
+// schedule's tile count leave at once.
+__global__ __launch_bounds__(512) void mx_grouped_kernel(MxArgs base, const int4* __restrict__ tiles,
+                                                         const int* __restrict__ n_tiles,
+                                                         int64_t max_tiles, int64_t NT,
+                                                         int64_t w_stride, int64_t w_scale_off) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[MxTile::kLdsBytes];
+  const int64_t T = max_tiles * NT;
+  const int64_t per = (T + 7) / 8;
+  const int64_t t = (blockIdx.x % 8) * per + blockIdx.x / 8;
+  if (t >= T) return;
+  const int64_t tm = t % max_tiles, tn = t / max_tiles;
+  if (tm >= *n_tiles) return;
+  const int4 rec = tiles[tm];
+  MxArgs p = base;
+  p.a = base.a + (int64_t)(rec.z / 16) * p.KB * 1024;
+  p.a_scale = base.a_scale + (int64_t)rec.z * 2;
+  p.Mclamp = (rec.w + 1) & ~1;
+  p.w = base.w + (int64_t)rec.x * w_stride;
+  p.w_scale = p.w + w_scale_off;
+  p.y = base.y + (int64_t)rec.y * p.N;
+  f32x16 acc[MxTile::TM][MxTile::TN];
+  MxTile::mainloop(p, smem, acc, 0, rec.w, (int)(tn * MxTile::BN / 16));
+  MxTile::epilogue(p, acc, 0, rec.w, tn * MxTile::BN);
+}
+
+// ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
 int64_t mx_scale_kb_bytes(int64_t rows_padded, int64_t K) { return ceil_div(K, 64) * rows_padded * 2; }
@@ -465,8 +627,8 @@ hipError_t launch_mx_quant(const uint16_t* x, int64_t M, int64_t K, int scale_al
                            hipStream_t stream) {
   const int64_t n = M * (K / 8);
   if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(mx_quant_kernel, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, stream, x, M, K,
-                     scale_alg, payload, blocked ? 1 : 0, scale_rm, scale_kb, Mp);
+  hipLaunchKernelGGL(mx_quant_kernel<0>, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, stream, x, K,
+                     M, K, scale_alg, payload, blocked ? 1 : 0, scale_rm, scale_kb, Mp);
   return hipGetLastError();
 }
 
@@ -487,6 +649,7 @@ hipError_t launch_mx_gemm(const uint8_t* a, const uint8_t* a_scale_kb, int64_t M
   p.a = a;
   p.a_scale = a_scale_kb;
   p.Mp = Mp;
+  p.Mclamp = Mp;
   p.w = w_packed;
   p.w_scale = w_scale_kb;
   p.M = M;
@@ -497,6 +660,63 @@ hipError_t launch_mx_gemm(const uint8_t* a, const uint8_t* a_scale_kb, int64_t M
   p.y = y;
   const int64_t T = ceil_div(M, MxTile::BM) * ceil_div(N, MxTile::BN);
   hipLaunchKernelGGL(mx_gemm_kernel, dim3((unsigned)round_up(T, 8)), dim3(512), 0, stream, p);
+  return hipGetLastError();
+}
+
+int64_t mx_max_tiles(int64_t R, int64_t E) { return ceil_div(R, MxTile::BM) + E; }
+int64_t mx_padded_rows(int64_t R, int64_t E) { return round_up(R + 15 * E, 16); }
+
+hipError_t launch_mx_swiglu_quant(const uint16_t* h, int64_t R, int64_t I, int scale_alg,
+                                  uint8_t* payload, uint8_t* scale_rm, hipStream_t stream) {
+  const int64_t n = R * (I / 8);
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(mx_quant_kernel<1>, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, stream, h,
+                     2 * I, R, I, scale_alg, payload, 0, scale_rm, nullptr, (int64_t)0);
+  return hipGetLastError();
+}
+
+hipError_t launch_mx_group_schedule(const int64_t* group_list, int64_t E, int64_t R, int4* tiles,
+                                    int* n_tiles, hipStream_t stream) {
+  hipLaunchKernelGGL(mx_group_schedule_kernel, dim3(1), dim3(1024), 0, stream, group_list, (int)E, R,
+                     mx_max_tiles(R, E), tiles, n_tiles);
+  return hipGetLastError();
+}
+
+hipError_t launch_mx_quant_tiles(const uint16_t* x, int64_t ldx, int64_t K, int act, const int4* tiles,
+                                 const int* n_tiles, int64_t R, int64_t E, int scale_alg,
+                                 uint8_t* payload, uint8_t* scale_kb, hipStream_t stream) {
+  const int64_t grid = mx_max_tiles(R, E) * kMxSub;
+  const int64_t Rs = mx_padded_rows(R, E);
+  if (act)
+    hipLaunchKernelGGL(mx_quant_tiles_kernel<1>, dim3((unsigned)grid), dim3(256), 0, stream, x, ldx, K,
+                       tiles, n_tiles, scale_alg, payload, scale_kb, Rs);
+  else
+    hipLaunchKernelGGL(mx_quant_tiles_kernel<0>, dim3((unsigned)grid), dim3(256), 0, stream, x, ldx, K,
+                       tiles, n_tiles, scale_alg, payload, scale_kb, Rs);
+  return hipGetLastError();
+}
+
+hipError_t launch_mx_grouped_gemm(const uint8_t* payload, const uint8_t* scale_kb, int64_t R,
+                                  int64_t E, int64_t K, const int4* tiles, const int* n_tiles,
+                                  const uint8_t* w_packed, int64_t w_stride, int64_t w_scale_off,
+                                  int64_t N, uint16_t* y, hipStream_t stream) {
+  MxArgs p{};
+  p.a = payload;
+  p.a_scale = scale_kb;
+  p.Mp = mx_padded_rows(R, E);
+  p.Mclamp = p.Mp;
+  p.w = w_packed;
+  p.w_scale = nullptr;
+  p.M = R;
+  p.N = N;
+  p.K = K;
+  p.KB = (int)ceil_div(K, 64);
+  p.NB = (int)ceil_div(N, 16);
+  p.y = y;
+  const int64_t max_tiles = mx_max_tiles(R, E);
+  const int64_t NT = ceil_div(N, MxTile::BN);
+  hipLaunchKernelGGL(mx_grouped_kernel, dim3((unsigned)round_up(max_tiles * NT, 8)), dim3(512), 0,
+                     stream, p, tiles, n_tiles, max_tiles, NT, w_stride, w_scale_off);
   return hipGetLastError();
 }
 

@@ -163,3 +163,37 @@ def test_moe_io_validation_before_launch(w):
                             need, None) == 3
     assert L.w8a8_moe_layer(None, 0, 256, None, None, 8, 16, 128, None, None, None, None, None,
                             None, 0, None) == 0
+
+
+def test_mx_moe_validation_before_launch(w):
+    L = w.lib
+    p = ctypes.c_void_p(256)  # never dereferenced: validation fails first
+    ws = L.w8a8_mx_grouped_workspace_bytes(100, 4, 128)
+    # grouped: K % 32, E in [1, 1024], act, scale_alg, workspace, alignment
+    assert L.w8a8_mx_grouped_gemm(p, p, 100, 4, 64, 100, 0, p, 0, p, p, ws, None) == 4    # K % 32
+    assert L.w8a8_mx_grouped_gemm(p, p, 100, 2000, 64, 128, 0, p, 0, p, p, ws, None) == 4
+    assert L.w8a8_mx_grouped_gemm(p, p, 100, 4, 64, 128, 2, p, 0, p, p, ws, None) == 4     # act
+    assert L.w8a8_mx_grouped_gemm(p, p, 100, 4, 64, 128, 0, p, 3, p, p, ws, None) == 4     # scale_alg
+    assert L.w8a8_mx_grouped_gemm(p, p, 100, 4, 64, 128, 0, p, 0, p, p, ws - 1, None) == 5
+    assert L.w8a8_mx_grouped_gemm(p, p, 100, 4, 64, 128, 0, None, 0, p, p, ws, None) == 1
+    assert L.w8a8_mx_grouped_gemm(ctypes.c_void_p(264), p, 100, 4, 64, 128, 0, p, 0, p, p, ws,
+                                  None) == 3
+    assert L.w8a8_mx_grouped_gemm(None, None, 0, 4, 64, 128, 0, None, 0, None, None, 0, None) == 0
+    # chain
+    need = L.w8a8_mx_moe_workspace_bytes(100, 4, 256, 128)
+    assert need >= 100 * 2 * 128 * 2 + 100 * 256
+    assert L.w8a8_mx_moe_grouped(p, p, 100, 4, 256, 128, p, p, 0, p, p, need - 1, None) == 5
+    assert L.w8a8_mx_moe_grouped(p, p, 100, 4, 256, 100, p, p, 0, p, p, need, None) == 4  # I % 32
+    assert L.w8a8_mx_moe_grouped(p, None, 100, 4, 256, 128, p, p, 0, p, p, need, None) == 1
+    # preparation and the SwiGLU MX quant
+    assert L.w8a8_mx_moe_staging_bytes(64, 96) == 64 * 96 * 2
+    assert L.w8a8_mx_moe_packed_bytes(3, 64, 96) == 3 * L.w8a8_mx_packed_bytes(64, 96)
+    assert L.w8a8_mx_moe_prepare(p, p, 2, 64, 96, 128, 128, 0, p, None, p, 64 * 96 * 2 - 1,
+                                 None) == 5
+    assert L.w8a8_mx_moe_prepare(p, p, 2, 64, 100, 128, 128, 0, p, None, p, 1 << 20, None) == 4
+    assert L.w8a8_mx_moe_prepare(p, p, 2, 64, 96, 128, 128, 0, None, None, p, 1 << 20, None) == 1
+    assert L.w8a8_mx_moe_prepare(p, p, 2, 64, 96, 128, 128, 0, p, ctypes.c_void_p(384), p,
+                                 1 << 20, None) == 3
+    assert L.w8a8_mx_swiglu_quant(p, 4, 48, 0, p, p, None) == 4                            # I % 32
+    assert L.w8a8_mx_swiglu_quant(ctypes.c_void_p(264), 4, 64, 0, p, p, None) == 3
+    assert L.w8a8_mx_swiglu_quant(None, 0, 64, 0, None, None, None) == 0
