@@ -21,6 +21,8 @@
 // adjacent; rows_p = rows rounded up to even for activations, to 16 for
 // weights), so the scales of one stage are a contiguous, dword-aligned run
 // per operand.
+#include <algorithm>
+
 #include "device_common.hpp"
 #include "launch.hpp"
 #include "mx.hpp"
@@ -246,16 +248,22 @@ __device__ __forceinline__ void mx_wait_barrier() {
 typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
+template <int BM_>
 struct MxTile {
-  static constexpr int BM = 192, BN = 256, WM = 2, WN = 4, kWaves = 8, RING = 5;
-  static constexpr int TM = BM / WM / 32;  // 3
+  static constexpr int BM = BM_, BN = 256, WM = 2, WN = 4, kWaves = 8, RING = 5;
+  static constexpr int TM = BM / WM / 32;  // 3 (BM 192) or 1 (BM 64)
   static constexpr int TN = BN / WN / 32;  // 2
-  static constexpr int kABlocks = BM / 16, kBBlocks = BN / 16;  // 12, 16
-  static constexpr int kLoads = 5;                              // DMA per wavefront per stage
+  static constexpr int kABlocks = BM / 16, kBBlocks = BN / 16;  // 12 or 4, and 16
+  // payload blocks per wavefront: kPayHi on wavefronts 0..3, one fewer on 4..7
+  static constexpr int kPayHi = (kABlocks + kBBlocks + 7) / 8;  // 4 or 3
+  static constexpr int kASlices = BM / 64, kSlices = kASlices + 4;  // 128-byte scale slices
+  static constexpr int kLoads = kPayHi + 1;                     // DMA per wavefront per stage
   static constexpr int kScaleOfs = (kABlocks + kBBlocks) * 1024;
   static constexpr int kStageBytes = kScaleOfs + 1024;
   static constexpr int kLdsBytes = RING * kStageBytes;
-  static_assert(kABlocks + kBBlocks == 4 * 4 + 4 * 3, "payload split over the wavefronts");
+  static_assert(BM % 64 == 0 && TM >= 1, "tile height");
+  static_assert(kABlocks + kBBlocks == 4 * kPayHi + 4 * (kPayHi - 1), "payload split over the wavefronts");
+  static_assert(kPayHi <= 4 && kSlices >= 5, "DMA source slots");
   static_assert(kLdsBytes <= 163840, "LDS");
 
   // DMA sources of one wavefront: payload blocks (16 bytes per lane) and scale
@@ -287,12 +295,12 @@ struct MxTile {
     }
   }
 
-  // scale slice q (0..6): A rows [64q, 64q + 64) for q < 3, else B columns
-  // [64(q-3), 64(q-3) + 64); lanes 0..31 bring two rows (columns) each
+  // scale slice q: A rows [64q, 64q + 64) for q < kASlices, else B columns
+  // [64(q - kASlices), + 64); lanes 0..31 bring two rows (columns) each
   __device__ __forceinline__ static void scale_src(const MxArgs& p, int q, int lane, int64_t row0,
                                                    int nb0, const uint8_t*& base, int64_t& step,
                                                    int& dst) {
-    if (q < 3) {
+    if (q < kASlices) {
       int64_t r = row0 + q * 64 + 2 * (lane & 31);
       r = r < p.Mclamp - 2 ? r : p.Mclamp - 2;
       base = p.a_scale + r * 2;
@@ -300,28 +308,29 @@ struct MxTile {
       dst = kScaleOfs + q * 128;
     } else {
       const int64_t np = (int64_t)p.NB * 16;
-      int64_t c = (int64_t)nb0 * 16 + (q - 3) * 64 + 2 * (lane & 31);
+      int64_t c = (int64_t)nb0 * 16 + (q - kASlices) * 64 + 2 * (lane & 31);
       c = c < np - 2 ? c : np - 2;
       base = p.w_scale + c * 2;
       step = np * 2;
-      dst = kScaleOfs + 512 + (q - 3) * 128;
+      dst = kScaleOfs + 512 + (q - kASlices) * 128;
     }
   }
 
   __device__ __forceinline__ static void sources(const MxArgs& p, Src& s, int wave, int lane,
                                                  int64_t row0, int64_t row_last, int nb0) {
-    // payload: wavefronts 0..3 blocks 4w..4w+3, 4..7 blocks 16+3(w-4)..+2
-    const int first = wave < 4 ? 4 * wave : 16 + 3 * (wave - 4);
-    const int count = wave < 4 ? 4 : 3;
+    // payload: wavefronts 0..3 kPayHi blocks each, 4..7 one fewer
+    const int first = wave < 4 ? kPayHi * wave : 4 * kPayHi + (kPayHi - 1) * (wave - 4);
+    const int count = wave < 4 ? kPayHi : kPayHi - 1;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < kPayHi; ++i) {
       const int bi = first + (i < count ? i : count - 1);
       payload_src(p, bi, lane, row0, row_last, nb0, s.pbase[i], s.pstep[i]);
       s.pdst[i] = bi * 1024;
     }
-    // scale slices: wavefronts 0..3 slice w; 4: 4, 5; 5: 6, 6; 6, 7: 6, 6
-    const int q0 = wave < 4 ? wave : (wave == 4 ? 4 : 6);
-    const int q1 = wave == 4 ? 5 : 6;
+    // scale slices: wavefronts 0..3 slice w; 4: slices 4 and 5; 5..7 the last
+    // slice twice (spares repeat it: identical bytes to the same place)
+    const int q0 = wave < 4 ? wave : (wave == 4 ? 4 : kSlices - 1);
+    const int q1 = wave == 4 ? (5 < kSlices ? 5 : kSlices - 1) : kSlices - 1;
     scale_src(p, q0, lane, row0, nb0, s.sbase[0], s.sstep[0], s.sdst[0]);
     scale_src(p, q1, lane, row0, nb0, s.sbase[1], s.sstep[1], s.sdst[1]);
   }
@@ -332,8 +341,8 @@ struct MxTile {
     uint8_t* st = smem + buf * kStageBytes;
     const bool four = wave < 4;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (i == 3 && !four) break;
+    for (int i = 0; i < kPayHi; ++i) {
+      if (i == kPayHi - 1 && !four) break;
       const uint8_t* src = s.pbase[i] + kb * s.pstep[i];
       __builtin_amdgcn_global_load_lds(src, (W8A8_LDS_MX void*)((W8A8_LDS_MX uint8_t*)st + s.pdst[i]),
                                        16, 0, 0);
@@ -473,31 +482,37 @@ struct MxTile {
   }
 };
 
+using MxBig = MxTile<192>;
+using MxSmall = MxTile<64>;
+
 __global__ __launch_bounds__(512) void mx_gemm_kernel(MxArgs p) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[MxTile::kLdsBytes];
-  const int64_t MT = (p.M + MxTile::BM - 1) / MxTile::BM, NT = (p.N + MxTile::BN - 1) / MxTile::BN;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[MxBig::kLdsBytes];
+  const int64_t MT = (p.M + MxBig::BM - 1) / MxBig::BM, NT = (p.N + MxBig::BN - 1) / MxBig::BN;
   const int64_t T = MT * NT;
   // XCD-chunked tile order, m fastest inside an XCD's range
   const int64_t per = (T + 7) / 8;
   const int64_t t = (blockIdx.x % 8) * per + blockIdx.x / 8;
   if (t >= T) return;
   const int64_t tm = t % MT, tn = t / MT;
-  const int64_t row0 = tm * MxTile::BM;
-  const int64_t row_end = min(row0 + MxTile::BM, p.M);
-  f32x16 acc[MxTile::TM][MxTile::TN];
-  MxTile::mainloop(p, smem, acc, row0, row_end, (int)(tn * MxTile::BN / 16));
-  MxTile::epilogue(p, acc, row0, row_end, tn * MxTile::BN);
+  const int64_t row0 = tm * MxBig::BM;
+  const int64_t row_end = min(row0 + MxBig::BM, p.M);
+  f32x16 acc[MxBig::TM][MxBig::TN];
+  MxBig::mainloop(p, smem, acc, row0, row_end, (int)(tn * MxBig::BN / 16));
+  MxBig::epilogue(p, acc, row0, row_end, tn * MxBig::BN);
 }
 
 // ---------------------------------------------------------------------------
 // Grouped (MoE) form. The routed rows of expert e are R rows grouped by expert
 // (group_list, as the INT8 grouped path); the MX activation of a grouped
 // matmul is written in the P16x64 block layout with every expert starting on
-// a 16-row boundary ("padded rows"), so that a 192-row tile of one expert is
-// a run of whole blocks. A schedule of tile records {expert, first source row,
-// first padded row, rows} drives both the quant and the matmul.
+// a 16-row boundary ("padded rows"), so that a tile of one expert is a run of
+// whole blocks. The schedule cuts each expert into 192-row tiles; a last
+// piece of at most 64 rows gets a 64-row tile instead (most experts of a
+// skewed routing are that small). Records int4 {expert, first source row,
+// first padded row, rows}: 192-row tiles in slots [0, max_big), 64-row tiles
+// in slots [max_big, max_big + E); counts[0] and counts[1] say how many.
 // ---------------------------------------------------------------------------
-constexpr int kMxSub = MxTile::BM / 16;  // 16-row groups per tile
+constexpr int kMxSub = MxBig::BM / 16;  // 16-row groups per record slot
 
 // exclusive scan over the 1024 threads of the block (one value each)
 __device__ __forceinline__ int block_scan_1024(int v, int* wsum, int& total) {
@@ -522,11 +537,12 @@ __device__ __forceinline__ int block_scan_1024(int v, int* wsum, int& total) {
 
 // One 1024-thread workgroup, thread e = expert e (E <= 1024). Counts are cut
 // to what fits in R rows (a group_list summing past R writes nothing out of
-// bounds), so sum(padded rows) <= R + 15 E and records <= ceil(R/192) + E.
+// bounds), so sum(padded rows) <= R + 15 E, 192-row records <= ceil(R/192) +
+// E = max_big and 64-row records <= E.
 __global__ __launch_bounds__(1024) void mx_group_schedule_kernel(const int64_t* __restrict__ group_list,
-                                                                 int E, int64_t R, int64_t max_tiles,
+                                                                 int E, int64_t R, int64_t max_big,
                                                                  int4* __restrict__ tiles,
-                                                                 int* __restrict__ n_tiles) {
+                                                                 int* __restrict__ counts) {
   __shared__ int wsum[16];
   const int e = threadIdx.x;
   int64_t n = e < E ? group_list[e] : 0;
@@ -536,64 +552,130 @@ __global__ __launch_bounds__(1024) void mx_group_schedule_kernel(const int64_t* 
   const int64_t left = R - roff;
   const int rows = (int)(left <= 0 ? 0 : (n < left ? n : left));
   const int poff = block_scan_1024((rows + 15) & ~15, wsum, total);
-  const int nt = (rows + MxTile::BM - 1) / MxTile::BM;
-  int nt_total;
-  const int toff = block_scan_1024(nt, wsum, nt_total);
-  for (int j = 0; j < nt; ++j) {
-    if (toff + j >= max_tiles) break;
-    const int r = j * MxTile::BM;
-    tiles[toff + j] = int4{e, roff + r, poff + r, min(MxTile::BM, rows - r)};
+  const int full = rows / MxBig::BM, rem = rows % MxBig::BM;
+  const int nb = full + (rem > MxSmall::BM ? 1 : 0);
+  const int ns = (rem > 0 && rem <= MxSmall::BM) ? 1 : 0;
+  int nb_total, ns_total;
+  const int boff = block_scan_1024(nb, wsum, nb_total);
+  const int soff = block_scan_1024(ns, wsum, ns_total);
+  for (int j = 0; j < nb; ++j) {
+    if (boff + j >= max_big) break;
+    const int r = j * MxBig::BM;
+    tiles[boff + j] = int4{e, roff + r, poff + r, min(MxBig::BM, rows - r)};
   }
-  if (threadIdx.x == 0) *n_tiles = (int)(nt_total < max_tiles ? nt_total : max_tiles);
+  if (ns) {
+    const int r = full * MxBig::BM;
+    tiles[max_big + soff] = int4{e, roff + r, poff + r, rem};
+  }
+  if (threadIdx.x == 0) {
+    counts[0] = (int)(nb_total < max_big ? nb_total : max_big);
+    counts[1] = ns_total;
+  }
 }
 
-// MX quant of the rows of the tile records: block (tile, 16-row group); rows
-// of the group past the tile's rows get zero codes and scale byte 0.
+// record slot m holds a scheduled tile
+__device__ __forceinline__ bool mx_slot_live(int64_t m, int64_t max_big, const int* counts) {
+  return m < max_big ? m < counts[0] : m - max_big < counts[1];
+}
+
+// MX quant straight into the P16x64 block layout: one wavefront per output
+// block (16 rows x one 64-deep k-block). Lane l takes row l / 4 and the 16
+// values k = 64 kb + 16 (l % 4) .. + 15 (four consecutive lanes read a row's
+// 128 contiguous bytes); its 16 codes are bytes (l / 4 + 16 (l % 4)) * 16 ..
+// of the block, so the wavefront's stores cover the 1 KB block. A 32-group is
+// lanes l and l ^ 1; lane 4 r stores row r's two scale bytes of the k-block
+// ([KB][scale_rows][2]) as one 16-bit word. Rows past the real ones
+// and the ragged upper half of a last k-block (K % 64 == 32) get zero codes
+// and scale byte 0.
+// Workgroup (x, y): x = (tile record, 16-row group) of the grouped schedule
+// (source row rec.y + lr, padded row rec.z + lr, rec.w real rows), k-blocks
+// y * 4 + wave, stepping by 4 * gridDim.y (a few k-blocks per wavefront, so
+// that enough wavefronts run).
 template <int ACT>
-__global__ __launch_bounds__(256) void mx_quant_tiles_kernel(const uint16_t* __restrict__ x,
-                                                             int64_t ldx, int64_t K,
-                                                             const int4* __restrict__ tiles,
-                                                             const int* __restrict__ n_tiles,
-                                                             int scale_alg,
-                                                             uint8_t* __restrict__ payload,
-                                                             uint8_t* __restrict__ scale_kb,
-                                                             int64_t Rs) {
-  const int tm = blockIdx.x / kMxSub, sub = blockIdx.x % kMxSub;
-  if (tm >= *n_tiles) return;
-  const int4 rec = tiles[tm];
-  if (16 * sub >= rec.w) return;
-  const int64_t chunks = K / 8;
-  const int64_t total = 16 * chunks;
-  for (int64_t base = 0; base < total; base += 256) {
-    const int64_t idx = base + threadIdx.x;
-    const bool live = idx < total;
-    const int64_t lr = 16 * sub + (live ? idx / chunks : 0), c = live ? idx % chunks : 0;
-    const bool real = live && lr < rec.w;
-    uint32_t w[4] = {0u, 0u, 0u, 0u};
-    if (real) mx_load8<ACT>(x, ldx, K, rec.y + lr, c, w);
-    const uint32_t amax = mx_quad_amax(w);
-    if (live) {
-      const int e = mx_exponent(bf16_to_f32(amax), scale_alg);
-      mx_store8(mx_codes8(w, e), (uint8_t)(e + 127), rec.z + lr, c, K, payload, 1, nullptr,
-                scale_kb, Rs);
+__device__ __forceinline__ void mx_load16(const uint16_t* __restrict__ x, int64_t ldx, int64_t K,
+                                          int64_t row, int64_t k, uint32_t (&w)[8]) {
+  const uint4* src = reinterpret_cast<const uint4*>(x + row * ldx + k);
+  const uint4 v0 = src[0], v1 = src[1];
+  const uint32_t g[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+  if (ACT == 0) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) w[j] = g[j];
+  } else {
+    const uint4* usrc = reinterpret_cast<const uint4*>(x + row * ldx + K + k);
+    const uint4 u0 = usrc[0], u1 = usrc[1];
+    const uint32_t up[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float a0 = swiglu_fixed(bf16_to_f32(g[j] & 0xFFFFu), bf16_to_f32(up[j] & 0xFFFFu));
+      const float a1 = swiglu_fixed(bf16_to_f32(g[j] >> 16), bf16_to_f32(up[j] >> 16));
+      w[j] = f32_to_bf16(a0) | (f32_to_bf16(a1) << 16);
     }
   }
 }
 
-// Grouped block-scaled matmul: one 192 x 256 tile per workgroup, tiles of all
-// experts (records) x n-tiles, XCD-chunked with m fastest; workgroups past the
-// schedule's tile count leave at once.
+template <int ACT>
+__global__ __launch_bounds__(256) void mx_quant_tiles_kernel(const uint16_t* __restrict__ x,
+                                                              int64_t ldx, int64_t K,
+                                                              const int4* __restrict__ tiles,
+                                                              const int* __restrict__ counts,
+                                                              int64_t max_big, int scale_alg,
+                                                              uint8_t* __restrict__ payload,
+                                                              uint8_t* __restrict__ scale_kb,
+                                                              int64_t scale_rows) {
+  const int tm = blockIdx.x / kMxSub, sub = blockIdx.x % kMxSub;
+  if (!mx_slot_live(tm, max_big, counts)) return;
+  const int4 rec = tiles[tm];
+  if (16 * sub >= rec.w) return;
+  const int64_t src0 = (int64_t)rec.y + 16 * sub;
+  const int64_t prow0 = (int64_t)rec.z + 16 * sub;
+  const int64_t nreal = rec.w - 16 * sub;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = lane >> 2, ch = lane & 3;
+  const bool real = r < nreal;
+  const int64_t prow = prow0 + r;
+  const int KB = (int)((K + 63) / 64);
+  uint8_t* blocks = payload + (prow0 >> 4) * (int64_t)KB * 1024;
+  // k-blocks split over blockIdx.y and the 4 wavefronts
+  for (int kb = (int)blockIdx.y * 4 + wave; kb < KB; kb += 4 * (int)gridDim.y) {
+    const int64_t k = (int64_t)kb * 64 + 16 * ch;
+    uint32_t w[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+    if (real && k < K) mx_load16<ACT>(x, ldx, K, src0 + r, k, w);
+    uint32_t amax = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) amax = max(amax, max(w[j] & 0x7FFFu, (w[j] >> 16) & 0x7FFFu));
+    amax = max(amax, (uint32_t)__shfl_xor((int)amax, 1, kWave));
+    const int e = mx_exponent(bf16_to_f32(amax), scale_alg);
+    const uint2 lo = mx_codes8(*reinterpret_cast<const uint32_t(*)[4]>(&w[0]), e);
+    const uint2 hi = mx_codes8(*reinterpret_cast<const uint32_t(*)[4]>(&w[4]), e);
+    *reinterpret_cast<uint4*>(blocks + (int64_t)kb * 1024 + (r + 16 * ch) * 16) =
+        uint4{lo.x, lo.y, hi.x, hi.y};
+    const int e_g1 = __shfl_xor(e, 2, kWave);  // group 1 of the row: chunk 2
+    if (ch == 0 && prow < scale_rows) {
+      const uint32_t b0 = (uint32_t)(e + 127);
+      const uint32_t b1 = (int64_t)kb * 64 + 32 < K ? (uint32_t)(e_g1 + 127) : 0u;
+      *reinterpret_cast<uint16_t*>(scale_kb + ((int64_t)kb * scale_rows + prow) * 2) =
+          (uint16_t)(b0 | (b1 << 8));
+    }
+  }
+}
+
+// Grouped block-scaled matmul: one tile per workgroup (a 192 x 256 or a
+// 64 x 256 one, by record slot), slots x n-tiles, XCD-chunked with m fastest;
+// workgroups of unused slots leave at once.
 __global__ __launch_bounds__(512) void mx_grouped_kernel(MxArgs base, const int4* __restrict__ tiles,
-                                                         const int* __restrict__ n_tiles,
-                                                         int64_t max_tiles, int64_t NT,
-                                                         int64_t w_stride, int64_t w_scale_off) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[MxTile::kLdsBytes];
-  const int64_t T = max_tiles * NT;
+                                                         const int* __restrict__ counts,
+                                                         int64_t max_big, int64_t max_small,
+                                                         int64_t NT, int64_t w_stride,
+                                                         int64_t w_scale_off) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[MxBig::kLdsBytes];
+  static_assert(MxSmall::kLdsBytes <= MxBig::kLdsBytes, "LDS shared by both tiles");
+  const int64_t MT = max_big + max_small;
+  const int64_t T = MT * NT;
   const int64_t per = (T + 7) / 8;
   const int64_t t = (blockIdx.x % 8) * per + blockIdx.x / 8;
   if (t >= T) return;
-  const int64_t tm = t % max_tiles, tn = t / max_tiles;
-  if (tm >= *n_tiles) return;
+  const int64_t tm = t % MT, tn = t / MT;
+  if (!mx_slot_live(tm, max_big, counts)) return;
   const int4 rec = tiles[tm];
   MxArgs p = base;
   p.a = base.a + (int64_t)(rec.z / 16) * p.KB * 1024;
@@ -602,14 +684,23 @@ __global__ __launch_bounds__(512) void mx_grouped_kernel(MxArgs base, const int4
   p.w = base.w + (int64_t)rec.x * w_stride;
   p.w_scale = p.w + w_scale_off;
   p.y = base.y + (int64_t)rec.y * p.N;
-  f32x16 acc[MxTile::TM][MxTile::TN];
-  MxTile::mainloop(p, smem, acc, 0, rec.w, (int)(tn * MxTile::BN / 16));
-  MxTile::epilogue(p, acc, 0, rec.w, tn * MxTile::BN);
+  const int nb0 = (int)(tn * MxBig::BN / 16);
+  if (tm < max_big) {
+    f32x16 acc[MxBig::TM][MxBig::TN];
+    MxBig::mainloop(p, smem, acc, 0, rec.w, nb0);
+    MxBig::epilogue(p, acc, 0, rec.w, tn * MxBig::BN);
+  } else {
+    f32x16 acc[MxSmall::TM][MxSmall::TN];
+    MxSmall::mainloop(p, smem, acc, 0, rec.w, nb0);
+    MxSmall::epilogue(p, acc, 0, rec.w, tn * MxSmall::BN);
+  }
 }
 
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
+// k-split of mx_quant_blocks_kernel: about 4 k-blocks per wavefront
+static int64_t mx_quant_ksplit(int64_t K) { return std::max<int64_t>(1, ceil_div(K, 64) / 16); }
 int64_t mx_scale_kb_bytes(int64_t rows_padded, int64_t K) { return ceil_div(K, 64) * rows_padded * 2; }
 
 hipError_t launch_mx_resolve(const uint8_t* w, const float* s, int64_t N, int64_t K, int64_t BN,
@@ -658,12 +749,13 @@ hipError_t launch_mx_gemm(const uint8_t* a, const uint8_t* a_scale_kb, int64_t M
   p.KB = (int)ceil_div(K, 64);
   p.NB = (int)ceil_div(N, 16);
   p.y = y;
-  const int64_t T = ceil_div(M, MxTile::BM) * ceil_div(N, MxTile::BN);
+  const int64_t T = ceil_div(M, MxBig::BM) * ceil_div(N, MxBig::BN);
   hipLaunchKernelGGL(mx_gemm_kernel, dim3((unsigned)round_up(T, 8)), dim3(512), 0, stream, p);
   return hipGetLastError();
 }
 
-int64_t mx_max_tiles(int64_t R, int64_t E) { return ceil_div(R, MxTile::BM) + E; }
+static int64_t mx_max_big(int64_t R, int64_t E) { return ceil_div(R, MxBig::BM) + E; }
+int64_t mx_max_tiles(int64_t R, int64_t E) { return mx_max_big(R, E) + E; }
 int64_t mx_padded_rows(int64_t R, int64_t E) { return round_up(R + 15 * E, 16); }
 
 hipError_t launch_mx_swiglu_quant(const uint16_t* h, int64_t R, int64_t I, int scale_alg,
@@ -676,28 +768,28 @@ hipError_t launch_mx_swiglu_quant(const uint16_t* h, int64_t R, int64_t I, int s
 }
 
 hipError_t launch_mx_group_schedule(const int64_t* group_list, int64_t E, int64_t R, int4* tiles,
-                                    int* n_tiles, hipStream_t stream) {
+                                    int* counts, hipStream_t stream) {
   hipLaunchKernelGGL(mx_group_schedule_kernel, dim3(1), dim3(1024), 0, stream, group_list, (int)E, R,
-                     mx_max_tiles(R, E), tiles, n_tiles);
+                     mx_max_big(R, E), tiles, counts);
   return hipGetLastError();
 }
 
 hipError_t launch_mx_quant_tiles(const uint16_t* x, int64_t ldx, int64_t K, int act, const int4* tiles,
-                                 const int* n_tiles, int64_t R, int64_t E, int scale_alg,
+                                 const int* counts, int64_t R, int64_t E, int scale_alg,
                                  uint8_t* payload, uint8_t* scale_kb, hipStream_t stream) {
-  const int64_t grid = mx_max_tiles(R, E) * kMxSub;
+  const dim3 grid((unsigned)(mx_max_tiles(R, E) * kMxSub), (unsigned)mx_quant_ksplit(K));
   const int64_t Rs = mx_padded_rows(R, E);
   if (act)
-    hipLaunchKernelGGL(mx_quant_tiles_kernel<1>, dim3((unsigned)grid), dim3(256), 0, stream, x, ldx, K,
-                       tiles, n_tiles, scale_alg, payload, scale_kb, Rs);
+    hipLaunchKernelGGL(mx_quant_tiles_kernel<1>, grid, dim3(256), 0, stream, x, ldx, K, tiles,
+                       counts, mx_max_big(R, E), scale_alg, payload, scale_kb, Rs);
   else
-    hipLaunchKernelGGL(mx_quant_tiles_kernel<0>, dim3((unsigned)grid), dim3(256), 0, stream, x, ldx, K,
-                       tiles, n_tiles, scale_alg, payload, scale_kb, Rs);
+    hipLaunchKernelGGL(mx_quant_tiles_kernel<0>, grid, dim3(256), 0, stream, x, ldx, K, tiles,
+                       counts, mx_max_big(R, E), scale_alg, payload, scale_kb, Rs);
   return hipGetLastError();
 }
 
 hipError_t launch_mx_grouped_gemm(const uint8_t* payload, const uint8_t* scale_kb, int64_t R,
-                                  int64_t E, int64_t K, const int4* tiles, const int* n_tiles,
+                                  int64_t E, int64_t K, const int4* tiles, const int* counts,
                                   const uint8_t* w_packed, int64_t w_stride, int64_t w_scale_off,
                                   int64_t N, uint16_t* y, hipStream_t stream) {
   MxArgs p{};
@@ -713,10 +805,9 @@ hipError_t launch_mx_grouped_gemm(const uint8_t* payload, const uint8_t* scale_k
   p.KB = (int)ceil_div(K, 64);
   p.NB = (int)ceil_div(N, 16);
   p.y = y;
-  const int64_t max_tiles = mx_max_tiles(R, E);
-  const int64_t NT = ceil_div(N, MxTile::BN);
-  hipLaunchKernelGGL(mx_grouped_kernel, dim3((unsigned)round_up(max_tiles * NT, 8)), dim3(512), 0,
-                     stream, p, tiles, n_tiles, max_tiles, NT, w_stride, w_scale_off);
+  const int64_t NT = ceil_div(N, MxBig::BN);
+  hipLaunchKernelGGL(mx_grouped_kernel, dim3((unsigned)round_up(mx_max_tiles(R, E) * NT, 8)), dim3(512), 0,
+                     stream, p, tiles, counts, mx_max_big(R, E), E, NT, w_stride, w_scale_off);
   return hipGetLastError();
 }
 

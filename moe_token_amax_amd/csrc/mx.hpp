@@ -29,19 +29,20 @@ hipError_t launch_mx_swiglu_quant(const uint16_t* h, int64_t R, int64_t I, int s
                                   uint8_t* payload, uint8_t* scale_rm, hipStream_t stream);
 
 // Grouped (MoE) form. Tile records int4 {expert, first source row, first
-// padded row, rows}, at most mx_max_tiles(R, E); the MX activation lives in
+// padded row, rows} in mx_max_tiles(R, E) slots (192-row tiles first, then
+// one 64-row slot per expert), counts int[2]; the MX activation lives in
 // mx_padded_rows(R, E) padded rows (P16x64 blocks, k-block-major scales).
 int64_t mx_max_tiles(int64_t R, int64_t E);
 int64_t mx_padded_rows(int64_t R, int64_t E);
 hipError_t launch_mx_group_schedule(const int64_t* group_list, int64_t E, int64_t R, int4* tiles,
-                                    int* n_tiles, hipStream_t stream);
+                                    int* counts, hipStream_t stream);
 // act 0: the rows of x [R, K] (row stride ldx); act 1: SwiGLU of x = h [R, 2K]
 hipError_t launch_mx_quant_tiles(const uint16_t* x, int64_t ldx, int64_t K, int act, const int4* tiles,
-                                 const int* n_tiles, int64_t R, int64_t E, int scale_alg,
+                                 const int* counts, int64_t R, int64_t E, int scale_alg,
                                  uint8_t* payload, uint8_t* scale_kb, hipStream_t stream);
 // expert e's packed weight at w_packed + e * w_stride, its scales w_scale_off further
 hipError_t launch_mx_grouped_gemm(const uint8_t* payload, const uint8_t* scale_kb, int64_t R,
-                                  int64_t E, int64_t K, const int4* tiles, const int* n_tiles,
+                                  int64_t E, int64_t K, const int4* tiles, const int* counts,
                                   const uint8_t* w_packed, int64_t w_stride, int64_t w_scale_off,
                                   int64_t N, uint16_t* y, hipStream_t stream);
 
