@@ -57,7 +57,7 @@ def _args():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode",
                     choices=["decode", "prefill", "moe", "moe_layer", "tiny", "copy", "mx",
-                             "mx_moe", "static"])
+                             "mx_moe", "static", "w4a16"])
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="approximate budget of the oracle timing on the host")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -604,6 +604,98 @@ class MxMoeWorkload(Workload):
                            f"tokens = rows / top_k")
 
 
+class W4Workload(Workload):
+    """The decode-shaped linear with W4A16 weights: X BF16 [M, 7168] for M in 1,
+    4, 16, 64 (0.5 % x20 outliers), the weight [4096, 7168] INT4 per 32 input
+    channels with BF16 scales, rotated over 32 packed copies (past the MALL)."""
+    Ms = (1, 4, 16, 64)
+
+    def __init__(self, w, torch):
+        super().__init__(w, torch)
+        import numpy as np
+
+        import synth
+        self.name = "w4a16"
+        d = synth.decode(seed=0)
+        self.K, self.N = d.x.shape[1], 4096
+        dev = "cuda"
+        r = np.random.default_rng([0, 44])
+        wf = r.standard_normal((self.N, self.K)).astype(np.float32) * \
+            r.uniform(0.005, 0.05, (self.N, 1)).astype(np.float32)
+        wb = torch.from_numpy(synth.to_bf16_bits(wf).view(np.int16)).to(dev).view(torch.bfloat16)
+        _, _, packed = w.w4a16_quant_weight(wb)
+        del wb
+        self.copies = 32
+        self.wp = torch.empty((self.copies, packed.numel()), dtype=torch.uint8, device=dev)
+        for c in range(self.copies):
+            self.wp[c].copy_(packed)
+        del packed
+        self.x = torch.from_numpy(d.x.view(np.int16)).to(dev).view(torch.bfloat16)
+        self.y = {M: torch.empty((M, self.N), dtype=torch.bfloat16, device=dev) for M in self.Ms}
+        per = len(self.Ms)
+        steps = [self._make_step([(p * per + j) % self.copies for j in range(per)])
+                 for p in range(self.copies // per)]
+        self.capture(steps, [(self._make_linears(M, self.copies), self.copies, M) for M in self.Ms])
+        self.unit = "GB/s"
+        self.bound = "hbm"
+
+    def _linear(self, M, c):
+        self.w.w4a16_linear(self.x[:M], self.wp[c], self.N, y=self.y[M])
+
+    def _make_step(self, copy_ids):
+        def fn():
+            for M, c in zip(self.Ms, copy_ids):
+                self._linear(M, c)
+        return fn
+
+    def _make_linears(self, M, n):
+        def fn():
+            for i in range(n):
+                self._linear(M, i % self.copies)
+        return fn
+
+    def gemm_bytes(self, M):
+        """One launch: INT4 codes (N K / 2) + BF16 scales (2 N K / 32), BF16 x in, BF16 y out."""
+        return self.N * self.K // 2 + 2 * self.N * self.K // 32 + 2 * M * self.K + 2 * M * self.N
+
+    def alg_bytes(self):
+        return sum(self.gemm_bytes(M) for M in self.Ms)
+
+    def value(self, sec_per_step):
+        return self.alg_bytes() / sec_per_step / 1e9
+
+    def dominant(self, per_key_ms):
+        tot_ms = sum(per_key_ms[M] for M in self.Ms)
+        ach = self.alg_bytes() / (tot_ms * 1e-3) / 1e9
+        return dict(bound="hbm", achieved=ach, peak=PEAK_HBM_GBS, unit="GB/s", frac=ach / PEAK_HBM_GBS)
+
+    def config(self):
+        return {"workload": "w4a16", "M": list(self.Ms), "K": self.K, "N": self.N,
+                "weight": "BF16 N(0,1) x per-row U[0.005, 0.05] -> INT4 per 32 input channels, "
+                          "BF16 scale = amax / 7", "copies": self.copies}
+
+    def cpu_baseline(self, budget_s):
+        import numpy as np
+
+        import oracle as O
+        import synth
+        d = synth.decode(seed=0)
+        r = np.random.default_rng([0, 44])
+        wf = r.standard_normal((self.N, self.K)).astype(np.float32) * \
+            r.uniform(0.005, 0.05, (self.N, 1)).astype(np.float32)
+        q, s = O.w4a16.w4_quant(synth.to_bf16_bits(wf))
+        t0 = time.perf_counter()
+        n = 0
+        while time.perf_counter() - t0 < budget_s:
+            for M in self.Ms:
+                O.w4a16.w4a16_linear_ref64(d.x[:M], q, s)
+            n += 1
+        dt = (time.perf_counter() - t0) / n
+        return dict(value=self.alg_bytes() / dt / 1e9, unit="GB/s",
+                    sample=f"oracle dequantization + float64 product of the 4 decode linears, "
+                           f"{n} whole steps (weight quantized outside the timing)")
+
+
 class MxWorkload(Workload):
     def __init__(self, w, torch):
         super().__init__(w, torch)
@@ -896,6 +988,8 @@ def main():
         wl = MoeLayerWorkload(w, torch)
     elif args.workload == "mx_moe":
         wl = MxMoeWorkload(w, torch)
+    elif args.workload == "w4a16":
+        wl = W4Workload(w, torch)
     else:
         wl = MoeWorkload(w, torch)
 
@@ -945,7 +1039,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8-e4m3 (MX)" if wl.name in ("mx", "mx_moe") else "int8",
+        "dtype": {"mx": "fp8-e4m3 (MX)", "mx_moe": "fp8-e4m3 (MX)",
+                  "w4a16": "bf16 (int4 weights)"}.get(wl.name, "int8"),
         "data": "synthetic (seeded numpy; see synth/)",
         "config": wl.config(),
         "roofline": {k: (round(v, 4) if isinstance(v, float) else v) for k, v in roof.items()},

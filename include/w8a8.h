@@ -417,6 +417,39 @@ int w8a8_static_linear(const int8_t* q, int64_t M, int64_t K, const void* w_pack
                        const float* deq_scale, const int32_t* quant_bias, int64_t N, void* y,
                        int out, void* stream);
 
+/*
+ * W4A16 weight variant.  [LOWBIT] = "超大 MoE 的低比特推理：INT4、FP4 与量化感知训练":
+ * the INT4 format with one BF16 scale per 32 weights ("4 比特对万亿 MoE 意味着
+ * 什么"), the symmetric per-32-input-channel quantizer of its QAT section
+ * (scale = group amax / 7, codes clamped to [-8, 7]), and the W4A16 kernel row
+ * of "不同硬件上的 kernel" (weights dequantized to BF16 in registers, BF16
+ * matrix units; decode, where reading the weights is the bound).
+ *
+ * w8a8_w4a16_quant_weight (load time): BF16 w [N, K] (K % 32 == 0, else
+ *   W8A8_ERR_UNSUPPORTED) -> per row and group of 32 along K:
+ *   s = BF16(fl32(amax / 7)) (round half to even), q = clamp(rint(fl32(w /
+ *   s)), -8, 7) against that stored scale; amax 0 gives s = 0 and q = 0.
+ *   Writes any of: q int8 [N, K], scale BF16 bits [N, K/32], packed (16-byte
+ *   aligned, w8a8_w4a16_packed_bytes(N, K) bytes); null outputs are skipped,
+ *   at least one must be given.
+ * w8a8_w4a16_pack: pre-quantized codes (int8, clamped to [-8, 7]) and BF16
+ *   scales -> the packed layout.
+ * w8a8_w4a16_linear: x BF16 [M, K] (16-byte aligned) -> y BF16 [M, N] =
+ *   BF16(sum_k x[m, k] * BF16(q * s)[n, k]): each weight dequantized once to
+ *   BF16 (round half to even of the exact q * s), exact BF16 products,
+ *   fp32 accumulation (not bit-exact against a float64 sum; no bias).
+ * Packed layout: per 16-column block and 128-deep k-chunk 1152 bytes (codes +
+ *   8 in nibbles in the BF16 MFMA's operand order, then the 16 x 4 BF16
+ *   scales); K padded to 128 with zero weights.
+ */
+int64_t w8a8_w4a16_packed_bytes(int64_t N, int64_t K);
+int w8a8_w4a16_quant_weight(const uint16_t* w, int64_t N, int64_t K, int8_t* q, uint16_t* scale,
+                            void* packed, void* stream);
+int w8a8_w4a16_pack(const int8_t* q, const uint16_t* scale, int64_t N, int64_t K, void* packed,
+                    void* stream);
+int w8a8_w4a16_linear(const uint16_t* x, int64_t M, int64_t K, const void* w_packed, int64_t N,
+                      uint16_t* y, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -56,6 +56,10 @@ __all__ = [
     "mx_grouped_gemm",
     "mx_moe_workspace_bytes",
     "mx_moe_grouped",
+    "w4a16_packed_bytes",
+    "w4a16_quant_weight",
+    "w4a16_pack",
+    "w4a16_linear",
     "mx_workspace_operands",
     "static_quant",
     "static_quant_packed",
@@ -133,6 +137,10 @@ def _load():
         "w8a8_mx_moe_workspace_bytes": (_c_i64, [_c_i64, _c_i64, _c_i64, _c_i64]),
         "w8a8_mx_moe_grouped": (ctypes.c_int, [_c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i64, _c_p,
                                                _c_p, ctypes.c_int, _c_p, _c_p, _c_i64, _c_p]),
+        "w8a8_w4a16_packed_bytes": (_c_i64, [_c_i64, _c_i64]),
+        "w8a8_w4a16_quant_weight": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p]),
+        "w8a8_w4a16_pack": (ctypes.c_int, [_c_p, _c_p, _c_i64, _c_i64, _c_p, _c_p]),
+        "w8a8_w4a16_linear": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_i64, _c_p, _c_p]),
         "w8a8_static_quant": (ctypes.c_int, [_c_p, _c_i64, _c_i64, ctypes.c_float, ctypes.c_float,
                                              _c_p, _c_p]),
         "w8a8_static_quant_packed": (ctypes.c_int, [_c_p, _c_i64, _c_i64, ctypes.c_float,
@@ -703,6 +711,57 @@ def mx_moe_grouped(x_rows: torch.Tensor, group_list: torch.Tensor, w13_packed: t
     ws, ws_n = _workspace(mx_moe_workspace_bytes(R, E, H, I), x_rows.device, workspace)
     _check(lib.w8a8_mx_moe_grouped(_ptr(x_rows), _ptr(group_list), R, E, H, I, _ptr(w13_packed),
                                    _ptr(w2_packed), scale_alg, _ptr(y), _ptr(ws), ws_n, _stream()))
+    return y
+
+
+# ---------------------------------------------------------------------------
+# W4A16 weight variant
+# ---------------------------------------------------------------------------
+
+def w4a16_packed_bytes(N: int, K: int) -> int:
+    return int(lib.w8a8_w4a16_packed_bytes(N, K))
+
+
+def w4a16_quant_weight(w: torch.Tensor, codes: bool = False, scales: bool = False,
+                       pack: bool = True):
+    """BF16 weight [N, K] -> (int8 codes [N, K] or None, BF16 scales [N, K/32] or
+    None, packed uint8 buffer or None): INT4 per 32 input channels, scale amax / 7."""
+    _need(w, torch.bfloat16, "w", 2)
+    N, K = w.shape
+    dev = w.device
+    q = torch.empty((N, K), dtype=torch.int8, device=dev) if codes else None
+    s = torch.empty((N, max(K // 32, 1)), dtype=torch.bfloat16, device=dev) if scales else None
+    p = torch.empty((w4a16_packed_bytes(N, K),), dtype=torch.uint8, device=dev) if pack else None
+    _check(lib.w8a8_w4a16_quant_weight(_ptr(w), N, K, _ptr(q), _ptr(s), _ptr(p), _stream()))
+    return q, s, p
+
+
+def w4a16_pack(q: torch.Tensor, s: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Pre-quantized int8 codes [N, K] in [-8, 7] and BF16 scales [N, K/32] -> packed."""
+    _need(q, torch.int8, "q", 2)
+    _need(s, torch.bfloat16, "s", 2)
+    N, K = q.shape
+    if tuple(s.shape) != (N, K // 32):
+        raise ValueError("scales must be [N, K/32]")
+    if out is None:
+        out = torch.empty((w4a16_packed_bytes(N, K),), dtype=torch.uint8, device=q.device)
+    _need(out, torch.uint8, "out", 1)
+    _check(lib.w8a8_w4a16_pack(_ptr(q), _ptr(s), N, K, _ptr(out), _stream()))
+    return out
+
+
+def w4a16_linear(x: torch.Tensor, w_packed: torch.Tensor, N: int,
+                 y: torch.Tensor | None = None) -> torch.Tensor:
+    """BF16 x [M, K] times the packed INT4 weight [N, K] -> BF16 [M, N]."""
+    _need(x, torch.bfloat16, "x", 2)
+    _need(w_packed, torch.uint8, "w_packed", 1)
+    M, K = x.shape
+    if w_packed.numel() < w4a16_packed_bytes(N, K):
+        raise ValueError("w_packed too small for [N, K]")
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    _need(y, torch.bfloat16, "y", 2)
+    _check(lib.w8a8_w4a16_linear(_ptr(x), M, K, _ptr(w_packed), N, _ptr(y), _stream()))
     return y
 
 

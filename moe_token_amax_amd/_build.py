@@ -14,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libw8a8.so")
-SOURCES = ["api.hip", "quant.hip", "prepack.hip", "gemm.hip", "mx.hip", "static.hip", "moe_io.hip"]
+SOURCES = ["api.hip", "quant.hip", "prepack.hip", "gemm.hip", "mx.hip", "static.hip", "moe_io.hip", "w4a16.hip"]
 ARCH = os.environ.get("W8A8_OFFLOAD_ARCH", "gfx950")
 
 FLAGS = [

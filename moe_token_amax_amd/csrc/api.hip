@@ -8,6 +8,7 @@
 #include "../../include/w8a8.h"
 #include "launch.hpp"
 #include "mx.hpp"
+#include "w4.hpp"
 
 namespace {
 
@@ -720,6 +721,61 @@ int w8a8_mx_moe_grouped(const uint16_t* x_rows, const int64_t* group_list, int64
   return launched(w8a8::launch_mx_grouped_gemm(pay, sc2, R, E, I, tiles, count, w2,
                                                w8a8_mx_packed_bytes(H, I), mx_payload_bytes(H, I), H, y, s),
                   "mx_moe_grouped: W2");
+}
+
+
+// ---------------------------------------------------------------------------
+// W4A16 weight variant
+// ---------------------------------------------------------------------------
+static int check_w4(const char* who, int64_t N, int64_t K) {
+  if (N < 1 || K < 1 || N >= kMaxDim || K > W8A8_MAX_K)
+    return fail(W8A8_ERR_SHAPE, "%s: need N >= 1 and 1 <= K <= %d", who, W8A8_MAX_K);
+  if (K % 32)
+    return fail(W8A8_ERR_UNSUPPORTED, "%s: K = %lld is not a multiple of the group size 32", who,
+                (long long)K);
+  return W8A8_OK;
+}
+
+int64_t w8a8_w4a16_packed_bytes(int64_t N, int64_t K) {
+  if (N < 1 || K < 1) return 0;
+  return w8a8::w4_packed_bytes(N, K);
+}
+
+int w8a8_w4a16_quant_weight(const uint16_t* w, int64_t N, int64_t K, int8_t* q, uint16_t* scale,
+                            void* packed, void* stream) {
+  int st = check_w4("w4a16_quant_weight", N, K);
+  if (st) return st;
+  if (!w || (!q && !scale && !packed)) return fail(W8A8_ERR_NULL, "w4a16_quant_weight: null pointer");
+  if (!aligned(w, 2) || (scale && !aligned(scale, 2)) || (packed && !aligned(packed, 16)))
+    return fail(W8A8_ERR_ALIGN, "w4a16_quant_weight: misaligned buffer");
+  return launched(w8a8::launch_w4_quant_pack(w, N, K, q, scale, reinterpret_cast<uint8_t*>(packed),
+                                             (hipStream_t)stream),
+                  "w4a16_quant_weight");
+}
+
+int w8a8_w4a16_pack(const int8_t* q, const uint16_t* scale, int64_t N, int64_t K, void* packed,
+                    void* stream) {
+  int st = check_w4("w4a16_pack", N, K);
+  if (st) return st;
+  if (!q || !scale || !packed) return fail(W8A8_ERR_NULL, "w4a16_pack: null pointer");
+  if (!aligned(scale, 2) || !aligned(packed, 16)) return fail(W8A8_ERR_ALIGN, "w4a16_pack: misaligned buffer");
+  return launched(w8a8::launch_w4_pack(q, scale, N, K, reinterpret_cast<uint8_t*>(packed),
+                                       (hipStream_t)stream),
+                  "w4a16_pack");
+}
+
+int w8a8_w4a16_linear(const uint16_t* x, int64_t M, int64_t K, const void* w_packed, int64_t N,
+                      uint16_t* y, void* stream) {
+  int st = check_w4("w4a16_linear", N, K);
+  if (st) return st;
+  if (M < 0 || M >= kMaxDim) return fail(W8A8_ERR_SHAPE, "w4a16_linear: bad M");
+  if (M == 0) return ok();
+  if (!x || !w_packed || !y) return fail(W8A8_ERR_NULL, "w4a16_linear: null pointer");
+  if (!aligned(x, 16) || !aligned(w_packed, 16) || !aligned(y, 2))
+    return fail(W8A8_ERR_ALIGN, "w4a16_linear: x and w_packed need 16-byte alignment");
+  return launched(w8a8::launch_w4a16_linear(x, M, K, reinterpret_cast<const uint8_t*>(w_packed), N, y,
+                                            (hipStream_t)stream),
+                  "w4a16_linear");
 }
 
 }  // extern "C"

@@ -1,0 +1,23 @@
+// Internal launchers of the W4A16 kernels (host side).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace w8a8 {
+
+// 128-deep k-chunks of the packed INT4 weight, and its bytes (1152 per
+// 16-column block and chunk)
+int64_t w4_chunks(int64_t K);
+int64_t w4_packed_bytes(int64_t N, int64_t K);
+// BF16 w [N, K] -> codes (int8, may be null), BF16 scales [N, K/32] (may be
+// null) and the packed layout (may be null)
+hipError_t launch_w4_quant_pack(const uint16_t* w, int64_t N, int64_t K, int8_t* q, uint16_t* s,
+                                uint8_t* packed, hipStream_t stream);
+hipError_t launch_w4_pack(const int8_t* q, const uint16_t* s, int64_t N, int64_t K, uint8_t* packed,
+                          hipStream_t stream);
+// y BF16 [M, N] = x BF16 [M, K] times the dequantized packed weight
+hipError_t launch_w4a16_linear(const uint16_t* x, int64_t M, int64_t K, const uint8_t* wp, int64_t N,
+                               uint16_t* y, hipStream_t stream);
+
+}  // namespace w8a8

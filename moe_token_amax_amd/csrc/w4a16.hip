@@ -1,0 +1,272 @@
+// W4A16 weight variant for gfx950 ("超大 MoE 的低比特推理：INT4、FP4 与量化感知训练":
+// the INT4 format with one BF16 scale per 32 weights; the quantizer of its QAT
+// section, symmetric, scale = group amax / 7, codes rounded and clamped to
+// [-8, 7]; the W4A16 kernel row of its kernel table: weights dequantized to
+// BF16 in registers, BF16 matrix units, a decode-bound use).
+//
+//  * quant (load time): per row, per 32 input channels: s = BF16(amax / 7),
+//    q = clamp(rint(w / s), -8, 7) against the stored scale (IEEE fp32
+//    division, ties to even); amax 0 gives s = 0, q = 0.
+//  * packed layout: per 16-column block and 128-deep k-chunk, 1152 bytes:
+//    1 KB of codes, lane l's 16 bytes holding column l % 16 and, for each of
+//    the chunk's four 32-deep steps j, k = 32 j + 8 (l / 16) + i (i = 0..7) as
+//    the nibbles of 32-bit word j (nibble i = bits 4i..4i+3, code + 8), then
+//    128 bytes of scales, BF16 [16 columns][4 groups]. K is padded to 128 with
+//    code 0 and scale 0; N to 16.
+//  * linear: y = BF16(sum_k x[m, k] * BF16(q * s)[n, k]) with the dequantized
+//    weight fed to v_mfma_f32_16x16x32_bf16 and fp32 accumulation.
+#include <algorithm>
+
+#include "device_common.hpp"
+#include "w4.hpp"
+
+namespace w8a8 {
+
+constexpr int kW4Group = 32, kW4Chunk = 128, kW4ChunkBytes = 1152;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------------------
+// quant + pack: one thread per (16-column block, k-chunk, lane): the lane's
+// column and 8 k per step, the group amax of its (column, step) over the 4
+// lanes l, l + 16, l + 32, l + 48 that share it
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void w4_quant_pack_kernel(const uint16_t* __restrict__ w, int64_t N,
+                                                            int64_t K, int64_t KC,
+                                                            int8_t* __restrict__ q_out,
+                                                            uint16_t* __restrict__ s_out,
+                                                            uint8_t* __restrict__ packed) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t NB = (N + 15) / 16;
+  const int lane = threadIdx.x & 63;
+  const int64_t unit = t >> 6;             // one wavefront per (block, chunk)
+  if (unit >= NB * KC) return;             // whole wavefront leaves together
+  const int64_t nb = unit / KC, kc = unit % KC;
+  const int64_t n = nb * 16 + (lane & 15);
+  uint32_t words[4];
+  uint16_t scales[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t k0 = kc * kW4Chunk + 32 * j + 8 * (lane >> 4);
+    const bool live = n < N && k0 < K;
+    float v[8];
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      v[i] = live ? bf16_to_f32(w[n * K + k0 + i]) : 0.f;
+      amax = fmaxf(amax, fabsf(v[i]));
+    }
+    // group of 32 = the 4 lanes of this column in this step (l, l^16, l^32, l^48)
+    amax = fmaxf(amax, __shfl_xor(amax, 16, kWave));
+    amax = fmaxf(amax, __shfl_xor(amax, 32, kWave));
+    const uint32_t sb = f32_to_bf16(amax / 7.0f);
+    const float s = bf16_to_f32(sb);
+    uint32_t word = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      int code = 0;
+      if (s > 0.f) code = (int)fminf(fmaxf(__builtin_rintf(v[i] / s), -8.f), 7.f);
+      if (q_out && live) q_out[n * K + k0 + i] = (int8_t)code;
+      word |= (uint32_t)(code + 8) << (4 * i);
+    }
+    words[j] = word;
+    scales[j] = (uint16_t)sb;
+    if (s_out && live && (lane >> 4) == 0) s_out[n * (K / kW4Group) + (k0 / kW4Group)] = (uint16_t)sb;
+  }
+  if (packed) {
+    uint8_t* base = packed + unit * kW4ChunkBytes;
+    reinterpret_cast<uint4*>(base)[lane] = uint4{words[0], words[1], words[2], words[3]};
+    if (lane < 16)
+      reinterpret_cast<uint2*>(base + 1024)[lane] =
+          uint2{scales[0] | ((uint32_t)scales[1] << 16), scales[2] | ((uint32_t)scales[3] << 16)};
+  }
+}
+
+// pack pre-quantized codes (int8 in [-8, 7]) and BF16 scales
+__global__ __launch_bounds__(256) void w4_pack_kernel(const int8_t* __restrict__ q,
+                                                      const uint16_t* __restrict__ s, int64_t N,
+                                                      int64_t K, int64_t KC,
+                                                      uint8_t* __restrict__ packed) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t NB = (N + 15) / 16;
+  const int lane = threadIdx.x & 63;
+  const int64_t unit = t >> 6;
+  if (unit >= NB * KC) return;
+  const int64_t nb = unit / KC, kc = unit % KC;
+  const int64_t n = nb * 16 + (lane & 15);
+  uint32_t words[4];
+  uint16_t scales[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t k0 = kc * kW4Chunk + 32 * j + 8 * (lane >> 4);
+    const bool live = n < N && k0 < K;
+    uint32_t word = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      int code = live ? (int)q[n * K + k0 + i] : 0;
+      code = code < -8 ? -8 : (code > 7 ? 7 : code);
+      word |= (uint32_t)(code + 8) << (4 * i);
+    }
+    words[j] = word;
+    scales[j] = live ? s[n * (K / kW4Group) + k0 / kW4Group] : (uint16_t)0;
+  }
+  uint8_t* base = packed + unit * kW4ChunkBytes;
+  reinterpret_cast<uint4*>(base)[lane] = uint4{words[0], words[1], words[2], words[3]};
+  if (lane < 16)
+    reinterpret_cast<uint2*>(base + 1024)[lane] =
+        uint2{scales[0] | ((uint32_t)scales[1] << 16), scales[2] | ((uint32_t)scales[3] << 16)};
+}
+
+// ---------------------------------------------------------------------------
+// decode linear: one workgroup per 16-column block and 16 MB rows, WAVES
+// wavefronts over interleaved k-chunks (UNR chunks of codes, scales and
+// activation fragments loaded before any of them is used), partial sums met
+// in LDS
+// ---------------------------------------------------------------------------
+
+// 8 BF16 weights of one step from a packed word and the group scale. The
+// nibbles are split into the bytes of two words (even and odd nibbles), each
+// byte converts to fp32 in one instruction, and fma(nibble, s, -8 s) is the
+// exact q * s (at most 12 significant bits: the fused operation does not
+// round); one RNE to BF16 per value.
+__device__ __forceinline__ bf16x8 w4_dequant8(uint32_t word, float s) {
+  uint32_t ev = word & 0x0F0F0F0Fu, od = (word >> 4) & 0x0F0F0F0Fu;
+  // keep the byte split: extracting each nibble from the word again costs a
+  // shift and a mask per value, each byte of ev / od converts in one instruction
+  asm volatile("" : "+v"(ev), "+v"(od));
+  const float ms = -8.0f * s;  // exact
+  uint32_t pk[4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const f32x2 v = {fmaf((float)((ev >> (8 * b)) & 0xFFu), s, ms),   // nibble 2b
+                     fmaf((float)((od >> (8 * b)) & 0xFFu), s, ms)};  // nibble 2b + 1
+    pk[b] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+  }
+  return __builtin_bit_cast(bf16x8, uint4{pk[0], pk[1], pk[2], pk[3]});
+}
+
+template <int MB, int UNR, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void w4a16_decode_kernel(const uint16_t* __restrict__ x,
+                                                                  int64_t M, int64_t K,
+                                                                  const uint8_t* __restrict__ wp,
+                                                                  int64_t KC, int64_t N,
+                                                                  uint16_t* __restrict__ y) {
+  __shared__ f32x4 part[WAVES][MB][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t nb = blockIdx.x;
+  const int64_t row0 = (int64_t)blockIdx.y * 16 * MB;
+  const uint8_t* wblk = wp + nb * KC * kW4ChunkBytes;
+  // A rows of this lane (row l % 16 of each 16-row block). Rows past M read
+  // row M - 1 instead: an MFMA output row depends on its own A row only, and
+  // those output rows are not stored.
+  const uint16_t* arow[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    const int64_t r = row0 + 16 * mb + (lane & 15);
+    arow[mb] = x + (r < M ? r : M - 1) * K + 8 * (lane >> 4);
+  }
+  f32x4 acc[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int64_t c0 = wave; c0 < KC; c0 += WAVES * UNR) {
+    // all loads of UNR chunks first (codes, scales and the activation
+    // fragments), then the dequantization and the MFMAs
+    uint4 codes[UNR];
+    uint2 sc[UNR];
+    bf16x8 a[UNR][4][MB];
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const int64_t kc = c0 + WAVES * u;
+      if (kc < KC) {
+        const uint8_t* ch = wblk + kc * kW4ChunkBytes;
+        codes[u] = reinterpret_cast<const uint4*>(ch)[lane];
+        sc[u] = reinterpret_cast<const uint2*>(ch + 1024)[lane & 15];
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t k = kc * kW4Chunk + 32 * j;
+        // k past K (the zero-weight padding of the last chunk): zeros, not reads
+        // past the row (wavefront-uniform)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+          a[u][j][mb] = (kc < KC && k < K) ? *reinterpret_cast<const bf16x8*>(arow[mb] + k) : bf16x8{};
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const int64_t kc = c0 + WAVES * u;
+      if (kc >= KC) break;
+      const uint32_t cw[4] = {codes[u].x, codes[u].y, codes[u].z, codes[u].w};
+      const float s[4] = {__uint_as_float(sc[u].x << 16), __uint_as_float(sc[u].x & 0xFFFF0000u),
+                          __uint_as_float(sc[u].y << 16), __uint_as_float(sc[u].y & 0xFFFF0000u)};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bf16x8 b = w4_dequant8(cw[j], s[j]);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+          acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u][j][mb], b, acc[mb], 0, 0, 0);
+      }
+    }
+  }
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) part[wave][mb][lane] = acc[mb];
+  __syncthreads();
+  // lane l holds rows 4 (l / 16) .. + 3 of column l % 16 in each 16-row block;
+  // wavefronts 0 .. MB - 1 sum the WAVES partials of block mb = wave in order
+  if (wave < MB) {
+    f32x4 s = part[0][wave][lane];
+#pragma unroll
+    for (int w = 1; w < WAVES; ++w) s = s + part[w][wave][lane];
+    const int64_t n = nb * 16 + (lane & 15);
+    if (n < N) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t m = row0 + 16 * wave + 4 * (lane >> 4) + i;
+        if (m < M) y[m * N + n] = (uint16_t)f32_to_bf16(s[i]);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+int64_t w4_chunks(int64_t K) { return (K + kW4Chunk - 1) / kW4Chunk; }
+int64_t w4_packed_bytes(int64_t N, int64_t K) { return (N + 15) / 16 * w4_chunks(K) * kW4ChunkBytes; }
+
+hipError_t launch_w4_quant_pack(const uint16_t* w, int64_t N, int64_t K, int8_t* q, uint16_t* s,
+                                uint8_t* packed, hipStream_t stream) {
+  const int64_t units = (N + 15) / 16 * w4_chunks(K);
+  if (units == 0) return hipSuccess;
+  hipLaunchKernelGGL(w4_quant_pack_kernel, dim3((unsigned)((units + 3) / 4)), dim3(256), 0, stream, w,
+                     N, K, w4_chunks(K), q, s, packed);
+  return hipGetLastError();
+}
+
+hipError_t launch_w4_pack(const int8_t* q, const uint16_t* s, int64_t N, int64_t K, uint8_t* packed,
+                          hipStream_t stream) {
+  const int64_t units = (N + 15) / 16 * w4_chunks(K);
+  if (units == 0) return hipSuccess;
+  hipLaunchKernelGGL(w4_pack_kernel, dim3((unsigned)((units + 3) / 4)), dim3(256), 0, stream, q, s, N,
+                     K, w4_chunks(K), packed);
+  return hipGetLastError();
+}
+
+hipError_t launch_w4a16_linear(const uint16_t* x, int64_t M, int64_t K, const uint8_t* wp, int64_t N,
+                               uint16_t* y, hipStream_t stream) {
+  if (M == 0) return hipSuccess;
+  const int64_t NB = (N + 15) / 16, KC = w4_chunks(K);
+  if (M <= 16) {
+    hipLaunchKernelGGL((w4a16_decode_kernel<1, 4, 16>), dim3((unsigned)NB, 1), dim3(1024), 0, stream, x, M,
+                       K, wp, KC, N, y);
+  } else {
+    hipLaunchKernelGGL((w4a16_decode_kernel<4, 2, 8>), dim3((unsigned)NB, (unsigned)((M + 63) / 64)),
+                       dim3(512), 0, stream, x, M, K, wp, KC, N, y);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace w8a8

@@ -1,0 +1,142 @@
+"""Parity of the W4A16 weight variant (through the C ABI) with the CPU oracle.
+
+Codes, BF16 scales and the packed layout are compared exactly. The linear
+multiplies exactly dequantized BF16 weights (BF16 x BF16 products are exact in
+fp32) and accumulates in fp32, so its BF16 output is compared with the float64
+sum under the BF16 bound max(2**-8 |ref|, 1e-5) plus an allowance for the fp32
+additions: LAMBDA * sqrt(K) * 2**-24 * sum_k |x w| (the probabilistic bound of
+Higham & Mary, 2019, for sums whose rounding errors are independent and of
+random sign, as with these inputs). Inputs are seeded; expected values come
+only from ``oracle``.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synth
+from tests.conftest import gpu_available
+from tests.gpu_util import bf16_dev, bf16_host, dev, host, show, sync
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
+
+W4 = O.w4a16
+LAMBDA = 6.0
+
+
+@pytest.fixture(scope="module")
+def w():
+    import moe_token_amax_amd as w
+    return w
+
+
+def _assert_eq(got, want, what):
+    got = np.asarray(got)
+    want = np.asarray(want)
+    assert got.shape == want.shape, (what, got.shape, want.shape)
+    bad = np.argwhere(got != want)
+    assert bad.size == 0, f"{what}: {len(bad)} mismatches, first at {bad[:5].tolist()}: " \
+                          f"got {got[tuple(bad[0])]} want {want[tuple(bad[0])]}"
+
+
+def _weight(N, K, seed):
+    r = np.random.default_rng([seed, 44])
+    w = r.standard_normal((N, K)).astype(np.float32) * r.uniform(0.005, 0.05, (N, 1)).astype(np.float32)
+    w[0, :32] = 0.0                          # an all-zero group
+    return O.f32_to_bf16(w)
+
+
+def _unpack(buf, N, K):
+    """Test-side inverse of the packed layout: codes [N, K] and BF16 scale bits
+    [N, K/32] from the 1152-byte (16 columns x 128 k) chunks."""
+    NB, KC = -(-N // 16), -(-K // 128)
+    b = np.asarray(buf, np.uint8)[:NB * KC * 1152].reshape(NB, KC, 1152)
+    codes = b[:, :, :1024].reshape(NB, KC, 4, 16, 4, 4)      # [nb][kc][l/16][col][step][byte]
+    lo = (codes & 0xF).astype(np.int16) - 8
+    hi = (codes >> 4).astype(np.int16) - 8
+    nib = np.stack([lo, hi], axis=-1).reshape(NB, KC, 4, 16, 4, 8)   # ...[step][i]
+    # k = 128 kc + 32 step + 8 (l / 16) + i
+    q = nib.transpose(0, 3, 1, 4, 2, 5).reshape(NB * 16, KC * 128)[:N, :K].astype(np.int8)
+    sc = b[:, :, 1024:].view(np.uint16).reshape(NB, KC, 16, 4)        # [nb][kc][col][step]
+    s = sc.transpose(0, 2, 1, 3).reshape(NB * 16, KC * 4)[:N, :K // 32]
+    return q, s
+
+
+@pytest.mark.parametrize("N,K", [(64, 128), (50, 96), (33, 32), (4096, 7168), (160, 2080)])
+def test_w4_quant_and_pack_bit_exact(w, N, K):
+    show(f"w4a16_quant_weight N={N} K={K}")
+    wb = _weight(N, K, seed=N + K)
+    q, s, p = w.w4a16_quant_weight(bf16_dev(wb), codes=True, scales=True, pack=True)
+    p2 = w.w4a16_pack(q, s)
+    sync()
+    q_o, s_o = W4.w4_quant(wb)
+    _assert_eq(host(q), q_o, "codes")
+    _assert_eq(host(s.view(torch.int16)).view(np.uint16), s_o, "scales")
+    qu, su = _unpack(host(p), N, K)
+    _assert_eq(qu, q_o, "packed codes")
+    _assert_eq(su, s_o, "packed scales")
+    _assert_eq(host(p2), host(p), "pack of the codes == quant's packing")
+
+
+def _check_linear(y_bits, x_bits, q, s):
+    ref = W4.w4a16_linear_ref64(x_bits, q, s)
+    xf = O.bf16_to_f32(x_bits).astype(np.float64)
+    wf = O.bf16_to_f32(W4.w4_dequant(q, s)).astype(np.float64)
+    mag = np.abs(xf) @ np.abs(wf).T
+    allow = LAMBDA * np.sqrt(xf.shape[1]) * 2.0 ** -24 * mag
+    y = O.bf16_to_f32(y_bits).astype(np.float64)
+    err = np.abs(y - ref)
+    base = np.maximum(O.REL_TOL * np.abs(ref), O.ABS_FLOOR)
+    ok = err <= base + allow
+    plain = float(np.mean(err <= base))
+    show(f"  max|err| {err.max():.3e}, within the BF16 bound alone {plain:.5f}")
+    if not ok.all():
+        i = tuple(np.argwhere(~ok)[0])
+        raise AssertionError(f"{int((~ok).sum())} of {ok.size} outside tolerance, first {i}: "
+                             f"got {y[i]} want {ref[i]} allowance {allow[i]}")
+    assert plain >= 0.99
+
+
+# (M, K, N): decode rows 1 / 4 / 16 / 64, rows past a 16- and a 64-row block,
+# K not a multiple of 128, N not a multiple of 16
+LINEAR_CASES = [(1, 256, 64), (4, 1024, 96), (16, 512, 50), (17, 320, 64), (64, 2048, 512),
+                (100, 2048, 256), (3, 96, 40), (1, 7168, 4096)]
+
+
+@pytest.mark.parametrize("M,K,N", LINEAR_CASES)
+def test_w4a16_linear_within_tolerance(w, M, K, N):
+    show(f"w4a16_linear M={M} K={K} N={N}")
+    x = synth.activations(M, K, 0.005, seed=M + K + N)
+    wb = _weight(N, K, seed=K + N)
+    _, _, p = w.w4a16_quant_weight(bf16_dev(wb))
+    y = w.w4a16_linear(bf16_dev(x), p, N)
+    sync()
+    q_o, s_o = W4.w4_quant(wb)
+    _check_linear(bf16_host(y), x, q_o, s_o)
+
+
+@pytest.mark.timeout(300)
+def test_w4a16_decode_config(w):
+    """The decode-shaped linear in full: X BF16 [M in 1, 4, 16, 64, K = 7168]
+    (0.5 % x20 outliers), the weight [4096, 7168] quantized to INT4 per 32."""
+    d = synth.decode(seed=0)
+    K, N = d.x.shape[1], 4096
+    wb = _weight(N, K, seed=0)
+    _, _, p = w.w4a16_quant_weight(bf16_dev(wb))
+    q_o, s_o = W4.w4_quant(wb)
+    for M in (1, 4, 16, 64):
+        show(f"w4a16 decode config M={M}")
+        y = w.w4a16_linear(bf16_dev(d.x[:M]), p, N)
+        sync()
+        _check_linear(bf16_host(y), d.x[:M], q_o, s_o)
+
+
+def test_w4a16_zero_rows(w):
+    _, _, p = w.w4a16_quant_weight(bf16_dev(_weight(32, 64, 1)))
+    y = w.w4a16_linear(torch.empty((0, 64), dtype=torch.bfloat16, device="cuda"), p, 32)
+    sync()
+    assert y.shape == (0, 32)

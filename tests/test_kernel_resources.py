@@ -17,7 +17,7 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "moe_token_amax_amd", "csrc")
 MAX_SCRATCH = 128  # bytes per lane
-SOURCES = ["quant.hip", "prepack.hip", "gemm.hip", "mx.hip", "static.hip", "moe_io.hip"]
+SOURCES = ["quant.hip", "prepack.hip", "gemm.hip", "mx.hip", "static.hip", "moe_io.hip", "w4a16.hip"]
 
 
 def _hipcc():

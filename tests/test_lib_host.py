@@ -197,3 +197,21 @@ def test_mx_moe_validation_before_launch(w):
     assert L.w8a8_mx_swiglu_quant(p, 4, 48, 0, p, p, None) == 4                            # I % 32
     assert L.w8a8_mx_swiglu_quant(ctypes.c_void_p(264), 4, 64, 0, p, p, None) == 3
     assert L.w8a8_mx_swiglu_quant(None, 0, 64, 0, None, None, None) == 0
+
+
+def test_w4a16_validation_before_launch(w):
+    L = w.lib
+    p = ctypes.c_void_p(256)  # never dereferenced: validation fails first
+    # 1152 bytes per 16 columns and 128-deep chunk; K padded to 128, N to 16
+    assert L.w8a8_w4a16_packed_bytes(4096, 7168) == 256 * 56 * 1152
+    assert L.w8a8_w4a16_packed_bytes(17, 160) == 2 * 2 * 1152
+    assert L.w8a8_w4a16_quant_weight(p, 16, 100, p, p, p, None) == 4          # K % 32
+    assert L.w8a8_w4a16_quant_weight(p, 0, 64, p, p, p, None) == 2
+    assert L.w8a8_w4a16_quant_weight(p, 16, 64, None, None, None, None) == 1   # no output
+    assert L.w8a8_w4a16_quant_weight(p, 16, 64, None, None, ctypes.c_void_p(264), None) == 3
+    assert L.w8a8_w4a16_pack(p, None, 16, 64, p, None) == 1
+    assert L.w8a8_w4a16_pack(p, p, 16, 48, p, None) == 4
+    assert L.w8a8_w4a16_linear(ctypes.c_void_p(264), 4, 64, p, 16, p, None) == 3
+    assert L.w8a8_w4a16_linear(p, 4, 64, None, 16, p, None) == 1
+    assert L.w8a8_w4a16_linear(None, 0, 64, None, 16, None, None) == 0         # M == 0
+    assert L.w8a8_w4a16_linear(p, -1, 64, p, 16, p, None) == 2
