@@ -263,8 +263,8 @@ hipError_t launch_w4a16_linear(const uint16_t* x, int64_t M, int64_t K, const ui
     hipLaunchKernelGGL((w4a16_decode_kernel<1, 4, 16>), dim3((unsigned)NB, 1), dim3(1024), 0, stream, x, M,
                        K, wp, KC, N, y);
   } else {
-    hipLaunchKernelGGL((w4a16_decode_kernel<4, 2, 8>), dim3((unsigned)NB, (unsigned)((M + 63) / 64)),
-                       dim3(512), 0, stream, x, M, K, wp, KC, N, y);
+    hipLaunchKernelGGL((w4a16_decode_kernel<4, 1, 16>), dim3((unsigned)NB, (unsigned)((M + 63) / 64)),
+                       dim3(1024), 0, stream, x, M, K, wp, KC, N, y);
   }
   return hipGetLastError();
 }
