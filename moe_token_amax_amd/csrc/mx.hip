@@ -8,7 +8,8 @@
 //
 // Formats: E4M3 = OCP E4M3FN (bias 7, largest finite 448, no infinities);
 // E8M0 byte b = 2^(b - 127). Encoding rounds to nearest, ties to the even
-// code, keeps subnormals, saturates to 448 and keeps the sign of zero. The
+// code, keeps subnormals, saturates to 448 and keeps the sign of zero (a clamp
+// to +-448, then the hardware conversion v_cvt_pk_fp8_f32). The
 // shared exponent of a group of 32 is floor(log2(amax)) - 8 (scale rule 0) or
 // the smallest E with amax / 2^E <= 448 (scale rule 1), clamped to
 // [-127, 127]; amax == 0 gives byte 0.
@@ -38,23 +39,6 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
   const uint32_t e = (b >> 3) & 15u, m = b & 7u;
   float v = e ? __builtin_ldexpf((float)(8u + m), (int)e - 10) : __builtin_ldexpf((float)m, -9);
   return (b & 0x80u) ? -v : v;
-}
-
-// |v| < 2^9 expected (the group scaling guarantees it); larger saturates.
-__device__ __forceinline__ uint32_t f32_to_e4m3(float v) {
-  const uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
-  const float a = fabsf(v);
-  uint32_t code;
-  if (a >= 448.0f) {
-    code = 0x7Eu;
-  } else if (a < 0.015625f) {                 // below 2^-6: subnormal grid of 2^-9
-    code = (uint32_t)__builtin_rintf(a * 512.0f);  // 0..8 (8 = smallest normal)
-  } else {
-    const int e = __builtin_amdgcn_frexp_expf(a) - 1;                // floor(log2 a), -6..8
-    const uint32_t m = (uint32_t)__builtin_rintf(__builtin_ldexpf(a, 3 - e));  // 8..16
-    code = (uint32_t)(e + 7) * 8u + (m - 8u);  // m == 16 carries into the exponent
-  }
-  return code | sign;
 }
 
 // shared exponent of a group (without the +127 bias)
@@ -140,15 +124,25 @@ __device__ __forceinline__ uint32_t mx_quad_amax(const uint32_t (&w)[4]) {
   return amax;
 }
 
+// 8 E4M3 codes of the BF16 values w scaled by 2^-e: the exact power-of-two
+// scaling, a clamp to [-448, 448] (the saturation rule: an encoder input is
+// then never past the largest finite code) and the hardware's round-to-
+// nearest-even conversion, two values per instruction (subnormals and the sign
+// of zero kept; the bit-exact MX tests pin it against the encoding rules).
+__device__ __forceinline__ float mx_scaled(uint32_t bf16_bits, int e) {
+  return fminf(fmaxf(__builtin_ldexpf(bf16_to_f32(bf16_bits), -e), -448.0f), 448.0f);
+}
+
 __device__ __forceinline__ uint2 mx_codes8(const uint32_t (&w)[4], int e) {
-  uint32_t b[8];
+  uint32_t o[2];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    b[2 * j] = f32_to_e4m3(__builtin_ldexpf(bf16_to_f32(w[j] & 0xFFFFu), -e));
-    b[2 * j + 1] = f32_to_e4m3(__builtin_ldexpf(bf16_to_f32(w[j] >> 16), -e));
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t a = w[2 * h], b = w[2 * h + 1];
+    int v = __builtin_amdgcn_cvt_pk_fp8_f32(mx_scaled(a & 0xFFFFu, e), mx_scaled(a >> 16, e), 0, false);
+    v = __builtin_amdgcn_cvt_pk_fp8_f32(mx_scaled(b & 0xFFFFu, e), mx_scaled(b >> 16, e), v, true);
+    o[h] = (uint32_t)v;
   }
-  return uint2{b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24),
-               b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24)};
+  return uint2{o[0], o[1]};
 }
 
 // stores of chunk c (8 codes) of row `row` and, on the first lane of the
