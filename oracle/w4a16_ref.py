@@ -24,10 +24,22 @@ Readings (the page gives the recipe, not the rounding of a stored format):
     (float64 here; the GPU accumulates the exact BF16 products in fp32 and is
     compared within a derived tolerance); no bias.
 
-Parity status (tests/test_oracle_w4a16_pins.py): the quantizer pinned by hand
-groups (exact scales, ties to even, the clamp, a BF16-rounded scale, the zero
-group), by exact-rational recomputation and by the half-step error bound; the
-dequantization by exact recomputation; the linear by brute force.
+FP4 weights (the same W4A16 row lists "INT4 / FP4"; MXFP4 = one E8M0 scale
+per 32 values, 0.5 + 1/32 bytes per parameter): E2M1 values (1 sign, 2
+exponent bits with bias 1, 1 mantissa bit: magnitudes 0, 0.5, 1, 1.5, 2, 3,
+4, 6). Readings, as for the MXFP8 variant's rule 0: the shared exponent of a
+group of 32 along K is E = floor(log2 amax) - 2 (2 is E2M1's largest
+exponent), clamped to [-127, 127], byte E + 127; amax 0 gives byte 0 and zero
+codes; each value w / 2^E (exact) is encoded to the nearest E2M1 value, ties
+to the even code, saturating at 6, the sign kept (-0 is code 8). The
+dequantized weight 2^E * value is exact in BF16.
+
+Parity status (tests/test_oracle_w4a16_pins.py): the INT4 quantizer pinned by
+hand groups (exact scales, ties to even, the clamp, a BF16-rounded scale, the
+zero group), by exact-rational recomputation and by the half-step error bound;
+the dequantization by exact recomputation; the linear by brute force. The FP4
+quantizer by hand groups (every tie), an exhaustive nearest-value search and
+the half-step bound; its dequantization and linear by brute force.
 """
 
 from __future__ import annotations
@@ -36,7 +48,8 @@ import numpy as np
 
 from .w8a8_ref import bf16_to_f32, f32_to_bf16
 
-__all__ = ["W4_GROUP", "w4_quant", "w4_dequant", "w4a16_linear_ref64"]
+__all__ = ["W4_GROUP", "w4_quant", "w4_dequant", "w4a16_linear_ref64", "E2M1_VALUES", "fp4_quant",
+           "fp4_dequant", "fp4_linear_ref64"]
 
 W4_GROUP = 32
 
@@ -72,4 +85,57 @@ def w4a16_linear_ref64(x_bits, q, s_bits):
     """float64 sum over k of x[m, k] * BF16(q * s)[n, k]."""
     x = bf16_to_f32(x_bits).astype(np.float64)
     w = bf16_to_f32(w4_dequant(q, s_bits)).astype(np.float64)
+    return x @ w.T
+
+
+# E2M1 magnitudes by code (bits e1 e0 m): exponent field 0 is subnormal (m * 0.5)
+E2M1_VALUES = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+
+def _e2m1_encode(t):
+    """float64 values -> E2M1 codes (uint8 0..15): nearest magnitude, ties to the
+    even code, saturating at 6, sign bit 8."""
+    t = np.asarray(t, np.float64)
+    a = np.minimum(np.abs(t), 6.0)
+    d = np.abs(a[..., None] - E2M1_VALUES)            # distance to every magnitude
+    best = d.min(axis=-1, keepdims=True)
+    tie = d == best
+    # among the nearest, the even code (mantissa bit 0) when there are two
+    idx = np.arange(8)
+    even_pick = np.where(tie & (idx % 2 == 0), idx, 99).min(axis=-1)
+    any_pick = np.where(tie, idx, 99).min(axis=-1)
+    code = np.where(tie.sum(axis=-1) > 1, even_pick, any_pick)
+    return (code + 8 * np.signbit(t)).astype(np.uint8)
+
+
+def fp4_quant(w_bits):
+    """BF16 weight [N, K] (K % 32 == 0) -> (E2M1 codes uint8 [N, K], E8M0 scale
+    bytes uint8 [N, K / 32])."""
+    w = bf16_to_f32(w_bits).astype(np.float64)
+    N, K = w.shape
+    if K % W4_GROUP:
+        raise ValueError("K must be a multiple of 32")
+    g = w.reshape(N, K // W4_GROUP, W4_GROUP)
+    amax = np.max(np.abs(g), axis=2)
+    _, ex = np.frexp(amax)                            # amax = f * 2**ex, f in [0.5, 1)
+    e = np.clip(ex.astype(np.int64) - 1 - 2, -127, 127)
+    codes = _e2m1_encode(np.ldexp(g, -e[:, :, None]))
+    codes = np.where((amax > 0)[:, :, None], codes, codes & 8)   # zero groups: signed zeros
+    scales = np.where(amax > 0, e + 127, 0).astype(np.uint8)
+    return codes.reshape(N, K), scales
+
+
+def fp4_dequant(codes, scales):
+    """BF16 bits of the exact values 2^(scale - 127) * E2M1(code)."""
+    c = np.asarray(codes, np.uint8)
+    N, K = c.shape
+    mag = E2M1_VALUES[c & 7] * np.where(c & 8, -1.0, 1.0)
+    v = mag.reshape(N, K // W4_GROUP, W4_GROUP) * np.ldexp(1.0, scales.astype(np.int64) - 127)[:, :, None]
+    return f32_to_bf16(v.reshape(N, K).astype(np.float32))
+
+
+def fp4_linear_ref64(x_bits, codes, scales):
+    """float64 sum over k of x[m, k] * dequantized FP4 weight[n, k]."""
+    x = bf16_to_f32(x_bits).astype(np.float64)
+    w = bf16_to_f32(fp4_dequant(codes, scales)).astype(np.float64)
     return x @ w.T

@@ -2,9 +2,11 @@
 (exact and BF16-rounded scales, ties to even, the zero group), exact-rational
 recomputation of the quantizer and the dequantization, the half-step error
 bound, the page's recipe itself where the scale is exactly representable, and
-a brute-force product. A slip such as amax / 8, a truncating round, the fp32
-scale instead of the stored BF16 one, groups along N, or a dropped scale
-fails one of them.
+a brute-force product; for the FP4 (E2M1 + E8M0) weights, hand groups with
+every tie and the saturation, an independent nearest-value search, the error
+bound and a brute-force product. A slip such as amax / 8, a truncating
+round, the fp32 scale instead of the stored BF16 one, groups along N, a
+dropped scale, emax 3 instead of 2 or ties away from zero fails one of them.
 """
 
 from __future__ import annotations
@@ -136,3 +138,69 @@ def test_linear_brute_force():
                                                                 np.float32)))[0])
                 acc += float(xf[m, k]) * wq
             assert ref[m, n] == acc or abs(ref[m, n] - acc) <= 1e-12 * abs(acc)
+
+
+# ---------------------------------------------------------------------------
+# FP4 (E2M1 + E8M0 per 32) weights
+# ---------------------------------------------------------------------------
+
+def test_fp4_hand_group():
+    # amax 6 -> E = floor(log2 6) - 2 = 0 (byte 127): the values themselves are
+    # encoded; 0.25 / 0.75 / 1.25 / 1.75 / 2.5 / 3.5 / 5 are ties and go to the
+    # even codes 0 (0), 2 (1.0), 2 (1.0), 4 (2.0), 4 (2.0), 6 (4.0), 6 (4.0);
+    # -0.0 keeps its sign (code 8); 0.3 -> 0.5 (code 1); -6 -> code 15
+    w = _group([6.0, -6.0, 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, -0.0, 0.3])
+    c, s = W4.fp4_quant(w)
+    assert s.tolist() == [[127]]
+    assert c[0, :11].tolist() == [7, 15, 0, 2, 2, 4, 4, 6, 6, 8, 1]
+    # amax 1 -> E = -2 (byte 125): 1.0 / 2^-2 = 4 -> code 6; 0.375 -> 1.5 ->
+    # code 3; -0.125 -> -0.5 -> code 1 + 8
+    c, s = W4.fp4_quant(_group([1.0, 0.375, -0.125]))
+    assert s.tolist() == [[125]] and c[0, :3].tolist() == [6, 3, 9]
+    # amax 7 -> E = 0: 7 saturates to 6 (code 7); a zero group gets byte 0
+    c, s = W4.fp4_quant(np.concatenate([_group([7.0]), _group([0.0])], axis=1))
+    assert s.tolist() == [[127, 0]] and c[0, 0] == 7 and not c[0, 32:].any()
+
+
+def test_fp4_exhaustive_nearest_and_bound():
+    rng = np.random.default_rng(6)
+    N, K = 5, 128
+    w = (rng.standard_normal((N, K)) * np.exp(rng.uniform(-6, 3, (N, 1)))).astype(np.float32)
+    wb = O.f32_to_bf16(w)
+    c, s = W4.fp4_quant(wb)
+    wf = O.bf16_to_f32(wb).astype(np.float64)
+    mags = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    for n in range(N):
+        for g in range(K // 32):
+            grp = wf[n, 32 * g:32 * g + 32]
+            amax = float(np.max(np.abs(grp)))
+            e = int(np.floor(np.log2(amax))) - 2
+            assert s[n, g] == e + 127
+            for j, v in enumerate(grp):
+                t = min(abs(v) / 2.0 ** e, 6.0)
+                dist = [abs(t - m) for m in mags]
+                best = min(dist)
+                cands = [i for i in range(8) if dist[i] == best]
+                code = cands[0] if len(cands) == 1 else [i for i in cands if i % 2 == 0][0]
+                code += 8 if np.signbit(v) else 0
+                assert c[n, 32 * g + j] == code, (n, g, j, v)
+    d = O.bf16_to_f32(W4.fp4_dequant(c, s)).astype(np.float64)
+    step = np.repeat(2.0 ** (s.astype(np.float64) - 127), 32, axis=1)
+    assert np.all(np.abs(d - wf) <= 0.25 * np.abs(wf) + 0.25 * step)
+
+
+def test_fp4_linear_brute_force():
+    rng = np.random.default_rng(7)
+    M, N, K = 2, 3, 64
+    x = O.f32_to_bf16(rng.standard_normal((M, K)).astype(np.float32))
+    c, s = W4.fp4_quant(O.f32_to_bf16((rng.standard_normal((N, K)) * 0.02).astype(np.float32)))
+    ref = W4.fp4_linear_ref64(x, c, s)
+    xf = O.bf16_to_f32(x)
+    mags = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    for m in range(M):
+        for n in range(N):
+            acc = 0.0
+            for k in range(K):
+                v = mags[c[n, k] & 7] * (-1.0 if c[n, k] & 8 else 1.0) * 2.0 ** (int(s[n, k // 32]) - 127)
+                acc += float(xf[m, k]) * v
+            assert abs(ref[m, n] - acc) <= 1e-12 * abs(acc) + 1e-300
