@@ -57,7 +57,7 @@ def _args():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode",
                     choices=["decode", "prefill", "moe", "moe_layer", "tiny", "copy", "mx",
-                             "mx_moe", "static", "w4a16"])
+                             "mx_moe", "static", "w4a16", "fp4"])
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="approximate budget of the oracle timing on the host")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -607,15 +607,17 @@ class MxMoeWorkload(Workload):
 class W4Workload(Workload):
     """The decode-shaped linear with W4A16 weights: X BF16 [M, 7168] for M in 1,
     4, 16, 64 (0.5 % x20 outliers), the weight [4096, 7168] INT4 per 32 input
-    channels with BF16 scales, rotated over 32 packed copies (past the MALL)."""
+    channels with BF16 scales (fmt "int4") or FP4 E2M1 with an E8M0 scale per 32
+    (fmt "fp4"), rotated over 32 packed copies (past the MALL)."""
     Ms = (1, 4, 16, 64)
 
-    def __init__(self, w, torch):
+    def __init__(self, w, torch, fmt="int4"):
         super().__init__(w, torch)
         import numpy as np
 
         import synth
-        self.name = "w4a16"
+        self.fmt = fmt
+        self.name = "w4a16" if fmt == "int4" else "fp4"
         d = synth.decode(seed=0)
         self.K, self.N = d.x.shape[1], 4096
         dev = "cuda"
@@ -623,7 +625,8 @@ class W4Workload(Workload):
         wf = r.standard_normal((self.N, self.K)).astype(np.float32) * \
             r.uniform(0.005, 0.05, (self.N, 1)).astype(np.float32)
         wb = torch.from_numpy(synth.to_bf16_bits(wf).view(np.int16)).to(dev).view(torch.bfloat16)
-        _, _, packed = w.w4a16_quant_weight(wb)
+        quant = w.w4a16_quant_weight if fmt == "int4" else w.fp4_quant_weight
+        _, _, packed = quant(wb)
         del wb
         self.copies = 32
         self.wp = torch.empty((self.copies, packed.numel()), dtype=torch.uint8, device=dev)
@@ -640,7 +643,8 @@ class W4Workload(Workload):
         self.bound = "hbm"
 
     def _linear(self, M, c):
-        self.w.w4a16_linear(self.x[:M], self.wp[c], self.N, y=self.y[M])
+        lin = self.w.w4a16_linear if self.fmt == "int4" else self.w.fp4_linear
+        lin(self.x[:M], self.wp[c], self.N, y=self.y[M])
 
     def _make_step(self, copy_ids):
         def fn():
@@ -655,8 +659,10 @@ class W4Workload(Workload):
         return fn
 
     def gemm_bytes(self, M):
-        """One launch: INT4 codes (N K / 2) + BF16 scales (2 N K / 32), BF16 x in, BF16 y out."""
-        return self.N * self.K // 2 + 2 * self.N * self.K // 32 + 2 * M * self.K + 2 * M * self.N
+        """One launch: 4-bit codes (N K / 2) + scales (BF16: 2 N K / 32; E8M0:
+        N K / 32), BF16 x in, BF16 y out."""
+        sbytes = 2 if self.fmt == "int4" else 1
+        return self.N * self.K // 2 + sbytes * self.N * self.K // 32 + 2 * M * self.K + 2 * M * self.N
 
     def alg_bytes(self):
         return sum(self.gemm_bytes(M) for M in self.Ms)
@@ -670,9 +676,10 @@ class W4Workload(Workload):
         return dict(bound="hbm", achieved=ach, peak=PEAK_HBM_GBS, unit="GB/s", frac=ach / PEAK_HBM_GBS)
 
     def config(self):
-        return {"workload": "w4a16", "M": list(self.Ms), "K": self.K, "N": self.N,
-                "weight": "BF16 N(0,1) x per-row U[0.005, 0.05] -> INT4 per 32 input channels, "
-                          "BF16 scale = amax / 7", "copies": self.copies}
+        fmt = ("INT4 per 32 input channels, BF16 scale = amax / 7" if self.fmt == "int4" else
+               "FP4 E2M1 per 32 input channels, E8M0 scale 2^(floor(log2 amax) - 2)")
+        return {"workload": self.name, "M": list(self.Ms), "K": self.K, "N": self.N,
+                "weight": "BF16 N(0,1) x per-row U[0.005, 0.05] -> " + fmt, "copies": self.copies}
 
     def cpu_baseline(self, budget_s):
         import numpy as np
@@ -683,12 +690,17 @@ class W4Workload(Workload):
         r = np.random.default_rng([0, 44])
         wf = r.standard_normal((self.N, self.K)).astype(np.float32) * \
             r.uniform(0.005, 0.05, (self.N, 1)).astype(np.float32)
-        q, s = O.w4a16.w4_quant(synth.to_bf16_bits(wf))
+        if self.fmt == "int4":
+            q, s = O.w4a16.w4_quant(synth.to_bf16_bits(wf))
+            ref = O.w4a16.w4a16_linear_ref64
+        else:
+            q, s = O.w4a16.fp4_quant(synth.to_bf16_bits(wf))
+            ref = O.w4a16.fp4_linear_ref64
         t0 = time.perf_counter()
         n = 0
         while time.perf_counter() - t0 < budget_s:
             for M in self.Ms:
-                O.w4a16.w4a16_linear_ref64(d.x[:M], q, s)
+                ref(d.x[:M], q, s)
             n += 1
         dt = (time.perf_counter() - t0) / n
         return dict(value=self.alg_bytes() / dt / 1e9, unit="GB/s",
@@ -990,6 +1002,8 @@ def main():
         wl = MxMoeWorkload(w, torch)
     elif args.workload == "w4a16":
         wl = W4Workload(w, torch)
+    elif args.workload == "fp4":
+        wl = W4Workload(w, torch, fmt="fp4")
     else:
         wl = MoeWorkload(w, torch)
 
@@ -1040,7 +1054,7 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": {"mx": "fp8-e4m3 (MX)", "mx_moe": "fp8-e4m3 (MX)",
-                  "w4a16": "bf16 (int4 weights)"}.get(wl.name, "int8"),
+                  "w4a16": "bf16 (int4 weights)", "fp4": "bf16 (fp4 weights)"}.get(wl.name, "int8"),
         "data": "synthetic (seeded numpy; see synth/)",
         "config": wl.config(),
         "roofline": {k: (round(v, 4) if isinstance(v, float) else v) for k, v in roof.items()},

@@ -450,6 +450,28 @@ int w8a8_w4a16_pack(const int8_t* q, const uint16_t* scale, int64_t N, int64_t K
 int w8a8_w4a16_linear(const uint16_t* x, int64_t M, int64_t K, const void* w_packed, int64_t N,
                       uint16_t* y, void* stream);
 
+/*
+ * FP4 weights for the same W4A16 path ([LOWBIT]: the W4A16 row lists INT4 /
+ * FP4 weights; MXFP4 = E2M1 values with one E8M0 scale per 32, 0.5 + 1/32
+ * bytes per parameter).
+ * w8a8_fp4_quant_weight (load time): BF16 w [N, K] (K % 32 == 0) -> per row
+ *   and group of 32 along K: E = floor(log2 amax) - 2 (2 = E2M1's largest
+ *   exponent), clamped to [-127, 127], scale byte E + 127 (0 for an all-zero
+ *   group); each w / 2^E encoded to the nearest of 0, 0.5, 1, 1.5, 2, 3, 4, 6
+ *   (ties to the even code, saturating at 6), sign bit 8 (-0 kept). Writes any
+ *   of: codes uint8 [N, K] (0..15), scales uint8 [N, K/32], packed (16-byte
+ *   aligned, w8a8_w4a16_packed_bytes(N, K) bytes: the layout of
+ *   w8a8_w4a16_quant_weight with the codes as nibbles and the E8M0 bytes
+ *   [16 columns][4 groups] in the scale area).
+ * w8a8_fp4_linear: x BF16 [M, K] (16-byte aligned) -> y BF16 [M, N] =
+ *   BF16(sum_k x[m, k] * 2^E value[n, k]): the dequantized weights are exact
+ *   in BF16 (-0 becomes +0), products exact, fp32 accumulation.
+ */
+int w8a8_fp4_quant_weight(const uint16_t* w, int64_t N, int64_t K, uint8_t* codes, uint8_t* scales,
+                          void* packed, void* stream);
+int w8a8_fp4_linear(const uint16_t* x, int64_t M, int64_t K, const void* w_packed, int64_t N,
+                    uint16_t* y, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -60,6 +60,8 @@ __all__ = [
     "w4a16_quant_weight",
     "w4a16_pack",
     "w4a16_linear",
+    "fp4_quant_weight",
+    "fp4_linear",
     "mx_workspace_operands",
     "static_quant",
     "static_quant_packed",
@@ -141,6 +143,8 @@ def _load():
         "w8a8_w4a16_quant_weight": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p]),
         "w8a8_w4a16_pack": (ctypes.c_int, [_c_p, _c_p, _c_i64, _c_i64, _c_p, _c_p]),
         "w8a8_w4a16_linear": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_i64, _c_p, _c_p]),
+        "w8a8_fp4_quant_weight": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p]),
+        "w8a8_fp4_linear": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_i64, _c_p, _c_p]),
         "w8a8_static_quant": (ctypes.c_int, [_c_p, _c_i64, _c_i64, ctypes.c_float, ctypes.c_float,
                                              _c_p, _c_p]),
         "w8a8_static_quant_packed": (ctypes.c_int, [_c_p, _c_i64, _c_i64, ctypes.c_float,
@@ -762,6 +766,35 @@ def w4a16_linear(x: torch.Tensor, w_packed: torch.Tensor, N: int,
         y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
     _need(y, torch.bfloat16, "y", 2)
     _check(lib.w8a8_w4a16_linear(_ptr(x), M, K, _ptr(w_packed), N, _ptr(y), _stream()))
+    return y
+
+
+def fp4_quant_weight(w: torch.Tensor, codes: bool = False, scales: bool = False,
+                     pack: bool = True):
+    """BF16 weight [N, K] -> (E2M1 codes uint8 [N, K] or None, E8M0 bytes uint8
+    [N, K/32] or None, packed uint8 buffer or None): FP4 with one E8M0 scale per 32."""
+    _need(w, torch.bfloat16, "w", 2)
+    N, K = w.shape
+    dev = w.device
+    c = torch.empty((N, K), dtype=torch.uint8, device=dev) if codes else None
+    s = torch.empty((N, max(K // 32, 1)), dtype=torch.uint8, device=dev) if scales else None
+    p = torch.empty((w4a16_packed_bytes(N, K),), dtype=torch.uint8, device=dev) if pack else None
+    _check(lib.w8a8_fp4_quant_weight(_ptr(w), N, K, _ptr(c), _ptr(s), _ptr(p), _stream()))
+    return c, s, p
+
+
+def fp4_linear(x: torch.Tensor, w_packed: torch.Tensor, N: int,
+               y: torch.Tensor | None = None) -> torch.Tensor:
+    """BF16 x [M, K] times the packed FP4 weight [N, K] -> BF16 [M, N]."""
+    _need(x, torch.bfloat16, "x", 2)
+    _need(w_packed, torch.uint8, "w_packed", 1)
+    M, K = x.shape
+    if w_packed.numel() < w4a16_packed_bytes(N, K):
+        raise ValueError("w_packed too small for [N, K]")
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    _need(y, torch.bfloat16, "y", 2)
+    _check(lib.w8a8_fp4_linear(_ptr(x), M, K, _ptr(w_packed), N, _ptr(y), _stream()))
     return y
 
 

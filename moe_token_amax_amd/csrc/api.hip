@@ -764,6 +764,32 @@ int w8a8_w4a16_pack(const int8_t* q, const uint16_t* scale, int64_t N, int64_t K
                   "w4a16_pack");
 }
 
+int w8a8_fp4_quant_weight(const uint16_t* w, int64_t N, int64_t K, uint8_t* codes, uint8_t* scales,
+                          void* packed, void* stream) {
+  int st = check_w4("fp4_quant_weight", N, K);
+  if (st) return st;
+  if (!w || (!codes && !scales && !packed)) return fail(W8A8_ERR_NULL, "fp4_quant_weight: null pointer");
+  if (!aligned(w, 2) || (packed && !aligned(packed, 16)))
+    return fail(W8A8_ERR_ALIGN, "fp4_quant_weight: misaligned buffer");
+  return launched(w8a8::launch_fp4_quant_pack(w, N, K, codes, scales, reinterpret_cast<uint8_t*>(packed),
+                                              (hipStream_t)stream),
+                  "fp4_quant_weight");
+}
+
+int w8a8_fp4_linear(const uint16_t* x, int64_t M, int64_t K, const void* w_packed, int64_t N,
+                    uint16_t* y, void* stream) {
+  int st = check_w4("fp4_linear", N, K);
+  if (st) return st;
+  if (M < 0 || M >= kMaxDim) return fail(W8A8_ERR_SHAPE, "fp4_linear: bad M");
+  if (M == 0) return ok();
+  if (!x || !w_packed || !y) return fail(W8A8_ERR_NULL, "fp4_linear: null pointer");
+  if (!aligned(x, 16) || !aligned(w_packed, 16) || !aligned(y, 2))
+    return fail(W8A8_ERR_ALIGN, "fp4_linear: x and w_packed need 16-byte alignment");
+  return launched(w8a8::launch_fp4_linear(x, M, K, reinterpret_cast<const uint8_t*>(w_packed), N, y,
+                                          (hipStream_t)stream),
+                  "fp4_linear");
+}
+
 int w8a8_w4a16_linear(const uint16_t* x, int64_t M, int64_t K, const void* w_packed, int64_t N,
                       uint16_t* y, void* stream) {
   int st = check_w4("w4a16_linear", N, K);

@@ -15,6 +15,12 @@
 //    code 0 and scale 0; N to 16.
 //  * linear: y = BF16(sum_k x[m, k] * BF16(q * s)[n, k]) with the dequantized
 //    weight fed to v_mfma_f32_16x16x32_bf16 and fp32 accumulation.
+//  * FP4 weights (the same kernel row lists INT4 / FP4; MXFP4 = E2M1 values
+//    with one E8M0 scale per 32): E = floor(log2 amax) - 2 per group (2 is
+//    E2M1's largest exponent), each w / 2^E encoded to the nearest of 0, 0.5,
+//    1, 1.5, 2, 3, 4, 6 (ties to the even code, saturating at 6, sign bit 8);
+//    same packed layout with the codes as nibbles and E8M0 bytes [16][4] in
+//    the scale area; dequantization 2^E * value is exact in BF16.
 #include <algorithm>
 
 #include "device_common.hpp"
@@ -120,6 +126,66 @@ __global__ __launch_bounds__(256) void w4_pack_kernel(const int8_t* __restrict__
         uint2{scales[0] | ((uint32_t)scales[1] << 16), scales[2] | ((uint32_t)scales[3] << 16)};
 }
 
+// E2M1 code (0..15) of t = w / 2^E, exact comparisons: each count is a
+// half-way point, with the tie going to the even code
+__device__ __forceinline__ uint32_t e2m1_code(float t) {
+  const float a = fabsf(t);
+  uint32_t c = (a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) + (a > 2.5f) + (a >= 3.5f) +
+               (a > 5.0f);
+  return c | (__float_as_uint(t) >> 31 << 3);
+}
+
+// FP4 quant + pack: as w4_quant_pack_kernel, one wavefront per (block, chunk)
+__global__ __launch_bounds__(256) void fp4_quant_pack_kernel(const uint16_t* __restrict__ w, int64_t N,
+                                                             int64_t K, int64_t KC,
+                                                             uint8_t* __restrict__ c_out,
+                                                             uint8_t* __restrict__ s_out,
+                                                             uint8_t* __restrict__ packed) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t NB = (N + 15) / 16;
+  const int lane = threadIdx.x & 63;
+  const int64_t unit = t >> 6;
+  if (unit >= NB * KC) return;
+  const int64_t nb = unit / KC, kc = unit % KC;
+  const int64_t n = nb * 16 + (lane & 15);
+  uint32_t words[4], sbytes = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t k0 = kc * kW4Chunk + 32 * j + 8 * (lane >> 4);
+    const bool live = n < N && k0 < K;
+    float v[8];
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      v[i] = live ? bf16_to_f32(w[n * K + k0 + i]) : 0.f;
+      amax = fmaxf(amax, fabsf(v[i]));
+    }
+    amax = fmaxf(amax, __shfl_xor(amax, 16, kWave));
+    amax = fmaxf(amax, __shfl_xor(amax, 32, kWave));
+    int e = __builtin_amdgcn_frexp_expf(amax) - 1 - 2;  // floor(log2 amax) - 2
+    e = e < -127 ? -127 : (e > 127 ? 127 : e);
+    const uint32_t sb = amax > 0.f ? (uint32_t)(e + 127) : 0u;
+    uint32_t word = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      // a zero group: codes keep only the sign
+      const uint32_t code = amax > 0.f ? e2m1_code(__builtin_ldexpf(v[i], -e))
+                                       : (__float_as_uint(v[i]) >> 31 << 3);
+      if (c_out && live) c_out[n * K + k0 + i] = (uint8_t)code;
+      word |= code << (4 * i);
+    }
+    words[j] = word;
+    sbytes |= sb << (8 * j);
+    if (s_out && live && (lane >> 4) == 0) s_out[n * (K / kW4Group) + k0 / kW4Group] = (uint8_t)sb;
+  }
+  if (packed) {
+    uint8_t* base = packed + unit * kW4ChunkBytes;
+    reinterpret_cast<uint4*>(base)[lane] = uint4{words[0], words[1], words[2], words[3]};
+    if (lane < 16) reinterpret_cast<uint32_t*>(base + 1024)[lane] = sbytes;
+    else if (lane < 32) reinterpret_cast<uint32_t*>(base + 1024)[lane] = 0u;  // unused half
+  }
+}
+
 // ---------------------------------------------------------------------------
 // decode linear: one workgroup per 16-column block and 16 MB rows, WAVES
 // wavefronts over interleaved k-chunks (UNR chunks of codes, scales and
@@ -148,7 +214,34 @@ __device__ __forceinline__ bf16x8 w4_dequant8(uint32_t word, float s) {
   return __builtin_bit_cast(bf16x8, uint4{pk[0], pk[1], pk[2], pk[3]});
 }
 
-template <int MB, int UNR, int WAVES>
+// 8 BF16 weights of one step from 8 E2M1 codes and sc = 2^(E - 1): a byte
+// permute looks up t + 12 for each code (t = the signed value in units of
+// 0.5: 0, 1, 2, 3, 4, 6, 8, 12 for the magnitudes, negated for sign bit 8),
+// then fma(t + 12, sc, -12 sc) = value * 2^E exactly; the BF16 conversion
+// is exact (at most 2 significant bits). -0 comes out as +0.
+__device__ __forceinline__ uint32_t fp4_lut4(uint32_t x) {
+  const uint32_t mag = x & 0x07070707u;
+  const uint32_t neg = ((x >> 3) & 0x01010101u) * 0xFFu;               // 0xFF per negative byte
+  const uint32_t pos = __builtin_amdgcn_perm(0x18141210u, 0x0F0E0D0Cu, mag);  // 12 + t
+  const uint32_t ngv = __builtin_amdgcn_perm(0x00040608u, 0x090A0B0Cu, mag);  // 12 - t
+  return (ngv & neg) | (pos & ~neg);
+}
+
+__device__ __forceinline__ bf16x8 fp4_dequant8(uint32_t word, float sc) {
+  uint32_t ev = fp4_lut4(word & 0x0F0F0F0Fu), od = fp4_lut4((word >> 4) & 0x0F0F0F0Fu);
+  asm volatile("" : "+v"(ev), "+v"(od));
+  const float m12 = -12.0f * sc;  // exact
+  uint32_t pk[4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const f32x2 v = {fmaf((float)((ev >> (8 * b)) & 0xFFu), sc, m12),   // code 2b
+                     fmaf((float)((od >> (8 * b)) & 0xFFu), sc, m12)};  // code 2b + 1
+    pk[b] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+  }
+  return __builtin_bit_cast(bf16x8, uint4{pk[0], pk[1], pk[2], pk[3]});
+}
+
+template <int MB, int UNR, int WAVES, int FMT>
 __global__ __launch_bounds__(64 * WAVES) void w4a16_decode_kernel(const uint16_t* __restrict__ x,
                                                                   int64_t M, int64_t K,
                                                                   const uint8_t* __restrict__ wp,
@@ -175,7 +268,7 @@ __global__ __launch_bounds__(64 * WAVES) void w4a16_decode_kernel(const uint16_t
     // all loads of UNR chunks first (codes, scales and the activation
     // fragments), then the dequantization and the MFMAs
     uint4 codes[UNR];
-    uint2 sc[UNR];
+    uint2 sc[UNR];  // FMT 0: 4 BF16 scales; FMT 1: 4 E8M0 bytes in .x
     bf16x8 a[UNR][4][MB];
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
@@ -183,7 +276,8 @@ __global__ __launch_bounds__(64 * WAVES) void w4a16_decode_kernel(const uint16_t
       if (kc < KC) {
         const uint8_t* ch = wblk + kc * kW4ChunkBytes;
         codes[u] = reinterpret_cast<const uint4*>(ch)[lane];
-        sc[u] = reinterpret_cast<const uint2*>(ch + 1024)[lane & 15];
+        if (FMT == 0) sc[u] = reinterpret_cast<const uint2*>(ch + 1024)[lane & 15];
+        else sc[u].x = reinterpret_cast<const uint32_t*>(ch + 1024)[lane & 15];
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -200,11 +294,20 @@ __global__ __launch_bounds__(64 * WAVES) void w4a16_decode_kernel(const uint16_t
       const int64_t kc = c0 + WAVES * u;
       if (kc >= KC) break;
       const uint32_t cw[4] = {codes[u].x, codes[u].y, codes[u].z, codes[u].w};
-      const float s[4] = {__uint_as_float(sc[u].x << 16), __uint_as_float(sc[u].x & 0xFFFF0000u),
-                          __uint_as_float(sc[u].y << 16), __uint_as_float(sc[u].y & 0xFFFF0000u)};
+      float s[4];
+      if (FMT == 0) {
+        s[0] = __uint_as_float(sc[u].x << 16);
+        s[1] = __uint_as_float(sc[u].x & 0xFFFF0000u);
+        s[2] = __uint_as_float(sc[u].y << 16);
+        s[3] = __uint_as_float(sc[u].y & 0xFFFF0000u);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)  // 2^(E - 1) = 2^(byte - 128)
+          s[j] = __builtin_ldexpf(1.0f, (int)((sc[u].x >> (8 * j)) & 0xFFu) - 128);
+      }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const bf16x8 b = w4_dequant8(cw[j], s[j]);
+        const bf16x8 b = FMT == 0 ? w4_dequant8(cw[j], s[j]) : fp4_dequant8(cw[j], s[j]);
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
           acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u][j][mb], b, acc[mb], 0, 0, 0);
@@ -255,18 +358,38 @@ hipError_t launch_w4_pack(const int8_t* q, const uint16_t* s, int64_t N, int64_t
   return hipGetLastError();
 }
 
-hipError_t launch_w4a16_linear(const uint16_t* x, int64_t M, int64_t K, const uint8_t* wp, int64_t N,
-                               uint16_t* y, hipStream_t stream) {
+hipError_t launch_fp4_quant_pack(const uint16_t* w, int64_t N, int64_t K, uint8_t* c, uint8_t* s,
+                                 uint8_t* packed, hipStream_t stream) {
+  const int64_t units = (N + 15) / 16 * w4_chunks(K);
+  if (units == 0) return hipSuccess;
+  hipLaunchKernelGGL(fp4_quant_pack_kernel, dim3((unsigned)((units + 3) / 4)), dim3(256), 0, stream, w,
+                     N, K, w4_chunks(K), c, s, packed);
+  return hipGetLastError();
+}
+
+template <int FMT>
+static hipError_t launch_decode(const uint16_t* x, int64_t M, int64_t K, const uint8_t* wp, int64_t N,
+                                uint16_t* y, hipStream_t stream) {
   if (M == 0) return hipSuccess;
   const int64_t NB = (N + 15) / 16, KC = w4_chunks(K);
   if (M <= 16) {
-    hipLaunchKernelGGL((w4a16_decode_kernel<1, 4, 16>), dim3((unsigned)NB, 1), dim3(1024), 0, stream, x, M,
-                       K, wp, KC, N, y);
+    hipLaunchKernelGGL((w4a16_decode_kernel<1, 4, 16, FMT>), dim3((unsigned)NB, 1), dim3(1024), 0, stream,
+                       x, M, K, wp, KC, N, y);
   } else {
-    hipLaunchKernelGGL((w4a16_decode_kernel<4, 1, 16>), dim3((unsigned)NB, (unsigned)((M + 63) / 64)),
+    hipLaunchKernelGGL((w4a16_decode_kernel<4, 1, 16, FMT>), dim3((unsigned)NB, (unsigned)((M + 63) / 64)),
                        dim3(1024), 0, stream, x, M, K, wp, KC, N, y);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_w4a16_linear(const uint16_t* x, int64_t M, int64_t K, const uint8_t* wp, int64_t N,
+                               uint16_t* y, hipStream_t stream) {
+  return launch_decode<0>(x, M, K, wp, N, y, stream);
+}
+
+hipError_t launch_fp4_linear(const uint16_t* x, int64_t M, int64_t K, const uint8_t* wp, int64_t N,
+                             uint16_t* y, hipStream_t stream) {
+  return launch_decode<1>(x, M, K, wp, N, y, stream);
 }
 
 }  // namespace w8a8

@@ -1,4 +1,5 @@
-"""Parity of the W4A16 weight variant (through the C ABI) with the CPU oracle.
+"""Parity of the W4A16 weight variant, INT4 and FP4 weights (through the C ABI),
+with the CPU oracle.
 
 Codes, BF16 scales and the packed layout are compared exactly. The linear
 multiplies exactly dequantized BF16 weights (BF16 x BF16 products are exact in
@@ -140,3 +141,76 @@ def test_w4a16_zero_rows(w):
     y = w.w4a16_linear(torch.empty((0, 64), dtype=torch.bfloat16, device="cuda"), p, 32)
     sync()
     assert y.shape == (0, 32)
+
+
+# ---------------------------------------------------------------------------
+# FP4 (E2M1 + E8M0 per 32) weights in the same packed layout
+# ---------------------------------------------------------------------------
+
+def _unpack_fp4(buf, N, K):
+    NB, KC = -(-N // 16), -(-K // 128)
+    b = np.asarray(buf, np.uint8)[:NB * KC * 1152].reshape(NB, KC, 1152)
+    codes = b[:, :, :1024].reshape(NB, KC, 4, 16, 4, 4)
+    nib = np.stack([codes & 0xF, codes >> 4], axis=-1).reshape(NB, KC, 4, 16, 4, 8)
+    c = nib.transpose(0, 3, 1, 4, 2, 5).reshape(NB * 16, KC * 128)[:N, :K]
+    sc = b[:, :, 1024:1088].reshape(NB, KC, 16, 4)                    # [nb][kc][col][step]
+    s = sc.transpose(0, 2, 1, 3).reshape(NB * 16, KC * 4)[:N, :K // 32]
+    return c, s
+
+
+@pytest.mark.parametrize("N,K", [(64, 128), (50, 96), (33, 32), (4096, 7168), (160, 2080)])
+def test_fp4_quant_and_pack_bit_exact(w, N, K):
+    show(f"fp4_quant_weight N={N} K={K}")
+    wb = _weight(N, K, seed=N + K + 1)
+    c, s, p = w.fp4_quant_weight(bf16_dev(wb), codes=True, scales=True, pack=True)
+    sync()
+    c_o, s_o = W4.fp4_quant(wb)
+    _assert_eq(host(c), c_o, "codes")
+    _assert_eq(host(s), s_o, "scales")
+    cu, su = _unpack_fp4(host(p), N, K)
+    _assert_eq(cu, c_o, "packed codes")
+    _assert_eq(su, s_o, "packed scales")
+
+
+def _check_fp4_linear(y_bits, x_bits, c, s):
+    ref = W4.fp4_linear_ref64(x_bits, c, s)
+    xf = O.bf16_to_f32(x_bits).astype(np.float64)
+    wf = O.bf16_to_f32(W4.fp4_dequant(c, s)).astype(np.float64)
+    mag = np.abs(xf) @ np.abs(wf).T
+    allow = LAMBDA * np.sqrt(xf.shape[1]) * 2.0 ** -24 * mag
+    y = O.bf16_to_f32(y_bits).astype(np.float64)
+    err = np.abs(y - ref)
+    base = np.maximum(O.REL_TOL * np.abs(ref), O.ABS_FLOOR)
+    ok = err <= base + allow
+    show(f"  max|err| {err.max():.3e}, within the BF16 bound alone {np.mean(err <= base):.5f}")
+    if not ok.all():
+        i = tuple(np.argwhere(~ok)[0])
+        raise AssertionError(f"{int((~ok).sum())} of {ok.size} outside tolerance, first {i}: "
+                             f"got {y[i]} want {ref[i]} allowance {allow[i]}")
+    assert np.mean(err <= base) >= 0.99
+
+
+@pytest.mark.parametrize("M,K,N", LINEAR_CASES)
+def test_fp4_linear_within_tolerance(w, M, K, N):
+    show(f"fp4_linear M={M} K={K} N={N}")
+    x = synth.activations(M, K, 0.005, seed=M + K + N + 1)
+    wb = _weight(N, K, seed=K + N + 1)
+    _, _, p = w.fp4_quant_weight(bf16_dev(wb))
+    y = w.fp4_linear(bf16_dev(x), p, N)
+    sync()
+    c_o, s_o = W4.fp4_quant(wb)
+    _check_fp4_linear(bf16_host(y), x, c_o, s_o)
+
+
+@pytest.mark.timeout(300)
+def test_fp4_decode_config(w):
+    d = synth.decode(seed=0)
+    K, N = d.x.shape[1], 4096
+    wb = _weight(N, K, seed=0)
+    _, _, p = w.fp4_quant_weight(bf16_dev(wb))
+    c_o, s_o = W4.fp4_quant(wb)
+    for M in (1, 4, 16, 64):
+        show(f"fp4 decode config M={M}")
+        y = w.fp4_linear(bf16_dev(d.x[:M]), p, N)
+        sync()
+        _check_fp4_linear(bf16_host(y), d.x[:M], c_o, s_o)

@@ -215,3 +215,14 @@ def test_w4a16_validation_before_launch(w):
     assert L.w8a8_w4a16_linear(p, 4, 64, None, 16, p, None) == 1
     assert L.w8a8_w4a16_linear(None, 0, 64, None, 16, None, None) == 0         # M == 0
     assert L.w8a8_w4a16_linear(p, -1, 64, p, 16, p, None) == 2
+
+
+def test_fp4_validation_before_launch(w):
+    L = w.lib
+    p = ctypes.c_void_p(256)  # never dereferenced: validation fails first
+    assert L.w8a8_fp4_quant_weight(p, 16, 100, p, p, p, None) == 4          # K % 32
+    assert L.w8a8_fp4_quant_weight(p, 16, 64, None, None, None, None) == 1  # no output
+    assert L.w8a8_fp4_quant_weight(p, 16, 64, None, None, ctypes.c_void_p(264), None) == 3
+    assert L.w8a8_fp4_linear(p, 4, 48, p, 16, p, None) == 4
+    assert L.w8a8_fp4_linear(ctypes.c_void_p(264), 4, 64, p, 16, p, None) == 3
+    assert L.w8a8_fp4_linear(None, 0, 64, None, 16, None, None) == 0
