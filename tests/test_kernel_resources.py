@@ -26,8 +26,13 @@ def _hipcc():
 
 
 def _flags():
-    from moe_token_amax_amd._build import FLAGS
-    return [*FLAGS, "--cuda-device-only", "-I" + CSRC]
+    # _build.py on its own (importing the package would load the library)
+    import importlib.util
+    spec = importlib.util.spec_from_file_location("w8a8_build", os.path.join(ROOT, "moe_token_amax_amd",
+                                                                           "_build.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return [*mod.FLAGS, "--cuda-device-only", "-I" + CSRC]
 
 
 @pytest.mark.skipif(_hipcc() is None, reason="hipcc not available")
