@@ -635,6 +635,8 @@ class W4Workload(Workload):
         del packed
         self.x = torch.from_numpy(d.x.view(np.int16)).to(dev).view(torch.bfloat16)
         self.y = {M: torch.empty((M, self.N), dtype=torch.bfloat16, device=dev) for M in self.Ms}
+        self.ws = {M: torch.empty((max(1, w.w4a16_linear_workspace_bytes(M, self.K)),), dtype=torch.uint8,
+                                  device=dev) for M in self.Ms}
         per = len(self.Ms)
         steps = [self._make_step([(p * per + j) % self.copies for j in range(per)])
                  for p in range(self.copies // per)]
@@ -644,7 +646,7 @@ class W4Workload(Workload):
 
     def _linear(self, M, c):
         lin = self.w.w4a16_linear if self.fmt == "int4" else self.w.fp4_linear
-        lin(self.x[:M], self.wp[c], self.N, y=self.y[M])
+        lin(self.x[:M], self.wp[c], self.N, y=self.y[M], workspace=self.ws[M])
 
     def _make_step(self, copy_ids):
         def fn():

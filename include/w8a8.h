@@ -438,6 +438,9 @@ int w8a8_static_linear(const int8_t* q, int64_t M, int64_t K, const void* w_pack
  *   BF16(sum_k x[m, k] * BF16(q * s)[n, k]): each weight dequantized once to
  *   BF16 (round half to even of the exact q * s), exact BF16 products,
  *   fp32 accumulation (not bit-exact against a float64 sum; no bias).
+ *   workspace: w8a8_w4a16_linear_workspace_bytes(M, K) bytes, 256-byte
+ *   aligned (0, and NULL allowed, for M <= 16; above, the activation packed
+ *   into the MFMA's 1 KB operand blocks), rewritten by every call.
  * Packed layout: per 16-column block and 128-deep k-chunk 1152 bytes (codes +
  *   8 in nibbles in the BF16 MFMA's operand order, then the 16 x 4 BF16
  *   scales); K padded to 128 with zero weights.
@@ -447,8 +450,9 @@ int w8a8_w4a16_quant_weight(const uint16_t* w, int64_t N, int64_t K, int8_t* q, 
                             void* packed, void* stream);
 int w8a8_w4a16_pack(const int8_t* q, const uint16_t* scale, int64_t N, int64_t K, void* packed,
                     void* stream);
+int64_t w8a8_w4a16_linear_workspace_bytes(int64_t M, int64_t K);
 int w8a8_w4a16_linear(const uint16_t* x, int64_t M, int64_t K, const void* w_packed, int64_t N,
-                      uint16_t* y, void* stream);
+                      uint16_t* y, void* workspace, int64_t ws_bytes, void* stream);
 
 /*
  * FP4 weights for the same W4A16 path ([LOWBIT]: the W4A16 row lists INT4 /
@@ -465,12 +469,13 @@ int w8a8_w4a16_linear(const uint16_t* x, int64_t M, int64_t K, const void* w_pac
  *   [16 columns][4 groups] in the scale area).
  * w8a8_fp4_linear: x BF16 [M, K] (16-byte aligned) -> y BF16 [M, N] =
  *   BF16(sum_k x[m, k] * 2^E value[n, k]): the dequantized weights are exact
- *   in BF16 (-0 becomes +0), products exact, fp32 accumulation.
+ *   in BF16 (-0 becomes +0), products exact, fp32 accumulation. Workspace
+ *   as for w8a8_w4a16_linear.
  */
 int w8a8_fp4_quant_weight(const uint16_t* w, int64_t N, int64_t K, uint8_t* codes, uint8_t* scales,
                           void* packed, void* stream);
 int w8a8_fp4_linear(const uint16_t* x, int64_t M, int64_t K, const void* w_packed, int64_t N,
-                    uint16_t* y, void* stream);
+                    uint16_t* y, void* workspace, int64_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -59,6 +59,7 @@ __all__ = [
     "w4a16_packed_bytes",
     "w4a16_quant_weight",
     "w4a16_pack",
+    "w4a16_linear_workspace_bytes",
     "w4a16_linear",
     "fp4_quant_weight",
     "fp4_linear",
@@ -142,9 +143,12 @@ def _load():
         "w8a8_w4a16_packed_bytes": (_c_i64, [_c_i64, _c_i64]),
         "w8a8_w4a16_quant_weight": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p]),
         "w8a8_w4a16_pack": (ctypes.c_int, [_c_p, _c_p, _c_i64, _c_i64, _c_p, _c_p]),
-        "w8a8_w4a16_linear": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_i64, _c_p, _c_p]),
+        "w8a8_w4a16_linear_workspace_bytes": (_c_i64, [_c_i64, _c_i64]),
+        "w8a8_w4a16_linear": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_i64, _c_p, _c_p, _c_i64,
+                                             _c_p]),
         "w8a8_fp4_quant_weight": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p]),
-        "w8a8_fp4_linear": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_i64, _c_p, _c_p]),
+        "w8a8_fp4_linear": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_i64, _c_p, _c_p, _c_i64,
+                                           _c_p]),
         "w8a8_static_quant": (ctypes.c_int, [_c_p, _c_i64, _c_i64, ctypes.c_float, ctypes.c_float,
                                              _c_p, _c_p]),
         "w8a8_static_quant_packed": (ctypes.c_int, [_c_p, _c_i64, _c_i64, ctypes.c_float,
@@ -754,8 +758,13 @@ def w4a16_pack(q: torch.Tensor, s: torch.Tensor, out: torch.Tensor | None = None
     return out
 
 
+def w4a16_linear_workspace_bytes(M: int, K: int) -> int:
+    return int(lib.w8a8_w4a16_linear_workspace_bytes(M, K))
+
+
 def w4a16_linear(x: torch.Tensor, w_packed: torch.Tensor, N: int,
-                 y: torch.Tensor | None = None) -> torch.Tensor:
+                 y: torch.Tensor | None = None,
+                 workspace: torch.Tensor | None = None) -> torch.Tensor:
     """BF16 x [M, K] times the packed INT4 weight [N, K] -> BF16 [M, N]."""
     _need(x, torch.bfloat16, "x", 2)
     _need(w_packed, torch.uint8, "w_packed", 1)
@@ -765,7 +774,9 @@ def w4a16_linear(x: torch.Tensor, w_packed: torch.Tensor, N: int,
     if y is None:
         y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
     _need(y, torch.bfloat16, "y", 2)
-    _check(lib.w8a8_w4a16_linear(_ptr(x), M, K, _ptr(w_packed), N, _ptr(y), _stream()))
+    ws, ws_n = _workspace(w4a16_linear_workspace_bytes(M, K), x.device, workspace)
+    _check(lib.w8a8_w4a16_linear(_ptr(x), M, K, _ptr(w_packed), N, _ptr(y), _ptr(ws), ws_n,
+                                 _stream()))
     return y
 
 
@@ -784,7 +795,8 @@ def fp4_quant_weight(w: torch.Tensor, codes: bool = False, scales: bool = False,
 
 
 def fp4_linear(x: torch.Tensor, w_packed: torch.Tensor, N: int,
-               y: torch.Tensor | None = None) -> torch.Tensor:
+               y: torch.Tensor | None = None,
+               workspace: torch.Tensor | None = None) -> torch.Tensor:
     """BF16 x [M, K] times the packed FP4 weight [N, K] -> BF16 [M, N]."""
     _need(x, torch.bfloat16, "x", 2)
     _need(w_packed, torch.uint8, "w_packed", 1)
@@ -794,7 +806,9 @@ def fp4_linear(x: torch.Tensor, w_packed: torch.Tensor, N: int,
     if y is None:
         y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
     _need(y, torch.bfloat16, "y", 2)
-    _check(lib.w8a8_fp4_linear(_ptr(x), M, K, _ptr(w_packed), N, _ptr(y), _stream()))
+    ws, ws_n = _workspace(w4a16_linear_workspace_bytes(M, K), x.device, workspace)
+    _check(lib.w8a8_fp4_linear(_ptr(x), M, K, _ptr(w_packed), N, _ptr(y), _ptr(ws), ws_n,
+                               _stream()))
     return y
 
 

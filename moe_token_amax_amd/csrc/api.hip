@@ -741,6 +741,11 @@ int64_t w8a8_w4a16_packed_bytes(int64_t N, int64_t K) {
   return w8a8::w4_packed_bytes(N, K);
 }
 
+int64_t w8a8_w4a16_linear_workspace_bytes(int64_t M, int64_t K) {
+  if (M < 1 || K < 1) return 0;
+  return w8a8::w4_linear_ws_bytes(M, K);
+}
+
 int w8a8_w4a16_quant_weight(const uint16_t* w, int64_t N, int64_t K, int8_t* q, uint16_t* scale,
                             void* packed, void* stream) {
   int st = check_w4("w4a16_quant_weight", N, K);
@@ -777,7 +782,7 @@ int w8a8_fp4_quant_weight(const uint16_t* w, int64_t N, int64_t K, uint8_t* code
 }
 
 int w8a8_fp4_linear(const uint16_t* x, int64_t M, int64_t K, const void* w_packed, int64_t N,
-                    uint16_t* y, void* stream) {
+                    uint16_t* y, void* workspace, int64_t ws_bytes, void* stream) {
   int st = check_w4("fp4_linear", N, K);
   if (st) return st;
   if (M < 0 || M >= kMaxDim) return fail(W8A8_ERR_SHAPE, "fp4_linear: bad M");
@@ -785,13 +790,17 @@ int w8a8_fp4_linear(const uint16_t* x, int64_t M, int64_t K, const void* w_packe
   if (!x || !w_packed || !y) return fail(W8A8_ERR_NULL, "fp4_linear: null pointer");
   if (!aligned(x, 16) || !aligned(w_packed, 16) || !aligned(y, 2))
     return fail(W8A8_ERR_ALIGN, "fp4_linear: x and w_packed need 16-byte alignment");
-  return launched(w8a8::launch_fp4_linear(x, M, K, reinterpret_cast<const uint8_t*>(w_packed), N, y,
+  const int64_t need = w8a8::w4_linear_ws_bytes(M, K);
+  if (need > 0 && (!workspace || ws_bytes < need || !aligned(workspace, 256)))
+    return fail(W8A8_ERR_WORKSPACE, "fp4_linear: needs %lld workspace bytes (256-byte aligned), got %lld",
+                (long long)need, (long long)ws_bytes);
+  return launched(w8a8::launch_fp4_linear(x, M, K, reinterpret_cast<const uint8_t*>(w_packed), N, y, workspace,
                                           (hipStream_t)stream),
                   "fp4_linear");
 }
 
 int w8a8_w4a16_linear(const uint16_t* x, int64_t M, int64_t K, const void* w_packed, int64_t N,
-                      uint16_t* y, void* stream) {
+                      uint16_t* y, void* workspace, int64_t ws_bytes, void* stream) {
   int st = check_w4("w4a16_linear", N, K);
   if (st) return st;
   if (M < 0 || M >= kMaxDim) return fail(W8A8_ERR_SHAPE, "w4a16_linear: bad M");
@@ -799,7 +808,11 @@ int w8a8_w4a16_linear(const uint16_t* x, int64_t M, int64_t K, const void* w_pac
   if (!x || !w_packed || !y) return fail(W8A8_ERR_NULL, "w4a16_linear: null pointer");
   if (!aligned(x, 16) || !aligned(w_packed, 16) || !aligned(y, 2))
     return fail(W8A8_ERR_ALIGN, "w4a16_linear: x and w_packed need 16-byte alignment");
-  return launched(w8a8::launch_w4a16_linear(x, M, K, reinterpret_cast<const uint8_t*>(w_packed), N, y,
+  const int64_t need = w8a8::w4_linear_ws_bytes(M, K);
+  if (need > 0 && (!workspace || ws_bytes < need || !aligned(workspace, 256)))
+    return fail(W8A8_ERR_WORKSPACE, "w4a16_linear: needs %lld workspace bytes (256-byte aligned), got %lld",
+                (long long)need, (long long)ws_bytes);
+  return launched(w8a8::launch_w4a16_linear(x, M, K, reinterpret_cast<const uint8_t*>(w_packed), N, y, workspace,
                                             (hipStream_t)stream),
                   "w4a16_linear");
 }

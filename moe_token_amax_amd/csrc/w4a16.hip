@@ -214,6 +214,23 @@ __device__ __forceinline__ bf16x8 w4_dequant8(uint32_t word, float s) {
   return __builtin_bit_cast(bf16x8, uint4{pk[0], pk[1], pk[2], pk[3]});
 }
 
+// BF16 activation x [M, K] -> 1 KB blocks [ceil(M/16)][K/32] in the BF16 MFMA's
+// A operand order: byte l * 16 of block (mb, kb) holds x[16 mb + l % 16][32 kb
+// + 8 (l / 16) .. + 7]; rows past M repeat row M - 1 (their outputs are not
+// stored). One thread per 16-byte piece.
+__global__ __launch_bounds__(256) void w4_pack_a_kernel(const uint16_t* __restrict__ x, int64_t M,
+                                                        int64_t K, uint8_t* __restrict__ out) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t KB = K / 32, MB = (M + 15) / 16;
+  if (t >= MB * KB * 64) return;
+  const int lane = (int)(t & 63);
+  const int64_t blk = t >> 6, mb = blk / KB, kb = blk % KB;
+  int64_t row = mb * 16 + (lane & 15);
+  row = row < M ? row : M - 1;
+  reinterpret_cast<uint4*>(out)[t] =
+      *reinterpret_cast<const uint4*>(x + row * K + kb * 32 + 8 * (lane >> 4));
+}
+
 // 8 BF16 weights of one step from 8 E2M1 codes and sc = 2^(E - 1): a byte
 // permute looks up t + 12 for each code (t = the signed value in units of
 // 0.5: 0, 1, 2, 3, 4, 6, 8, 12 for the magnitudes, negated for sign bit 8),
@@ -241,12 +258,13 @@ __device__ __forceinline__ bf16x8 fp4_dequant8(uint32_t word, float sc) {
   return __builtin_bit_cast(bf16x8, uint4{pk[0], pk[1], pk[2], pk[3]});
 }
 
-template <int MB, int UNR, int WAVES, int FMT>
+template <int MB, int UNR, int WAVES, int FMT, bool ABLK>
 __global__ __launch_bounds__(64 * WAVES) void w4a16_decode_kernel(const uint16_t* __restrict__ x,
                                                                   int64_t M, int64_t K,
                                                                   const uint8_t* __restrict__ wp,
                                                                   int64_t KC, int64_t N,
                                                                   uint16_t* __restrict__ y) {
+  // ABLK: x is the packed activation of w4_pack_a_kernel (1 KB blocks)
   __shared__ f32x4 part[WAVES][MB][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t nb = blockIdx.x;
@@ -285,8 +303,20 @@ __global__ __launch_bounds__(64 * WAVES) void w4a16_decode_kernel(const uint16_t
         // k past K (the zero-weight padding of the last chunk): zeros, not reads
         // past the row (wavefront-uniform)
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-          a[u][j][mb] = (kc < KC && k < K) ? *reinterpret_cast<const bf16x8*>(arow[mb] + k) : bf16x8{};
+        for (int mb = 0; mb < MB; ++mb) {
+          if (ABLK) {
+            // 16-row blocks past the last packed one read the last (rows >= M: not stored)
+            int64_t rb = row0 / 16 + mb;
+            rb = rb < (M + 15) / 16 ? rb : (M + 15) / 16 - 1;
+            const int64_t blk = rb * (K / 32) + k / 32;
+            a[u][j][mb] = (kc < KC && k < K)
+                              ? reinterpret_cast<const bf16x8*>(
+                                    reinterpret_cast<const uint8_t*>(x) + blk * 1024)[lane]
+                              : bf16x8{};
+          } else {
+            a[u][j][mb] = (kc < KC && k < K) ? *reinterpret_cast<const bf16x8*>(arow[mb] + k) : bf16x8{};
+          }
+        }
       }
     }
 #pragma unroll
@@ -367,29 +397,38 @@ hipError_t launch_fp4_quant_pack(const uint16_t* w, int64_t N, int64_t K, uint8_
   return hipGetLastError();
 }
 
+int64_t w4_linear_ws_bytes(int64_t M, int64_t K) { return M > 16 ? (M + 15) / 16 * (K / 32) * 1024 : 0; }
+
 template <int FMT>
 static hipError_t launch_decode(const uint16_t* x, int64_t M, int64_t K, const uint8_t* wp, int64_t N,
-                                uint16_t* y, hipStream_t stream) {
+                                uint16_t* y, void* ws, hipStream_t stream) {
   if (M == 0) return hipSuccess;
   const int64_t NB = (N + 15) / 16, KC = w4_chunks(K);
   if (M <= 16) {
-    hipLaunchKernelGGL((w4a16_decode_kernel<1, 4, 16, FMT>), dim3((unsigned)NB, 1), dim3(1024), 0, stream,
-                       x, M, K, wp, KC, N, y);
-  } else {
-    hipLaunchKernelGGL((w4a16_decode_kernel<4, 1, 16, FMT>), dim3((unsigned)NB, (unsigned)((M + 63) / 64)),
-                       dim3(1024), 0, stream, x, M, K, wp, KC, N, y);
+    hipLaunchKernelGGL((w4a16_decode_kernel<1, 4, 16, FMT, false>), dim3((unsigned)NB, 1), dim3(1024), 0,
+                       stream, x, M, K, wp, KC, N, y);
+    return hipGetLastError();
   }
+  // more rows: the activation is packed into contiguous 1 KB operand blocks
+  // first, so that each fragment load of the linear is one contiguous block
+  const int64_t pieces = (M + 15) / 16 * (K / 32) * 64;
+  hipLaunchKernelGGL(w4_pack_a_kernel, dim3((unsigned)((pieces + 255) / 256)), dim3(256), 0, stream, x, M,
+                     K, reinterpret_cast<uint8_t*>(ws));
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL((w4a16_decode_kernel<4, 1, 16, FMT, true>), dim3((unsigned)NB, (unsigned)((M + 63) / 64)),
+                     dim3(1024), 0, stream, reinterpret_cast<const uint16_t*>(ws), M, K, wp, KC, N, y);
   return hipGetLastError();
 }
 
 hipError_t launch_w4a16_linear(const uint16_t* x, int64_t M, int64_t K, const uint8_t* wp, int64_t N,
-                               uint16_t* y, hipStream_t stream) {
-  return launch_decode<0>(x, M, K, wp, N, y, stream);
+                               uint16_t* y, void* ws, hipStream_t stream) {
+  return launch_decode<0>(x, M, K, wp, N, y, ws, stream);
 }
 
 hipError_t launch_fp4_linear(const uint16_t* x, int64_t M, int64_t K, const uint8_t* wp, int64_t N,
-                             uint16_t* y, hipStream_t stream) {
-  return launch_decode<1>(x, M, K, wp, N, y, stream);
+                             uint16_t* y, void* ws, hipStream_t stream) {
+  return launch_decode<1>(x, M, K, wp, N, y, ws, stream);
 }
 
 }  // namespace w8a8

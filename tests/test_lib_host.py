@@ -211,10 +211,15 @@ def test_w4a16_validation_before_launch(w):
     assert L.w8a8_w4a16_quant_weight(p, 16, 64, None, None, ctypes.c_void_p(264), None) == 3
     assert L.w8a8_w4a16_pack(p, None, 16, 64, p, None) == 1
     assert L.w8a8_w4a16_pack(p, p, 16, 48, p, None) == 4
-    assert L.w8a8_w4a16_linear(ctypes.c_void_p(264), 4, 64, p, 16, p, None) == 3
-    assert L.w8a8_w4a16_linear(p, 4, 64, None, 16, p, None) == 1
-    assert L.w8a8_w4a16_linear(None, 0, 64, None, 16, None, None) == 0         # M == 0
-    assert L.w8a8_w4a16_linear(p, -1, 64, p, 16, p, None) == 2
+    assert L.w8a8_w4a16_linear(ctypes.c_void_p(264), 4, 64, p, 16, p, None, 0, None) == 3
+    assert L.w8a8_w4a16_linear(p, 4, 64, None, 16, p, None, 0, None) == 1
+    assert L.w8a8_w4a16_linear(None, 0, 64, None, 16, None, None, 0, None) == 0   # M == 0
+    assert L.w8a8_w4a16_linear(p, -1, 64, p, 16, p, None, 0, None) == 2
+    # up to 16 rows no workspace; above, the packed activation
+    assert L.w8a8_w4a16_linear_workspace_bytes(16, 7168) == 0
+    assert L.w8a8_w4a16_linear_workspace_bytes(64, 7168) == 4 * 224 * 1024
+    assert L.w8a8_w4a16_linear(p, 64, 64, p, 16, p, None, 0, None) == 5
+    assert L.w8a8_w4a16_linear(p, 64, 64, p, 16, p, p, 4 * 2 * 1024 - 1, None) == 5
 
 
 def test_fp4_validation_before_launch(w):
@@ -223,6 +228,7 @@ def test_fp4_validation_before_launch(w):
     assert L.w8a8_fp4_quant_weight(p, 16, 100, p, p, p, None) == 4          # K % 32
     assert L.w8a8_fp4_quant_weight(p, 16, 64, None, None, None, None) == 1  # no output
     assert L.w8a8_fp4_quant_weight(p, 16, 64, None, None, ctypes.c_void_p(264), None) == 3
-    assert L.w8a8_fp4_linear(p, 4, 48, p, 16, p, None) == 4
-    assert L.w8a8_fp4_linear(ctypes.c_void_p(264), 4, 64, p, 16, p, None) == 3
-    assert L.w8a8_fp4_linear(None, 0, 64, None, 16, None, None) == 0
+    assert L.w8a8_fp4_linear(p, 4, 48, p, 16, p, None, 0, None) == 4
+    assert L.w8a8_fp4_linear(ctypes.c_void_p(264), 4, 64, p, 16, p, None, 0, None) == 3
+    assert L.w8a8_fp4_linear(None, 0, 64, None, 16, None, None, 0, None) == 0
+    assert L.w8a8_fp4_linear(p, 17, 64, p, 16, p, None, 0, None) == 5
