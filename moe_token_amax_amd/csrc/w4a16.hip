@@ -231,31 +231,19 @@ __global__ __launch_bounds__(256) void w4_pack_a_kernel(const uint16_t* __restri
       *reinterpret_cast<const uint4*>(x + row * K + kb * 32 + 8 * (lane >> 4));
 }
 
-// 8 BF16 weights of one step from 8 E2M1 codes and sc = 2^(E - 1): a byte
-// permute looks up t + 12 for each code (t = the signed value in units of
-// 0.5: 0, 1, 2, 3, 4, 6, 8, 12 for the magnitudes, negated for sign bit 8),
-// then fma(t + 12, sc, -12 sc) = value * 2^E exactly; the BF16 conversion
-// is exact (at most 2 significant bits). -0 comes out as +0.
-__device__ __forceinline__ uint32_t fp4_lut4(uint32_t x) {
-  const uint32_t mag = x & 0x07070707u;
-  const uint32_t neg = ((x >> 3) & 0x01010101u) * 0xFFu;               // 0xFF per negative byte
-  const uint32_t pos = __builtin_amdgcn_perm(0x18141210u, 0x0F0E0D0Cu, mag);  // 12 + t
-  const uint32_t ngv = __builtin_amdgcn_perm(0x00040608u, 0x090A0B0Cu, mag);  // 12 - t
-  return (ngv & neg) | (pos & ~neg);
-}
-
+// 8 BF16 weights of one step from 8 E2M1 codes (weight 2b in the low nibble
+// of byte b, 2b + 1 in the high one) and the group's scale sc = 2^E: gfx950's
+// MX conversion v_cvt_scalef32_pk_bf16_fp4 decodes the two codes of one byte
+// and multiplies them by sc, so one instruction yields two weights. Every
+// value * 2^E is exact in BF16 (at most 2 significant bits; E in [-127, 125]
+// for any BF16 group, subnormal results included), so no rounding happens.
 __device__ __forceinline__ bf16x8 fp4_dequant8(uint32_t word, float sc) {
-  uint32_t ev = fp4_lut4(word & 0x0F0F0F0Fu), od = fp4_lut4((word >> 4) & 0x0F0F0F0Fu);
-  asm volatile("" : "+v"(ev), "+v"(od));
-  const float m12 = -12.0f * sc;  // exact
-  uint32_t pk[4];
-#pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    const f32x2 v = {fmaf((float)((ev >> (8 * b)) & 0xFFu), sc, m12),   // code 2b
-                     fmaf((float)((od >> (8 * b)) & 0xFFu), sc, m12)};  // code 2b + 1
-    pk[b] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
-  }
-  return __builtin_bit_cast(bf16x8, uint4{pk[0], pk[1], pk[2], pk[3]});
+  const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, sc, 0);
+  const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, sc, 1);
+  const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, sc, 2);
+  const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, sc, 3);
+  return __builtin_bit_cast(bf16x8, uint4{__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
+                                          __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3)});
 }
 
 template <int MB, int UNR, int WAVES, int FMT, bool ABLK>
@@ -332,8 +320,8 @@ __global__ __launch_bounds__(64 * WAVES) void w4a16_decode_kernel(const uint16_t
         s[3] = __uint_as_float(sc[u].y & 0xFFFF0000u);
       } else {
 #pragma unroll
-        for (int j = 0; j < 4; ++j)  // 2^(E - 1) = 2^(byte - 128)
-          s[j] = __builtin_ldexpf(1.0f, (int)((sc[u].x >> (8 * j)) & 0xFFu) - 128);
+        for (int j = 0; j < 4; ++j)  // 2^E = 2^(byte - 127), byte 0 the subnormal 2^-127
+          s[j] = __builtin_ldexpf(1.0f, (int)((sc[u].x >> (8 * j)) & 0xFFu) - 127);
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
