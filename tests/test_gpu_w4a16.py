@@ -214,3 +214,59 @@ def test_fp4_decode_config(w):
         y = w.fp4_linear(bf16_dev(d.x[:M]), p, N)
         sync()
         _check_fp4_linear(bf16_host(y), d.x[:M], c_o, s_o)
+
+
+# ---------------------------------------------------------------------------
+# Dequantized weights read back exactly: with one-hot activation rows
+# (x[m, k_m] = 1, zeros elsewhere) every output is 1 * w_deq[n, k_m] plus
+# exact zeros, so y[m, n] equals the BF16 dequantized weight itself.
+# ---------------------------------------------------------------------------
+
+def _wide_range_weight(N, K, seed, lo_exp, hi_exp):
+    """BF16 [N, K] whose groups of 32 have magnitudes 2^e, e drawn from
+    [lo_exp, hi_exp], plus an all-zero group and a group with negative zeros."""
+    r = np.random.default_rng([seed, 45])
+    w = r.standard_normal((N, K)) * np.ldexp(1.0, r.integers(lo_exp, hi_exp + 1, (N, K // 32))).repeat(32, axis=1)
+    w[1, :32] = 0.0
+    w[2, 32:64] = -0.0
+    return O.f32_to_bf16(w.astype(np.float32))
+
+
+def _one_hot(ks, K):
+    x = np.zeros((len(ks), K), np.float32)
+    x[np.arange(len(ks)), ks] = 1.0
+    return O.f32_to_bf16(x)
+
+
+def _readback_cases():
+    # (M, ks): every k through the packed-activation path, and 16 scattered k
+    # through the M <= 16 path
+    K = 256
+    return K, [np.arange(K), (np.arange(16) * 37 + 5) % K]
+
+
+@pytest.mark.parametrize("fmt", ["int4", "fp4"])
+@pytest.mark.parametrize("exps", [(-100, 100), (-133, -118), (110, 125)], ids=["normal", "tiny", "huge"])
+def test_dequant_exact_through_one_hot_rows(w, fmt, exps):
+    K, cases = _readback_cases()
+    N = 48
+    wb = _wide_range_weight(N, K, seed=3, lo_exp=exps[0], hi_exp=exps[1])
+    if fmt == "int4":
+        _, _, p = w.w4a16_quant_weight(bf16_dev(wb))
+        q, s = W4.w4_quant(wb)
+        deq = O.bf16_to_f32(W4.w4_dequant(q, s))
+        lin = w.w4a16_linear
+    else:
+        _, _, p = w.fp4_quant_weight(bf16_dev(wb))
+        c, s = W4.fp4_quant(wb)
+        deq = O.bf16_to_f32(W4.fp4_dequant(c, s))
+        lin = w.fp4_linear
+    for ks in cases:
+        show(f"{fmt} one-hot readback M={len(ks)} K={K} N={N}")
+        y = lin(bf16_dev(_one_hot(ks, K)), p, N)
+        sync()
+        got = O.bf16_to_f32(bf16_host(y))
+        want = deq[:, ks].T
+        bad = np.argwhere(got != want)          # +0 and -0 compare equal
+        assert bad.size == 0, f"{len(bad)} mismatches, first {bad[0].tolist()}: got {got[tuple(bad[0])]} " \
+                              f"want {want[tuple(bad[0])]}"
