@@ -194,23 +194,24 @@ __global__ __launch_bounds__(256) void fp4_quant_pack_kernel(const uint16_t* __r
 // ---------------------------------------------------------------------------
 
 // 8 BF16 weights of one step from a packed word and the group scale. The
-// nibbles are split into the bytes of two words (even and odd nibbles), each
-// byte converts to fp32 in one instruction, and fma(nibble, s, -8 s) is the
+// nibbles are split into the bytes of two words (even and odd nibbles). A
+// byte n <= 15 read as OCP E4M3 is n * 2^-9 exactly, so the MX conversion
+// v_cvt_scalef32_pk_f32_fp8 with the power-of-two scale 2^9 turns two bytes
+// into the floats n0, n1 in one instruction. fma(n, s, -8 s) is then the
 // exact q * s (at most 12 significant bits: the fused operation does not
-// round); one RNE to BF16 per value.
+// round), and one RNE to BF16 per value follows.
 __device__ __forceinline__ bf16x8 w4_dequant8(uint32_t word, float s) {
-  uint32_t ev = word & 0x0F0F0F0Fu, od = (word >> 4) & 0x0F0F0F0Fu;
-  // keep the byte split: extracting each nibble from the word again costs a
-  // shift and a mask per value, each byte of ev / od converts in one instruction
-  asm volatile("" : "+v"(ev), "+v"(od));
+  const uint32_t ev = word & 0x0F0F0F0Fu, od = (word >> 4) & 0x0F0F0F0Fu;
+  const f32x2 e0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(ev, 512.0f, false);  // nibbles 0, 2
+  const f32x2 e1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(ev, 512.0f, true);   // nibbles 4, 6
+  const f32x2 o0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(od, 512.0f, false);  // nibbles 1, 3
+  const f32x2 o1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(od, 512.0f, true);   // nibbles 5, 7
   const float ms = -8.0f * s;  // exact
+  const f32x2 v[4] = {{fmaf(e0.x, s, ms), fmaf(o0.x, s, ms)}, {fmaf(e0.y, s, ms), fmaf(o0.y, s, ms)},
+                      {fmaf(e1.x, s, ms), fmaf(o1.x, s, ms)}, {fmaf(e1.y, s, ms), fmaf(o1.y, s, ms)}};
   uint32_t pk[4];
 #pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    const f32x2 v = {fmaf((float)((ev >> (8 * b)) & 0xFFu), s, ms),   // nibble 2b
-                     fmaf((float)((od >> (8 * b)) & 0xFFu), s, ms)};  // nibble 2b + 1
-    pk[b] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
-  }
+  for (int b = 0; b < 4; ++b) pk[b] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v[b], bf16x2));
   return __builtin_bit_cast(bf16x8, uint4{pk[0], pk[1], pk[2], pk[3]});
 }
 
@@ -279,32 +280,36 @@ __global__ __launch_bounds__(64 * WAVES) void w4a16_decode_kernel(const uint16_t
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
       const int64_t kc = c0 + WAVES * u;
-      if (kc < KC) {
-        const uint8_t* ch = wblk + kc * kW4ChunkBytes;
-        codes[u] = reinterpret_cast<const uint4*>(ch)[lane];
-        if (FMT == 0) sc[u] = reinterpret_cast<const uint2*>(ch + 1024)[lane & 15];
-        else sc[u].x = reinterpret_cast<const uint32_t*>(ch + 1024)[lane & 15];
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      if (kc >= KC) continue;  // wavefront-uniform; a chunk past KC is never used
+      const uint8_t* ch = wblk + kc * kW4ChunkBytes;
+      codes[u] = reinterpret_cast<const uint4*>(ch)[lane];
+      if (FMT == 0) sc[u] = reinterpret_cast<const uint2*>(ch + 1024)[lane & 15];
+      else sc[u].x = reinterpret_cast<const uint32_t*>(ch + 1024)[lane & 15];
+      // the activation fragment of step j, 16-row block mb (k = 128 kc + 32 j)
+      auto afrag = [&](int j, int mb) -> bf16x8 {
         const int64_t k = kc * kW4Chunk + 32 * j;
-        // k past K (the zero-weight padding of the last chunk): zeros, not reads
-        // past the row (wavefront-uniform)
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-          if (ABLK) {
-            // 16-row blocks past the last packed one read the last (rows >= M: not stored)
-            int64_t rb = row0 / 16 + mb;
-            rb = rb < (M + 15) / 16 ? rb : (M + 15) / 16 - 1;
-            const int64_t blk = rb * (K / 32) + k / 32;
-            a[u][j][mb] = (kc < KC && k < K)
-                              ? reinterpret_cast<const bf16x8*>(
-                                    reinterpret_cast<const uint8_t*>(x) + blk * 1024)[lane]
-                              : bf16x8{};
-          } else {
-            a[u][j][mb] = (kc < KC && k < K) ? *reinterpret_cast<const bf16x8*>(arow[mb] + k) : bf16x8{};
-          }
+        if (ABLK) {
+          // 16-row blocks past the last packed one read the last (rows >= M: not stored)
+          int64_t rb = row0 / 16 + mb;
+          rb = rb < (M + 15) / 16 ? rb : (M + 15) / 16 - 1;
+          const int64_t blk = rb * (K / 32) + k / 32;
+          return reinterpret_cast<const bf16x8*>(reinterpret_cast<const uint8_t*>(x) + blk * 1024)[lane];
         }
+        return *reinterpret_cast<const bf16x8*>(arow[mb] + k);
+      };
+      if ((kc + 1) * kW4Chunk <= K) {  // the whole chunk inside K (wavefront-uniform)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb) a[u][j][mb] = afrag(j, mb);
+      } else {
+        // the last chunk when K % 128 != 0: steps past K (zero-weight padding)
+        // take zeros instead of reads past the row
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb)
+            a[u][j][mb] = kc * kW4Chunk + 32 * j < K ? afrag(j, mb) : bf16x8{};
       }
     }
 #pragma unroll
