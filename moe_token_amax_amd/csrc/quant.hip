@@ -174,6 +174,56 @@ __global__ __launch_bounds__(kRowBlock) void quant_rows16_packed(const uint16_t*
   }
 }
 
+// The same packed codes in one pass over x, one wavefront per row (four rows
+// per 256-thread workgroup), for K <= 64 * 16 * P: lane l holds the 16-value
+// pieces j = l, l + 64, ... of its row (two contiguous 16-byte loads each) in
+// registers, the row amax is a wavefront reduction (no LDS, no barrier), and
+// each piece's 16 codes go to their place in the row-block's 1 KB blocks
+// (block j / 4, byte (r + 16 (j % 4)) * 16 for row r of the block). The
+// wavefronts of rows M .. the end of the last 16-row block, and the pieces
+// past K, write zero codes, so every block is written whole.
+template <int P>
+__global__ __launch_bounds__(256) void quant_rows_packed_wave(const uint16_t* __restrict__ x, int64_t M,
+                                                              int64_t K, int8_t* __restrict__ q,
+                                                              float* __restrict__ scale) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+  if (row >= (M + 15) / 16 * 16) return;  // whole wave leaves together
+  const int64_t kb = (K + 63) / 64, npc = kb * 4;  // 16-value pieces of a row, padding included
+  const bool live = row < M;
+  const uint16_t* xr = x + row * K;
+  uint4 v[P][2];
+  uint32_t am = 0;
+#pragma unroll
+  for (int p = 0; p < P; ++p) {
+    const int64_t k0 = (int64_t)(lane + p * kWave) * 16;
+    const bool in = live && k0 < K;
+    v[p][0] = in ? *reinterpret_cast<const uint4*>(xr + k0) : uint4{0u, 0u, 0u, 0u};
+    v[p][1] = in && k0 + 16 <= K ? *reinterpret_cast<const uint4*>(xr + k0 + 8) : uint4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      am = max(am, max(max(abs_bf16_pair_max(v[p][h].x), abs_bf16_pair_max(v[p][h].y)),
+                       max(abs_bf16_pair_max(v[p][h].z), abs_bf16_pair_max(v[p][h].w))));
+  }
+  am = wave_max_u32(am);
+  const float s = bf16_to_f32(am) / 127.0f;
+  if (lane == 0 && live) scale[row] = s;
+  int8_t* qb = q + (row >> 4) * kb * 1024 + (row & 15) * 16;
+#pragma unroll
+  for (int p = 0; p < P; ++p) {
+    const int64_t j = lane + p * kWave;
+    if (j >= npc) break;
+    uint4 o = uint4{0u, 0u, 0u, 0u};
+    if (live && j * 16 < K) {
+      const uint32_t w0[4] = {v[p][0].x, v[p][0].y, v[p][0].z, v[p][0].w};
+      const uint32_t w1[4] = {v[p][1].x, v[p][1].y, v[p][1].z, v[p][1].w};
+      const uint2 lo = quant8_bf16(w0, s), hi = quant8_bf16(w1, s);
+      o = uint4{lo.x, lo.y, hi.x, hi.y};
+    }
+    *reinterpret_cast<uint4*>(qb + ((j >> 2) * 64 + 16 * (j & 3)) * 16) = o;
+  }
+}
+
 __global__ __launch_bounds__(256) void quant_rows_generic(const uint16_t* __restrict__ x, int64_t M,
                                                           int64_t K, int8_t* __restrict__ q,
                                                           float* __restrict__ scale) {
@@ -273,9 +323,20 @@ hipError_t launch_dynamic_quant(const uint16_t* x, int64_t M, int64_t K, int8_t*
   if (packed && !vec) return hipErrorInvalidValue;
   const int64_t kb = packed ? (K + 63) / 64 : 0;
   if (packed && M > 512) {
-    // many rows: whole 1 KB blocks per store
-    hipLaunchKernelGGL(quant_rows16_packed, dim3((unsigned)((M + 15) / 16)), dim3(kRowBlock), 0,
-                       stream, x, M, K, q, scale);
+    // many rows: one pass over x, a wavefront per row, while a lane's pieces
+    // fit in registers (K <= 8192); else the two-pass 16-row kernel
+    const dim3 gw((unsigned)(((M + 15) / 16 * 16 + kRowsPerBlock - 1) / kRowsPerBlock));
+    switch ((kb * 4 + kWave - 1) / kWave) {
+#define W8A8_QPW(P)                                                                                  \
+  case P:                                                                                            \
+    hipLaunchKernelGGL(quant_rows_packed_wave<P>, gw, dim3(256), 0, stream, x, M, K, q, scale);      \
+    break;
+      W8A8_QPW(1) W8A8_QPW(2) W8A8_QPW(3) W8A8_QPW(4) W8A8_QPW(5) W8A8_QPW(6) W8A8_QPW(7) W8A8_QPW(8)
+#undef W8A8_QPW
+      default:
+        hipLaunchKernelGGL(quant_rows16_packed, dim3((unsigned)((M + 15) / 16)), dim3(kRowBlock), 0, stream, x,
+                           M, K, q, scale);
+    }
     return hipGetLastError();
   }
   const int64_t chunks = K / 8;
