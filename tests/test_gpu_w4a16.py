@@ -270,3 +270,29 @@ def test_dequant_exact_through_one_hot_rows(w, fmt, exps):
         bad = np.argwhere(got != want)          # +0 and -0 compare equal
         assert bad.size == 0, f"{len(bad)} mismatches, first {bad[0].tolist()}: got {got[tuple(bad[0])]} " \
                               f"want {want[tuple(bad[0])]}"
+
+
+def test_w4_pack_full_code_range_read_back_exact(w):
+    """Codes the quantizer never produces (-8) and scales it never produces
+    (arbitrary BF16, tiny to large, negative zero groups), packed by
+    w4a16_pack and read back through the linear with one-hot rows: every
+    dequantized weight equals the oracle's BF16(q * s)."""
+    K, cases = _readback_cases()
+    N = 40
+    r = np.random.default_rng([11, 46])
+    q = r.integers(-8, 8, (N, K)).astype(np.int8)
+    q[0, :16] = np.arange(-8, 8)                       # every code once in one group
+    s_f = (r.standard_normal((N, K // 32)) * np.ldexp(1.0, r.integers(-60, 60, (N, K // 32))))
+    s_f[3, 2] = 0.0
+    s = O.f32_to_bf16(np.abs(s_f).astype(np.float32))   # scales are non-negative
+    p = w.w4a16_pack(dev(q), torch.from_numpy(s.view(np.int16)).cuda().view(torch.bfloat16))
+    deq = O.bf16_to_f32(W4.w4_dequant(q, s))
+    for ks in cases:
+        show(f"w4a16_pack full code range, one-hot readback M={len(ks)}")
+        y = w.w4a16_linear(bf16_dev(_one_hot(ks, K)), p, N)
+        sync()
+        got = O.bf16_to_f32(bf16_host(y))
+        want = deq[:, ks].T
+        bad = np.argwhere(got != want)
+        assert bad.size == 0, f"{len(bad)} mismatches, first {bad[0].tolist()}: got {got[tuple(bad[0])]} " \
+                              f"want {want[tuple(bad[0])]}"
