@@ -432,15 +432,17 @@ int w8a8_static_linear(const int8_t* q, int64_t M, int64_t K, const void* w_pack
  *   Writes any of: q int8 [N, K], scale BF16 bits [N, K/32], packed (16-byte
  *   aligned, w8a8_w4a16_packed_bytes(N, K) bytes); null outputs are skipped,
  *   at least one must be given.
- * w8a8_w4a16_pack: pre-quantized codes (int8, clamped to [-8, 7]) and BF16
- *   scales -> the packed layout.
+ * w8a8_w4a16_pack: pre-quantized codes (int8; each is clamped to [-8, 7]
+ *   before packing) and BF16 scales -> the packed layout.
  * w8a8_w4a16_linear: x BF16 [M, K] (16-byte aligned) -> y BF16 [M, N] =
  *   BF16(sum_k x[m, k] * BF16(q * s)[n, k]): each weight dequantized once to
  *   BF16 (round half to even of the exact q * s), exact BF16 products,
  *   fp32 accumulation (not bit-exact against a float64 sum; no bias).
  *   workspace: w8a8_w4a16_linear_workspace_bytes(M, K) bytes, 256-byte
  *   aligned (0, and NULL allowed, for M <= 16; above, the activation packed
- *   into the MFMA's 1 KB operand blocks), rewritten by every call.
+ *   into the MFMA's 1 KB operand blocks), rewritten by every call; a missing,
+ *   short or misaligned workspace returns W8A8_ERR_WORKSPACE before any
+ *   launch.
  * Packed layout: per 16-column block and 128-deep k-chunk 1152 bytes (codes +
  *   8 in nibbles in the BF16 MFMA's operand order, then the 16 x 4 BF16
  *   scales); K padded to 128 with zero weights.
@@ -469,8 +471,8 @@ int w8a8_w4a16_linear(const uint16_t* x, int64_t M, int64_t K, const void* w_pac
  *   [16 columns][4 groups] in the scale area).
  * w8a8_fp4_linear: x BF16 [M, K] (16-byte aligned) -> y BF16 [M, N] =
  *   BF16(sum_k x[m, k] * 2^E value[n, k]): the dequantized weights are exact
- *   in BF16 (-0 becomes +0), products exact, fp32 accumulation. Workspace
- *   as for w8a8_w4a16_linear.
+ *   in BF16, products exact, fp32 accumulation from +0 (a -0 weight adds
+ *   nothing). Workspace as for w8a8_w4a16_linear.
  */
 int w8a8_fp4_quant_weight(const uint16_t* w, int64_t N, int64_t K, uint8_t* codes, uint8_t* scales,
                           void* packed, void* stream);
