@@ -727,6 +727,9 @@ int w8a8_mx_moe_grouped(const uint16_t* x_rows, const int64_t* group_list, int64
 // ---------------------------------------------------------------------------
 // W4A16 weight variant
 // ---------------------------------------------------------------------------
+// rows of one W4A16 / FP4 linear: 64-row workgroups along the grid's y (at most 65535)
+constexpr int64_t kW4MaxRows = (int64_t)64 * 65535;
+
 static int check_w4(const char* who, int64_t N, int64_t K) {
   if (N < 1 || K < 1 || N >= kMaxDim || K > W8A8_MAX_K)
     return fail(W8A8_ERR_SHAPE, "%s: need N >= 1 and 1 <= K <= %d", who, W8A8_MAX_K);
@@ -785,7 +788,8 @@ int w8a8_fp4_linear(const uint16_t* x, int64_t M, int64_t K, const void* w_packe
                     uint16_t* y, void* workspace, int64_t ws_bytes, void* stream) {
   int st = check_w4("fp4_linear", N, K);
   if (st) return st;
-  if (M < 0 || M >= kMaxDim) return fail(W8A8_ERR_SHAPE, "fp4_linear: bad M");
+  if (M < 0 || M > kW4MaxRows)
+    return fail(W8A8_ERR_SHAPE, "fp4_linear: need 0 <= M <= %lld (rows of one launch)", (long long)kW4MaxRows);
   if (M == 0) return ok();
   if (!x || !w_packed || !y) return fail(W8A8_ERR_NULL, "fp4_linear: null pointer");
   if (!aligned(x, 16) || !aligned(w_packed, 16) || !aligned(y, 2))
@@ -803,7 +807,8 @@ int w8a8_w4a16_linear(const uint16_t* x, int64_t M, int64_t K, const void* w_pac
                       uint16_t* y, void* workspace, int64_t ws_bytes, void* stream) {
   int st = check_w4("w4a16_linear", N, K);
   if (st) return st;
-  if (M < 0 || M >= kMaxDim) return fail(W8A8_ERR_SHAPE, "w4a16_linear: bad M");
+  if (M < 0 || M > kW4MaxRows)
+    return fail(W8A8_ERR_SHAPE, "w4a16_linear: need 0 <= M <= %lld (rows of one launch)", (long long)kW4MaxRows);
   if (M == 0) return ok();
   if (!x || !w_packed || !y) return fail(W8A8_ERR_NULL, "w4a16_linear: null pointer");
   if (!aligned(x, 16) || !aligned(w_packed, 16) || !aligned(y, 2))
