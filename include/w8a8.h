@@ -467,14 +467,16 @@ int w8a8_w4a16_linear(const uint16_t* x, int64_t M, int64_t K, const void* w_pac
  *   group); each w / 2^E encoded to the nearest of 0, 0.5, 1, 1.5, 2, 3, 4, 6
  *   (ties to the even code, saturating at 6), sign bit 8 (-0 kept). Writes any
  *   of: codes uint8 [N, K] (0..15), scales uint8 [N, K/32], packed (16-byte
- *   aligned, w8a8_w4a16_packed_bytes(N, K) bytes: the layout of
- *   w8a8_w4a16_quant_weight with the codes as nibbles and the E8M0 bytes
- *   [16 columns][4 groups] in the scale area).
+ *   aligned, w8a8_fp4_packed_bytes(N, K) bytes: per 16-column block and
+ *   128-deep k-chunk 1088 bytes, the 1 KB of codes as nibbles in the order of
+ *   w8a8_w4a16_quant_weight's layout, then the E8M0 bytes [16 columns][4
+ *   groups]; K padded to 128 with zero codes).
  * w8a8_fp4_linear: x BF16 [M, K] (16-byte aligned) -> y BF16 [M, N] =
  *   BF16(sum_k x[m, k] * 2^E value[n, k]): the dequantized weights are exact
  *   in BF16, products exact, fp32 accumulation from +0 (a -0 weight adds
  *   nothing). Workspace as for w8a8_w4a16_linear.
  */
+int64_t w8a8_fp4_packed_bytes(int64_t N, int64_t K);
 int w8a8_fp4_quant_weight(const uint16_t* w, int64_t N, int64_t K, uint8_t* codes, uint8_t* scales,
                           void* packed, void* stream);
 int w8a8_fp4_linear(const uint16_t* x, int64_t M, int64_t K, const void* w_packed, int64_t N,

@@ -57,6 +57,7 @@ __all__ = [
     "mx_moe_workspace_bytes",
     "mx_moe_grouped",
     "w4a16_packed_bytes",
+    "fp4_packed_bytes",
     "w4a16_quant_weight",
     "w4a16_pack",
     "w4a16_linear_workspace_bytes",
@@ -141,6 +142,7 @@ def _load():
         "w8a8_mx_moe_grouped": (ctypes.c_int, [_c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i64, _c_p,
                                                _c_p, ctypes.c_int, _c_p, _c_p, _c_i64, _c_p]),
         "w8a8_w4a16_packed_bytes": (_c_i64, [_c_i64, _c_i64]),
+        "w8a8_fp4_packed_bytes": (_c_i64, [_c_i64, _c_i64]),
         "w8a8_w4a16_quant_weight": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p]),
         "w8a8_w4a16_pack": (ctypes.c_int, [_c_p, _c_p, _c_i64, _c_i64, _c_p, _c_p]),
         "w8a8_w4a16_linear_workspace_bytes": (_c_i64, [_c_i64, _c_i64]),
@@ -730,6 +732,10 @@ def w4a16_packed_bytes(N: int, K: int) -> int:
     return int(lib.w8a8_w4a16_packed_bytes(N, K))
 
 
+def fp4_packed_bytes(N: int, K: int) -> int:
+    return int(lib.w8a8_fp4_packed_bytes(N, K))
+
+
 def w4a16_quant_weight(w: torch.Tensor, codes: bool = False, scales: bool = False,
                        pack: bool = True):
     """BF16 weight [N, K] -> (int8 codes [N, K] or None, BF16 scales [N, K/32] or
@@ -789,7 +795,7 @@ def fp4_quant_weight(w: torch.Tensor, codes: bool = False, scales: bool = False,
     dev = w.device
     c = torch.empty((N, K), dtype=torch.uint8, device=dev) if codes else None
     s = torch.empty((N, max(K // 32, 1)), dtype=torch.uint8, device=dev) if scales else None
-    p = torch.empty((w4a16_packed_bytes(N, K),), dtype=torch.uint8, device=dev) if pack else None
+    p = torch.empty((fp4_packed_bytes(N, K),), dtype=torch.uint8, device=dev) if pack else None
     _check(lib.w8a8_fp4_quant_weight(_ptr(w), N, K, _ptr(c), _ptr(s), _ptr(p), _stream()))
     return c, s, p
 
@@ -801,7 +807,7 @@ def fp4_linear(x: torch.Tensor, w_packed: torch.Tensor, N: int,
     _need(x, torch.bfloat16, "x", 2)
     _need(w_packed, torch.uint8, "w_packed", 1)
     M, K = x.shape
-    if w_packed.numel() < w4a16_packed_bytes(N, K):
+    if w_packed.numel() < fp4_packed_bytes(N, K):
         raise ValueError("w_packed too small for [N, K]")
     if y is None:
         y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)

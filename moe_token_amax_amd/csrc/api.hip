@@ -772,6 +772,11 @@ int w8a8_w4a16_pack(const int8_t* q, const uint16_t* scale, int64_t N, int64_t K
                   "w4a16_pack");
 }
 
+int64_t w8a8_fp4_packed_bytes(int64_t N, int64_t K) {
+  if (N < 1 || K < 1) return 0;
+  return w8a8::fp4_packed_bytes(N, K);
+}
+
 int w8a8_fp4_quant_weight(const uint16_t* w, int64_t N, int64_t K, uint8_t* codes, uint8_t* scales,
                           void* packed, void* stream) {
   int st = check_w4("fp4_quant_weight", N, K);

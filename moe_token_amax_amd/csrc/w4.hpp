@@ -10,6 +10,8 @@ namespace w8a8 {
 // 16-column block and chunk)
 int64_t w4_chunks(int64_t K);
 int64_t w4_packed_bytes(int64_t N, int64_t K);
+// FP4: 1088 bytes per 16-column block and chunk (1 KB of codes, 64 E8M0 bytes)
+int64_t fp4_packed_bytes(int64_t N, int64_t K);
 // BF16 w [N, K] -> codes (int8, may be null), BF16 scales [N, K/32] (may be
 // null) and the packed layout (may be null)
 hipError_t launch_w4_quant_pack(const uint16_t* w, int64_t N, int64_t K, int8_t* q, uint16_t* s,

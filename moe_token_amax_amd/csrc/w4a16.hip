@@ -29,6 +29,8 @@
 namespace w8a8 {
 
 constexpr int kW4Group = 32, kW4Chunk = 128, kW4ChunkBytes = 1152;
+// FP4 chunks: the 1 KB of codes, then the 16 x 4 E8M0 bytes
+constexpr int kFp4ChunkBytes = 1088;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -179,10 +181,9 @@ __global__ __launch_bounds__(256) void fp4_quant_pack_kernel(const uint16_t* __r
     if (s_out && live && (lane >> 4) == 0) s_out[n * (K / kW4Group) + k0 / kW4Group] = (uint8_t)sb;
   }
   if (packed) {
-    uint8_t* base = packed + unit * kW4ChunkBytes;
+    uint8_t* base = packed + unit * kFp4ChunkBytes;
     reinterpret_cast<uint4*>(base)[lane] = uint4{words[0], words[1], words[2], words[3]};
     if (lane < 16) reinterpret_cast<uint32_t*>(base + 1024)[lane] = sbytes;
-    else if (lane < 32) reinterpret_cast<uint32_t*>(base + 1024)[lane] = 0u;  // unused half
   }
 }
 
@@ -258,7 +259,8 @@ __global__ __launch_bounds__(64 * WAVES) void w4a16_decode_kernel(const uint16_t
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t nb = blockIdx.x;
   const int64_t row0 = (int64_t)blockIdx.y * 16 * MB;
-  const uint8_t* wblk = wp + nb * KC * kW4ChunkBytes;
+  constexpr int64_t kChunkBytes = FMT == 0 ? kW4ChunkBytes : kFp4ChunkBytes;
+  const uint8_t* wblk = wp + nb * KC * kChunkBytes;
   // A rows of this lane (row l % 16 of each 16-row block). Rows past M read
   // row M - 1 instead: an MFMA output row depends on its own A row only, and
   // those output rows are not stored.
@@ -281,7 +283,7 @@ __global__ __launch_bounds__(64 * WAVES) void w4a16_decode_kernel(const uint16_t
     for (int u = 0; u < UNR; ++u) {
       const int64_t kc = c0 + WAVES * u;
       if (kc >= KC) continue;  // wavefront-uniform; a chunk past KC is never used
-      const uint8_t* ch = wblk + kc * kW4ChunkBytes;
+      const uint8_t* ch = wblk + kc * kChunkBytes;
       codes[u] = reinterpret_cast<const uint4*>(ch)[lane];
       if (FMT == 0) sc[u] = reinterpret_cast<const uint2*>(ch + 1024)[lane & 15];
       else sc[u].x = reinterpret_cast<const uint32_t*>(ch + 1024)[lane & 15];
@@ -362,6 +364,7 @@ __global__ __launch_bounds__(64 * WAVES) void w4a16_decode_kernel(const uint16_t
 // ---------------------------------------------------------------------------
 int64_t w4_chunks(int64_t K) { return (K + kW4Chunk - 1) / kW4Chunk; }
 int64_t w4_packed_bytes(int64_t N, int64_t K) { return (N + 15) / 16 * w4_chunks(K) * kW4ChunkBytes; }
+int64_t fp4_packed_bytes(int64_t N, int64_t K) { return (N + 15) / 16 * w4_chunks(K) * kFp4ChunkBytes; }
 
 hipError_t launch_w4_quant_pack(const uint16_t* w, int64_t N, int64_t K, int8_t* q, uint16_t* s,
                                 uint8_t* packed, hipStream_t stream) {

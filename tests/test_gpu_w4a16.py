@@ -148,8 +148,10 @@ def test_w4a16_zero_rows(w):
 # ---------------------------------------------------------------------------
 
 def _unpack_fp4(buf, N, K):
+    """Test-side inverse of the FP4 layout: 1088-byte chunks (1 KB of codes in
+    the INT4 layout's order, then the E8M0 bytes [16 columns][4 groups])."""
     NB, KC = -(-N // 16), -(-K // 128)
-    b = np.asarray(buf, np.uint8)[:NB * KC * 1152].reshape(NB, KC, 1152)
+    b = np.asarray(buf, np.uint8)[:NB * KC * 1088].reshape(NB, KC, 1088)
     codes = b[:, :, :1024].reshape(NB, KC, 4, 16, 4, 4)
     nib = np.stack([codes & 0xF, codes >> 4], axis=-1).reshape(NB, KC, 4, 16, 4, 8)
     c = nib.transpose(0, 3, 1, 4, 2, 5).reshape(NB * 16, KC * 128)[:N, :K]
@@ -170,6 +172,7 @@ def test_fp4_quant_and_pack_bit_exact(w, N, K):
     cu, su = _unpack_fp4(host(p), N, K)
     _assert_eq(cu, c_o, "packed codes")
     _assert_eq(su, s_o, "packed scales")
+    assert p.numel() == w.fp4_packed_bytes(N, K) == -(-N // 16) * -(-K // 128) * 1088
 
 
 def _check_fp4_linear(y_bits, x_bits, c, s):

@@ -205,6 +205,9 @@ def test_w4a16_validation_before_launch(w):
     # 1152 bytes per 16 columns and 128-deep chunk; K padded to 128, N to 16
     assert L.w8a8_w4a16_packed_bytes(4096, 7168) == 256 * 56 * 1152
     assert L.w8a8_w4a16_packed_bytes(17, 160) == 2 * 2 * 1152
+    assert L.w8a8_fp4_packed_bytes(4096, 7168) == 256 * 56 * 1088
+    assert L.w8a8_fp4_packed_bytes(17, 160) == 2 * 2 * 1088
+    assert L.w8a8_fp4_packed_bytes(0, 160) == 0
     assert L.w8a8_w4a16_quant_weight(p, 16, 100, p, p, p, None) == 4          # K % 32
     assert L.w8a8_w4a16_quant_weight(p, 0, 64, p, p, p, None) == 2
     assert L.w8a8_w4a16_quant_weight(p, 16, 64, None, None, None, None) == 1   # no output
