@@ -1074,7 +1074,7 @@ __global__ __launch_bounds__(WM* WN* kWave) void grouped_mixed_kernel(GemmArgs p
 // per-wave INT32 partial sums are added in LDS and the epilogue runs on the
 // full sums: one kernel, no workspace, no second pass. Grid = ceil(N / 16).
 // ---------------------------------------------------------------------------
-template <int MB, int NBW, int WAVES, int UNR, bool AVEC, bool ABLK = false>
+template <int MB, int NBW, int WAVES, int UNR, bool AVEC, bool ABLK = false, bool PF = false>
 __global__ __launch_bounds__(WAVES* kWave) void decode_gemm_kernel(GemmArgs p) {
   static_assert(MB * NBW <= WAVES, "one wavefront per output block in the epilogue");
   __shared__ i32x4 red[WAVES][MB * NBW][kWave];
@@ -1104,6 +1104,19 @@ __global__ __launch_bounds__(WAVES* kWave) void decode_gemm_kernel(GemmArgs p) {
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
     for (int j = 0; j < NBW; ++j) acc[mb][j] = i32x4{0, 0, 0, 0};
+  // PF: the weights of the next round are loaded before this round's MFMAs
+  // (after its activation loads), so that their HBM latency overlaps them
+  i32x4 bn[PF ? UNR : 1][NBW];
+  if (PF) {
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const int kb = wave + u * WAVES;
+      const int kbc = kb < p.KB ? kb : p.KB - 1;
+#pragma unroll
+      for (int j = 0; j < NBW; ++j)
+        bn[u][j] = *reinterpret_cast<const i32x4*>(wcol[j] + (int64_t)kbc * kBlockBytes);
+    }
+  }
   for (int kb0 = wave; kb0 < p.KB; kb0 += WAVES * UNR) {
     i32x4 b[UNR][NBW];
     i32x4 a[UNR][MB];
@@ -1113,7 +1126,7 @@ __global__ __launch_bounds__(WAVES* kWave) void decode_gemm_kernel(GemmArgs p) {
       const int kbc = kb < p.KB ? kb : p.KB - 1;    // clamped: loads stay in bounds
 #pragma unroll
       for (int j = 0; j < NBW; ++j)
-        b[u][j] = *reinterpret_cast<const i32x4*>(wcol[j] + (int64_t)kbc * kBlockBytes);
+        b[u][j] = PF ? bn[u][j] : *reinterpret_cast<const i32x4*>(wcol[j] + (int64_t)kbc * kBlockBytes);
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
         const int64_t row = mb * 16 + (lane & 15);
@@ -1132,6 +1145,16 @@ __global__ __launch_bounds__(WAVES* kWave) void decode_gemm_kernel(GemmArgs p) {
         } else {
           a[u][mb] = load_a16(p, row, p.M, kcol);
         }
+      }
+    }
+    if (PF && kb0 + WAVES * UNR < p.KB) {  // wave-uniform
+#pragma unroll
+      for (int u = 0; u < UNR; ++u) {
+        const int kb = kb0 + WAVES * UNR + u * WAVES;
+        const int kbc = kb < p.KB ? kb : p.KB - 1;
+#pragma unroll
+        for (int j = 0; j < NBW; ++j)
+          bn[u][j] = *reinterpret_cast<const i32x4*>(wcol[j] + (int64_t)kbc * kBlockBytes);
       }
     }
     // keep every load of this round ahead of the first MFMA: without the
@@ -1343,7 +1366,7 @@ const DenseVariant kDense[] = {
     // 7..9: M <= 16 / 32 / 64 with packed A (1 KB blocks)
     {16, 16, decode_gemm_kernel<1, 1, kDecodeWaves, 14, true, true>, kDecodeWaves * 64, true, 1},
     {32, 16, decode_gemm_kernel<2, 1, kDecodeWaves, 14, true, true>, kDecodeWaves * 64, true, 1},
-    {64, 16, decode_gemm_kernel<4, kNbw64, kDecodeWaves, kUnr64, true, true>, kDecodeWaves * 64, true, kNbw64},
+    {64, 16, decode_gemm_kernel<4, kNbw64, kDecodeWaves, kUnr64, true, true, true>, kDecodeWaves * 64, true, kNbw64},
 };
 
 }  // namespace
