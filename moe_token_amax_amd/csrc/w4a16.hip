@@ -273,6 +273,18 @@ __global__ __launch_bounds__(64 * WAVES) void w4a16_decode_kernel(const uint16_t
   f32x4 acc[MB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // one chunk per round (UNR 1): the next round's codes and scales are loaded
+  // before this round's dequantization, so their HBM latency overlaps it
+  constexpr bool PF = UNR == 1;
+  auto load_w = [&](int64_t kc, uint4& c, uint2& sv) {
+    const uint8_t* ch = wblk + kc * kChunkBytes;
+    c = reinterpret_cast<const uint4*>(ch)[lane];
+    if (FMT == 0) sv = reinterpret_cast<const uint2*>(ch + 1024)[lane & 15];
+    else sv.x = reinterpret_cast<const uint32_t*>(ch + 1024)[lane & 15];
+  };
+  uint4 codes_n = uint4{0u, 0u, 0u, 0u};
+  uint2 sc_n = uint2{0u, 0u};
+  if (PF && wave < KC) load_w(wave, codes_n, sc_n);
   for (int64_t c0 = wave; c0 < KC; c0 += WAVES * UNR) {
     // all loads of UNR chunks first (codes, scales and the activation
     // fragments), then the dequantization and the MFMAs
@@ -283,10 +295,12 @@ __global__ __launch_bounds__(64 * WAVES) void w4a16_decode_kernel(const uint16_t
     for (int u = 0; u < UNR; ++u) {
       const int64_t kc = c0 + WAVES * u;
       if (kc >= KC) continue;  // wavefront-uniform; a chunk past KC is never used
-      const uint8_t* ch = wblk + kc * kChunkBytes;
-      codes[u] = reinterpret_cast<const uint4*>(ch)[lane];
-      if (FMT == 0) sc[u] = reinterpret_cast<const uint2*>(ch + 1024)[lane & 15];
-      else sc[u].x = reinterpret_cast<const uint32_t*>(ch + 1024)[lane & 15];
+      if (PF) {
+        codes[u] = codes_n;
+        sc[u] = sc_n;
+      } else {
+        load_w(kc, codes[u], sc[u]);
+      }
       // the activation fragment of step j, 16-row block mb (k = 128 kc + 32 j)
       auto afrag = [&](int j, int mb) -> bf16x8 {
         const int64_t k = kc * kW4Chunk + 32 * j;
@@ -314,6 +328,7 @@ __global__ __launch_bounds__(64 * WAVES) void w4a16_decode_kernel(const uint16_t
             a[u][j][mb] = kc * kW4Chunk + 32 * j < K ? afrag(j, mb) : bf16x8{};
       }
     }
+    if (PF && c0 + WAVES < KC) load_w(c0 + WAVES, codes_n, sc_n);  // wavefront-uniform
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
       const int64_t kc = c0 + WAVES * u;
