@@ -1212,10 +1212,11 @@ __device__ __forceinline__ uint32_t bf16_pair_absmax(uint32_t w) {
   return max(w & 0x7FFFu, (w >> 16) & 0x7FFFu);
 }
 
-template <int UNR>
-__global__ __launch_bounds__(8 * kWave) void decode_fused_kernel(GemmArgs p) {
-  constexpr int WAVES = 8, kThreadsF = WAVES * kWave;
-  constexpr int kRows = 4, kCpt = 4;  // rows, 8-value chunks per thread and row (K <= 16384)
+template <int UNR, int WAVES = 8>
+__global__ __launch_bounds__(WAVES * kWave) void decode_fused_kernel(GemmArgs p) {
+  constexpr int kThreadsF = WAVES * kWave;
+  // rows, 8-value chunks per thread and row (K <= 16384 = kCpt * kThreadsF * 8)
+  constexpr int kRows = 4, kCpt = 32 / WAVES;
   __shared__ i32x4 red[WAVES][kWave];
   __shared__ uint32_t wmax[WAVES][kRows];
   __shared__ float srow[kRows];
@@ -1472,7 +1473,7 @@ hipError_t launch_decode_fused(const uint16_t* x, int64_t M, int64_t K, const vo
   GemmArgs p = make_args(reinterpret_cast<const int8_t*>(x), nullptr, M, K, w_packed, w_scale, N, bias,
                          y, out);
   const size_t lds = (size_t)(M * round_up(K, 64));
-  hipLaunchKernelGGL(decode_fused_kernel<14>, dim3((unsigned)ceil_div(N, 16)), dim3(8 * 64), lds, stream,
+  hipLaunchKernelGGL((decode_fused_kernel<7, 16>), dim3((unsigned)ceil_div(N, 16)), dim3(16 * 64), lds, stream,
                      p);
   return hipGetLastError();
 }
