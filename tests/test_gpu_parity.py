@@ -348,7 +348,10 @@ def test_dynamic_quant_packed_bit_exact(w, M, K):
 
 
 PACKED_LINEAR_SHAPES = [(1, 4096, 7168), (4, 256, 512), (16, 4096, 7168), (33, 300, 1024),
-                        (64, 512, 7168), (65, 300, 520), (300, 1088, 600), (520, 512, 1024)]
+                        (64, 512, 7168), (65, 300, 520), (300, 1088, 600), (520, 512, 1024),
+                        # M <= 64 with two k-iterations per wavefront (next weights loaded
+                        # ahead), a ragged last k-block and a clamped fourth m-block
+                        (40, 264, 7000)]
 
 
 @pytest.mark.parametrize("M,N,K", PACKED_LINEAR_SHAPES)

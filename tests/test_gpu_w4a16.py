@@ -105,7 +105,10 @@ def _check_linear(y_bits, x_bits, q, s):
 # (M, K, N): decode rows 1 / 4 / 16 / 64, rows past a 16- and a 64-row block,
 # K not a multiple of 128, N not a multiple of 16
 LINEAR_CASES = [(1, 256, 64), (4, 1024, 96), (16, 512, 50), (17, 320, 64), (64, 2048, 512),
-                (100, 2048, 256), (3, 96, 40), (1, 7168, 4096)]
+                (100, 2048, 256), (3, 96, 40), (1, 7168, 4096),
+                # M > 16 with several chunks per wavefront (the next chunk's codes
+                # loaded ahead), a ragged last chunk (K % 128 = 64), ragged N
+                (80, 4160, 72)]
 
 
 @pytest.mark.parametrize("M,K,N", LINEAR_CASES)
