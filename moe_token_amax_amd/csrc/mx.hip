@@ -241,6 +241,26 @@ __device__ __forceinline__ void mx_wait_barrier() {
 
 typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// 2^(b - 127) for an E8M0 byte b (b = 0 gives the fp32 subnormal 2^-127)
+__device__ __forceinline__ float e8m0_scale(uint32_t b) { return __builtin_ldexpf(1.0f, (int)b - 127); }
+
+// Eight E4M3 codes (bytes of lo, then hi) times sc = 2^E as BF16, two per
+// instruction with gfx950's MX conversion v_cvt_scalef32_pk_bf16_fp8. The
+// product is exact: an E4M3 value has at most 4 significant bits, and for a
+// group scale of a BF16 source (E <= 119) code * 2^E stays inside the BF16
+// range. So the BF16 MFMA below multiplies the exact dequantized operands and
+// its products (at most 8 x 8 significant bits) are exact in fp32.
+__device__ __forceinline__ bf16x8 mx_dequant8(uint32_t lo, uint32_t hi, float sc) {
+  const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, sc, false);
+  const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, sc, true);
+  const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, sc, false);
+  const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, sc, true);
+  return __builtin_bit_cast(bf16x8, uint4{__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
+                                          __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3)});
+}
 
 template <int BM_>
 struct MxTile {
@@ -354,16 +374,16 @@ struct MxTile {
   struct Frags {
     i32x8 a[TM];
     i32x8 b[TN];
-    int sa[TM];
-    int sb[TN];
+    uint32_t sa[TM];  // E8M0 bytes of the lane's row: group 0 | group 1 << 8
+    uint32_t sb[TN];
   };
 
-  // Operand of 32 rows (columns) starting at 16-row block 2i. The scaled
-  // 32x32x64 MFMA takes, in lane l (row l & 31, h = l >> 5), bytes 0..15 =
-  // k [16h, 16h + 16) of the first 32-group and bytes 16..31 = k [32 + 16h,
-  // 48 + 16h) of the second, and lane l's scale byte belongs to group h. So
-  // lane l reads block 2i + (l>>4 & 1), row l & 15, 16-byte k-chunks h and
-  // h + 2, and the scale of (row, group h).
+  // Operand of 32 rows (columns) starting at 16-row block 2i. Lane l (row
+  // l & 31, h = l >> 5) reads block 2i + (l>>4 & 1), row l & 15, 16-byte
+  // k-chunks h and h + 2: bytes 0..15 hold k [16h, 16h + 16) of the
+  // k-block's first 32-group, bytes 16..31 hold k [32 + 16h, 48 + 16h) of
+  // the second. A and B fragments use the same lane -> k mapping, so every
+  // MFMA below pairs equal k.
   __device__ __forceinline__ static i32x8 read_operand(const uint8_t* blk, int lane) {
     const uint8_t* q = blk + (((lane >> 4) & 1) * 1024) + ((lane >> 5) * 16 + (lane & 15)) * 16;
     const i32x4 lo = *reinterpret_cast<const i32x4*>(q);
@@ -373,32 +393,49 @@ struct MxTile {
 
   __device__ __forceinline__ static void read_frags(const uint8_t* st, Frags& f, int wm, int wn,
                                                     int lane) {
-    const int r = lane & 31, g = lane >> 5;
+    const int r = lane & 31;
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
       const int c32 = wn * TN + j;
       f.b[j] = read_operand(st + (kABlocks + c32 * 2) * 1024, lane);
-      f.sb[j] = st[kScaleOfs + 512 + (c32 * 32 + r) * 2 + g];
+      f.sb[j] = *reinterpret_cast<const uint16_t*>(st + kScaleOfs + 512 + (c32 * 32 + r) * 2);
     }
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       const int r32 = wm * TM + i;
       f.a[i] = read_operand(st + r32 * 2 * 1024, lane);
-      f.sa[i] = st[kScaleOfs + (r32 * 32 + r) * 2 + g];
+      f.sa[i] = *reinterpret_cast<const uint16_t*>(st + kScaleOfs + (r32 * 32 + r) * 2);
     }
   }
 
-  __device__ __forceinline__ static void mfma_row(const Frags& f, f32x16 (&acc)[TM][TN], int i) {
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[i], f.b[j], acc[i][j], 0, 0, 0,
-                                                                  f.sa[i], 0, f.sb[j]);
+  // The 32 codes of a fragment times their group's 2^E as BF16 (exact:
+  // mx_dequant8), four MFMA operands of 8 values (k-steps t = 0..3; t < 2 in
+  // group 0, t >= 2 in group 1).
+  __device__ __forceinline__ static void dequant_frag(const i32x8& v, uint32_t sc, bf16x8 (&o)[4]) {
+    const float s0 = e8m0_scale(sc & 0xFFu), s1 = e8m0_scale((sc >> 8) & 0xFFu);
+    o[0] = mx_dequant8((uint32_t)v[0], (uint32_t)v[1], s0);
+    o[1] = mx_dequant8((uint32_t)v[2], (uint32_t)v[3], s0);
+    o[2] = mx_dequant8((uint32_t)v[4], (uint32_t)v[5], s1);
+    o[3] = mx_dequant8((uint32_t)v[6], (uint32_t)v[7], s1);
   }
 
+  // One k-block: B fragments dequantized once, then per accumulator row the A
+  // fragment and 4 x TN MFMAs of 32 x 32 x 16 (exact BF16 products, fp32 sums).
   __device__ __forceinline__ static void mfma_rows(const Frags& f, f32x16 (&acc)[TM][TN], int lo,
                                                    int hi) {
+    bf16x8 bq[TN][4];
 #pragma unroll
-    for (int i = lo; i < hi; ++i) mfma_row(f, acc, i);
+    for (int j = 0; j < TN; ++j) dequant_frag(f.b[j], f.sb[j], bq[j]);
+#pragma unroll
+    for (int i = lo; i < hi; ++i) {
+      bf16x8 aq[4];
+      dequant_frag(f.a[i], f.sa[i], aq);
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[t], bq[j][t], acc[i][j], 0, 0, 0);
+    }
   }
 
   // K loop in pairs of k-blocks over a five-buffer ring: one wait + barrier

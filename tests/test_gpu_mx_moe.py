@@ -2,12 +2,10 @@
 
 The one-expert-at-a-time preparation (payload written back over the source
 bytes, E8M0 scales, kernel layout) and the SwiGLU -> BF16 -> MX quant are
-compared exactly. The grouped block-scaled matmul is compared with the float64
-sum of the exactly dequantized products under the dense MX GEMM's derived
-tolerance (the BF16 bound plus the MFMA's per-group truncation allowance). The
-chain is its two grouped calls, each held to that tolerance (the second on the
-oracle's own W13 output), and its rows are compared with the oracle's chain
-under a normwise bound derived in the tests.
+compared exactly. Every output of the grouped block-scaled matmul is held to
+max(2**-8 |ref|, 1e-5) against the float64 sum of the exactly dequantized
+products. The chain is compared with the oracle's chain element by element
+(see ``_check_chain``).
 Inputs are seeded (``synth``); expected values come only from ``oracle``.
 """
 
@@ -21,7 +19,7 @@ import oracle as O
 import synth
 from tests.conftest import gpu_available
 from tests.gpu_util import bf16_dev, bf16_host, dev, host, show, sync
-from tests.test_gpu_mx import _assert_mx, _mx_allowance
+from tests.test_gpu_mx import _assert_mx
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
@@ -108,19 +106,16 @@ def test_mx_swiglu_quant_bit_exact(w, R, I, alg):
 
 
 def _per_expert(gl, yh, ap, as_, wp, ws, what):
-    """Every output within the MX GEMM tolerance of its expert's float64 product;
-    the share that meets the BF16 bound alone is taken over all the outputs
-    (a population figure, not one per expert of a few rows)."""
+    """Every output within the BF16 bound of its expert's float64 product."""
     off = O.group_offsets(gl)
-    refs, allows, rows = [], [], []
+    refs, rows = [], []
     for e in range(len(gl)):
         a, b = int(off[e]), int(off[e + 1])
         if b == a:
             continue
         refs.append(MX.mx_gemm_ref64(ap[a:b], as_[a:b], wp[e], ws[e]))
-        allows.append(_mx_allowance(ap[a:b], as_[a:b], wp[e], ws[e]))
         rows.append(yh[a:b])
-    _assert_mx(np.concatenate(rows), np.concatenate(refs), np.concatenate(allows), what)
+    _assert_mx(np.concatenate(rows), np.concatenate(refs), what)
 
 
 def _grouped_case(counts, N, K, act, seed):
@@ -169,23 +164,113 @@ def test_mx_grouped_gemm_zero_rows(w):
 CHAIN_CASES = [([12, 7, 0, 19], 64, 32), ([0, 200, 3, 0, 70], 256, 128),
                ([300, 5, 190], 512, 256)]
 
-# Normwise distance of a chain row from the oracle's chain: the GPU's W13 sum
-# is fp32, so an output can round to the other BF16 neighbour of the exact
-# value; that moves its SwiGLU output by one BF16 step and, near an E4M3 tie,
-# to the neighbouring code (1/8 of the element at most), which shifts the
-# whole row of W2 outputs by one term's share. The stages themselves are held
-# to the MX GEMM tolerance.
-CHAIN_ROW_TOL = 2.0 ** -4
+# Element-wise check of the chain. The W13 stage sums exact products in fp32,
+# so its BF16 output h can be either BF16 neighbour of the exact sum when that
+# sum lies near a rounding boundary: several chains are correct. The oracle
+# brackets what any fp32 accumulation in 64-deep k-blocks can return (each
+# MFMA step adds a partial sum of at most 16 exact products to the fp32
+# accumulator within one fp32 ulp of the magnitudes involved):
+#   delta = 2^-23 (4 sum_b |S_(b-1)| + 20 sum_k |p_k|),
+# S_b the exact partial sum after k-block b. The admissible h are the BF16
+# roundings of [h64 - delta, h64 + delta]; the GPU's h must be one of them.
+# Where an element has more than one, the oracle bounds how far SwiGLU ->
+# BF16 -> MX quant can move each dequantized value of the row over those
+# choices (_row_delta), Delta[r, k]; a chain output may then move by
+# sum_k Delta[r, k] |W2[n, k]| on top of the BF16 bound. Rows without such
+# an element are held to the BF16 bound alone.
+U23 = 2.0 ** -23
 
 
+def _accumulation_bound(A, W):
+    """(delta, exact sums) of the product A @ W.T over dequantized operands."""
+    S = np.zeros((A.shape[0], W.shape[0]))
+    tot = np.zeros_like(S)
+    for k0 in range(0, A.shape[1], 64):
+        tot += 4.0 * np.abs(S)
+        S += A[:, k0:k0 + 64] @ W[:, k0:k0 + 64].T
+    return U23 * (tot + 20.0 * (np.abs(A) @ np.abs(W).T)) * 1.01, S
+
+
+def _bf16_of64(v):
+    return O.f32_to_bf16(np.asarray(v, np.float64).astype(np.float32))
+
+
+def _row_delta(h_o, lo, hi, inter, base_deq):
+    """Largest change of each dequantized SwiGLU-MX value of one row when every
+    element of h (BF16 bits, [gate | up]) may take any value of its admissible
+    range [lo, hi] instead of the oracle's h_o. Interval bound: a = BF16(silu(g)
+    * u) is evaluated at the corners of its (gate, up) box (over such a short
+    range both factors are monotone), the group's shared exponent can be any
+    E of its amax range, and for each such E the quantizer (monotone) maps the
+    ends of an element's range to the ends of its codes."""
+    hs = [h_o]
+    for gsel in (lo, hi):
+        for usel in (lo, hi):
+            hs.append(np.concatenate([gsel[:inter], usel[inter:]]))
+    a = O.bf16_to_f32(O.f32_to_bf16(O.swiglu(np.stack(hs), inter))).astype(np.float64)
+    a_min, a_max = a.min(axis=0), a.max(axis=0)
+    abs_min = np.where((a_min <= 0) & (a_max >= 0), 0.0, np.minimum(np.abs(a_min), np.abs(a_max)))
+    abs_max = np.maximum(np.abs(a_min), np.abs(a_max))
+    G = inter // 32
+    e_lo = MX.mx_shared_exponent(abs_min.reshape(G, 32).max(axis=1))
+    e_hi = MX.mx_shared_exponent(abs_max.reshape(G, 32).max(axis=1))
+    base = base_deq.reshape(G, 32)
+    delta = np.zeros((G, 32))
+    for de in range(int((e_hi - e_lo).max()) + 1):
+        E = np.minimum(e_lo + de, e_hi)[:, None].astype(np.float64)
+        for v in (a_min, a_max):
+            q = MX.e4m3_decode(MX.e4m3_encode(np.ldexp(v.reshape(G, 32), -E.astype(np.int64))))
+            delta = np.maximum(delta, np.abs(np.ldexp(q, E.astype(np.int64)) - base))
+    return delta.reshape(inter)
+
+
+def _check_chain(gl, st, o13, o2, h_gpu, y_gpu, what):
+    """h_gpu within the admissible W13 outputs; every chain output within the
+    BF16 bound of the oracle chain's float64 W2 sum plus the allowance of its
+    row (zero for rows whose h has a single admissible value)."""
+    inter = o13[0].shape[1] // 2
+    off = O.group_offsets(gl)
+    hv = O.bf16_to_f32(h_gpu).astype(np.float64)
+    yv = O.bf16_to_f32(y_gpu).astype(np.float64)
+    n_two = n_rows = n_used = 0
+    worst = 0.0
+    for e in range(len(gl)):
+        a, b = int(off[e]), int(off[e + 1])
+        if b == a:
+            continue
+        A1 = MX.mx_dequant(st["q1"][a:b], st["s1"][a:b])
+        d, h64 = _accumulation_bound(A1, MX.mx_dequant(o13[0][e], o13[1][e]))
+        lo, hi = _bf16_of64(h64 - d), _bf16_of64(h64 + d)
+        lv, hv_ = O.bf16_to_f32(lo).astype(np.float64), O.bf16_to_f32(hi).astype(np.float64)
+        inside = (hv[a:b] >= lv) & (hv[a:b] <= hv_)
+        assert inside.all(), (f"{what}: W13 output outside the fp32-accumulation range at "
+                              f"{np.argwhere(~inside)[0].tolist()} (expert {e})")
+        W2 = MX.mx_dequant(o2[0][e], o2[1][e])
+        A2 = MX.mx_dequant(st["q2"][a:b], st["s2"][a:b])
+        y64 = A2 @ W2.T
+        allow = np.zeros_like(y64)
+        for r in range(b - a):
+            if (lo[r] != hi[r]).any():
+                n_two += int((lo[r] != hi[r]).sum())
+                n_rows += 1
+                allow[r] = np.abs(W2) @ _row_delta(st["h"][a + r], lo[r], hi[r], inter, A2[r])
+        base = np.maximum(O.REL_TOL * np.abs(y64), O.ABS_FLOOR)
+        err = np.abs(yv[a:b] - y64)
+        n_used += int((err > base).sum())
+        worst = max(worst, float(np.max(err / (base + 1.004 * allow))))
+        ok = err <= base + 1.004 * allow
+        assert ok.all(), (f"{what}: chain output {np.argwhere(~ok)[0].tolist()} of expert {e} "
+                          f"outside the bound + allowance")
+    show(f"  {what}: {n_two} W13 outputs with two admissible values in {n_rows} rows; "
+         f"{n_used} chain outputs past the BF16 bound alone; max err/tolerance {worst:.4f}")
 
 
 @pytest.mark.parametrize("counts,H,I", CHAIN_CASES)
 def test_mx_moe_chain(w, counts, H, I):
     """The chain equals its two grouped calls bit for bit; stage 1 is within the
-    MX GEMM tolerance of the oracle's W13; stage 2 run on the oracle's own W13
-    output is within the tolerance of the oracle's W2; the chain's rows are
-    within CHAIN_ROW_TOL (normwise) of the oracle's chain."""
+    BF16 bound of the oracle's W13; stage 2 run on the oracle's own W13 output
+    is within the bound of the oracle's W2; every chain output is within the
+    bound (plus its row's rounding allowance) of the oracle's chain."""
     show(f"mx_moe chain counts={counts} H={H} I={I}")
     gl = np.asarray(counts, np.int64)
     E, R = len(gl), int(gl.sum())
@@ -206,20 +291,16 @@ def test_mx_moe_chain(w, counts, H, I):
     _assert_eq(bf16_host(y), bf16_host(y2), "chain == two grouped calls")
     _per_expert(gl, bf16_host(h), st["q1"], st["s1"], *o13, "W13")
     _per_expert(gl, bf16_host(y3), st["q2"], st["s2"], *o2, "W2 on the oracle's h")
-    yh = O.bf16_to_f32(bf16_host(y)).astype(np.float64)
-    yo = O.bf16_to_f32(st["y"]).astype(np.float64)
-    rel = np.linalg.norm(yh - yo, axis=1) / np.maximum(np.linalg.norm(yo, axis=1), 1e-30)
-    show(f"  chain rows: max normwise distance {rel.max():.2e}, identical rows {np.mean(rel == 0):.3f}")
-    assert np.all(rel <= CHAIN_ROW_TOL)
+    _check_chain(gl, st, o13, o2, bf16_host(h), bf16_host(y), "chain")
 
 
-@pytest.mark.timeout(600)
+@pytest.mark.timeout(900)
 def test_mx_moe_config_sampled_rows(w):
     """The MoE workload with MXFP8 experts at full size. Experts of the sampled
     rows are prepared from their block-FP8 source; the others hold zero bytes
     (valid E4M3 / E8M0, same launch shapes). The oracle recomputes the sampled
-    rows one by one: W13 within the MX GEMM tolerance, the chain within
-    CHAIN_ROW_TOL."""
+    rows one by one: W13 within the BF16 bound, every chain output within the
+    bound plus its row's rounding allowance."""
     show("mx_moe full size, sampled rows")
     m = synth.mx_moe(seed=0)
     E, H, I = m.E, m.H, m.I
@@ -227,7 +308,7 @@ def test_mx_moe_config_sampled_rows(w):
     ex = np.repeat(np.arange(E), m.group_list)
     rng = np.random.default_rng(3)
     big = int(np.argmax(m.group_list))
-    rows = sorted(set(rng.integers(0, m.R, 6).tolist()) | {0, m.R - 1, int(off[big + 1]) - 1})
+    rows = sorted(set(rng.integers(0, m.R, 13).tolist()) | {0, m.R - 1, int(off[big + 1]) - 1})
     experts = sorted({int(ex[r]) for r in rows})
     s13b = w.mx_moe_packed_bytes(1, 2 * I, H)
     s2b = w.mx_moe_packed_bytes(1, H, I)
@@ -243,16 +324,17 @@ def test_mx_moe_config_sampled_rows(w):
     xd, gd = bf16_dev(xr), dev(m.group_list)
     y = w.mx_moe_grouped(xd, gd, p13, p2, I)
     h = w.mx_grouped_gemm(xd, gd, p13, 2 * I)
-    yh = O.bf16_to_f32(bf16_host(y)).astype(np.float64)
+    yh = bf16_host(y)
     hh = bf16_host(h)
     one = np.array([1], np.int64)
+    prepared = {}
     for r in rows:
         e = int(ex[r])
-        wa, sa, wb, sb = src[e]
-        o13 = MM.mx_moe_prepare(wa[None], sa[None], m.bn, m.bk)
-        o2 = MM.mx_moe_prepare(wb[None], sb[None], m.bn, m.bk)
+        if e not in prepared:
+            wa, sa, wb, sb = src[e]
+            prepared = {e: (MM.mx_moe_prepare(wa[None], sa[None], m.bn, m.bk),
+                            MM.mx_moe_prepare(wb[None], sb[None], m.bn, m.bk))}
+        o13, o2 = prepared[e]
         st = MM.mx_moe_grouped(one, xr[r:r + 1], *o13, *o2, keep=True)
         _per_expert(one, hh[r:r + 1], st["q1"], st["s1"], *o13, f"W13 row {r}")
-        want = O.bf16_to_f32(st["y"]).astype(np.float64)[0]
-        rel = np.linalg.norm(yh[r] - want) / max(np.linalg.norm(want), 1e-30)
-        assert rel <= CHAIN_ROW_TOL, (r, e, rel)
+        _check_chain(one, st, o13, o2, hh[r:r + 1], yh[r:r + 1], f"chain row {r} (expert {e})")

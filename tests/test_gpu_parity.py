@@ -154,32 +154,71 @@ def test_tiny_config(w):
     _assert_eq(bf16_host(y), yo, "tiny y")
 
 
-@pytest.mark.parametrize("M", [1, 4, 16, 64])
+def _decode_dispatch(w, M, x, wp, ws_, N, K, bias=None):
+    """The entry points a decode step uses for M rows: BF16 straight into the
+    linear (quant fused into the product) up to 2 rows; row-major codes for 3 to
+    15 rows; codes in the packed 1 KB blocks from 16 rows up."""
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    wsp = torch.empty((max(1, w.linear_workspace_bytes(M, N, K)),), dtype=torch.uint8,
+                      device="cuda")
+    if M <= 2 and K % 8 == 0:
+        w.linear_bf16(x, wp, ws_, N, bias=bias, y=y, workspace=wsp)
+        return "bf16 in (fused quant)", None, y
+    if M >= 16 and K % 8 == 0:
+        qp, sp = w.dynamic_quant_packed(x)
+        w.linear_packed(qp, sp, K, wp, ws_, N, bias=bias, y=y, workspace=wsp)
+        return "packed codes", _unpack_codes(host(qp), M, K), y
+    q, s = w.dynamic_quant(x)
+    w.linear(q, s, wp, ws_, N, bias=bias, y=y, workspace=wsp)
+    return "row-major codes", host(q), y
+
+
+@pytest.mark.parametrize("M", [1, 2, 4, 16, 64])
 def test_decode_config_full(w, M):
-    show(f"decode M={M}")
+    """The decode workload in full (M x 4096 x 7168), through the same entry
+    points and workspace the benchmark step uses; codes and BF16 outputs equal
+    the oracle's bit for bit."""
     d = synth.decode(seed=0, M=M)
-    q, s, y = _run_linear(w, d, w.OUT_BF16)
+    wp = w.prepack_weight(dev(d.w))
+    path, q, y = _decode_dispatch(w, M, bf16_dev(d.x), wp, dev(d.w_scale), d.N, d.K)
+    sync()
+    show(f"decode M={M}: {path}")
     qo, so = O.dynamic_quant(d.x)
-    _assert_eq(host(q), qo, "q")
+    if q is not None:
+        _assert_eq(q, qo, "q")
     yo, acc = O.linear(qo, so, d.w, d.w_scale, None)
     yh = bf16_host(y)
-    _assert_eq(yh, yo, "y")
+    _assert_eq(yh, yo, f"y ({path})")
     assert O.bf16_within_tolerance(yh, O.linear_ref64(acc, so, d.w_scale, None)).all()
 
 
-@pytest.mark.timeout(300)
-def test_prefill_config_sampled_rows(w):
-    show("prefill full size, sampled rows")
+@pytest.mark.timeout(600)
+def test_prefill_config_full(w):
+    """The prefill workload in full (8192 x 4096 x 7168 with bias), every row:
+    the packed path the benchmark step takes (codes in 1 KB blocks, LDS-DMA
+    tiles) and the row-major path, INT32 and BF16 against the oracle."""
+    show("prefill full size, all rows")
     d = synth.prefill(seed=0)
-    q, s, y = _run_linear(w, d, w.OUT_BF16)
+    x = bf16_dev(d.x)
+    wp = w.prepack_weight(dev(d.w))
+    ws_, bias = dev(d.w_scale), bf16_dev(d.bias)
+    qp, sp = w.dynamic_quant_packed(x)
+    acc_pk = host(w.linear_packed(qp, sp, d.K, wp, ws_, d.N, out=w.OUT_I32))
+    y_pk = bf16_host(w.linear_packed(qp, sp, d.K, wp, ws_, d.N, bias=bias))
+    q, s = w.dynamic_quant(x)
+    y_rm = bf16_host(w.linear(q, s, wp, ws_, d.N, bias=bias))
+    sync()
     qo, so = O.dynamic_quant(d.x)
     _assert_eq(host(q), qo, "q")
-    _assert_eq(host(s), so, "scale")
-    rng = np.random.default_rng(0)
-    rows = np.unique(np.concatenate([[0, 8191], rng.integers(0, 8192, 30)]))
-    yo, acc = O.linear(qo[rows], so[rows], d.w, d.w_scale, d.bias)
-    yh = bf16_host(y)[rows]
-    _assert_eq(yh, yo, "y rows")
+    _assert_eq(host(s).view(np.uint32), so.view(np.uint32), "scale")
+    _assert_eq(_unpack_codes(host(qp), d.M, d.K), qo, "q (blocks)")
+    _assert_eq(host(sp).view(np.uint32), so.view(np.uint32), "scale (packed path)")
+    del q, s, qp, sp
+    yo, acc = O.linear(qo, so, d.w, d.w_scale, d.bias)
+    _assert_eq(acc_pk, acc.astype(np.int32), "acc (packed)")
+    _assert_eq(y_pk, yo, "y (packed)")
+    _assert_eq(y_rm, yo, "y (row-major)")
+    assert O.bf16_within_tolerance(y_pk, O.linear_ref64(acc, so, d.w_scale, d.bias)).all()
 
 
 # ---------------------------------------------------------------------------
@@ -285,10 +324,13 @@ def test_moe_chain_bit_exact(w, counts, H, I):
     _assert_eq(bf16_host(y2), st["y"], "y (int8 input)")
 
 
-@pytest.mark.timeout(600)
-def test_moe_config_sampled_rows(w):
-    """Full MoE workload; the oracle recomputes a sample of rows one by one."""
-    show("moe full size, sampled rows")
+@pytest.mark.timeout(900)
+def test_moe_config_all_rows(w):
+    """Full MoE workload (2048 tokens top-8 over 256 experts, H 4096, I 2048):
+    every one of the 16384 output rows against the oracle, one expert at a
+    time (the oracle's chain on that expert's rows alone; experts are
+    independent, so this is the oracle's whole chain)."""
+    show("moe full size, all rows")
     m = synth.moe(seed=0)
     E, H, I = m.E, m.H, m.I
     w13p = torch.empty(w.packed_weight_bytes(E, 2 * I, H), dtype=torch.uint8, device="cuda")
@@ -303,19 +345,21 @@ def test_moe_config_sampled_rows(w):
     y = w.moe_grouped(bf16_dev(xr), dev(m.group_list), w13p, dev(m.w13_scale), w2p,
                       dev(m.w2_scale))
     yh = bf16_host(y)
-    ex = O.expert_of_rows(m.group_list)
-    rng = np.random.default_rng(1)
+    del w13p, w2p
     off = O.group_offsets(m.group_list)
-    rows = set(rng.integers(0, m.R, 24).tolist())
-    big = int(np.argmax(m.group_list))
-    rows |= {int(off[big]), int(off[big + 1]) - 1, 0, m.R - 1}
-    for r in sorted(rows):
-        e = int(ex[r])
-        one = np.array([1], np.int64)
-        st = O.moe_grouped(one, m.w13(e)[None], m.w13_scale[e][None], m.w2(e)[None],
-                           m.w2_scale[e][None], x_bits=xr[r:r + 1])
-        _assert_eq(yh[r:r + 1], st, f"row {r} (expert {e})")
+    done = 0
+    for e in range(E):
+        a, b = int(off[e]), int(off[e + 1])
+        if b == a:
+            continue
+        st = O.moe_grouped(np.array([b - a], np.int64), m.w13(e)[None], m.w13_scale[e][None],
+                           m.w2(e)[None], m.w2_scale[e][None], x_bits=xr[a:b])
+        _assert_eq(yh[a:b], st, f"rows {a}..{b - 1} (expert {e})")
         m.drop_cache()
+        done += b - a
+        if e % 32 == 31:
+            show(f"  experts 0..{e}: {done} rows equal")
+    assert done == m.R
 
 
 # ---------------------------------------------------------------------------
@@ -348,7 +392,7 @@ def test_dynamic_quant_packed_bit_exact(w, M, K):
 
 
 PACKED_LINEAR_SHAPES = [(1, 4096, 7168), (4, 256, 512), (16, 4096, 7168), (33, 300, 1024),
-                        (64, 512, 7168), (65, 300, 520), (300, 1088, 600), (520, 512, 1024),
+                        (64, 512, 7168), (64, 4096, 7168), (65, 300, 520), (300, 1088, 600), (520, 512, 1024),
                         # M <= 64 with two k-iterations per wavefront (next weights loaded
                         # ahead), a ragged last k-block and a clamped fourth m-block
                         (40, 264, 7000)]
@@ -368,9 +412,11 @@ def test_linear_packed_matches_row_major(w, M, N, K):
     y_pk = w.linear_packed(qp, sp, K, wp, ws_, N, bias=bias)
     acc_pk = w.linear_packed(qp, sp, K, wp, ws_, N, out=w.OUT_I32)
     sync()
-    _assert_eq(bf16_host(y_pk), bf16_host(y_rm), "packed vs row-major BF16")
     qo, so = O.dynamic_quant(d.x)
-    _assert_eq(host(acc_pk), O.int8_matmul_acc(qo, d.w), "packed INT32")
+    yo, acc_o = O.linear(qo, so, d.w, d.w_scale, d.bias)
+    _assert_eq(host(acc_pk), acc_o, "packed INT32")
+    _assert_eq(bf16_host(y_pk), yo, "packed BF16 vs oracle")
+    _assert_eq(bf16_host(y_rm), yo, "row-major BF16 vs oracle")
 
 
 # ---------------------------------------------------------------------------
@@ -397,6 +443,8 @@ def test_linear_bf16_input_matches_quant_then_linear(w, M, N, K):
     y = w.linear_bf16(x, wp, ws_, N, bias=bias)
     acc = w.linear_bf16(x, wp, ws_, N, out=w.OUT_I32)
     sync()
-    _assert_eq(bf16_host(y), bf16_host(y_ref), "BF16 input vs quant + linear")
     qo, so = O.dynamic_quant(d.x)
-    _assert_eq(host(acc), O.int8_matmul_acc(qo, d.w), "BF16 input INT32")
+    yo, acc_o = O.linear(qo, so, d.w, d.w_scale, d.bias)
+    _assert_eq(host(acc), acc_o, "BF16 input INT32")
+    _assert_eq(bf16_host(y), yo, "BF16 input vs oracle")
+    _assert_eq(bf16_host(y_ref), yo, "quant + linear vs oracle")
