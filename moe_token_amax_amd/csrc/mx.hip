@@ -516,20 +516,308 @@ struct MxTile {
 using MxBig = MxTile<192>;
 using MxSmall = MxTile<64>;
 
-__global__ __launch_bounds__(512) void mx_gemm_kernel(MxArgs p) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[MxBig::kLdsBytes];
-  const int64_t MT = (p.M + MxBig::BM - 1) / MxBig::BM, NT = (p.N + MxBig::BN - 1) / MxBig::BN;
+// ---------------------------------------------------------------------------
+// Dense block-scaled GEMM tile: BM x BN = (WM TM 16) x (WN TN 16), WM x WN
+// wavefronts, each a TM x TN grid of 16 x 16 fp32 accumulator blocks fed by
+// v_mfma_f32_16x16x32_bf16. The default 256 x 160 tile with 4 x 2 wavefronts
+// (two per SIMD) gives 8 x 32 = 256 equal tiles for a 2048 x 5120 output: one
+// per CU, none idle. A stage holds BM/16 A blocks and BN/16 B blocks (1 KB
+// P16x64 each) and 1 KB of scales (BM A rows x 2 at byte 0, BN B columns x 2
+// at byte 512). In a P16x64 block lane l's 16 bytes (bytes 16 l ..) are row
+// l % 16 and k = 16 (l / 16) .. + 15, all in 32-group l / 32: one
+// ds_read_b128 per lane per block, dequantized to two MFMA operands (k-steps
+// t = 0, 1: bytes 8t .. 8t + 7). The BF16 MFMA's lane l supplies k' = 8 (l /
+// 16) + e of its k-step, here original k = 16 (l / 16) + 8 t + e for A and B
+// alike, so every product pairs equal k and each k of the k-block is used
+// once. The FP8 -> BF16 conversion is a half-rate VALU instruction (two values
+// each): with two wavefronts per SIMD, one's conversions issue while the
+// other's MFMAs run.
+// ---------------------------------------------------------------------------
+#ifndef W8A8_MXW_WM
+#define W8A8_MXW_WM 4
+#endif
+#ifndef W8A8_MXW_WN
+#define W8A8_MXW_WN 2
+#endif
+#ifndef W8A8_MXW_TM
+#define W8A8_MXW_TM 4
+#endif
+#ifndef W8A8_MXW_TN
+#define W8A8_MXW_TN 5
+#endif
+
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+
+template <int WM_, int WN_, int TM_, int TN_>
+struct MxWide {
+  static constexpr int WM = WM_, WN = WN_, TM = TM_, TN = TN_;
+  static constexpr int BM = WM * TM * 16, BN = WN * TN * 16, kWaves = WM * WN, RING = 5;
+  static constexpr int kABlocks = BM / 16, kBBlocks = BN / 16;
+  static constexpr int kScaleOfs = (kABlocks + kBBlocks) * 1024;
+  static constexpr int kStageBytes = kScaleOfs + 1024;
+  static constexpr int kLdsBytes = RING * kStageBytes;
+  // DMA per stage and wavefront: kPay payload blocks (16 bytes per lane) and
+  // one 256-byte scale piece (4 bytes per lane). The pieces are A rows
+  // [128 q, 128 q + 128) for q < kAPieces, then B columns likewise; slots
+  // past the last block or piece repeat it (identical bytes to the same place).
+  static constexpr int kAPieces = (BM + 127) / 128, kBPieces = (BN + 127) / 128;
+  static constexpr int kPay = (kABlocks + kBBlocks + kWaves - 1) / kWaves;
+  static constexpr int kLoads = kPay + 1;
+  static_assert(kAPieces <= 2 && kBPieces <= 2 && kAPieces + kBPieces <= kWaves, "scale pieces");
+  static_assert(kLdsBytes <= 163840, "LDS");
+  // A fragments are read this many accumulator rows ahead of their use
+  static constexpr int kAhead = 2;
+
+  struct Src {
+    const uint8_t* pay[kPay];
+    int pdst[kPay];
+    const uint8_t* sc;
+    int64_t sc_step;
+    int sdst;
+  };
+
+  __device__ __forceinline__ static void sources(const MxArgs& p, Src& s, int wave, int lane, int64_t row0,
+                                                 int64_t row_last, int nb0) {
+#pragma unroll
+    for (int i = 0; i < kPay; ++i) {
+      int L = wave * kPay + i;
+      L = L < kABlocks + kBBlocks ? L : kABlocks + kBBlocks - 1;
+      if (L < kABlocks) {  // A: 16-row block mb, k-block kb at (mb * KB + kb) KB
+        int64_t mb = row0 / 16 + L;
+        mb = mb < row_last / 16 ? mb : row_last / 16;
+        s.pay[i] = p.a + mb * p.KB * 1024 + lane * 16;
+      } else {
+        int nb = nb0 + (L - kABlocks);
+        nb = nb < p.NB ? nb : p.NB - 1;
+        s.pay[i] = p.w + (int64_t)nb * p.KB * 1024 + lane * 16;
+      }
+      s.pdst[i] = L * 1024;
+    }
+    const int q = wave < kAPieces + kBPieces ? wave : kAPieces + kBPieces - 1;
+    if (q < kAPieces) {  // lane l: rows 2 l, 2 l + 1 of the piece
+      int64_t r = row0 + 128 * q + 2 * lane;
+      r = r < p.Mclamp - 2 ? r : p.Mclamp - 2;
+      s.sc = p.a_scale + r * 2;
+      s.sc_step = p.Mp * 2;
+      s.sdst = kScaleOfs + q * 256;
+    } else {
+      const int64_t np = (int64_t)p.NB * 16;
+      int64_t c = (int64_t)nb0 * 16 + 128 * (q - kAPieces) + 2 * lane;
+      c = c < np - 2 ? c : np - 2;
+      s.sc = p.w_scale + c * 2;
+      s.sc_step = np * 2;
+      s.sdst = kScaleOfs + 512 + (q - kAPieces) * 256;
+    }
+  }
+
+  // load i (< kLoads) of stage kb into ring buffer buf: payload slots first,
+  // the scale piece last
+  __device__ __forceinline__ static void issue_one(const Src& s, uint8_t* smem, int buf, int kb, int i) {
+    W8A8_LDS_MX uint8_t* st = (W8A8_LDS_MX uint8_t*)(smem + buf * kStageBytes);
+    if (i < kPay)
+      __builtin_amdgcn_global_load_lds(s.pay[i] + (int64_t)kb * 1024, (W8A8_LDS_MX void*)(st + s.pdst[i]), 16,
+                                       0, 0);
+    else
+      __builtin_amdgcn_global_load_lds(s.sc + kb * s.sc_step, (W8A8_LDS_MX void*)(st + s.sdst), 4, 0, 0);
+  }
+
+  __device__ __forceinline__ static void issue(const Src& s, uint8_t* smem, int buf, int kb) {
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) issue_one(s, smem, buf, kb, i);
+  }
+
+  // the 16 codes of a lane's block piece times 2^E: the operands of k-steps 0, 1
+  __device__ __forceinline__ static void deq(const i32x4& v, uint32_t sbyte, bf16x8 (&o)[2]) {
+    const float sc = e8m0_scale(sbyte);
+    o[0] = mx_dequant8((uint32_t)v[0], (uint32_t)v[1], sc);
+    o[1] = mx_dequant8((uint32_t)v[2], (uint32_t)v[3], sc);
+  }
+
+  __device__ __forceinline__ static i32x4 ld_a(const uint8_t* st, int wm, int i, int lane) {
+    return *reinterpret_cast<const i32x4*>(st + (wm * TM + i) * 1024 + lane * 16);
+  }
+  __device__ __forceinline__ static uint32_t ls_a(const uint8_t* st, int wm, int i, int lane) {
+    return st[kScaleOfs + ((wm * TM + i) * 16 + (lane & 15)) * 2 + (lane >> 5)];
+  }
+  __device__ __forceinline__ static i32x4 ld_b(const uint8_t* st, int wn, int j, int lane) {
+    return *reinterpret_cast<const i32x4*>(st + (kABlocks + wn * TN + j) * 1024 + lane * 16);
+  }
+  __device__ __forceinline__ static uint32_t ls_b(const uint8_t* st, int wn, int j, int lane) {
+    return st[kScaleOfs + 512 + ((wn * TN + j) * 16 + (lane & 15)) * 2 + (lane >> 5)];
+  }
+
+  // The MFMAs of one k-block (operands A, B), accumulator row by row. With a
+  // next stage (nx != null) its fragments are read and dequantized in between:
+  // B read at the start and dequantized into Bn (the other operand set) spread
+  // over the rows, A row i in place right after row i's MFMAs, its LDS read
+  // kAhead rows earlier.
+  // The DMA of a later stage (dkb >= 0) is issued between the rows, a few
+  // loads after each (an issue that waits for room in the memory queue then
+  // stalls behind MFMAs already in the matrix pipe, not ahead of them).
+  template <bool NEXT, bool DMA>
+  __device__ __forceinline__ static void kblock(f32x4v (&acc)[TM][TN], bf16x8 (&A)[TM][2],
+                                                const bf16x8 (&B)[TN][2], bf16x8 (&Bn)[TN][2],
+                                                const uint8_t* nx, int wm, int wn, int lane,
+                                                const Src* src = nullptr, uint8_t* smem = nullptr,
+                                                int dbuf = 0, int dkb = 0) {
+    i32x4 rb[TN], ra[TM];
+    uint32_t sb[TN], sa[TM];
+    if (NEXT) {
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        rb[j] = ld_b(nx, wn, j, lane);
+        sb[j] = ls_b(nx, wn, j, lane);
+      }
+#pragma unroll
+      for (int i = 0; i < kAhead; ++i) {
+        ra[i] = ld_a(nx, wm, i, lane);
+        sa[i] = ls_a(nx, wm, i, lane);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      if (NEXT && i + kAhead < TM) {
+        ra[i + kAhead] = ld_a(nx, wm, i + kAhead, lane);
+        sa[i + kAhead] = ls_a(nx, wm, i + kAhead, lane);
+      }
+      // k-step outer: consecutive MFMAs write different accumulators
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[i][t], B[j][t], acc[i][j], 0, 0, 0);
+      if (DMA) {
+#pragma unroll
+        for (int l = i * kLoads / TM; l < (i + 1) * kLoads / TM; ++l) issue_one(*src, smem, dbuf, dkb, l);
+      }
+      if (NEXT) {
+        deq(ra[i], sa[i], A[i]);
+#pragma unroll
+        for (int j = 0; j < TN; ++j)  // B block j refilled after row j TM / TN
+          if (j * TM / TN == i) deq(rb[j], sb[j], Bn[j]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+  template <int VM>
+  __device__ __forceinline__ static void wait_barrier() {
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(VM) : "memory");
+  }
+
+  // Phase kb (< KB - 1): stage kb + 1 must have landed (own DMA waited, then
+  // a barrier for everyone's); the barrier also means every wavefront has
+  // dequantized stage kb, so its buffer takes stage kb + RING (with DMA,
+  // issued between the rows of kb). Stage kb + 1 is read and dequantized
+  // under the MFMAs of kb. Each phase body is straight-line code: a branch
+  // inside it would split the scheduling regions and the conversions would
+  // no longer issue between the MFMAs.
+  template <bool DMA>
+  __device__ __forceinline__ static void phase(const Src& src, uint8_t* smem, int kb, int KB, int wm, int wn,
+                                               int lane, f32x4v (&acc)[TM][TN], bf16x8 (&A)[TM][2],
+                                               const bf16x8 (&B)[TN][2], bf16x8 (&Bn)[TN][2]) {
+    if (DMA) {
+      wait_barrier<(RING - 2) * kLoads>();  // stages kb + 2 .. kb + RING - 1 in flight
+    } else {
+      const int n = KB - 2 - kb;  // stages issued after kb + 1
+      if (n >= 3) wait_barrier<3 * kLoads>();
+      else if (n == 2) wait_barrier<2 * kLoads>();
+      else if (n == 1) wait_barrier<kLoads>();
+      else wait_barrier<0>();
+    }
+    kblock<true, DMA>(acc, A, B, Bn, smem + ((kb + 1) % RING) * kStageBytes, wm, wn, lane, &src, smem,
+                      kb % RING, kb + RING);
+  }
+
+  __device__ static void mainloop(const MxArgs& p, uint8_t* smem, f32x4v (&acc)[TM][TN], int64_t row0,
+                                  int64_t row_end, int nb0) {
+    static_assert(RING == 5, "wait cases");
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave / WN, wn = wave % WN;
+    const int KB = p.KB;
+    Src src;
+    sources(p, src, wave, lane, row0, row_end - 1, nb0);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) acc[i][j] = f32x4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < RING; ++s)
+      if (s < KB) issue(src, smem, s, s);
+    if (KB >= 5) wait_barrier<4 * kLoads>();
+    else if (KB == 4) wait_barrier<3 * kLoads>();
+    else if (KB == 3) wait_barrier<2 * kLoads>();
+    else if (KB == 2) wait_barrier<kLoads>();
+    else wait_barrier<0>();
+    bf16x8 A[TM][2], B0[TN][2], B1[TN][2];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) deq(ld_a(smem, wm, i, lane), ls_a(smem, wm, i, lane), A[i]);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) deq(ld_b(smem, wn, j, lane), ls_b(smem, wn, j, lane), B0[j]);
+    // k-blocks in pairs (the two B operand sets trade roles): the steady
+    // state, where both phases issue a stage; the pair where only the first
+    // does; the pairs with nothing left to load; the last one or two
+    int kb = 0;
+    for (; kb + RING + 1 < KB; kb += 2) {
+      phase<true>(src, smem, kb, KB, wm, wn, lane, acc, A, B0, B1);
+      phase<true>(src, smem, kb + 1, KB, wm, wn, lane, acc, A, B1, B0);
+    }
+    if (kb + RING < KB) {
+      phase<true>(src, smem, kb, KB, wm, wn, lane, acc, A, B0, B1);
+      phase<false>(src, smem, kb + 1, KB, wm, wn, lane, acc, A, B1, B0);
+      kb += 2;
+    }
+    for (; kb + 2 < KB; kb += 2) {
+      phase<false>(src, smem, kb, KB, wm, wn, lane, acc, A, B0, B1);
+      phase<false>(src, smem, kb + 1, KB, wm, wn, lane, acc, A, B1, B0);
+    }
+    if (kb + 2 == KB) {
+      phase<false>(src, smem, kb, KB, wm, wn, lane, acc, A, B0, B1);
+      kblock<false, false>(acc, A, B1, B0, nullptr, wm, wn, lane);
+    } else {
+      kblock<false, false>(acc, A, B0, B1, nullptr, wm, wn, lane);
+    }
+  }
+
+  // register v of block (i, j): row 4 (l / 16) + v, column l % 16
+  __device__ static void epilogue(const MxArgs& p, const f32x4v (&acc)[TM][TN], int64_t row0,
+                                  int64_t row_end, int64_t n0) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int wm = wave / WN, wn = wave % WN;
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int64_t n = n0 + (wn * TN + j) * 16 + (lane & 15);
+      if (n >= p.N) continue;
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int64_t m = row0 + (wm * TM + i) * 16 + 4 * (lane >> 4) + v;
+          if (m < row_end) p.y[m * p.N + n] = (uint16_t)f32_to_bf16(acc[i][j][v]);
+        }
+      }
+    }
+  }
+};
+
+using MxDense = MxWide<W8A8_MXW_WM, W8A8_MXW_WN, W8A8_MXW_TM, W8A8_MXW_TN>;
+
+__global__ __launch_bounds__(64 * MxDense::kWaves) void mx_gemm_kernel(MxArgs p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[MxDense::kLdsBytes];
+  const int64_t MT = (p.M + MxDense::BM - 1) / MxDense::BM, NT = (p.N + MxDense::BN - 1) / MxDense::BN;
   const int64_t T = MT * NT;
   // XCD-chunked tile order, m fastest inside an XCD's range
   const int64_t per = (T + 7) / 8;
   const int64_t t = (blockIdx.x % 8) * per + blockIdx.x / 8;
   if (t >= T) return;
   const int64_t tm = t % MT, tn = t / MT;
-  const int64_t row0 = tm * MxBig::BM;
-  const int64_t row_end = min(row0 + MxBig::BM, p.M);
-  f32x16 acc[MxBig::TM][MxBig::TN];
-  MxBig::mainloop(p, smem, acc, row0, row_end, (int)(tn * MxBig::BN / 16));
-  MxBig::epilogue(p, acc, row0, row_end, tn * MxBig::BN);
+  const int64_t row0 = tm * MxDense::BM;
+  const int64_t row_end = min(row0 + MxDense::BM, p.M);
+  f32x4v acc[MxDense::TM][MxDense::TN];
+  MxDense::mainloop(p, smem, acc, row0, row_end, (int)(tn * MxDense::BN / 16));
+  MxDense::epilogue(p, acc, row0, row_end, tn * MxDense::BN);
 }
 
 // ---------------------------------------------------------------------------
@@ -780,8 +1068,9 @@ hipError_t launch_mx_gemm(const uint8_t* a, const uint8_t* a_scale_kb, int64_t M
   p.KB = (int)ceil_div(K, 64);
   p.NB = (int)ceil_div(N, 16);
   p.y = y;
-  const int64_t T = ceil_div(M, MxBig::BM) * ceil_div(N, MxBig::BN);
-  hipLaunchKernelGGL(mx_gemm_kernel, dim3((unsigned)round_up(T, 8)), dim3(512), 0, stream, p);
+  const int64_t T = ceil_div(M, MxDense::BM) * ceil_div(N, MxDense::BN);
+  hipLaunchKernelGGL(mx_gemm_kernel, dim3((unsigned)round_up(T, 8)), dim3(64 * MxDense::kWaves), 0, stream,
+                     p);
   return hipGetLastError();
 }
 
