@@ -172,6 +172,25 @@ int w8a8_grouped_gemm(const int8_t* a, const float* a_scale,
                       int64_t ws_bytes, void* stream);
 
 /*
+ * Grouped GEMM for callers that cannot allocate (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * arguments, kernels and results as w8a8_grouped_gemm, without the workspace.
+ * The schedule goes to a device array of this library (one copy per GPU,
+ * 17,408 bytes: the schedule of E = 1024 experts, the most any call accepts;
+ * held until the process ends). The device is the caller's current one, which
+ * must own `stream`. Its device address is looked up on the first call on
+ * each device; the call itself allocates nothing. Every call on one GPU shares
+ * that array and rewrites it, so calls that overlap on one GPU (other streams,
+ * other threads) race and must be serialized by the caller. Returns
+ * W8A8_ERR_UNSUPPORTED for E > 1024, the other errors as w8a8_grouped_gemm.
+ */
+int w8a8_grouped_gemm_noalloc(const int8_t* a, const float* a_scale,
+                              const int64_t* group_list, int64_t R, int64_t E,
+                              int64_t N, int64_t K, const void* w_packed,
+                              const float* w_scale, void* y, int out,
+                              void* stream);
+
+/*
  * Fused SwiGLU + per-token requant.  [DSV4 §三 and §五: "SwiGLU + Requant"
  * produces a new INT8 payload and a new per-token scale between W13 and W2;
  * §一: W13 is gate_proj + up_proj]

@@ -31,6 +31,7 @@ __all__ = [
     "linear_packed",
     "linear_bf16",
     "grouped_gemm",
+    "grouped_gemm_noalloc",
     "swiglu_quant",
     "moe_workspace_bytes",
     "moe_grouped",
@@ -107,6 +108,8 @@ def _load():
         "w8a8_grouped_workspace_bytes": (_c_i64, [_c_i64, _c_i64, _c_i64, _c_i64]),
         "w8a8_grouped_gemm": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i64,
                                              _c_p, _c_p, _c_p, ctypes.c_int, _c_p, _c_i64, _c_p]),
+        "w8a8_grouped_gemm_noalloc": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64,
+                                                     _c_i64, _c_p, _c_p, _c_p, ctypes.c_int, _c_p]),
         "w8a8_swiglu_quant": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p]),
         "w8a8_moe_workspace_bytes": (_c_i64, [_c_i64, _c_i64, _c_i64, _c_i64]),
         "w8a8_moe_grouped": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i64,
@@ -374,6 +377,30 @@ def grouped_gemm(a: torch.Tensor, a_scale: torch.Tensor, group_list: torch.Tenso
     _check(lib.w8a8_grouped_gemm(_ptr(a), _ptr(a_scale), _ptr(group_list), R, E, N, K,
                                  _ptr(w_packed), _ptr(w_scale), _ptr(y), out, _ptr(ws), ws_n,
                                  _stream()))
+    return y
+
+
+def grouped_gemm_noalloc(a: torch.Tensor, a_scale: torch.Tensor, group_list: torch.Tensor,
+                         w_packed: torch.Tensor, w_scale: torch.Tensor, N: int, y: torch.Tensor,
+                         out: int = OUT_BF16):
+    """grouped_gemm into a caller-given y, with the schedule in the library's own
+    device array (no workspace; the call allocates nothing)."""
+    _need(a, torch.int8, "a", 2)
+    _need(a_scale, torch.float32, "a_scale", 1)
+    _need(group_list, torch.int64, "group_list", 1)
+    _need(w_packed, torch.uint8, "w_packed", 1)
+    _need(w_scale, torch.float32, "w_scale", 2)
+    R, K = a.shape
+    E = group_list.shape[0]
+    if tuple(w_scale.shape) != (E, N) or a_scale.shape[0] != R:
+        raise ValueError("scale shape mismatch")
+    if w_packed.numel() < packed_weight_bytes(E, N, K):
+        raise ValueError("w_packed too small for [E, N, K]")
+    _need(y, torch.bfloat16 if out == OUT_BF16 else torch.int32, "y", 2)
+    if tuple(y.shape) != (R, N):
+        raise ValueError("y must be [R, N]")
+    _check(lib.w8a8_grouped_gemm_noalloc(_ptr(a), _ptr(a_scale), _ptr(group_list), R, E, N, K,
+                                         _ptr(w_packed), _ptr(w_scale), _ptr(y), out, _stream()))
     return y
 
 

@@ -3,6 +3,7 @@
 #include <algorithm>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "../../include/w8a8.h"
@@ -197,19 +198,29 @@ static int check_grouped(const char* who, int64_t R, int64_t E, int64_t N, int64
   return W8A8_OK;
 }
 
+static int check_grouped_call(const char* who, const int8_t* a, const float* a_scale,
+                              const int64_t* group_list, int64_t R, int64_t E, int64_t N, int64_t K,
+                              const void* w_packed, const float* w_scale, void* y, int out) {
+  int st = check_grouped(who, R, E, N, K);
+  if (st) return st;
+  if (out != W8A8_OUT_BF16 && out != W8A8_OUT_I32)
+    return fail(W8A8_ERR_UNSUPPORTED, "%s: unknown output kind %d", who, out);
+  if (R == 0) return W8A8_OK;
+  if (!a || !a_scale || !group_list || !w_packed || !w_scale || !y)
+    return fail(W8A8_ERR_NULL, "%s: null pointer", who);
+  if (!aligned(w_packed, 16) || !aligned(a_scale, 4) || !aligned(w_scale, 4) || !aligned(y, 4) ||
+      !aligned(group_list, 8))
+    return fail(W8A8_ERR_ALIGN, "%s: misaligned buffer", who);
+  return W8A8_OK;
+}
+
 int w8a8_grouped_gemm(const int8_t* a, const float* a_scale, const int64_t* group_list, int64_t R,
                       int64_t E, int64_t N, int64_t K, const void* w_packed, const float* w_scale,
                       void* y, int out, void* workspace, int64_t ws_bytes, void* stream) {
-  int st = check_grouped("grouped_gemm", R, E, N, K);
+  const int st = check_grouped_call("grouped_gemm", a, a_scale, group_list, R, E, N, K, w_packed, w_scale,
+                                    y, out);
   if (st) return st;
-  if (out != W8A8_OUT_BF16 && out != W8A8_OUT_I32)
-    return fail(W8A8_ERR_UNSUPPORTED, "grouped_gemm: unknown output kind %d", out);
   if (R == 0) return ok();
-  if (!a || !a_scale || !group_list || !w_packed || !w_scale || !y)
-    return fail(W8A8_ERR_NULL, "grouped_gemm: null pointer");
-  if (!aligned(w_packed, 16) || !aligned(a_scale, 4) || !aligned(w_scale, 4) || !aligned(y, 4) ||
-      !aligned(group_list, 8))
-    return fail(W8A8_ERR_ALIGN, "grouped_gemm: misaligned buffer");
   const int64_t need = w8a8::grouped_ws_bytes(R, E, N, K);
   if (need > 0 && (!workspace || ws_bytes < need || !aligned(workspace, 256)))
     return fail(W8A8_ERR_WORKSPACE, "grouped_gemm: needs %lld workspace bytes (256-byte aligned), got %lld",
@@ -901,4 +912,61 @@ int w8a8_static_linear(const int8_t* q, int64_t M, int64_t K, const void* w_pack
   return launched(w8a8::launch_dense_gemm(plan, q, nullptr, M, K, w_packed, deq_scale, N, nullptr, y, out,
                                           packed, nullptr, (hipStream_t)stream, quant_bias),
                   "static_linear");
+}
+
+// ---------------------------------------------------------------------------
+// Grouped GEMM without a caller workspace. Its schedule goes to `scratch`, a
+// device array of this library: each GPU holds its own copy at its own
+// address until the process ends. In host code `scratch` names a host-side
+// stand-in, never the device memory, so the device address is taken once per
+// device with hipGetSymbolAddress and only that address reaches a kernel.
+// ---------------------------------------------------------------------------
+constexpr int64_t kScratchBytes = w8a8::group_sched_bytes(kMaxExperts);
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace {
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kScratchDevices];  // device address of `scratch`, per device
+
+// device address of the current device's `scratch` (taken on its first use)
+int scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(W8A8_ERR_LAUNCH, "grouped_gemm_noalloc: hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kScratchDevices)
+    return fail(W8A8_ERR_UNSUPPORTED, "grouped_gemm_noalloc: device %d past the %d this library tracks", dev,
+                kScratchDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(W8A8_ERR_LAUNCH, "grouped_gemm_noalloc: hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    g_scratch_addr[dev] = p;
+  }
+  *out = g_scratch_addr[dev];
+  return W8A8_OK;
+}
+}  // namespace
+
+int w8a8_grouped_gemm_noalloc(const int8_t* a, const float* a_scale, const int64_t* group_list, int64_t R,
+                              int64_t E, int64_t N, int64_t K, const void* w_packed, const float* w_scale,
+                              void* y, int out, void* stream) {
+  const int st = check_grouped_call("grouped_gemm_noalloc", a, a_scale, group_list, R, E, N, K, w_packed,
+                                    w_scale, y, out);
+  if (st) return st;
+  if (R == 0) return ok();
+  const int64_t need = w8a8::grouped_ws_bytes(R, E, N, K);
+  if (need > kScratchBytes)
+    return fail(W8A8_ERR_UNSUPPORTED, "grouped_gemm_noalloc: the schedule of %lld experts needs %lld bytes, "
+                "past the library's %lld-byte scratch", (long long)E, (long long)need, (long long)kScratchBytes);
+  void* ws = nullptr;
+  const int sa = scratch_address(&ws);
+  if (sa) return sa;
+  // the schedule kernel rewrites every byte the GEMM reads (work-queue
+  // counters included), so nothing left by an earlier call matters
+  return launched(w8a8::launch_grouped_gemm(a, a_scale, group_list, R, E, N, K, w_packed, w_scale, y, out, ws,
+                                            (hipStream_t)stream),
+                  "grouped_gemm_noalloc");
 }

@@ -726,25 +726,17 @@ __global__ __launch_bounds__(WM* WN* kWave) void grouped_gemm_kernel(GemmArgs p)
 constexpr int kSmallRows = 64;
 constexpr int kGroupBM = 256, kGroupBN = 256;
 
-// Schedule in the workspace: row_off[E + 1] (first row of each expert),
-// tile_off[E + 1] (first m-tile of each large expert; small and empty experts
-// own none), small[E + 1] (the ids of the non-empty small experts, their
-// count in small[E]) and the work-queue counters of the mixed kernel (one per
-// XCD).
-constexpr int kQueues = 8;
-
+// Schedule in the workspace (its size is group_sched_bytes in launch.hpp):
+// row_off[E + 1] (first row of each expert), tile_off[E + 1] (first m-tile of
+// each large expert; small and empty experts own none), small[E + 1] (the ids
+// of the non-empty small experts, their count in small[E]) and the kQueues
+// work-queue counters of the mixed kernel (one per XCD).
 struct GroupSched {
   int64_t* row_off;
   int* tile_off;
   int* small;
   unsigned* queue;
 };
-
-__host__ __device__ inline int64_t sched_align(int64_t b) { return (b + 255) / 256 * 256; }
-
-__host__ __device__ inline int64_t group_sched_bytes(int64_t E) {
-  return sched_align((E + 1) * 8) + 2 * sched_align((E + 1) * 4) + sched_align(kQueues * 4);
-}
 
 __host__ __device__ inline GroupSched group_sched(void* ws, int64_t E) {
   GroupSched g;

@@ -48,6 +48,14 @@ hipError_t launch_static_prepare(const int8_t* w, int64_t N, int64_t K, const fl
                                  float* deq_scale, int32_t* quant_bias, hipStream_t stream);
 
 int64_t grouped_ws_bytes(int64_t R, int64_t E, int64_t N, int64_t K);
+// the grouped GEMM's schedule for E experts: row offsets int64 [E + 1], large-
+// expert tile offsets int32 [E + 1], small-expert ids int32 [E + 1] and kQueues
+// work-queue counters, each part 256-byte aligned (grouped_ws_bytes returns it)
+constexpr int kQueues = 8;
+__host__ __device__ constexpr int64_t sched_align(int64_t b) { return (b + 255) / 256 * 256; }
+__host__ __device__ constexpr int64_t group_sched_bytes(int64_t E) {
+  return sched_align((E + 1) * 8) + 2 * sched_align((E + 1) * 4) + sched_align(kQueues * 4);
+}
 
 // around the MoE chain: routing of (token, slot) expert ids, gather of the INT8
 // rows, and the weighted combine (moe_io.hip)
