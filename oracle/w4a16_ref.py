@@ -34,22 +34,33 @@ codes; each value w / 2^E (exact) is encoded to the nearest E2M1 value, ties
 to the even code, saturating at 6, the sign kept (-0 is code 8). The
 dequantized weight 2^E * value is exact in BF16.
 
+MoE form (the same kernel row: the grouped expert matmul takes the low-bit
+expert weights). Readings: rows grouped by expert as on the INT8 path
+(group_list = rows per expert, [DSV4] §三); activations stay BF16 (A16): the
+W13 output h is rounded once to BF16 (through fp32), the SwiGLU output a =
+BF16(silu(gate) * up) by the fixed fp32 sequence of ``w8a8_ref.swiglu``, and
+the W2 output is compared as the dense linear's; no requant between them.
+
 Parity status (tests/test_oracle_w4a16_pins.py): the INT4 quantizer pinned by
 hand groups (exact scales, ties to even, the clamp, a BF16-rounded scale, the
 zero group), by exact-rational recomputation and by the half-step error bound;
 the dequantization by exact recomputation; the linear by brute force. The FP4
 quantizer by hand groups (every tie), an exhaustive nearest-value search and
-the half-step bound; its dequantization and linear by brute force.
+the half-step bound; its dequantization and linear by brute force. The grouped
+form by brute force per expert on the page's row counts 12/7/0/19 (an empty
+expert included), the SwiGLU by hand values (signed zero, overflowing exp), and
+the chain stage by stage against brute force.
 """
 
 from __future__ import annotations
 
 import numpy as np
 
-from .w8a8_ref import bf16_to_f32, f32_to_bf16
+from .w8a8_ref import bf16_to_f32, f32_to_bf16, group_offsets, swiglu
 
 __all__ = ["W4_GROUP", "w4_quant", "w4_dequant", "w4a16_linear_ref64", "E2M1_VALUES", "fp4_quant",
-           "fp4_dequant", "fp4_linear_ref64"]
+           "fp4_dequant", "fp4_linear_ref64", "lowbit_dequant", "lowbit_grouped_ref64",
+           "lowbit_swiglu", "lowbit_moe"]
 
 W4_GROUP = 32
 
@@ -139,3 +150,47 @@ def fp4_linear_ref64(x_bits, codes, scales):
     x = bf16_to_f32(x_bits).astype(np.float64)
     w = bf16_to_f32(fp4_dequant(codes, scales)).astype(np.float64)
     return x @ w.T
+
+
+# ---------------------------------------------------------------------------
+# MoE form: grouped matmul over low-bit expert weights, and the expert chain
+# ---------------------------------------------------------------------------
+
+def lowbit_dequant(fmt, codes, scales):
+    """BF16 bits of one expert's dequantized weight: fmt "int4" (codes int8,
+    BF16 scale bits) or "fp4" (E2M1 codes, E8M0 bytes)."""
+    return w4_dequant(codes, scales) if fmt == "int4" else fp4_dequant(codes, scales)
+
+
+def lowbit_grouped_ref64(fmt, x_bits, group_list, codes, scales):
+    """Rows of expert e (rows grouped by expert, group_list = rows per expert)
+    times expert e's dequantized weight [N, K]: float64 sums [R, N]."""
+    off = group_offsets(group_list)
+    x = bf16_to_f32(x_bits).astype(np.float64)
+    N = np.asarray(codes).shape[1]
+    y = np.zeros((x.shape[0], N))
+    for e in range(len(off) - 1):
+        a, b = int(off[e]), int(off[e + 1])
+        if b > a:
+            w = bf16_to_f32(lowbit_dequant(fmt, codes[e], scales[e])).astype(np.float64)
+            y[a:b] = x[a:b] @ w.T
+    return y
+
+
+def lowbit_swiglu(h_bits, inter):
+    """a = BF16(silu(gate) * up) of h = [gate | up] [R, 2I] (BF16 out)."""
+    return f32_to_bf16(swiglu(h_bits, inter))
+
+
+def lowbit_moe(fmt, group_list, x_bits, w13_codes, w13_scales, w2_codes, w2_scales, keep=False):
+    """Low-bit expert chain on expert-grouped BF16 rows x [R, H]: h = BF16 of the
+    W13 sums, a = BF16 SwiGLU of h, y64 = the float64 W2 sums of a (unrounded).
+    Returns y64, or a dict of every stage when ``keep``."""
+    inter = np.asarray(w13_codes).shape[1] // 2
+    h64 = lowbit_grouped_ref64(fmt, x_bits, group_list, w13_codes, w13_scales)
+    h = f32_to_bf16(h64.astype(np.float32))
+    a = lowbit_swiglu(h, inter)
+    y64 = lowbit_grouped_ref64(fmt, a, group_list, w2_codes, w2_scales)
+    if keep:
+        return dict(h64=h64, h=h, a=a, y64=y64)
+    return y64

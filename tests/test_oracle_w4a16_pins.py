@@ -204,3 +204,99 @@ def test_fp4_linear_brute_force():
                 v = mags[c[n, k] & 7] * (-1.0 if c[n, k] & 8 else 1.0) * 2.0 ** (int(s[n, k // 32]) - 127)
                 acc += float(xf[m, k]) * v
             assert abs(ref[m, n] - acc) <= 1e-12 * abs(acc) + 1e-300
+
+
+# ---------------------------------------------------------------------------
+# MoE form: grouped matmul over low-bit expert weights, and the expert chain
+# ---------------------------------------------------------------------------
+
+def _golden_counts():
+    import os
+    path = os.path.join(os.path.dirname(__file__), "golden", "moe_group_counts.txt")
+    line = [l for l in open(path, encoding="utf-8") if not l.startswith("#") and l.strip()][0]
+    return [int(v) for v in line.split()]
+
+
+def _experts(fmt, E, N, K, seed):
+    rng = np.random.default_rng(seed)
+    codes, scales = [], []
+    for e in range(E):
+        # experts of very different magnitude, so that a row multiplied by the
+        # wrong expert's weight cannot pass
+        w = O.f32_to_bf16((rng.standard_normal((N, K)) * 0.02 * 4.0 ** e).astype(np.float32))
+        c, s = W4.w4_quant(w) if fmt == "int4" else W4.fp4_quant(w)
+        codes.append(c)
+        scales.append(s)
+    return np.stack(codes), np.stack(scales)
+
+
+def _value(fmt, codes, scales, n, k):
+    """Dequantized weight element by its definition (one element, plain Python)."""
+    if fmt == "int4":
+        s = float(O.bf16_to_f32(np.array([scales[n, k // 32]], np.uint16))[0])
+        v = np.float32(codes[n, k]) * np.float32(s)
+        return float(O.bf16_to_f32(O.f32_to_bf16(np.array([v], np.float32)))[0])
+    mags = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    return mags[codes[n, k] & 7] * (-1.0 if codes[n, k] & 8 else 1.0) * 2.0 ** (int(scales[n, k // 32]) - 127)
+
+
+def _brute_grouped(fmt, x_bits, counts, codes, scales):
+    xf = O.bf16_to_f32(x_bits)
+    N, K = codes.shape[1], codes.shape[2]
+    out, r = [], 0
+    for e, n_e in enumerate(counts):          # rows grouped by expert, in order
+        for _ in range(n_e):
+            out.append([sum(float(xf[r, k]) * _value(fmt, codes[e], scales[e], n, k) for k in range(K))
+                        for n in range(N)])
+            r += 1
+    return np.array(out)
+
+
+def test_lowbit_grouped_brute_force_on_the_page_counts():
+    counts = _golden_counts()            # 12, 7, 0, 19: the third expert is empty
+    rng = np.random.default_rng(8)
+    R, N, K = sum(counts), 3, 64
+    x = O.f32_to_bf16(rng.standard_normal((R, K)).astype(np.float32))
+    for fmt in ("int4", "fp4"):
+        c, s = _experts(fmt, len(counts), N, K, seed=9)
+        ref = W4.lowbit_grouped_ref64(fmt, x, np.array(counts), c, s)
+        want = _brute_grouped(fmt, x, counts, c, s)
+        assert np.allclose(ref, want, rtol=1e-12, atol=1e-300), fmt
+
+
+def test_lowbit_swiglu_hand_values():
+    # silu(2) * 3 = 2 / (1 + e^-2) * 3 = 5.28478...; BF16 neighbours 5.28125 and
+    # 5.3125 -> 5.28125. silu(0) * 7 = 0; silu(-100) * 1 = -0 (the exponential
+    # overflows to +inf); gate 20: silu(20) = 19.99999996 -> 20 after BF16.
+    g = np.array([[2.0, 0.0, -100.0, 20.0]], np.float32)
+    u = np.array([[3.0, 7.0, 1.0, 1.0]], np.float32)
+    a = O.bf16_to_f32(W4.lowbit_swiglu(O.f32_to_bf16(np.concatenate([g, u], axis=1)), 4))[0]
+    assert a.tolist() == [5.28125, 0.0, 0.0, 20.0]
+    assert np.signbit(a[2])
+
+
+def test_lowbit_moe_chain_brute_force():
+    import math
+    counts = [3, 0, 2]
+    rng = np.random.default_rng(10)
+    R, H, I = sum(counts), 64, 32
+    x = O.f32_to_bf16(rng.standard_normal((R, H)).astype(np.float32))
+    for fmt in ("int4", "fp4"):
+        c13, s13 = _experts(fmt, len(counts), 2 * I, H, seed=11)
+        c2, s2 = _experts(fmt, len(counts), H, I, seed=12)
+        st = W4.lowbit_moe(fmt, np.array(counts), x, c13, s13, c2, s2, keep=True)
+        h64 = _brute_grouped(fmt, x, counts, c13, s13)
+        assert np.allclose(st["h64"], h64, rtol=1e-12, atol=1e-300)
+        h = O.f32_to_bf16(h64.astype(np.float32))
+        assert np.array_equal(st["h"], h)
+        hf = O.bf16_to_f32(h).astype(np.float64)
+        a_exact = hf[:, :I] / (1.0 + np.exp(-hf[:, :I])) * hf[:, I:]
+        af = O.bf16_to_f32(st["a"]).astype(np.float64)
+        # BF16 of the exact value, except where it sits within fp32 noise of a
+        # rounding boundary (the fixed exp is ~1 ulp accurate)
+        want = O.bf16_to_f32(O.f32_to_bf16(a_exact.astype(np.float32))).astype(np.float64)
+        near = np.abs(a_exact - want) > 0.49 * np.abs(want) * 2.0 ** -8
+        assert np.all((af == want) | near)
+        y64 = _brute_grouped(fmt, st["a"], counts, c2, s2)
+        assert np.allclose(st["y64"], y64, rtol=1e-12, atol=1e-300)
+        assert math.isfinite(float(np.abs(y64).max()))
