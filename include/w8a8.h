@@ -501,6 +501,49 @@ int w8a8_fp4_quant_weight(const uint16_t* w, int64_t N, int64_t K, uint8_t* code
 int w8a8_fp4_linear(const uint16_t* x, int64_t M, int64_t K, const void* w_packed, int64_t N,
                     uint16_t* y, void* workspace, int64_t ws_bytes, void* stream);
 
+/*
+ * Grouped form of the W4A16 / FP4 weight variant: the MoE experts' matmul with
+ * low-bit expert weights ([LOWBIT]: MoE weights published as MXFP4 or INT4,
+ * and in its kernel-table section 4-bit weights halve the bytes a decode step
+ * reads; [DSV4] §三 for the grouping: rows sorted by expert, group_list =
+ * rows per expert).
+ *
+ * fmt: W8A8_LOWBIT_INT4 (w8a8_w4a16_quant_weight's packed layout) or
+ *   W8A8_LOWBIT_FP4 (w8a8_fp4_quant_weight's). Expert e's packed [N, K]
+ *   weight starts at w_packed + e * w8a8_w4a16_packed_bytes(N, K) (INT4) or
+ *   + e * w8a8_fp4_packed_bytes(N, K) (FP4); with N % 16 == 0 this is the
+ *   packed layout of the stacked weight [E * N, K], so one quant call on the
+ *   stack prepares every expert.
+ * w8a8_w4a16_grouped_gemm: x BF16 rows [R, K] (16-byte aligned), grouped by
+ *   expert: rows [off_e, off_e + n_e) with n_e = group_list[e] (device int64
+ *   [E], E <= 1024, negative counts own no rows, counts summing past R are a
+ *   caller error whose rows at or past R are never touched) times expert e's
+ *   dequantized weight -> y BF16 [R, N] (8-byte aligned), each output as in
+ *   w8a8_w4a16_linear / w8a8_fp4_linear: BF16 weights, exact products, fp32
+ *   accumulation. N % 16 == 0 and K % 32 == 0, else W8A8_ERR_UNSUPPORTED. No
+ *   workspace; group_list is read on the device only.
+ * w8a8_w4a16_swiglu: h BF16 [R, 2I] = [gate | up] -> a BF16 [R, I] =
+ *   BF16(silu(gate) * up), silu(g) * u = (g / (1 + exp(-g))) * u by the same
+ *   fixed fp32 sequence as w8a8_swiglu_quant (bit-exact, round half to even).
+ * w8a8_w4a16_moe_grouped: the expert chain on expert-grouped BF16 rows x_rows
+ *   [R, H] -> y BF16 [R, H]: w8a8_w4a16_grouped_gemm with w13 (N = 2I, K = H;
+ *   columns [0, I) gate, [I, 2I) up) into h BF16 [R, 2I], w8a8_w4a16_swiglu
+ *   into a BF16 [R, I], w8a8_w4a16_grouped_gemm with w2 (N = H, K = I). No
+ *   requantization between them (A16: the activations stay BF16). workspace:
+ *   w8a8_w4a16_moe_workspace_bytes(R, H, I) bytes, 256-byte aligned: h at
+ *   offset 0, a at the next 256-byte boundary after h (both left there);
+ *   H % 32 == 0 and I % 32 == 0.
+ */
+#define W8A8_LOWBIT_INT4 0
+#define W8A8_LOWBIT_FP4 1
+int w8a8_w4a16_grouped_gemm(int fmt, const uint16_t* x, const int64_t* group_list, int64_t R, int64_t E,
+                            int64_t N, int64_t K, const void* w_packed, uint16_t* y, void* stream);
+int w8a8_w4a16_swiglu(const uint16_t* h, int64_t R, int64_t I, uint16_t* a, void* stream);
+int64_t w8a8_w4a16_moe_workspace_bytes(int64_t R, int64_t H, int64_t I);
+int w8a8_w4a16_moe_grouped(int fmt, const uint16_t* x_rows, const int64_t* group_list, int64_t R, int64_t E,
+                           int64_t H, int64_t I, const void* w13_packed, const void* w2_packed, uint16_t* y,
+                           void* workspace, int64_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -65,6 +65,12 @@ __all__ = [
     "w4a16_linear",
     "fp4_quant_weight",
     "fp4_linear",
+    "LOWBIT_INT4",
+    "LOWBIT_FP4",
+    "w4a16_grouped_gemm",
+    "w4a16_swiglu",
+    "w4a16_moe_workspace_bytes",
+    "w4a16_moe_grouped",
     "mx_workspace_operands",
     "static_quant",
     "static_quant_packed",
@@ -154,6 +160,12 @@ def _load():
         "w8a8_fp4_quant_weight": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p]),
         "w8a8_fp4_linear": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_i64, _c_p, _c_p, _c_i64,
                                            _c_p]),
+        "w8a8_w4a16_grouped_gemm": (ctypes.c_int, [ctypes.c_int, _c_p, _c_p, _c_i64, _c_i64, _c_i64,
+                                                   _c_i64, _c_p, _c_p, _c_p]),
+        "w8a8_w4a16_swiglu": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_p]),
+        "w8a8_w4a16_moe_workspace_bytes": (_c_i64, [_c_i64, _c_i64, _c_i64]),
+        "w8a8_w4a16_moe_grouped": (ctypes.c_int, [ctypes.c_int, _c_p, _c_p, _c_i64, _c_i64, _c_i64,
+                                                  _c_i64, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_p]),
         "w8a8_static_quant": (ctypes.c_int, [_c_p, _c_i64, _c_i64, ctypes.c_float, ctypes.c_float,
                                              _c_p, _c_p]),
         "w8a8_static_quant_packed": (ctypes.c_int, [_c_p, _c_i64, _c_i64, ctypes.c_float,
@@ -842,6 +854,78 @@ def fp4_linear(x: torch.Tensor, w_packed: torch.Tensor, N: int,
     ws, ws_n = _workspace(w4a16_linear_workspace_bytes(M, K), x.device, workspace)
     _check(lib.w8a8_fp4_linear(_ptr(x), M, K, _ptr(w_packed), N, _ptr(y), _ptr(ws), ws_n,
                                _stream()))
+    return y
+
+
+LOWBIT_INT4 = 0   # w4a16_quant_weight's packed layout
+LOWBIT_FP4 = 1    # fp4_quant_weight's packed layout
+
+
+def _lowbit_bytes(fmt: int, N: int, K: int) -> int:
+    if fmt == LOWBIT_INT4:
+        return w4a16_packed_bytes(N, K)
+    if fmt == LOWBIT_FP4:
+        return fp4_packed_bytes(N, K)
+    raise ValueError(f"unknown low-bit weight format {fmt}")
+
+
+def w4a16_grouped_gemm(x: torch.Tensor, group_list: torch.Tensor, w_packed: torch.Tensor, N: int,
+                       fmt: int = LOWBIT_INT4, y: torch.Tensor | None = None) -> torch.Tensor:
+    """Expert-grouped BF16 rows [R, K] times each expert's packed INT4 / FP4 weight
+    [N, K] (experts stacked, one packed weight each) -> BF16 [R, N]."""
+    _need(x, torch.bfloat16, "x", 2)
+    _need(group_list, torch.int64, "group_list", 1)
+    _need(w_packed, torch.uint8, "w_packed", 1)
+    R, K = x.shape
+    E = group_list.shape[0]
+    if w_packed.numel() < E * _lowbit_bytes(fmt, N, K):
+        raise ValueError("w_packed too small for [E, N, K]")
+    if y is None:
+        y = torch.empty((R, N), dtype=torch.bfloat16, device=x.device)
+    _need(y, torch.bfloat16, "y", 2)
+    _check(lib.w8a8_w4a16_grouped_gemm(fmt, _ptr(x), _ptr(group_list), R, E, N, K, _ptr(w_packed),
+                                       _ptr(y), _stream()))
+    return y
+
+
+def w4a16_swiglu(h: torch.Tensor, a: torch.Tensor | None = None) -> torch.Tensor:
+    """BF16 [R, 2I] = [gate | up] -> BF16 [R, I] = BF16(silu(gate) * up)."""
+    _need(h, torch.bfloat16, "h", 2)
+    R, I2 = h.shape
+    if I2 % 2:
+        raise ValueError("h must have an even number of columns")
+    if a is None:
+        a = torch.empty((R, I2 // 2), dtype=torch.bfloat16, device=h.device)
+    _need(a, torch.bfloat16, "a", 2)
+    _check(lib.w8a8_w4a16_swiglu(_ptr(h), R, I2 // 2, _ptr(a), _stream()))
+    return a
+
+
+def w4a16_moe_workspace_bytes(R: int, H: int, I: int) -> int:
+    return int(lib.w8a8_w4a16_moe_workspace_bytes(R, H, I))
+
+
+def w4a16_moe_grouped(x_rows: torch.Tensor, group_list: torch.Tensor, w13_packed: torch.Tensor,
+                      w2_packed: torch.Tensor, I: int, fmt: int = LOWBIT_INT4,
+                      y: torch.Tensor | None = None, workspace: torch.Tensor | None = None):
+    """Low-bit expert chain on expert-grouped BF16 rows [R, H] -> BF16 [R, H]:
+    W13 -> BF16 SwiGLU -> W2, activations kept in BF16."""
+    _need(x_rows, torch.bfloat16, "x_rows", 2)
+    _need(group_list, torch.int64, "group_list", 1)
+    _need(w13_packed, torch.uint8, "w13_packed", 1)
+    _need(w2_packed, torch.uint8, "w2_packed", 1)
+    R, H = x_rows.shape
+    E = group_list.shape[0]
+    if w13_packed.numel() < E * _lowbit_bytes(fmt, 2 * I, H) or \
+            w2_packed.numel() < E * _lowbit_bytes(fmt, H, I):
+        raise ValueError("packed expert weights too small")
+    if y is None:
+        y = torch.empty((R, H), dtype=torch.bfloat16, device=x_rows.device)
+    _need(y, torch.bfloat16, "y", 2)
+    ws, ws_n = _workspace(w4a16_moe_workspace_bytes(R, H, I), x_rows.device, workspace)
+    _check(lib.w8a8_w4a16_moe_grouped(fmt, _ptr(x_rows), _ptr(group_list), R, E, H, I,
+                                      _ptr(w13_packed), _ptr(w2_packed), _ptr(y), _ptr(ws), ws_n,
+                                      _stream()))
     return y
 
 

@@ -819,6 +819,80 @@ int w8a8_fp4_linear(const uint16_t* x, int64_t M, int64_t K, const void* w_packe
                   "fp4_linear");
 }
 
+// ---------------------------------------------------------------------------
+// grouped form (low-bit expert weights)
+// ---------------------------------------------------------------------------
+static int check_lowbit_grouped(const char* who, int fmt, int64_t R, int64_t E, int64_t N, int64_t K) {
+  if (fmt != W8A8_LOWBIT_INT4 && fmt != W8A8_LOWBIT_FP4)
+    return fail(W8A8_ERR_UNSUPPORTED, "%s: unknown weight format %d", who, fmt);
+  int st = check_w4(who, N, K);
+  if (st) return st;
+  if (R < 0 || R >= kMaxDim || E < 1)
+    return fail(W8A8_ERR_SHAPE, "%s: need 0 <= R < 2^31 and E >= 1", who);
+  if (E > kMaxExperts) return fail(W8A8_ERR_UNSUPPORTED, "%s: at most %lld experts", who, (long long)kMaxExperts);
+  if (N % 16)
+    return fail(W8A8_ERR_UNSUPPORTED, "%s: N = %lld is not a multiple of 16 (one packed column block)", who,
+                (long long)N);
+  return W8A8_OK;
+}
+
+int w8a8_w4a16_grouped_gemm(int fmt, const uint16_t* x, const int64_t* group_list, int64_t R, int64_t E,
+                            int64_t N, int64_t K, const void* w_packed, uint16_t* y, void* stream) {
+  int st = check_lowbit_grouped("w4a16_grouped_gemm", fmt, R, E, N, K);
+  if (st) return st;
+  if (R == 0) return ok();
+  if (!x || !group_list || !w_packed || !y) return fail(W8A8_ERR_NULL, "w4a16_grouped_gemm: null pointer");
+  if (!aligned(x, 16) || !aligned(w_packed, 16) || !aligned(y, 8) || !aligned(group_list, 8))
+    return fail(W8A8_ERR_ALIGN, "w4a16_grouped_gemm: x and w_packed need 16-byte, y 8-byte alignment");
+  return launched(w8a8::launch_lowbit_grouped(fmt, x, group_list, R, E, N, K,
+                                              reinterpret_cast<const uint8_t*>(w_packed), y, (hipStream_t)stream),
+                  "w4a16_grouped_gemm");
+}
+
+int w8a8_w4a16_swiglu(const uint16_t* h, int64_t R, int64_t I, uint16_t* a, void* stream) {
+  if (R < 0 || I < 1 || R >= kMaxDim || I >= kMaxDim / 2)
+    return fail(W8A8_ERR_SHAPE, "w4a16_swiglu: need R >= 0 and I >= 1");
+  if (R == 0) return ok();
+  if (!h || !a) return fail(W8A8_ERR_NULL, "w4a16_swiglu: null pointer");
+  if (!aligned(h, 2) || !aligned(a, 2)) return fail(W8A8_ERR_ALIGN, "w4a16_swiglu: misaligned buffer");
+  return launched(w8a8::launch_lowbit_swiglu(h, R, I, a, (hipStream_t)stream), "w4a16_swiglu");
+}
+
+int64_t w8a8_w4a16_moe_workspace_bytes(int64_t R, int64_t H, int64_t I) {
+  if (R < 1 || H < 1 || I < 1) return 0;
+  return align256(R * 2 * I * 2) + align256(R * I * 2);
+}
+
+int w8a8_w4a16_moe_grouped(int fmt, const uint16_t* x_rows, const int64_t* group_list, int64_t R, int64_t E,
+                           int64_t H, int64_t I, const void* w13_packed, const void* w2_packed, uint16_t* y,
+                           void* workspace, int64_t ws_bytes, void* stream) {
+  int st = check_lowbit_grouped("w4a16_moe_grouped", fmt, R, E, 2 * I, H);
+  if (st) return st;
+  st = check_lowbit_grouped("w4a16_moe_grouped", fmt, R, E, H, I);
+  if (st) return st;
+  if (R == 0) return ok();
+  if (!x_rows || !group_list || !w13_packed || !w2_packed || !y)
+    return fail(W8A8_ERR_NULL, "w4a16_moe_grouped: null pointer");
+  if (!aligned(x_rows, 16) || !aligned(w13_packed, 16) || !aligned(w2_packed, 16) || !aligned(y, 8) ||
+      !aligned(group_list, 8))
+    return fail(W8A8_ERR_ALIGN, "w4a16_moe_grouped: misaligned buffer");
+  const int64_t need = w8a8_w4a16_moe_workspace_bytes(R, H, I);
+  if (!workspace || ws_bytes < need || !aligned(workspace, 256))
+    return fail(W8A8_ERR_WORKSPACE, "w4a16_moe_grouped: needs %lld workspace bytes (256-byte aligned), got %lld",
+                (long long)need, (long long)ws_bytes);
+  uint16_t* h = reinterpret_cast<uint16_t*>(workspace);
+  uint16_t* a = reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(workspace) + align256(R * 2 * I * 2));
+  const hipStream_t s = (hipStream_t)stream;
+  hipError_t err = w8a8::launch_lowbit_grouped(fmt, x_rows, group_list, R, E, 2 * I, H,
+                                               reinterpret_cast<const uint8_t*>(w13_packed), h, s);
+  if (err != hipSuccess) return launched(err, "w4a16_moe_grouped: W13");
+  err = w8a8::launch_lowbit_swiglu(h, R, I, a, s);
+  if (err != hipSuccess) return launched(err, "w4a16_moe_grouped: swiglu");
+  return launched(w8a8::launch_lowbit_grouped(fmt, a, group_list, R, E, H, I,
+                                              reinterpret_cast<const uint8_t*>(w2_packed), y, s),
+                  "w4a16_moe_grouped: W2");
+}
+
 int w8a8_w4a16_linear(const uint16_t* x, int64_t M, int64_t K, const void* w_packed, int64_t N,
                       uint16_t* y, void* workspace, int64_t ws_bytes, void* stream) {
   int st = check_w4("w4a16_linear", N, K);

@@ -620,67 +620,6 @@ __global__ __launch_bounds__(WM* WN* kWave) void dense_gemm_kernel(GemmArgs p) {
 // per-expert row counts and m-tile counts, in LDS), so there is no host sync
 // and no extra launch. Experts with 0 rows own no tiles.
 // ---------------------------------------------------------------------------
-constexpr int kMaxExperts = 1024;
-
-// Exclusive prefix sums of the per-expert row counts and m-tile counts, for
-// E <= 1024 experts, by a 256-thread workgroup: each thread owns 4 consecutive
-// experts, a wavefront scans with shfl_up, and the 4 wave totals are combined
-// through LDS. row_off[E] / tile_off[E] receive the totals.
-template <int BM>
-__device__ void build_schedule(const int64_t* __restrict__ gl, int E, int64_t* row_off,
-                               int* tile_off) {
-  __shared__ int64_t wave_rows[4];
-  __shared__ int wave_tiles[4];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  int64_t n[4];
-  int64_t rs = 0;
-  int ts = 0;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int e = 4 * tid + j;
-    n[j] = e < E ? max(gl[e], (int64_t)0) : 0;  // a negative count owns no rows
-    rs += n[j];
-    ts += (int)((n[j] + BM - 1) / BM);
-  }
-  int64_t ri = rs;
-  int ti = ts;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int64_t ro = __shfl_up(ri, d, 64);
-    const int to = __shfl_up(ti, d, 64);
-    if (lane >= d) {
-      ri += ro;
-      ti += to;
-    }
-  }
-  if (lane == 63) {
-    wave_rows[wave] = ri;
-    wave_tiles[wave] = ti;
-  }
-  __syncthreads();
-  int64_t r = ri - rs;
-  int t = ti - ts;
-  for (int w = 0; w < wave; ++w) {
-    r += wave_rows[w];
-    t += wave_tiles[w];
-  }
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int e = 4 * tid + j;
-    if (e < E) {
-      row_off[e] = r;
-      tile_off[e] = t;
-    }
-    r += n[j];
-    t += (int)((n[j] + BM - 1) / BM);
-  }
-  if (tid == 255) {
-    row_off[E] = r;
-    tile_off[E] = t;
-  }
-  __syncthreads();
-}
-
 template <int BM, int BN, int WM, int WN, int BKB>
 __global__ __launch_bounds__(WM* WN* kWave) void grouped_gemm_kernel(GemmArgs p) {
   static_assert(WM * WN * kWave == 256, "schedule scan assumes 256 threads");

@@ -30,4 +30,12 @@ hipError_t launch_fp4_quant_pack(const uint16_t* w, int64_t N, int64_t K, uint8_
 hipError_t launch_fp4_linear(const uint16_t* x, int64_t M, int64_t K, const uint8_t* wp, int64_t N,
                              uint16_t* y, void* ws, hipStream_t stream);
 
+// grouped form: rows grouped by expert (group_list = rows per expert, E <=
+// 1024), expert e's packed weight (fmt 0 INT4, 1 FP4) at wp + e * the packed
+// bytes of one [N, K] weight; y BF16 [R, N]; no workspace
+hipError_t launch_lowbit_grouped(int fmt, const uint16_t* x, const int64_t* group_list, int64_t R, int64_t E,
+                                 int64_t N, int64_t K, const uint8_t* wp, uint16_t* y, hipStream_t stream);
+// a BF16 [R, I] = BF16(silu(gate) * up) of h BF16 [R, 2I] (gate first)
+hipError_t launch_lowbit_swiglu(const uint16_t* h, int64_t R, int64_t I, uint16_t* a, hipStream_t stream);
+
 }  // namespace w8a8

@@ -375,6 +375,276 @@ __global__ __launch_bounds__(64 * WAVES) void w4a16_decode_kernel(const uint16_t
 }
 
 // ---------------------------------------------------------------------------
+// Grouped form: the MoE experts' matmul with low-bit weights. Rows are grouped
+// by expert (group_list = rows per expert, as on the INT8 path); expert e's
+// packed weight starts at wp + e * w_stride.
+//
+// Work item = (expert e, 256-column group g, m-tile of up to 64 rows). Items
+// are ordered expert, column group, m-tile, and XCD x (workgroups b with
+// b % 8 == x) walks its own contiguous eighth of the list, so the m-tiles that
+// read the same weight columns run side by side on one XCD and share its L2.
+// Every workgroup derives the list from group_list itself (expert scan in
+// LDS): no workspace, no host sync.
+//
+// Workgroup = 4 wavefronts. Wavefront w owns the 16-column n-blocks 4w..4w+3
+// of the column group, so each weight is dequantized by exactly one wavefront,
+// and all rows of the tile. Per 128-deep k-chunk the tile's activations (MBr
+// 16-row blocks x 4 steps of 32, BF16, one 1 KB block per (step, m-block) in
+// the MFMA operand order) are loaded into registers 2 chunks ahead, each
+// wavefront loading a quarter of the blocks, and written to a ring of 3 LDS
+// slots one chunk ahead; each lane's packed codes and scales go to registers,
+// also 2 chunks ahead. All global traffic is ordinary loads, so the waits on
+// them are the compiler's, by register. One barrier per chunk.
+// The MFMA operands are swapped with respect to the linear above: A is the
+// dequantized weight (row = n), B the activation (column = m), so result lane
+// l holds the 4 adjacent columns n = 4 (l / 16) + {0..3} of row m = l % 16 and
+// stores them in one 8-byte write.
+//
+// Out-of-range reads are clamped, not masked: a row past the expert's last
+// reads that last row (its outputs are not stored), a step of the last chunk
+// past K reads the chunk's first step (it meets the zero padding of the
+// weight: a finite value times +0 adds nothing to the sum), and the loads "2
+// chunks ahead" of the last two chunks reload the last chunk (never used).
+// ---------------------------------------------------------------------------
+constexpr int kLbWaves = 4, kLbNBW = 4, kLbCols = 16 * kLbNBW * kLbWaves, kLbRows = 64, kLbRing = 3;
+constexpr int kLbStageMax = 4 * (kLbRows / 16) * 1024;
+
+struct LbArgs {
+  const uint16_t* x;     // BF16 rows [R, K]
+  const int64_t* gl;     // rows per expert [E]
+  const uint8_t* wp;     // packed expert weights, w_stride bytes apart
+  uint16_t* y;           // BF16 [R, N]
+  int64_t R, K, N, KC, NB, w_stride;
+  int E;
+};
+
+// codes (16 bytes) and scales (FMT 0: 4 BF16; FMT 1: 4 E8M0 bytes in .x) of the
+// wavefront's 4 n-blocks for one chunk
+struct LbW {
+  uint4 c[kLbNBW];
+  uint2 s[kLbNBW];
+};
+
+// the LDS writes of this wavefront are done and every wavefront got here (no
+// wait on global loads, unlike __syncthreads)
+__device__ __forceinline__ void lb_lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+template <int FMT, int MBr>
+struct LbItem {
+  static constexpr int64_t kChunkBytes = FMT == 0 ? kW4ChunkBytes : kFp4ChunkBytes;
+  static constexpr int kStage = 4 * MBr * 1024;
+
+  const uint8_t* wb[kLbNBW];      // n-block bases of this wavefront
+  int coff, soff;                 // lane offsets in a chunk: its 16 code bytes, its column's scales
+  const uint16_t* ab[MBr];        // activation row of this lane in each of this wavefront's blocks
+  int aj[MBr];                    // their step within the chunk, in elements (32 j)
+  int ablk[MBr];                  // their block index within a stage
+
+  __device__ __forceinline__ void load_w(LbW& w, int64_t kc) const {
+#pragma unroll
+    for (int q = 0; q < kLbNBW; ++q) {
+      const uint8_t* ch = wb[q] + kc * kChunkBytes;
+      w.c[q] = *reinterpret_cast<const uint4*>(ch + coff);
+      if (FMT == 0) w.s[q] = *reinterpret_cast<const uint2*>(ch + soff);
+      else w.s[q].x = *reinterpret_cast<const uint32_t*>(ch + soff);
+    }
+  }
+
+  __device__ __forceinline__ void load_a(uint4 (&a)[MBr], int64_t kc, int64_t K) const {
+#pragma unroll
+    for (int i = 0; i < MBr; ++i) {
+      const int64_t k0 = kc * kW4Chunk;
+      const int64_t col = k0 + aj[i] < K ? k0 + aj[i] : k0;  // wavefront-uniform
+      a[i] = *reinterpret_cast<const uint4*>(ab[i] + col);
+    }
+  }
+
+  __device__ __forceinline__ void store_a(uint8_t* stage, const uint4 (&a)[MBr], int lane) const {
+#pragma unroll
+    for (int i = 0; i < MBr; ++i) *reinterpret_cast<uint4*>(stage + ablk[i] * 1024 + lane * 16) = a[i];
+  }
+
+  __device__ __forceinline__ static void compute(const uint8_t* stage, const LbW& w, f32x4 (&acc)[kLbNBW][MBr],
+                                                 int lane) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      bf16x8 bw[kLbNBW];
+#pragma unroll
+      for (int q = 0; q < kLbNBW; ++q) {
+        const uint32_t word = j == 0 ? w.c[q].x : j == 1 ? w.c[q].y : j == 2 ? w.c[q].z : w.c[q].w;
+        if (FMT == 0) {
+          const uint32_t h = j < 2 ? w.s[q].x : w.s[q].y;
+          const float sc = __uint_as_float((j & 1) ? (h & 0xFFFF0000u) : (h << 16));
+          bw[q] = w4_dequant8(word, sc);
+        } else {
+          const float sc = __builtin_ldexpf(1.0f, (int)((w.s[q].x >> (8 * j)) & 0xFFu) - 127);
+          bw[q] = fp4_dequant8(word, sc);
+        }
+      }
+      bf16x8 ba[MBr];
+#pragma unroll
+      for (int mb = 0; mb < MBr; ++mb)
+        ba[mb] = *reinterpret_cast<const bf16x8*>(stage + (j * MBr + mb) * 1024 + lane * 16);
+#pragma unroll
+      for (int q = 0; q < kLbNBW; ++q)
+#pragma unroll
+        for (int mb = 0; mb < MBr; ++mb)
+          acc[q][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bw[q], ba[mb], acc[q][mb], 0, 0, 0);
+    }
+  }
+
+  // register sets of 3 chunks in flight: set c % 3 holds chunk c
+  struct Regs {
+    LbW w[kLbRing];
+    uint4 a[kLbRing][MBr];
+  };
+
+  // chunk kc (ring slot and register set S = kc % 3): loads chunk kc + 2 into
+  // set (S + 2) % 3, computes chunk kc and writes the activations of chunk
+  // kc + 1 to its slot
+  template <int S>
+  __device__ __forceinline__ void chunk(const LbArgs& p, uint8_t* ring, int64_t kc, Regs& r,
+                                        f32x4 (&acc)[kLbNBW][MBr], int lane) const {
+    // slot S (written during chunk kc - 1) complete; slot (S + 1) % 3 (chunk
+    // kc - 2) no longer read by anyone
+    lb_lds_barrier();
+    const int64_t kn = kc + 2 < p.KC ? kc + 2 : p.KC - 1;
+    load_w(r.w[(S + 2) % kLbRing], kn);
+    load_a(r.a[(S + 2) % kLbRing], kn, p.K);
+    compute(ring + S * kStage, r.w[S], acc, lane);
+    store_a(ring + ((S + 1) % kLbRing) * kStage, r.a[(S + 1) % kLbRing], lane);
+  }
+
+  __device__ __forceinline__ void run(const LbArgs& p, uint8_t* ring, int e, int64_t row0, int64_t row_end,
+                                      int64_t nb0, int lane, int wave) {
+#pragma unroll
+    for (int q = 0; q < kLbNBW; ++q) {
+      const int64_t nb = nb0 + q < p.NB ? nb0 + q : p.NB - 1;
+      wb[q] = p.wp + e * p.w_stride + nb * p.KC * kChunkBytes;
+    }
+    coff = lane * 16;
+    soff = 1024 + (lane & 15) * (FMT == 0 ? 8 : 4);
+#pragma unroll
+    for (int i = 0; i < MBr; ++i) {
+      const int b = wave + kLbWaves * i;  // block b = step j * MBr + m-block mb
+      const int j = b / MBr, mb = b % MBr;
+      int64_t r = row0 + 16 * mb + (lane & 15);
+      r = r < row_end ? r : row_end - 1;
+      ab[i] = p.x + r * p.K + 8 * (lane >> 4);
+      aj[i] = 32 * j;
+      ablk[i] = b;
+    }
+    f32x4 acc[kLbNBW][MBr];
+#pragma unroll
+    for (int q = 0; q < kLbNBW; ++q)
+#pragma unroll
+      for (int mb = 0; mb < MBr; ++mb) acc[q][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    Regs r;
+    const int64_t k1 = p.KC > 1 ? 1 : 0;
+    load_a(r.a[0], 0, p.K);
+    load_w(r.w[0], 0);
+    load_a(r.a[1], k1, p.K);
+    load_w(r.w[1], k1);
+    store_a(ring, r.a[0], lane);
+    // one call site per register set (a second one, for a remainder after
+    // the loop, lets the compiler merge them and index the sets at run time)
+    for (int64_t kc = 0; kc < p.KC; kc += 3) {
+      chunk<0>(p, ring, kc, r, acc, lane);
+      if (kc + 1 < p.KC) chunk<1>(p, ring, kc + 1, r, acc, lane);
+      if (kc + 2 < p.KC) chunk<2>(p, ring, kc + 2, r, acc, lane);
+    }
+    // result lane l: columns 4 (l / 16) + {0..3} of n-block q, row l % 16 of m-block mb
+#pragma unroll
+    for (int q = 0; q < kLbNBW; ++q) {
+      if (nb0 + q >= p.NB) continue;  // wavefront-uniform
+      const int64_t n = (nb0 + q) * 16 + 4 * (lane >> 4);
+#pragma unroll
+      for (int mb = 0; mb < MBr; ++mb) {
+        const int64_t m = row0 + 16 * mb + (lane & 15);
+        if (m < row_end) {
+          const f32x4 v = acc[q][mb];
+          *reinterpret_cast<uint2*>(p.y + m * p.N + n) =
+              uint2{f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16), f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16)};
+        }
+      }
+    }
+    lb_lds_barrier();  // every wavefront done with the ring before the next item writes it
+  }
+};
+
+template <int FMT>
+__global__ __launch_bounds__(64 * kLbWaves, 2) void lowbit_grouped_kernel(LbArgs p) {
+  static_assert(kLbWaves * kWave == 256, "the expert scan assumes 256 threads");
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[kLbRing * kLbStageMax];
+  __shared__ int64_t row_off[kMaxExperts + 1];
+  __shared__ int tile_off[kMaxExperts + 1];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int E = p.E;
+  build_schedule<kLbRows>(p.gl, E, row_off, tile_off);
+  const int64_t NG = (p.N + kLbCols - 1) / kLbCols;
+  const int64_t total = (int64_t)tile_off[E] * NG;
+  const int64_t per = (total + 7) / 8;
+  const int64_t first = (int64_t)(blockIdx.x % 8) * per;
+  const int64_t end = min(first + per, total);
+  const int64_t slots = gridDim.x / 8;  // the grid is a multiple of 8
+  for (int64_t i = first + blockIdx.x / 8; i < end; i += slots) {
+    // expert of item i: last e with tile_off[e] * NG <= i
+    int lo = 0, hi = E - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if ((int64_t)tile_off[mid] * NG <= i) lo = mid; else hi = mid - 1;
+    }
+    const int e = lo;
+    const int64_t mtiles = tile_off[e + 1] - tile_off[e];
+    const int64_t local = i - (int64_t)tile_off[e] * NG;
+    const int64_t g = local / mtiles, mt = local % mtiles;
+    const int64_t row0 = row_off[e] + mt * kLbRows;
+    // counts that sum past R are a caller error; rows at or past R are never touched
+    const int64_t row_end = min(min(row_off[e + 1], row0 + kLbRows), p.R);
+    if (row0 >= row_end) continue;
+    const int64_t nb0 = g * (kLbCols / 16) + kLbNBW * wave;
+    const int64_t rows = row_end - row0;
+    // tiles of 1, 2 or 4 16-row blocks (a third variant of 3 blocks makes the
+    // compiler keep a register array in scratch memory)
+    if (rows > 32) LbItem<FMT, 4>().run(p, ring, e, row0, row_end, nb0, lane, wave);
+    else if (rows > 16) LbItem<FMT, 2>().run(p, ring, e, row0, row_end, nb0, lane, wave);
+    else LbItem<FMT, 1>().run(p, ring, e, row0, row_end, nb0, lane, wave);
+  }
+}
+
+// a = BF16(silu(gate) * up) of h = [gate | up] [R, 2I], the fixed fp32 sequence
+// of swiglu_fixed; 8 outputs per thread with 16-byte accesses (VEC) or one
+__global__ __launch_bounds__(256) void lowbit_swiglu_vec(const uint16_t* __restrict__ h, int64_t R, int64_t I,
+                                                         uint16_t* __restrict__ a) {
+  const int64_t per_row = I / 8;
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= R * per_row) return;
+  const int64_t r = t / per_row, j = (t % per_row) * 8;
+  const uint4 g = *reinterpret_cast<const uint4*>(h + r * 2 * I + j);
+  const uint4 u = *reinterpret_cast<const uint4*>(h + r * 2 * I + I + j);
+  const uint32_t gw[4] = {g.x, g.y, g.z, g.w}, uw[4] = {u.x, u.y, u.z, u.w};
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float lo = swiglu_fixed(bf16_to_f32(gw[i] & 0xFFFFu), bf16_to_f32(uw[i] & 0xFFFFu));
+    const float hi = swiglu_fixed(bf16_to_f32(gw[i] >> 16), bf16_to_f32(uw[i] >> 16));
+    o[i] = f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+  }
+  *reinterpret_cast<uint4*>(a + r * I + j) = uint4{o[0], o[1], o[2], o[3]};
+}
+
+__global__ __launch_bounds__(256) void lowbit_swiglu_generic(const uint16_t* __restrict__ h, int64_t R,
+                                                             int64_t I, uint16_t* __restrict__ a) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= R * I) return;
+  const int64_t r = t / I, j = t % I;
+  a[t] = (uint16_t)f32_to_bf16(swiglu_fixed(bf16_to_f32(h[r * 2 * I + j]), bf16_to_f32(h[r * 2 * I + I + j])));
+}
+
+// ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
 int64_t w4_chunks(int64_t K) { return (K + kW4Chunk - 1) / kW4Chunk; }
@@ -440,6 +710,38 @@ hipError_t launch_w4a16_linear(const uint16_t* x, int64_t M, int64_t K, const ui
 hipError_t launch_fp4_linear(const uint16_t* x, int64_t M, int64_t K, const uint8_t* wp, int64_t N,
                              uint16_t* y, void* ws, hipStream_t stream) {
   return launch_decode<1>(x, M, K, wp, N, y, ws, stream);
+}
+
+hipError_t launch_lowbit_grouped(int fmt, const uint16_t* x, const int64_t* group_list, int64_t R, int64_t E,
+                                 int64_t N, int64_t K, const uint8_t* wp, uint16_t* y, hipStream_t stream) {
+  if (R == 0 || N == 0) return hipSuccess;
+  LbArgs p;
+  p.x = x;
+  p.gl = group_list;
+  p.wp = wp;
+  p.y = y;
+  p.R = R;
+  p.K = K;
+  p.N = N;
+  p.KC = w4_chunks(K);
+  p.NB = (N + 15) / 16;
+  p.w_stride = fmt == 0 ? w4_packed_bytes(N, K) : fp4_packed_bytes(N, K);
+  p.E = (int)E;
+  // two workgroups per CU, 256 CUs
+  constexpr unsigned kGrid = 512;
+  if (fmt == 0) hipLaunchKernelGGL(lowbit_grouped_kernel<0>, dim3(kGrid), dim3(64 * kLbWaves), 0, stream, p);
+  else hipLaunchKernelGGL(lowbit_grouped_kernel<1>, dim3(kGrid), dim3(64 * kLbWaves), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_lowbit_swiglu(const uint16_t* h, int64_t R, int64_t I, uint16_t* a, hipStream_t stream) {
+  if (R == 0) return hipSuccess;
+  const bool vec = I % 8 == 0 && ((uintptr_t)h & 15) == 0 && ((uintptr_t)a & 15) == 0;
+  const int64_t threads = vec ? R * (I / 8) : R * I;
+  const dim3 grid((unsigned)((threads + 255) / 256));
+  if (vec) hipLaunchKernelGGL(lowbit_swiglu_vec, grid, dim3(256), 0, stream, h, R, I, a);
+  else hipLaunchKernelGGL(lowbit_swiglu_generic, grid, dim3(256), 0, stream, h, R, I, a);
+  return hipGetLastError();
 }
 
 }  // namespace w8a8

@@ -18,6 +18,9 @@ Shapes and distributions (the five workloads):
   moe       T=2048 tokens, H=4096, E=256 experts, top-8, I=2048; X BF16 N(0,1);
             logits N(0,1) + per-expert bias N(0, 1.5); W13 int8 [E, 2I, H],
             W2 int8 [E, H, I]; scales U[1e-3, 1e-2]
+  lowbit_moe the moe routing and activations with BF16 expert weights W13
+            [E, 2I, H], W2 [E, H, I] drawn N(0, 0.02^2), quantized to INT4 or
+            FP4 at load time
 """
 
 from __future__ import annotations
@@ -29,7 +32,7 @@ import torch
 
 # stream tags
 (_T_X, _T_W, _T_WS, _T_B, _T_LOGITS, _T_EBIAS, _T_W13, _T_W2, _T_W13S, _T_W2S, _T_MXW,
- _T_MXS, _T_MXW13, _T_MXS13, _T_MXW2, _T_MXS2) = range(16)
+ _T_MXS, _T_MXW13, _T_MXS13, _T_MXW2, _T_MXS2, _T_LBW13, _T_LBW2) = range(18)
 
 
 def rng_for(seed: int, tag: int, index: int = 0) -> np.random.Generator:
@@ -278,3 +281,49 @@ def mx_moe(T: int = 2048, H: int = 4096, I: int = 2048, E: int = 256, top_k: int
     x = activations(T, H, 0.0, seed)
     row_token, _, group_list = route_topk(T, E, top_k, seed, ebias_sigma)
     return MxMoE(T, H, I, E, top_k, seed, bn, bk, x, row_token, group_list)
+
+
+# ---------------------------------------------------------------------------
+# low-bit (INT4 / FP4) expert weights on the MoE workload
+# ---------------------------------------------------------------------------
+
+LOWBIT_SIGMA = 0.02
+
+
+@dataclass
+class LowbitMoE:
+    T: int
+    H: int
+    I: int
+    E: int
+    top_k: int
+    seed: int
+    x_tokens: np.ndarray      # BF16 bits [T, H]
+    row_token: np.ndarray     # [R]
+    group_list: np.ndarray    # int64 [E]
+
+    @property
+    def R(self):
+        return int(self.row_token.shape[0])
+
+    def x_rows(self) -> np.ndarray:
+        return self.x_tokens[self.row_token]
+
+    def _w(self, N, K, tag, e):
+        r = rng_for(self.seed, tag, e)
+        return to_bf16_bits(r.standard_normal((N, K), dtype=np.float32) * np.float32(LOWBIT_SIGMA))
+
+    def w13(self, e: int) -> np.ndarray:
+        """BF16 bits [2I, H] of expert e."""
+        return self._w(2 * self.I, self.H, _T_LBW13, e)
+
+    def w2(self, e: int) -> np.ndarray:
+        """BF16 bits [H, I] of expert e."""
+        return self._w(self.H, self.I, _T_LBW2, e)
+
+
+def lowbit_moe(T: int = 2048, H: int = 4096, I: int = 2048, E: int = 256, top_k: int = 8,
+               seed: int = 0, ebias_sigma: float = 1.5) -> LowbitMoE:
+    x = activations(T, H, 0.0, seed)
+    row_token, _, group_list = route_topk(T, E, top_k, seed, ebias_sigma)
+    return LowbitMoE(T, H, I, E, top_k, seed, x, row_token, group_list)

@@ -69,7 +69,7 @@ def _innermost_mfma_loops(lines):
 
 
 @pytest.mark.skipif(_hipcc() is None, reason="hipcc not available")
-@pytest.mark.parametrize("src", ["gemm.hip", "mx.hip"])
+@pytest.mark.parametrize("src", ["gemm.hip", "mx.hip", "w4a16.hip"])
 def test_mfma_loops_do_not_touch_scratch(src, tmp_path):
     out = tmp_path / "k.s"
     r = subprocess.run([_hipcc(), *_flags(), "-S", os.path.join(CSRC, src), "-o", str(out)],

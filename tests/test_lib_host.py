@@ -238,3 +238,37 @@ def test_fp4_validation_before_launch(w):
     assert L.w8a8_fp4_linear(ctypes.c_void_p(264), 4, 64, p, 16, p, None, 0, None) == 3
     assert L.w8a8_fp4_linear(None, 0, 64, None, 16, None, None, 0, None) == 0
     assert L.w8a8_fp4_linear(p, 17, 64, p, 16, p, None, 0, None) == 5
+
+
+def test_lowbit_grouped_validation_before_launch(w):
+    L = w.lib
+    p = ctypes.c_void_p(256)  # never dereferenced: validation fails first
+    g = L.w8a8_w4a16_grouped_gemm
+    assert g(2, p, p, 64, 4, 32, 64, p, p, None) == 4            # unknown weight format
+    assert g(0, p, p, 64, 4, 24, 64, p, p, None) == 4            # N % 16
+    assert g(1, p, p, 64, 4, 32, 48, p, p, None) == 4            # K % 32
+    assert g(0, p, p, 64, 1025, 32, 64, p, p, None) == 4         # more than 1024 experts
+    assert g(0, p, p, 64, 0, 32, 64, p, p, None) == 2            # no expert
+    assert g(0, p, p, -1, 4, 32, 64, p, p, None) == 2
+    assert g(0, None, None, 0, 4, 32, 64, None, None, None) == 0  # R == 0: nothing to do
+    assert g(0, None, p, 64, 4, 32, 64, p, p, None) == 1
+    assert g(0, ctypes.c_void_p(264), p, 64, 4, 32, 64, p, p, None) == 3   # x 16-byte aligned
+    assert g(1, p, p, 64, 4, 32, 64, p, ctypes.c_void_p(260), None) == 3   # y 8-byte aligned
+    s = L.w8a8_w4a16_swiglu
+    assert s(p, -1, 64, p, None) == 2
+    assert s(p, 4, 0, p, None) == 2
+    assert s(None, 0, 64, None, None) == 0
+    assert s(p, 4, 64, None, None) == 1
+    # workspace: h BF16 [R, 2I], then a BF16 [R, I], each 256-byte aligned
+    assert L.w8a8_w4a16_moe_workspace_bytes(16384, 4096, 2048) == 16384 * 4096 * 2 + 16384 * 2048 * 2
+    assert L.w8a8_w4a16_moe_workspace_bytes(3, 64, 32) == 512 + 256
+    assert L.w8a8_w4a16_moe_workspace_bytes(0, 64, 32) == 0
+    m = L.w8a8_w4a16_moe_grouped
+    need = L.w8a8_w4a16_moe_workspace_bytes(64, 64, 32)
+    assert m(0, p, p, 64, 4, 64, 48, p, p, p, p, 1 << 30, None) == 4          # I % 32
+    assert m(0, p, p, 64, 4, 48, 32, p, p, p, p, 1 << 30, None) == 4          # H % 32
+    assert m(0, p, p, 64, 4, 64, 32, p, p, p, None, 0, None) == 5
+    assert m(0, p, p, 64, 4, 64, 32, p, p, p, p, need - 1, None) == 5
+    assert m(0, p, p, 64, 4, 64, 32, p, p, p, ctypes.c_void_p(272), need, None) == 5
+    assert m(0, p, p, 64, 4, 64, 32, None, p, p, p, need, None) == 1
+    assert m(1, None, None, 0, 4, 64, 32, None, None, None, None, 0, None) == 0
