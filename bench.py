@@ -61,7 +61,7 @@ def _args():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="default",
                     choices=["default", "decode", "prefill", "moe", "moe_layer", "tiny", "copy", "mx",
-                             "mx_moe", "static", "w4a16", "fp4"])
+                             "mx_moe", "static", "w4a16", "fp4", "w4a16_moe", "fp4_moe"])
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="approximate budget of the oracle timing on the host")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -714,6 +714,140 @@ class W4Workload(Workload):
                            f"{n} whole steps (weight quantized outside the timing)")
 
 
+class LowbitMoeWorkload(Workload):
+    """The MoE workload (2048 tokens, top-8 of 256 experts, H 4096, I 2048,
+    skewed routing) with low-bit expert weights: BF16 N(0, 0.02^2) drawn on the
+    device from a seeded generator, quantized at load time to INT4 (BF16 scale
+    per 32) or FP4 (E8M0 scale per 32). Step = the chain W13 -> BF16 SwiGLU ->
+    W2 on the expert-grouped BF16 rows."""
+
+    def __init__(self, w, torch, fmt="int4"):
+        super().__init__(w, torch)
+        import numpy as np
+
+        import synth
+        self.fmt = fmt
+        self.code = w.LOWBIT_INT4 if fmt == "int4" else w.LOWBIT_FP4
+        self.name = "w4a16_moe" if fmt == "int4" else "fp4_moe"
+        m = synth.lowbit_moe(seed=0)
+        self.m = m
+        E, H, I = m.E, m.H, m.I
+        dev = "cuda"
+        quant = w.w4a16_quant_weight if fmt == "int4" else w.fp4_quant_weight
+        nbytes = w.w4a16_packed_bytes if fmt == "int4" else w.fp4_packed_bytes
+        self.b13, self.b2 = nbytes(2 * I, H), nbytes(H, I)
+        self.w13p = torch.empty((E * self.b13,), dtype=torch.uint8, device=dev)
+        self.w2p = torch.empty((E * self.b2,), dtype=torch.uint8, device=dev)
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(0)
+        chunk = 16   # experts per quantization call (a 512 MiB BF16 stack)
+        for e0 in range(0, E, chunk):
+            for N, K, buf, b in ((2 * I, H, self.w13p, self.b13), (H, I, self.w2p, self.b2)):
+                wb = (torch.randn((chunk * N, K), generator=gen, device=dev) * synth.LOWBIT_SIGMA).to(torch.bfloat16)
+                _, _, pk = quant(wb)
+                buf[e0 * b:(e0 + chunk) * b].copy_(pk[:chunk * b])
+                del wb, pk
+        self.gl = torch.from_numpy(m.group_list).to(dev)
+        self.x = torch.from_numpy(m.x_rows().view(np.int16)).to(dev).view(torch.bfloat16)
+        R = m.R
+        self.y = torch.empty((R, H), dtype=torch.bfloat16, device=dev)
+        self.h = torch.empty((R, 2 * I), dtype=torch.bfloat16, device=dev)
+        self.a = torch.empty((R, I), dtype=torch.bfloat16, device=dev)
+        self.ws = torch.empty((w.w4a16_moe_workspace_bytes(R, H, I),), dtype=torch.uint8, device=dev)
+        self.unit = "tokens/s"
+        self.bound = "mfma"
+        self.capture([self._step], [(self._w13, 1, "w13"), (self._w2, 1, "w2")])
+
+    def _step(self):
+        self.w.w4a16_moe_grouped(self.x, self.gl, self.w13p, self.w2p, self.m.I, fmt=self.code, y=self.y,
+                                 workspace=self.ws)
+
+    def _w13(self):
+        self.w.w4a16_grouped_gemm(self.x, self.gl, self.w13p, 2 * self.m.I, fmt=self.code, y=self.h)
+
+    def _w2(self):
+        self.w.w4a16_grouped_gemm(self.a, self.gl, self.w2p, self.m.H, fmt=self.code, y=self.y)
+
+    def nonempty(self):
+        return int((self.m.group_list > 0).sum())
+
+    def gemm_flops(self, which):
+        m = self.m
+        return 2 * m.R * (2 * m.I) * m.H if which == "w13" else 2 * m.R * m.H * m.I
+
+    def gemm_bytes(self):
+        """Both grouped GEMMs: weights (codes + scales) of the experts that own
+        rows, BF16 rows in and out, group_list."""
+        m = self.m
+        R, H, I = m.R, m.H, m.I
+        return self.nonempty() * (self.b13 + self.b2) + 2 * R * (H + 2 * I) + 2 * R * (I + H) + 16 * m.E
+
+    def alg_bytes(self):
+        """The GEMMs' bytes and the SwiGLU's (BF16 [R, 2I] in, [R, I] out)."""
+        m = self.m
+        return self.gemm_bytes() + 2 * m.R * 3 * m.I
+
+    def value(self, sec_per_step):
+        return self.m.T / sec_per_step
+
+    def dominant(self, per_key_ms):
+        fl = self.gemm_flops("w13") + self.gemm_flops("w2")
+        tot = per_key_ms["w13"] + per_key_ms["w2"]
+        ach = fl / (tot * 1e-3) / 1e12
+        return dict(bound="mfma", achieved=ach, peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
+                    frac=ach / PEAK_BF16_TFLOPS,
+                    gemm_hbm_gbs=self.gemm_bytes() / (tot * 1e-3) / 1e9)
+
+    def config(self):
+        m = self.m
+        g = m.group_list
+        fmt = ("INT4 per 32 input channels, BF16 scale = amax / 7" if self.fmt == "int4" else
+               "FP4 E2M1 per 32 input channels, E8M0 scale 2^(floor(log2 amax) - 2)")
+        return {"workload": self.name, "T": m.T, "top_k": m.top_k, "E": m.E, "H": m.H, "I": m.I,
+                "R": m.R, "nonempty_experts": self.nonempty(), "max_rows_per_expert": int(g.max()),
+                "weights": "BF16 N(0, 0.02^2) -> " + fmt,
+                "routing": "logits N(0,1) + expert bias N(0,1.5), top-8"}
+
+    def cpu_baseline(self, budget_s):
+        import numpy as np
+
+        import oracle as O
+        m = self.m
+        W4 = O.w4a16
+        off = O.group_offsets(m.group_list)
+        xr = m.x_rows()
+        H, I = m.H, m.I
+
+        def codes_scales(N, K, r):
+            # seeded codes and scales of the format's ranges (the chain's cost
+            # does not depend on their values; the oracle's FP4 quantizer, an
+            # exhaustive nearest-value search, would take ~9 s per expert)
+            if self.fmt == "int4":
+                q = r.integers(-8, 8, (N, K), dtype=np.int8)
+                sc = O.f32_to_bf16(r.uniform(0.004, 0.01, (N, K // 32)).astype(np.float32))
+            else:
+                q = r.integers(0, 16, (N, K), dtype=np.uint8)
+                sc = r.integers(118, 123, (N, K // 32), dtype=np.uint8)
+            return q[None], sc[None]
+
+        timed, rows, e = 0.0, 0, 0
+        while timed < budget_s and e < m.E:
+            a, b = int(off[e]), int(off[e + 1])
+            if b > a:
+                r = np.random.default_rng([0, 77, e])
+                q13, s13 = codes_scales(2 * I, H, r)
+                q2, s2 = codes_scales(H, I, r)
+                t0 = time.perf_counter()
+                W4.lowbit_moe(self.fmt, np.array([b - a], np.int64), xr[a:b], q13, s13, q2, s2)
+                timed += time.perf_counter() - t0
+                rows += b - a
+            e += 1
+        return dict(value=rows / m.top_k / timed, unit="tokens/s",
+                    sample=f"oracle low-bit MoE chain over experts 0..{e - 1} ({rows} of {m.R} rows) on "
+                           f"seeded codes and scales of the format's ranges (drawn outside the timing), "
+                           f"tokens = rows / top_k")
+
+
 class MxWorkload(Workload):
     def __init__(self, w, torch):
         super().__init__(w, torch)
@@ -998,6 +1132,10 @@ def _make_workload(name, w, torch):
         return W4Workload(w, torch)
     if name == "fp4":
         return W4Workload(w, torch, fmt="fp4")
+    if name == "w4a16_moe":
+        return LowbitMoeWorkload(w, torch)
+    if name == "fp4_moe":
+        return LowbitMoeWorkload(w, torch, fmt="fp4")
     return MoeWorkload(w, torch)
 
 
@@ -1044,7 +1182,8 @@ def _run(name, w, torch, steps, warmup, cpu_seconds, cpu_baseline):
         "unit": wl.unit,
         "ms_per_step": round(sec * 1e3, 5),
         "dtype": {"mx": "bf16 (E4M3 x 2^E operands)", "mx_moe": "bf16 (E4M3 x 2^E operands)",
-                  "w4a16": "bf16 (int4 weights)", "fp4": "bf16 (fp4 weights)"}.get(wl.name, "int8"),
+                  "w4a16": "bf16 (int4 weights)", "fp4": "bf16 (fp4 weights)",
+                  "w4a16_moe": "bf16 (int4 weights)", "fp4_moe": "bf16 (fp4 weights)"}.get(wl.name, "int8"),
         "config": wl.config(),
         "roofline": {k: (round(v, 4) if isinstance(v, float) else v) for k, v in roof.items()},
     }

@@ -448,7 +448,8 @@ struct LbItem {
       const uint8_t* ch = wb[q] + kc * kChunkBytes;
       w.c[q] = *reinterpret_cast<const uint4*>(ch + coff);
       if (FMT == 0) w.s[q] = *reinterpret_cast<const uint2*>(ch + soff);
-      else w.s[q].x = *reinterpret_cast<const uint32_t*>(ch + soff);
+      // FP4: .y set too (an undefined half keeps the register sets in memory)
+      else w.s[q] = uint2{*reinterpret_cast<const uint32_t*>(ch + soff), 0u};
     }
   }
 
