@@ -311,8 +311,9 @@ int w8a8_mx_prepack_weight(const uint8_t* w_e4m3, const uint8_t* w_e8m0, int64_t
 
 /*
  * w8a8_mx_linear  [MXFP8 Deep Dive 5]: y [M, N] BF16 = block-scaled product of
- *   the MX activation and the packed MX weight, fp32 accumulation
- *   (v_mfma_scale_f32_32x32x64_f8f6f4), BF16 round to nearest even.
+ *   the MX activation and the packed MX weight: both operands dequantized
+ *   exactly to BF16 (E4M3 x 2^E), exact products on the BF16 MFMA, fp32
+ *   accumulation, BF16 round to nearest even.
  *   x: BF16 [M, K] (MX-quantized inside with scale_alg) when x_e8m0 == NULL,
  *   else an E4M3 payload [M, K] with its E8M0 scales x_e8m0 [M, K/32].
  *   workspace: w8a8_mx_linear_workspace_bytes(M, K) bytes, 256-byte aligned.
@@ -367,7 +368,7 @@ int w8a8_mx_gemm(const uint8_t* a_e4m3, const uint8_t* a_scale_kb, int64_t M, in
  *   input is then the BF16 SwiGLU above), 16-byte aligned; each row is
  *   MX-quantized at run time (scale_alg), multiplied with its expert's
  *   prepared weight (w_packed: E x w8a8_mx_packed_bytes(N, K), from
- *   w8a8_mx_moe_prepare) by the block-scaled MFMA with fp32 accumulation ->
+ *   w8a8_mx_moe_prepare) with exact BF16 products and fp32 accumulation ->
  *   y BF16 [R, N]. workspace: w8a8_mx_grouped_workspace_bytes(R, E, K), 256-byte
  *   aligned (tile schedule and the MX activation, every expert padded to 16
  *   rows). K % 32 == 0, E <= 1024.

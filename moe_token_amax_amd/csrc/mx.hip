@@ -1,5 +1,7 @@
 // MXFP8 variant for gfx950: block-FP8 resolve, MX quantization and the
-// block-scaled GEMM on v_mfma_scale_f32_32x32x64_f8f6f4.
+// block-scaled GEMM, whose operands are dequantized exactly to BF16 in
+// registers (E4M3 x 2^E by v_cvt_scalef32_pk_bf16_fp8) and multiplied on the
+// BF16 MFMAs with fp32 accumulation (every product exact).
 //
 // ("Qwen3.8-FP8 on Ascend 950: Why Weights Become MXFP8 at Load Time":
 // Deep Dive 2 resolve equation, Deep Dive 3 E4M3 payload + E8M0 scale per 32
