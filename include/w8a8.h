@@ -84,6 +84,16 @@ int w8a8_dynamic_quant(const uint16_t* x, int64_t M, int64_t K, int8_t* q,
                        float* x_scale, void* stream);
 
 /*
+ * w8a8_dynamic_quant_ld: w8a8_dynamic_quant on row-strided buffers: row m of
+ *   x at x + m * ldx (ldx >= K BF16 elements), its codes at q + m * ldq
+ *   (ldq >= K bytes); codes and scales identical to w8a8_dynamic_quant
+ *   (which is the case ldx = ldq = K). A ld below K is W8A8_ERR_SHAPE. For a
+ *   column slice of a wider activation without a copy.
+ */
+int w8a8_dynamic_quant_ld(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int8_t* q, int64_t ldq,
+                          float* x_scale, void* stream);
+
+/*
  * The same quantization with the codes written in the packed block layout of
  * the weights (w8a8_prepack_weight with E = 1, the activation rows in the
  * place of the weight rows): 1 KB blocks [ceil(M/16)][ceil(K/64)], byte
@@ -143,6 +153,19 @@ int w8a8_linear(const int8_t* q, const float* x_scale, int64_t M, int64_t K,
                 const void* w_packed, const float* w_scale, int64_t N,
                 const uint16_t* bias, void* y, int out, void* workspace,
                 int64_t ws_bytes, void* stream);
+
+/*
+ * w8a8_linear_ld [DSV4] §二: w8a8_linear on row-major INT8 codes with row
+ *   strides: row m of q at q + m * ldq (ldq >= K), row m of y at y + m * ldy
+ *   elements (ldy >= N; BF16 or INT32 by out). x_scale is required (codes
+ *   input; the BF16-input and W8A8_A_PACKED forms stay with w8a8_linear).
+ *   Results identical to w8a8_linear, which is the case ldq = K, ldy = N.
+ *   Workspace as w8a8_linear's for codes input. A ld below K / N is
+ *   W8A8_ERR_SHAPE.
+ */
+int w8a8_linear_ld(const int8_t* q, int64_t ldq, const float* x_scale, int64_t M, int64_t K,
+                   const void* w_packed, const float* w_scale, int64_t N, const uint16_t* bias, void* y,
+                   int64_t ldy, int out, void* workspace, int64_t ws_bytes, void* stream);
 
 /*
  * Grouped INT8 matmul over experts.  [DSV4 §三: npu_grouped_matmul(x, weight,

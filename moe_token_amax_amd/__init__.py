@@ -106,6 +106,9 @@ def _load():
         "w8a8_abi_version": (ctypes.c_int, []),
         "w8a8_dynamic_quant": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p]),
         "w8a8_dynamic_quant_packed": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p]),
+        "w8a8_dynamic_quant_ld": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_i64, _c_p, _c_p]),
+        "w8a8_linear_ld": (ctypes.c_int, [_c_p, _c_i64, _c_p, _c_i64, _c_i64, _c_p, _c_p, _c_i64, _c_p, _c_p,
+                                          _c_i64, ctypes.c_int, _c_p, _c_i64, _c_p]),
         "w8a8_packed_weight_bytes": (_c_i64, [_c_i64, _c_i64, _c_i64]),
         "w8a8_prepack_weight": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p]),
         "w8a8_linear_workspace_bytes": (_c_i64, [_c_i64, _c_i64, _c_i64]),
@@ -198,6 +201,25 @@ def _ptr(t: torch.Tensor | None):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _rows(t: torch.Tensor, dtype, name: str) -> int:
+    """A 2-D tensor whose rows are contiguous (a row stride of at least its
+    width, e.g. a column slice of a wider matrix); returns the row stride."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a GPU device")
+    if t.dim() != 2:
+        raise ValueError(f"{name} must have 2 dims, got {t.dim()}")
+    if t.shape[1] > 1 and t.stride(1) != 1:
+        raise ValueError(f"{name}: the elements of a row must be contiguous")
+    ld = t.stride(0) if t.shape[0] > 1 else t.shape[1]
+    if ld < t.shape[1]:
+        raise ValueError(f"{name}: row stride below the row width")
+    return int(ld)
+
+
 def _need(t: torch.Tensor, dtype, name: str, ndim: int | None = None):
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
@@ -213,18 +235,22 @@ def _need(t: torch.Tensor, dtype, name: str, ndim: int | None = None):
 
 def dynamic_quant(x: torch.Tensor, q: torch.Tensor | None = None,
                   scale: torch.Tensor | None = None):
-    """BF16 [M, K] -> (int8 [M, K], float32 [M])."""
-    _need(x, torch.bfloat16, "x", 2)
+    """BF16 [M, K] -> (int8 [M, K], float32 [M]). x and q may be row-strided
+    (rows contiguous, e.g. column slices of wider matrices)."""
+    ldx = _rows(x, torch.bfloat16, "x")
     M, K = x.shape
     if q is None:
         q = torch.empty((M, K), dtype=torch.int8, device=x.device)
     if scale is None:
         scale = torch.empty((M,), dtype=torch.float32, device=x.device)
-    _need(q, torch.int8, "q", 2)
+    ldq = _rows(q, torch.int8, "q")
     _need(scale, torch.float32, "scale", 1)
     if tuple(q.shape) != (M, K) or scale.shape[0] != M:
         raise ValueError("q / scale shape mismatch")
-    _check(lib.w8a8_dynamic_quant(_ptr(x), M, K, _ptr(q), _ptr(scale), _stream()))
+    if ldx == K and ldq == K:
+        _check(lib.w8a8_dynamic_quant(_ptr(x), M, K, _ptr(q), _ptr(scale), _stream()))
+    else:
+        _check(lib.w8a8_dynamic_quant_ld(_ptr(x), M, K, ldx, _ptr(q), ldq, _ptr(scale), _stream()))
     return q, scale
 
 
@@ -286,8 +312,9 @@ def _workspace(nbytes: int, device, ws: torch.Tensor | None):
 def linear(q: torch.Tensor, x_scale: torch.Tensor, w_packed: torch.Tensor, w_scale: torch.Tensor,
            N: int, bias: torch.Tensor | None = None, out: int = OUT_BF16,
            y: torch.Tensor | None = None, workspace: torch.Tensor | None = None):
-    """INT8 [M, K] x packed W [N, K] -> BF16 [M, N] (or int32 with out=OUT_I32)."""
-    _need(q, torch.int8, "q", 2)
+    """INT8 [M, K] x packed W [N, K] -> BF16 [M, N] (or int32 with out=OUT_I32).
+    q and y may be row-strided (rows contiguous)."""
+    ldq = _rows(q, torch.int8, "q")
     _need(x_scale, torch.float32, "x_scale", 1)
     _need(w_packed, torch.uint8, "w_packed", 1)
     _need(w_scale, torch.float32, "w_scale", 1)
@@ -303,10 +330,16 @@ def linear(q: torch.Tensor, x_scale: torch.Tensor, w_packed: torch.Tensor, w_sca
     ydt = torch.bfloat16 if out == OUT_BF16 else torch.int32
     if y is None:
         y = torch.empty((M, N), dtype=ydt, device=q.device)
-    _need(y, ydt, "y", 2)
+    ldy = _rows(y, ydt, "y")
+    if tuple(y.shape) != (M, N):
+        raise ValueError("y shape mismatch")
     ws, ws_n = _workspace(linear_workspace_bytes(M, N, K), q.device, workspace)
-    _check(lib.w8a8_linear(_ptr(q), _ptr(x_scale), M, K, _ptr(w_packed), _ptr(w_scale), N,
-                           _ptr(bias), _ptr(y), out, _ptr(ws), ws_n, _stream()))
+    if ldq == K and ldy == N:
+        _check(lib.w8a8_linear(_ptr(q), _ptr(x_scale), M, K, _ptr(w_packed), _ptr(w_scale), N,
+                               _ptr(bias), _ptr(y), out, _ptr(ws), ws_n, _stream()))
+    else:
+        _check(lib.w8a8_linear_ld(_ptr(q), ldq, _ptr(x_scale), M, K, _ptr(w_packed), _ptr(w_scale), N,
+                                  _ptr(bias), _ptr(y), ldy, out, _ptr(ws), ws_n, _stream()))
     return y
 
 

@@ -81,17 +81,25 @@ const char* w8a8_last_error(void) { return g_last_error.c_str(); }
 
 int w8a8_abi_version(void) { return 1; }
 
-int w8a8_dynamic_quant(const uint16_t* x, int64_t M, int64_t K, int8_t* q, float* x_scale,
-                       void* stream) {
+int w8a8_dynamic_quant_ld(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int8_t* q, int64_t ldq,
+                          float* x_scale, void* stream) {
   if (M < 0 || K < 1 || M >= kMaxDim * 4 || K > W8A8_MAX_K)
     return fail(W8A8_ERR_SHAPE, "dynamic_quant: need M >= 0 and 1 <= K <= %d (M=%lld K=%lld)",
                 W8A8_MAX_K, (long long)M, (long long)K);
+  if (ldx < K || ldq < K)
+    return fail(W8A8_ERR_SHAPE, "dynamic_quant: need ldx >= K and ldq >= K (ldx=%lld ldq=%lld K=%lld)",
+                (long long)ldx, (long long)ldq, (long long)K);
   if (M == 0) return ok();
   if (!x || !q || !x_scale) return fail(W8A8_ERR_NULL, "dynamic_quant: null pointer");
   if (!aligned(x, 2) || !aligned(x_scale, 4))
     return fail(W8A8_ERR_ALIGN, "dynamic_quant: x must be 2-byte and x_scale 4-byte aligned");
-  return launched(w8a8::launch_dynamic_quant(x, M, K, q, x_scale, false, (hipStream_t)stream),
+  return launched(w8a8::launch_dynamic_quant(x, M, K, q, x_scale, false, (hipStream_t)stream, ldx, ldq),
                   "dynamic_quant");
+}
+
+int w8a8_dynamic_quant(const uint16_t* x, int64_t M, int64_t K, int8_t* q, float* x_scale,
+                       void* stream) {
+  return w8a8_dynamic_quant_ld(x, M, K, K, q, K, x_scale, stream);
 }
 
 int w8a8_dynamic_quant_packed(const uint16_t* x, int64_t M, int64_t K, void* q_packed,
@@ -184,6 +192,30 @@ int w8a8_linear(const int8_t* q, const float* x_scale, int64_t M, int64_t K, con
   return launched(w8a8::launch_dense_gemm(plan, q, x_scale, M, K, w_packed, w_scale, N, bias, y, out,
                                           packed, workspace, (hipStream_t)stream),
                   "linear");
+}
+
+int w8a8_linear_ld(const int8_t* q, int64_t ldq, const float* x_scale, int64_t M, int64_t K,
+                   const void* w_packed, const float* w_scale, int64_t N, const uint16_t* bias, void* y,
+                   int64_t ldy, int out, void* workspace, int64_t ws_bytes, void* stream) {
+  if (M < 0 || K < 1 || N < 1 || M >= kMaxDim || N >= kMaxDim || K > W8A8_MAX_K)
+    return fail(W8A8_ERR_SHAPE, "linear_ld: need M >= 0, N >= 1, 1 <= K <= %d", W8A8_MAX_K);
+  if (ldq < K || ldy < N)
+    return fail(W8A8_ERR_SHAPE, "linear_ld: need ldq >= K and ldy >= N (ldq=%lld ldy=%lld)", (long long)ldq,
+                (long long)ldy);
+  if (out != W8A8_OUT_BF16 && out != W8A8_OUT_I32)
+    return fail(W8A8_ERR_UNSUPPORTED, "linear_ld: row-major INT8 codes only; unknown output kind %d", out);
+  if (M == 0) return ok();
+  if (!q || !x_scale || !w_packed || !w_scale || !y) return fail(W8A8_ERR_NULL, "linear_ld: null pointer");
+  if (!aligned(w_packed, 16) || !aligned(x_scale, 4) || !aligned(w_scale, 4) || !aligned(y, 4) ||
+      (bias && !aligned(bias, 2)))
+    return fail(W8A8_ERR_ALIGN, "linear_ld: w_packed 16-byte, scales and y 4-byte alignment");
+  const w8a8::DensePlan plan = w8a8::plan_dense(M, N, K);
+  if (plan.ws_bytes > 0 && (!workspace || ws_bytes < plan.ws_bytes || !aligned(workspace, 16)))
+    return fail(W8A8_ERR_WORKSPACE, "linear_ld: needs %lld workspace bytes (16-byte aligned), got %lld",
+                (long long)plan.ws_bytes, (long long)ws_bytes);
+  return launched(w8a8::launch_dense_gemm(plan, q, x_scale, M, K, w_packed, w_scale, N, bias, y, out, false,
+                                          workspace, (hipStream_t)stream, nullptr, ldq, ldy),
+                  "linear_ld");
 }
 
 int64_t w8a8_grouped_workspace_bytes(int64_t R, int64_t E, int64_t N, int64_t K) {

@@ -27,7 +27,7 @@ namespace w8a8 {
 constexpr int kBlockBytes = 1024;  // 16 rows/cols x 64 k of int8
 
 struct GemmArgs {
-  const int8_t* a;          // [rows, K] row-major
+  const int8_t* a;          // [rows, K] row-major, row stride lda
   const float* a_scale;     // [rows]
   int64_t M;                // rows (dense) / R (grouped)
   int64_t K;
@@ -37,7 +37,7 @@ struct GemmArgs {
   const float* w_scale;     // [E, N]
   int64_t N;
   const uint16_t* bias;     // [N] or null
-  void* y;                  // [rows, N]
+  void* y;                  // [rows, N], row stride ldy
   int out;                  // OutKind
   int a_blk;                // A in 1 KB blocks [ceil(M/16)][KB] (dense kernels only)
   bool a_vec;               // K % 16 == 0 and a 16-byte aligned
@@ -47,6 +47,7 @@ struct GemmArgs {
   // with w_scale holding the dequant scale and a_scale / bias unused; null
   // for the dynamic scheme
   const int32_t* qbias;
+  int64_t lda, ldy;         // row strides of row-major A and of y (K and N unless given)
 };
 
 // fp32 value of one output before the BF16 rounding. Dynamic scheme:
@@ -78,7 +79,7 @@ __device__ __forceinline__ i32x4 load_a16(const GemmArgs& p, int64_t row, int64_
                                           int64_t kcol) {
   i32x4 v = {0, 0, 0, 0};
   if (row >= row_end || kcol >= p.K) return v;
-  const int8_t* src = p.a + row * p.K + kcol;
+  const int8_t* src = p.a + row * p.lda + kcol;
   if (p.a_vec) return *reinterpret_cast<const i32x4*>(src);
   uint32_t w[4] = {0, 0, 0, 0};
   const int64_t n = min((int64_t)16, p.K - kcol);
@@ -219,10 +220,10 @@ struct Tile {
           if (m >= row_end) continue;
           const int32_t v = acc[i][j][t];
           if (p.out == kOutI32) {
-            reinterpret_cast<int32_t*>(p.y)[m * p.N + n] = v;
+            reinterpret_cast<int32_t*>(p.y)[m * p.ldy + n] = v;
           } else {
             const float f = out_value(p, v, p.a_scale ? p.a_scale[m] : 0.0f, ws, b, qb);
-            reinterpret_cast<uint16_t*>(p.y)[m * p.N + n] = (uint16_t)f32_to_bf16(f);
+            reinterpret_cast<uint16_t*>(p.y)[m * p.ldy + n] = (uint16_t)f32_to_bf16(f);
           }
         }
       }
@@ -324,7 +325,7 @@ struct DmaTile {
         int64_t row = row0 + bi * 16 + (lane & 15);
         row = row < row_last ? row : row_last;
         s.base[i] = reinterpret_cast<const uint8_t*>(p.a);
-        s.off[i] = (uint32_t)(row * p.K + (lane >> 4) * 16);
+        s.off[i] = (uint32_t)(row * p.lda + (lane >> 4) * 16);
         s.step[i] = 64;
       } else {
         int nb = nb0 + (bi - kABlocks);
@@ -484,10 +485,10 @@ struct DmaTile {
           if (m >= row_end) continue;
           const int32_t val = acc[i][j][v];
           if (p.out == kOutI32) {
-            reinterpret_cast<int32_t*>(p.y)[m * p.N + n] = val;
+            reinterpret_cast<int32_t*>(p.y)[m * p.ldy + n] = val;
           } else {
             const float f = out_value(p, val, p.a_scale ? p.a_scale[m] : 0.0f, ws, b, qb);
-            reinterpret_cast<uint16_t*>(p.y)[m * p.N + n] = (uint16_t)f32_to_bf16(f);
+            reinterpret_cast<uint16_t*>(p.y)[m * p.ldy + n] = (uint16_t)f32_to_bf16(f);
           }
         }
       }
@@ -542,7 +543,7 @@ struct DmaTile {
     }
     __syncthreads();
     constexpr int kChunks = BN * 2 / 16;  // 16-byte pieces per staged row
-    const bool vec = (p.N % 8 == 0) && (((uintptr_t)p.y & 15) == 0);
+    const bool vec = (p.N % 8 == 0) && (p.ldy % 8 == 0) && (((uintptr_t)p.y & 15) == 0);
     for (int c = opaque_tid(); c < BM * kChunks; c += kThreads) {
       const int r = c / kChunks, cc = c % kChunks;
       const int64_t m = row0 + r;
@@ -550,7 +551,7 @@ struct DmaTile {
       const int64_t n = n0 + cc * 8;
       if (n >= p.N) continue;
       const uint8_t* src = smem + r * kPitch + cc * 16;
-      uint16_t* dst = reinterpret_cast<uint16_t*>(p.y) + m * p.N + n;
+      uint16_t* dst = reinterpret_cast<uint16_t*>(p.y) + m * p.ldy + n;
       if (vec && n + 8 <= p.N) {
         *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
       } else {
@@ -842,7 +843,7 @@ struct SmallItem {
       // output rows that are never stored
       int64_t r = mb * 16 + (lane & 15);
       r = r < rows ? r : rows - 1;
-      s.aoff[mb] = (uint32_t)((row0 + r) * p.K + (lane >> 4) * 16);
+      s.aoff[mb] = (uint32_t)((row0 + r) * p.lda + (lane >> 4) * 16);
     }
 #pragma unroll
     for (int j = 0; j < NBW; ++j) {
@@ -901,12 +902,12 @@ struct SmallItem {
           if (m >= rows) continue;
           const int64_t row = row0 + m;
           if (p.out == kOutI32) {
-            reinterpret_cast<int32_t*>(p.y)[row * p.N + n] = acc[mb][j][t];
+            reinterpret_cast<int32_t*>(p.y)[row * p.ldy + n] = acc[mb][j][t];
           } else {
             float f = (float)acc[mb][j][t];
             f = f * p.a_scale[row];
             f = f * ws;
-            reinterpret_cast<uint16_t*>(p.y)[row * p.N + n] = (uint16_t)f32_to_bf16(f);
+            reinterpret_cast<uint16_t*>(p.y)[row * p.ldy + n] = (uint16_t)f32_to_bf16(f);
           }
         }
       }
@@ -1026,7 +1027,7 @@ __global__ __launch_bounds__(WAVES* kWave) void decode_gemm_kernel(GemmArgs p) {
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
     const int64_t row = mb * 16 + (lane & 15);
-    arow[mb] = p.a + (row < p.M ? row : mlast) * p.K + (lane >> 4) * 16;
+    arow[mb] = p.a + (row < p.M ? row : mlast) * p.lda + (lane >> 4) * 16;
   }
   const int64_t col_last = (int64_t)(p.KB - 1) * 64 + (lane >> 4) * 16;
   const int64_t pull = col_last > p.K - 16 ? col_last - (p.K - 16) : 0;
@@ -1122,10 +1123,10 @@ __global__ __launch_bounds__(WAVES* kWave) void decode_gemm_kernel(GemmArgs p) {
     const int64_t m = mbk * 16 + (lane >> 4) * 4 + t;
     if (m >= p.M) continue;
     if (p.out == kOutI32) {
-      reinterpret_cast<int32_t*>(p.y)[m * p.N + n] = sum[t];
+      reinterpret_cast<int32_t*>(p.y)[m * p.ldy + n] = sum[t];
     } else {
       const float f = out_value(p, sum[t], p.a_scale ? p.a_scale[m] : 0.0f, ws, bsv, qb);
-      reinterpret_cast<uint16_t*>(p.y)[m * p.N + n] = (uint16_t)f32_to_bf16(f);
+      reinterpret_cast<uint16_t*>(p.y)[m * p.ldy + n] = (uint16_t)f32_to_bf16(f);
     }
   }
 }
@@ -1250,13 +1251,13 @@ __global__ __launch_bounds__(WAVES * kWave) void decode_fused_kernel(GemmArgs p)
     const int m = (lane >> 4) * 4 + t;
     if (m >= M) continue;
     if (p.out == kOutI32) {
-      reinterpret_cast<int32_t*>(p.y)[m * p.N + n] = sum[t];
+      reinterpret_cast<int32_t*>(p.y)[m * p.ldy + n] = sum[t];
     } else {
       float f = (float)sum[t];
       f = f * srow[m];
       f = f * ws;
       if (p.bias) f = f + bsv;
-      reinterpret_cast<uint16_t*>(p.y)[m * p.N + n] = (uint16_t)f32_to_bf16(f);
+      reinterpret_cast<uint16_t*>(p.y)[m * p.ldy + n] = (uint16_t)f32_to_bf16(f);
     }
   }
 }
@@ -1333,6 +1334,8 @@ static GemmArgs make_args(const int8_t* a, const float* a_scale, int64_t M, int6
   p.y = y;
   p.out = out;
   p.a_vec = (K % 16 == 0) && (((uintptr_t)a & 15) == 0);
+  p.lda = K;
+  p.ldy = N;
   return p;
 }
 
@@ -1340,17 +1343,21 @@ static GemmArgs make_args(const int8_t* a, const float* a_scale, int64_t M, int6
 // 32-bit per-lane byte offsets.
 static bool offsets32_ok(const GemmArgs& p) {
   const int64_t lim = (int64_t)1 << 32;
-  return p.M * p.K + 64 < lim && (int64_t)p.NB * p.KB * kBlockBytes < lim;
+  return p.M * p.lda + 64 < lim && (int64_t)p.NB * p.KB * kBlockBytes < lim;
 }
 
 hipError_t launch_dense_gemm(const DensePlan& plan, const int8_t* q, const float* x_scale, int64_t M,
                              int64_t K, const void* w_packed, const float* w_scale, int64_t N,
                              const uint16_t* bias, void* y, int out, bool a_packed, void* ws,
-                             hipStream_t stream, const int32_t* qbias) {
+                             hipStream_t stream, const int32_t* qbias, int64_t lda, int64_t ldy) {
   (void)ws;
   if (M == 0 || N == 0) return hipSuccess;
   GemmArgs p = make_args(q, x_scale, M, K, w_packed, w_scale, N, bias, y, out);
   p.qbias = qbias;
+  if (lda) p.lda = lda;
+  if (ldy) p.ldy = ldy;
+  // 16-byte row loads of A need every row aligned
+  p.a_vec = p.a_vec && (p.lda % 16 == 0);
   int variant = plan.variant;
   if (a_packed) {
     // packed A (1 KB blocks): the decode kernels' block variants, or the tiles

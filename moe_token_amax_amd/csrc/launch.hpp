@@ -9,8 +9,10 @@ namespace w8a8 {
 
 // codes row-major [M, K], or (packed) in the weight's 1 KB block layout
 // [ceil(M/16)][ceil(K/64)]; packed needs K % 8 == 0 and 16-byte aligned rows
+// ldx / ldq: row strides of x and of the row-major codes (0: K; packed codes
+// need ldx == K)
 hipError_t launch_dynamic_quant(const uint16_t* x, int64_t M, int64_t K, int8_t* q, float* scale,
-                                bool packed, hipStream_t stream);
+                                bool packed, hipStream_t stream, int64_t ldx = 0, int64_t ldq = 0);
 hipError_t launch_swiglu_quant(const uint16_t* h, int64_t R, int64_t I, int8_t* q, float* scale,
                                hipStream_t stream);
 hipError_t launch_prepack(const int8_t* w, int64_t E, int64_t N, int64_t K, void* packed,
@@ -32,10 +34,12 @@ bool decode_fused_ok(int64_t M, int64_t K, const void* x);
 hipError_t launch_decode_fused(const uint16_t* x, int64_t M, int64_t K, const void* w_packed,
                                const float* w_scale, int64_t N, const uint16_t* bias, void* y, int out,
                                hipStream_t stream);
+// lda / ldy: row strides of row-major codes and of y (0: K and N)
 hipError_t launch_dense_gemm(const DensePlan& plan, const int8_t* q, const float* x_scale, int64_t M,
                              int64_t K, const void* w_packed, const float* w_scale, int64_t N,
                              const uint16_t* bias, void* y, int out, bool a_packed, void* ws,
-                             hipStream_t stream, const int32_t* qbias = nullptr);
+                             hipStream_t stream, const int32_t* qbias = nullptr, int64_t lda = 0,
+                             int64_t ldy = 0);
 // static W8A8: the GEMM above with qbias set (w_scale = the dequant scale,
 // x_scale = bias = null); the static activation quant and the load-time
 // dequant scale / integer bias

@@ -28,13 +28,14 @@ __device__ __forceinline__ uint32_t abs_bf16_pair_max(uint32_t w) {
   return max(w & 0x7FFFu, (w >> 16) & 0x7FFFu);
 }
 
-// Store of 8 codes (row, k = 8 c .. 8 c + 7): row-major q [M, K] when kb == 0,
-// else the packed block layout of the weights with kb k-blocks per 16 rows:
-// block (row / 16, k / 64), byte (row % 16 + 16 (k % 64 / 16)) * 16 + k % 16.
-__device__ __forceinline__ void store_codes8(int8_t* q, int64_t row, int c, int64_t K, int64_t kb,
+// Store of 8 codes (row, k = 8 c .. 8 c + 7): row-major q (row stride ldq)
+// when kb == 0, else the packed block layout of the weights with kb k-blocks
+// per 16 rows: block (row / 16, k / 64), byte (row % 16 + 16 (k % 64 / 16)) *
+// 16 + k % 16.
+__device__ __forceinline__ void store_codes8(int8_t* q, int64_t row, int c, int64_t ldq, int64_t kb,
                                              uint2 o) {
   if (kb == 0) {
-    reinterpret_cast<uint2*>(q + row * K)[c] = o;
+    reinterpret_cast<uint2*>(q + row * ldq)[c] = o;
   } else {
     const int64_t k = (int64_t)c * 8;
     const int64_t at = ((row >> 4) * kb + (k >> 6)) * 1024 + ((row & 15) + 16 * ((k & 63) >> 4)) * 16 +
@@ -46,12 +47,13 @@ __device__ __forceinline__ void store_codes8(int8_t* q, int64_t row, int c, int6
 template <int CPL>
 __global__ __launch_bounds__(256) void quant_rows_vec(const uint16_t* __restrict__ x, int64_t M,
                                                       int64_t K, int8_t* __restrict__ q,
-                                                      float* __restrict__ scale, int64_t kb) {
+                                                      float* __restrict__ scale, int64_t kb, int64_t ldx,
+                                                      int64_t ldq) {
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
   if (row >= M) return;  // whole wave leaves together
   const int nchunk = (int)(K >> 3);
-  const uint4* xr = reinterpret_cast<const uint4*>(x + row * K);
+  const uint4* xr = reinterpret_cast<const uint4*>(x + row * ldx);
   uint4 v[CPL];
   uint32_t amax = 0;
 #pragma unroll
@@ -71,7 +73,7 @@ __global__ __launch_bounds__(256) void quant_rows_vec(const uint16_t* __restrict
     const int c = lane + i * kWave;
     if (c < nchunk) {
       const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
-      store_codes8(q, row, c, K, kb, quant8_bf16(w, s));
+      store_codes8(q, row, c, ldq, kb, quant8_bf16(w, s));
     }
   }
 }
@@ -85,12 +87,13 @@ template <int CPL>
 __global__ __launch_bounds__(kRowBlock) void quant_rows_block(const uint16_t* __restrict__ x,
                                                               int64_t M, int64_t K,
                                                               int8_t* __restrict__ q,
-                                                              float* __restrict__ scale, int64_t kb) {
+                                                              float* __restrict__ scale, int64_t kb,
+                                                              int64_t ldx, int64_t ldq) {
   __shared__ uint32_t wave_max[kRowBlock / kWave];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t row = blockIdx.x;
   const int nchunk = (int)(K >> 3);
-  const uint4* xr = reinterpret_cast<const uint4*>(x + row * K);
+  const uint4* xr = reinterpret_cast<const uint4*>(x + row * ldx);
   uint4 v[CPL];
   uint32_t amax = 0;
 #pragma unroll
@@ -115,7 +118,7 @@ __global__ __launch_bounds__(kRowBlock) void quant_rows_block(const uint16_t* __
     const int c = tid + i * kRowBlock;
     if (c < nchunk) {
       const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
-      store_codes8(q, row, c, K, kb, quant8_bf16(w, s));
+      store_codes8(q, row, c, ldq, kb, quant8_bf16(w, s));
     }
   }
 }
@@ -226,17 +229,17 @@ __global__ __launch_bounds__(256) void quant_rows_packed_wave(const uint16_t* __
 
 __global__ __launch_bounds__(256) void quant_rows_generic(const uint16_t* __restrict__ x, int64_t M,
                                                           int64_t K, int8_t* __restrict__ q,
-                                                          float* __restrict__ scale) {
+                                                          float* __restrict__ scale, int64_t ldx, int64_t ldq) {
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
   if (row >= M) return;
-  const uint16_t* xr = x + row * K;
+  const uint16_t* xr = x + row * ldx;
   uint32_t amax = 0;
   for (int64_t k = lane; k < K; k += kWave) amax = max(amax, (uint32_t)xr[k] & 0x7FFFu);
   amax = wave_max_u32(amax);
   const float s = bf16_to_f32(amax) / 127.0f;
   if (lane == 0) scale[row] = s;
-  int8_t* qr = q + row * K;
+  int8_t* qr = q + row * ldq;
   for (int64_t k = lane; k < K; k += kWave) qr[k] = (int8_t)quant_code(bf16_to_f32(xr[k]), s);
 }
 
@@ -315,12 +318,18 @@ __global__ __launch_bounds__(256) void swiglu_quant_generic(const uint16_t* __re
 static inline bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
 hipError_t launch_dynamic_quant(const uint16_t* x, int64_t M, int64_t K, int8_t* q, float* scale,
-                                bool packed, hipStream_t stream) {
+                                bool packed, hipStream_t stream, int64_t ldx, int64_t ldq) {
   if (M == 0) return hipSuccess;
+  if (ldx == 0) ldx = K;
+  if (ldq == 0) ldq = K;
   const dim3 grid((unsigned)((M + kRowsPerBlock - 1) / kRowsPerBlock)), block(256);
-  const bool vec = (K % 8 == 0) && aligned(x, 16) && aligned(q, 8);
+  // 16-byte loads and 8-byte code stores need aligned rows
+  const bool vec = (K % 8 == 0) && (ldx % 8 == 0) && (packed || ldq % 8 == 0) && aligned(x, 16) &&
+                   aligned(q, 8);
   // packed codes need the vector kernels (the caller checks K % 16 == 0 and alignment)
   if (packed && !vec) return hipErrorInvalidValue;
+  // the packed kernels read x with row stride K
+  if (packed && ldx != K) return hipErrorInvalidValue;
   const int64_t kb = packed ? (K + 63) / 64 : 0;
   if (packed && M > 512) {
     // many rows: one pass over x, a wavefront per row, while a lane's pieces
@@ -344,22 +353,22 @@ hipError_t launch_dynamic_quant(const uint16_t* x, int64_t M, int64_t K, int8_t*
     // few rows: a whole workgroup per row
     if (chunks <= kRowBlock)
       hipLaunchKernelGGL(quant_rows_block<1>, dim3((unsigned)M), dim3(kRowBlock), 0, stream, x, M,
-                         K, q, scale, kb);
+                         K, q, scale, kb, ldx, ldq);
     else
       hipLaunchKernelGGL(quant_rows_block<2>, dim3((unsigned)M), dim3(kRowBlock), 0, stream, x, M,
-                         K, q, scale, kb);
+                         K, q, scale, kb, ldx, ldq);
   } else if (vec && chunks <= 64 * 1)
-    hipLaunchKernelGGL(quant_rows_vec<1>, grid, block, 0, stream, x, M, K, q, scale, kb);
+    hipLaunchKernelGGL(quant_rows_vec<1>, grid, block, 0, stream, x, M, K, q, scale, kb, ldx, ldq);
   else if (vec && chunks <= 64 * 2)
-    hipLaunchKernelGGL(quant_rows_vec<2>, grid, block, 0, stream, x, M, K, q, scale, kb);
+    hipLaunchKernelGGL(quant_rows_vec<2>, grid, block, 0, stream, x, M, K, q, scale, kb, ldx, ldq);
   else if (vec && chunks <= 64 * 4)
-    hipLaunchKernelGGL(quant_rows_vec<4>, grid, block, 0, stream, x, M, K, q, scale, kb);
+    hipLaunchKernelGGL(quant_rows_vec<4>, grid, block, 0, stream, x, M, K, q, scale, kb, ldx, ldq);
   else if (vec && chunks <= 64 * 8)
-    hipLaunchKernelGGL(quant_rows_vec<8>, grid, block, 0, stream, x, M, K, q, scale, kb);
+    hipLaunchKernelGGL(quant_rows_vec<8>, grid, block, 0, stream, x, M, K, q, scale, kb, ldx, ldq);
   else if (vec && chunks <= 64 * 16)
-    hipLaunchKernelGGL(quant_rows_vec<16>, grid, block, 0, stream, x, M, K, q, scale, kb);
+    hipLaunchKernelGGL(quant_rows_vec<16>, grid, block, 0, stream, x, M, K, q, scale, kb, ldx, ldq);
   else
-    hipLaunchKernelGGL(quant_rows_generic, grid, block, 0, stream, x, M, K, q, scale);
+    hipLaunchKernelGGL(quant_rows_generic, grid, block, 0, stream, x, M, K, q, scale, ldx, ldq);
   return hipGetLastError();
 }
 

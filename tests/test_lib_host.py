@@ -72,6 +72,25 @@ def test_validation_before_launch(w):
     assert L.w8a8_linear(ctypes.c_void_p(8), p, 4, 64, p, p, 8, None, p, 4, None, 0, None) == 3
 
 
+def test_strided_validation_before_launch(w):
+    L = w.lib
+    p = ctypes.c_void_p(16)  # never dereferenced: validation fails first
+    # row strides below the row width
+    assert L.w8a8_dynamic_quant_ld(p, 4, 64, 63, p, 64, p, None) == 2
+    assert L.w8a8_dynamic_quant_ld(p, 4, 64, 64, p, 10, p, None) == 2
+    assert L.w8a8_dynamic_quant_ld(None, 4, 64, 80, None, 72, None, None) == 1
+    assert L.w8a8_dynamic_quant_ld(None, 0, 64, 80, None, 72, None, None) == 0  # M == 0
+    assert L.w8a8_dynamic_quant_ld(ctypes.c_void_p(17), 4, 64, 80, p, 72, p, None) == 3
+    # linear_ld: ldq < K, ldy < N, unknown output kinds (packed codes are not strided)
+    assert L.w8a8_linear_ld(p, 63, p, 4, 64, p, p, 8, None, p, 8, 0, None, 0, None) == 2
+    assert L.w8a8_linear_ld(p, 64, p, 4, 64, p, p, 8, None, p, 7, 0, None, 0, None) == 2
+    assert L.w8a8_linear_ld(p, 64, p, 4, 64, p, p, 8, None, p, 8, 7, None, 0, None) == 4
+    assert L.w8a8_linear_ld(p, 64, p, 4, 64, p, p, 8, None, p, 8, 4, None, 0, None) == 4
+    assert L.w8a8_linear_ld(p, 64, None, 4, 64, p, p, 8, None, p, 8, 0, None, 0, None) == 1
+    assert L.w8a8_linear_ld(p, 64, p, 4, 64, ctypes.c_void_p(24), p, 8, None, p, 8, 0, None, 0, None) == 3
+    assert L.w8a8_linear_ld(None, 64, None, 0, 64, None, None, 8, None, None, 8, 0, None, 0, None) == 0
+
+
 def test_mx_validation_before_launch(w):
     L = w.lib
     p = ctypes.c_void_p(256)  # never dereferenced: validation fails first
