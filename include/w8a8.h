@@ -260,7 +260,9 @@ int w8a8_moe_grouped(const void* x_rows, const float* x_scale,
  *   expert-major row; entries past sum(group_list) are 0) and pair_row int32
  *   [T, top_k] (the row of pair (t, j), -1 for an id outside [0, E), which is
  *   dropped). Rows of one expert keep the order of the pair index
- *   t * top_k + j. 1 <= E <= 1024, T * top_k < 2^31. One workgroup does it.
+ *   t * top_k + j. 1 <= E <= 1024, T * top_k < 2^31. Work grows linearly
+ *   with T * top_k; no workspace (past 32 * 1024 pairs pair_row holds
+ *   per-chunk counts between the call's launches).
  * w8a8_moe_gather: q int8 [T, H] and scale float [T] of the tokens (from
  *   w8a8_dynamic_quant) -> q_rows int8 [R, H], s_rows float [R] with row p =
  *   token row_token[p]; a token outside [0, T) gives a zero row, scale 0.

@@ -33,15 +33,59 @@ __device__ __forceinline__ uint64_t match_lanes(int key) {
   return same;
 }
 
-// One workgroup per chunk of 1024 pairs (E <= 1024), one launch. Every
-// workgroup counts all pairs itself in LDS (per-expert totals, and the counts
-// of the pairs before its chunk), scans the totals into expert offsets, and
-// places the pairs of its chunk: a pair's row is its expert's offset, plus
-// that expert's pairs in earlier chunks, in earlier wavefronts of this chunk
-// and in earlier lanes of its wavefront. Lanes with the same expert are found
-// with one ballot per bit of the id, so the order is the pair order. Row
-// slots past the number of routed pairs get token 0 (a valid index for a
-// gather over all T * top_k rows).
+// Exclusive scan over the workgroup of one value per thread: off[t] for
+// threads t < E. Every thread of the workgroup must take part.
+__device__ __forceinline__ void route_scan_block(int c, int E, int* off, int* wsum, int tid, int lane,
+                                                 int wave) {
+  int incl = c;
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int o = __shfl_up(incl, d, kWave);
+    if (lane >= d) incl += o;
+  }
+  if (lane == kWave - 1) wsum[wave] = incl;
+  __syncthreads();
+  for (int w = 0; w < wave; ++w) incl += wsum[w];
+  if (tid < E) off[tid] = incl - c;
+}
+
+// Places the pairs of the chunk that starts at pair c0: a pair's row is its
+// expert's offset off[e], plus base[e] (that expert's pairs in earlier
+// chunks), plus its pairs in earlier wavefronts of this chunk and in earlier
+// lanes of its wavefront. Lanes with the same expert are found with one
+// ballot per bit of the id, so the order is the pair order. wcnt must be
+// zero; off and base are read after this function's barrier.
+__device__ __forceinline__ void route_place_chunk(const int32_t* __restrict__ ids, int64_t P, int k, int E,
+                                                  int64_t c0, const int* off, const int* base,
+                                                  unsigned char (*wcnt)[kMaxExpertsDev],
+                                                  int32_t* __restrict__ row_token,
+                                                  int32_t* __restrict__ pair_row, int tid, int lane,
+                                                  int wave) {
+  const int64_t i = c0 + tid;
+  const int e = i < P ? ids[i] : -1;
+  const bool valid = e >= 0 && e < E;
+  const uint64_t same = match_lanes(valid ? e : kMaxExpertsDev);
+  const int before = __popcll(same & ((1ull << lane) - 1ull));
+  if (valid && before == 0) wcnt[wave][e] = (unsigned char)__popcll(same);
+  __syncthreads();
+  if (valid) {
+    int pos = off[e] + base[e] + before;
+    for (int w = 0; w < wave; ++w) pos += wcnt[w][e];
+    row_token[pos] = (int32_t)(i / k);
+    pair_row[i] = pos;
+  } else if (i < P) {
+    pair_row[i] = -1;
+  }
+}
+
+// Few chunks (at most kRouteDirectChunks of 1024 pairs, E <= 1024): one
+// launch, one workgroup per chunk, and every workgroup counts all pairs itself
+// in LDS (per-expert totals, and the counts of the pairs before its chunk),
+// scans the totals into expert offsets and places its chunk. Row slots past
+// the number of routed pairs get token 0 (a valid index for a gather over all
+// T * top_k rows).
+constexpr int kRouteDirectChunks = 32;
+
 __global__ __launch_bounds__(kRouteThreads) void route_kernel(const int32_t* __restrict__ ids,
                                                               int64_t P, int k, int E,
                                                               int64_t* __restrict__ group_list,
@@ -89,37 +133,112 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(const int32_t* __r
   }
   for (int64_t i = 4 * P4 + tid; i < P; i += kRouteThreads) count(ids[i], i);
   __syncthreads();
-  // exclusive scan of tot[0 .. E) (one value per thread)
   const int c = tid < E ? tot[tid] : 0;
-  int incl = c;
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    const int o = __shfl_up(incl, d, kWave);
-    if (lane >= d) incl += o;
-  }
-  if (lane == kWave - 1) wsum[wave] = incl;
+  route_scan_block(c, E, off, wsum, tid, lane, wave);
+  if (blockIdx.x == 0 && tid < E) group_list[tid] = c;
+  route_place_chunk(ids, P, k, E, c0, off, pre, wcnt, row_token, pair_row, tid, lane, wave);
+  const int routed = off[E - 1] + tot[E - 1];
+  for (int64_t p = routed + c0 + tid; p < P; p += (int64_t)gridDim.x * kRouteThreads)
+    row_token[p] = 0;
+}
+
+// Many chunks: three launches whose work grows linearly with the pairs, and
+// no workspace. The per-chunk expert counts of the C - 1 full chunks live in
+// pair_row, chunk c's E counts in pair_row[1024 c .. 1024 c + E) (its own
+// pairs' slots, E <= 1024), until the place step of that chunk overwrites
+// them with the pairs' rows.
+//   count: chunk c < C - 1 counts its pairs per expert into its slots.
+//   scan:  per expert, the counts are replaced by their exclusive prefix over
+//          the chunks, and group_list gets the expert's total (the last,
+//          possibly partial, chunk counted directly).
+//   place: chunk c reads its prefixes (the last chunk: total minus its own
+//          counts), scans group_list into expert offsets and places its pairs.
+__global__ __launch_bounds__(kRouteThreads) void route_count_kernel(const int32_t* __restrict__ ids, int E,
+                                                                    int32_t* __restrict__ table) {
+  __shared__ int cnt[kMaxExpertsDev];
+  const int tid = threadIdx.x;
+  const int64_t c0 = (int64_t)blockIdx.x * kRouteThreads;  // a full chunk: every id is in range
+  if (tid < E) cnt[tid] = 0;
   __syncthreads();
-  for (int w = 0; w < wave; ++w) incl += wsum[w];
+  const int e = ids[c0 + tid];
+  if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+  __syncthreads();
+  if (tid < E) table[c0 + tid] = cnt[tid];
+}
+
+// kWave experts per workgroup: lane = expert, wavefront = a contiguous slice
+// of the full chunks.
+__global__ __launch_bounds__(kRouteThreads) void route_scan_kernel(const int32_t* __restrict__ ids, int64_t P,
+                                                                   int E, int nfull,
+                                                                   int64_t* __restrict__ group_list,
+                                                                   int32_t* __restrict__ table) {
+  __shared__ int ssum[kRouteWaves][kWave];
+  __shared__ int last[kWave];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int e0 = blockIdx.x * kWave, e = e0 + lane;
+  if (tid < kWave) last[tid] = 0;
+  const int per = (nfull + kRouteWaves - 1) / kRouteWaves;
+  const int cb = min(wave * per, nfull), ce = min(cb + per, nfull);
+  int s = 0;
+  if (e < E) {
+#pragma unroll 8
+    for (int c = cb; c < ce; ++c) s += table[(int64_t)c * kRouteThreads + e];
+  }
+  ssum[wave][lane] = s;
+  __syncthreads();
+  // the last chunk's pairs of this workgroup's experts
+  const int64_t i = (int64_t)nfull * kRouteThreads + tid;
+  if (i < P) {
+    const int id = ids[i];
+    if (id >= e0 && id < e0 + kWave && id < E) atomicAdd(&last[id - e0], 1);
+  }
+  int run = 0;
+  for (int w = 0; w < wave; ++w) run += ssum[w][lane];
+  if (e < E) {
+#pragma unroll 8
+    for (int c = cb; c < ce; ++c) {
+      const int64_t o = (int64_t)c * kRouteThreads + e;
+      const int v = table[o];
+      table[o] = run;
+      run += v;
+    }
+  }
+  __syncthreads();
+  // the last wavefront's running sum is the total over all full chunks
+  if (wave == kRouteWaves - 1 && e < E) group_list[e] = (int64_t)run + last[lane];
+}
+
+__global__ __launch_bounds__(kRouteThreads) void route_place_kernel(const int32_t* __restrict__ ids,
+                                                                    int64_t P, int k, int E, int nfull,
+                                                                    const int64_t* __restrict__ group_list,
+                                                                    int32_t* __restrict__ row_token,
+                                                                    int32_t* __restrict__ pair_row) {
+  __shared__ int tot[kMaxExpertsDev];
+  __shared__ int base[kMaxExpertsDev];
+  __shared__ int off[kMaxExpertsDev];
+  __shared__ __align__(16) unsigned char wcnt[kRouteWaves][kMaxExpertsDev];
+  __shared__ int wsum[kRouteWaves];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t c0 = (int64_t)blockIdx.x * kRouteThreads;
+  const bool is_last = (int)blockIdx.x == nfull;
+  reinterpret_cast<uint4*>(&wcnt[0][0])[tid] = uint4{0u, 0u, 0u, 0u};
+  const int g = tid < E ? (int)group_list[tid] : 0;
   if (tid < E) {
-    off[tid] = incl - c;
-    if (blockIdx.x == 0) group_list[tid] = c;
+    tot[tid] = g;
+    // a full chunk's prefixes, read before the barrier below: the place
+    // step then overwrites these slots
+    base[tid] = is_last ? 0 : pair_row[c0 + tid];
   }
-  // this workgroup's chunk
-  const int64_t i = c0 + tid;
-  int e = i < P ? ids[i] : -1;
-  const bool valid = e >= 0 && e < E;
-  const uint64_t same = match_lanes(valid ? e : kMaxExpertsDev);
-  const int before = __popcll(same & ((1ull << lane) - 1ull));
-  if (valid && before == 0) wcnt[wave][e] = (unsigned char)__popcll(same);
   __syncthreads();
-  if (valid) {
-    int pos = off[e] + pre[e] + before;
-    for (int w = 0; w < wave; ++w) pos += wcnt[w][e];
-    row_token[pos] = (int32_t)(i / k);
-    pair_row[i] = pos;
-  } else if (i < P) {
-    pair_row[i] = -1;
+  if (is_last) {
+    const int64_t i = c0 + tid;
+    const int e = i < P ? ids[i] : -1;
+    if (e >= 0 && e < E) atomicAdd(&base[e], 1);
+    __syncthreads();
+    if (tid < E) base[tid] = g - base[tid];
   }
+  route_scan_block(g, E, off, wsum, tid, lane, wave);
+  route_place_chunk(ids, P, k, E, c0, off, base, wcnt, row_token, pair_row, tid, lane, wave);
   const int routed = off[E - 1] + tot[E - 1];
   for (int64_t p = routed + c0 + tid; p < P; p += (int64_t)gridDim.x * kRouteThreads)
     row_token[p] = 0;
@@ -236,9 +355,19 @@ hipError_t launch_route(const int32_t* ids, int64_t T, int64_t k, int64_t E, int
                         int32_t* row_token, int32_t* pair_row, hipStream_t stream) {
   // T == 0 still runs one workgroup: it writes the zero counts
   const int64_t P = T * k;
-  const int64_t grid = std::max<int64_t>(1, (P + kRouteThreads - 1) / kRouteThreads);
-  hipLaunchKernelGGL(route_kernel, dim3((unsigned)grid), dim3(kRouteThreads), 0, stream, ids, P,
-                     (int)k, (int)E, group_list, row_token, pair_row);
+  const int64_t chunks = std::max<int64_t>(1, (P + kRouteThreads - 1) / kRouteThreads);
+  if (chunks <= kRouteDirectChunks) {
+    hipLaunchKernelGGL(route_kernel, dim3((unsigned)chunks), dim3(kRouteThreads), 0, stream, ids, P,
+                       (int)k, (int)E, group_list, row_token, pair_row);
+    return hipGetLastError();
+  }
+  const int nfull = (int)(chunks - 1);
+  hipLaunchKernelGGL(route_count_kernel, dim3((unsigned)nfull), dim3(kRouteThreads), 0, stream, ids, (int)E,
+                     pair_row);
+  hipLaunchKernelGGL(route_scan_kernel, dim3((unsigned)((E + kWave - 1) / kWave)), dim3(kRouteThreads), 0,
+                     stream, ids, P, (int)E, nfull, group_list, pair_row);
+  hipLaunchKernelGGL(route_place_kernel, dim3((unsigned)chunks), dim3(kRouteThreads), 0, stream, ids, P,
+                     (int)k, (int)E, nfull, group_list, row_token, pair_row);
   return hipGetLastError();
 }
 

@@ -61,10 +61,16 @@ def _route_full(ids, E):
 
 # (T, top_k, E, ids): empty, single pair, the MoE workload's routing, many
 # chunks of 1024 pairs with the largest expert count, one expert for every
-# pair (4 chunks of 64 equal ids per wavefront), dropped ids
+# pair (4 chunks of 64 equal ids per wavefront), dropped ids. Up to 32 chunks
+# of 1024 pairs take the one-launch kernel; past that the count / scan /
+# place launches: 33 chunks with an 8-pair last chunk, 64 full chunks, the
+# 40-chunk case with E = 1024, 512 chunks (T = 65536), one expert for 40000
+# pairs, a single expert.
 ROUTE_CASES = [(0, 8, 4, "uniform"), (1, 1, 1, "uniform"), (97, 8, 33, "invalid"),
                (2048, 8, 256, "synth"), (5000, 8, 1024, "uniform"), (3000, 1, 4, "one"),
-               (1500, 6, 7, "invalid"), (333, 3, 1000, "synth")]
+               (1500, 6, 7, "invalid"), (333, 3, 1000, "synth"), (4096, 8, 64, "uniform"),
+               (4097, 8, 7, "invalid"), (8192, 8, 256, "synth"), (65536, 8, 256, "synth"),
+               (40000, 1, 9, "one"), (33 * 1024 + 5, 1, 1, "uniform"), (6000, 7, 1000, "invalid")]
 
 
 @pytest.mark.parametrize("T,k,E,kind", ROUTE_CASES)
