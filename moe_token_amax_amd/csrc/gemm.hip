@@ -1004,7 +1004,8 @@ __global__ __launch_bounds__(WM* WN* kWave) void grouped_mixed_kernel(GemmArgs p
 // UNR blocks per wave in flight at once; the MB m-blocks of A (<= 64 rows,
 // shared by all workgroups and served from L2) are loaded the same way. The
 // per-wave INT32 partial sums are added in LDS and the epilogue runs on the
-// full sums: one kernel, no workspace, no second pass. Grid = ceil(N / 16).
+// full sums: one kernel, no workspace, no second pass. Grid = ceil(N / 16 /
+// NBW) x ceil(M / (16 MB)): blockIdx.y selects the workgroup's 16 MB rows.
 // ---------------------------------------------------------------------------
 template <int MB, int NBW, int WAVES, int UNR, bool AVEC, bool ABLK = false, bool PF = false>
 __global__ __launch_bounds__(WAVES* kWave) void decode_gemm_kernel(GemmArgs p) {
@@ -1012,6 +1013,7 @@ __global__ __launch_bounds__(WAVES* kWave) void decode_gemm_kernel(GemmArgs p) {
   __shared__ i32x4 red[WAVES][MB * NBW][kWave];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nb0 = blockIdx.x * NBW;
+  const int64_t mrow0 = (int64_t)blockIdx.y * MB * 16;  // this workgroup's first row
   const uint8_t* wcol[NBW];
 #pragma unroll
   for (int j = 0; j < NBW; ++j) {
@@ -1026,7 +1028,7 @@ __global__ __launch_bounds__(WAVES* kWave) void decode_gemm_kernel(GemmArgs p) {
   const int8_t* arow[MB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
-    const int64_t row = mb * 16 + (lane & 15);
+    const int64_t row = mrow0 + mb * 16 + (lane & 15);
     arow[mb] = p.a + (row < p.M ? row : mlast) * p.lda + (lane >> 4) * 16;
   }
   const int64_t col_last = (int64_t)(p.KB - 1) * 64 + (lane >> 4) * 16;
@@ -1061,12 +1063,13 @@ __global__ __launch_bounds__(WAVES* kWave) void decode_gemm_kernel(GemmArgs p) {
         b[u][j] = PF ? bn[u][j] : *reinterpret_cast<const i32x4*>(wcol[j] + (int64_t)kbc * kBlockBytes);
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
-        const int64_t row = mb * 16 + (lane & 15);
+        const int64_t row = mrow0 + mb * 16 + (lane & 15);
         const int64_t kcol = (int64_t)kbc * 64 + (lane >> 4) * 16;
         if (ABLK) {
           // packed A: one contiguous 1 KB block per (m-block, k-block); m-blocks
           // past the last one are read clamped (their rows are never stored)
-          const int64_t mbc = mb <= mlast / 16 ? mb : mlast / 16;
+          const int64_t mbg = mrow0 / 16 + mb;
+          const int64_t mbc = mbg <= mlast / 16 ? mbg : mlast / 16;
           a[u][mb] = *reinterpret_cast<const i32x4*>(p.a + (mbc * p.KB + kbc) * kBlockBytes +
                                                      lane * 16);
         } else if (AVEC) {
@@ -1120,7 +1123,7 @@ __global__ __launch_bounds__(WAVES* kWave) void decode_gemm_kernel(GemmArgs p) {
   const int32_t qb = p.qbias ? p.qbias[n] : 0;
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
-    const int64_t m = mbk * 16 + (lane >> 4) * 4 + t;
+    const int64_t m = mrow0 + mbk * 16 + (lane >> 4) * 4 + t;
     if (m >= p.M) continue;
     if (p.out == kOutI32) {
       reinterpret_cast<int32_t*>(p.y)[m * p.ldy + n] = sum[t];
@@ -1273,33 +1276,30 @@ struct DenseVariant {
   int threads;
   bool decode;   // grid = n-blocks / nbw, one workgroup per nbw 16-column blocks
   int nbw;
+  int mrows;     // decode: rows per workgroup (grid.y = ceil(M / mrows))
 };
 
 constexpr int kDecodeWaves = 8;
 
 // 0: M > 64 fallback (K % 16 != 0 or unaligned A): 128x128 tiles, VGPR-staged
-// 1..3: M <= 16 / 32 / 64: decode kernel with 1 / 2 / 4 m-blocks
+// 1..3: M <= 16 / 32 / 64: decode kernel with 1 / 2 m-blocks of one n-block;
+// M <= 64 as two row groups of 32 (grid.y) with 2 m-blocks x 2 n-blocks per
+// workgroup: a workgroup reads half the activation rows for twice the
+// columns (458 instead of 573 KB per workgroup at K = 7168), and the weights
+// of a column pair twice, by two workgroups on the same XCD
 // 4..6: the same for K % 16 != 0 or an unaligned activation pointer
-#ifndef W8A8_DECODE64_NBW
-#define W8A8_DECODE64_NBW 1
-#endif
-#ifndef W8A8_DECODE64_UNR
-#define W8A8_DECODE64_UNR 7
-#endif
-constexpr int kNbw64 = W8A8_DECODE64_NBW;
-constexpr int kUnr64 = W8A8_DECODE64_UNR;
 const DenseVariant kDense[] = {
-    {128, 128, dense_gemm_kernel<128, 128, 2, 2, 2>, 256, false, 1},
-    {16, 16, decode_gemm_kernel<1, 1, kDecodeWaves, 14, true>, kDecodeWaves * 64, true, 1},
-    {32, 16, decode_gemm_kernel<2, 1, kDecodeWaves, 14, true>, kDecodeWaves * 64, true, 1},
-    {64, 16, decode_gemm_kernel<4, kNbw64, kDecodeWaves, kUnr64, true>, kDecodeWaves * 64, true, kNbw64},
-    {16, 16, decode_gemm_kernel<1, 1, kDecodeWaves, 14, false>, kDecodeWaves * 64, true, 1},
-    {32, 16, decode_gemm_kernel<2, 1, kDecodeWaves, 14, false>, kDecodeWaves * 64, true, 1},
-    {64, 16, decode_gemm_kernel<4, kNbw64, kDecodeWaves, kUnr64, false>, kDecodeWaves * 64, true, kNbw64},
+    {128, 128, dense_gemm_kernel<128, 128, 2, 2, 2>, 256, false, 1, 0},
+    {16, 16, decode_gemm_kernel<1, 1, kDecodeWaves, 14, true>, kDecodeWaves * 64, true, 1, 16},
+    {32, 16, decode_gemm_kernel<2, 1, kDecodeWaves, 14, true>, kDecodeWaves * 64, true, 1, 32},
+    {64, 16, decode_gemm_kernel<2, 2, kDecodeWaves, 7, true, false, true>, kDecodeWaves * 64, true, 2, 32},
+    {16, 16, decode_gemm_kernel<1, 1, kDecodeWaves, 14, false>, kDecodeWaves * 64, true, 1, 16},
+    {32, 16, decode_gemm_kernel<2, 1, kDecodeWaves, 14, false>, kDecodeWaves * 64, true, 1, 32},
+    {64, 16, decode_gemm_kernel<2, 2, kDecodeWaves, 7, false, false, true>, kDecodeWaves * 64, true, 2, 32},
     // 7..9: M <= 16 / 32 / 64 with packed A (1 KB blocks)
-    {16, 16, decode_gemm_kernel<1, 1, kDecodeWaves, 14, true, true>, kDecodeWaves * 64, true, 1},
-    {32, 16, decode_gemm_kernel<2, 1, kDecodeWaves, 14, true, true>, kDecodeWaves * 64, true, 1},
-    {64, 16, decode_gemm_kernel<4, kNbw64, kDecodeWaves, kUnr64, true, true, true>, kDecodeWaves * 64, true, kNbw64},
+    {16, 16, decode_gemm_kernel<1, 1, kDecodeWaves, 14, true, true>, kDecodeWaves * 64, true, 1, 16},
+    {32, 16, decode_gemm_kernel<2, 1, kDecodeWaves, 14, true, true>, kDecodeWaves * 64, true, 1, 32},
+    {64, 16, decode_gemm_kernel<2, 2, kDecodeWaves, 7, true, true, true>, kDecodeWaves * 64, true, 2, 32},
 };
 
 }  // namespace
@@ -1365,8 +1365,8 @@ hipError_t launch_dense_gemm(const DensePlan& plan, const int8_t* q, const float
     p.a_vec = true;
     if (variant != 0) {
       const DenseVariant& v = kDense[6 + (M <= 16 ? 1 : (M <= 32 ? 2 : 3))];
-      hipLaunchKernelGGL(v.fn, dim3((unsigned)ceil_div(ceil_div(N, 16), v.nbw)), dim3(v.threads), 0,
-                         stream, p);
+      hipLaunchKernelGGL(v.fn, dim3((unsigned)ceil_div(ceil_div(N, 16), v.nbw), (unsigned)ceil_div(M, v.mrows)),
+                         dim3(v.threads), 0, stream, p);
       return hipGetLastError();
     }
     if (!offsets32_ok(p)) return hipErrorInvalidValue;
@@ -1391,7 +1391,8 @@ hipError_t launch_dense_gemm(const DensePlan& plan, const int8_t* q, const float
   }
   const DenseVariant& v = kDense[variant];
   const int64_t tiles = v.decode ? ceil_div(ceil_div(N, 16), v.nbw) : ceil_div(M, v.BM) * ceil_div(N, v.BN);
-  hipLaunchKernelGGL(v.fn, dim3((unsigned)tiles), dim3(v.threads), 0, stream, p);
+  const int64_t gy = v.decode ? ceil_div(M, v.mrows) : 1;
+  hipLaunchKernelGGL(v.fn, dim3((unsigned)tiles, (unsigned)gy), dim3(v.threads), 0, stream, p);
   return hipGetLastError();
 }
 
