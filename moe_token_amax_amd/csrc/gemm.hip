@@ -381,10 +381,13 @@ struct DmaTile {
   // The ring holds five k-blocks (the whole 160 KB of LDS) and advances two at
   // a time, with one wait + barrier per pair of k-blocks (kb, kb + 1) whose
   // fragments are F and G:
-  //   F rows 0..H-1 | LDS reads of G | F rows H..TM-1 | G rows 0..H-1 |
-  //   wait for the DMA of kb + 2, kb + 3 (kb + 4 stays in flight), s_barrier |
-  //   DMA of kb + 5, kb + 6 into the buffers of kb, kb + 1 | LDS reads of the
-  //   next F (kb + 2) | G rows H..TM-1.
+  //   DMA of kb + 4 into the buffer of kb - 1 | F rows 0..H-1 | LDS reads of
+  //   G | F rows H..TM-1 | G rows 0..H-1 | wait for the DMA of kb + 2, kb + 3
+  //   (kb + 4 stays in flight), s_barrier | LDS reads of the next F (kb + 2) |
+  //   DMA of kb + 5 into the buffer of kb | G rows H..TM-1.
+  // The DMA of each pair is split over two points, after the next fragment
+  // reads and before the next pair's first rows, rather than issued all at
+  // once after the barrier (that burst cost about 6% of the prefill GEMM).
   // So two to three k-blocks of DMA are always in flight (a wait for every
   // load at each barrier would drain the DMA queue and expose its latency once
   // per pair), one barrier per two k-blocks keeps the two wavefronts of a SIMD
@@ -423,11 +426,18 @@ struct DmaTile {
     Frags F, G;
     read_frags(smem, F, wm, wn, lane);
     int buf = 0;  // ring buffer of k-block kb (kb % 5)
+    int pend_buf = -1, pend_kb = 0;  // the DMA deferred to the next pair (kb + 4 there)
     for (int kb = 0; kb < KB; kb += 2) {
       const int buf1 = buf == 4 ? 0 : buf + 1;
       const int buf2 = buf1 == 4 ? 0 : buf1 + 1;
       const bool has1 = kb + 1 < KB;
       const bool more = kb + 2 < KB;
+      __builtin_amdgcn_sched_barrier(0);
+      if (pend_buf >= 0) {  // wave-uniform
+#pragma unroll
+        for (int i = 0; i < kPerWave; ++i) issue_one(p, src, smem, pend_buf, pend_kb, wave, lane, i);
+        pend_buf = -1;
+      }
       __builtin_amdgcn_sched_barrier(0);
       mfma_rows(F, acc, 0, H);
       __builtin_amdgcn_sched_barrier(0);
@@ -439,19 +449,21 @@ struct DmaTile {
       __builtin_amdgcn_sched_barrier(0);
       if (more) {
         // every wavefront's DMA of kb + 2 and kb + 3 landed (kb + 4 may still
-        // be in flight), every read of the buffers of kb and kb + 1 done;
-        // refill those with kb + 5 and kb + 6
+        // be in flight: it is the last one issued), every read of the
+        // buffers of kb and kb + 1 done; refill those with kb + 5 now and
+        // kb + 6 at the start of the next pair (the vmcnt order stays the
+        // issue order: kb + 6 is again the last one in flight at the next wait)
         if (kb + 4 < KB) wait_vm_barrier<kPerWave>();
         else wait_vm_barrier<0>();
+        if (kb + 6 < KB) {
+          pend_buf = buf1;
+          pend_kb = kb + 6;
+        }
+        read_frags(smem + buf2 * kStageBytes, F, wm, wn, lane);
         if (kb + 5 < KB) {
 #pragma unroll
           for (int i = 0; i < kPerWave; ++i) issue_one(p, src, smem, buf, kb + 5, wave, lane, i);
         }
-        if (kb + 6 < KB) {
-#pragma unroll
-          for (int i = 0; i < kPerWave; ++i) issue_one(p, src, smem, buf1, kb + 6, wave, lane, i);
-        }
-        read_frags(smem + buf2 * kStageBytes, F, wm, wn, lane);
       }
       __builtin_amdgcn_sched_barrier(0);
       if (has1) mfma_rows(G, acc, H, TM);
