@@ -21,7 +21,14 @@
  *     check launches nothing and returns a non-zero w8a8_status;
  *     w8a8_last_error() then returns a message for the calling thread.
  *   - Device-side problems (e.g. a group_list whose counts do not sum to R)
- *     are not detected; results are then undefined.
+ *     are not detected by default. The kernels stay in bounds anyway (a
+ *     negative count owns no rows; rows past R are never read or written),
+ *     but the results are then not meaningful. With W8A8_CHECK set to
+ *     anything but "" or "0" in the environment (read at every call), each
+ *     call that takes a group_list first copies it to the host, which
+ *     synchronizes the call's stream, and returns W8A8_ERR_SHAPE, launching
+ *     nothing, for a negative count or counts summing past R. A debugging
+ *     aid: it cannot be used under graph capture.
  *   - Sizes are int64_t element counts. M == 0 or R == 0 is a valid no-op.
  */
 #ifndef W8A8_H

@@ -3,8 +3,11 @@
 #include <algorithm>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
+#include <cstring>
 #include <mutex>
 #include <string>
+#include <vector>
 
 #include "../../include/w8a8.h"
 #include "launch.hpp"
@@ -36,6 +39,39 @@ int launched(hipError_t err, const char* what) {
 }
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+// W8A8_CHECK set to anything but "" or "0" in the environment (read at every
+// call): the grouped calls copy group_list to the host, synchronizing the
+// call's stream, and reject a negative count or counts summing past R before
+// anything is launched. A debugging aid, off by default: it synchronizes, so
+// it cannot be used under graph capture. Without it the kernels still stay
+// in bounds (a negative count owns no rows, rows past R are never touched),
+// but the results of such a list are not meaningful.
+bool debug_checks() {
+  const char* v = std::getenv("W8A8_CHECK");
+  return v && v[0] && std::strcmp(v, "0") != 0;
+}
+
+int check_group_list(const char* who, const int64_t* group_list, int64_t E, int64_t R, void* stream) {
+  if (!debug_checks()) return W8A8_OK;
+  std::vector<int64_t> h((size_t)E);
+  const hipStream_t s = (hipStream_t)stream;
+  hipError_t err = hipMemcpyAsync(h.data(), group_list, (size_t)E * sizeof(int64_t), hipMemcpyDeviceToHost, s);
+  if (err == hipSuccess) err = hipStreamSynchronize(s);
+  if (err != hipSuccess)
+    return fail(W8A8_ERR_LAUNCH, "%s: W8A8_CHECK copy of group_list: %s", who, hipGetErrorString(err));
+  int64_t sum = 0;
+  for (int64_t e = 0; e < E; ++e) {
+    if (h[(size_t)e] < 0)
+      return fail(W8A8_ERR_SHAPE, "%s: group_list[%lld] = %lld is negative", who, (long long)e,
+                  (long long)h[(size_t)e]);
+    sum += h[(size_t)e];
+    if (sum > R)
+      return fail(W8A8_ERR_SHAPE, "%s: group_list counts pass R = %lld rows at expert %lld", who, (long long)R,
+                  (long long)e);
+  }
+  return W8A8_OK;
+}
 
 constexpr int64_t kMaxDim = (int64_t)1 << 31;  // rows / columns limit of the grids
 constexpr int64_t kMaxExperts = 1024;           // LDS tile table of the grouped kernel
@@ -249,14 +285,15 @@ static int check_grouped_call(const char* who, const int8_t* a, const float* a_s
 int w8a8_grouped_gemm(const int8_t* a, const float* a_scale, const int64_t* group_list, int64_t R,
                       int64_t E, int64_t N, int64_t K, const void* w_packed, const float* w_scale,
                       void* y, int out, void* workspace, int64_t ws_bytes, void* stream) {
-  const int st = check_grouped_call("grouped_gemm", a, a_scale, group_list, R, E, N, K, w_packed, w_scale,
-                                    y, out);
+  int st = check_grouped_call("grouped_gemm", a, a_scale, group_list, R, E, N, K, w_packed, w_scale, y, out);
   if (st) return st;
   if (R == 0) return ok();
   const int64_t need = w8a8::grouped_ws_bytes(R, E, N, K);
   if (need > 0 && (!workspace || ws_bytes < need || !aligned(workspace, 256)))
     return fail(W8A8_ERR_WORKSPACE, "grouped_gemm: needs %lld workspace bytes (256-byte aligned), got %lld",
                 (long long)need, (long long)ws_bytes);
+  st = check_group_list("grouped_gemm", group_list, E, R, stream);
+  if (st) return st;
   return launched(w8a8::launch_grouped_gemm(a, a_scale, group_list, R, E, N, K, w_packed, w_scale, y,
                                             out, workspace, (hipStream_t)stream),
                   "grouped_gemm");
@@ -296,6 +333,8 @@ int w8a8_moe_grouped(const void* x_rows, const float* x_scale, const int64_t* gr
   if (!workspace || ws_bytes < L.total || !aligned(workspace, 256))
     return fail(W8A8_ERR_WORKSPACE, "moe_grouped: needs %lld workspace bytes (256-byte aligned), got %lld",
                 (long long)L.total, (long long)ws_bytes);
+  st = check_group_list("moe_grouped", group_list, E, R, stream);
+  if (st) return st;
   hipStream_t s = (hipStream_t)stream;
   char* ws = reinterpret_cast<char*>(workspace);
   const int8_t* q1 = reinterpret_cast<const int8_t*>(x_rows);
@@ -695,6 +734,8 @@ int w8a8_mx_grouped_gemm(const uint16_t* x, const int64_t* group_list, int64_t R
   if (!workspace || ws_bytes < L.total || !aligned(workspace, 256))
     return fail(W8A8_ERR_WORKSPACE, "mx_grouped_gemm: needs %lld workspace bytes (256-byte aligned), got %lld",
                 (long long)L.total, (long long)ws_bytes);
+  st = check_group_list("mx_grouped_gemm", group_list, E, R, stream);
+  if (st) return st;
   hipStream_t s = (hipStream_t)stream;
   char* ws = reinterpret_cast<char*>(workspace);
   int4* tiles = reinterpret_cast<int4*>(ws + L.tiles);
@@ -736,6 +777,8 @@ int w8a8_mx_moe_grouped(const uint16_t* x_rows, const int64_t* group_list, int64
   if (!workspace || ws_bytes < need || !aligned(workspace, 256))
     return fail(W8A8_ERR_WORKSPACE, "mx_moe_grouped: needs %lld workspace bytes (256-byte aligned), got %lld",
                 (long long)need, (long long)ws_bytes);
+  st = check_group_list("mx_moe_grouped", group_list, E, R, stream);
+  if (st) return st;
   hipStream_t s = (hipStream_t)stream;
   char* ws = reinterpret_cast<char*>(workspace);
   // the two stages share the schedule and the activation region (W13's MX
@@ -876,6 +919,8 @@ int w8a8_w4a16_grouped_gemm(int fmt, const uint16_t* x, const int64_t* group_lis
   if (!x || !group_list || !w_packed || !y) return fail(W8A8_ERR_NULL, "w4a16_grouped_gemm: null pointer");
   if (!aligned(x, 16) || !aligned(w_packed, 16) || !aligned(y, 8) || !aligned(group_list, 8))
     return fail(W8A8_ERR_ALIGN, "w4a16_grouped_gemm: x and w_packed need 16-byte, y 8-byte alignment");
+  st = check_group_list("w4a16_grouped_gemm", group_list, E, R, stream);
+  if (st) return st;
   return launched(w8a8::launch_lowbit_grouped(fmt, x, group_list, R, E, N, K,
                                               reinterpret_cast<const uint8_t*>(w_packed), y, (hipStream_t)stream),
                   "w4a16_grouped_gemm");
@@ -912,6 +957,8 @@ int w8a8_w4a16_moe_grouped(int fmt, const uint16_t* x_rows, const int64_t* group
   if (!workspace || ws_bytes < need || !aligned(workspace, 256))
     return fail(W8A8_ERR_WORKSPACE, "w4a16_moe_grouped: needs %lld workspace bytes (256-byte aligned), got %lld",
                 (long long)need, (long long)ws_bytes);
+  st = check_group_list("w4a16_moe_grouped", group_list, E, R, stream);
+  if (st) return st;
   uint16_t* h = reinterpret_cast<uint16_t*>(workspace);
   uint16_t* a = reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(workspace) + align256(R * 2 * I * 2));
   const hipStream_t s = (hipStream_t)stream;
@@ -1059,10 +1106,12 @@ int scratch_address(void** out) {
 int w8a8_grouped_gemm_noalloc(const int8_t* a, const float* a_scale, const int64_t* group_list, int64_t R,
                               int64_t E, int64_t N, int64_t K, const void* w_packed, const float* w_scale,
                               void* y, int out, void* stream) {
-  const int st = check_grouped_call("grouped_gemm_noalloc", a, a_scale, group_list, R, E, N, K, w_packed,
-                                    w_scale, y, out);
+  int st = check_grouped_call("grouped_gemm_noalloc", a, a_scale, group_list, R, E, N, K, w_packed, w_scale, y,
+                              out);
   if (st) return st;
   if (R == 0) return ok();
+  st = check_group_list("grouped_gemm_noalloc", group_list, E, R, stream);
+  if (st) return st;
   const int64_t need = w8a8::grouped_ws_bytes(R, E, N, K);
   if (need > kScratchBytes)
     return fail(W8A8_ERR_UNSUPPORTED, "grouped_gemm_noalloc: the schedule of %lld experts needs %lld bytes, "
