@@ -116,19 +116,31 @@ class Workload:
     def group_steps(self, g):
         """Capture the steps in graphs of g consecutive steps: graph j holds
         steps j*g .. j*g + g - 1 (mod the phase cycle)."""
-        import math
-        P = len(self.step_fns)
         self.g = g
-        n = P // math.gcd(P, g)
         self.phases = []
-        for j in range(n):
-            fns = [self.step_fns[(j * g + t) % P] for t in range(g)]
+        for plan in graph_plan(len(self.step_fns), g):
+            fns = [self.step_fns[k] for k in plan]
             self.phases.append(self._graph(lambda fns=fns: [f() for f in fns]))
 
     def step(self, i):
         """Step i; the graph of its group is replayed at the group's last step."""
         if i % self.g == self.g - 1:
             self.phases[(i // self.g) % len(self.phases)].replay()
+
+
+def graph_plan(P, g):
+    """Phases held by each step graph when P phases cycle (phase i % P at step
+    i) and every graph holds g consecutive steps: graph j covers steps j*g ..
+    j*g + g - 1, and replaying graphs 0, 1, .. in turn (wrapping) runs every
+    step's own phase."""
+    n = P // math.gcd(P, g)
+    return [[(j * g + t) % P for t in range(g)] for j in range(n)]
+
+
+def steps_per_graph(steps, warmup):
+    """Steps per captured graph: a divisor of both counts (at most 16), so the
+    warm-up and the timed region are whole graph replays."""
+    return math.gcd(16, steps, warmup) if warmup else math.gcd(16, steps)
 
 
 def _ev(torch):
@@ -1165,7 +1177,7 @@ def _run(name, w, torch, steps, warmup, cpu_seconds, cpu_baseline):
     """One workload: warm-up, K timed steps, the dominant kernel's event timing
     and (optionally) the oracle on the host. Returns the result fields."""
     wl = _make_workload(name, w, torch)
-    per_graph = math.gcd(16, steps, warmup) if warmup else math.gcd(16, steps)
+    per_graph = steps_per_graph(steps, warmup)
     wl.group_steps(per_graph)
     for i in range(warmup):
         wl.step(i)
