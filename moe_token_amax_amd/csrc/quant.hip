@@ -190,7 +190,16 @@ __global__ __launch_bounds__(256) void quant_rows_packed_wave(const uint16_t* __
                                                               int64_t K, int8_t* __restrict__ q,
                                                               float* __restrict__ scale) {
   const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+  // The four workgroups of a 16-row block write into the same 1 KB code
+  // blocks; workgroup b runs on XCD b % 8, so when the grid allows, row block
+  // indices are laid out so that those four share one XCD (and its L2)
+  // instead of leaving four partial copies of each line in four L2s.
+  int64_t bidx = blockIdx.x;
+  if (gridDim.x % (8 * 16 / kRowsPerBlock) == 0) {
+    const int64_t per = gridDim.x / 8;
+    bidx = (int64_t)(blockIdx.x % 8) * per + blockIdx.x / 8;
+  }
+  const int64_t row = bidx * kRowsPerBlock + (threadIdx.x >> 6);
   if (row >= (M + 15) / 16 * 16) return;  // whole wave leaves together
   const int64_t kb = (K + 63) / 64, npc = kb * 4;  // 16-value pieces of a row, padding included
   const bool live = row < M;
