@@ -186,11 +186,23 @@ __global__ __launch_bounds__(256) void mx_quant_kernel(const uint16_t* __restric
                                                        uint8_t* __restrict__ scale_rm,
                                                        uint8_t* __restrict__ scale_kb,
                                                        int64_t Mp) {
-  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t chunks = K / 8;             // K % 32 == 0, so quads never straddle rows
-  const bool live = t < M * chunks;
-  const int64_t tc = live ? t : 0;
-  const int64_t row = tc / chunks, c = tc % chunks;
+  int64_t row, c;
+  bool live;
+  if (blocked) {
+    // a workgroup per 16 rows x 128 k: it writes whole P16x64 blocks (full
+    // cache lines), instead of 16 rows' pieces from 16 workgroups
+    const int64_t KT = (chunks + 15) / 16;
+    row = (int64_t)(blockIdx.x / KT) * 16 + (threadIdx.x >> 4);
+    c = (int64_t)(blockIdx.x % KT) * 16 + (threadIdx.x & 15);
+    live = row < M && c < chunks;
+  } else {
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    live = t < M * chunks;
+    const int64_t tc = live ? t : 0;
+    row = tc / chunks;
+    c = tc % chunks;
+  }
   uint32_t w[4] = {0u, 0u, 0u, 0u};
   if (live) mx_load8<ACT>(x, ldx, K, row, c, w);
   const uint32_t amax = mx_quad_amax(w);
@@ -1039,7 +1051,8 @@ hipError_t launch_mx_quant(const uint16_t* x, int64_t M, int64_t K, int scale_al
                            hipStream_t stream) {
   const int64_t n = M * (K / 8);
   if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(mx_quant_kernel<0>, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, stream, x, K,
+  const int64_t grid = blocked ? ceil_div(M, 16) * ceil_div(K / 8, 16) : ceil_div(n, 256);
+  hipLaunchKernelGGL(mx_quant_kernel<0>, dim3((unsigned)grid), dim3(256), 0, stream, x, K,
                      M, K, scale_alg, payload, blocked ? 1 : 0, scale_rm, scale_kb, Mp);
   return hipGetLastError();
 }
