@@ -91,7 +91,8 @@ int w8a8_dynamic_quant(const uint16_t* x, int64_t M, int64_t K, int8_t* q,
                        float* x_scale, void* stream);
 
 /*
- * w8a8_dynamic_quant_ld: w8a8_dynamic_quant on row-strided buffers: row m of
+ * w8a8_dynamic_quant_ld [DSV4 §二 npu_dynamic_quant]: w8a8_dynamic_quant on
+ *   row-strided buffers: row m of
  *   x at x + m * ldx (ldx >= K BF16 elements), its codes at q + m * ldq
  *   (ldq >= K bytes); codes and scales identical to w8a8_dynamic_quant
  *   (which is the case ldx = ldq = K). A ld below K is W8A8_ERR_SHAPE. For a
