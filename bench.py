@@ -5,9 +5,10 @@ python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload default|decode|p
 
 Prints ONE JSON line. A step is one pass of the workload's whole hot path over
 resident, seeded synthetic inputs. The default run reports the decode workload
-as the headline (value, roofline, cpu_baseline) and the metric's other two
-parts, prefill TOPS and MoE tokens/s, as nested objects under "also" (each
-with its own value, ms_per_step, roofline and cpu_baseline).
+as the headline (value, roofline, cpu_baseline) and, as nested objects under
+"also" (each with its own value, ms_per_step, roofline and cpu_baseline), the
+metric's other two parts, prefill TOPS and MoE tokens/s, plus the MXFP8
+linear (TFLOPS) and the tiny latency case.
   decode   per-token quant + INT8 linear for M = 1, 4, 16 and 64 rows,
            K = 7168, N = 4096, no bias. Sixteen copies of the packed weight
            (16 x 29.4 MB) are used round-robin so that no weight read is served
@@ -1267,11 +1268,12 @@ def main():
     }
     out.update(res)
     if args.workload == "default":
-        # the metric's other two parts on their own workloads: prefill-shaped
-        # linear TOPS and MoE grouped-GEMM tokens/s, each with its roofline and
-        # oracle timing (at most 48 timed steps and 16 warm-up steps)
+        # the metric's other parts on their own workloads: prefill-shaped
+        # linear TOPS, MoE grouped-GEMM tokens/s, and the other two configs of
+        # the metric (the MXFP8 linear, the tiny latency case), each with its
+        # roofline and oracle timing (at most 48 timed steps and 16 warm-up)
         extra = {}
-        for name in ("prefill", "moe"):
+        for name in ("prefill", "moe", "mx", "tiny"):
             r = _run(name, w, torch, min(args.steps, 48), min(args.warmup, 16), args.cpu_seconds,
                      not args.no_cpu_baseline)
             r["steps"] = min(args.steps, 48)
