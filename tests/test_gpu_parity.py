@@ -127,6 +127,9 @@ LINEAR_SHAPES = [  # M, K, N, bias
     (96, 48, 16, True),
     # prefill-sized M with K % 16 != 0 (VGPR-staged fallback)
     (65, 100, 50, True), (200, 37, 33, False),
+    # 33..64 rows with K % 16 != 0: the element-wise decode kernel on two
+    # 32-row groups of 2 x 2 blocks, a partial second group and N tail
+    (48, 100, 72, True), (33, 200, 40, False),
 ]
 
 

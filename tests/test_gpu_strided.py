@@ -83,6 +83,7 @@ LINEAR_CASES = [
     (4, 2064, 160, False, 48, 16, 8, 0),     # decode, ragged last k-block
     (16, 1024, 256, True, 7, 5, 3, 2),       # decode, unaligned code rows
     (40, 1040, 96, False, 16, 0, 0, 0),      # decode, only q strided
+    (40, 1040, 96, True, 3, 1, 0, 0),        # decode, 33..64 rows on unaligned code rows
     (64, 4096, 512, True, 128, 64, 64, 0),   # decode M = 64
     (300, 1088, 600, True, 64, 0, 40, 8),    # prefill tiles through the LDS ring
     (257, 4096, 512, False, 16, 16, 7, 2),   # prefill, odd ldy: element-wise stores
