@@ -48,6 +48,8 @@ def _ids(T, k, E, kind, seed):
         return rng.integers(-3, E + 3, (T, k)).astype(np.int32)
     if kind == "one":                   # every pair on one expert
         return np.full((T, k), E // 2, np.int32)
+    if kind == "none":                  # every id dropped
+        return np.where(rng.random((T, k)) < 0.5, -1, E).astype(np.int32)
     raise ValueError(kind)
 
 
@@ -70,7 +72,8 @@ ROUTE_CASES = [(0, 8, 4, "uniform"), (1, 1, 1, "uniform"), (97, 8, 33, "invalid"
                (2048, 8, 256, "synth"), (5000, 8, 1024, "uniform"), (3000, 1, 4, "one"),
                (1500, 6, 7, "invalid"), (333, 3, 1000, "synth"), (4096, 8, 64, "uniform"),
                (4097, 8, 7, "invalid"), (8192, 8, 256, "synth"), (65536, 8, 256, "synth"),
-               (40000, 1, 9, "one"), (33 * 1024 + 5, 1, 1, "uniform"), (6000, 7, 1000, "invalid")]
+               (40000, 1, 9, "one"), (33 * 1024 + 5, 1, 1, "uniform"), (6000, 7, 1000, "invalid"),
+               (33 * 1024 + 1, 1, 1024, "none"), (3000, 1, 4, "none")]
 
 
 @pytest.mark.parametrize("T,k,E,kind", ROUTE_CASES)
