@@ -492,11 +492,9 @@ int w8a8_static_linear(const int8_t* q, int64_t M, int64_t K, const void* w_pack
  *   BF16(sum_k x[m, k] * BF16(q * s)[n, k]): each weight dequantized once to
  *   BF16 (round half to even of the exact q * s), exact BF16 products,
  *   fp32 accumulation (not bit-exact against a float64 sum; no bias).
- *   workspace: w8a8_w4a16_linear_workspace_bytes(M, K) bytes, 256-byte
- *   aligned (0, and NULL allowed, for M <= 16; above, the activation packed
- *   into the MFMA's 1 KB operand blocks), rewritten by every call; a missing,
- *   short or misaligned workspace returns W8A8_ERR_WORKSPACE before any
- *   launch.
+ *   workspace: w8a8_w4a16_linear_workspace_bytes(M, K) bytes, which is 0
+ *   for every shape (NULL / 0 accepted; the linear stages its activation
+ *   rows in LDS); the argument stays so that the signature does not change.
  * Packed layout: per 16-column block and 128-deep k-chunk 1152 bytes (codes +
  *   8 in nibbles in the BF16 MFMA's operand order, then the 16 x 4 BF16
  *   scales); K padded to 128 with zero weights.

@@ -18,7 +18,7 @@ hipError_t launch_w4_quant_pack(const uint16_t* w, int64_t N, int64_t K, int8_t*
                                 uint8_t* packed, hipStream_t stream);
 hipError_t launch_w4_pack(const int8_t* q, const uint16_t* s, int64_t N, int64_t K, uint8_t* packed,
                           hipStream_t stream);
-// workspace of the linears: the packed activation when M > 16 (else 0)
+// workspace of the linears: none (0 bytes for every shape)
 int64_t w4_linear_ws_bytes(int64_t M, int64_t K);
 // y BF16 [M, N] = x BF16 [M, K] times the dequantized packed weight
 hipError_t launch_w4a16_linear(const uint16_t* x, int64_t M, int64_t K, const uint8_t* wp, int64_t N,

@@ -216,23 +216,6 @@ __device__ __forceinline__ bf16x8 w4_dequant8(uint32_t word, float s) {
   return __builtin_bit_cast(bf16x8, uint4{pk[0], pk[1], pk[2], pk[3]});
 }
 
-// BF16 activation x [M, K] -> 1 KB blocks [ceil(M/16)][K/32] in the BF16 MFMA's
-// A operand order: byte l * 16 of block (mb, kb) holds x[16 mb + l % 16][32 kb
-// + 8 (l / 16) .. + 7]; rows past M repeat row M - 1 (their outputs are not
-// stored). One thread per 16-byte piece.
-__global__ __launch_bounds__(256) void w4_pack_a_kernel(const uint16_t* __restrict__ x, int64_t M,
-                                                        int64_t K, uint8_t* __restrict__ out) {
-  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t KB = K / 32, MB = (M + 15) / 16;
-  if (t >= MB * KB * 64) return;
-  const int lane = (int)(t & 63);
-  const int64_t blk = t >> 6, mb = blk / KB, kb = blk % KB;
-  int64_t row = mb * 16 + (lane & 15);
-  row = row < M ? row : M - 1;
-  reinterpret_cast<uint4*>(out)[t] =
-      *reinterpret_cast<const uint4*>(x + row * K + kb * 32 + 8 * (lane >> 4));
-}
-
 // 8 BF16 weights of one step from 8 E2M1 codes (weight 2b in the low nibble
 // of byte b, 2b + 1 in the high one) and the group's scale sc = 2^E: gfx950's
 // MX conversion v_cvt_scalef32_pk_bf16_fp4 decodes the two codes of one byte
@@ -248,14 +231,13 @@ __device__ __forceinline__ bf16x8 fp4_dequant8(uint32_t word, float sc) {
                                           __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3)});
 }
 
-template <int MB, int NBW, int UNR, int WAVES, int FMT, bool ABLK>
+template <int MB, int NBW, int UNR, int WAVES, int FMT>
 __global__ __launch_bounds__(64 * WAVES) void w4a16_decode_kernel(const uint16_t* __restrict__ x,
                                                                   int64_t M, int64_t K,
                                                                   const uint8_t* __restrict__ wp,
                                                                   int64_t KC, int64_t N,
                                                                   uint16_t* __restrict__ y) {
   static_assert(MB * NBW <= WAVES, "one wavefront per output block in the epilogue");
-  // ABLK: x is the packed activation of w4_pack_a_kernel (1 KB blocks)
   __shared__ f32x4 part[WAVES][MB * NBW][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t NB = (N + 15) / 16;
@@ -324,15 +306,7 @@ __global__ __launch_bounds__(64 * WAVES) void w4a16_decode_kernel(const uint16_t
       }
       // the activation fragment of step j, 16-row block mb (k = 128 kc + 32 j)
       auto afrag = [&](int j, int mb) -> bf16x8 {
-        const int64_t k = kc * kW4Chunk + 32 * j;
-        if (ABLK) {
-          // 16-row blocks past the last packed one read the last (rows >= M: not stored)
-          int64_t rb = row0 / 16 + mb;
-          rb = rb < (M + 15) / 16 ? rb : (M + 15) / 16 - 1;
-          const int64_t blk = rb * (K / 32) + k / 32;
-          return reinterpret_cast<const bf16x8*>(reinterpret_cast<const uint8_t*>(x) + blk * 1024)[lane];
-        }
-        return *reinterpret_cast<const bf16x8*>(arow[mb] + k);
+        return *reinterpret_cast<const bf16x8*>(arow[mb] + kc * kW4Chunk + 32 * j);
       };
       if ((kc + 1) * kW4Chunk <= K) {  // the whole chunk inside K (wavefront-uniform)
 #pragma unroll
@@ -707,7 +681,145 @@ hipError_t launch_fp4_quant_pack(const uint16_t* w, int64_t N, int64_t K, uint8_
   return hipGetLastError();
 }
 
-int64_t w4_linear_ws_bytes(int64_t M, int64_t K) { return M > 16 ? (M + 15) / 16 * (K / 32) * 1024 : 0; }
+// ---------------------------------------------------------------------------
+// More than 16 rows: the row-major activation is staged through LDS, one
+// region per wavefront. For each chunk (128 k) the wavefront loads its 16 MB
+// rows with whole-row 16-byte loads (lane l: row 4 i + l / 16, bytes
+// 16 (l % 16) of the chunk's 256), writes them to its region (row pitch 272
+// bytes, so that both the writes and the fragment reads below are free of
+// bank conflicts), and reads the MFMA fragments back (lane l: row l % 16,
+// k 32 j + 8 (l / 16)). Only the wavefront itself touches its region, and its
+// LDS operations complete in order, so no barrier is needed. The next chunk's
+// codes, scales and activation rows are loaded before this chunk's
+// dequantization. A workgroup covers 16 MB rows x 16 NBW columns (grid.y:
+// row groups). After the loop each wavefront's partial sums go into its own
+// region for the reduction.
+// ---------------------------------------------------------------------------
+template <int MB, int NBW, int FMT>
+__global__ __launch_bounds__(1024) void w4a16_rows_kernel(const uint16_t* __restrict__ x, int64_t M,
+                                                          int64_t K, const uint8_t* __restrict__ wp,
+                                                          int64_t KC, int64_t N, uint16_t* __restrict__ y) {
+  constexpr int WAVES = 16;
+  constexpr int R = 16 * MB;                  // rows of the workgroup
+  constexpr int kPitch = 2 * kW4Chunk + 16;   // LDS bytes per staged row
+  constexpr int kStage = R * kPitch;          // LDS bytes per wavefront
+  constexpr int kLoads = R / 4;               // 16-byte row loads per lane and chunk
+  static_assert(MB * NBW <= WAVES && MB * NBW * 64 * 16 <= kStage, "partials fit in a region");
+  __shared__ __attribute__((aligned(16))) uint8_t lds[WAVES * kStage];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t NB = (N + 15) / 16;
+  const int64_t row0 = (int64_t)blockIdx.y * R;
+  constexpr int64_t kChunkBytes = FMT == 0 ? kW4ChunkBytes : kFp4ChunkBytes;
+  const uint8_t* wblk[NBW];
+#pragma unroll
+  for (int q = 0; q < NBW; ++q) {
+    const int64_t nb = (int64_t)blockIdx.x * NBW + q;
+    wblk[q] = wp + (nb < NB ? nb : NB - 1) * KC * kChunkBytes;  // past the last: not stored
+  }
+  // this lane's staged rows row0 + 4 i + lane / 16 (rows past M load nothing:
+  // their outputs are not stored)
+  const int64_t r_lane = row0 + (lane >> 4);
+  const uint16_t* xr = x + (r_lane < M ? r_lane : 0) * K + 8 * (lane & 15);
+  uint8_t* st = lds + wave * kStage;
+  auto load_w = [&](int64_t kc, uint4 (&c)[NBW], uint2 (&sv)[NBW]) {
+#pragma unroll
+    for (int q = 0; q < NBW; ++q) {
+      const uint8_t* ch = wblk[q] + kc * kChunkBytes;
+      c[q] = reinterpret_cast<const uint4*>(ch)[lane];
+      if (FMT == 0) sv[q] = reinterpret_cast<const uint2*>(ch + 1024)[lane & 15];
+      else sv[q] = uint2{reinterpret_cast<const uint32_t*>(ch + 1024)[lane & 15], 0u};
+    }
+  };
+  auto load_x = [&](int64_t kc, uint4 (&v)[kLoads]) {
+    const bool in = kc * kW4Chunk + 8 * (lane & 15) < K;  // past K: zeros (zero-weight padding)
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i)
+      v[i] = r_lane + 4 * i < M && in ? *reinterpret_cast<const uint4*>(xr + (4 * i) * K + kc * kW4Chunk)
+                                      : uint4{0u, 0u, 0u, 0u};
+  };
+  f32x4 acc[MB][NBW];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int q = 0; q < NBW; ++q) acc[mb][q] = f32x4{0.f, 0.f, 0.f, 0.f};
+  uint4 codes_n[NBW], xn[kLoads];
+  uint2 sc_n[NBW];
+#pragma unroll
+  for (int q = 0; q < NBW; ++q) {
+    codes_n[q] = uint4{0u, 0u, 0u, 0u};
+    sc_n[q] = uint2{0u, 0u};
+  }
+#pragma unroll
+  for (int i = 0; i < kLoads; ++i) xn[i] = uint4{0u, 0u, 0u, 0u};
+  if (wave < KC) {
+    load_w(wave, codes_n, sc_n);
+    load_x(wave, xn);
+  }
+  for (int64_t kc = wave; kc < KC; kc += WAVES) {
+    uint4 codes[NBW];
+    uint2 sc[NBW];
+#pragma unroll
+    for (int q = 0; q < NBW; ++q) {
+      codes[q] = codes_n[q];
+      sc[q] = sc_n[q];
+    }
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i)
+      *reinterpret_cast<uint4*>(st + (4 * i + (lane >> 4)) * kPitch + (lane & 15) * 16) = xn[i];
+    if (kc + WAVES < KC) {  // wavefront-uniform
+      load_w(kc + WAVES, codes_n, sc_n);
+      load_x(kc + WAVES, xn);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      bf16x8 a[MB];
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+        a[mb] = *reinterpret_cast<const bf16x8*>(st + (16 * mb + (lane & 15)) * kPitch +
+                                                 (4 * j + (lane >> 4)) * 16);
+#pragma unroll
+      for (int q = 0; q < NBW; ++q) {
+        const uint32_t cw = j == 0 ? codes[q].x : j == 1 ? codes[q].y : j == 2 ? codes[q].z : codes[q].w;
+        float s;
+        if (FMT == 0) {
+          const uint32_t sw = j < 2 ? sc[q].x : sc[q].y;
+          s = __uint_as_float((j & 1) ? (sw & 0xFFFF0000u) : (sw << 16));
+        } else {  // 2^E = 2^(byte - 127), byte 0 the subnormal 2^-127
+          s = __builtin_ldexpf(1.0f, (int)((sc[q].x >> (8 * j)) & 0xFFu) - 127);
+        }
+        const bf16x8 b = FMT == 0 ? w4_dequant8(cw, s) : fp4_dequant8(cw, s);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+          acc[mb][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mb], b, acc[mb][q], 0, 0, 0);
+      }
+    }
+  }
+  // partials into this wavefront's own region (its last reads are done: LDS
+  // operations of a wavefront complete in order)
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int q = 0; q < NBW; ++q)
+      *reinterpret_cast<f32x4*>(st + ((mb * NBW + q) * 64 + lane) * 16) = acc[mb][q];
+  __syncthreads();
+  if (wave < MB * NBW) {
+    f32x4 s = *reinterpret_cast<const f32x4*>(lds + (wave * 64 + lane) * 16);
+#pragma unroll
+    for (int w = 1; w < WAVES; ++w)
+      s = s + *reinterpret_cast<const f32x4*>(lds + w * kStage + (wave * 64 + lane) * 16);
+    const int mb = wave / NBW, q = wave % NBW;
+    const int64_t n = ((int64_t)blockIdx.x * NBW + q) * 16 + (lane & 15);
+    if (n < N) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t m = row0 + 16 * mb + 4 * (lane >> 4) + i;
+        if (m < M) y[m * N + n] = (uint16_t)f32_to_bf16(s[i]);
+      }
+    }
+  }
+}
+
+int64_t w4_linear_ws_bytes(int64_t, int64_t) { return 0; }
 
 template <int FMT>
 static hipError_t launch_decode(const uint16_t* x, int64_t M, int64_t K, const uint8_t* wp, int64_t N,
@@ -715,24 +827,18 @@ static hipError_t launch_decode(const uint16_t* x, int64_t M, int64_t K, const u
   if (M == 0) return hipSuccess;
   const int64_t NB = (N + 15) / 16, KC = w4_chunks(K);
   if (M <= 16) {
-    hipLaunchKernelGGL((w4a16_decode_kernel<1, 1, 4, 16, FMT, false>), dim3((unsigned)NB, 1), dim3(1024), 0,
+    hipLaunchKernelGGL((w4a16_decode_kernel<1, 1, 4, 16, FMT>), dim3((unsigned)NB, 1), dim3(1024), 0,
                        stream, x, M, K, wp, KC, N, y);
     return hipGetLastError();
   }
-  // more rows: the activation is packed into contiguous 1 KB operand blocks
-  // first, so that each fragment load of the linear is one contiguous block
-  const int64_t pieces = (M + 15) / 16 * (K / 32) * 64;
-  hipLaunchKernelGGL(w4_pack_a_kernel, dim3((unsigned)((pieces + 255) / 256)), dim3(256), 0, stream, x, M,
-                     K, reinterpret_cast<uint8_t*>(ws));
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
+  (void)ws;  // no workspace: the activation rows are staged in LDS
   // a workgroup covers 16 MB rows x 16 NBW columns: INT4 32 x 32, FP4 (whose
   // dequantization is 4 instructions per 8 weights against INT4's 19) 16 x 64,
   // so a workgroup reads 458 / 229 KB of the 64-row activation instead of 917
   constexpr int MB = FMT == 0 ? 2 : 1, NBW = FMT == 0 ? 2 : 4;
-  hipLaunchKernelGGL((w4a16_decode_kernel<MB, NBW, 1, 16, FMT, true>),
+  hipLaunchKernelGGL((w4a16_rows_kernel<MB, NBW, FMT>),
                      dim3((unsigned)((NB + NBW - 1) / NBW), (unsigned)((M + 16 * MB - 1) / (16 * MB))), dim3(1024),
-                     0, stream, reinterpret_cast<const uint16_t*>(ws), M, K, wp, KC, N, y);
+                     0, stream, x, M, K, wp, KC, N, y);
   return hipGetLastError();
 }
 
