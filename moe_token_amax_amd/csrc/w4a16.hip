@@ -187,13 +187,6 @@ __global__ __launch_bounds__(256) void fp4_quant_pack_kernel(const uint16_t* __r
   }
 }
 
-// ---------------------------------------------------------------------------
-// decode linear: one workgroup per NBW 16-column blocks and 16 MB rows, WAVES
-// wavefronts over interleaved k-chunks (UNR chunks of codes, scales and
-// activation fragments loaded before any of them is used), partial sums met
-// in LDS
-// ---------------------------------------------------------------------------
-
 // 8 BF16 weights of one step from a packed word and the group scale. The
 // nibbles are split into the bytes of two words (even and odd nibbles). A
 // byte n <= 15 read as OCP E4M3 is n * 2^-9 exactly, so the MX conversion
@@ -231,150 +224,6 @@ __device__ __forceinline__ bf16x8 fp4_dequant8(uint32_t word, float sc) {
                                           __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3)});
 }
 
-template <int MB, int NBW, int UNR, int WAVES, int FMT>
-__global__ __launch_bounds__(64 * WAVES) void w4a16_decode_kernel(const uint16_t* __restrict__ x,
-                                                                  int64_t M, int64_t K,
-                                                                  const uint8_t* __restrict__ wp,
-                                                                  int64_t KC, int64_t N,
-                                                                  uint16_t* __restrict__ y) {
-  static_assert(MB * NBW <= WAVES, "one wavefront per output block in the epilogue");
-  __shared__ f32x4 part[WAVES][MB * NBW][64];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t NB = (N + 15) / 16;
-  const int64_t row0 = (int64_t)blockIdx.y * 16 * MB;
-  constexpr int64_t kChunkBytes = FMT == 0 ? kW4ChunkBytes : kFp4ChunkBytes;
-  // this workgroup's NBW n-blocks; n-blocks past the last read the last (their
-  // outputs are not stored)
-  const uint8_t* wblk[NBW];
-#pragma unroll
-  for (int q = 0; q < NBW; ++q) {
-    const int64_t nb = (int64_t)blockIdx.x * NBW + q;
-    wblk[q] = wp + (nb < NB ? nb : NB - 1) * KC * kChunkBytes;
-  }
-  // A rows of this lane (row l % 16 of each 16-row block). Rows past M read
-  // row M - 1 instead: an MFMA output row depends on its own A row only, and
-  // those output rows are not stored.
-  const uint16_t* arow[MB];
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
-    const int64_t r = row0 + 16 * mb + (lane & 15);
-    arow[mb] = x + (r < M ? r : M - 1) * K + 8 * (lane >> 4);
-  }
-  f32x4 acc[MB][NBW];
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-    for (int q = 0; q < NBW; ++q) acc[mb][q] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // one chunk per round (UNR 1): the next round's codes and scales are loaded
-  // before this round's dequantization, so their HBM latency overlaps it
-  constexpr bool PF = UNR == 1;
-  auto load_w = [&](int64_t kc, uint4 (&c)[NBW], uint2 (&sv)[NBW]) {
-#pragma unroll
-    for (int q = 0; q < NBW; ++q) {
-      const uint8_t* ch = wblk[q] + kc * kChunkBytes;
-      c[q] = reinterpret_cast<const uint4*>(ch)[lane];
-      if (FMT == 0) sv[q] = reinterpret_cast<const uint2*>(ch + 1024)[lane & 15];
-      else sv[q] = uint2{reinterpret_cast<const uint32_t*>(ch + 1024)[lane & 15], 0u};
-    }
-  };
-  uint4 codes_n[NBW];
-  uint2 sc_n[NBW];
-#pragma unroll
-  for (int q = 0; q < NBW; ++q) {
-    codes_n[q] = uint4{0u, 0u, 0u, 0u};
-    sc_n[q] = uint2{0u, 0u};
-  }
-  if (PF && wave < KC) load_w(wave, codes_n, sc_n);
-  for (int64_t c0 = wave; c0 < KC; c0 += WAVES * UNR) {
-    // all loads of UNR chunks first (codes, scales and the activation
-    // fragments), then the dequantization and the MFMAs
-    uint4 codes[UNR][NBW];
-    uint2 sc[UNR][NBW];  // FMT 0: 4 BF16 scales; FMT 1: 4 E8M0 bytes in .x
-    bf16x8 a[UNR][4][MB];
-#pragma unroll
-    for (int u = 0; u < UNR; ++u) {
-      const int64_t kc = c0 + WAVES * u;
-      if (kc >= KC) continue;  // wavefront-uniform; a chunk past KC is never used
-      if (PF) {
-#pragma unroll
-        for (int q = 0; q < NBW; ++q) {
-          codes[u][q] = codes_n[q];
-          sc[u][q] = sc_n[q];
-        }
-      } else {
-        load_w(kc, codes[u], sc[u]);
-      }
-      // the activation fragment of step j, 16-row block mb (k = 128 kc + 32 j)
-      auto afrag = [&](int j, int mb) -> bf16x8 {
-        return *reinterpret_cast<const bf16x8*>(arow[mb] + kc * kW4Chunk + 32 * j);
-      };
-      if ((kc + 1) * kW4Chunk <= K) {  // the whole chunk inside K (wavefront-uniform)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-          for (int mb = 0; mb < MB; ++mb) a[u][j][mb] = afrag(j, mb);
-      } else {
-        // the last chunk when K % 128 != 0: steps past K (zero-weight padding)
-        // take zeros instead of reads past the row
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-          for (int mb = 0; mb < MB; ++mb)
-            a[u][j][mb] = kc * kW4Chunk + 32 * j < K ? afrag(j, mb) : bf16x8{};
-      }
-    }
-    if (PF && c0 + WAVES < KC) load_w(c0 + WAVES, codes_n, sc_n);  // wavefront-uniform
-#pragma unroll
-    for (int u = 0; u < UNR; ++u) {
-      const int64_t kc = c0 + WAVES * u;
-      if (kc >= KC) break;
-#pragma unroll
-      for (int q = 0; q < NBW; ++q) {
-        const uint32_t cw[4] = {codes[u][q].x, codes[u][q].y, codes[u][q].z, codes[u][q].w};
-        float s[4];
-        if (FMT == 0) {
-          s[0] = __uint_as_float(sc[u][q].x << 16);
-          s[1] = __uint_as_float(sc[u][q].x & 0xFFFF0000u);
-          s[2] = __uint_as_float(sc[u][q].y << 16);
-          s[3] = __uint_as_float(sc[u][q].y & 0xFFFF0000u);
-        } else {
-#pragma unroll
-          for (int j = 0; j < 4; ++j)  // 2^E = 2^(byte - 127), byte 0 the subnormal 2^-127
-            s[j] = __builtin_ldexpf(1.0f, (int)((sc[u][q].x >> (8 * j)) & 0xFFu) - 127);
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const bf16x8 b = FMT == 0 ? w4_dequant8(cw[j], s[j]) : fp4_dequant8(cw[j], s[j]);
-#pragma unroll
-          for (int mb = 0; mb < MB; ++mb)
-            acc[mb][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u][j][mb], b, acc[mb][q], 0, 0, 0);
-        }
-      }
-    }
-  }
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-    for (int q = 0; q < NBW; ++q) part[wave][mb * NBW + q][lane] = acc[mb][q];
-  __syncthreads();
-  // lane l holds rows 4 (l / 16) .. + 3 of column l % 16 in each 16-row block;
-  // wavefront w < MB * NBW sums the WAVES partials of block (w / NBW, w % NBW)
-  // in order
-  if (wave < MB * NBW) {
-    f32x4 s = part[0][wave][lane];
-#pragma unroll
-    for (int w = 1; w < WAVES; ++w) s = s + part[w][wave][lane];
-    const int mb = wave / NBW, q = wave % NBW;
-    const int64_t n = ((int64_t)blockIdx.x * NBW + q) * 16 + (lane & 15);
-    if (n < N) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int64_t m = row0 + 16 * mb + 4 * (lane >> 4) + i;
-        if (m < M) y[m * N + n] = (uint16_t)f32_to_bf16(s[i]);
-      }
-    }
-  }
-}
 
 // ---------------------------------------------------------------------------
 // Grouped form: the MoE experts' matmul with low-bit weights. Rows are grouped
@@ -682,7 +531,8 @@ hipError_t launch_fp4_quant_pack(const uint16_t* w, int64_t N, int64_t K, uint8_
 }
 
 // ---------------------------------------------------------------------------
-// More than 16 rows: the row-major activation is staged through LDS, one
+// Linear: one workgroup per 16 MB rows x 16 NBW columns, 16 wavefronts over
+// interleaved k-chunks. The row-major activation is staged through LDS, one
 // region per wavefront. For each chunk (128 k) the wavefront loads its 16 MB
 // rows with whole-row 16-byte loads (lane l: row 4 i + l / 16, bytes
 // 16 (l % 16) of the chunk's 256), writes them to its region (row pitch 272
@@ -826,15 +676,16 @@ static hipError_t launch_decode(const uint16_t* x, int64_t M, int64_t K, const u
                                 uint16_t* y, void* ws, hipStream_t stream) {
   if (M == 0) return hipSuccess;
   const int64_t NB = (N + 15) / 16, KC = w4_chunks(K);
-  if (M <= 16) {
-    hipLaunchKernelGGL((w4a16_decode_kernel<1, 1, 4, 16, FMT>), dim3((unsigned)NB, 1), dim3(1024), 0,
-                       stream, x, M, K, wp, KC, N, y);
+  (void)ws;  // no workspace: the activation rows are staged in LDS
+  if (M <= 16) {  // one 16-column block per workgroup: 256 workgroups at N = 4096
+    hipLaunchKernelGGL((w4a16_rows_kernel<1, 1, FMT>), dim3((unsigned)NB, 1), dim3(1024), 0, stream, x, M, K,
+                       wp, KC, N, y);
     return hipGetLastError();
   }
-  (void)ws;  // no workspace: the activation rows are staged in LDS
-  // a workgroup covers 16 MB rows x 16 NBW columns: INT4 32 x 32, FP4 (whose
-  // dequantization is 4 instructions per 8 weights against INT4's 19) 16 x 64,
-  // so a workgroup reads 458 / 229 KB of the 64-row activation instead of 917
+  // more rows: a workgroup covers 16 MB rows x 16 NBW columns: INT4 32 x 32,
+  // FP4 (whose dequantization is 4 instructions per 8 weights against INT4's
+  // 19) 16 x 64, so a workgroup reads 458 / 229 KB of the 64-row activation
+  // instead of 917
   constexpr int MB = FMT == 0 ? 2 : 1, NBW = FMT == 0 ? 2 : 4;
   hipLaunchKernelGGL((w4a16_rows_kernel<MB, NBW, FMT>),
                      dim3((unsigned)((NB + NBW - 1) / NBW), (unsigned)((M + 16 * MB - 1) / (16 * MB))), dim3(1024),
