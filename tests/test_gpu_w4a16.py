@@ -107,7 +107,11 @@ LINEAR_CASES = [(1, 256, 64), (4, 1024, 96), (16, 512, 50), (17, 320, 64), (64, 
                 (100, 2048, 256), (3, 96, 40), (1, 7168, 4096),
                 # M > 16 with several chunks per wavefront (the next chunk's codes
                 # loaded ahead), a ragged last chunk (K % 128 = 64), ragged N
-                (80, 4160, 72)]
+                (80, 4160, 72),
+                # row groups of 32 (INT4) / 16 (FP4) with a partial last one,
+                # a last chunk a quarter inside K, a partial last column group;
+                # one partial chunk for 16 wavefronts; a larger decode-like case
+                (33, 1056, 200), (5, 32, 16), (48, 7168, 1024)]
 
 
 @pytest.mark.parametrize("M,K,N", LINEAR_CASES)
