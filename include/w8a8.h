@@ -487,7 +487,7 @@ int w8a8_static_linear(const int8_t* q, int64_t M, int64_t K, const void* w_pack
  *   at least one must be given.
  * w8a8_w4a16_pack: pre-quantized codes (int8; each is clamped to [-8, 7]
  *   before packing) and BF16 scales -> the packed layout.
- * w8a8_w4a16_linear: x BF16 [M, K] (16-byte aligned; M <= 64 * 65535, the
+ * w8a8_w4a16_linear: x BF16 [M, K] (16-byte aligned; M <= 16 * 65535, the
  *   rows of one launch, else W8A8_ERR_SHAPE) -> y BF16 [M, N] =
  *   BF16(sum_k x[m, k] * BF16(q * s)[n, k]): each weight dequantized once to
  *   BF16 (round half to even of the exact q * s), exact BF16 products,

@@ -813,8 +813,9 @@ int w8a8_mx_moe_grouped(const uint16_t* x_rows, const int64_t* group_list, int64
 // ---------------------------------------------------------------------------
 // W4A16 weight variant
 // ---------------------------------------------------------------------------
-// rows of one W4A16 / FP4 linear: 64-row workgroups along the grid's y (at most 65535)
-constexpr int64_t kW4MaxRows = (int64_t)64 * 65535;
+// rows of one W4A16 / FP4 linear: row groups of 16 (FP4) or 32 (INT4) rows
+// along the grid's y, which holds at most 65535
+constexpr int64_t kW4MaxRows = (int64_t)16 * 65535;
 
 static int check_w4(const char* who, int64_t N, int64_t K) {
   if (N < 1 || K < 1 || N >= kMaxDim || K > W8A8_MAX_K)

@@ -237,9 +237,9 @@ def test_w4a16_validation_before_launch(w):
     assert L.w8a8_w4a16_linear(p, 4, 64, None, 16, p, None, 0, None) == 1
     assert L.w8a8_w4a16_linear(None, 0, 64, None, 16, None, None, 0, None) == 0   # M == 0
     assert L.w8a8_w4a16_linear(p, -1, 64, p, 16, p, None, 0, None) == 2
-    # rows past one launch's 64-row workgroups along the grid's y (64 * 65535)
-    assert L.w8a8_w4a16_linear(p, 64 * 65535 + 1, 64, p, 16, p, p, 1 << 40, None) == 2
-    assert L.w8a8_fp4_linear(p, 64 * 65535 + 1, 64, p, 16, p, p, 1 << 40, None) == 2
+    # rows past one launch's 16-row groups along the grid's y (16 * 65535)
+    assert L.w8a8_w4a16_linear(p, 16 * 65535 + 1, 64, p, 16, p, p, 1 << 40, None) == 2
+    assert L.w8a8_fp4_linear(p, 16 * 65535 + 1, 64, p, 16, p, p, 1 << 40, None) == 2
     # no workspace for any M (the rows are staged in LDS)
     assert L.w8a8_w4a16_linear_workspace_bytes(16, 7168) == 0
     assert L.w8a8_w4a16_linear_workspace_bytes(64, 7168) == 0
