@@ -1147,25 +1147,32 @@ __global__ __launch_bounds__(WAVES* kWave) void decode_gemm_kernel(GemmArgs p) {
 }
 
 // ---------------------------------------------------------------------------
-// Dynamic quant fused into the decode GEMM, for a few rows (M <= 2): every
-// workgroup quantizes the M BF16 rows itself (they are L2-resident after the
-// first reads) into LDS — row amax over the workgroup, one IEEE division for
-// the scale and one per element, exactly as the standalone quant — and then
-// runs the decode K loop with the A fragments from LDS (rows >= M read as
-// zero). Saves the quant launch; the results are bit-identical to
-// quant + linear. Dynamic LDS: M * ceil(K/64) * 64 code bytes.
+// Dynamic quant fused into the decode GEMM, for a few values (M * K <=
+// kFusedElems): every workgroup quantizes the M BF16 rows itself (they are
+// L2-resident after the first reads) into LDS — row amax over the workgroup,
+// one IEEE division for the scale and one per element, exactly as the
+// standalone quant — and then runs the decode K loop with the A fragments
+// from LDS (rows >= M read as zero). Saves the quant launch; the results are
+// bit-identical to quant + linear. ROWS <= 4: each thread holds CPT 8-value
+// chunks of every row (K <= CPT * 8 * threads), amax by wavefront reductions.
+// More rows: the M x ceil(K/64)*64 codes are numbered flat and each thread
+// takes up to kFlat chunks of them, wherever the row boundaries fall; the row
+// amax is an LDS atomic max over the chunks' amaxes. Dynamic LDS:
+// M * ceil(K/64) * 64 code bytes.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ uint32_t bf16_pair_absmax(uint32_t w) {
   return max(w & 0x7FFFu, (w >> 16) & 0x7FFFu);
 }
 
-template <int UNR, int WAVES = 8>
+template <int UNR, int WAVES, int ROWS, int CPT>
 __global__ __launch_bounds__(WAVES * kWave) void decode_fused_kernel(GemmArgs p) {
   constexpr int kThreadsF = WAVES * kWave;
-  // rows, 8-value chunks per thread and row (K <= 16384 = kCpt * kThreadsF * 8)
-  constexpr int kRows = 4, kCpt = 32 / WAVES;
+  constexpr int kRows = ROWS, kCpt = CPT;
+  constexpr bool kFlatRows = ROWS > 4;
+  constexpr int kFlat = 3;  // chunks per thread, flat numbering (M * Kp / 8 <= kFlat * threads)
   __shared__ i32x4 red[WAVES][kWave];
-  __shared__ uint32_t wmax[WAVES][kRows];
+  __shared__ uint32_t wmax[kFlatRows ? 1 : WAVES][kRows];
+  __shared__ uint32_t ramax[kRows];
   __shared__ float srow[kRows];
   extern __shared__ __attribute__((aligned(16))) int8_t qlds[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -1176,15 +1183,26 @@ __global__ __launch_bounds__(WAVES * kWave) void decode_fused_kernel(GemmArgs p)
   // The activation rows are loaded first and the first round of weights right
   // after: the wait for the activations (loads retire in issue order) then
   // leaves every weight load in flight while the rows are quantized.
-  uint4 v[kRows][kCpt];
+  uint4 v[kFlatRows ? 1 : kRows][kCpt];
+  uint4 vf[kFlatRows ? kFlat : 1];
+  if constexpr (kFlatRows) {
+    if (tid < kRows) ramax[tid] = 0u;
 #pragma unroll
-  for (int r = 0; r < kRows; ++r)
-#pragma unroll
-    for (int i = 0; i < kCpt; ++i) {
-      const int c = tid + i * kThreadsF;
-      v[r][i] = (r < M && c < nchunk) ? reinterpret_cast<const uint4*>(x + (int64_t)r * K)[c]
-                                      : uint4{0u, 0u, 0u, 0u};
+    for (int i = 0; i < kFlat; ++i) {
+      const int f = tid + i * kThreadsF, r = f / nchunk_p, c = f % nchunk_p;
+      vf[i] = (r < M && c < nchunk) ? reinterpret_cast<const uint4*>(x + (int64_t)r * K)[c]
+                                    : uint4{0u, 0u, 0u, 0u};
     }
+  } else {
+#pragma unroll
+    for (int r = 0; r < kRows; ++r)
+#pragma unroll
+      for (int i = 0; i < kCpt; ++i) {
+        const int c = tid + i * kThreadsF;
+        v[r][i] = (r < M && c < nchunk) ? reinterpret_cast<const uint4*>(x + (int64_t)r * K)[c]
+                                        : uint4{0u, 0u, 0u, 0u};
+      }
+  }
   __builtin_amdgcn_sched_barrier(0);
   const int nb = blockIdx.x;
   const uint8_t* wcol = p.w + (int64_t)nb * p.KB * kBlockBytes + lane * 16;
@@ -1196,6 +1214,30 @@ __global__ __launch_bounds__(WAVES * kWave) void decode_fused_kernel(GemmArgs p)
     b[u] = *reinterpret_cast<const i32x4*>(wcol + (int64_t)kbc * kBlockBytes);
   }
   __builtin_amdgcn_sched_barrier(0);
+  if constexpr (kFlatRows) {
+    // amax: LDS atomic max of every chunk's |BF16| bit patterns into its row
+    __syncthreads();  // ramax zeroed
+#pragma unroll
+    for (int i = 0; i < kFlat; ++i) {
+      const int f = tid + i * kThreadsF, r = f / nchunk_p;
+      if (r < M)
+        atomicMax(&ramax[r], max(max(bf16_pair_absmax(vf[i].x), bf16_pair_absmax(vf[i].y)),
+                                 max(bf16_pair_absmax(vf[i].z), bf16_pair_absmax(vf[i].w))));
+    }
+    __syncthreads();
+    if (tid < M) srow[tid] = bf16_to_f32(ramax[tid]) / 127.0f;
+#pragma unroll
+    for (int i = 0; i < kFlat; ++i) {
+      const int f = tid + i * kThreadsF, r = f / nchunk_p, c = f % nchunk_p;
+      if (r >= M) break;
+      uint2 o = uint2{0u, 0u};  // past K: zero codes
+      if (c < nchunk) {
+        const uint32_t w4[4] = {vf[i].x, vf[i].y, vf[i].z, vf[i].w};
+        o = quant8_bf16(w4, bf16_to_f32(ramax[r]) / 127.0f);
+      }
+      *reinterpret_cast<uint2*>(qlds + r * Kp + (int64_t)c * 8) = o;
+    }
+  } else {
   // quant of the M rows: one barrier for the amax, one for the codes
 #pragma unroll
   for (int r = 0; r < kRows; ++r) {
@@ -1227,6 +1269,7 @@ __global__ __launch_bounds__(WAVES * kWave) void decode_fused_kernel(GemmArgs p)
       }
       *reinterpret_cast<uint2*>(qlds + r * Kp + (int64_t)c * 8) = o;
     }
+  }
   }
   __syncthreads();
   const int arow = lane & 15;
@@ -1409,11 +1452,13 @@ hipError_t launch_dense_gemm(const DensePlan& plan, const int8_t* q, const float
 }
 
 bool decode_fused_ok(int64_t M, int64_t K, const void* x) {
-  // K <= 16384: four 8-value chunks per thread and row
-  // (M <= 2: every workgroup quantizes the rows again, which outgrows the
-  // saved launch at four rows)
-  return M >= 1 && M <= 2 && K % 8 == 0 && K <= 16384 && ((uintptr_t)x & 15) == 0 &&
-         M * round_up(K, 64) <= kFusedLdsBytes;
+  // every workgroup quantizes the M x K values again: past kFusedElems (four
+  // rows of K = 7168 measured slower than the separate quant launch) the
+  // saved launch does not pay for it. Up to 2 rows K <= 16384 (two 8-value
+  // chunks per thread and row); up to 16 rows, the flat numbering (3 chunks
+  // per thread: M * Kp / 8 <= 3072 for M * K <= 16384, M <= 16)
+  return M >= 1 && M <= 16 && M * K <= kFusedElems && K % 8 == 0 && K <= 16384 &&
+         ((uintptr_t)x & 15) == 0 && M * round_up(K, 64) <= kFusedLdsBytes;
 }
 
 hipError_t launch_decode_fused(const uint16_t* x, int64_t M, int64_t K, const void* w_packed,
@@ -1424,8 +1469,12 @@ hipError_t launch_decode_fused(const uint16_t* x, int64_t M, int64_t K, const vo
   GemmArgs p = make_args(reinterpret_cast<const int8_t*>(x), nullptr, M, K, w_packed, w_scale, N, bias,
                          y, out);
   const size_t lds = (size_t)(M * round_up(K, 64));
-  hipLaunchKernelGGL((decode_fused_kernel<7, 16>), dim3((unsigned)ceil_div(N, 16)), dim3(16 * 64), lds, stream,
-                     p);
+  if (M <= 2)
+    hipLaunchKernelGGL((decode_fused_kernel<7, 16, 2, 2>), dim3((unsigned)ceil_div(N, 16)), dim3(16 * 64), lds,
+                       stream, p);
+  else
+    hipLaunchKernelGGL((decode_fused_kernel<7, 16, 16, 1>), dim3((unsigned)ceil_div(N, 16)), dim3(16 * 64), lds,
+                       stream, p);  // CPT unused: flat chunks
   return hipGetLastError();
 }
 

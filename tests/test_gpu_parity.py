@@ -150,21 +150,28 @@ def test_linear_acc_and_bf16_bit_exact(w, M, K, N, bias):
 
 
 def test_tiny_config(w):
+    """The tiny config through quant + linear and through the BF16-input linear
+    the benchmark step uses (quant inside the product kernel: 16 x 256 values)."""
     d = synth.tiny(seed=0)
     _, _, y = _run_linear(w, d, w.OUT_BF16)
+    y_in = w.linear_bf16(bf16_dev(d.x), w.prepack_weight(dev(d.w)), dev(d.w_scale), d.N,
+                         bias=bf16_dev(d.bias))
+    sync()
     qo, so = O.dynamic_quant(d.x)
     yo, _ = O.linear(qo, so, d.w, d.w_scale, d.bias)
     _assert_eq(bf16_host(y), yo, "tiny y")
+    _assert_eq(bf16_host(y_in), yo, "tiny y (BF16 input)")
 
 
 def _decode_dispatch(w, M, x, wp, ws_, N, K, bias=None):
     """The entry points a decode step uses for M rows: BF16 straight into the
-    linear (quant fused into the product) up to 2 rows; row-major codes for 3 to
-    15 rows; codes in the packed 1 KB blocks from 16 rows up."""
+    linear (quant fused into the product) up to 16 rows of M * K <= 16384 values;
+    else row-major codes below 16 rows and codes in the packed 1 KB blocks from
+    16 rows up."""
     y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
     wsp = torch.empty((max(1, w.linear_workspace_bytes(M, N, K)),), dtype=torch.uint8,
                       device="cuda")
-    if M <= 2 and K % 8 == 0:
+    if M <= 16 and M * K <= 16384 and K % 8 == 0:
         w.linear_bf16(x, wp, ws_, N, bias=bias, y=y, workspace=wsp)
         return "bf16 in (fused quant)", None, y
     if M >= 16 and K % 8 == 0:
@@ -428,7 +435,14 @@ def test_linear_packed_matches_row_major(w, M, N, K):
 
 BF16_LINEAR_SHAPES = [(1, 4096, 7168), (2, 256, 512), (3, 100, 256), (4, 4096, 7168), (5, 300, 520),
                       (16, 4096, 7168), (64, 512, 7168), (65, 300, 520), (3, 64, 100), (300, 1088, 600),
-                      (4, 64, 16392)]
+                      (4, 64, 16392),
+                      # quant inside the product for up to 16 rows of M * K <= 16384
+                      # values (chunks numbered flat): the tiny shape, exactly
+                      # 16384 values, K % 64 != 0 (zero code chunks), M * Kp / 8
+                      # near the 3 chunks per thread, K = 8; then just past the
+                      # limit (quant launch + product)
+                      (16, 128, 256), (16, 200, 1024), (9, 96, 1000), (7, 48, 2336), (15, 40, 8),
+                      (16, 64, 1032)]
 
 
 @pytest.mark.parametrize("M,N,K", BF16_LINEAR_SHAPES)
