@@ -542,10 +542,12 @@ hipError_t launch_fp4_quant_pack(const uint16_t* w, int64_t N, int64_t K, uint8_
 // LDS operations complete in order, so no barrier is needed. The next chunk's
 // codes, scales and activation rows are loaded before this chunk's
 // dequantization. A workgroup covers 16 MB rows x 16 NBW columns (grid.y:
-// row groups). After the loop each wavefront's partial sums go into its own
-// region for the reduction.
+// row groups). SKIP (few rows): groups of 4 rows wholly past M are not
+// written to LDS either (the fragments then read stale rows, whose outputs
+// are never stored). After the loop each wavefront's partial sums go into
+// its own region for the reduction.
 // ---------------------------------------------------------------------------
-template <int MB, int NBW, int FMT>
+template <int MB, int NBW, int FMT, bool SKIP>
 __global__ __launch_bounds__(1024) void w4a16_rows_kernel(const uint16_t* __restrict__ x, int64_t M,
                                                           int64_t K, const uint8_t* __restrict__ wp,
                                                           int64_t KC, int64_t N, uint16_t* __restrict__ y) {
@@ -615,7 +617,8 @@ __global__ __launch_bounds__(1024) void w4a16_rows_kernel(const uint16_t* __rest
     }
 #pragma unroll
     for (int i = 0; i < kLoads; ++i)
-      *reinterpret_cast<uint4*>(st + (4 * i + (lane >> 4)) * kPitch + (lane & 15) * 16) = xn[i];
+      if (!SKIP || row0 + 4 * i < M)  // wavefront-uniform
+        *reinterpret_cast<uint4*>(st + (4 * i + (lane >> 4)) * kPitch + (lane & 15) * 16) = xn[i];
     if (kc + WAVES < KC) {  // wavefront-uniform
       load_w(kc + WAVES, codes_n, sc_n);
       load_x(kc + WAVES, xn);
@@ -678,8 +681,8 @@ static hipError_t launch_decode(const uint16_t* x, int64_t M, int64_t K, const u
   const int64_t NB = (N + 15) / 16, KC = w4_chunks(K);
   (void)ws;  // no workspace: the activation rows are staged in LDS
   if (M <= 16) {  // one 16-column block per workgroup: 256 workgroups at N = 4096
-    hipLaunchKernelGGL((w4a16_rows_kernel<1, 1, FMT>), dim3((unsigned)NB, 1), dim3(1024), 0, stream, x, M, K,
-                       wp, KC, N, y);
+    hipLaunchKernelGGL((w4a16_rows_kernel<1, 1, FMT, true>), dim3((unsigned)NB, 1), dim3(1024), 0, stream, x, M,
+                       K, wp, KC, N, y);
     return hipGetLastError();
   }
   // more rows: a workgroup covers 16 MB rows x 16 NBW columns: INT4 32 x 32,
@@ -687,7 +690,7 @@ static hipError_t launch_decode(const uint16_t* x, int64_t M, int64_t K, const u
   // 19) 16 x 64, so a workgroup reads 458 / 229 KB of the 64-row activation
   // instead of 917
   constexpr int MB = FMT == 0 ? 2 : 1, NBW = FMT == 0 ? 2 : 4;
-  hipLaunchKernelGGL((w4a16_rows_kernel<MB, NBW, FMT>),
+  hipLaunchKernelGGL((w4a16_rows_kernel<MB, NBW, FMT, false>),
                      dim3((unsigned)((NB + NBW - 1) / NBW), (unsigned)((M + 16 * MB - 1) / (16 * MB))), dim3(1024),
                      0, stream, x, M, K, wp, KC, N, y);
   return hipGetLastError();
