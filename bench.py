@@ -184,7 +184,8 @@ class DenseWorkload(Workload):
         # BF16 straight into linear where it quantizes inside the product kernel
         # (every workgroup quantizes the rows again: up to 16 rows of at most
         # 16384 values, K % 8 == 0)
-        self.fused = {M: M <= 16 and M * K <= 16384 and K % 8 == 0 for M in self.Ms}
+        self.fused = {M: (M <= 2 or (M <= 16 and M * K <= 16384)) and K <= 16384 and K % 8 == 0
+                      for M in self.Ms}
         self.q = {M: (torch.empty((w.packed_weight_bytes(1, M, K),), dtype=torch.uint8, device=dev)
                       if self.packed[M] else torch.empty((M, K), dtype=torch.int8, device=dev))
                   for M in self.Ms}

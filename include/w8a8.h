@@ -140,9 +140,10 @@ int w8a8_prepack_weight(const int8_t* w, int64_t E, int64_t N, int64_t K,
  *            w8a8_dynamic_quant_packed; or, when x_scale == NULL, the BF16
  *            activation x [M, K] row-major, quantized inside exactly as
  *            w8a8_dynamic_quant does ([DSV4 §三]: quantize only when the
- *            per-token scale is missing) — for M <= 16 with M * K <= 16384
- *            (K % 8 == 0, x 16-byte aligned; every workgroup quantizes the
- *            rows again) in the same kernel as the product, else through the
+ *            per-token scale is missing) — for M <= 2, or M <= 16 with
+ *            M * K <= 16384 (K <= 16384, K % 8 == 0, x 16-byte aligned; every
+ *            workgroup quantizes the rows again) in the same kernel as the
+ *            product, else through the
  *            workspace; the result equals quant + linear bit for bit
  *   x_scale  device, float [M], or NULL for BF16 input
  *   w_packed device, packed weight of one [N, K] matrix (E = 1)

@@ -1454,10 +1454,10 @@ hipError_t launch_dense_gemm(const DensePlan& plan, const int8_t* q, const float
 bool decode_fused_ok(int64_t M, int64_t K, const void* x) {
   // every workgroup quantizes the M x K values again: past kFusedElems (four
   // rows of K = 7168 measured slower than the separate quant launch) the
-  // saved launch does not pay for it. Up to 2 rows K <= 16384 (two 8-value
-  // chunks per thread and row); up to 16 rows, the flat numbering (3 chunks
-  // per thread: M * Kp / 8 <= 3072 for M * K <= 16384, M <= 16)
-  return M >= 1 && M <= 16 && M * K <= kFusedElems && K % 8 == 0 && K <= 16384 &&
+  // saved launch does not pay for it, except for 1 or 2 rows (K <= 16384: two
+  // 8-value chunks per thread and row). 3 to 16 rows take the flat numbering
+  // (3 chunks per thread: M * Kp / 8 <= 3072 for M * K <= 16384, M <= 16)
+  return M >= 1 && (M <= 2 || (M <= 16 && M * K <= kFusedElems)) && K % 8 == 0 && K <= 16384 &&
          ((uintptr_t)x & 15) == 0 && M * round_up(K, 64) <= kFusedLdsBytes;
 }
 

@@ -27,9 +27,9 @@ struct DensePlan {
   int64_t ws_bytes;  // device workspace the variant needs (0 for every variant today)
 };
 DensePlan plan_dense(int64_t M, int64_t N, int64_t K);
-// quant fused into the decode GEMM (BF16 input, M <= 16 and M * K <=
-// kFusedElems, K % 8 == 0, 16-byte aligned x, the codes of all rows within
-// kFusedLdsBytes of LDS)
+// quant fused into the decode GEMM (BF16 input, M <= 2 or M <= 16 with
+// M * K <= kFusedElems, K <= 16384, K % 8 == 0, 16-byte aligned x, the codes
+// of all rows within kFusedLdsBytes of LDS)
 constexpr int64_t kFusedLdsBytes = 65536;
 constexpr int64_t kFusedElems = 16384;
 bool decode_fused_ok(int64_t M, int64_t K, const void* x);

@@ -165,13 +165,14 @@ def test_tiny_config(w):
 
 def _decode_dispatch(w, M, x, wp, ws_, N, K, bias=None):
     """The entry points a decode step uses for M rows: BF16 straight into the
-    linear (quant fused into the product) up to 16 rows of M * K <= 16384 values;
+    linear (quant fused into the product) for 1 or 2 rows and up to 16 rows of
+    M * K <= 16384 values;
     else row-major codes below 16 rows and codes in the packed 1 KB blocks from
     16 rows up."""
     y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
     wsp = torch.empty((max(1, w.linear_workspace_bytes(M, N, K)),), dtype=torch.uint8,
                       device="cuda")
-    if M <= 16 and M * K <= 16384 and K % 8 == 0:
+    if (M <= 2 or (M <= 16 and M * K <= 16384)) and K <= 16384 and K % 8 == 0:
         w.linear_bf16(x, wp, ws_, N, bias=bias, y=y, workspace=wsp)
         return "bf16 in (fused quant)", None, y
     if M >= 16 and K % 8 == 0:
@@ -442,7 +443,9 @@ BF16_LINEAR_SHAPES = [(1, 4096, 7168), (2, 256, 512), (3, 100, 256), (4, 4096, 7
                       # near the 3 chunks per thread, K = 8; then just past the
                       # limit (quant launch + product)
                       (16, 128, 256), (16, 200, 1024), (9, 96, 1000), (7, 48, 2336), (15, 40, 8),
-                      (16, 64, 1032)]
+                      (16, 64, 1032),
+                      # two rows of K = 16384 (fused; past the 16384-value limit)
+                      (2, 80, 16384)]
 
 
 @pytest.mark.parametrize("M,N,K", BF16_LINEAR_SHAPES)
